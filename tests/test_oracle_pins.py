@@ -1,0 +1,362 @@
+"""Pins for the float64 oracle, each against something other than the oracle
+itself: printed numbers on the pages, hand-derived closed forms, brute force
+over subsets, an independent library (torch's SDPA in float64 on the CPU),
+special cases and invariants.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- Eq. (12)
+
+def test_eq12_ratio_matches_printed_28_4():
+    g = _golden("eq12_flop_ratio.json")
+    f_gqa, f_idx, f_main = orc.flops_eq12(g["n"], g["h_q"], g["h_kv"], g["d_h"], 128,
+                                          g["top_k"], g["block"])
+    ratio = f_gqa / (f_idx + f_main)
+    assert abs(ratio - g["ratio_printed"]) < g["printed_precision"]
+    # the index term is quadratic, the main term linear in N
+    f2 = orc.flops_eq12(2 * g["n"], g["h_q"], g["h_kv"], g["d_h"], 128, g["top_k"])
+    assert f2[1] == pytest.approx(4 * f_idx)
+    assert f2[2] == pytest.approx(2 * f_main)
+
+
+# ------------------------------------------------- index branch: closed form
+
+def _closed_form_inputs(g):
+    n_kv, d = g["n_kv"], g["d_idx"]
+    k_idx = np.zeros((n_kv, d))
+    k_idx[:, 0] = -1.0
+    for b, (v, o) in enumerate(zip(g["peak_value"], g["peak_offset"])):
+        k_idx[b * 128 + o, 0] = v
+    q_row = np.zeros((g["h_kv"], d))
+    q_row[:, 0] = g["group_coef"]
+    return q_row, k_idx
+
+
+def test_closed_form_selection_and_scores():
+    g = _golden("closed_form_selection.json")
+    q_row, k_idx = _closed_form_inputs(g)
+    for case in g["cases"]:
+        p = case["p"]
+        ids, sc, pooled = orc.index_topk(q_row[None], k_idx, p, case["top_k"],
+                                         force_local=case["force_local"])
+        assert ids[0].tolist() == case["expect"], case["why"]
+        if "expect_score_group0" in case:
+            np.testing.assert_allclose(sc[0, 0], case["expect_score_group0"], rtol=1e-12)
+        if "expect_diag_score_group0" in case:
+            assert pooled[0][0, p // 128] == pytest.approx(case["expect_diag_score_group0"], rel=1e-12)
+
+
+def test_token_scores_closed_form_scale():
+    # S_j = <q, k_j> / sqrt(d): orthogonal unit vectors give 0, parallel give |q||k|/sqrt(d)
+    d = 16
+    q = np.zeros((1, d))
+    q[0, 3] = 5.0
+    k = np.zeros((4, d))
+    k[0, 3] = 2.0
+    k[1, 4] = 7.0
+    k[2, 3] = -1.5
+    k[3, :] = 1.0
+    s = orc.index_token_scores(q, k, 3)
+    np.testing.assert_allclose(s[0], [10.0 / 4.0, 0.0, -7.5 / 4.0, 5.0 / 4.0], rtol=1e-15)
+    s2 = orc.index_token_scores(q, k, 1, idx_scale=1.0)
+    np.testing.assert_allclose(s2[0], [10.0, 0.0])
+
+
+# ---------------------------------------------- index branch: brute force
+
+def _brute_force_topk(m, diag, k, force_local):
+    """Enumerate every subset of the eligible blocks of the right size and keep
+    the one(s) where every chosen block beats every left-out block under
+    (score desc, index asc)."""
+    cand = list(range(diag)) if force_local else list(range(diag + 1))
+    take = min(len(cand), k - 1 if force_local else k)
+    winners = []
+    for sub in itertools.combinations(cand, take):
+        rest = [b for b in cand if b not in sub]
+        ok = all((m[s] > m[u]) or (m[s] == m[u] and s < u) for s in sub for u in rest)
+        if ok:
+            winners.append(sorted(list(sub) + ([diag] if force_local else [])))
+    assert len(winners) == 1
+    w = winners[0]
+    return w + [-1] * (k - len(w))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_selection_matches_subset_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    diag = int(rng.integers(0, 9))
+    k = int(rng.integers(1, 6))
+    # few distinct values so ties are common
+    m = rng.integers(-3, 4, size=diag + 1).astype(np.float64) * 0.5
+    for force in (True, False):
+        if not force and k < 1:
+            continue
+        got = orc.select_blocks(m, diag, k, force_local=force).tolist()
+        assert got == _brute_force_topk(m, diag, k, force)
+
+
+def test_exp_free_selection_invariance():
+    # selection on raw pooled scores equals selection on exp(scores) and on a
+    # row softmax of the token scores (monotone maps keep the order)
+    rng = np.random.default_rng(7)
+    n, d = 1500, 16
+    q = rng.standard_normal((6, 2, d))
+    k = rng.standard_normal((n, d))
+    for i in range(q.shape[0]):
+        p = int(rng.integers(0, n))
+        s = orc.index_token_scores(q[i], k, p)
+        m_raw = orc.block_max_pool(s, p)
+        m_exp = orc.block_max_pool(np.exp(s), p)
+        soft = np.exp(s - s.max(axis=1, keepdims=True))
+        soft /= soft.sum(axis=1, keepdims=True)
+        m_soft = orc.block_max_pool(soft, p)
+        for r in range(2):
+            a = orc.select_blocks(m_raw[r], p // 128, 5)
+            assert (a == orc.select_blocks(m_exp[r], p // 128, 5)).all()
+            assert (a == orc.select_blocks(m_soft[r], p // 128, 5)).all()
+
+
+def test_selection_invariants_random():
+    rng = np.random.default_rng(11)
+    n, d, h_kv, k = 3000, 32, 3, 6
+    q = rng.standard_normal((n, h_kv, d))
+    kk = rng.standard_normal((n, d))
+    rows = rng.choice(n, 60, replace=False)
+    ids, sc, _ = orc.index_topk(q, kk, 0, k, rows=rows)
+    for t, i in enumerate(rows):
+        diag = i // 128
+        for r in range(h_kv):
+            row = ids[t, r]
+            valid = row[row >= 0]
+            assert len(valid) == min(k, diag + 1)
+            assert (row[len(valid):] == -1).all()
+            assert (np.diff(valid) > 0).all()
+            assert valid.max() == diag and diag in valid
+            assert (sc[t, r][row < 0] == -np.inf).all()
+    # scaling either index tensor by c > 0 changes nothing
+    ids2, _, _ = orc.index_topk(q * 3.5, kk, 0, k, rows=rows)
+    ids3, _, _ = orc.index_topk(q, kk * 0.25, 0, k, rows=rows)
+    assert (ids2 == ids).all() and (ids3 == ids).all()
+
+
+def test_block_pool_is_order_free_inside_past_blocks():
+    rng = np.random.default_rng(5)
+    n, d = 1024, 8
+    q = rng.standard_normal((2, d))
+    k = rng.standard_normal((n, d))
+    p = 1000
+    m0 = orc.block_max_pool(orc.index_token_scores(q, k, p), p)
+    k2 = k.copy()
+    perm = rng.permutation(128) + 256          # shuffle tokens of block 2
+    k2[256:384] = k[perm]
+    m1 = orc.block_max_pool(orc.index_token_scores(q, k2, p), p)
+    np.testing.assert_array_equal(m0, m1)
+    # moving the block's best token into the next block moves the block max
+    s = orc.index_token_scores(q, k, p)
+    j = 256 + int(np.argmax(s[0, 256:384]))
+    k3 = k.copy()
+    k3[[j, 384]] = k3[[384, j]]
+    m3 = orc.block_max_pool(orc.index_token_scores(q, k3, p), p)
+    assert m3[0, 3] >= m0[0, 2]
+
+
+def test_planted_blocks_are_retrieved():
+    # scaled-down version of the planted long-context workload
+    from synth import gen_planted_prefill
+    from synth.inputs import HeadShape as HS
+    shape = HS(h_q=8, h_kv=4, d_h=32, d_idx=64, top_k=16)
+    inp = gen_planted_prefill(16384, shape, dtype=torch.float32, n_designated=12,
+                              plant_hi=64, designated_after=8192, seed=21)
+    q_idx = inp["q_idx"].double().numpy()
+    k_idx = inp["k_idx"].double().numpy()
+    rows = inp["designated"].tolist()
+    ids, _, _ = orc.index_topk(q_idx, k_idx, 0, 16, rows=rows)
+    for t in range(len(rows)):
+        for r in range(4):
+            assert set(inp["planted_blocks"][r].tolist()) <= set(ids[t, r].tolist())
+
+
+# ------------------------------------------------- main branch pins
+
+def _sdpa_masked(q, k, v, mask, scale=None):
+    """torch SDPA in float64 on the CPU with an explicit boolean mask
+    [n_q, n_kv] per KV group.  q [n_q, h_q, d]; k/v [n_kv, h_kv, d]."""
+    n_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    g = h_q // h_kv
+    qt = torch.from_numpy(np.ascontiguousarray(q)).permute(1, 0, 2)              # [h_q, n_q, d]
+    kt = torch.from_numpy(np.ascontiguousarray(k)).permute(1, 0, 2).repeat_interleave(g, 0)
+    vt = torch.from_numpy(np.ascontiguousarray(v)).permute(1, 0, 2).repeat_interleave(g, 0)
+    m = torch.from_numpy(mask).repeat_interleave(g, 0)                          # [h_q, n_q, n_kv]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def _rand_qkv(rng, n_q, n_kv, h_q, h_kv, d):
+    return (rng.standard_normal((n_q, h_q, d)), rng.standard_normal((n_kv, h_kv, d)),
+            rng.standard_normal((n_kv, h_kv, d)))
+
+
+def test_dense_matches_torch_sdpa():
+    rng = np.random.default_rng(3)
+    n_kv, n_q, h_q, h_kv, d = 300, 50, 8, 2, 16
+    q, k, v = _rand_qkv(rng, n_q, n_kv, h_q, h_kv, d)
+    q_start = n_kv - n_q
+    o, lse = orc.dense_attention(q, k, v, q_start)
+    pos = q_start + np.arange(n_q)
+    mask = (np.arange(n_kv)[None, :] <= pos[:, None])
+    ref = _sdpa_masked(q, k, v, np.broadcast_to(mask, (h_kv, n_q, n_kv)).copy())
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+    # lse against torch.logsumexp of the masked scores
+    s = np.einsum("ihd,jhd->hij", q[:, :1], k[:, :1]) / math.sqrt(d)
+    s = np.where(mask[None], s, -np.inf)
+    ref_lse = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()[0]
+    np.testing.assert_allclose(lse[:, 0], ref_lse, rtol=1e-12)
+
+
+def test_sparse_matches_masked_sdpa_for_arbitrary_selections():
+    rng = np.random.default_rng(4)
+    n, h_q, h_kv, d, k = 900, 8, 2, 16, 3
+    q, kk, v = _rand_qkv(rng, n, n, h_q, h_kv, d)
+    bidx = np.full((n, h_kv, k), -1, dtype=np.int64)
+    mask = np.zeros((h_kv, n, n), dtype=bool)
+    for i in range(n):
+        diag = i // 128
+        for r in range(h_kv):
+            chosen = sorted(set(rng.choice(diag + 1, size=min(k, diag + 1), replace=False).tolist()))
+            bidx[i, r, :len(chosen)] = chosen
+            for b in chosen:
+                mask[r, i, b * 128:min(b * 128 + 128, i + 1)] = True
+    rows = list(range(0, n, 7))
+    o, _ = orc.sparse_attention(q, kk, v, bidx, 0, rows=rows)
+    ref = _sdpa_masked(q, kk, v, mask)
+    np.testing.assert_allclose(o, ref[rows], rtol=1e-10, atol=1e-12)
+    # a scale argument reaches the softmax
+    o2, _ = orc.sparse_attention(q, kk, v, bidx, 0, rows=rows, sm_scale=0.3)
+    ref2 = _sdpa_masked(q, kk, v, mask, scale=0.3)
+    np.testing.assert_allclose(o2, ref2[rows], rtol=1e-10, atol=1e-12)
+
+
+def test_full_coverage_and_short_sequences_reduce_to_dense():
+    rng = np.random.default_rng(6)
+    n, h_q, h_kv, d = 700, 4, 1, 8
+    q, k, v = _rand_qkv(rng, n, n, h_q, h_kv, d)
+    qi = rng.standard_normal((n, h_kv, 4))
+    ki = rng.standard_normal((n, 4))
+    nb = -(-n // 128)
+    ids, _, _ = orc.index_topk(qi, ki, 0, nb)
+    o_s, l_s = orc.sparse_attention(q, k, v, ids, 0)
+    o_d, l_d = orc.dense_attention(q, k, v, 0)
+    np.testing.assert_allclose(o_s, o_d, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l_s, l_d, rtol=1e-12)
+    # N <= 128: one block, any k gives dense attention
+    ids1, _, _ = orc.index_topk(qi[:100], ki[:100], 0, 1)
+    o1, _ = orc.sparse_attention(q[:100], k[:100], v[:100], ids1, 0)
+    np.testing.assert_allclose(o1, orc.dense_attention(q[:100], k[:100], v[:100], 0)[0], rtol=1e-12)
+
+
+def test_k_equal_one_is_block_local_attention():
+    rng = np.random.default_rng(8)
+    n, h_q, h_kv, d = 400, 4, 2, 8
+    q, k, v = _rand_qkv(rng, n, n, h_q, h_kv, d)
+    qi = rng.standard_normal((n, h_kv, 4))
+    ki = rng.standard_normal((n, 4))
+    ids, _, _ = orc.index_topk(qi, ki, 0, 1)
+    assert (ids[:, :, 0] == (np.arange(n) // 128)[:, None]).all()
+    o, _ = orc.sparse_attention(q, k, v, ids, 0)
+    blk = np.arange(n) // 128
+    mask = (blk[None, :] == blk[:, None]) & (np.arange(n)[None, :] <= np.arange(n)[:, None])
+    ref = _sdpa_masked(q, k, v, np.broadcast_to(mask, (h_kv, n, n)).copy())
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_uniform_values_and_two_key_closed_form():
+    rng = np.random.default_rng(9)
+    n, h_q, h_kv, d = 260, 4, 1, 8
+    q, k, _ = _rand_qkv(rng, n, n, h_q, h_kv, d)
+    vrow = rng.standard_normal(d)
+    v = np.broadcast_to(vrow, (n, h_kv, d)).copy()
+    ids = np.tile(np.array([0, 1, 2, -1]), (n, h_kv, 1))
+    o, _ = orc.sparse_attention(q, k, v, ids, 0)
+    np.testing.assert_allclose(o, np.broadcast_to(vrow, o.shape), rtol=1e-13)
+    # two visible keys with scores 0 and ln 3 -> weights 1/4 and 3/4
+    d = 4
+    q2 = np.zeros((2, 1, d))
+    q2[1, 0, 0] = 2.0
+    k2 = np.zeros((2, 1, d))
+    k2[1, 0, 0] = math.log(3.0)            # (2 * ln3) / sqrt(4) = ln 3
+    v2 = np.array([[[1.0, 0, 0, 0]], [[0, 1.0, 0, 0]]])
+    o2, lse2 = orc.sparse_attention(q2, k2, v2, np.array([[[0]], [[0]]]), 0)
+    np.testing.assert_allclose(o2[1, 0], [0.25, 0.75, 0, 0], rtol=1e-14)
+    assert lse2[1, 0] == pytest.approx(math.log(4.0))
+    np.testing.assert_allclose(o2[0, 0], v2[0, 0])
+
+
+def test_lse_merge_of_per_block_results_equals_whole():
+    rng = np.random.default_rng(10)
+    n, h_q, h_kv, d = 800, 8, 2, 16
+    q, k, v = _rand_qkv(rng, n, n, h_q, h_kv, d)
+    i = 777
+    ids = np.array([[[0, 2, 5, 6], [1, 3, 4, 6]]])
+    o, lse = orc.sparse_attention(q[i:i + 1], k, v, ids, i)
+    parts = []
+    for j in range(4):
+        one = ids[:, :, j:j + 1]
+        parts.append(orc.sparse_attention(q[i:i + 1], k, v, one, i))
+    lses = np.stack([pl for _, pl in parts])            # [4, 1, h_q]
+    outs = np.stack([po for po, _ in parts])            # [4, 1, h_q, d]
+    top = lses.max(axis=0)
+    w = np.exp(lses - top)
+    merged = (w[..., None] * outs).sum(axis=0) / w.sum(axis=0)[..., None]
+    np.testing.assert_allclose(merged, o, rtol=1e-12)
+    np.testing.assert_allclose(top + np.log(w.sum(axis=0)), lse, rtol=1e-12)
+
+
+# ------------------------------------------------------------ paged caches
+
+def test_paged_oracles_equal_contiguous():
+    rng = np.random.default_rng(12)
+    h_q, h_kv, d, di, k = 8, 2, 16, 8, 4
+    lens = [700, 129, 1024]
+    max_pages = 8
+    n_pages = len(lens) * max_pages
+    pt = rng.permutation(n_pages).reshape(len(lens), max_pages)
+    kp = rng.standard_normal((n_pages, h_kv, 128, d))
+    vp = rng.standard_normal((n_pages, h_kv, 128, d))
+    ip = rng.standard_normal((n_pages, 128, di))
+    q = rng.standard_normal((len(lens), h_q, d))
+    qi = rng.standard_normal((len(lens), h_kv, di))
+    ids, _, _ = orc.index_topk_decode(qi, ip, pt, lens, k)
+    o, lse = orc.sparse_decode(q, kp, vp, pt, lens, ids)
+    for s, L in enumerate(lens):
+        # contiguous copies built here by scattering page rows token by token
+        kc = np.empty((L, h_kv, d))
+        vc = np.empty((L, h_kv, d))
+        ic = np.empty((L, di))
+        for j in range(L):
+            page, row = pt[s, j // 128], j % 128
+            kc[j] = kp[page, :, row, :]
+            vc[j] = vp[page, :, row, :]
+            ic[j] = ip[page, row, :]
+        ids_c, _, _ = orc.index_topk(qi[s:s + 1], ic, L - 1, k)
+        assert (ids_c[0] == ids[s]).all()
+        o_c, l_c = orc.sparse_attention(q[s:s + 1], kc, vc, ids_c, L - 1)
+        np.testing.assert_allclose(o[s], o_c[0], rtol=1e-13)
+        np.testing.assert_allclose(lse[s], l_c[0], rtol=1e-13)
