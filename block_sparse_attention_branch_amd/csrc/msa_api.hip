@@ -1,0 +1,323 @@
+// msa_api.hip - the C ABI of libmsa (declared in include/msa.h): argument
+// validation, workspace layout and kernel dispatch.  Every check runs on the
+// host before anything is launched; on failure the call returns a status,
+// launches nothing and leaves the outputs untouched.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/msa.h"
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float idx_scale_of(const msa_shape& s) { return s.idx_scale > 0.f ? s.idx_scale : 1.0f / sqrtf((float)s.d_idx); }
+float sm_scale_of(const msa_shape& s) { return s.sm_scale > 0.f ? s.sm_scale : 1.0f / sqrtf((float)s.d_h); }
+
+// Checks common to every call.  `need_idx` / `need_attn` select the fields used.
+msa_status check_shape(const msa_shape* s, bool need_idx, bool need_attn) {
+  if (!s) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->h_q <= 0 || s->h_kv <= 0) return fail(MSA_ERR_INVALID_ARG, "h_q=%d h_kv=%d must be > 0", s->h_q, s->h_kv);
+  if (s->h_q % s->h_kv != 0) return fail(MSA_ERR_INVALID_ARG, "h_q=%d is not a multiple of h_kv=%d", s->h_q, s->h_kv);
+  const int G = s->h_q / s->h_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(MSA_ERR_UNSUPPORTED, "heads per group h_q/h_kv=%d not in {1,2,4,8,16}", G);
+  if (s->block_size != MSA_BLOCK_SIZE) return fail(MSA_ERR_UNSUPPORTED, "block_size=%d, only 128 is built", s->block_size);
+  if (s->dtype != MSA_BF16 && s->dtype != MSA_FP32) return fail(MSA_ERR_INVALID_ARG, "dtype=%d is not a msa_dtype", s->dtype);
+  if (s->top_k < 1 || s->top_k > MSA_MAX_TOP_K) return fail(MSA_ERR_UNSUPPORTED, "top_k=%d not in [1,16]", s->top_k);
+  if (s->force_local != 0 && s->force_local != 1) return fail(MSA_ERR_INVALID_ARG, "force_local=%d must be 0 or 1", s->force_local);
+  if (!(s->sm_scale >= 0.f) || !(s->idx_scale >= 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "sm_scale=%g idx_scale=%g must be >= 0 (0 = default)", s->sm_scale, s->idx_scale);
+  if (need_idx && !msa::ki_supported(s->dtype, s->d_idx))
+    return fail(MSA_ERR_UNSUPPORTED, "d_idx=%d not in {32,64,128}", s->d_idx);
+  if (need_attn && !msa::attn_supported(s->dtype, s->d_h))
+    return fail(MSA_ERR_UNSUPPORTED, "d_h=%d not in {64,128}", s->d_h);
+  return MSA_OK;
+}
+
+msa_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MSA_OK;
+  if (!ws) return fail(MSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return MSA_OK;
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t ki_prefill_ws(const msa_shape& s, int32_t n_q, int32_t q_start, int need_diag) {
+  const msa::KiPlan p = msa::ki_prefill_plan(n_q, s.h_kv, q_start, need_diag);
+  if (p.n_chunks <= 1) return 0;
+  const size_t keys = (size_t)p.n_rows * p.n_chunks * 16 * 8;
+  return ((keys + 255) & ~size_t(255)) + (((size_t)p.n_rows * 4 + 255) & ~size_t(255));
+}
+
+constexpr int32_t kMaxDecodePages = 16384;
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_status_string(msa_status st) {
+  switch (st) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int32_t n_q, int32_t q_start,
+                          int32_t n_kv, int32_t max_pages) {
+  if (op < 0 || op > 4) {
+    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..4", op);
+    return 0;
+  }
+  if (check_shape(shape, op == 0 || op == 4, op >= 1 && op <= 3) != MSA_OK) return 0;
+  if (batch < 0 || n_q < 0 || q_start < 0 || n_kv < 0 || max_pages < 0) {
+    fail(MSA_ERR_INVALID_ARG, "negative size");
+    return 0;
+  }
+  const msa_shape& s = *shape;
+  (void)n_kv;
+  ok();
+  switch (op) {
+    case 0:
+      return std::max(ki_prefill_ws(s, n_q, q_start, 0), ki_prefill_ws(s, n_q, q_start, 1));
+    case 4:  // decode mode: pooled score of every page
+      return (size_t)batch * s.h_kv * max_pages * 4;
+    case 1:
+      if (n_q == 0) return 0;
+      return msa::prefill_plan(s.dtype, n_q, q_start, n_kv, s.h_q, s.h_kv, s.d_h, s.top_k).total;
+    case 2:
+      return msa::decode_plan(batch, s.h_q, s.h_kv, s.d_h, s.top_k).total;
+    default:
+      return 0;
+  }
+}
+
+msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, int32_t q_start,
+                          const void* q_idx, const msa_kv* kv, int32_t* block_idx, float* block_score,
+                          void* workspace, size_t ws_bytes, void* hip_stream) {
+  msa_status st = check_shape(shape, true, false);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (batch < 0 || n_q < 0 || q_start < 0) return fail(MSA_ERR_INVALID_ARG, "batch=%d n_q=%d q_start=%d", batch, n_q, q_start);
+  if (!kv->k_idx) return fail(MSA_ERR_INVALID_ARG, "kv->k_idx is NULL");
+  if (!aligned16(q_idx) || !aligned16(kv->k_idx)) return fail(MSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const float idx_scale = idx_scale_of(s);
+  const int need_diag = (block_score != nullptr) ? 1 : 0;
+
+  if (kv->seq_lens) {  // decode mode
+    if (n_q != 1) return fail(MSA_ERR_INVALID_ARG, "decode mode (seq_lens given) needs n_q == 1, got %d", n_q);
+    if (!kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs a page_table");
+    if (kv->max_pages < 1 || kv->max_pages > kMaxDecodePages)
+      return fail(MSA_ERR_UNSUPPORTED, "max_pages=%d not in [1,%d]", kv->max_pages, kMaxDecodePages);
+    if (batch == 0) return ok();
+    if (!q_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "q_idx/block_idx is NULL");
+    const size_t need = (size_t)batch * s.h_kv * kv->max_pages * 4;
+    if ((st = check_ws(workspace, ws_bytes, need)) != MSA_OK) return st;
+    msa::KiDecodeArgs a{};
+    a.q_idx = q_idx;
+    a.k_idx = kv->k_idx;
+    a.page_table = kv->page_table;
+    a.seq_lens = kv->seq_lens;
+    a.batch = batch;
+    a.h_kv = s.h_kv;
+    a.max_pages = kv->max_pages;
+    a.pages_per_wg = 16;
+    a.idx_scale = idx_scale;
+    a.force_local = s.force_local;
+    a.top_k = s.top_k;
+    a.need_diag = need_diag;
+    a.scores = static_cast<float*>(workspace);
+    a.block_idx = block_idx;
+    a.block_score = block_score;
+    return hip_status(msa::launch_ki_decode(s.dtype, s.d_idx, a, stream), "msa_index_topk(decode)");
+  }
+
+  if (batch != 1) return fail(MSA_ERR_INVALID_ARG, "prefill mode handles one sequence: batch must be 1, got %d", batch);
+  if ((int64_t)q_start + n_q > kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "q_start + n_q = %lld exceeds n_kv = %d", (long long)q_start + n_q, kv->n_kv);
+  if (kv->page_table && (int64_t)kv->max_pages * MSA_BLOCK_SIZE < kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "max_pages=%d too small for n_kv=%d", kv->max_pages, kv->n_kv);
+  if ((int64_t)n_q * s.h_kv * s.top_k >= (int64_t(1) << 31)) return fail(MSA_ERR_UNSUPPORTED, "n_q too large");
+  if (n_q == 0) return ok();
+  if (!q_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "q_idx/block_idx is NULL");
+  const msa::KiPlan p = msa::ki_prefill_plan(n_q, s.h_kv, q_start, need_diag);
+  const size_t need = ki_prefill_ws(s, n_q, q_start, need_diag);
+  if ((st = check_ws(workspace, ws_bytes, need)) != MSA_OK) return st;
+  msa::KiPrefillArgs a{};
+  a.q_idx = q_idx;
+  a.k_idx = kv->k_idx;
+  a.page_table = kv->page_table;
+  a.n_rows = p.n_rows;
+  a.h_kv = s.h_kv;
+  a.q_start = q_start;
+  a.n_kv = kv->n_kv;
+  a.chunk_blocks = p.chunk_blocks;
+  a.n_chunks = p.n_chunks;
+  a.n_tiles = p.n_tiles;
+  a.idx_scale = idx_scale;
+  a.force_local = s.force_local;
+  a.top_k = s.top_k;
+  a.need_diag = need_diag;
+  a.block_idx = block_idx;
+  a.block_score = block_score;
+  if (p.n_chunks > 1) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t keys = ((size_t)p.n_rows * p.n_chunks * 16 * 8 + 255) & ~size_t(255);
+    a.part_keys = reinterpret_cast<uint64_t*>(ws);
+    a.part_diag = reinterpret_cast<float*>(ws + keys);
+  }
+  return hip_status(msa::launch_ki_prefill(s.dtype, s.d_idx, a, stream), "msa_index_topk(prefill)");
+}
+
+msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
+                              const msa_kv* kv, const int32_t* block_idx, void* o, float* lse,
+                              void* workspace, size_t ws_bytes, void* hip_stream) {
+  msa_status st = check_shape(shape, false, true);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_prefill takes one sequence: seq_lens must be NULL");
+  if (n_q < 0 || q_start < 0) return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d", n_q, q_start);
+  if ((int64_t)q_start + n_q > kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "q_start + n_q = %lld exceeds n_kv = %d", (long long)q_start + n_q, kv->n_kv);
+  if (kv->page_table && (int64_t)kv->max_pages * MSA_BLOCK_SIZE < kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "max_pages=%d too small for n_kv=%d", kv->max_pages, kv->n_kv);
+  if ((int64_t)n_q * s.h_kv * s.top_k >= (int64_t(1) << 27)) return fail(MSA_ERR_UNSUPPORTED, "n_q too large");
+  if (n_q == 0) return ok();
+  if (!q || !kv->k || !kv->v || !block_idx || !o) return fail(MSA_ERR_INVALID_ARG, "q/k/v/block_idx/o is NULL");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o))
+    return fail(MSA_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+  const msa::PrefillPlan pl = msa::prefill_plan(s.dtype, n_q, q_start, kv->n_kv, s.h_q, s.h_kv, s.d_h, s.top_k);
+  if ((st = check_ws(workspace, ws_bytes, pl.total)) != MSA_OK) return st;
+  msa::AttnArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.block_idx = block_idx;
+  a.o = o;
+  a.lse = lse;
+  a.n_q = n_q;
+  a.q_start = q_start;
+  a.n_kv = kv->n_kv;
+  a.batch = 1;
+  a.max_pages = kv->max_pages;
+  a.h_q = s.h_q;
+  a.h_kv = s.h_kv;
+  a.group = s.h_q / s.h_kv;
+  a.top_k = s.top_k;
+  a.sm_scale = sm_scale_of(s);
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  return hip_status(msa::launch_sparse_prefill(s.dtype, s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
+                    "msa_sparse_prefill");
+}
+
+msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* q, const msa_kv* kv,
+                             const int32_t* block_idx, void* o, float* lse, void* workspace, size_t ws_bytes,
+                             void* hip_stream) {
+  msa_status st = check_shape(shape, false, true);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!msa::decode_supported(s.dtype, s.d_h)) return fail(MSA_ERR_UNSUPPORTED, "decode is built for bf16 only");
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (!kv->page_table || !kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "decode needs a paged cache with seq_lens");
+  if (kv->max_pages < 1) return fail(MSA_ERR_INVALID_ARG, "max_pages=%d", kv->max_pages);
+  if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch=%d", batch);
+  if (batch == 0) return ok();
+  if (!q || !kv->k || !kv->v || !block_idx || !o) return fail(MSA_ERR_INVALID_ARG, "q/k/v/block_idx/o is NULL");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o))
+    return fail(MSA_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+  const msa::DecodePlan pl = msa::decode_plan(batch, s.h_q, s.h_kv, s.d_h, s.top_k);
+  if ((st = check_ws(workspace, ws_bytes, pl.total)) != MSA_OK) return st;
+  msa::AttnArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.block_idx = block_idx;
+  a.o = o;
+  a.lse = lse;
+  a.batch = batch;
+  a.max_pages = kv->max_pages;
+  a.h_q = s.h_q;
+  a.h_kv = s.h_kv;
+  a.group = s.h_q / s.h_kv;
+  a.top_k = s.top_k;
+  a.sm_scale = sm_scale_of(s);
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  return hip_status(msa::launch_sparse_decode(s.dtype, s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
+                    "msa_sparse_decode");
+}
+
+msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
+                             const msa_kv* kv, void* o, float* lse, void* workspace, size_t ws_bytes,
+                             void* hip_stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  msa_status st = check_shape(shape, false, true);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->page_table || kv->seq_lens) return fail(MSA_ERR_UNSUPPORTED, "dense prefill takes a contiguous cache");
+  if (n_q < 0 || q_start < 0 || (int64_t)q_start + n_q > kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d n_kv=%d", n_q, q_start, kv->n_kv);
+  if (n_q == 0) return ok();
+  if (!q || !kv->k || !kv->v || !o) return fail(MSA_ERR_INVALID_ARG, "q/k/v/o is NULL");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o))
+    return fail(MSA_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+  msa::AttnArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.o = o;
+  a.lse = lse;
+  a.n_q = n_q;
+  a.q_start = q_start;
+  a.n_kv = kv->n_kv;
+  a.h_q = s.h_q;
+  a.h_kv = s.h_kv;
+  a.group = s.h_q / s.h_kv;
+  a.sm_scale = sm_scale_of(s);
+  return hip_status(msa::launch_dense_prefill(s.dtype, s.d_h, a, static_cast<hipStream_t>(hip_stream)),
+                    "msa_dense_prefill");
+}
+
+}  // extern "C"

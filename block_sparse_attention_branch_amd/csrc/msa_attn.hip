@@ -1,0 +1,1040 @@
+// msa_attn.hip - main branch of MiniMax Sparse Attention on gfx950.
+//
+// Eq. (8) of the "MiniMax Sparse Attention" digest (titansim.online, §4.3):
+// every query head of KV group r attends, with exact softmax, to the causally
+// visible keys of the blocks its group selected.
+//
+// Prefill is KV-outer (digest §4.4.2): the selected (group, block) pairs are
+// the outer loop and the queries that picked a block are gathered into the
+// MFMA's N dimension, so one 128-token K/V block staged in LDS serves every
+// (token, head) row that selected it.  The schedule inverts the index lists
+// into per-(window, group, block) token lists and cuts each list into work
+// items of at most `chunk` tokens (the pages' pre-scheduled tile chunking).
+// Each item writes one normalised partial (O_b, lse_b) per (token, head); a
+// merge kernel then combines a token's partials with log-sum-exp weights (the
+// second stage).  Query tokens are processed in windows so that the partial
+// buffer of one window stays small enough to live in the last-level cache
+// between the two stages.  No atomics touch floating-point data, so results
+// are bitwise reproducible.
+//
+// Decode gathers, for each (sequence, group), the 16 selected pages of the
+// paged cache with 16x16x32 MFMA (the 16 heads of the group on one side),
+// splitting the selected keys over workgroups when the batch is small.
+//
+// The dense kernel (Eq. (1), §2.2) is the Q-outer comparison path.
+#include "msa_common.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// ----------------------------------------------------------------- LDS tile
+template <typename T, int D>
+struct KvLds {
+  static constexpr int KS = D * (int)sizeof(T) + 16;                        // bytes per key row
+  static constexpr int VS = 128 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // bytes per d row of V^T
+  static constexpr int K_BYTES = 128 * KS;
+  static constexpr int BYTES = K_BYTES + D * VS;
+};
+
+// Row j of block b of KV group r, or nullptr past the end of a contiguous cache.
+template <typename T>
+__device__ __forceinline__ const T* kv_row(const T* base, const int32_t* pt, int b, int j, int r,
+                                           int h_kv, int D, int n_kv) {
+  if (pt) return base + (((size_t)pt[b] * h_kv + r) * kBlock + j) * D;
+  const int64_t tok = (int64_t)b * kBlock + j;
+  if (tok >= n_kv) return nullptr;
+  return base + ((size_t)tok * h_kv + r) * D;
+}
+
+// Stage K_b row-major and V_b transposed (V^T[d][key]) into LDS, whole block.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_kv(char* lds, const T* k, const T* v, const int32_t* pt, int b,
+                                         int r, int h_kv, int n_kv) {
+  using L = KvLds<T, D>;
+  constexpr int CPR = D * (int)sizeof(T) / 16;
+  for (int u = threadIdx.x; u < 128 * CPR; u += NT) {
+    const int j = u / CPR, c = u % CPR;
+    const T* src = kv_row(k, pt, b, j, r, h_kv, D, n_kv);
+    const u32x4 x = src ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + c * 16)
+                        : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = x;
+  }
+  char* vt = lds + L::K_BYTES;
+  if constexpr (sizeof(T) == 2) {
+    constexpr int DC = D / 8;
+    for (int u = threadIdx.x; u < 64 * DC; u += NT) {
+      const int kp = (u & 15) + 16 * (u / (16 * DC));
+      const int dc = (u >> 4) % DC;
+      const T* s0 = kv_row(v, pt, b, 2 * kp, r, h_kv, D, n_kv);
+      const T* s1 = kv_row(v, pt, b, 2 * kp + 1, r, h_kv, D, n_kv);
+      const u32x4 x = s0 ? *reinterpret_cast<const u32x4*>(s0 + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 y = s1 ? *reinterpret_cast<const u32x4*>(s1 + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
+        const uint32_t hi = (x[t] >> 16) | (y[t] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t) * L::VS + kp * 4) = lo;
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t + 1) * L::VS + kp * 4) = hi;
+      }
+    }
+  } else {
+    constexpr int DC = D / 4;
+    for (int u = threadIdx.x; u < 128 * DC; u += NT) {
+      const int key = (u & 31) + 32 * (u / (32 * DC));
+      const int dc = (u >> 5) % DC;
+      const T* s0 = kv_row(v, pt, b, key, r, h_kv, D, n_kv);
+      const f32x4 x = s0 ? *reinterpret_cast<const f32x4*>(s0 + 4 * dc) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
+    }
+  }
+}
+
+// A fragment of V^T: row d, elements 0..3 = keys ka..ka+3, 4..7 = keys kb..kb+3.
+template <typename T>
+__device__ __forceinline__ Frag<T> vt_frag(const char* vt, int vs, int d, int ka, int kb) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(vt + d * vs + ka * 2);
+    const bf16x4 y = *reinterpret_cast<const bf16x4*>(vt + d * vs + kb * 2);
+    f = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  } else {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(vt + d * vs + ka * 4);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(vt + d * vs + kb * 4);
+    f = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> to_frag(float a0, float a1, float a2, float a3, float a4, float a5,
+                                           float a6, float a7) {
+  Frag<T> f;
+  f[0] = from_f32<T>(a0); f[1] = from_f32<T>(a1); f[2] = from_f32<T>(a2); f[3] = from_f32<T>(a3);
+  f[4] = from_f32<T>(a4); f[5] = from_f32<T>(a5); f[6] = from_f32<T>(a6); f[7] = from_f32<T>(a7);
+  return f;
+}
+
+// Store 4 consecutive values (d .. d+3) of one output row.
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+  }
+}
+
+// ------------------------------------------------------------ row tile math
+// One wave processes RT tiles of 32 (token, head) rows against the staged
+// block.  S^T = K . Q^T puts keys on the MFMA rows: lane l holds 16 keys of
+// row (l % 32) per 32-key tile, so softmax reductions are in-lane plus one
+// exchange between lanes l and l+32.
+template <typename T, int D, int RT>
+struct TileRegs {
+  Frag<T> qf[RT][D / 16];
+  f32x16 s[RT][4];
+  f32x16 o[RT][D / 32];
+  int pos[RT];
+};
+
+template <typename T, int D, int RT>
+__device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* lds, int b, bool mask) {
+  using L = KvLds<T, D>;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) t.s[rt][kt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const Frag<T> a = *reinterpret_cast<const Frag<T>*>(lds + (kt * 32 + l32) * L::KS +
+                                                          (ks * 16 + half * 8) * (int)sizeof(T));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) mma32(t.s[rt][kt], a, t.qf[rt][ks]);
+    }
+  }
+  if (mask) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key > t.pos[rt]) t.s[rt][kt][v] = -__builtin_inff();
+        }
+  }
+}
+
+// O^T += V^T . P^T with P^T taken from the (already exponentiated) scores.
+template <typename T, int D, int RT>
+__device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) {
+  using L = KvLds<T, D>;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const char* vt = lds + L::K_BYTES;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      Frag<T> pf[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const f32x16& p = t.s[rt][kt];
+        const int o = 8 * h2;
+        pf[rt] = to_frag<T>(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
+      }
+      const int base = kt * 32 + h2 * 16;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const Frag<T> a = vt_frag<T>(vt, L::VS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], a, pf[rt]);
+      }
+    }
+  }
+}
+
+// ====================================================================
+// Prefill schedule: invert block lists into per-(window, group, block)
+// token lists.  Slot j of row (i, r) is used iff its block is >= 0, causal
+// (<= diag) and larger than the previous used block of the row.
+// ====================================================================
+struct SchedArgs {
+  const int32_t* block_idx;
+  int32_t n_q, q_start, h_kv, top_k, n_blocks, window, chunk;
+  int64_t n_cells;
+  int32_t* count;     // [n_cells]
+  int32_t* fill;      // [n_cells]
+  int32_t* cell_off;  // [n_cells + 1]
+  int32_t* item_off;  // [n_cells + 1]
+  int32_t* entries;   // [n_q * h_kv * top_k]
+  int32_t* items;     // [max_items]
+  int32_t* scan;      // [4 * n_scan_tiles]
+  int32_t n_scan_tiles;
+};
+
+__device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
+  uint32_t m = 0;
+  int prev = -1;
+  for (int j = 0; j < top_k; ++j) {
+    const int b = row[j];
+    if (b > prev && b <= diag) {
+      m |= 1u << j;
+      prev = b;
+    }
+  }
+  return m;
+}
+
+__global__ void ks_zero_kernel(SchedArgs a) {
+  for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < a.n_cells; c += (int64_t)gridDim.x * 256) {
+    a.count[c] = 0;
+    a.fill[c] = 0;
+  }
+}
+
+__global__ void ks_count_kernel(SchedArgs a) {
+  const int64_t row = blockIdx.x * 256ll + threadIdx.x;  // (i, r)
+  if (row >= (int64_t)a.n_q * a.h_kv) return;
+  const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
+  const int diag = (a.q_start + i) >> 7;
+  const int32_t* br = a.block_idx + row * a.top_k;
+  const uint32_t m = used_slots(br, a.top_k, diag);
+  const int64_t cell0 = ((int64_t)(i / a.window) * a.h_kv + r) * a.n_blocks;
+  for (int j = 0; j < a.top_k; ++j)
+    if (m & (1u << j)) atomicAdd(&a.count[cell0 + br[j]], 1);
+}
+
+constexpr int kScanPerThread = 16;
+constexpr int kScanTile = 256 * kScanPerThread;
+
+__device__ __forceinline__ void block_excl_scan2(int& x, int& y, int* sh) {
+  // sh: 512 ints
+  const int t = threadIdx.x;
+  sh[t] = x;
+  sh[256 + t] = y;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int ax = t >= off ? sh[t - off] : 0;
+    const int ay = t >= off ? sh[256 + t - off] : 0;
+    __syncthreads();
+    sh[t] += ax;
+    sh[256 + t] += ay;
+    __syncthreads();
+  }
+  const int ix = sh[t], iy = sh[256 + t];
+  __syncthreads();
+  x = ix - x;
+  y = iy - y;
+}
+
+__global__ __launch_bounds__(256) void ks_scan_a_kernel(SchedArgs a) {
+  __shared__ int sh[512];
+  const int64_t c0 = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPerThread;
+  int se = 0, si = 0;
+  for (int k = 0; k < kScanPerThread; ++k) {
+    const int64_t c = c0 + k;
+    if (c < a.n_cells) {
+      const int n = a.count[c];
+      se += n;
+      si += (n + a.chunk - 1) / a.chunk;
+    }
+  }
+  int xe = se, xi = si;
+  block_excl_scan2(xe, xi, sh);
+  if (threadIdx.x == 255) {
+    a.scan[blockIdx.x] = xe + se;
+    a.scan[a.n_scan_tiles + blockIdx.x] = xi + si;
+  }
+}
+
+__global__ __launch_bounds__(256) void ks_scan_b_kernel(SchedArgs a) {
+  __shared__ int sh[512];
+  const int per = (a.n_scan_tiles + 255) / 256;
+  const int t0 = threadIdx.x * per;
+  int se = 0, si = 0;
+  for (int k = 0; k < per; ++k)
+    if (t0 + k < a.n_scan_tiles) {
+      se += a.scan[t0 + k];
+      si += a.scan[a.n_scan_tiles + t0 + k];
+    }
+  int xe = se, xi = si;
+  block_excl_scan2(xe, xi, sh);
+  for (int k = 0; k < per; ++k)
+    if (t0 + k < a.n_scan_tiles) {
+      const int ve = a.scan[t0 + k], vi = a.scan[a.n_scan_tiles + t0 + k];
+      a.scan[2 * a.n_scan_tiles + t0 + k] = xe;
+      a.scan[3 * a.n_scan_tiles + t0 + k] = xi;
+      xe += ve;
+      xi += vi;
+    }
+  if (threadIdx.x == 255) {
+    a.cell_off[a.n_cells] = xe;
+    a.item_off[a.n_cells] = xi;
+  }
+}
+
+__global__ __launch_bounds__(256) void ks_scan_c_kernel(SchedArgs a) {
+  __shared__ int sh[512];
+  const int64_t c0 = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPerThread;
+  int se = 0, si = 0;
+  for (int k = 0; k < kScanPerThread; ++k) {
+    const int64_t c = c0 + k;
+    if (c < a.n_cells) {
+      const int n = a.count[c];
+      se += n;
+      si += (n + a.chunk - 1) / a.chunk;
+    }
+  }
+  int xe = se, xi = si;
+  block_excl_scan2(xe, xi, sh);
+  xe += a.scan[2 * a.n_scan_tiles + blockIdx.x];
+  xi += a.scan[3 * a.n_scan_tiles + blockIdx.x];
+  for (int k = 0; k < kScanPerThread; ++k) {
+    const int64_t c = c0 + k;
+    if (c < a.n_cells) {
+      const int n = a.count[c];
+      a.cell_off[c] = xe;
+      a.item_off[c] = xi;
+      xe += n;
+      xi += (n + a.chunk - 1) / a.chunk;
+    }
+  }
+}
+
+__global__ void ks_scatter_kernel(SchedArgs a) {
+  const int64_t row = blockIdx.x * 256ll + threadIdx.x;
+  if (row >= (int64_t)a.n_q * a.h_kv) return;
+  const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
+  const int diag = (a.q_start + i) >> 7;
+  const int32_t* br = a.block_idx + row * a.top_k;
+  const uint32_t m = used_slots(br, a.top_k, diag);
+  const int64_t cell0 = ((int64_t)(i / a.window) * a.h_kv + r) * a.n_blocks;
+  for (int j = 0; j < a.top_k; ++j)
+    if (m & (1u << j)) {
+      const int64_t cell = cell0 + br[j];
+      const int pos = a.cell_off[cell] + atomicAdd(&a.fill[cell], 1);
+      a.entries[pos] = (i << 4) | j;
+    }
+}
+
+__global__ void ks_items_kernel(SchedArgs a) {
+  const int64_t cell = blockIdx.x * 256ll + threadIdx.x;
+  if (cell >= a.n_cells) return;
+  const int b = a.item_off[cell], e = a.item_off[cell + 1];
+  for (int it = b; it < e; ++it) a.items[it] = (int32_t)cell;
+}
+
+// ====================================================================
+// KV-outer sparse attention (one window of query tokens)
+// ====================================================================
+struct KpArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* cell_off;
+  const int32_t* item_off;
+  const int32_t* entries;
+  const int32_t* items;
+  void* part_o;       // [window, h_kv, top_k, G, D]
+  float* part_lse;    // [window, h_kv, top_k, G]
+  int32_t n_kv, q_start, h_q, h_kv, group, top_k, n_blocks, window, chunk, w;
+  float sm_scale;
+};
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256) void kp_kernel(KpArgs a) {
+  using L = KvLds<T, D>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int64_t cell_begin = (int64_t)a.w * a.h_kv * a.n_blocks;
+  const int item_begin = a.item_off[cell_begin];
+  const int item_end = a.item_off[cell_begin + (int64_t)a.h_kv * a.n_blocks];
+  const int it = item_begin + (int)blockIdx.x;
+  if (it >= item_end) return;
+  const int cell = a.items[it];
+  const int c = it - a.item_off[cell];
+  const int b = cell % a.n_blocks;
+  const int r = (cell / a.n_blocks) % a.h_kv;
+  const int e_begin = a.cell_off[cell] + c * a.chunk;
+  const int e_end = min(e_begin + a.chunk, a.cell_off[cell + 1]);
+  const int G = a.group;
+  const int nrows = (e_end - e_begin) * G;
+
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  stage_kv<T, D, 256>(lds, static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.page_table, b, r,
+                      a.h_kv, a.n_kv);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const float c2 = a.sm_scale * kLog2e;
+  T* part_o = static_cast<T*>(a.part_o);
+  for (int row0 = wave * RT * 32; row0 < nrows; row0 += 4 * RT * 32) {
+    TileRegs<T, D, RT> t;
+    int slot[RT], head[RT];
+    bool ok[RT];
+    bool need_mask = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int rho = row0 + rt * 32 + l32;
+      ok[rt] = rho < nrows;
+      const int ent = ok[rt] ? a.entries[e_begin + rho / G] : 0;
+      const int i = ent >> 4, j = ent & 15;
+      head[rt] = rho % G;
+      slot[rt] = ((i - a.w * a.window) * a.h_kv + r) * a.top_k + j;
+      t.pos[rt] = ok[rt] ? a.q_start + i : -1;
+      need_mask |= ok[rt] && (b * kBlock + kBlock - 1 > t.pos[rt]);
+      const T* qrow = q + ((size_t)i * a.h_q + r * G + head[rt]) * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] = f32x16{};
+    }
+    tile_scores<T, D, RT>(t, lds, b, __any(need_mask));
+    float mx[RT], l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m = fmaxf(m, t.s[rt][kt][v]);
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      mx[rt] = m;
+      const float mc = (m == -__builtin_inff()) ? 0.0f : m * c2;
+      float sum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(fmaf(t.s[rt][kt][v], c2, -mc));
+          t.s[rt][kt][v] = p;
+          sum += p;
+        }
+      l[rt] = sum + __shfl_xor(sum, 32, 64);
+    }
+    tile_pv<T, D, RT>(t, lds);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (!ok[rt]) continue;
+      const float inv = 1.0f / l[rt];
+      T* dst = part_o + ((size_t)slot[rt] * G + head[rt]) * D + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+          store4<T>(dst + dt * 32 + 8 * vv, t.o[rt][dt][4 * vv] * inv, t.o[rt][dt][4 * vv + 1] * inv,
+                    t.o[rt][dt][4 * vv + 2] * inv, t.o[rt][dt][4 * vv + 3] * inv);
+      if (half == 0)
+        a.part_lse[(size_t)slot[rt] * G + head[rt]] =
+            mx[rt] * a.sm_scale + __builtin_amdgcn_logf(l[rt]) * kLn2;
+    }
+  }
+}
+
+// Second stage: log-sum-exp merge of a token's per-block partials.
+struct KmArgs {
+  const int32_t* block_idx;
+  const void* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int32_t n_q, q_start, h_q, h_kv, group, top_k, window, w, pairs_per_wg;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
+  constexpr int DC = D / 8;
+  const int G = a.group;
+  const int per_pair = G * DC;
+  const int sub = threadIdx.x / per_pair;
+  const int t = threadIdx.x % per_pair;
+  if (sub >= a.pairs_per_wg) return;
+  const int64_t pair = (int64_t)blockIdx.x * a.pairs_per_wg + sub;  // (i_local, r)
+  const int il = (int)(pair / a.h_kv), r = (int)(pair % a.h_kv);
+  const int i = a.w * a.window + il;
+  if (il >= a.window || i >= a.n_q) return;
+  const int g = t / DC, dc = t % DC;
+  const int diag = (a.q_start + i) >> 7;
+  const int32_t* br = a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k;
+  const uint32_t used = used_slots(br, a.top_k, diag);
+  const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
+  float mx = -__builtin_inff();
+  for (int j = 0; j < a.top_k; ++j)
+    if (used & (1u << j)) mx = fmaxf(mx, a.part_lse[(slot0 + j) * G + g]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float wsum = 0.0f;
+  const T* po = static_cast<const T*>(a.part_o);
+  for (int j = 0; j < a.top_k; ++j) {
+    if (!(used & (1u << j))) continue;
+    const float w = fast_exp2((a.part_lse[(slot0 + j) * G + g] - mx) * kLog2e);
+    wsum += w;
+    const T* src = po + ((slot0 + j) * G + g) * D + dc * 8;
+    const Frag<T> x = load_frag<T>(src);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(x[e]), acc[e]);
+  }
+  T* out = static_cast<T*>(a.o) + ((size_t)i * a.h_q + r * G + g) * D + dc * 8;
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  store4<T>(out, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  store4<T>(out + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (a.lse && dc == 0)
+    a.lse[(size_t)i * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+}
+
+// ====================================================================
+// Dense causal GQA (Q-outer, online softmax) - the comparison kernel
+// ====================================================================
+struct KgArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t n_q, q_start, n_kv, h_q, h_kv, group, n_tiles, rows_per_tile;
+  float sm_scale;
+};
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
+  using L = KvLds<T, D>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int tile = a.n_tiles - 1 - (int)blockIdx.x;  // longest first
+  const int r = blockIdx.y;
+  const int G = a.group;
+  const int tok_per_tile = a.rows_per_tile / G;
+  const int tok0 = tile * tok_per_tile;
+  const int tok_last = min(tok0 + tok_per_tile, a.n_q) - 1;
+  const int min_diag = (a.q_start + tok0) >> 7;
+  const int max_diag = (a.q_start + tok_last) >> 7;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const float c2 = a.sm_scale * kLog2e;
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+
+  TileRegs<T, D, RT> t;
+  int tok[RT], head[RT];
+  bool ok[RT];
+  float mrun[RT], lrun[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rho = wave * RT * 32 + rt * 32 + l32;
+    tok[rt] = tok0 + rho / G;
+    head[rt] = rho % G;
+    ok[rt] = (rho < a.rows_per_tile) && tok[rt] < a.n_q;
+    t.pos[rt] = ok[rt] ? a.q_start + tok[rt] : -1;
+    const T* qrow = q + ((size_t)tok[rt] * a.h_q + r * G + head[rt]) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] = f32x16{};
+    mrun[rt] = -__builtin_inff();
+    lrun[rt] = 0.0f;
+  }
+  for (int b = 0; b <= max_diag; ++b) {
+    __syncthreads();
+    stage_kv<T, D, 256>(lds, static_cast<const T*>(a.k), static_cast<const T*>(a.v), nullptr, b, r,
+                        a.h_kv, a.n_kv);
+    __syncthreads();
+    tile_scores<T, D, RT>(t, lds, b, b >= min_diag);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m = fmaxf(m, t.s[rt][kt][v]);
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const float mnew = fmaxf(mrun[rt], m);
+      const float mref = (mnew == -__builtin_inff()) ? 0.0f : mnew * c2;
+      const float alpha = fast_exp2(fmaf(mrun[rt], c2, -mref));
+      float sum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(fmaf(t.s[rt][kt][v], c2, -mref));
+          t.s[rt][kt][v] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      lrun[rt] = lrun[rt] * alpha + sum;
+      mrun[rt] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] *= alpha;
+    }
+    tile_pv<T, D, RT>(t, lds);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (!ok[rt]) continue;
+    const float inv = 1.0f / lrun[rt];
+    T* dst = static_cast<T*>(a.o) + ((size_t)tok[rt] * a.h_q + r * G + head[rt]) * D + 4 * half;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv)
+        store4<T>(dst + dt * 32 + 8 * vv, t.o[rt][dt][4 * vv] * inv, t.o[rt][dt][4 * vv + 1] * inv,
+                  t.o[rt][dt][4 * vv + 2] * inv, t.o[rt][dt][4 * vv + 3] * inv);
+    if (a.lse && half == 0)
+      a.lse[(size_t)tok[rt] * a.h_q + r * G + head[rt]] =
+          mrun[rt] * a.sm_scale + __builtin_amdgcn_logf(lrun[rt]) * kLn2;
+  }
+}
+
+// ====================================================================
+// Sparse decode
+// ====================================================================
+struct KdArgs {
+  const void* q;             // [batch, h_q, D]
+  const void* k;             // pages [*, h_kv, 128, D]
+  const void* v;
+  const int32_t* page_table; // [batch, max_pages]
+  const int32_t* seq_lens;
+  const int32_t* block_idx;  // [batch, h_kv, top_k]
+  void* o;
+  float* lse;
+  float* part_o;             // [batch, h_kv, split, G, D] (split > 1)
+  float* part_lse;           // [batch, h_kv, split, G]
+  int32_t batch, h_q, h_kv, group, top_k, max_pages, split;
+  float sm_scale;
+};
+
+constexpr int kKdVtStride = 32 * 2 + 8;  // bytes per d row of a 32-key V^T slice (bf16)
+
+template <int D>
+__global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
+  typedef bf16_t T;
+  __shared__ __attribute__((aligned(16))) char vts[4][D * kKdVtStride];
+  __shared__ float olds[4][16][D + 1];
+  __shared__ float llds[4][16];
+  const int sp = blockIdx.x % a.split;
+  const int sr = blockIdx.x / a.split;
+  const int s = sr / a.h_kv, r = sr % a.h_kv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+  const int G = a.group;
+  const int L = a.seq_lens[s];
+  const int p = L - 1, diag = p >> 7;
+  const int32_t* br = a.block_idx + ((size_t)s * a.h_kv + r) * a.top_k;
+  const uint32_t used = used_slots(br, a.top_k, diag);
+  const float c2 = a.sm_scale * kLog2e;
+  const T* __restrict__ qp = static_cast<const T*>(a.q) + ((size_t)s * a.h_q + r * G) * D;
+  Frag<T> qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = (l16 < G) ? load_frag<T>(qp + (size_t)l16 * D + ks * 32 + q4 * 8) : zero_frag<T>();
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+  float mrun = -__builtin_inff(), lrun = 0.0f;
+  char* vt = vts[wave];
+  const int n_units = a.top_k * 4;
+  for (int u = sp * 4 + wave; u < n_units; u += a.split * 4) {
+    const int j = u >> 2, qq = u & 3;
+    if (!(used & (1u << j))) continue;
+    const int b = br[j];
+    const int page = a.page_table[(size_t)s * a.max_pages + b];
+    const size_t base = (((size_t)page * a.h_kv + r) * kBlock + qq * 32) * D;
+    const T* kb = static_cast<const T*>(a.k) + base;
+    const T* vb = static_cast<const T*>(a.v) + base;
+    Frag<T> kf[2][D / 32];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) kf[tt][ks] = load_frag<T>(kb + (tt * 16 + l16) * D + ks * 32 + q4 * 8);
+    u32x4 vx[D / 32], vy[D / 32];
+#pragma unroll
+    for (int it = 0; it < D / 32; ++it) {
+      const int dc = q4 + 4 * it;
+      vx[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16) * D + 8 * dc);
+      vy[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16 + 1) * D + 8 * dc);
+    }
+    f32x4 sc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], kf[tt][ks], qf[ks]);
+    }
+    // sc[tt][v]: key qq*32 + tt*16 + 4*q4 + v, head l16
+    const int key0 = b * kBlock + qq * 32;
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (key0 + tt * 16 + 4 * q4 + v > p) sc[tt][v] = -__builtin_inff();
+        m = fmaxf(m, sc[tt][v]);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    // transpose V into LDS: V^T[d][key], key pairs packed per dword
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < D / 32; ++it) {
+      const int dc = q4 + 4 * it;
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const uint32_t lo = (vx[it][t2] & 0xffffu) | (vy[it][t2] << 16);
+        const uint32_t hi = (vx[it][t2] >> 16) | (vy[it][t2] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2) * kKdVtStride + l16 * 4) = lo;
+        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2 + 1) * kKdVtStride + l16 * 4) = hi;
+      }
+    }
+    const float mnew = fmaxf(mrun, m);
+    const float mref = (mnew == -__builtin_inff()) ? 0.0f : mnew * c2;
+    const float alpha = fast_exp2(fmaf(mrun, c2, -mref));
+    float pv[8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[tt * 4 + v] = fast_exp2(fmaf(sc[tt][v], c2, -mref));
+        sum += pv[tt * 4 + v];
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    lrun = lrun * alpha + sum;
+    mrun = mnew;
+    const Frag<T> pf = to_frag<T>(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      o[dt] *= alpha;
+      const Frag<T> af = vt_frag<T>(vt, kKdVtStride, dt * 16 + l16, 4 * q4, 16 + 4 * q4);
+      mma16(o[dt], af, pf);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // o[dt][v]: d = dt*16 + 4*q4 + v, head l16.  Combine the 4 waves in LDS.
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) olds[wave][l16][dt * 16 + 4 * q4 + v] = o[dt][v];
+  if (q4 == 0) {
+    llds[wave][l16] = (lrun > 0.0f) ? mrun * a.sm_scale + __builtin_amdgcn_logf(lrun) * kLn2 : -__builtin_inff();
+  }
+  // store unnormalised o with its own lse: rescale below with exp(lse_w - M) / l_w
+  __shared__ float lrs[4][16];
+  if (q4 == 0) lrs[wave][l16] = lrun;
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * D; x += 256) {
+    const int g = x / D, d = x % D;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, llds[w][g]);
+    float acc = 0.0f, wsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (lrs[w][g] > 0.0f) {
+        const float ww = fast_exp2((llds[w][g] - mx) * kLog2e);
+        acc += ww * olds[w][g][d] / lrs[w][g];
+        wsum += ww;
+      }
+    }
+    const float lse_all = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+    if (a.split == 1) {
+      T* out = static_cast<T*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
+      *out = from_f32<T>(wsum > 0.0f ? acc / wsum : 0.0f);
+      if (a.lse && d == 0) a.lse[(size_t)s * a.h_q + r * G + g] = lse_all;
+    } else {
+      const size_t pidx = ((size_t)sr * a.split + sp) * G + g;
+      a.part_o[pidx * D + d] = wsum > 0.0f ? acc / wsum : 0.0f;
+      if (d == 0) a.part_lse[pidx] = lse_all;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void kd_merge_kernel(KdArgs a, int D) {
+  const int sr = blockIdx.x;
+  const int s = sr / a.h_kv, r = sr % a.h_kv;
+  const int G = a.group;
+  for (int x = threadIdx.x; x < G * D; x += 256) {
+    const int g = x / D, d = x % D;
+    float mx = -__builtin_inff();
+    for (int k = 0; k < a.split; ++k) mx = fmaxf(mx, a.part_lse[((size_t)sr * a.split + k) * G + g]);
+    float acc = 0.0f, wsum = 0.0f;
+    for (int k = 0; k < a.split; ++k) {
+      const size_t pidx = ((size_t)sr * a.split + k) * G + g;
+      const float l = a.part_lse[pidx];
+      if (l == -__builtin_inff()) continue;
+      const float ww = fast_exp2((l - mx) * kLog2e);
+      acc += ww * a.part_o[pidx * D + d];
+      wsum += ww;
+    }
+    bf16_t* out = static_cast<bf16_t*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
+    *out = from_f32<bf16_t>(wsum > 0.0f ? acc / wsum : 0.0f);
+    if (a.lse && d == 0)
+      a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+  }
+}
+
+// ====================================================================
+// Host side: plans and launches
+// ====================================================================
+static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+static int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
+                         int32_t h_kv, int32_t d_h, int32_t top_k) {
+  PrefillPlan p{};
+  const size_t esz = dtype == 0 ? 2 : 4;
+  const int G = h_q / h_kv;
+  p.n_blocks = (int32_t)(((int64_t)q_start + n_q - 1) / kBlock + 1);
+  (void)n_kv;
+  const size_t per_token = (size_t)h_kv * top_k * G * (d_h * esz + 4);
+  const size_t budget = (size_t)env_int("MSA_PARTIAL_BUDGET_MB", 128) << 20;
+  int64_t w = (int64_t)(budget / per_token);
+  w = std::max<int64_t>(64, (w / 64) * 64);
+  w = std::min<int64_t>(w, std::max<int32_t>(n_q, 1));
+  p.window = (int32_t)w;
+  p.n_windows = (int32_t)((n_q + w - 1) / w);
+  p.chunk = std::max(1, std::min(16 * 64, env_int("MSA_KP_CHUNK", 32)));
+  p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
+  const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
+  p.max_items = n_entries / p.chunk + p.n_cells + 1;
+  const int64_t n_scan_tiles = (p.n_cells + kScanTile - 1) / kScanTile;
+  size_t off = 0;
+  p.off_count = off; off = align_up(off + p.n_cells * 4);
+  p.off_fill = off; off = align_up(off + p.n_cells * 4);
+  p.off_cell_off = off; off = align_up(off + (p.n_cells + 1) * 4);
+  p.off_item_off = off; off = align_up(off + (p.n_cells + 1) * 4);
+  p.off_entries = off; off = align_up(off + n_entries * 4);
+  p.off_items = off; off = align_up(off + p.max_items * 4);
+  p.off_scan = off; off = align_up(off + 4 * n_scan_tiles * 4);
+  p.off_part_o = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * d_h * esz);
+  p.off_part_lse = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * 4);
+  p.total = off;
+  return p;
+}
+
+bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (d_h == 64 || d_h == 128); }
+bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
+bool decode_supported(int dtype, int d_h) { return dtype == 0 && (d_h == 64 || d_h == 128); }
+
+template <typename T, int D>
+static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
+  char* ws = static_cast<char*>(a.ws);
+  SchedArgs s{};
+  s.block_idx = a.block_idx;
+  s.n_q = a.n_q;
+  s.q_start = a.q_start;
+  s.h_kv = a.h_kv;
+  s.top_k = a.top_k;
+  s.n_blocks = pl.n_blocks;
+  s.window = pl.window;
+  s.chunk = pl.chunk;
+  s.n_cells = pl.n_cells;
+  s.count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+  s.fill = reinterpret_cast<int32_t*>(ws + pl.off_fill);
+  s.cell_off = reinterpret_cast<int32_t*>(ws + pl.off_cell_off);
+  s.item_off = reinterpret_cast<int32_t*>(ws + pl.off_item_off);
+  s.entries = reinterpret_cast<int32_t*>(ws + pl.off_entries);
+  s.items = reinterpret_cast<int32_t*>(ws + pl.off_items);
+  s.scan = reinterpret_cast<int32_t*>(ws + pl.off_scan);
+  s.n_scan_tiles = (int32_t)((pl.n_cells + kScanTile - 1) / kScanTile);
+  const int64_t rows = (int64_t)a.n_q * a.h_kv;
+  const unsigned row_blocks = (unsigned)((rows + 255) / 256);
+  const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
+  hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_count_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scan_a_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scan_b_kernel, dim3(1), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_items_kernel, dim3(cell_blocks), dim3(256), 0, st, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  KpArgs kp{};
+  kp.q = a.q;
+  kp.k = a.k;
+  kp.v = a.v;
+  kp.page_table = a.page_table;
+  kp.cell_off = s.cell_off;
+  kp.item_off = s.item_off;
+  kp.entries = s.entries;
+  kp.items = s.items;
+  kp.part_o = ws + pl.off_part_o;
+  kp.part_lse = reinterpret_cast<float*>(ws + pl.off_part_lse);
+  kp.n_kv = a.n_kv;
+  kp.q_start = a.q_start;
+  kp.h_q = a.h_q;
+  kp.h_kv = a.h_kv;
+  kp.group = a.group;
+  kp.top_k = a.top_k;
+  kp.n_blocks = pl.n_blocks;
+  kp.window = pl.window;
+  kp.chunk = pl.chunk;
+  kp.sm_scale = a.sm_scale;
+
+  KmArgs km{};
+  km.block_idx = a.block_idx;
+  km.part_o = kp.part_o;
+  km.part_lse = kp.part_lse;
+  km.o = a.o;
+  km.lse = a.lse;
+  km.n_q = a.n_q;
+  km.q_start = a.q_start;
+  km.h_q = a.h_q;
+  km.h_kv = a.h_kv;
+  km.group = a.group;
+  km.top_k = a.top_k;
+  km.window = pl.window;
+  km.pairs_per_wg = std::max(1, 256 / (a.group * (D / 8)));
+
+  for (int w = 0; w < pl.n_windows; ++w) {
+    const int tok = std::min<int>(pl.window, a.n_q - w * pl.window);
+    const int64_t bound = (int64_t)tok * a.h_kv * a.top_k / pl.chunk + (int64_t)a.h_kv * pl.n_blocks + 1;
+    kp.w = w;
+    hipLaunchKernelGGL((kp_kernel<T, D, 2>), dim3((unsigned)bound), dim3(256), 0, st, kp);
+    km.w = w;
+    const int64_t pairs = (int64_t)tok * a.h_kv;
+    hipLaunchKernelGGL((km_kernel<T, D>), dim3((unsigned)((pairs + km.pairs_per_wg - 1) / km.pairs_per_wg)),
+                       dim3(256), 0, st, km);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const PrefillPlan& pl,
+                                 hipStream_t st) {
+  if (dtype == 0 && d_h == 128) return sparse_prefill_typed<bf16_t, 128>(a, pl, st);
+  if (dtype == 0 && d_h == 64) return sparse_prefill_typed<bf16_t, 64>(a, pl, st);
+  if (dtype == 1 && d_h == 128) return sparse_prefill_typed<float, 128>(a, pl, st);
+  if (dtype == 1 && d_h == 64) return sparse_prefill_typed<float, 64>(a, pl, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t dense_typed(const AttnArgs& a, hipStream_t st) {
+  KgArgs g{};
+  g.q = a.q;
+  g.k = a.k;
+  g.v = a.v;
+  g.o = a.o;
+  g.lse = a.lse;
+  g.n_q = a.n_q;
+  g.q_start = a.q_start;
+  g.n_kv = a.n_kv;
+  g.h_q = a.h_q;
+  g.h_kv = a.h_kv;
+  g.group = a.group;
+  g.rows_per_tile = 256;
+  const int tok_per_tile = 256 / a.group;
+  g.n_tiles = (a.n_q + tok_per_tile - 1) / tok_per_tile;
+  g.sm_scale = a.sm_scale;
+  hipLaunchKernelGGL((kg_kernel<T, D, 2>), dim3(g.n_tiles, a.h_kv), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_prefill(int dtype, int d_h, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 0 && d_h == 128) return dense_typed<bf16_t, 128>(a, st);
+  if (dtype == 0 && d_h == 64) return dense_typed<bf16_t, 64>(a, st);
+  if (dtype == 1 && d_h == 128) return dense_typed<float, 128>(a, st);
+  if (dtype == 1 && d_h == 64) return dense_typed<float, 64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, int32_t top_k) {
+  DecodePlan p{};
+  const int pairs = batch * h_kv;
+  int split = 1;
+  // aim for >= ~1024 workgroups of 4 waves; each wave takes whole 32-key units
+  while (split < 16 && (int64_t)pairs * split < 1024 && split * 4 < top_k * 4) split <<= 1;
+  const int env = env_int("MSA_KD_SPLIT", 0);
+  if (env > 0) split = std::min(16, env);
+  p.split = split;
+  const int G = h_q / h_kv;
+  size_t off = 0;
+  p.off_part_o = off; off = align_up(off + (size_t)pairs * split * G * d_h * 4);
+  p.off_part_lse = off; off = align_up(off + (size_t)pairs * split * G * 4);
+  p.total = split > 1 ? off : 0;
+  return p;
+}
+
+template <int D>
+static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStream_t st) {
+  KdArgs k{};
+  k.q = a.q;
+  k.k = a.k;
+  k.v = a.v;
+  k.page_table = a.page_table;
+  k.seq_lens = a.seq_lens;
+  k.block_idx = a.block_idx;
+  k.o = a.o;
+  k.lse = a.lse;
+  char* ws = static_cast<char*>(a.ws);
+  k.part_o = pl.split > 1 ? reinterpret_cast<float*>(ws + pl.off_part_o) : nullptr;
+  k.part_lse = pl.split > 1 ? reinterpret_cast<float*>(ws + pl.off_part_lse) : nullptr;
+  k.batch = a.batch;
+  k.h_q = a.h_q;
+  k.h_kv = a.h_kv;
+  k.group = a.group;
+  k.top_k = a.top_k;
+  k.max_pages = a.max_pages;
+  k.split = pl.split;
+  k.sm_scale = a.sm_scale;
+  hipLaunchKernelGGL((kd_kernel<D>), dim3(a.batch * a.h_kv * pl.split), dim3(256), 0, st, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.split == 1) return e;
+  hipLaunchKernelGGL(kd_merge_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, st, k, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_decode(int dtype, int d_h, const AttnArgs& a, const DecodePlan& pl,
+                                hipStream_t st) {
+  if (dtype != 0) return hipErrorInvalidValue;
+  if (d_h == 128) return decode_typed<128>(a, pl, st);
+  if (d_h == 64) return decode_typed<64>(a, pl, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

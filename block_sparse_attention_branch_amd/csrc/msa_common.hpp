@@ -1,0 +1,159 @@
+// msa_common.hpp - device-side building blocks shared by the libmsa kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Fragment convention used everywhere: an MFMA operand fragment is 8 values
+// per lane.  For the 32x32 shapes lane l supplies row/col (l % 32) and the
+// contraction indices 8*(l/32) + e, e = 0..7; for the 16x16 shapes lane l
+// supplies row/col (l % 16) and contraction indices 8*(l/16) + e.  A bf16
+// fragment feeds one v_mfma_f32_{32x32x16,16x16x32}_bf16; an fp32 fragment
+// feeds eight v_mfma_f32_{32x32x2,16x16x4}_f32, instruction e contracting
+// element e of every lane.  Because A and B use the same per-lane index map,
+// any fixed permutation of the contraction index is harmless.
+//
+// Accumulator layouts (gfx9 MFMA):
+//   32x32: acc[v] of lane l holds C[8*(v/4) + 4*(l/32) + (v%4)][l % 32]
+//   16x16: acc[v] of lane l holds C[4*(l/16) + v][l % 16]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace msa {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 128;     // tokens per KV block / page
+constexpr int kMaxTopK = 16;    // capacity of the per-row top-k lists
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- fragments
+template <typename T> struct FragT;
+template <> struct FragT<bf16_t> { typedef bf16x8 type; };
+template <> struct FragT<float> { typedef f32x8 type; };
+template <typename T> using Frag = typename FragT<T>::type;
+
+template <typename T>
+__device__ __forceinline__ Frag<T> load_frag(const T* p) {
+  return *reinterpret_cast<const Frag<T>*>(p);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> zero_frag() {
+  Frag<T> z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = T(0.0f);
+  return z;
+}
+
+__device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+// -------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f32(bf16_t x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ top-k keys
+// A candidate block is packed into one 64-bit key whose unsigned order is the
+// selection order: pooled score descending, then block index ascending.
+// Key 0 means "empty slot" and loses to every real candidate.
+__device__ __forceinline__ uint32_t order_f32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unorder_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float score, int32_t block) {
+  return (static_cast<uint64_t>(order_f32(score)) << 32) |
+         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(block));
+}
+__device__ __forceinline__ int32_t key_block(uint64_t k) {
+  return static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(k));
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+  return unorder_f32(static_cast<uint32_t>(k >> 32));
+}
+
+// Insert v into the descending list `keys` (capacity L, unique keys).
+// The caller checks v > keys[L-1]; the last entry falls off.
+template <int L>
+__device__ __forceinline__ void list_insert(uint64_t (&keys)[L], uint64_t v) {
+  bool prev_better = true;
+  uint64_t prev = 0;
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const uint64_t cur = keys[s];
+    const bool better = cur > v;
+    keys[s] = better ? cur : (prev_better ? v : prev);
+    prev = cur;
+    prev_better = better;
+  }
+}
+
+// Write one row's final index list: the `n_take` best keys of `keys`
+// (descending, 0 = empty), plus `forced` (>= 0) if given, as ascending block
+// ids padded with -1 to top_k; the pooled score of each id goes to `score_out`
+// (nullable), forced_score for the forced block, -inf for padding.
+template <int L>
+__device__ __forceinline__ void write_row_list(const uint64_t (&keys)[L], int n_take, int forced,
+                                               float forced_score, int top_k, int32_t* idx_out,
+                                               float* score_out) {
+  int32_t id[L + 1];
+  float sc[L + 1];
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const bool ok = (s < n_take) && (keys[s] != 0ull);
+    id[s] = ok ? key_block(keys[s]) : 0x7fffffff;
+    sc[s] = ok ? key_score(keys[s]) : 0.0f;
+  }
+  id[L] = forced >= 0 ? forced : 0x7fffffff;
+  sc[L] = forced_score;
+  for (int t = 0; t < top_k; ++t) {
+    idx_out[t] = -1;
+    if (score_out) score_out[t] = -__builtin_inff();
+  }
+#pragma unroll
+  for (int s = 0; s <= L; ++s) {
+    int rank = 0;
+#pragma unroll
+    for (int t = 0; t <= L; ++t) rank += (id[t] < id[s]) ? 1 : 0;
+    if (id[s] != 0x7fffffff && rank < top_k) {
+      idx_out[rank] = id[s];
+      if (score_out) score_out[rank] = sc[s];
+    }
+  }
+}
+
+// --------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_xor_f32(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+}  // namespace msa

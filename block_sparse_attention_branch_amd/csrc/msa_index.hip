@@ -1,0 +1,397 @@
+// msa_index.hip - index branch of MiniMax Sparse Attention on gfx950.
+//
+// Computes, per query and KV group r ("MiniMax Sparse Attention" digest,
+// titansim.online, §4.2 Eq. (6) and §4.4.1; tensor shapes per the 163.com
+// commentary, "Step 1 Index Attention"):
+//   S_j = q_idx^(r) . k_idx_j * idx_scale        (keys j <= p)
+//   M_b = max_{j in block b, j <= p} S_j          (block max-pool)
+//   I   = top-k of M on the raw scores (no exp / softmax: the order is the
+//         same), ties to the lower block, diagonal block kept if forced.
+//
+// Prefill kernel: one workgroup = 256 (query, group) rows x one chunk of KV
+// blocks.  Each 128-key index block is staged once in LDS and shared by the 4
+// waves; a wave computes S^T = K_idx_block . Q_idx^T for its 64 rows with
+// v_mfma_f32_32x32x16_bf16 (keys on the MFMA rows, so the max-pool over the
+// block's 128 keys is an in-lane reduction plus one lane-half exchange), and
+// feeds the pooled score straight into a per-lane descending top-16 list kept
+// in registers.  S and M are never written to memory.  When a tile's block
+// range is split over several workgroups, each writes its sorted partial list
+// and a merge kernel combines them (the pages' two-stage merge, §4.4.2).
+//
+// Decode: a paged scan writes M for every page of each sequence (HBM-bound,
+// one query per group, 16x16x32 MFMA with the groups as rows), then one
+// workgroup per (sequence, group) selects the top-k with a threshold filter
+// and LDS bitonic sorts.
+#include "msa_common.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+constexpr int kKiThreads = 256;
+constexpr int kKiRowsPerTile = 256;
+
+// --------------------------------------------------------------- planning
+KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_diag) {
+  KiPlan p{};
+  p.n_rows = n_q * h_kv;
+  p.n_tiles = (p.n_rows + kKiRowsPerTile - 1) / kKiRowsPerTile;
+  if (p.n_tiles == 0) {
+    p.chunk_blocks = 1;
+    p.n_chunks = 1;
+    return p;
+  }
+  // blocks that need scoring in the last (longest) tile, and in total
+  auto hi_of = [&](int64_t t) -> int64_t {
+    int64_t last = std::min<int64_t>(t * kKiRowsPerTile + kKiRowsPerTile - 1, p.n_rows - 1);
+    return ((q_start + last / h_kv) >> 7) + (need_diag ? 1 : 0);
+  };
+  const int64_t hi_last = hi_of(p.n_tiles - 1);
+  const int64_t hi_first = hi_of(0);
+  const int64_t work = (hi_first + hi_last) * p.n_tiles / 2 + 1;
+  int64_t cb = std::max<int64_t>(8, (hi_last + 63) / 64);
+  cb = std::max<int64_t>(cb, (work + 4095) / 4096);
+  p.chunk_blocks = static_cast<int32_t>(cb);
+  p.n_chunks = static_cast<int32_t>(std::max<int64_t>(1, (hi_last + cb - 1) / cb));
+  return p;
+}
+
+// ----------------------------------------------------------- prefill kernel
+template <typename T, int DIDX>
+__global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a) {
+  constexpr int KS = DIDX / 16;                       // 16-wide contraction steps
+  constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
+  constexpr int LDS_STRIDE = ROW_BYTES + 16;          // padded row, bytes
+  constexpr int CHUNKS_PER_ROW = ROW_BYTES / 16;
+  constexpr int LOADS = 128 * CHUNKS_PER_ROW / kKiThreads;
+  static_assert(LOADS >= 1 && (128 * CHUNKS_PER_ROW) % kKiThreads == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) char lds[2][128 * LDS_STRIDE];
+
+  const int tile = a.n_tiles - 1 - (int)blockIdx.y;  // longest tiles first
+  const int chunk = blockIdx.x;
+  const int row0 = tile * kKiRowsPerTile;
+  const int row_last = min(row0 + kKiRowsPerTile - 1, a.n_rows - 1);
+  const int min_diag = (a.q_start + row0 / a.h_kv) >> 7;
+  const int max_diag = (a.q_start + row_last / a.h_kv) >> 7;
+  const int hi = max_diag + (a.need_diag ? 1 : 0);
+  const int nch = max(1, (hi + a.chunk_blocks - 1) / a.chunk_blocks);
+  if (chunk >= nch) return;
+  const int b_begin = chunk * a.chunk_blocks;
+  const int b_end = min(b_begin + a.chunk_blocks, hi);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
+  const T* __restrict__ k_idx = static_cast<const T*>(a.k_idx);
+
+  const int my_row = row0 + wave * 64 + lane;  // row whose list this lane owns
+  const bool my_valid = my_row < a.n_rows;
+  const int my_diag = (a.q_start + (my_valid ? my_row : row_last) / a.h_kv) >> 7;
+
+  // S^T columns of this lane: rows wave*64 + rt*32 + l32
+  int col_pos[2];
+  Frag<T> qf[2][KS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = row0 + wave * 64 + rt * 32 + l32;
+    const bool ok = r < a.n_rows;
+    col_pos[rt] = ok ? a.q_start + r / a.h_kv : -1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[rt][ks] = ok ? load_frag<T>(q_idx + (size_t)r * DIDX + ks * 16 + half * 8) : zero_frag<T>();
+  }
+
+  uint64_t keys[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
+  float diag_score = -__builtin_inff();
+
+  u32x4 pre[LOADS];
+  auto load_block = [&](int b) {
+    const int64_t base_tok = a.page_table ? (int64_t)a.page_table[b] * kBlock : (int64_t)b * kBlock;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + kKiThreads * i;
+      const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
+      const bool ok = a.page_table != nullptr || ((int64_t)b * kBlock + j < a.n_kv);
+      const char* src = reinterpret_cast<const char*>(k_idx + (base_tok + j) * DIDX) + c * 16;
+      pre[i] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + kKiThreads * i;
+      const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
+      *reinterpret_cast<u32x4*>(&lds[buf][j * LDS_STRIDE + c * 16]) = pre[i];
+    }
+  };
+
+  if (b_begin < b_end) {
+    load_block(b_begin);
+    store_block(0);
+  }
+  __syncthreads();
+  for (int b = b_begin; b < b_end; ++b) {
+    const int buf = (b - b_begin) & 1;
+    if (b + 1 < b_end) load_block(b + 1);
+    const char* K = lds[buf];
+    const bool masked = b >= min_diag;
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const Frag<T> af = *reinterpret_cast<const Frag<T>*>(
+            K + (kt * 32 + l32) * LDS_STRIDE + (ks * 16 + half * 8) * (int)sizeof(T));
+        mma32(acc0, af, qf[0][ks]);
+        mma32(acc1, af, qf[1][ks]);
+      }
+      if (masked) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key > col_pos[0]) acc0[v] = -__builtin_inff();
+          if (key > col_pos[1]) acc1[v] = -__builtin_inff();
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        m0 = fmaxf(m0, acc0[v]);
+        m1 = fmaxf(m1, acc1[v]);
+      }
+    }
+    // lanes l and l+32 hold the two key halves of rows l and 32+l: swap so
+    // that lane L ends with the whole-block max of wave row L
+    const float send = half ? m0 : m1;
+    const float recv = __shfl_xor(send, 32, 64);
+    const float pooled = fmaxf(half ? m1 : m0, recv) * a.idx_scale;
+    if (my_valid) {
+      const bool cand = a.force_local ? (b < my_diag) : (b <= my_diag);
+      if (cand) {
+        const uint64_t k = make_key(pooled, b);
+        if (k > keys[kMaxTopK - 1]) list_insert(keys, k);
+      }
+      if (b == my_diag) diag_score = pooled;
+    }
+    if (b + 1 < b_end) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!my_valid) return;
+  if (a.n_chunks == 1) {
+    const int n_take = a.top_k - (a.force_local ? 1 : 0);
+    write_row_list(keys, n_take, a.force_local ? my_diag : -1, diag_score, a.top_k,
+                   a.block_idx + (size_t)my_row * a.top_k,
+                   a.block_score ? a.block_score + (size_t)my_row * a.top_k : nullptr);
+  } else {
+    uint64_t* dst = a.part_keys + ((size_t)my_row * a.n_chunks + chunk) * kMaxTopK;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) dst[s] = keys[s];
+    if (a.need_diag && my_diag >= b_begin && my_diag < b_end) a.part_diag[my_row] = diag_score;
+  }
+}
+
+// Second stage of the split: merge the sorted partial lists of each row.
+__global__ __launch_bounds__(256) void ki_merge_kernel(KiPrefillArgs a) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= a.n_rows) return;
+  const int tile = row / kKiRowsPerTile;
+  const int row_last = min(tile * kKiRowsPerTile + kKiRowsPerTile - 1, a.n_rows - 1);
+  const int max_diag = (a.q_start + row_last / a.h_kv) >> 7;
+  const int hi = max_diag + (a.need_diag ? 1 : 0);
+  const int nch = max(1, (hi + a.chunk_blocks - 1) / a.chunk_blocks);
+  const int my_diag = (a.q_start + row / a.h_kv) >> 7;
+  uint64_t keys[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
+  const uint64_t* src = a.part_keys + (size_t)row * a.n_chunks * kMaxTopK;
+  for (int c = 0; c < nch; ++c) {
+    for (int s = 0; s < kMaxTopK; ++s) {
+      const uint64_t k = src[c * kMaxTopK + s];
+      if (k <= keys[kMaxTopK - 1]) break;  // lists are descending
+      list_insert(keys, k);
+    }
+  }
+  const float dscore = (a.need_diag && a.force_local) ? a.part_diag[row] : -__builtin_inff();
+  const int n_take = a.top_k - (a.force_local ? 1 : 0);
+  write_row_list(keys, n_take, a.force_local ? my_diag : -1, dscore, a.top_k,
+                 a.block_idx + (size_t)row * a.top_k,
+                 a.block_score ? a.block_score + (size_t)row * a.top_k : nullptr);
+}
+
+// ------------------------------------------------------------ decode kernels
+template <typename T, int DIDX>
+__global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
+  constexpr int KS = DIDX / 32;
+  const int s = blockIdx.y;
+  const int L = a.seq_lens[s];
+  const int p = L - 1;
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int hi = (a.need_diag || !a.force_local) ? nb : nb - 1;
+  const int pg_begin = blockIdx.x * a.pages_per_wg;
+  const int pg_end = min(pg_begin + a.pages_per_wg, hi);
+  if (pg_begin >= pg_end) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
+  const T* __restrict__ k_idx = static_cast<const T*>(a.k_idx);
+  Frag<T> qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ks * 32 + q4 * 8)
+                            : zero_frag<T>();
+  const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
+  for (int pg = pg_begin + wave; pg < pg_end; pg += 4) {
+    const T* kp = k_idx + (size_t)pt[pg] * kBlock * DIDX;
+    Frag<T> bfr[8][KS];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bfr[kt][ks] = load_frag<T>(kp + (kt * 16 + l16) * DIDX + ks * 32 + q4 * 8);
+    float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    const bool masked = (pg == nb - 1);
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      f32x4 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], bfr[kt][ks]);
+      const bool vis = !masked || (pg * kBlock + kt * 16 + l16 <= p);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m[v] = fmaxf(m[v], vis ? acc[v] : -__builtin_inff());
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) m[v] = fmaxf(m[v], __shfl_xor(m[v], off, 64));
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int g = 4 * q4 + v;
+        if (g < a.h_kv) a.scores[((size_t)s * a.h_kv + g) * a.max_pages + pg] = m[v] * a.idx_scale;
+      }
+    }
+  }
+}
+
+// Descending bitonic sort of n (power of two) keys in LDS by the whole block.
+__device__ void lds_bitonic_desc(uint64_t* x, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t u = x[i], w = x[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (u < w) : (u > w)) {
+            x[i] = w;
+            x[ixj] = u;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+constexpr int kSelectMaxSurvivors = 1024;  // 16 lists x up to 64 candidates per thread
+
+__global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
+  __shared__ uint64_t sh[kSelectMaxSurvivors];
+  __shared__ int count;
+  const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
+  const int L = a.seq_lens[s];
+  const int diag = (L - 1) / kBlock;
+  const int ncand = a.force_local ? diag : diag + 1;
+  const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
+  const int tid = threadIdx.x;
+
+  // 1) per-thread maxima; the 16th largest of them bounds the answer from below
+  uint64_t tmax = 0;
+  for (int b = tid; b < ncand; b += 256) {
+    const uint64_t k = make_key(sc[b], b);
+    tmax = k > tmax ? k : tmax;
+  }
+  sh[tid] = tmax;
+  if (tid == 0) count = 0;
+  __syncthreads();
+  lds_bitonic_desc(sh, 256);
+  const uint64_t thr = sh[kMaxTopK - 1];
+  __syncthreads();
+  // 2) every candidate at or above the bound survives (at most 16 threads own one)
+  for (int b = tid; b < ncand; b += 256) {
+    const uint64_t k = make_key(sc[b], b);
+    if (k >= thr) {
+      const int pos = atomicAdd(&count, 1);
+      if (pos < kSelectMaxSurvivors) sh[pos] = k;
+    }
+  }
+  __syncthreads();
+  const int n = min(count, kSelectMaxSurvivors);
+  int n2 = 16;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + tid; i < n2; i += 256) sh[i] = 0ull;
+  __syncthreads();
+  lds_bitonic_desc(sh, n2);
+  if (tid == 0) {
+    uint64_t keys[kMaxTopK];
+#pragma unroll
+    for (int t = 0; t < kMaxTopK; ++t) keys[t] = sh[t];
+    float dscore = -__builtin_inff();
+    if (a.force_local && a.need_diag) dscore = sc[diag];
+    const int n_take = a.top_k - (a.force_local ? 1 : 0);
+    const size_t row = (size_t)s * a.h_kv + r;
+    write_row_list(keys, n_take, a.force_local ? diag : -1, dscore, a.top_k,
+                   a.block_idx + row * a.top_k, a.block_score ? a.block_score + row * a.top_k : nullptr);
+  }
+}
+
+// ----------------------------------------------------------------- launch
+template <typename T, int DIDX>
+static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
+  dim3 grid(a.n_chunks, a.n_tiles);
+  hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX>), grid, dim3(kKiThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_chunks == 1) return e;
+  hipLaunchKernelGGL(ki_merge_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DIDX>
+static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
+  dim3 grid((a.max_pages + a.pages_per_wg - 1) / a.pages_per_wg, a.batch);
+  hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ki_decode_select_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+bool ki_supported(int dtype, int d_idx) {
+  return (dtype == 0 || dtype == 1) && (d_idx == 32 || d_idx == 64 || d_idx == 128);
+}
+
+#define MSA_KI_DISPATCH(FN, ...)                                         \
+  do {                                                                  \
+    if (dtype == 0) {                                                   \
+      if (d_idx == 32) return FN<bf16_t, 32>(__VA_ARGS__);              \
+      if (d_idx == 64) return FN<bf16_t, 64>(__VA_ARGS__);              \
+      if (d_idx == 128) return FN<bf16_t, 128>(__VA_ARGS__);            \
+    } else {                                                            \
+      if (d_idx == 32) return FN<float, 32>(__VA_ARGS__);               \
+      if (d_idx == 64) return FN<float, 64>(__VA_ARGS__);               \
+      if (d_idx == 128) return FN<float, 128>(__VA_ARGS__);             \
+    }                                                                   \
+    return hipErrorInvalidValue;                                        \
+  } while (0)
+
+hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipStream_t st) {
+  MSA_KI_DISPATCH(ki_prefill_typed, a, st);
+}
+hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st) {
+  MSA_KI_DISPATCH(ki_decode_typed, a, st);
+}
+
+}  // namespace msa

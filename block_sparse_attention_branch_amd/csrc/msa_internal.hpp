@@ -1,0 +1,111 @@
+// msa_internal.hpp - host-side launch interface between the C ABI layer
+// (msa_api.hip) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// ---------------------------------------------------------------- index
+// Tiles of 256 (query, group) rows; the block range [0, hi) of a tile is cut
+// into chunks of `chunk_blocks` blocks; every (tile, chunk) is one workgroup.
+struct KiPrefillArgs {
+  const void* q_idx;        // [n_q, h_kv, d_idx]
+  const void* k_idx;        // contiguous [n_kv, d_idx] or pages [*, 128, d_idx]
+  const int32_t* page_table;  // NULL or [max_pages] of the one sequence
+  int32_t n_rows;           // n_q * h_kv
+  int32_t h_kv;
+  int32_t q_start;
+  int32_t n_kv;
+  int32_t chunk_blocks;
+  int32_t n_chunks;         // chunks of the longest tile (grid.x)
+  int32_t n_tiles;
+  float idx_scale;
+  int32_t force_local;
+  int32_t top_k;
+  int32_t need_diag;        // diagonal block must be scored
+  int32_t* block_idx;       // [n_rows, top_k]
+  float* block_score;       // nullable
+  uint64_t* part_keys;      // [n_rows, n_chunks, 16] when n_chunks > 1
+  float* part_diag;         // [n_rows]
+};
+
+struct KiDecodeArgs {
+  const void* q_idx;        // [batch, h_kv, d_idx]
+  const void* k_idx;        // pages [*, 128, d_idx]
+  const int32_t* page_table;  // [batch, max_pages]
+  const int32_t* seq_lens;  // [batch]
+  int32_t batch;
+  int32_t h_kv;
+  int32_t max_pages;
+  int32_t pages_per_wg;
+  float idx_scale;
+  int32_t force_local;
+  int32_t top_k;
+  int32_t need_diag;
+  float* scores;            // workspace [batch, h_kv, max_pages]
+  int32_t* block_idx;       // [batch, h_kv, top_k]
+  float* block_score;       // nullable
+};
+
+// Host-side tiling rule of the prefill index kernel, shared with the
+// workspace-size query so both agree.
+struct KiPlan {
+  int32_t n_rows, n_tiles, chunk_blocks, n_chunks;
+};
+KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_diag);
+
+hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipStream_t st);
+hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st);
+bool ki_supported(int dtype, int d_idx);
+
+// ------------------------------------------------------- main branch
+struct AttnArgs {
+  const void* q;             // prefill [n_q, h_q, d] / decode [batch, h_q, d]
+  const void* k;             // contiguous [n_kv, h_kv, d] or pages [*, h_kv, 128, d]
+  const void* v;
+  const int32_t* page_table; // NULL = contiguous
+  const int32_t* seq_lens;   // decode only
+  const int32_t* block_idx;  // [rows, h_kv, top_k]
+  void* o;
+  float* lse;                // nullable
+  int32_t n_q, q_start, n_kv, batch, max_pages;
+  int32_t h_q, h_kv, group, top_k;
+  float sm_scale;
+  // prefill schedule / decode split workspace
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Prefill schedule geometry (windows of query tokens, KV-outer items).
+struct PrefillPlan {
+  int32_t window;           // query tokens per window
+  int32_t n_windows;
+  int32_t n_blocks;         // KV blocks addressable by the call
+  int32_t chunk;            // max tokens per KV-outer work item
+  int64_t n_cells;          // n_windows * h_kv * n_blocks
+  size_t off_count, off_fill, off_cell_off, off_item_off, off_entries, off_items,
+      off_part_o, off_part_lse, off_scan, total;
+  int64_t max_items;
+};
+PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
+                         int32_t h_kv, int32_t d_h, int32_t top_k);
+hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const PrefillPlan& pl,
+                                 hipStream_t st);
+bool attn_supported(int dtype, int d_h);
+
+struct DecodePlan {
+  int32_t split;            // workgroups per (sequence, group)
+  size_t off_part_o, off_part_lse, total;
+};
+DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, int32_t top_k);
+hipError_t launch_sparse_decode(int dtype, int d_h, const AttnArgs& a, const DecodePlan& pl,
+                                hipStream_t st);
+bool decode_supported(int dtype, int d_h);
+
+hipError_t launch_dense_prefill(int dtype, int d_h, const AttnArgs& a, hipStream_t st);
+bool dense_supported(int dtype, int d_h);
+
+}  // namespace msa

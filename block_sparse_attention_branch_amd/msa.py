@@ -1,0 +1,219 @@
+"""ctypes binding of libmsa (include/msa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch is used for device memory and the current stream.  The
+binding raises if libmsa.so has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_BF16, MSA_FP32 = 0, 1
+OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE = 0, 1, 2, 3, 4
+BLOCK = 128
+
+
+class MsaError(RuntimeError):
+    """A libmsa call returned a non-zero msa_status."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("force_local", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_idx", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("n_kv", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
+_lib = None
+
+EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
+           "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version"]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_branch_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.msa_index_topk.argtypes = [P(Shape), i32, i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
+        L.msa_sparse_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
+        L.msa_sparse_decode.argtypes = [P(Shape), i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
+        L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
+        for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill"):
+            getattr(L, f).restype = ctypes.c_int
+        L.msa_workspace_size.argtypes = [i32, P(Shape), i32, i32, i32, i32, i32]
+        L.msa_workspace_size.restype = sz
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_last_error.argtypes = []
+        L.msa_last_error.restype = ctypes.c_char_p
+        L.msa_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise MsaError(status, L.msa_status_string(status).decode(), L.msa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    if t.dtype == torch.float32:
+        return MSA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_shape(h_q, h_kv, d_h, d_idx, top_k, dtype_code, *, force_local=True,
+               sm_scale=0.0, idx_scale=0.0) -> Shape:
+    return Shape(int(h_q), int(h_kv), int(d_h), int(d_idx), BLOCK, int(top_k),
+                 1 if force_local else 0, float(sm_scale), float(idx_scale), int(dtype_code))
+
+
+def workspace_size(op: int, shape: Shape, *, batch=1, n_q=0, q_start=0, n_kv=0, max_pages=0) -> int:
+    L = lib()
+    n = L.msa_workspace_size(op, ctypes.byref(shape), batch, n_q, q_start, n_kv, max_pages)
+    err = L.msa_last_error().decode()
+    if err:
+        raise MsaError(1, "MSA_ERR_INVALID_ARG", err)
+    return int(n)
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- calls
+
+def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale=0.0,
+               page_table=None, n_kv=None, seq_lens=None, max_pages=None, h_q=None,
+               with_scores=False, out=None, workspace=None, stream=None):
+    """msa_index_topk.  Prefill mode: q_idx [n_q, h_kv, d_idx], k_idx
+    [n_kv, d_idx] (or pages [*, 128, d_idx] with ``page_table``).  Decode mode
+    (``seq_lens`` given): q_idx [batch, h_kv, d_idx], one query per sequence.
+    Returns block_idx int32 [rows, h_kv, top_k] (and fp32 scores)."""
+    decode = seq_lens is not None
+    if decode:
+        batch, h_kv, d_idx = q_idx.shape
+        n_q, qs = 1, 0
+        rows = batch
+        mp = page_table.shape[1]
+        nkv = 0
+    else:
+        n_q, h_kv, d_idx = q_idx.shape
+        batch, qs, rows = 1, int(q_start), n_q
+        nkv = int(n_kv) if n_kv is not None else (k_idx.shape[0] if page_table is None else None)
+        if nkv is None:
+            raise ValueError("n_kv is required with a paged k_idx")
+        mp = page_table.numel() if page_table is not None else 0
+    if max_pages is not None:
+        mp = int(max_pages)
+    dt = _dtype_code(q_idx)
+    shape = make_shape(h_q or h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local,
+                       idx_scale=idx_scale)
+    dev = q_idx.device
+    bidx = out if out is not None else torch.empty((rows, h_kv, top_k), dtype=torch.int32, device=dev)
+    scores = torch.empty((rows, h_kv, top_k), dtype=torch.float32, device=dev) if with_scores else None
+    if decode:
+        nws = workspace_size(OP_INDEX_DECODE, shape, batch=batch, n_q=1, max_pages=mp)
+    else:
+        nws = workspace_size(OP_INDEX, shape, n_q=n_q, q_start=qs, n_kv=nkv)
+    ws = _workspace(nws, dev, workspace)
+    kv = KV(None, None, _ptr(k_idx), _ptr(page_table), _ptr(seq_lens), nkv, mp)
+    _check(lib().msa_index_topk(ctypes.byref(shape), batch, n_q, qs, _ptr(q_idx), ctypes.byref(kv),
+                                _ptr(bidx), _ptr(scores), _ptr(ws), nws, _stream(stream)))
+    return (bidx, scores) if with_scores else bidx
+
+
+def sparse_prefill(q, k, v, block_idx, *, q_start=0, sm_scale=0.0, page_table=None, n_kv=None,
+                   with_lse=False, out=None, workspace=None, stream=None):
+    """msa_sparse_prefill.  q [n_q, h_q, d_h]; k/v [n_kv, h_kv, d_h] (or pages
+    [*, h_kv, 128, d_h] with ``page_table`` and ``n_kv``); block_idx int32
+    [n_q, h_kv, top_k].  Returns o [n_q, h_q, d_h] (and lse fp32 [n_q, h_q])."""
+    n_q, h_q, d_h = q.shape
+    h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
+    nkv = int(n_kv) if n_kv is not None else k.shape[0]
+    mp = page_table.numel() if page_table is not None else 0
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, _dtype_code(q), sm_scale=sm_scale)
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((n_q, h_q), dtype=torch.float32, device=q.device) if with_lse else None
+    nws = workspace_size(OP_PREFILL, shape, n_q=n_q, q_start=int(q_start), n_kv=nkv)
+    ws = _workspace(nws, q.device, workspace)
+    kv = KV(_ptr(k), _ptr(v), None, _ptr(page_table), None, nkv, mp)
+    _check(lib().msa_sparse_prefill(ctypes.byref(shape), n_q, int(q_start), _ptr(q), ctypes.byref(kv),
+                                    _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(stream)))
+    return (o, lse) if with_lse else o
+
+
+def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *, sm_scale=0.0,
+                  with_lse=False, out=None, workspace=None, stream=None):
+    """msa_sparse_decode.  q [batch, h_q, d_h]; pages [*, h_kv, 128, d_h];
+    page_table int32 [batch, max_pages]; seq_lens int32 [batch]; block_idx
+    int32 [batch, h_kv, top_k].  Returns o [batch, h_q, d_h] (and lse)."""
+    batch, h_q, d_h = q.shape
+    h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, _dtype_code(q), sm_scale=sm_scale)
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((batch, h_q), dtype=torch.float32, device=q.device) if with_lse else None
+    nws = workspace_size(OP_DECODE, shape, batch=batch, n_q=1)
+    ws = _workspace(nws, q.device, workspace)
+    kv = KV(_ptr(k_pages), _ptr(v_pages), None, _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1])
+    _check(lib().msa_sparse_decode(ctypes.byref(shape), batch, _ptr(q), ctypes.byref(kv), _ptr(block_idx),
+                                   _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(stream)))
+    return (o, lse) if with_lse else o
+
+
+def dense_prefill(q, k, v, *, q_start=0, sm_scale=0.0, with_lse=False, out=None, stream=None):
+    """msa_dense_prefill (Eq. (1), the dense GQA comparison kernel)."""
+    n_q, h_q, d_h = q.shape
+    h_kv = k.shape[1]
+    shape = make_shape(h_q, h_kv, d_h, 64, 16, _dtype_code(q), sm_scale=sm_scale)
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((n_q, h_q), dtype=torch.float32, device=q.device) if with_lse else None
+    kv = KV(_ptr(k), _ptr(v), None, None, None, k.shape[0], 0)
+    _check(lib().msa_dense_prefill(ctypes.byref(shape), n_q, int(q_start), _ptr(q), ctypes.byref(kv),
+                                   _ptr(o), _ptr(lse), None, 0, _stream(stream)))
+    return (o, lse) if with_lse else o

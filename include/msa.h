@@ -1,0 +1,179 @@
+/*
+ * msa.h - C ABI of libmsa, the MI355X (gfx950) hot path of MiniMax Sparse
+ * Attention (MSA): the index branch (block scoring and exp-free causal top-k)
+ * and the main branch (exact softmax attention over the selected blocks) for
+ * prefill and paged decode.
+ *
+ * Sources:
+ *   [P1] "MiniMax Sparse Attention" digest, titansim.online blog:
+ *        §2.2 Eq. (1), §3.1 (shapes), §4.2 Eq. (6), §4.3 Eq. (8),
+ *        §4.4.1 (exp-free top-k), §4.4.2 (KV-outer traversal, tile chunking
+ *        with a two-stage merge), §5.2 Eq. (12).
+ *   [P4] "MiniMax Sparse Attention: Block-Level Top-K for Affordable
+ *        Million-Token Contexts", zhichai.net, key points (block size 128,
+ *        k = 16, 128-token-aligned memory transfers).
+ *   [P5] 163.com commentary on MSA, "Step 1 Index Attention" (one index
+ *        query per GQA group, one shared index key, block max-pool).
+ *
+ * Conventions common to every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; they must
+ *     stay valid until the work queued on `hip_stream` has finished.  The
+ *     library keeps no pointer after a call returns and allocates no device
+ *     memory: scratch space comes from the caller's `workspace`, sized by
+ *     msa_workspace_size().  Workspace contents need not be initialised.
+ *   - Calls are asynchronous and stream ordered on `hip_stream` (a
+ *     hipStream_t; NULL = the null stream).  They never synchronise the host.
+ *   - Every float tensor of a call has the dtype `shape->dtype` (bf16 or
+ *     fp32); outputs `o` use it too; `lse` and `block_score` are fp32.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     an error the call returns a non-zero msa_status, launches nothing and
+ *     leaves every output untouched; msa_last_error() then describes it.
+ *     A failed launch returns MSA_ERR_HIP.  Nothing aborts or throws.
+ *   - Block b of a sequence is the token range [128 b, 128 b + 127].  The
+ *     block size is fixed at 128 ([P1] §3.1; [P4]).
+ *   - Query head h belongs to KV group r = h / (h_q / h_kv).
+ *   - Block-index lists are ascending, unique, padded with -1 to `top_k`.
+ *
+ * Layouts
+ *   contiguous cache:  k, v   [n_kv, h_kv, d_h]   k_idx [n_kv, d_idx]
+ *   paged cache:       k, v   [num_pages, h_kv, 128, d_h]  (head-major page)
+ *                      k_idx  [num_pages, 128, d_idx]
+ *                      page_table [batch, max_pages] int32: block b of
+ *                      sequence s lives in physical page page_table[s*max_pages+b]
+ *   All row-major, densely packed, 16-byte aligned base pointers.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+#define MSA_BLOCK_SIZE 128
+#define MSA_MAX_TOP_K 16
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shape    */
+  MSA_ERR_UNSUPPORTED = 2, /* valid but not built: d_h, d_idx, k, dtype ...  */
+  MSA_ERR_WORKSPACE = 3,   /* workspace too small or misaligned              */
+  MSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
+} msa_status;
+
+typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1 } msa_dtype;
+
+/* Head shapes and method hyper-parameters.
+ *   h_q, h_kv    query heads and KV heads (GQA groups); h_q % h_kv == 0 and
+ *                G = h_q / h_kv in {1, 2, 4, 8, 16}.
+ *   d_h          head dim of q/k/v: 64 or 128.
+ *   d_idx        index dim of q_idx/k_idx: 32, 64 or 128 (the pages leave it
+ *                open; [P1] §4.2 calls it low-dimensional).
+ *   block_size   must be 128.
+ *   top_k        blocks per (query, group), 1..16 ([P1] §3.1 uses 16).
+ *   force_local  1: the query's own (diagonal) block always takes one of the
+ *                k slots ([P1] §4.2); 0: plain top-k over visible blocks.
+ *   sm_scale     softmax scale of Eq. (8); 0 means 1/sqrt(d_h).
+ *   idx_scale    score scale of Eq. (6); 0 means 1/sqrt(d_idx).
+ *   dtype        msa_dtype of every float tensor of the call.            */
+typedef struct msa_shape {
+  int32_t h_q, h_kv, d_h, d_idx, block_size, top_k, force_local;
+  float sm_scale, idx_scale;
+  int32_t dtype;
+} msa_shape;
+
+/* The KV side of a call.
+ *   page_table == NULL: contiguous single-sequence cache of n_kv tokens.
+ *   page_table != NULL: paged cache; max_pages = columns of page_table.
+ *     seq_lens == NULL: one sequence (batch must be 1) of n_kv tokens.
+ *     seq_lens != NULL: device int32 [batch], tokens held per sequence,
+ *                       each in [1, 128*max_pages] (decode calls).       */
+typedef struct msa_kv {
+  const void* k;
+  const void* v;
+  const void* k_idx;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t n_kv;
+  int32_t max_pages;
+} msa_kv;
+
+/* Index branch: [P1] §4.2 Eq. (6) and §4.4.1; shapes from [P5] Step 1.
+ * For every query and KV group r:
+ *   S_j  = q_idx^(r) . k_idx_j * idx_scale           for keys j <= p
+ *   M_b  = max over visible j in block b of S_j      (block max-pool)
+ *   I    = exp-free top-k of M (ties: lower block wins), diagonal block
+ *          kept when force_local.
+ * Two modes, chosen by kv->seq_lens:
+ *   prefill (seq_lens == NULL): batch must be 1; q_idx [n_q, h_kv, d_idx];
+ *     query i sits at position q_start + i; q_start + n_q <= kv->n_kv.
+ *   decode  (seq_lens != NULL, paged): n_q must be 1, q_start is ignored;
+ *     q_idx [batch, h_kv, d_idx]; the query of sequence s sits at position
+ *     seq_lens[s] - 1 and the cache already holds it.
+ * Outputs: block_idx int32 [batch*n_q, h_kv, top_k]; block_score (nullable)
+ *   fp32, same shape: the pooled score of each listed block (-inf for -1).
+ *   Uses k_idx only; k and v may be NULL.                               */
+msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q,
+                          int32_t q_start, const void* q_idx, const msa_kv* kv,
+                          int32_t* block_idx, float* block_score,
+                          void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Main branch, prefill: [P1] §4.3 Eq. (8), run KV-outer (§4.4.2).
+ *   q [n_q, h_q, d_h]; query i at position q_start + i; one sequence
+ *   (contiguous, or paged with seq_lens == NULL); block_idx int32
+ *   [n_q, h_kv, top_k] as produced by msa_index_topk (any ascending -1
+ *   padded list of blocks b <= (q_start+i)/128 is accepted).
+ *   Each head of group r attends with exact softmax to the causally visible
+ *   keys (j <= p) of its group's listed blocks.
+ * Outputs: o [n_q, h_q, d_h] (dtype of the call, round-to-nearest-even);
+ *   lse (nullable) fp32 [n_q, h_q], natural-log sum of exp of the scaled
+ *   scores.  A query with no listed block gets o = 0, lse = -inf.        */
+msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_start,
+                              const void* q, const msa_kv* kv,
+                              const int32_t* block_idx, void* o, float* lse,
+                              void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Main branch, decode: Eq. (8) for the newest token of each sequence.
+ *   q [batch, h_q, d_h]; kv must be paged with seq_lens; block_idx int32
+ *   [batch, h_kv, top_k] (from msa_index_topk in decode mode).
+ * Outputs: o [batch, h_q, d_h]; lse (nullable) fp32 [batch, h_q].        */
+msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* q,
+                             const msa_kv* kv, const int32_t* block_idx, void* o,
+                             float* lse, void* workspace, size_t ws_bytes,
+                             void* hip_stream);
+
+/* Dense causal GQA attention, [P1] §2.2 Eq. (1): the comparison kernel.
+ *   Same arguments as msa_sparse_prefill without block_idx; contiguous cache
+ *   only.  top_k, force_local and the index fields of `shape` are ignored. */
+msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_start,
+                             const void* q, const msa_kv* kv, void* o, float* lse,
+                             void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes a call needs.  op: 0 = msa_index_topk in prefill mode,
+ * 1 = msa_sparse_prefill, 2 = msa_sparse_decode, 3 = msa_dense_prefill,
+ * 4 = msa_index_topk in decode mode.  Pass the same shape, batch, n_q,
+ * q_start and cache geometry (n_kv; max_pages for decode mode) as the
+ * call.  Returns 0 when no workspace is needed or for an invalid request
+ * (then msa_last_error() is non-empty).                                 */
+size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch,
+                          int32_t n_q, int32_t q_start, int32_t n_kv,
+                          int32_t max_pages);
+
+/* Human-readable name of a status.  Static storage.                    */
+const char* msa_status_string(msa_status status);
+
+/* Detail of the last error on the calling thread ("" if none).  Valid
+ * until the next library call on that thread.                           */
+const char* msa_last_error(void);
+
+/* MSA_ABI_VERSION of the built library.                                 */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

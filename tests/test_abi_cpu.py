@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before launching
+anything (outputs untouched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_branch_amd import msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(msa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert set(names) == set(msa.EXPORTS), names
+    L = msa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.msa_abi_version() == 1
+    for st in range(5):
+        assert L.msa_status_string(st).decode().startswith("MSA_")
+
+
+def _shape(**kw):
+    base = dict(h_q=64, h_kv=4, d_h=128, d_idx=64, top_k=16, dtype_code=0)
+    base.update(kw)
+    return msa.make_shape(base["h_q"], base["h_kv"], base["d_h"], base["d_idx"], base["top_k"],
+                          base["dtype_code"])
+
+
+FAKE = 1 << 20  # 16-byte aligned non-null "device" address, never dereferenced
+
+
+def _idx_call(shape, *, batch=1, n_q=8, q_start=0, q_idx=FAKE, k_idx=FAKE, n_kv=64, page_table=None,
+              seq_lens=None, max_pages=0, out=FAKE, ws=None, ws_bytes=0):
+    kv = msa.KV(None, None, k_idx, page_table, seq_lens, n_kv, max_pages)
+    return msa.lib().msa_index_topk(ctypes.byref(shape) if shape is not None else None, batch, n_q, q_start,
+                                    q_idx, ctypes.byref(kv), out, None, ws, ws_bytes, None)
+
+
+def _err():
+    return msa.lib().msa_last_error().decode()
+
+
+@pytest.mark.parametrize("bad,status,msg", [
+    (dict(h_kv=3), 1, "multiple"),
+    (dict(h_q=96, h_kv=2), 2, "heads per group"),
+    (dict(d_idx=48), 2, "d_idx"),
+    (dict(top_k=17), 2, "top_k"),
+    (dict(top_k=0), 2, "top_k"),
+    (dict(dtype_code=7), 1, "dtype"),
+])
+def test_index_shape_validation(bad, status, msg):
+    assert _idx_call(_shape(**bad)) == status
+    assert msg in _err()
+
+
+def test_index_argument_validation():
+    s = _shape()
+    assert _idx_call(None) == 1 and "shape" in _err()
+    assert _idx_call(s, batch=2) == 1 and "batch" in _err()
+    assert _idx_call(s, n_q=60, q_start=10, n_kv=64) == 1 and "exceeds" in _err()
+    assert _idx_call(s, k_idx=None) == 1 and "k_idx" in _err()
+    assert _idx_call(s, q_idx=FAKE + 4) == 1 and "aligned" in _err()
+    assert _idx_call(s, out=None) == 1 and "NULL" in _err()
+    # decode mode
+    assert _idx_call(s, n_q=2, seq_lens=FAKE, page_table=FAKE, max_pages=4) == 1 and "n_q == 1" in _err()
+    assert _idx_call(s, n_q=1, seq_lens=FAKE, max_pages=4) == 1 and "page_table" in _err()
+    assert _idx_call(s, n_q=1, seq_lens=FAKE, page_table=FAKE, max_pages=20000) == 2
+    # workspace: a long prefill needs one
+    need = msa.workspace_size(msa.OP_INDEX, s, n_q=20000, n_kv=20000)
+    assert need > 0
+    assert _idx_call(s, n_q=20000, n_kv=20000) == 3 and "workspace" in _err()
+    assert _idx_call(s, n_q=20000, n_kv=20000, ws=FAKE, ws_bytes=need - 1) == 3
+    assert _idx_call(s, n_q=20000, n_kv=20000, ws=FAKE + 16, ws_bytes=need) == 3 and "aligned" in _err()
+    # empty inputs are a no-op
+    assert _idx_call(s, n_q=0) == 0 and _err() == ""
+
+
+def test_prefill_decode_dense_validation():
+    L = msa.lib()
+    s = _shape()
+    kv = msa.KV(FAKE, FAKE, None, None, None, 256, 0)
+    assert L.msa_sparse_prefill(ctypes.byref(s), 300, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0, None) == 1
+    assert "exceeds" in _err()
+    assert L.msa_sparse_prefill(ctypes.byref(_shape(d_h=96)), 8, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None,
+                                None, 0, None) == 2
+    assert L.msa_sparse_prefill(ctypes.byref(s), 8, 0, FAKE, ctypes.byref(kv), None, FAKE, None, None, 0, None) == 1
+    need = msa.workspace_size(msa.OP_PREFILL, s, n_q=8, n_kv=256)
+    assert need > 0
+    assert L.msa_sparse_prefill(ctypes.byref(s), 8, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0, None) == 3
+    # decode needs paging, and is bf16-only
+    assert L.msa_sparse_decode(ctypes.byref(s), 2, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0, None) == 1
+    kvp = msa.KV(FAKE, FAKE, None, FAKE, FAKE, 0, 8)
+    assert L.msa_sparse_decode(ctypes.byref(_shape(dtype_code=1)), 2, FAKE, ctypes.byref(kvp), FAKE, FAKE, None,
+                               None, 0, None) == 2
+    assert L.msa_sparse_decode(ctypes.byref(s), 0, FAKE, ctypes.byref(kvp), FAKE, FAKE, None, None, 0, None) == 0
+    # dense takes a contiguous cache only
+    assert L.msa_dense_prefill(ctypes.byref(s), 8, 0, FAKE, ctypes.byref(kvp), FAKE, None, None, 0, None) == 2
+    assert L.msa_dense_prefill(ctypes.byref(s), 8, 250, FAKE, ctypes.byref(kv), FAKE, None, None, 0, None) == 1
+
+
+def test_workspace_size_queries():
+    s = _shape()
+    assert msa.workspace_size(msa.OP_INDEX, s, n_q=1000, n_kv=1000) >= 0
+    p = msa.workspace_size(msa.OP_PREFILL, s, n_q=32768, n_kv=32768)
+    assert p > 0
+    assert msa.workspace_size(msa.OP_INDEX_DECODE, s, batch=64, n_q=1, max_pages=1024) == 64 * 4 * 1024 * 4
+    assert msa.workspace_size(msa.OP_DENSE, s, n_q=100, n_kv=100) == 0
+    with pytest.raises(msa.MsaError):
+        msa.workspace_size(9, s)

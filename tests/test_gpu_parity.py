@@ -1,0 +1,247 @@
+"""GPU parity of the libmsa HIP path against the float64 oracle.
+
+Every call goes through the C ABI (ctypes binding).  Inputs come from the
+seeded generators in synth/; the oracle reads back the exact bits the GPU
+consumed.  Sizes span several tiles and a ragged tail while the oracle still
+finishes in seconds; the full-size cases check sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as orc
+from synth import MODEL_SHAPE, TINY_SHAPE, gen_decode_paged, gen_prefill
+from synth.inputs import HeadShape
+
+from _helpers import compare_index_rows, compare_lse, compare_out, np64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _msa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_attention_branch_amd import msa
+    msa.lib()
+    return msa
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ index branch
+
+def _index_case(shape, n_kv, n_q, dtype, seed, *, force_local=True, with_scores=False, scaled=True):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=dtype, seed=seed, device=DEV, scaled=scaled)
+    q_start = inp["q_start"]
+    _say("index_topk", shape, n_kv, n_q, dtype, seed, force_local)
+    out = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k, q_start=q_start,
+                         force_local=force_local, with_scores=with_scores)
+    torch.cuda.synchronize()
+    ids, sc = out if with_scores else (out, None)
+    o_ids, o_sc, pooled = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q_start, shape.top_k,
+                                         force_local=force_local)
+    diags = (q_start + np.arange(n_q)) // 128
+    n_exact, n_exc = compare_index_rows(ids.cpu().numpy(), o_ids, pooled, diags, force_local)
+    if sc is not None:
+        g = ids.cpu().numpy()
+        gs = sc.cpu().numpy().astype(np.float64)
+        for t in range(n_q):
+            for r in range(shape.h_kv):
+                for j in range(shape.top_k):
+                    b = g[t, r, j]
+                    if b < 0:
+                        assert gs[t, r, j] == -np.inf
+                    else:
+                        ref = pooled[t][r][b]
+                        assert abs(gs[t, r, j] - ref) <= 1e-5 * max(1.0, abs(ref)), (t, r, b, gs[t, r, j], ref)
+    return n_exact, n_exc
+
+
+def test_index_tiny_fp32():
+    n_exact, n_exc = _index_case(TINY_SHAPE, 2048, 2048, torch.float32, 0, scaled=False)
+    assert n_exc <= 2
+
+
+def test_index_model_shape_bf16_ragged_tail():
+    _index_case(MODEL_SHAPE, 2125, 2125, torch.bfloat16, 1)
+
+
+def test_index_chunked_unaligned_q_start_with_scores():
+    _index_case(MODEL_SHAPE, 3000, 700, torch.bfloat16, 2, with_scores=True)
+
+
+def test_index_no_forced_local_block():
+    _index_case(HeadShape(8, 2, 64, 64, 5), 1500, 1500, torch.bfloat16, 3, force_local=False, with_scores=True)
+
+
+def test_index_small_k_and_d_idx_128():
+    _index_case(HeadShape(16, 4, 128, 128, 3), 1100, 1100, torch.bfloat16, 4)
+    _index_case(HeadShape(16, 4, 128, 32, 1), 600, 600, torch.float32, 5)
+
+
+def test_index_short_sequences():
+    # fewer than k eligible blocks, a single block, a single query
+    _index_case(MODEL_SHAPE, 130, 130, torch.bfloat16, 6)
+    _index_case(MODEL_SHAPE, 1, 1, torch.bfloat16, 7)
+    _index_case(MODEL_SHAPE, 500, 1, torch.bfloat16, 8)
+
+
+# ------------------------------------------------------------------ main branch
+
+def _prefill_case(shape, n_kv, n_q, dtype, seed, *, use_gpu_index=False, scaled=True):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=dtype, seed=seed, device=DEV, scaled=scaled)
+    q_start = inp["q_start"]
+    _say("sparse_prefill", shape, n_kv, n_q, dtype, seed, "gpu-index" if use_gpu_index else "oracle-index")
+    if use_gpu_index:
+        bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k, q_start=q_start)
+        ids = bidx.cpu().numpy()
+    else:
+        ids, _, _ = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q_start, shape.top_k)
+        bidx = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start)
+    compare_out(o, o_ref, dtype)
+    compare_lse(lse, lse_ref, dtype)
+    return inp, bidx, o
+
+
+def test_prefill_tiny_fp32():
+    _prefill_case(TINY_SHAPE, 2048, 2048, torch.float32, 0, scaled=False)
+
+
+def test_prefill_model_shape_bf16_ragged():
+    _prefill_case(MODEL_SHAPE, 2125, 2125, torch.bfloat16, 1)
+
+
+def test_prefill_chunked_q_start_fp32():
+    _prefill_case(HeadShape(16, 2, 128, 64, 6), 2600, 900, torch.float32, 9)
+
+
+def test_prefill_end_to_end_with_gpu_indices():
+    _prefill_case(MODEL_SHAPE, 1800, 1800, torch.bfloat16, 10, use_gpu_index=True)
+
+
+def test_prefill_d64_group4_bf16():
+    _prefill_case(HeadShape(8, 2, 64, 32, 4), 1300, 1300, torch.bfloat16, 11)
+
+
+def test_prefill_full_coverage_equals_dense():
+    msa = _msa()
+    shape = HeadShape(16, 2, 128, 64, 16)
+    n = 1900                                   # 15 blocks <= k: every block selected
+    inp = gen_prefill(n, shape, dtype=torch.bfloat16, seed=12, device=DEV)
+    _say("full coverage", n)
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o_s = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx)
+    o_d, lse_d = msa.dense_prefill(inp["q"], inp["k"], inp["v"], with_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.dense_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), 0)
+    compare_out(o_s, o_ref, torch.bfloat16, "sparse")
+    compare_out(o_d, o_ref, torch.bfloat16, "dense")
+    compare_lse(lse_d, lse_ref, torch.bfloat16)
+
+
+def test_dense_fp32_chunked():
+    msa = _msa()
+    shape = HeadShape(8, 2, 64, 32, 4)
+    inp = gen_prefill(1000, shape, n_q=333, dtype=torch.float32, seed=13, device=DEV)
+    _say("dense fp32 chunked")
+    o, lse = msa.dense_prefill(inp["q"], inp["k"], inp["v"], q_start=inp["q_start"], with_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.dense_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), inp["q_start"])
+    compare_out(o, o_ref, torch.float32)
+    compare_lse(lse, lse_ref, torch.float32)
+
+
+def test_prefill_deterministic_and_chunked_equals_one_shot():
+    msa = _msa()
+    shape = MODEL_SHAPE
+    n = 1500
+    inp = gen_prefill(n, shape, dtype=torch.bfloat16, seed=14, device=DEV)
+    _say("determinism + chunked == one-shot")
+    b1 = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o1 = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], b1)
+    b2 = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o2 = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], b2)
+    torch.cuda.synchronize()
+    assert torch.equal(b1, b2) and torch.equal(o1, o2)
+    cut = 650
+    parts_b, parts_o = [], []
+    for lo, hi in ((0, cut), (cut, n)):
+        kv = {k: inp[k][:hi].contiguous() for k in ("k", "v", "k_idx")}
+        bb = msa.index_topk(inp["q_idx"][lo:hi].contiguous(), kv["k_idx"], top_k=16, q_start=lo)
+        oo = msa.sparse_prefill(inp["q"][lo:hi].contiguous(), kv["k"], kv["v"], bb, q_start=lo)
+        parts_b.append(bb)
+        parts_o.append(oo)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts_b), b1)
+    assert torch.equal(torch.cat(parts_o), o1)
+
+
+# ------------------------------------------------------------------ decode
+
+def _decode_case(shape, seq_lens, seed, n_sets=1):
+    msa = _msa()
+    batch = len(seq_lens)
+    inp = gen_decode_paged(batch, max(seq_lens), shape, seed=seed, device=DEV, seq_lens=seq_lens)
+    _say("decode", shape, seq_lens, seed)
+    q_idx = inp["q_idx"][0].contiguous()
+    q = inp["q"][0].contiguous()
+    bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=shape.top_k, page_table=inp["page_table"],
+                          seq_lens=inp["seq_lens"])
+    o, lse = msa.sparse_decode(q, inp["k_pages"], inp["v_pages"], inp["page_table"], inp["seq_lens"], bidx,
+                               with_lse=True)
+    torch.cuda.synchronize()
+    pt = inp["page_table"].cpu().numpy()
+    kp = inp["k_pages"].cpu()
+    vp = inp["v_pages"].cpu()
+    ip = inp["k_idx_pages"].cpu()
+    o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), ip.double().numpy(), pt, seq_lens, shape.top_k)
+    diags = (np.asarray(seq_lens) - 1) // 128
+    compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, diags)
+    o_ref, lse_ref = orc.sparse_decode(np64(q), kp.double().numpy(), vp.double().numpy(), pt, seq_lens,
+                                       bidx.cpu().numpy())
+    compare_out(o, o_ref, torch.bfloat16)
+    compare_lse(lse, lse_ref, torch.bfloat16)
+
+
+def test_decode_mixed_lengths():
+    _decode_case(MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049], 20)
+
+
+def test_decode_batch_many_short():
+    _decode_case(HeadShape(32, 4, 128, 64, 16), [700 + 37 * i for i in range(40)], 21)
+
+
+def test_decode_single_long_sequence():
+    _decode_case(MODEL_SHAPE, [40000], 22)
+
+
+# ------------------------------------------------------------------ full size (sampled)
+
+def test_full_size_prefill_32k_sampled_rows():
+    msa = _msa()
+    shape = MODEL_SHAPE
+    n = 32768
+    inp = gen_prefill(n, shape, dtype=torch.bfloat16, seed=1, device=DEV)
+    _say("32K prefill full size")
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.sort(np.concatenate([rng.choice(n, 40, replace=False), [0, 127, 128, n - 129, n - 1]]))
+    o_ids, _, pooled = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), 0, 16, rows=rows)
+    g_ids = bidx.cpu().numpy()[rows]
+    compare_index_rows(g_ids, o_ids, pooled, rows // 128)
+    k64, v64 = np64(inp["k"]), np64(inp["v"])
+    q_rows = np64(inp["q"][torch.from_numpy(rows).to(DEV)])
+    o_ref = np.stack([orc.sparse_attention(q_rows[t:t + 1], k64, v64, g_ids[t:t + 1], int(i))[0][0]
+                      for t, i in enumerate(rows)])
+    compare_out(o[torch.from_numpy(rows).to(DEV)], o_ref, torch.bfloat16)
