@@ -1,0 +1,415 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one pass of every hot-path row over one batch of synthetic input:
+  prefill  (1 sequence, N = 32768, 64 query / 4 KV heads, d_h 128, d_idx 64,
+            B_k 128, k 16, bf16 N(0,1)/sqrt(d)):  msa_index_topk + msa_sparse_prefill
+  decode   (64 sequences x 131072-token paged cache, same heads, bf16 N(0,1),
+            4 rotating query sets):                msa_index_topk + msa_sparse_decode
+``value`` is prefill tokens/s of the step's prefill part; the decode part is
+reported as ``decode_us_per_step``.  Each ABI call is timed with HIP events on
+the stream it is launched on; ``roofline`` covers the dominant call
+(msa_sparse_prefill, bound by MFMA) and ``rooflines`` every call.  The dense
+GQA kernel is timed at the prefill shape for comparison, outside the step.
+The float64 oracle is timed on a bounded sample on the host (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload step|prefill128k|long1m]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synth import MODEL_SHAPE, gen_decode_paged, gen_long_context, gen_planted_prefill, gen_prefill  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+BLOCK = 128
+
+
+# ----------------------------------------------------------- work accounting
+
+def prefill_counts(n_q, q_start, shape=MODEL_SHAPE):
+    """Algorithmic work of one prefill call, exact causal counts.
+
+    index: 2 * d_idx FLOPs per (query, group, key) score over the strictly
+      past blocks (the diagonal block is kept without scoring);
+    main: 4 * d_h FLOPs per (query head, visible selected key): k-1 full past
+      blocks (fewer early on) plus the visible part of the diagonal block."""
+    p = q_start + np.arange(n_q, dtype=np.int64)
+    diag = p // BLOCK
+    past_keys = (BLOCK * diag).sum()
+    idx_flops = 2.0 * shape.d_idx * shape.h_kv * float(past_keys)
+    visible = BLOCK * np.minimum(shape.top_k - 1, diag) + (p % BLOCK) + 1
+    main_flops = 4.0 * shape.h_q * shape.d_h * float(visible.sum())
+    dense_flops = 4.0 * shape.h_q * shape.d_h * float((p + 1).sum())
+    return idx_flops, main_flops, dense_flops
+
+
+def decode_bytes(seq_lens, shape=MODEL_SHAPE, esz=2):
+    """Algorithmic HBM bytes of one decode step: the index keys of every past
+    page (index scan) and the visible keys/values of the k selected pages."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    diag = (L - 1) // BLOCK
+    idx_bytes = float((BLOCK * diag * shape.d_idx * esz).sum())
+    vis = BLOCK * np.minimum(shape.top_k - 1, diag) + (L - 1) % BLOCK + 1
+    main_bytes = float((vis * shape.h_kv * shape.d_h * esz * 2).sum())
+    main_bytes += float(len(L) * shape.h_q * shape.d_h * esz * 2)  # q in, o out
+    dense_bytes = float((L * shape.h_kv * shape.d_h * esz * 2).sum())
+    return idx_bytes, main_bytes, dense_bytes
+
+
+# ----------------------------------------------------------------- timing
+
+class CallTimer:
+    """HIP events around ABI calls on the current (launch) stream."""
+
+    def __init__(self, names):
+        self.names = names
+        self.records = {n: [] for n in names}
+
+    def step(self, fns):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        evs[0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            evs[i + 1].record()
+        return evs
+
+    def collect(self, ev_lists):
+        torch.cuda.synchronize()
+        for evs in ev_lists:
+            for i, n in enumerate(self.names):
+                self.records[n].append(evs[i].elapsed_time(evs[i + 1]))
+
+    def mean_ms(self, n):
+        return float(np.mean(self.records[n]))
+
+    def pct(self, n, q):
+        return float(np.percentile(self.records[n], q))
+
+
+def roofline(bound, work, ms, unit):
+    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    if unit == "TFLOP/s":
+        achieved = work / (ms * 1e-3) / 1e12
+    else:
+        achieved = work / (ms * 1e-3) / 1e9
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None}
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline_prefill(inp, shape, budget_s=12.0, seed=0):
+    """Time the float64 oracle on sampled query rows of the prefill input."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import msa_oracle as orc
+    q_idx = inp["q_idx"].double().cpu().numpy()
+    k_idx = inp["k_idx"].double().cpu().numpy()
+    k = inp["k"].double().cpu().numpy()
+    v = inp["v"].double().cpu().numpy()
+    q = inp["q"]
+    n = q.shape[0]
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(n)
+    t0 = time.perf_counter()
+    done = 0
+    for i in order:
+        i = int(i)
+        ids, _, _ = orc.index_topk(q_idx[i:i + 1], k_idx, i, shape.top_k)
+        orc.sparse_attention(q[i:i + 1].double().cpu().numpy(), k, v, ids, i)
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 8:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} random query rows of the 32768-token prefill (index top-k + sparse attention, "
+                      f"all 4 groups / 64 heads), {dt:.1f} s; BLAS threads {threads}, one Python thread"}
+
+
+def cpu_baseline_decode(dec, shape, n_seqs=2):
+    from oracle import msa_oracle as orc
+    t_total = 0.0
+    pt = dec["page_table"]
+    for s in range(n_seqs):
+        L = int(dec["seq_lens"][s])
+        nb = -(-L // BLOCK)
+        pages = pt[s, :nb].long()
+        kp = dec["k_pages"][pages].double().cpu().numpy()
+        vp = dec["v_pages"][pages].double().cpu().numpy()
+        ip = dec["k_idx_pages"][pages].double().cpu().numpy()
+        local_pt = np.arange(nb)[None, :]
+        qi = dec["q_idx"][0, s:s + 1].double().cpu().numpy()
+        q = dec["q"][0, s:s + 1].double().cpu().numpy()
+        t0 = time.perf_counter()
+        ids, _, _ = orc.index_topk_decode(qi, ip, local_pt, [L], shape.top_k)
+        orc.sparse_decode(q, kp, vp, local_pt, [L], ids)
+        t_total += time.perf_counter() - t0
+    per_seq = t_total / n_seqs
+    return {"us_per_step_extrapolated": round(per_seq * dec["q"].shape[1] * 1e6, 1),
+            "sample": f"{n_seqs} of {dec['q'].shape[1]} sequences, {t_total:.1f} s, extrapolated per sequence"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the path shards by KV group / decode batch, see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from block_sparse_attention_branch_amd import msa
+    msa.lib()
+    if args.workload == "step":
+        bench_step(msa, args)
+    elif args.workload == "prefill128k":
+        bench_prefill_only(msa, args, planted=True)
+    else:
+        bench_long(msa, args)
+
+
+def bench_step(msa, args):
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    n = 32768
+    t_gen = time.perf_counter()
+    pre = gen_prefill(n, shape, dtype=torch.bfloat16, seed=1, device=dev)
+    dec = gen_decode_paged(64, 131072, shape, seed=3, device=dev, n_query_sets=4)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    # outputs and workspaces allocated once, outside the timed region
+    bidx = torch.empty((n, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o = torch.empty_like(pre["q"])
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+    ws_idx = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX, s_idx, n_q=n, n_kv=n)), dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL, s_idx, n_q=n, n_kv=n)), dtype=torch.uint8, device=dev)
+    B = 64
+    mp = dec["page_table"].shape[1]
+    dbidx = [torch.empty((B, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev) for _ in range(4)]
+    do = torch.empty((B, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
+    ws_di = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX_DECODE, s_idx, batch=B, n_q=1, max_pages=mp)),
+                        dtype=torch.uint8, device=dev)
+    ws_dd = torch.empty(max(1, msa.workspace_size(msa.OP_DECODE, s_idx, batch=B, n_q=1)), dtype=torch.uint8, device=dev)
+    qsets = [dec["q"][i].contiguous() for i in range(4)]
+    qisets = [dec["q_idx"][i].contiguous() for i in range(4)]
+
+    def calls(step):
+        j = step % 4
+        return [
+            lambda: msa.index_topk(pre["q_idx"], pre["k_idx"], top_k=16, out=bidx, workspace=ws_idx),
+            lambda: msa.sparse_prefill(pre["q"], pre["k"], pre["v"], bidx, out=o, workspace=ws_pre),
+            lambda: msa.index_topk(qisets[j], dec["k_idx_pages"], top_k=16, page_table=dec["page_table"],
+                                   seq_lens=dec["seq_lens"], out=dbidx[j], workspace=ws_di),
+            lambda: msa.sparse_decode(qsets[j], dec["k_pages"], dec["v_pages"], dec["page_table"],
+                                      dec["seq_lens"], dbidx[j], out=do, workspace=ws_dd),
+        ]
+
+    names = ["index_prefill", "sparse_prefill", "index_decode", "sparse_decode"]
+    timer = CallTimer(names)
+    for w in range(args.warmup):
+        for fn in calls(w):
+            fn()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs.append(timer.step(calls(s)))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect(evs)
+    print(f"[bench] {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    ms_step = wall * 1e3 / args.steps
+    t_ip, t_sp = timer.mean_ms("index_prefill"), timer.mean_ms("sparse_prefill")
+    t_id, t_sd = timer.mean_ms("index_decode"), timer.mean_ms("sparse_decode")
+    prefill_ms = t_ip + t_sp
+    idx_fl, main_fl, dense_fl = prefill_counts(n, 0, shape)
+    didx_b, dmain_b, ddense_b = decode_bytes([131072] * B, shape)
+    rl = {
+        "index_prefill": dict(roofline("mfma", idx_fl, t_ip, "TFLOP/s"), kernel="ki_prefill_kernel+ki_merge_kernel"),
+        "sparse_prefill": dict(roofline("mfma", main_fl, t_sp, "TFLOP/s"),
+                               kernel="ks_* schedule + kp_kernel + km_kernel (per window)"),
+        "index_decode": dict(roofline("hbm", didx_b, t_id, "GB/s"), kernel="ki_decode_scan_kernel+ki_decode_select_kernel"),
+        "sparse_decode": dict(roofline("hbm", dmain_b, t_sd, "GB/s"), kernel="kd_kernel+kd_merge_kernel"),
+    }
+    for k_, ms_ in (("index_prefill", t_ip), ("sparse_prefill", t_sp), ("index_decode", t_id), ("sparse_decode", t_sd)):
+        rl[k_]["ms"] = round(ms_, 4)
+        rl[k_]["p10_ms"] = round(timer.pct(k_, 10), 4)
+        rl[k_]["p90_ms"] = round(timer.pct(k_, 90), 4)
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(pre["q"])
+        msa.dense_prefill(pre["q"], pre["k"], pre["v"], out=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 3
+        for _ in range(reps):
+            msa.dense_prefill(pre["q"], pre["k"], pre["v"], out=od)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / reps
+        dense = {"ms": round(dms, 3), "tflops": round(dense_fl / (dms * 1e-3) / 1e12, 1),
+                 "speedup_msa_prefill_vs_dense": round(dms / prefill_ms, 2),
+                 "kernel": "kg_kernel (Q-outer, Eq. (1))"}
+        del od
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_prefill(pre, shape)
+        cpu["decode"] = cpu_baseline_decode(dec, shape)
+
+    line = {
+        "metric": "MSA prefill tok/s + decode us/step; % MFMA / HBM roofline",
+        "value": round(n / (prefill_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic, seeded (N(0,1)/sqrt(d) prefill, N(0,1) decode); no weights",
+        "config": {"workload": "prefill 1x32768 + decode step 64x131072 paged; 64 q / 4 kv heads, d_h 128, "
+                               "d_idx 64, B_k 128, k 16, causal, diagonal block kept",
+                   "global_batch": 1, "seq_len": n, "decode_batch": B, "decode_ctx": 131072,
+                   "parallelism": "single GPU"},
+        "prefill_ms": round(prefill_ms, 4),
+        "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
+        "roofline": dict(rl["sparse_prefill"], name="msa_sparse_prefill"),
+        "rooflines": rl,
+        "dense_gqa": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def bench_prefill_only(msa, args, planted=True):
+    """Planted 131072-token prefill (index + sparse prefill)."""
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    n = 131072
+    inp = gen_planted_prefill(n, shape, device=dev) if planted else gen_prefill(n, shape, device=dev)
+    bidx = torch.empty((n, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o = torch.empty_like(inp["q"])
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+    ws_idx = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX, s_idx, n_q=n, n_kv=n)), dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL, s_idx, n_q=n, n_kv=n)), dtype=torch.uint8, device=dev)
+    fns = [lambda: msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16, out=bidx, workspace=ws_idx),
+           lambda: msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, out=o, workspace=ws_pre)]
+    timer = CallTimer(["index_prefill", "sparse_prefill"])
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    evs = [timer.step(fns) for _ in range(args.steps)]
+    timer.collect(evs)
+    t_ip, t_sp = timer.mean_ms("index_prefill"), timer.mean_ms("sparse_prefill")
+    idx_fl, main_fl, _ = prefill_counts(n, 0, shape)
+    got = bidx.cpu()
+    des = inp["designated"]
+    hit = all(set(inp["planted_blocks"][r].tolist()) <= set(got[int(i), r].tolist())
+              for i in des[:256] for r in range(shape.h_kv))
+    print(json.dumps({"workload": "prefill 1x131072 planted", "index_ms": round(t_ip, 3),
+                      "sparse_ms": round(t_sp, 3), "tokens_per_s": round(n / ((t_ip + t_sp) * 1e-3), 1),
+                      "index_roofline": roofline("mfma", idx_fl, t_ip, "TFLOP/s"),
+                      "sparse_roofline": roofline("mfma", main_fl, t_sp, "TFLOP/s"),
+                      "planted_blocks_retrieved": bool(hit)}))
+
+
+def bench_long(msa, args):
+    """1M-token paged cache: chunked prefill of the last 8192 queries, then
+    256 decode steps (each appends its token first), batch 1."""
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    lc = gen_long_context(device=dev)
+    n_ctx, q_start = lc["n_ctx"], lc["q_start"]
+    nq = lc["chunk_q"].shape[0]
+    pt = lc["page_table"]
+    bidx = torch.empty((nq, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o = torch.empty_like(lc["chunk_q"])
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+    ws_idx = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX, s_idx, n_q=nq, q_start=q_start, n_kv=n_ctx)),
+                         dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL, s_idx, n_q=nq, q_start=q_start, n_kv=n_ctx)),
+                         dtype=torch.uint8, device=dev)
+    fns = [lambda: msa.index_topk(lc["chunk_q_idx"], lc["k_idx_pages"], top_k=16, q_start=q_start,
+                                  page_table=pt[0], n_kv=n_ctx, out=bidx, workspace=ws_idx),
+           lambda: msa.sparse_prefill(lc["chunk_q"], lc["k_pages"], lc["v_pages"], bidx, q_start=q_start,
+                                      page_table=pt[0], n_kv=n_ctx, out=o, workspace=ws_pre)]
+    timer = CallTimer(["index_prefill", "sparse_prefill"])
+    for _ in range(max(1, args.warmup // 2)):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    evs = [timer.step(fns) for _ in range(max(3, args.steps // 2))]
+    timer.collect(evs)
+    t_ip, t_sp = timer.mean_ms("index_prefill"), timer.mean_ms("sparse_prefill")
+    idx_fl, main_fl, _ = prefill_counts(nq, q_start, shape)
+    # decode steps
+    seq_lens = torch.tensor([n_ctx], dtype=torch.int32, device=dev)
+    dbidx = torch.empty((1, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    do = torch.empty((1, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
+    mp = pt.shape[1]
+    ws_di = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX_DECODE, s_idx, batch=1, n_q=1, max_pages=mp)),
+                        dtype=torch.uint8, device=dev)
+    ws_dd = torch.empty(max(1, msa.workspace_size(msa.OP_DECODE, s_idx, batch=1, n_q=1)), dtype=torch.uint8, device=dev)
+    n_dec = lc["step_q"].shape[0]
+    step_ms = []
+    for t in range(n_dec):
+        pos = n_ctx + t
+        page = pt[0, pos // BLOCK].long()
+        row = pos % BLOCK
+        lc["k_pages"][page, :, row] = lc["step_k"][t]
+        lc["v_pages"][page, :, row] = lc["step_v"][t]
+        lc["k_idx_pages"][page, row] = lc["step_k_idx"][t]
+        seq_lens.fill_(pos + 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        msa.index_topk(lc["step_q_idx"][t], lc["k_idx_pages"], top_k=16, page_table=pt, seq_lens=seq_lens,
+                       out=dbidx, workspace=ws_di)
+        msa.sparse_decode(lc["step_q"][t], lc["k_pages"], lc["v_pages"], pt, seq_lens, dbidx, out=do,
+                          workspace=ws_dd)
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms.append(e0.elapsed_time(e1))
+    step_us = np.array(step_ms[8:]) * 1e3
+    print(json.dumps({"workload": "1M context: chunked prefill 8192 @ q_start 1040384 + 256 decode steps",
+                      "chunk_index_ms": round(t_ip, 3), "chunk_sparse_ms": round(t_sp, 3),
+                      "chunk_tokens_per_s": round(nq / ((t_ip + t_sp) * 1e-3), 1),
+                      "chunk_index_roofline": roofline("mfma", idx_fl, t_ip, "TFLOP/s"),
+                      "chunk_sparse_roofline": roofline("mfma", main_fl, t_sp, "TFLOP/s"),
+                      "decode_us_p50": round(float(np.percentile(step_us, 50)), 1),
+                      "decode_us_p99": round(float(np.percentile(step_us, 99)), 1)}))
+
+
+if __name__ == "__main__":
+    main()

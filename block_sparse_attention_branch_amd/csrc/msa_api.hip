@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/msa.h"
+#include "msa.h"
 #include "msa_internal.hpp"
 
 namespace {

@@ -36,39 +36,98 @@ struct KvLds {
   static constexpr int BYTES = K_BYTES + D * VS;
 };
 
-// Row j of block b of KV group r, or nullptr past the end of a contiguous cache.
-template <typename T>
-__device__ __forceinline__ const T* kv_row(const T* base, const int32_t* pt, int b, int j, int r,
-                                           int h_kv, int D, int n_kv) {
-  if (pt) return base + (((size_t)pt[b] * h_kv + r) * kBlock + j) * D;
-  const int64_t tok = (int64_t)b * kBlock + j;
-  if (tok >= n_kv) return nullptr;
-  return base + ((size_t)tok * h_kv + r) * D;
+// Two-phase staging for double buffering: global -> registers (issued before
+// the current block's math) and registers -> LDS (after it).  NT threads.
+template <typename T, int D, int NT>
+struct StageRegs {
+  static constexpr int CPR = D * (int)sizeof(T) / 16;
+  static constexpr int KL = 128 * CPR / NT;                                  // K chunks per thread
+  static constexpr int VU = (sizeof(T) == 2 ? 64 * (D / 8) : 128 * (D / 4)) / NT;  // V units per thread
+  static constexpr int VW = sizeof(T) == 2 ? 2 : 1;                          // loads per V unit
+  static_assert(KL >= 1 && VU >= 1, "staging split");
+  u32x4 k[KL];
+  u32x4 v[VU][VW];
+};
+
+// Base addresses of block b of KV group r: row j of K is k + j * stride.
+struct BlockPtr {
+  const char* k;
+  const char* v;
+  int stride;  // bytes between consecutive key rows
+  int valid;   // rows that exist (a contiguous cache may end inside the block)
+};
+
+template <typename T, int D>
+__device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, const int32_t* pt, int b, int r,
+                                              int h_kv, int n_kv) {
+  BlockPtr p;
+  size_t off;
+  if (pt) {
+    off = (((size_t)pt[b] * h_kv + r) * kBlock) * D * sizeof(T);
+    p.stride = D * (int)sizeof(T);
+    p.valid = kBlock;
+  } else {
+    off = (((size_t)b * kBlock) * h_kv + r) * D * sizeof(T);
+    p.stride = h_kv * D * (int)sizeof(T);
+    p.valid = min(kBlock, n_kv - b * kBlock);
+  }
+  p.k = static_cast<const char*>(k) + off;
+  p.v = static_cast<const char*>(v) + off;
+  return p;
 }
 
-// Stage K_b row-major and V_b transposed (V^T[d][key]) into LDS, whole block.
 template <typename T, int D, int NT>
-__device__ __forceinline__ void stage_kv(char* lds, const T* k, const T* v, const int32_t* pt, int b,
-                                         int r, int h_kv, int n_kv) {
+__device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPtr& p) {
+  using S = StageRegs<T, D, NT>;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < S::KL; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int j = u / S::CPR, c = u % S::CPR;
+    g.k[i] = j < p.valid ? *reinterpret_cast<const u32x4*>(p.k + (size_t)j * p.stride + c * 16) : z;
+  }
+  if constexpr (sizeof(T) == 2) {
+    constexpr int DC = D / 8;
+#pragma unroll
+    for (int i = 0; i < S::VU; ++i) {
+      const int u = threadIdx.x + NT * i;
+      const int kp = (u & 15) + 16 * (u / (16 * DC));
+      const int dc = (u >> 4) % DC;
+      const char* r0 = p.v + (size_t)(2 * kp) * p.stride + dc * 16;
+      g.v[i][0] = 2 * kp < p.valid ? *reinterpret_cast<const u32x4*>(r0) : z;
+      g.v[i][1] = 2 * kp + 1 < p.valid ? *reinterpret_cast<const u32x4*>(r0 + p.stride) : z;
+    }
+  } else {
+    constexpr int DC = D / 4;
+#pragma unroll
+    for (int i = 0; i < S::VU; ++i) {
+      const int u = threadIdx.x + NT * i;
+      const int key = (u & 31) + 32 * (u / (32 * DC));
+      const int dc = (u >> 5) % DC;
+      g.v[i][0] = key < p.valid ? *reinterpret_cast<const u32x4*>(p.v + (size_t)key * p.stride + dc * 16) : z;
+    }
+  }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* lds) {
+  using S = StageRegs<T, D, NT>;
   using L = KvLds<T, D>;
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  for (int u = threadIdx.x; u < 128 * CPR; u += NT) {
-    const int j = u / CPR, c = u % CPR;
-    const T* src = kv_row(k, pt, b, j, r, h_kv, D, n_kv);
-    const u32x4 x = src ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + c * 16)
-                        : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = x;
+#pragma unroll
+  for (int i = 0; i < S::KL; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int j = u / S::CPR, c = u % S::CPR;
+    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = g.k[i];
   }
   char* vt = lds + L::K_BYTES;
   if constexpr (sizeof(T) == 2) {
     constexpr int DC = D / 8;
-    for (int u = threadIdx.x; u < 64 * DC; u += NT) {
+#pragma unroll
+    for (int i = 0; i < S::VU; ++i) {
+      const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      const T* s0 = kv_row(v, pt, b, 2 * kp, r, h_kv, D, n_kv);
-      const T* s1 = kv_row(v, pt, b, 2 * kp + 1, r, h_kv, D, n_kv);
-      const u32x4 x = s0 ? *reinterpret_cast<const u32x4*>(s0 + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 y = s1 ? *reinterpret_cast<const u32x4*>(s1 + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x = g.v[i][0], y = g.v[i][1];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
@@ -79,13 +138,14 @@ __device__ __forceinline__ void stage_kv(char* lds, const T* k, const T* v, cons
     }
   } else {
     constexpr int DC = D / 4;
-    for (int u = threadIdx.x; u < 128 * DC; u += NT) {
+#pragma unroll
+    for (int i = 0; i < S::VU; ++i) {
+      const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
-      const T* s0 = kv_row(v, pt, b, key, r, h_kv, D, n_kv);
-      const f32x4 x = s0 ? *reinterpret_cast<const f32x4*>(s0 + 4 * dc) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = g.v[i][0][e];
     }
   }
 }
@@ -125,6 +185,14 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
   }
 }
 
+// Keeps the scheduler from hoisting every unrolled LDS fragment load to the
+// top of a loop nest (which costs registers and forces spills).
+#ifndef MSA_NO_SCHED_FENCE
+#define MSA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define MSA_SCHED_FENCE() do {} while (0)
+#endif
+
 // ------------------------------------------------------------ row tile math
 // One wave processes RT tiles of 32 (token, head) rows against the staged
 // block.  S^T = K . Q^T puts keys on the MFMA rows: lane l holds 16 keys of
@@ -134,6 +202,7 @@ template <typename T, int D, int RT>
 struct TileRegs {
   Frag<T> qf[RT][D / 16];
   f32x16 s[RT][4];
+  Frag<T> pf[RT][4][2];   // P^T fragments (keys kt*32 + 16*h2 + ...)
   f32x16 o[RT][D / 32];
   int pos[RT];
 };
@@ -153,6 +222,7 @@ __device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* l
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) mma32(t.s[rt][kt], a, t.qf[rt][ks]);
     }
+    MSA_SCHED_FENCE();
   }
   if (mask) {
 #pragma unroll
@@ -167,7 +237,20 @@ __device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* l
   }
 }
 
-// O^T += V^T . P^T with P^T taken from the (already exponentiated) scores.
+// Pack the exponentiated scores of row tile rt into P^T fragments.
+template <typename T, int D, int RT>
+__device__ __forceinline__ void tile_pack_p(TileRegs<T, D, RT>& t, int rt) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const f32x16& p = t.s[rt][kt];
+      const int o = 8 * h2;
+      t.pf[rt][kt][h2] = to_frag<T>(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
+    }
+}
+
+// O^T += V^T . P^T.
 template <typename T, int D, int RT>
 __device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) {
   using L = KvLds<T, D>;
@@ -177,20 +260,14 @@ __device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) 
   for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      Frag<T> pf[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const f32x16& p = t.s[rt][kt];
-        const int o = 8 * h2;
-        pf[rt] = to_frag<T>(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
-      }
       const int base = kt * 32 + h2 * 16;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const Frag<T> a = vt_frag<T>(vt, L::VS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], a, pf[rt]);
+        for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], a, t.pf[rt][kt][h2]);
       }
+      MSA_SCHED_FENCE();
     }
   }
 }
@@ -213,6 +290,23 @@ struct SchedArgs {
   int32_t* scan;      // [4 * n_scan_tiles]
   int32_t n_scan_tiles;
 };
+
+// Cells are the (window, group, block) token lists.  Within a window they are
+// numbered XCD-major: cell (r, b) belongs to XCD (r * nbp + b) % 8, and the
+// KV-outer workgroups running on that XCD take exactly its cells, so a KV
+// block stays in one L2 across windows.  nbp = blocks rounded up to 8.
+__device__ __forceinline__ int64_t cell_key(int w, int r, int b, int nbp, int h_kv) {
+  const int n_l = h_kv * nbp, per = n_l >> 3;
+  const int cl = r * nbp + b;
+  return (int64_t)w * n_l + (cl & 7) * per + (cl >> 3);
+}
+__device__ __forceinline__ void cell_rb(int64_t k, int nbp, int h_kv, int& r, int& b) {
+  const int n_l = h_kv * nbp, per = n_l >> 3;
+  const int kl = (int)(k % n_l);
+  const int cl = (kl % per) * 8 + kl / per;
+  r = cl / nbp;
+  b = cl % nbp;
+}
 
 __device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
   uint32_t m = 0;
@@ -241,9 +335,9 @@ __global__ void ks_count_kernel(SchedArgs a) {
   const int diag = (a.q_start + i) >> 7;
   const int32_t* br = a.block_idx + row * a.top_k;
   const uint32_t m = used_slots(br, a.top_k, diag);
-  const int64_t cell0 = ((int64_t)(i / a.window) * a.h_kv + r) * a.n_blocks;
+  const int w = i / a.window;
   for (int j = 0; j < a.top_k; ++j)
-    if (m & (1u << j)) atomicAdd(&a.count[cell0 + br[j]], 1);
+    if (m & (1u << j)) atomicAdd(&a.count[cell_key(w, r, br[j], a.n_blocks, a.h_kv)], 1);
 }
 
 constexpr int kScanPerThread = 16;
@@ -350,10 +444,10 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
   const int diag = (a.q_start + i) >> 7;
   const int32_t* br = a.block_idx + row * a.top_k;
   const uint32_t m = used_slots(br, a.top_k, diag);
-  const int64_t cell0 = ((int64_t)(i / a.window) * a.h_kv + r) * a.n_blocks;
+  const int w = i / a.window;
   for (int j = 0; j < a.top_k; ++j)
     if (m & (1u << j)) {
-      const int64_t cell = cell0 + br[j];
+      const int64_t cell = cell_key(w, r, br[j], a.n_blocks, a.h_kv);
       const int pos = a.cell_off[cell] + atomicAdd(&a.fill[cell], 1);
       a.entries[pos] = (i << 4) | j;
     }
@@ -378,71 +472,106 @@ struct KpArgs {
   const int32_t* item_off;
   const int32_t* entries;
   const int32_t* items;
-  void* part_o;       // [window, h_kv, top_k, G, D]
-  float* part_lse;    // [window, h_kv, top_k, G]
-  int32_t n_kv, q_start, h_q, h_kv, group, top_k, n_blocks, window, chunk, w;
+  void* part_o;       // [window, h_kv, top_k, G, D]  un-normalised sum_j p_j v_j
+  float2* part_ml;    // [window, h_kv, top_k, G]     (row max * sm_scale, sum_j p_j)
+  int32_t n_kv, q_start, h_q, h_kv, group, g_shift, top_k, n_blocks, window, chunk, w;
   float sm_scale;
 };
 
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void kp_kernel(KpArgs a) {
-  using L = KvLds<T, D>;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
-  const int64_t cell_begin = (int64_t)a.w * a.h_kv * a.n_blocks;
-  const int item_begin = a.item_off[cell_begin];
-  const int item_end = a.item_off[cell_begin + (int64_t)a.h_kv * a.n_blocks];
-  const int it = item_begin + (int)blockIdx.x;
-  if (it >= item_end) return;
+
+// One KV-outer work item: (group r, block b) and a run of the tokens that
+// selected b.  The K/V block is staged once in LDS and shared by all rows.
+struct KpItem {
+  int b, r, e_begin, e_end;
+};
+
+__device__ __forceinline__ KpItem kp_item(const KpArgs& a, int it) {
+  KpItem m;
   const int cell = a.items[it];
   const int c = it - a.item_off[cell];
-  const int b = cell % a.n_blocks;
-  const int r = (cell / a.n_blocks) % a.h_kv;
-  const int e_begin = a.cell_off[cell] + c * a.chunk;
-  const int e_end = min(e_begin + a.chunk, a.cell_off[cell + 1]);
-  const int G = a.group;
-  const int nrows = (e_end - e_begin) * G;
+  cell_rb(cell, a.n_blocks, a.h_kv, m.r, m.b);
+  m.e_begin = a.cell_off[cell] + c * a.chunk;
+  m.e_end = min(m.e_begin + a.chunk, a.cell_off[cell + 1]);
+  return m;
+}
 
+// Query rows of one pass (RT tiles of 32 (token, head) rows) of one item.
+template <typename T, int D, int RT>
+struct KpPass {
+  Frag<T> qf[RT][D / 16];
+  int pos[RT], slot[RT], head[RT];
+  bool ok[RT];
+  bool ready;
+};
+
+template <typename T, int D, int RT>
+__device__ __forceinline__ void kp_load_pass(KpPass<T, D, RT>& ps, const KpArgs& a, const KpItem& m, int row0) {
   const T* __restrict__ q = static_cast<const T*>(a.q);
-  stage_kv<T, D, 256>(lds, static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.page_table, b, r,
-                      a.h_kv, a.n_kv);
-  __syncthreads();
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int G = a.group;
+  const int nrows = (m.e_end - m.e_begin) * G;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rho = row0 + rt * 32 + l32;
+    ps.ok[rt] = rho < nrows;
+    const int ent = ps.ok[rt] ? a.entries[m.e_begin + (rho >> a.g_shift)] : 0;
+    const int i = ent >> 4, j = ent & 15;
+    ps.head[rt] = rho & (G - 1);
+    ps.slot[rt] = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
+    ps.pos[rt] = ps.ok[rt] ? a.q_start + i : -1;
+    const T* qrow = q + ((size_t)i * a.h_q + m.r * G + ps.head[rt]) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ps.qf[rt][ks] = ps.ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
+  }
+  ps.ready = true;
+}
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+// All passes of one item for this wave.  The next pass's queries (of this
+// item, or the first pass of `nxt`) are loaded into the query registers as
+// soon as the scores no longer need them, so their latency overlaps P.V.
+template <typename T, int D, int RT, int NT>
+__device__ __forceinline__ void kp_compute(const KpArgs& a, const KpItem& m, bool has_nxt, const KpItem nxt,
+                                           const char* lds, KpPass<T, D, RT>& ps) {
+  constexpr int ROWS_PER_PASS = (NT / 64) * RT * 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const float c2 = a.sm_scale * kLog2e;
+  const int G = a.group;
+  const int nrows = (m.e_end - m.e_begin) * G;
   T* part_o = static_cast<T*>(a.part_o);
-  for (int row0 = wave * RT * 32; row0 < nrows; row0 += 4 * RT * 32) {
+  for (int row0 = wave * RT * 32; row0 < nrows; row0 += ROWS_PER_PASS) {
+    if (!ps.ready) kp_load_pass<T, D, RT>(ps, a, m, row0);
     TileRegs<T, D, RT> t;
     int slot[RT], head[RT];
     bool ok[RT];
     bool need_mask = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int rho = row0 + rt * 32 + l32;
-      ok[rt] = rho < nrows;
-      const int ent = ok[rt] ? a.entries[e_begin + rho / G] : 0;
-      const int i = ent >> 4, j = ent & 15;
-      head[rt] = rho % G;
-      slot[rt] = ((i - a.w * a.window) * a.h_kv + r) * a.top_k + j;
-      t.pos[rt] = ok[rt] ? a.q_start + i : -1;
-      need_mask |= ok[rt] && (b * kBlock + kBlock - 1 > t.pos[rt]);
-      const T* qrow = q + ((size_t)i * a.h_q + r * G + head[rt]) * D + half * 8;
+      slot[rt] = ps.slot[rt];
+      head[rt] = ps.head[rt];
+      ok[rt] = ps.ok[rt];
+      t.pos[rt] = ps.pos[rt];
+      need_mask |= ok[rt] && (m.b * kBlock + kBlock - 1 > t.pos[rt]);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] = f32x16{};
+      for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ps.qf[rt][ks];
     }
-    tile_scores<T, D, RT>(t, lds, b, __any(need_mask));
+    tile_scores<T, D, RT>(t, lds, m.b, __any(need_mask));
+    ps.ready = false;
+    if (row0 + ROWS_PER_PASS < nrows) {
+      kp_load_pass<T, D, RT>(ps, a, m, row0 + ROWS_PER_PASS);
+    } else if (has_nxt && wave * RT * 32 < (nxt.e_end - nxt.e_begin) * G) {
+      kp_load_pass<T, D, RT>(ps, a, nxt, wave * RT * 32);
+    }
     float mx[RT], l[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float m = -__builtin_inff();
+      float mm = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) m = fmaxf(m, t.s[rt][kt][v]);
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      mx[rt] = m;
-      const float mc = (m == -__builtin_inff()) ? 0.0f : m * c2;
+        for (int v = 0; v < 16; ++v) mm = fmaxf(mm, t.s[rt][kt][v]);
+      mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+      mx[rt] = mm;
+      const float mc = (mm == -__builtin_inff()) ? 0.0f : mm * c2;
       float sum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -453,23 +582,67 @@ __global__ __launch_bounds__(256) void kp_kernel(KpArgs a) {
           sum += p;
         }
       l[rt] = sum + __shfl_xor(sum, 32, 64);
+      tile_pack_p<T, D, RT>(t, rt);
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] = f32x16{};
     tile_pv<T, D, RT>(t, lds);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (!ok[rt]) continue;
-      const float inv = 1.0f / l[rt];
       T* dst = part_o + ((size_t)slot[rt] * G + head[rt]) * D + 4 * half;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv)
-          store4<T>(dst + dt * 32 + 8 * vv, t.o[rt][dt][4 * vv] * inv, t.o[rt][dt][4 * vv + 1] * inv,
-                    t.o[rt][dt][4 * vv + 2] * inv, t.o[rt][dt][4 * vv + 3] * inv);
-      if (half == 0)
-        a.part_lse[(size_t)slot[rt] * G + head[rt]] =
-            mx[rt] * a.sm_scale + __builtin_amdgcn_logf(l[rt]) * kLn2;
+          store4<T>(dst + dt * 32 + 8 * vv, t.o[rt][dt][4 * vv], t.o[rt][dt][4 * vv + 1],
+                    t.o[rt][dt][4 * vv + 2], t.o[rt][dt][4 * vv + 3]);
+      if (half == 0) a.part_ml[(size_t)slot[rt] * G + head[rt]] = float2{mx[rt] * a.sm_scale, l[rt]};
     }
+  }
+}
+
+// Persistent over this XCD's items of the window: the grid is a multiple of 8
+// and workgroup g (dispatched to XCD g % 8) takes the XCD's items sub, sub +
+// nsub, ...; the next item's K/V is prefetched into registers while computing.
+template <typename T, int D, int RT, int NT>
+__global__ __launch_bounds__(NT) void kp_kernel(KpArgs a) {
+  using L = KvLds<T, D>;
+  constexpr int NB = (2 * L::BYTES <= 160 * 1024) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char lds[NB][L::BYTES];
+  const int x = blockIdx.x & 7, sub = blockIdx.x >> 3, nsub = gridDim.x >> 3;
+  const int64_t n_l = (int64_t)a.h_kv * a.n_blocks, per = n_l >> 3;
+  const int64_t k0 = (int64_t)a.w * n_l + x * per;
+  const int item_begin = a.item_off[k0];
+  const int item_end = a.item_off[k0 + per];
+  int it = item_begin + sub;
+  if (it >= item_end) return;
+  StageRegs<T, D, NT> pre;
+  KpItem cur = kp_item(a, it);
+  stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv));
+  stage_store<T, D, NT>(pre, lds[0]);
+  __syncthreads();
+  KpPass<T, D, RT> ps;
+  ps.ready = false;
+  int buf = 0;
+  for (;;) {
+    const int nx = it + nsub;
+    const bool has_next = nx < item_end;
+    KpItem nxt = cur;
+    if (has_next) {
+      nxt = kp_item(a, nx);
+      stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv));
+    }
+    kp_compute<T, D, RT, NT>(a, cur, has_next, nxt, lds[buf], ps);
+    if (!has_next) break;
+    if (NB == 1) __syncthreads();
+    stage_store<T, D, NT>(pre, lds[NB == 2 ? (buf ^ 1) : 0]);
+    __syncthreads();
+    it = nx;
+    cur = nxt;
+    if (NB == 2) buf ^= 1;
   }
 }
 
@@ -477,7 +650,7 @@ __global__ __launch_bounds__(256) void kp_kernel(KpArgs a) {
 struct KmArgs {
   const int32_t* block_idx;
   const void* part_o;
-  const float* part_lse;
+  const float2* part_ml;
   void* o;
   float* lse;
   int32_t n_q, q_start, h_q, h_kv, group, top_k, window, w, pairs_per_wg;
@@ -500,27 +673,34 @@ __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
   const int32_t* br = a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k;
   const uint32_t used = used_slots(br, a.top_k, diag);
   const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
-  float mx = -__builtin_inff();
-  for (int j = 0; j < a.top_k; ++j)
-    if (used & (1u << j)) mx = fmaxf(mx, a.part_lse[(slot0 + j) * G + g]);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.0f;
   const T* po = static_cast<const T*>(a.part_o);
-  for (int j = 0; j < a.top_k; ++j) {
-    if (!(used & (1u << j))) continue;
-    const float w = fast_exp2((a.part_lse[(slot0 + j) * G + g] - mx) * kLog2e);
-    wsum += w;
-    const T* src = po + ((slot0 + j) * G + g) * D + dc * 8;
-    const Frag<T> x = load_frag<T>(src);
+  float2 ml[kMaxTopK];
+  Frag<T> x[kMaxTopK];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(x[e]), acc[e]);
+  for (int j = 0; j < kMaxTopK; ++j) {
+    const bool u = (used >> j) & 1u;
+    ml[j] = u ? a.part_ml[(slot0 + j) * G + g] : float2{-__builtin_inff(), 0.0f};
+    x[j] = u ? load_frag<T>(po + ((slot0 + j) * G + g) * D + dc * 8) : zero_frag<T>();
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) mx = fmaxf(mx, ml[j].x);
+  const float mref = mx == -__builtin_inff() ? 0.0f : mx;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float den = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    const float w = fast_exp2((ml[j].x - mref) * kLog2e);
+    den = fmaf(w, ml[j].y, den);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(x[j][e]), acc[e]);
   }
   T* out = static_cast<T*>(a.o) + ((size_t)i * a.h_q + r * G + g) * D + dc * 8;
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   store4<T>(out, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   store4<T>(out + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if (a.lse && dc == 0)
-    a.lse[(size_t)i * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+    a.lse[(size_t)i * a.h_q + r * G + g] = den > 0.0f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
 }
 
 // ====================================================================
@@ -536,10 +716,11 @@ struct KgArgs {
   float sm_scale;
 };
 
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
+template <typename T, int D, int RT, int NT>
+__global__ __launch_bounds__(NT) void kg_kernel(KgArgs a) {
   using L = KvLds<T, D>;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  constexpr int NB = (2 * L::BYTES <= 160 * 1024) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char lds[NB][L::BYTES];
   const int tile = a.n_tiles - 1 - (int)blockIdx.x;  // longest first
   const int r = blockIdx.y;
   const int G = a.group;
@@ -551,7 +732,6 @@ __global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   const float c2 = a.sm_scale * kLog2e;
   const T* __restrict__ q = static_cast<const T*>(a.q);
-
   TileRegs<T, D, RT> t;
   int tok[RT], head[RT];
   bool ok[RT];
@@ -563,7 +743,7 @@ __global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
     head[rt] = rho % G;
     ok[rt] = (rho < a.rows_per_tile) && tok[rt] < a.n_q;
     t.pos[rt] = ok[rt] ? a.q_start + tok[rt] : -1;
-    const T* qrow = q + ((size_t)tok[rt] * a.h_q + r * G + head[rt]) * D + half * 8;
+    const T* qrow = q + ((size_t)(ok[rt] ? tok[rt] : 0) * a.h_q + r * G + head[rt]) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
 #pragma unroll
@@ -571,19 +751,22 @@ __global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
     mrun[rt] = -__builtin_inff();
     lrun[rt] = 0.0f;
   }
+  StageRegs<T, D, NT> pre;
+  stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, nullptr, 0, r, a.h_kv, a.n_kv));
+  stage_store<T, D, NT>(pre, lds[0]);
+  __syncthreads();
+  int buf = 0;
   for (int b = 0; b <= max_diag; ++b) {
-    __syncthreads();
-    stage_kv<T, D, 256>(lds, static_cast<const T*>(a.k), static_cast<const T*>(a.v), nullptr, b, r,
-                        a.h_kv, a.n_kv);
-    __syncthreads();
-    tile_scores<T, D, RT>(t, lds, b, b >= min_diag);
+    const bool has_next = b < max_diag;
+    if (has_next) stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, nullptr, b + 1, r, a.h_kv, a.n_kv));
+    tile_scores<T, D, RT>(t, lds[buf], b, b >= min_diag);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float m = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) m = fmaxf(m, t.s[rt][kt][v]);
+        for (int vv = 0; vv < 16; ++vv) m = fmaxf(m, t.s[rt][kt][vv]);
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       const float mnew = fmaxf(mrun[rt], m);
       const float mref = (mnew == -__builtin_inff()) ? 0.0f : mnew * c2;
@@ -592,9 +775,9 @@ __global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(t.s[rt][kt][v], c2, -mref));
-          t.s[rt][kt][v] = p;
+        for (int vv = 0; vv < 16; ++vv) {
+          const float p = fast_exp2(fmaf(t.s[rt][kt][vv], c2, -mref));
+          t.s[rt][kt][vv] = p;
           sum += p;
         }
       sum += __shfl_xor(sum, 32, 64);
@@ -602,8 +785,15 @@ __global__ __launch_bounds__(256) void kg_kernel(KgArgs a) {
       mrun[rt] = mnew;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] *= alpha;
+      tile_pack_p<T, D, RT>(t, rt);
     }
-    tile_pv<T, D, RT>(t, lds);
+    tile_pv<T, D, RT>(t, lds[buf]);
+    if (has_next) {
+      if (NB == 1) __syncthreads();
+      stage_store<T, D, NT>(pre, lds[NB == 2 ? (buf ^ 1) : 0]);
+      __syncthreads();
+      if (NB == 2) buf ^= 1;
+    }
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -823,14 +1013,40 @@ static int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
+#ifndef KP_RT
+#define KP_RT 1
+#endif
+#ifndef KP_NT
+#define KP_NT 512
+#endif
+
+// Compute units of the current device (cached per device).
+static int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <typename T, int D>
+static int kp_wgs_per_cu() {
+  const int e = env_int("MSA_KP_WG_PER_CU", 0);
+  return e > 0 ? e : 1;
+}
+
 PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
                          int32_t h_kv, int32_t d_h, int32_t top_k) {
   PrefillPlan p{};
   const size_t esz = dtype == 0 ? 2 : 4;
   const int G = h_q / h_kv;
-  p.n_blocks = (int32_t)(((int64_t)q_start + n_q - 1) / kBlock + 1);
+  p.n_blocks = (int32_t)((((int64_t)q_start + n_q - 1) / kBlock + 1 + 7) & ~int64_t(7));
   (void)n_kv;
-  const size_t per_token = (size_t)h_kv * top_k * G * (d_h * esz + 4);
+  const size_t per_token = (size_t)h_kv * top_k * G * (d_h * esz + 8);
   const size_t budget = (size_t)env_int("MSA_PARTIAL_BUDGET_MB", 128) << 20;
   int64_t w = (int64_t)(budget / per_token);
   w = std::max<int64_t>(64, (w / 64) * 64);
@@ -851,7 +1067,7 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   p.off_items = off; off = align_up(off + p.max_items * 4);
   p.off_scan = off; off = align_up(off + 4 * n_scan_tiles * 4);
   p.off_part_o = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * d_h * esz);
-  p.off_part_lse = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * 4);
+  p.off_part_lse = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * 8);
   p.total = off;
   return p;
 }
@@ -904,12 +1120,13 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   kp.entries = s.entries;
   kp.items = s.items;
   kp.part_o = ws + pl.off_part_o;
-  kp.part_lse = reinterpret_cast<float*>(ws + pl.off_part_lse);
+  kp.part_ml = reinterpret_cast<float2*>(ws + pl.off_part_lse);
   kp.n_kv = a.n_kv;
   kp.q_start = a.q_start;
   kp.h_q = a.h_q;
   kp.h_kv = a.h_kv;
   kp.group = a.group;
+  kp.g_shift = __builtin_ctz((unsigned)a.group);
   kp.top_k = a.top_k;
   kp.n_blocks = pl.n_blocks;
   kp.window = pl.window;
@@ -919,7 +1136,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   KmArgs km{};
   km.block_idx = a.block_idx;
   km.part_o = kp.part_o;
-  km.part_lse = kp.part_lse;
+  km.part_ml = kp.part_ml;
   km.o = a.o;
   km.lse = a.lse;
   km.n_q = a.n_q;
@@ -931,11 +1148,14 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   km.window = pl.window;
   km.pairs_per_wg = std::max(1, 256 / (a.group * (D / 8)));
 
+  const int n_cu = num_cus();
   for (int w = 0; w < pl.n_windows; ++w) {
     const int tok = std::min<int>(pl.window, a.n_q - w * pl.window);
     const int64_t bound = (int64_t)tok * a.h_kv * a.top_k / pl.chunk + (int64_t)a.h_kv * pl.n_blocks + 1;
     kp.w = w;
-    hipLaunchKernelGGL((kp_kernel<T, D, 2>), dim3((unsigned)bound), dim3(256), 0, st, kp);
+    int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kp_wgs_per_cu<T, D>());
+    const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
+    hipLaunchKernelGGL((kp_kernel<T, D, KP_RT, KP_NT>), dim3(grid), dim3(KP_NT), 0, st, kp);
     km.w = w;
     const int64_t pairs = (int64_t)tok * a.h_kv;
     hipLaunchKernelGGL((km_kernel<T, D>), dim3((unsigned)((pairs + km.pairs_per_wg - 1) / km.pairs_per_wg)),
@@ -967,11 +1187,12 @@ static hipError_t dense_typed(const AttnArgs& a, hipStream_t st) {
   g.h_q = a.h_q;
   g.h_kv = a.h_kv;
   g.group = a.group;
-  g.rows_per_tile = 256;
-  const int tok_per_tile = 256 / a.group;
+  constexpr int RT = 1, NT = 512;
+  g.rows_per_tile = (NT / 64) * RT * 32;
+  const int tok_per_tile = g.rows_per_tile / a.group;
   g.n_tiles = (a.n_q + tok_per_tile - 1) / tok_per_tile;
   g.sm_scale = a.sm_scale;
-  hipLaunchKernelGGL((kg_kernel<T, D, 2>), dim3(g.n_tiles, a.h_kv), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((kg_kernel<T, D, RT, NT>), dim3(g.n_tiles, a.h_kv), dim3(NT), 0, st, g);
   return hipGetLastError();
 }
 
