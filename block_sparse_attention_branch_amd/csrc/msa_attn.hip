@@ -47,7 +47,16 @@ struct StageRegs {
   static_assert(KL >= 1 && VU >= 1, "staging split");
   u32x4 k[KL];
   u32x4 v[VU][VW];
+  uint32_t zero_mask;  // bit i: K load i past the end; bit 16 + 2u + w: V load (u, w)
 };
+
+// Uniform reads through the constant address space become scalar loads (they
+// count against lgkmcnt, so they never wait for outstanding vector stores).
+template <typename U>
+__device__ __forceinline__ U scalar_load(const U* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) U* CP;
+  return ((CP)p)[i];
+}
 
 // Base addresses of block b of KV group r: row j of K is k + j * stride.
 struct BlockPtr {
@@ -63,7 +72,7 @@ __device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, cons
   BlockPtr p;
   size_t off;
   if (pt) {
-    off = (((size_t)pt[b] * h_kv + r) * kBlock) * D * sizeof(T);
+    off = (((size_t)scalar_load(pt, b) * h_kv + r) * kBlock) * D * sizeof(T);
     p.stride = D * (int)sizeof(T);
     p.valid = kBlock;
   } else {
@@ -78,13 +87,19 @@ __device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, cons
 
 template <typename T, int D, int NT>
 __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPtr& p) {
+  // Every load is issued unconditionally (rows past the end of a contiguous
+  // cache read the last valid row); the values are zeroed only when stored to
+  // LDS, so nothing here waits for the loads to land.
   using S = StageRegs<T, D, NT>;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  static_assert(S::KL <= 16 && S::VU * S::VW <= 16, "zero mask layout");
+  const int last = p.valid - 1;
+  uint32_t zm = 0;
 #pragma unroll
   for (int i = 0; i < S::KL; ++i) {
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
-    g.k[i] = j < p.valid ? *reinterpret_cast<const u32x4*>(p.k + (size_t)j * p.stride + c * 16) : z;
+    g.k[i] = *reinterpret_cast<const u32x4*>(p.k + (size_t)min(j, last) * p.stride + c * 16);
+    zm |= (j > last ? 1u : 0u) << i;
   }
   if constexpr (sizeof(T) == 2) {
     constexpr int DC = D / 8;
@@ -93,9 +108,10 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPt
       const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      const char* r0 = p.v + (size_t)(2 * kp) * p.stride + dc * 16;
-      g.v[i][0] = 2 * kp < p.valid ? *reinterpret_cast<const u32x4*>(r0) : z;
-      g.v[i][1] = 2 * kp + 1 < p.valid ? *reinterpret_cast<const u32x4*>(r0 + p.stride) : z;
+      g.v[i][0] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(2 * kp, last) * p.stride + dc * 16);
+      g.v[i][1] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(2 * kp + 1, last) * p.stride + dc * 16);
+      zm |= (2 * kp > last ? 1u : 0u) << (16 + 2 * i);
+      zm |= (2 * kp + 1 > last ? 1u : 0u) << (17 + 2 * i);
     }
   } else {
     constexpr int DC = D / 4;
@@ -104,20 +120,23 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPt
       const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
-      g.v[i][0] = key < p.valid ? *reinterpret_cast<const u32x4*>(p.v + (size_t)key * p.stride + dc * 16) : z;
+      g.v[i][0] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(key, last) * p.stride + dc * 16);
+      zm |= (key > last ? 1u : 0u) << (16 + 2 * i);
     }
   }
+  g.zero_mask = zm;
 }
 
 template <typename T, int D, int NT>
 __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* lds) {
   using S = StageRegs<T, D, NT>;
   using L = KvLds<T, D>;
+  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < S::KL; ++i) {
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
-    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = g.k[i];
+    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = ((g.zero_mask >> i) & 1u) ? z : g.k[i];
   }
   char* vt = lds + L::K_BYTES;
   if constexpr (sizeof(T) == 2) {
@@ -127,7 +146,8 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* 
       const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      const u32x4 x = g.v[i][0], y = g.v[i][1];
+      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : g.v[i][0];
+      const u32x4 y = ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : g.v[i][1];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
@@ -143,9 +163,9 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* 
       const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
+      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : g.v[i][0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = g.v[i][0][e];
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
     }
   }
 }
@@ -193,6 +213,19 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
 #define MSA_SCHED_FENCE() do {} while (0)
 #endif
 
+// Store 8 consecutive values (one 16-byte store for bf16, two for fp32).
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const f32x16& o, int base) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x8*>(dst) =
+        bf16x8{from_f32<T>(o[base]), from_f32<T>(o[base + 1]), from_f32<T>(o[base + 2]), from_f32<T>(o[base + 3]),
+               from_f32<T>(o[base + 4]), from_f32<T>(o[base + 5]), from_f32<T>(o[base + 6]), from_f32<T>(o[base + 7])};
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[base], o[base + 1], o[base + 2], o[base + 3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[base + 4], o[base + 5], o[base + 6], o[base + 7]};
+  }
+}
+
 // ------------------------------------------------------------ row tile math
 // One wave processes RT tiles of 32 (token, head) rows against the staged
 // block.  S^T = K . Q^T puts keys on the MFMA rows: lane l holds 16 keys of
@@ -208,20 +241,32 @@ struct TileRegs {
 };
 
 template <typename T, int D, int RT>
-__device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* lds, int b, bool mask) {
+__device__ __forceinline__ Frag<T> k_frag(const char* lds, int step) {
   using L = KvLds<T, D>;
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int kt = step / (D / 16), ks = step % (D / 16);
+  return *reinterpret_cast<const Frag<T>*>(lds + (kt * 32 + l32) * L::KS + (ks * 16 + half * 8) * (int)sizeof(T));
+}
+
+// S^T = K . Q^T for the staged block; fragments are read two steps ahead.
+template <typename T, int D, int RT>
+__device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* lds, int b, bool mask) {
+  constexpr int KS = D / 16, NS = 4 * KS;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  Frag<T> f0 = k_frag<T, D, RT>(lds, 0), f1 = k_frag<T, D, RT>(lds, 1);
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int step = 0; step < NS; ++step) {
+    const int kt = step / KS, ks = step % KS;
+    Frag<T> f2;
+    if (step + 2 < NS) f2 = k_frag<T, D, RT>(lds, step + 2);
+    if (ks == 0) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) t.s[rt][kt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const Frag<T> a = *reinterpret_cast<const Frag<T>*>(lds + (kt * 32 + l32) * L::KS +
-                                                          (ks * 16 + half * 8) * (int)sizeof(T));
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) mma32(t.s[rt][kt], a, t.qf[rt][ks]);
+      for (int rt = 0; rt < RT; ++rt) t.s[rt][kt] = f32x16{};
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mma32(t.s[rt][kt], f0, t.qf[rt][ks]);
+    f0 = f1;
+    f1 = f2;
     MSA_SCHED_FENCE();
   }
   if (mask) {
@@ -250,25 +295,30 @@ __device__ __forceinline__ void tile_pack_p(TileRegs<T, D, RT>& t, int rt) {
     }
 }
 
-// O^T += V^T . P^T.
+// O^T += V^T . P^T; V^T fragments are read two steps ahead.
 template <typename T, int D, int RT>
-__device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) {
+__device__ __forceinline__ Frag<T> v_frag(const char* lds, int step) {
   using L = KvLds<T, D>;
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const char* vt = lds + L::K_BYTES;
+  const int kt = step / (2 * (D / 32)), h2 = (step / (D / 32)) & 1, dt = step % (D / 32);
+  const int base = kt * 32 + h2 * 16;
+  return vt_frag<T>(lds + L::K_BYTES, L::VS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half);
+}
+
+template <typename T, int D, int RT>
+__device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) {
+  constexpr int DT = D / 32, NS = 4 * 2 * DT;
+  Frag<T> f0 = v_frag<T, D, RT>(lds, 0), f1 = v_frag<T, D, RT>(lds, 1);
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int step = 0; step < NS; ++step) {
+    const int kt = step / (2 * DT), h2 = (step / DT) & 1, dt = step % DT;
+    Frag<T> f2;
+    if (step + 2 < NS) f2 = v_frag<T, D, RT>(lds, step + 2);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int base = kt * 32 + h2 * 16;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const Frag<T> a = vt_frag<T>(vt, L::VS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], a, t.pf[rt][kt][h2]);
-      }
-      MSA_SCHED_FENCE();
-    }
+    for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], f0, t.pf[rt][kt][h2]);
+    f0 = f1;
+    f1 = f2;
+    MSA_SCHED_FENCE();
   }
 }
 
@@ -286,7 +336,7 @@ struct SchedArgs {
   int32_t* cell_off;  // [n_cells + 1]
   int32_t* item_off;  // [n_cells + 1]
   int32_t* entries;   // [n_q * h_kv * top_k]
-  int32_t* items;     // [max_items]
+  i32x4* items;       // [max_items] {b, r, e_begin, e_end}
   int32_t* scan;      // [4 * n_scan_tiles]
   int32_t n_scan_tiles;
 };
@@ -456,8 +506,14 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
 __global__ void ks_items_kernel(SchedArgs a) {
   const int64_t cell = blockIdx.x * 256ll + threadIdx.x;
   if (cell >= a.n_cells) return;
-  const int b = a.item_off[cell], e = a.item_off[cell + 1];
-  for (int it = b; it < e; ++it) a.items[it] = (int32_t)cell;
+  const int ib = a.item_off[cell], ie = a.item_off[cell + 1];
+  const int eb = a.cell_off[cell], ee = a.cell_off[cell + 1];
+  int r, b;
+  cell_rb(cell, a.n_blocks, a.h_kv, r, b);
+  for (int it = ib; it < ie; ++it) {
+    const int e0 = eb + (it - ib) * a.chunk;
+    a.items[it] = i32x4{b, r, e0, min(e0 + a.chunk, ee)};
+  }
 }
 
 // ====================================================================
@@ -471,10 +527,11 @@ struct KpArgs {
   const int32_t* cell_off;
   const int32_t* item_off;
   const int32_t* entries;
-  const int32_t* items;
+  const i32x4* items;
   void* part_o;       // [window, h_kv, top_k, G, D]  un-normalised sum_j p_j v_j
   float2* part_ml;    // [window, h_kv, top_k, G]     (row max * sm_scale, sum_j p_j)
   int32_t n_kv, q_start, h_q, h_kv, group, g_shift, top_k, n_blocks, window, chunk, w;
+  size_t trash_slot;  // first of two spare slot regions at the end of part_o / part_ml
   float sm_scale;
 };
 
@@ -485,160 +542,179 @@ struct KpItem {
   int b, r, e_begin, e_end;
 };
 
-__device__ __forceinline__ KpItem kp_item(const KpArgs& a, int it) {
-  KpItem m;
-  const int cell = a.items[it];
-  const int c = it - a.item_off[cell];
-  cell_rb(cell, a.n_blocks, a.h_kv, m.r, m.b);
-  m.e_begin = a.cell_off[cell] + c * a.chunk;
-  m.e_end = min(m.e_begin + a.chunk, a.cell_off[cell + 1]);
-  return m;
-}
 
-// Query rows of one pass (RT tiles of 32 (token, head) rows) of one item.
-template <typename T, int D, int RT>
+// Query rows of one pass (one 32-row tile per wave) of one item.
+template <typename T, int D>
 struct KpPass {
-  Frag<T> qf[RT][D / 16];
-  int pos[RT], slot[RT], head[RT];
-  bool ok[RT];
-  bool ready;
+  Frag<T> qf[D / 16];
+  int pos, slot, head;
+  bool ok;
 };
 
-template <typename T, int D, int RT>
-__device__ __forceinline__ void kp_load_pass(KpPass<T, D, RT>& ps, const KpArgs& a, const KpItem& m, int row0) {
+// Gathers the query fragments of this lane's row `rho` of item m.  `ent` is
+// the (token << 4 | slot) entry of that row.  Rows past the item's end load a
+// valid row (the caller clamps `ent`) and are flagged !ok; no branches, so
+// the number of outstanding loads is always known at compile time.
+template <typename T, int D>
+__device__ __forceinline__ void kp_load_pass(KpPass<T, D>& ps, const KpArgs& a, const KpItem& m, int rho, int ent) {
   const T* __restrict__ q = static_cast<const T*>(a.q);
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int half = (threadIdx.x & 63) >> 5;
   const int G = a.group;
-  const int nrows = (m.e_end - m.e_begin) * G;
+  ps.ok = rho < (m.e_end - m.e_begin) * G;
+  const int i = ent >> 4, j = ent & 15;
+  ps.head = rho & (G - 1);
+  ps.slot = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
+  ps.pos = ps.ok ? a.q_start + i : -1;
+  const T* qrow = q + ((size_t)i * a.h_q + m.r * G + ps.head) * D + half * 8;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int rho = row0 + rt * 32 + l32;
-    ps.ok[rt] = rho < nrows;
-    const int ent = ps.ok[rt] ? a.entries[m.e_begin + (rho >> a.g_shift)] : 0;
-    const int i = ent >> 4, j = ent & 15;
-    ps.head[rt] = rho & (G - 1);
-    ps.slot[rt] = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
-    ps.pos[rt] = ps.ok[rt] ? a.q_start + i : -1;
-    const T* qrow = q + ((size_t)i * a.h_q + m.r * G + ps.head[rt]) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) ps.qf[rt][ks] = ps.ok[rt] ? load_frag<T>(qrow + ks * 16) : zero_frag<T>();
-  }
-  ps.ready = true;
+  for (int ks = 0; ks < D / 16; ++ks) ps.qf[ks] = load_frag<T>(qrow + ks * 16);
 }
 
-// All passes of one item for this wave.  The next pass's queries (of this
-// item, or the first pass of `nxt`) are loaded into the query registers as
-// soon as the scores no longer need them, so their latency overlaps P.V.
-template <typename T, int D, int RT, int NT>
-__device__ __forceinline__ void kp_compute(const KpArgs& a, const KpItem& m, bool has_nxt, const KpItem nxt,
-                                           const char* lds, KpPass<T, D, RT>& ps) {
-  constexpr int ROWS_PER_PASS = (NT / 64) * RT * 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+template <typename T, int D>
+__device__ __forceinline__ int kp_entry(const KpItem& m, int rho, int g_shift, const int* ent_lds) {
+  return ent_lds[min(rho >> g_shift, m.e_end - m.e_begin - 1)];
+}
+
+// Scores, softmax and P.V for the rows in `ps`, then the partial stores.  The
+// math is skipped when no row of the wave is valid; the stores are not (rows
+// past the end write a trash row), keeping the memory-op count fixed.
+template <typename T, int D>
+__device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, D>& ps, const char* lds,
+                                        TileRegs<T, D, 1>& t, float& mx, float& l) {
   const float c2 = a.sm_scale * kLog2e;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) t.qf[0][ks] = ps.qf[ks];
+  t.pos[0] = ps.pos;
+  const bool need_mask = ps.ok && (b * kBlock + kBlock - 1 > ps.pos);
+  tile_scores<T, D, 1>(t, lds, b, __any(need_mask));
+  float mm = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mm = fmaxf(mm, t.s[0][kt][v]);
+  mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+  mx = mm;
+  const float mc = (mm == -__builtin_inff()) ? 0.0f : mm * c2;
+  float sum = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float pr = fast_exp2(fmaf(t.s[0][kt][v], c2, -mc));
+      t.s[0][kt][v] = pr;
+      sum += pr;
+    }
+  l = sum + __shfl_xor(sum, 32, 64);
+  tile_pack_p<T, D, 1>(t, 0);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) t.o[0][dt] = f32x16{};
+  tile_pv<T, D, 1>(t, lds);
+}
+
+// Partial layout.  The partial of (token, slot) is a region of G * D values
+// stored in the order the MFMA accumulators hold them: 8-value chunks indexed
+// ((dt * 2 + p) * 2 + half) * G + head hold d = dt*32 + 16p + 4half + {0..3}
+// and the same + 8.  A store instruction then writes, for each token of the
+// tile, 2 * G chunks back to back (full cache lines) instead of 64 scattered
+// 8-byte pieces.
+__device__ __forceinline__ int part_chunk(int dt, int p, int half, int head, int G) {
+  return ((dt * 2 + p) * 2 + half) * G + head;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void kp_store(const KpArgs& a, const KpPass<T, D>& ps, const TileRegs<T, D, 1>& t,
+                                         float mx, float l) {
+  const int half = (threadIdx.x & 63) >> 5;
   const int G = a.group;
-  const int nrows = (m.e_end - m.e_begin) * G;
-  T* part_o = static_cast<T*>(a.part_o);
-  for (int row0 = wave * RT * 32; row0 < nrows; row0 += ROWS_PER_PASS) {
-    if (!ps.ready) kp_load_pass<T, D, RT>(ps, a, m, row0);
-    TileRegs<T, D, RT> t;
-    int slot[RT], head[RT];
-    bool ok[RT];
-    bool need_mask = false;
+  const size_t slot = ps.ok ? (size_t)ps.slot : a.trash_slot;
+  T* region = static_cast<T*>(a.part_o) + slot * G * D;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      slot[rt] = ps.slot[rt];
-      head[rt] = ps.head[rt];
-      ok[rt] = ps.ok[rt];
-      t.pos[rt] = ps.pos[rt];
-      need_mask |= ok[rt] && (m.b * kBlock + kBlock - 1 > t.pos[rt]);
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) t.qf[rt][ks] = ps.qf[rt][ks];
+    for (int p = 0; p < 2; ++p) {
+      store8<T>(region + (size_t)part_chunk(dt, p, half, ps.head, G) * 8, t.o[0][dt], 8 * p);
     }
-    tile_scores<T, D, RT>(t, lds, m.b, __any(need_mask));
-    ps.ready = false;
-    if (row0 + ROWS_PER_PASS < nrows) {
-      kp_load_pass<T, D, RT>(ps, a, m, row0 + ROWS_PER_PASS);
-    } else if (has_nxt && wave * RT * 32 < (nxt.e_end - nxt.e_begin) * G) {
-      kp_load_pass<T, D, RT>(ps, a, nxt, wave * RT * 32);
-    }
-    float mx[RT], l[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float mm = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mm = fmaxf(mm, t.s[rt][kt][v]);
-      mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
-      mx[rt] = mm;
-      const float mc = (mm == -__builtin_inff()) ? 0.0f : mm * c2;
-      float sum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(t.s[rt][kt][v], c2, -mc));
-          t.s[rt][kt][v] = p;
-          sum += p;
-        }
-      l[rt] = sum + __shfl_xor(sum, 32, 64);
-      tile_pack_p<T, D, RT>(t, rt);
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) t.o[rt][dt] = f32x16{};
-    tile_pv<T, D, RT>(t, lds);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (!ok[rt]) continue;
-      T* dst = part_o + ((size_t)slot[rt] * G + head[rt]) * D + 4 * half;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-          store4<T>(dst + dt * 32 + 8 * vv, t.o[rt][dt][4 * vv], t.o[rt][dt][4 * vv + 1],
-                    t.o[rt][dt][4 * vv + 2], t.o[rt][dt][4 * vv + 3]);
-      if (half == 0) a.part_ml[(size_t)slot[rt] * G + head[rt]] = float2{mx[rt] * a.sm_scale, l[rt]};
-    }
-  }
+  const size_t mrow = (half == 0 ? slot : a.trash_slot + 1) * G + ps.head;
+  a.part_ml[mrow] = float2{mx * a.sm_scale, l};
+}
+
+constexpr int kKpThreads = 512;                    // 8 waves, 32 rows each per pass
+constexpr int kKpRowsPerPass = kKpThreads / 2;     // 256
+constexpr int kKpItemRows = 2 * kKpRowsPerPass;    // an item holds at most 512 (token, head) rows
+constexpr int kKpMaxChunk = kKpItemRows;           // tokens per item when G == 1
+
+template <typename T, int D>
+__device__ __forceinline__ KpItem kp_item_s(const KpArgs& a, int it) {
+  const i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
+  return KpItem{d[0], d[1], d[2], d[3]};
 }
 
 // Persistent over this XCD's items of the window: the grid is a multiple of 8
 // and workgroup g (dispatched to XCD g % 8) takes the XCD's items sub, sub +
-// nsub, ...; the next item's K/V is prefetched into registers while computing.
-template <typename T, int D, int RT, int NT>
-__global__ __launch_bounds__(NT) void kp_kernel(KpArgs a) {
+// nsub, ...  Each item is two passes of 256 rows.  The next item's K/V and
+// token entries are prefetched into registers at the start of an item, the
+// next pass's queries while the current pass runs P.V.
+template <typename T, int D>
+__global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
   using L = KvLds<T, D>;
-  constexpr int NB = (2 * L::BYTES <= 160 * 1024) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) char lds[NB][L::BYTES];
+  constexpr int NT = kKpThreads;
+  constexpr int BUF = L::BYTES + kKpMaxChunk * 4;   // K, V^T, token entries
+  constexpr int NB = (2 * BUF <= 160 * 1024) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char lds[NB][BUF];
   const int x = blockIdx.x & 7, sub = blockIdx.x >> 3, nsub = gridDim.x >> 3;
   const int64_t n_l = (int64_t)a.h_kv * a.n_blocks, per = n_l >> 3;
   const int64_t k0 = (int64_t)a.w * n_l + x * per;
-  const int item_begin = a.item_off[k0];
-  const int item_end = a.item_off[k0 + per];
+  const int item_begin = scalar_load(a.item_off, k0);
+  const int item_end = scalar_load(a.item_off, k0 + per);
   int it = item_begin + sub;
   if (it >= item_end) return;
+  const int wave = threadIdx.x >> 6, l32 = threadIdx.x & 31;
+  const int rho0 = wave * 32 + l32;                 // this lane's row in pass 0; pass 1 is + 256
+  const int tid = threadIdx.x;
+
   StageRegs<T, D, NT> pre;
-  KpItem cur = kp_item(a, it);
+  KpItem cur = kp_item_s<T, D>(a, it);
   stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv));
+  int pre_ent = a.entries[cur.e_begin + min(tid, cur.e_end - cur.e_begin - 1)];
   stage_store<T, D, NT>(pre, lds[0]);
+  reinterpret_cast<int*>(lds[0] + L::BYTES)[tid] = pre_ent;
   __syncthreads();
-  KpPass<T, D, RT> ps;
-  ps.ready = false;
+  KpPass<T, D> ps;
+  kp_load_pass<T, D>(ps, a, cur, rho0, kp_entry<T, D>(cur, rho0, a.g_shift, reinterpret_cast<const int*>(lds[0] + L::BYTES)));
   int buf = 0;
   for (;;) {
     const int nx = it + nsub;
     const bool has_next = nx < item_end;
     KpItem nxt = cur;
+    int nxt_ent = 0;
     if (has_next) {
-      nxt = kp_item(a, nx);
+      nxt = kp_item_s<T, D>(a, nx);
       stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv));
+      const int ne = nxt.e_end - nxt.e_begin;
+      pre_ent = a.entries[nxt.e_begin + min(tid, ne - 1)];
+      nxt_ent = a.entries[nxt.e_begin + min(rho0 >> a.g_shift, ne - 1)];
     }
-    kp_compute<T, D, RT, NT>(a, cur, has_next, nxt, lds[buf], ps);
+    const char* L0 = lds[buf];
+    const int* ent_lds = reinterpret_cast<const int*>(L0 + L::BYTES);
+    TileRegs<T, D, 1> t;
+    float mx = 0.f, l = 0.f;
+    // pass 0
+    KpPass<T, D> cp = ps;
+    const bool act0 = __any(cp.ok);
+    if (act0) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
+    kp_load_pass<T, D>(ps, a, cur, rho0 + kKpRowsPerPass, kp_entry<T, D>(cur, rho0 + kKpRowsPerPass, a.g_shift, ent_lds));
+    kp_store<T, D>(a, cp, t, mx, l);
+    // pass 1
+    cp = ps;
+    const bool act1 = __any(cp.ok);
+    if (act1) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
+    if (has_next) kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
+    kp_store<T, D>(a, cp, t, mx, l);
     if (!has_next) break;
     if (NB == 1) __syncthreads();
-    stage_store<T, D, NT>(pre, lds[NB == 2 ? (buf ^ 1) : 0]);
+    char* dst = lds[NB == 2 ? (buf ^ 1) : 0];
+    stage_store<T, D, NT>(pre, dst);
+    reinterpret_cast<int*>(dst + L::BYTES)[tid] = pre_ent;
     __syncthreads();
     it = nx;
     cur = nxt;
@@ -660,15 +736,16 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
   constexpr int DC = D / 8;
   const int G = a.group;
-  const int per_pair = G * DC;
+  const int per_pair = G * DC;                 // one 8-value chunk per thread
   const int sub = threadIdx.x / per_pair;
-  const int t = threadIdx.x % per_pair;
+  const int c = threadIdx.x % per_pair;        // chunk index within a (token, slot) region
   if (sub >= a.pairs_per_wg) return;
   const int64_t pair = (int64_t)blockIdx.x * a.pairs_per_wg + sub;  // (i_local, r)
   const int il = (int)(pair / a.h_kv), r = (int)(pair % a.h_kv);
   const int i = a.w * a.window + il;
   if (il >= a.window || i >= a.n_q) return;
-  const int g = t / DC, dc = t % DC;
+  const int g = c % G, half = (c / G) & 1, p = (c / (2 * G)) & 1, dt = c / (4 * G);
+  const int d0 = dt * 32 + 16 * p + 4 * half;  // chunk holds d0..d0+3 and d0+8..d0+11
   const int diag = (a.q_start + i) >> 7;
   const int32_t* br = a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k;
   const uint32_t used = used_slots(br, a.top_k, diag);
@@ -679,8 +756,10 @@ __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     const bool u = (used >> j) & 1u;
-    ml[j] = u ? a.part_ml[(slot0 + j) * G + g] : float2{-__builtin_inff(), 0.0f};
-    x[j] = u ? load_frag<T>(po + ((slot0 + j) * G + g) * D + dc * 8) : zero_frag<T>();
+    const size_t sj = slot0 + (u ? j : 0);
+    ml[j] = a.part_ml[sj * G + g];
+    x[j] = load_frag<T>(po + (sj * G * D + (size_t)c * 8));
+    if (!u) ml[j] = float2{-__builtin_inff(), 0.0f};
   }
   float mx = -__builtin_inff();
 #pragma unroll
@@ -695,11 +774,11 @@ __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(x[j][e]), acc[e]);
   }
-  T* out = static_cast<T*>(a.o) + ((size_t)i * a.h_q + r * G + g) * D + dc * 8;
+  T* out = static_cast<T*>(a.o) + ((size_t)i * a.h_q + r * G + g) * D;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  store4<T>(out, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  store4<T>(out + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse && dc == 0)
+  store4<T>(out + d0, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  store4<T>(out + d0 + 8, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (a.lse && c < G)
     a.lse[(size_t)i * a.h_q + r * G + g] = den > 0.0f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
 }
 
@@ -1013,13 +1092,6 @@ static int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
-#ifndef KP_RT
-#define KP_RT 1
-#endif
-#ifndef KP_NT
-#define KP_NT 512
-#endif
-
 // Compute units of the current device (cached per device).
 static int num_cus() {
   static int cached[64] = {0};
@@ -1053,7 +1125,7 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   w = std::min<int64_t>(w, std::max<int32_t>(n_q, 1));
   p.window = (int32_t)w;
   p.n_windows = (int32_t)((n_q + w - 1) / w);
-  p.chunk = std::max(1, std::min(16 * 64, env_int("MSA_KP_CHUNK", 32)));
+  p.chunk = 512 / G;  // tokens per KV-outer item: 512 (token, head) rows
   p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
   const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
   p.max_items = n_entries / p.chunk + p.n_cells + 1;
@@ -1064,10 +1136,11 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   p.off_cell_off = off; off = align_up(off + (p.n_cells + 1) * 4);
   p.off_item_off = off; off = align_up(off + (p.n_cells + 1) * 4);
   p.off_entries = off; off = align_up(off + n_entries * 4);
-  p.off_items = off; off = align_up(off + p.max_items * 4);
+  p.off_items = off; off = align_up(off + p.max_items * 16);
   p.off_scan = off; off = align_up(off + 4 * n_scan_tiles * 4);
-  p.off_part_o = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * d_h * esz);
-  p.off_part_lse = off; off = align_up(off + (size_t)p.window * h_kv * top_k * G * 8);
+  const size_t prow = ((size_t)p.window * h_kv * top_k + 2) * G;  // + two trash slots
+  p.off_part_o = off; off = align_up(off + prow * d_h * esz);
+  p.off_part_lse = off; off = align_up(off + prow * 8);
   p.total = off;
   return p;
 }
@@ -1094,7 +1167,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   s.cell_off = reinterpret_cast<int32_t*>(ws + pl.off_cell_off);
   s.item_off = reinterpret_cast<int32_t*>(ws + pl.off_item_off);
   s.entries = reinterpret_cast<int32_t*>(ws + pl.off_entries);
-  s.items = reinterpret_cast<int32_t*>(ws + pl.off_items);
+  s.items = reinterpret_cast<i32x4*>(ws + pl.off_items);
   s.scan = reinterpret_cast<int32_t*>(ws + pl.off_scan);
   s.n_scan_tiles = (int32_t)((pl.n_cells + kScanTile - 1) / kScanTile);
   const int64_t rows = (int64_t)a.n_q * a.h_kv;
@@ -1121,6 +1194,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   kp.items = s.items;
   kp.part_o = ws + pl.off_part_o;
   kp.part_ml = reinterpret_cast<float2*>(ws + pl.off_part_lse);
+  kp.trash_slot = (size_t)pl.window * a.h_kv * a.top_k;
   kp.n_kv = a.n_kv;
   kp.q_start = a.q_start;
   kp.h_q = a.h_q;
@@ -1155,7 +1229,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     kp.w = w;
     int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kp_wgs_per_cu<T, D>());
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
-    hipLaunchKernelGGL((kp_kernel<T, D, KP_RT, KP_NT>), dim3(grid), dim3(KP_NT), 0, st, kp);
+    hipLaunchKernelGGL((kp_kernel<T, D>), dim3(grid), dim3(kKpThreads), 0, st, kp);
     km.w = w;
     const int64_t pairs = (int64_t)tok * a.h_kv;
     hipLaunchKernelGGL((km_kernel<T, D>), dim3((unsigned)((pairs + km.pairs_per_wg - 1) / km.pairs_per_wg)),
