@@ -342,20 +342,44 @@ struct SchedArgs {
 };
 
 // Cells are the (window, group, block) token lists.  Within a window they are
-// numbered XCD-major: cell (r, b) belongs to XCD (r * nbp + b) % 8, and the
-// KV-outer workgroups running on that XCD take exactly its cells, so a KV
-// block stays in one L2 across windows.  nbp = blocks rounded up to 8.
+// numbered XCD-major, and the KV-outer workgroups running on XCD x take
+// exactly XCD x's cells.  A group's blocks are spread over S = 8 / h_kv XCDs
+// (by b mod S), so each XCD gathers the queries of one group only (they stay
+// in its L2 while the window's items run) and reads each KV block of its
+// cells from one L2 across windows.  nbp = blocks rounded up to 8.
 __device__ __forceinline__ int64_t cell_key(int w, int r, int b, int nbp, int h_kv) {
   const int n_l = h_kv * nbp, per = n_l >> 3;
-  const int cl = r * nbp + b;
-  return (int64_t)w * n_l + (cl & 7) * per + (cl >> 3);
+  int x, pos;
+  if (h_kv <= 8 && (8 % h_kv) == 0) {
+    const int S = 8 / h_kv;
+    x = r * S + b % S;
+    pos = b / S;
+  } else if ((h_kv & 7) == 0) {
+    x = r & 7;
+    pos = (r >> 3) * nbp + b;
+  } else {  // any other head count: interleave all cells over the XCDs
+    const int cl = r * nbp + b;
+    x = cl & 7;
+    pos = cl >> 3;
+  }
+  return (int64_t)w * n_l + (int64_t)x * per + pos;
 }
 __device__ __forceinline__ void cell_rb(int64_t k, int nbp, int h_kv, int& r, int& b) {
   const int n_l = h_kv * nbp, per = n_l >> 3;
   const int kl = (int)(k % n_l);
-  const int cl = (kl % per) * 8 + kl / per;
-  r = cl / nbp;
-  b = cl % nbp;
+  const int x = kl / per, pos = kl % per;
+  if (h_kv <= 8 && (8 % h_kv) == 0) {
+    const int S = 8 / h_kv;
+    r = x / S;
+    b = pos * S + x % S;
+  } else if ((h_kv & 7) == 0) {
+    r = (pos / nbp) * 8 + x;
+    b = pos % nbp;
+  } else {
+    const int cl = pos * 8 + x;
+    r = cl / nbp;
+    b = cl % nbp;
+  }
 }
 
 __device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
