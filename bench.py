@@ -175,8 +175,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the path shards by KV group / decode batch, see DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library has no "
+              "multi-GPU path (it would shard by KV group, decode batch or KV-block range).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

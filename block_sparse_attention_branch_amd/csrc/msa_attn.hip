@@ -10,9 +10,10 @@
 // (token, head) row that selected it.  The schedule inverts the index lists
 // into per-(window, group, block) token lists and cuts each list into work
 // items of at most `chunk` tokens (the pages' pre-scheduled tile chunking).
-// Each item writes one normalised partial (O_b, lse_b) per (token, head); a
-// merge kernel then combines a token's partials with log-sum-exp weights (the
-// second stage).  Query tokens are processed in windows so that the partial
+// Each item writes, per (token, head), the un-normalised partial output of
+// that block, sum_j exp(s_j - m_b) v_j in bf16, with its max m_b and sum l_b;
+// a merge kernel then combines a token's partials with log-sum-exp weights
+// (the second stage).  Query tokens are processed in windows so that the partial
 // buffer of one window stays small enough to live in the last-level cache
 // between the two stages.  No atomics touch floating-point data, so results
 // are bitwise reproducible.
@@ -722,18 +723,25 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
     const int* ent_lds = reinterpret_cast<const int*>(L0 + L::BYTES);
     TileRegs<T, D, 1> t;
     float mx = 0.f, l = 0.f;
+    // an item of at most 256 rows has no second pass (uniform)
+    const bool two = (cur.e_end - cur.e_begin) * a.group > kKpRowsPerPass;
     // pass 0
     KpPass<T, D> cp = ps;
     const bool act0 = __any(cp.ok);
     if (act0) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
-    kp_load_pass<T, D>(ps, a, cur, rho0 + kKpRowsPerPass, kp_entry<T, D>(cur, rho0 + kKpRowsPerPass, a.g_shift, ent_lds));
+    if (two)
+      kp_load_pass<T, D>(ps, a, cur, rho0 + kKpRowsPerPass, kp_entry<T, D>(cur, rho0 + kKpRowsPerPass, a.g_shift, ent_lds));
+    else if (has_next)
+      kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
     kp_store<T, D>(a, cp, t, mx, l);
     // pass 1
-    cp = ps;
-    const bool act1 = __any(cp.ok);
-    if (act1) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
-    if (has_next) kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
-    kp_store<T, D>(a, cp, t, mx, l);
+    if (two) {
+      cp = ps;
+      const bool act1 = __any(cp.ok);
+      if (act1) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
+      if (has_next) kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
+      kp_store<T, D>(a, cp, t, mx, l);
+    }
     if (!has_next) break;
     if (NB == 1) __syncthreads();
     char* dst = lds[NB == 2 ? (buf ^ 1) : 0];
@@ -1143,9 +1151,19 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   p.n_blocks = (int32_t)((((int64_t)q_start + n_q - 1) / kBlock + 1 + 7) & ~int64_t(7));
   (void)n_kv;
   const size_t per_token = (size_t)h_kv * top_k * G * (d_h * esz + 8);
+  // Window of query tokens per KV-outer pass.  Its partials should stay in
+  // the last-level cache (the budget), but with many blocks to choose from a
+  // small window leaves few tokens per (group, block) cell and the items
+  // mostly empty, so the window grows until a cell holds about
+  // `cell_tokens` tokens on average (bounded by a hard memory cap).
   const size_t budget = (size_t)env_int("MSA_PARTIAL_BUDGET_MB", 128) << 20;
+  const size_t cap = (size_t)env_int("MSA_PARTIAL_CAP_MB", 4096) << 20;
+  const int64_t cell_tokens = env_int("MSA_CELL_TOKENS", 32);
+  const int64_t blocks_seen = ((int64_t)q_start + n_q - 1) / kBlock + 1;
   int64_t w = (int64_t)(budget / per_token);
-  w = std::max<int64_t>(64, (w / 64) * 64);
+  const int64_t w_occ = (cell_tokens * blocks_seen + std::max(1, top_k - 1) - 1) / std::max(1, top_k - 1);
+  w = std::max<int64_t>(w, std::min<int64_t>(w_occ, (int64_t)(cap / per_token)));
+  w = std::max<int64_t>(64, ((w + 63) / 64) * 64);
   w = std::min<int64_t>(w, std::max<int32_t>(n_q, 1));
   p.window = (int32_t)w;
   p.n_windows = (int32_t)((n_q + w - 1) / w);

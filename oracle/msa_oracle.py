@@ -14,7 +14,7 @@ Sources (the pages this follows):
        per GQA group, one shared index key (Q_idx in R^{n x h x d},
        K_idx in R^{n x 1 x d}); max-pool rather than mean-pool.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   * query i of a call sits at absolute position p = q_start + i;
   * block b holds token positions [128 b, 128 b + 127]; the diagonal block of
     position p is p // 128 and its pooled score uses only keys j <= p;
