@@ -8,6 +8,8 @@
 #include <string>
 
 #include "msa.h"
+
+#include <cstdlib>
 #include "msa_internal.hpp"
 
 namespace {
@@ -156,7 +158,11 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
     a.batch = batch;
     a.h_kv = s.h_kv;
     a.max_pages = kv->max_pages;
-    a.pages_per_wg = 16;
+    {
+      const char* e = getenv("MSA_KI_PAGES_PER_WG");
+      const int v = e ? atoi(e) : 0;
+      a.pages_per_wg = (v >= 4 && v <= 256) ? v : 16;
+    }
     a.idx_scale = idx_scale;
     a.force_local = s.force_local;
     a.top_k = s.top_k;

@@ -51,13 +51,6 @@ struct StageRegs {
   uint32_t zero_mask;  // bit i: K load i past the end; bit 16 + 2u + w: V load (u, w)
 };
 
-// Uniform reads through the constant address space become scalar loads (they
-// count against lgkmcnt, so they never wait for outstanding vector stores).
-template <typename U>
-__device__ __forceinline__ U scalar_load(const U* p, int64_t i) {
-  typedef const __attribute__((address_space(4))) U* CP;
-  return ((CP)p)[i];
-}
 
 // Base addresses of block b of KV group r: row j of K is k + j * stride.
 struct BlockPtr {
@@ -941,23 +934,82 @@ struct KdArgs {
   float sm_scale;
 };
 
-constexpr int kKdVtStride = 32 * 2 + 8;  // bytes per d row of a 32-key V^T slice (bf16)
+constexpr int kKdVtStride = 32 * 2 + 8;
+constexpr int kKdWaves = 8;              // waves per decode workgroup  // bytes per d row of a 32-key V^T slice (bf16)
 
+// One 32-key unit of a selected page for one wave: K rows as 16x16x32 B
+// fragments (keys on the MFMA rows) and V rows as raw 16-byte pieces, to be
+// transposed through LDS.
 template <int D>
-__global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
+struct KdUnit {
+  Frag<bf16_t> kf[2][D / 32];
+  u32x4 vx[D / 32], vy[D / 32];
+};
+
+// `pages` holds, in lane j, the physical page of slot j (read once per
+// workgroup), so a unit's address needs no dependent load.
+template <int D>
+__device__ __forceinline__ void kd_load_unit(KdUnit<D>& x, const KdArgs& a, int pages, int r, int u) {
   typedef bf16_t T;
-  __shared__ __attribute__((aligned(16))) char vts[4][D * kKdVtStride];
-  __shared__ float olds[4][16][D + 1];
-  __shared__ float llds[4][16];
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+  const int j = u >> 2, qq = u & 3;
+  const int page = __builtin_amdgcn_readlane(pages, j);
+  const size_t base = (((size_t)page * a.h_kv + r) * kBlock + qq * 32) * D;
+  const T* kb = static_cast<const T*>(a.k) + base;
+  const T* vb = static_cast<const T*>(a.v) + base;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) x.kf[tt][ks] = load_frag<T>(kb + (tt * 16 + l16) * D + ks * 32 + q4 * 8);
+#pragma unroll
+  for (int it = 0; it < D / 32; ++it) {
+    const int dc = q4 + 4 * it;
+    x.vx[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16) * D + 8 * dc);
+    x.vy[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16 + 1) * D + 8 * dc);
+  }
+}
+
+__device__ __forceinline__ uint32_t used_slots_s(const int32_t* row, int top_k, int diag) {
+  uint32_t m = 0;
+  int prev = -1;
+  for (int j = 0; j < top_k; ++j) {
+    const int b = scalar_load(row, j);
+    if (b > prev && b <= diag) {
+      m |= 1u << j;
+      prev = b;
+    }
+  }
+  return m;
+}
+
+// Workgroup (sequence s, group r, split sp) of NW waves.  The selected keys
+// are cut into 32-key units (4 per page); wave w of split sp takes units
+// sp*NW + w, + NW*split, ...  Each wave keeps an online softmax over its
+// units with the next unit's loads in flight while the current one is
+// computed; the NW waves are then combined in LDS, and the splits by
+// kd_merge_kernel.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
+  typedef bf16_t T;
+  constexpr int kVtBytes = D * kKdVtStride;
+  constexpr int kOBytes = 16 * (D + 1) * 4;
+  constexpr int kSlab = kVtBytes > kOBytes ? kVtBytes : kOBytes;
+  // per wave: the V^T slice while units run, then its output rows
+  __shared__ __attribute__((aligned(16))) char slab[NW][kSlab];
+  __shared__ float llds[NW][16];
+  __shared__ float lrs[NW][16];
   const int sp = blockIdx.x % a.split;
   const int sr = blockIdx.x / a.split;
   const int s = sr / a.h_kv, r = sr % a.h_kv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
   const int G = a.group;
-  const int L = a.seq_lens[s];
+  const int L = scalar_load(a.seq_lens, s);
   const int p = L - 1, diag = p >> 7;
   const int32_t* br = a.block_idx + ((size_t)s * a.h_kv + r) * a.top_k;
-  const uint32_t used = used_slots(br, a.top_k, diag);
+  const uint32_t used = used_slots_s(br, a.top_k, diag);
+  // lane j: block and physical page of slot j
+  const int bl = (lane < a.top_k && ((used >> lane) & 1u)) ? br[lane] : 0;
+  const int pages = (lane < a.top_k && ((used >> lane) & 1u)) ? a.page_table[(size_t)s * a.max_pages + bl] : 0;
   const float c2 = a.sm_scale * kLog2e;
   const T* __restrict__ qp = static_cast<const T*>(a.q) + ((size_t)s * a.h_q + r * G) * D;
   Frag<T> qf[D / 32];
@@ -968,37 +1020,27 @@ __global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
   float mrun = -__builtin_inff(), lrun = 0.0f;
-  char* vt = vts[wave];
+  char* vt = slab[wave];
   const int n_units = a.top_k * 4;
-  for (int u = sp * 4 + wave; u < n_units; u += a.split * 4) {
-    const int j = u >> 2, qq = u & 3;
-    if (!(used & (1u << j))) continue;
-    const int b = br[j];
-    const int page = a.page_table[(size_t)s * a.max_pages + b];
-    const size_t base = (((size_t)page * a.h_kv + r) * kBlock + qq * 32) * D;
-    const T* kb = static_cast<const T*>(a.k) + base;
-    const T* vb = static_cast<const T*>(a.v) + base;
-    Frag<T> kf[2][D / 32];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) kf[tt][ks] = load_frag<T>(kb + (tt * 16 + l16) * D + ks * 32 + q4 * 8);
-    u32x4 vx[D / 32], vy[D / 32];
-#pragma unroll
-    for (int it = 0; it < D / 32; ++it) {
-      const int dc = q4 + 4 * it;
-      vx[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16) * D + 8 * dc);
-      vy[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16 + 1) * D + 8 * dc);
-    }
+  const int step = a.split * NW;
+  int u = sp * NW + wave;
+  while (u < n_units && !((used >> (u >> 2)) & 1u)) u += step;
+  KdUnit<D> cur, nxt;
+  if (u < n_units) kd_load_unit<D>(cur, a, pages, r, u);
+  while (u < n_units) {
+    int un = u + step;
+    while (un < n_units && !((used >> (un >> 2)) & 1u)) un += step;
+    if (un < n_units) kd_load_unit<D>(nxt, a, pages, r, un);
+    const int b = __builtin_amdgcn_readlane(bl, u >> 2);
     f32x4 sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       sc[tt] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], kf[tt][ks], qf[ks]);
+      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], cur.kf[tt][ks], qf[ks]);
     }
-    // sc[tt][v]: key qq*32 + tt*16 + 4*q4 + v, head l16
-    const int key0 = b * kBlock + qq * 32;
+    // sc[tt][v]: key (u%4)*32 + tt*16 + 4*q4 + v of block b, head l16
+    const int key0 = b * kBlock + (u & 3) * 32;
     float m = -__builtin_inff();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -1016,8 +1058,8 @@ __global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
       const int dc = q4 + 4 * it;
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
-        const uint32_t lo = (vx[it][t2] & 0xffffu) | (vy[it][t2] << 16);
-        const uint32_t hi = (vx[it][t2] >> 16) | (vy[it][t2] & 0xffff0000u);
+        const uint32_t lo = (cur.vx[it][t2] & 0xffffu) | (cur.vy[it][t2] << 16);
+        const uint32_t hi = (cur.vx[it][t2] >> 16) | (cur.vy[it][t2] & 0xffff0000u);
         *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2) * kKdVtStride + l16 * 4) = lo;
         *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2 + 1) * kKdVtStride + l16 * 4) = hi;
       }
@@ -1049,30 +1091,35 @@ __global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
       mma16(o[dt], af, pf);
     }
     __builtin_amdgcn_wave_barrier();
+    cur = nxt;
+    u = un;
   }
-  // o[dt][v]: d = dt*16 + 4*q4 + v, head l16.  Combine the 4 waves in LDS.
+  // o[dt][v]: d = dt*16 + 4*q4 + v, head l16.  Combine the NW waves in LDS
+  // (each wave's slab now holds its output rows).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* ow = reinterpret_cast<float*>(vt);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) olds[wave][l16][dt * 16 + 4 * q4 + v] = o[dt][v];
+    for (int v = 0; v < 4; ++v) ow[l16 * (D + 1) + dt * 16 + 4 * q4 + v] = o[dt][v];
   if (q4 == 0) {
     llds[wave][l16] = (lrun > 0.0f) ? mrun * a.sm_scale + __builtin_amdgcn_logf(lrun) * kLn2 : -__builtin_inff();
+    lrs[wave][l16] = lrun;
   }
-  // store unnormalised o with its own lse: rescale below with exp(lse_w - M) / l_w
-  __shared__ float lrs[4][16];
-  if (q4 == 0) lrs[wave][l16] = lrun;
   __syncthreads();
-  for (int x = threadIdx.x; x < G * D; x += 256) {
+  for (int x = threadIdx.x; x < G * D; x += NW * 64) {
     const int g = x / D, d = x % D;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, llds[w][g]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, llds[w][g]);
     float acc = 0.0f, wsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       if (lrs[w][g] > 0.0f) {
         const float ww = fast_exp2((llds[w][g] - mx) * kLog2e);
-        acc += ww * olds[w][g][d] / lrs[w][g];
+        acc += ww * reinterpret_cast<const float*>(slab[w])[g * (D + 1) + d] / lrs[w][g];
         wsum += ww;
       }
     }
@@ -1089,28 +1136,39 @@ __global__ __launch_bounds__(256) void kd_kernel(KdArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void kd_merge_kernel(KdArgs a, int D) {
-  const int sr = blockIdx.x;
-  const int s = sr / a.h_kv, r = sr % a.h_kv;
+// LSE merge of the splits: one workgroup of D threads per (sequence, group,
+// head); every split's lse and value are loaded up front.
+template <int D>
+__global__ __launch_bounds__(D) void kd_merge_kernel(KdArgs a) {
   const int G = a.group;
-  for (int x = threadIdx.x; x < G * D; x += 256) {
-    const int g = x / D, d = x % D;
-    float mx = -__builtin_inff();
-    for (int k = 0; k < a.split; ++k) mx = fmaxf(mx, a.part_lse[((size_t)sr * a.split + k) * G + g]);
-    float acc = 0.0f, wsum = 0.0f;
-    for (int k = 0; k < a.split; ++k) {
-      const size_t pidx = ((size_t)sr * a.split + k) * G + g;
-      const float l = a.part_lse[pidx];
-      if (l == -__builtin_inff()) continue;
-      const float ww = fast_exp2((l - mx) * kLog2e);
-      acc += ww * a.part_o[pidx * D + d];
-      wsum += ww;
+  const int sr = blockIdx.x / G, g = blockIdx.x % G;
+  const int s = sr / a.h_kv, r = sr % a.h_kv;
+  const int d = threadIdx.x;
+  const size_t base = (size_t)sr * a.split * G + g;   // + k * G for split k
+  float l[kMaxTopK], x[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    l[k] = -__builtin_inff();
+    x[k] = 0.0f;
+    if (k < a.split) {
+      l[k] = scalar_load(a.part_lse, (int64_t)(base + (size_t)k * G));
+      x[k] = a.part_o[(base + (size_t)k * G) * D + d];
     }
-    bf16_t* out = static_cast<bf16_t*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
-    *out = from_f32<bf16_t>(wsum > 0.0f ? acc / wsum : 0.0f);
-    if (a.lse && d == 0)
-      a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
   }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) mx = fmaxf(mx, l[k]);
+  float acc = 0.0f, wsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const float ww = (l[k] == -__builtin_inff()) ? 0.0f : fast_exp2((l[k] - mx) * kLog2e);
+    acc = fmaf(ww, x[k], acc);
+    wsum += ww;
+  }
+  bf16_t* out = static_cast<bf16_t*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
+  *out = from_f32<bf16_t>(wsum > 0.0f ? acc / wsum : 0.0f);
+  if (a.lse && d == 0)
+    a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
 }
 
 // ====================================================================
@@ -1325,7 +1383,9 @@ DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, in
   const int pairs = batch * h_kv;
   int split = 1;
   // aim for >= ~1024 workgroups of 4 waves; each wave takes whole 32-key units
-  while (split < 16 && (int64_t)pairs * split < 1024 && split * 4 < top_k * 4) split <<= 1;
+  // workgroups of kKdWaves waves; aim for >= 256 of them (one per CU) while
+  // every wave keeps at least one 32-key unit
+  while (split * kKdWaves < top_k * 4 && (int64_t)pairs * split < 256) split <<= 1;
   const int env = env_int("MSA_KD_SPLIT", 0);
   if (env > 0) split = std::min(16, env);
   p.split = split;
@@ -1359,10 +1419,10 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.max_pages = a.max_pages;
   k.split = pl.split;
   k.sm_scale = a.sm_scale;
-  hipLaunchKernelGGL((kd_kernel<D>), dim3(a.batch * a.h_kv * pl.split), dim3(256), 0, st, k);
+  hipLaunchKernelGGL((kd_kernel<D, kKdWaves>), dim3(a.batch * a.h_kv * pl.split), dim3(kKdWaves * 64), 0, st, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.split == 1) return e;
-  hipLaunchKernelGGL(kd_merge_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, st, k, D);
+  hipLaunchKernelGGL((kd_merge_kernel<D>), dim3(a.batch * a.h_kv * a.group), dim3(D), 0, st, k);
   return hipGetLastError();
 }
 

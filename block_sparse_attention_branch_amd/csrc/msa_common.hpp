@@ -154,6 +154,14 @@ __device__ __forceinline__ void write_row_list(const uint64_t (&keys)[L], int n_
   }
 }
 
+// Uniform reads through the constant address space become scalar loads (they
+// count against lgkmcnt, so they never wait for outstanding vector stores).
+template <typename U>
+__device__ __forceinline__ U scalar_load(const U* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) U* CP;
+  return ((CP)p)[i];
+}
+
 // --------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_xor_f32(float x, int mask) { return __shfl_xor(x, mask, 64); }
 

@@ -221,11 +221,22 @@ __global__ __launch_bounds__(256) void ki_merge_kernel(KiPrefillArgs a) {
 }
 
 // ------------------------------------------------------------ decode kernels
+// One 128-key page of index keys as 16x16x32 B fragments: kt-th 16-key
+// slice, keys on the MFMA columns.
+template <typename T, int DIDX>
+__device__ __forceinline__ void ki_load_page(Frag<T> (&f)[8][DIDX / 32], const T* kp) {
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < DIDX / 32; ++ks) f[kt][ks] = load_frag<T>(kp + (kt * 16 + l16) * DIDX + ks * 32 + q4 * 8);
+}
+
 template <typename T, int DIDX>
 __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   constexpr int KS = DIDX / 32;
   const int s = blockIdx.y;
-  const int L = a.seq_lens[s];
+  const int L = scalar_load(a.seq_lens, s);
   const int p = L - 1;
   const int nb = (L + kBlock - 1) / kBlock;
   const int hi = (a.need_diag || !a.force_local) ? nb : nb - 1;
@@ -242,21 +253,23 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ks * 32 + q4 * 8)
                             : zero_frag<T>();
   const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
-  for (int pg = pg_begin + wave; pg < pg_end; pg += 4) {
-    const T* kp = k_idx + (size_t)pt[pg] * kBlock * DIDX;
-    Frag<T> bfr[8][KS];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bfr[kt][ks] = load_frag<T>(kp + (kt * 16 + l16) * DIDX + ks * 32 + q4 * 8);
+  // For rows of up to 128 bytes the next page's index keys are loaded while
+  // the current page is scored (wider rows would not fit two pages).
+  constexpr bool kPipe = sizeof(T) * DIDX <= 128;
+  Frag<T> cur[8][KS], nxt[8][KS];
+  int pg = pg_begin + wave;
+  if (kPipe && pg < pg_end) ki_load_page<T, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
+  for (; pg < pg_end; pg += 4) {
+    if (!kPipe) ki_load_page<T, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
+    if (kPipe && pg + 4 < pg_end)
+      ki_load_page<T, DIDX>(nxt, k_idx + (size_t)scalar_load(pt, pg + 4) * kBlock * DIDX);
     float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
     const bool masked = (pg == nb - 1);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], bfr[kt][ks]);
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], cur[kt][ks]);
       const bool vis = !masked || (pg * kBlock + kt * 16 + l16 <= p);
 #pragma unroll
       for (int v = 0; v < 4; ++v) m[v] = fmaxf(m[v], vis ? acc[v] : -__builtin_inff());
@@ -273,72 +286,81 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
         if (g < a.h_kv) a.scores[((size_t)s * a.h_kv + g) * a.max_pages + pg] = m[v] * a.idx_scale;
       }
     }
-  }
-}
-
-// Descending bitonic sort of n (power of two) keys in LDS by the whole block.
-__device__ void lds_bitonic_desc(uint64_t* x, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t u = x[i], w = x[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (u < w) : (u > w)) {
-            x[i] = w;
-            x[ixj] = u;
-          }
-        }
-      }
-      __syncthreads();
+    if (kPipe) {
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cur[kt][ks] = nxt[kt][ks];
     }
   }
 }
 
-constexpr int kSelectMaxSurvivors = 1024;  // 16 lists x up to 64 candidates per thread
+constexpr int kSelectMaxSurvivors = 1024;  // 16 threads x up to 64 candidates each
 
+// Top-k of one (sequence, group) row of pooled page scores.  Keys are the
+// order-preserving bits of the score with the inverted block id below them,
+// so they are unique and "larger" means better (ties to the lower block).
+//  1) each thread takes the maximum of its candidates; the 16th largest of
+//     the 256 maxima T is a lower bound of the answer: the 16 threads whose
+//     maxima are >= T each hold a key >= T, so the 16 best keys are all >= T;
+//  2) every key >= T survives (only those 16 threads hold any);
+//  3) each survivor's rank among the survivors places the best 16 in order.
+// Ranks are counted against values in LDS, so the selection needs no sort
+// and only a few barriers.
 __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
-  __shared__ uint64_t sh[kSelectMaxSurvivors];
+  __shared__ uint64_t tm[256];
+  __shared__ uint64_t surv[kSelectMaxSurvivors];
+  __shared__ uint64_t top[kMaxTopK];
+  __shared__ uint64_t thr_s;
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
-  const int L = a.seq_lens[s];
+  const int L = scalar_load(a.seq_lens, s);
   const int diag = (L - 1) / kBlock;
   const int ncand = a.force_local ? diag : diag + 1;
   const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
   const int tid = threadIdx.x;
 
-  // 1) per-thread maxima; the 16th largest of them bounds the answer from below
   uint64_t tmax = 0;
   for (int b = tid; b < ncand; b += 256) {
     const uint64_t k = make_key(sc[b], b);
     tmax = k > tmax ? k : tmax;
   }
-  sh[tid] = tmax;
-  if (tid == 0) count = 0;
+  tm[tid] = tmax;
+  if (tid == 0) {
+    count = 0;
+    thr_s = 0;
+  }
+  if (tid < kMaxTopK) top[tid] = 0;
   __syncthreads();
-  lds_bitonic_desc(sh, 256);
-  const uint64_t thr = sh[kMaxTopK - 1];
+  int rank = 0;
+  for (int i = 0; i < 256; ++i) rank += tm[i] > tmax ? 1 : 0;
+  // With fewer than 16 non-empty threads nobody (or only empty threads, with
+  // key 0) has rank 15 and the bound stays 0: every candidate survives.
+  if (rank == kMaxTopK - 1) thr_s = tmax;
   __syncthreads();
-  // 2) every candidate at or above the bound survives (at most 16 threads own one)
-  for (int b = tid; b < ncand; b += 256) {
-    const uint64_t k = make_key(sc[b], b);
-    if (k >= thr) {
-      const int pos = atomicAdd(&count, 1);
-      if (pos < kSelectMaxSurvivors) sh[pos] = k;
+  const uint64_t thr = thr_s;
+  if (tmax >= thr && tmax != 0) {
+    for (int b = tid; b < ncand; b += 256) {
+      const uint64_t k = make_key(sc[b], b);
+      if (k >= thr) {
+        const int pos = atomicAdd(&count, 1);
+        if (pos < kSelectMaxSurvivors) surv[pos] = k;
+      }
     }
   }
   __syncthreads();
   const int n = min(count, kSelectMaxSurvivors);
-  int n2 = 16;
-  while (n2 < n) n2 <<= 1;
-  for (int i = n + tid; i < n2; i += 256) sh[i] = 0ull;
+  for (int i = tid; i < n; i += 256) {
+    const uint64_t k = surv[i];
+    int rk = 0;
+    for (int j = 0; j < n; ++j) rk += surv[j] > k ? 1 : 0;
+    if (rk < kMaxTopK) top[rk] = k;
+  }
   __syncthreads();
-  lds_bitonic_desc(sh, n2);
   if (tid == 0) {
     uint64_t keys[kMaxTopK];
 #pragma unroll
-    for (int t = 0; t < kMaxTopK; ++t) keys[t] = sh[t];
+    for (int t = 0; t < kMaxTopK; ++t) keys[t] = top[t];
     float dscore = -__builtin_inff();
     if (a.force_local && a.need_diag) dscore = sc[diag];
     const int n_take = a.top_k - (a.force_local ? 1 : 0);
