@@ -99,14 +99,133 @@ class CallTimer:
         return float(np.percentile(self.records[n], q))
 
 
-def roofline(bound, work, ms, unit):
+def roofline(bound, work, ms, unit, call=None, workload="step"):
     peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
     if unit == "TFLOP/s":
         achieved = work / (ms * 1e-3) / 1e12
     else:
         achieved = work / (ms * 1e-3) / 1e9
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None}
+            "frac": round(achieved / peak, 4), "traffic": traffic_bytes(workload, call)}
+
+
+# ------------------------------------------------------------- HBM traffic
+#
+# Measured HBM bytes per ABI call come from two rocprofv3 counter runs of this
+# script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+# the same counter reads for a plain device-to-device copy of known size
+# (``--workload copy``).  ``--summarize-traffic`` turns the four CSV files into
+# profiles/traffic.json, stamped with a hash of the kernel sources; the bench
+# reports null once the sources have changed since.
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30
+# kernels of each ABI call (substring of the kernel name)
+CALL_KERNELS = {
+    "index_prefill": ["ki_prefill_kernel", "ki_merge_kernel"],
+    "sparse_prefill": ["ks_zero_kernel", "ks_count_kernel", "ks_scan_a_kernel", "ks_scan_b_kernel",
+                       "ks_scan_c_kernel", "ks_scatter_kernel", "ks_items_kernel", "kp_kernel", "km_kernel"],
+    "index_decode": ["ki_decode_scan_kernel", "ki_decode_select_kernel"],
+    "sparse_decode": ["kd_kernel", "kd_merge_kernel"],
+}
+CALL_FIRST = {"index_prefill": "ki_prefill_kernel", "sparse_prefill": "ks_zero_kernel",
+              "index_decode": "ki_decode_scan_kernel", "sparse_decode": "kd_kernel"}
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_branch_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "msa.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload, call):
+    if call is None or not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        return None
+    rec = t.get("workloads", {}).get(workload, {}).get(call)
+    return None if rec is None else rec["bytes"]
+
+
+def _pmc_rows(path, counter):
+    import csv
+    out = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return out
+
+
+def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Per-call HBM bytes from rocprofv3 counter CSVs; writes profiles/traffic.json."""
+    def per_dispatch(path, counter):
+        d = {}
+        for name, did, v in _pmc_rows(path, counter):
+            d[did] = (name, d.get(did, (name, 0.0))[1] + v)
+        return list(d.values())
+
+    def copy_factor(path, counter):
+        vals = [v for n, v in per_dispatch(path, counter) if "copy" in n.lower()]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {path}")
+        kib = float(np.median(vals))
+        return (COPY_BYTES / 1024.0) / kib, kib
+
+    ff, fk = copy_factor(copy_fetch_csv, "FETCH_SIZE")
+    wf, wk = copy_factor(copy_write_csv, "WRITE_SIZE")
+    res = {}
+    for call, kernels in CALL_KERNELS.items():
+        tot = {}
+        for key, path, counter, fac in (("fetch", fetch_csv, "FETCH_SIZE", ff), ("write", write_csv, "WRITE_SIZE", wf)):
+            rows = per_dispatch(path, counter)
+            n_calls = sum(1 for n, _ in rows if CALL_FIRST[call] in n)
+            if n_calls == 0:
+                break
+            kib = sum(v for n, v in rows if any(k in n for k in kernels))
+            tot[key] = kib * 1024.0 * fac / n_calls
+        if len(tot) == 2:
+            res[call] = {"fetch_bytes": round(tot["fetch"]), "write_bytes": round(tot["write"]),
+                         "bytes": round(tot["fetch"] + tot["write"])}
+    t = {}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
+            t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        t = {"workloads": {}}
+    t["source_hash"] = source_hash()
+    t["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_read": fk, "write_kib_read": wk,
+                             "fetch_factor": ff, "write_factor": wf}
+    t["workloads"][workload] = res
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(t, fh, indent=1)
+    print(json.dumps(t))
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of COPY_BYTES (counter calibration)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(max(1, args.steps)):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(1, args.steps)
+    print(json.dumps({"workload": "copy", "bytes": COPY_BYTES, "ms": round(ms, 4),
+                      "read_plus_write_GBs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}))
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -170,10 +289,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m"])
+    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                             "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json for --workload from rocprofv3 counter CSVs (no GPU)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, *args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library has no "
               "multi-GPU path (it would shard by KV group, decode batch or KV-block range).", file=sys.stderr)
@@ -183,7 +308,9 @@ def main():
         sys.exit(1)
     from block_sparse_attention_branch_amd import msa
     msa.lib()
-    if args.workload == "step":
+    if args.workload == "copy":
+        bench_copy(args)
+    elif args.workload == "step":
         bench_step(msa, args)
     elif args.workload == "prefill128k":
         bench_prefill_only(msa, args, planted=True)
@@ -250,11 +377,14 @@ def bench_step(msa, args):
     idx_fl, main_fl, dense_fl = prefill_counts(n, 0, shape)
     didx_b, dmain_b, ddense_b = decode_bytes([131072] * B, shape)
     rl = {
-        "index_prefill": dict(roofline("mfma", idx_fl, t_ip, "TFLOP/s"), kernel="ki_prefill_kernel+ki_merge_kernel"),
-        "sparse_prefill": dict(roofline("mfma", main_fl, t_sp, "TFLOP/s"),
+        "index_prefill": dict(roofline("mfma", idx_fl, t_ip, "TFLOP/s", "index_prefill"),
+                              kernel="ki_prefill_kernel+ki_merge_kernel"),
+        "sparse_prefill": dict(roofline("mfma", main_fl, t_sp, "TFLOP/s", "sparse_prefill"),
                                kernel="ks_* schedule + kp_kernel + km_kernel (per window)"),
-        "index_decode": dict(roofline("hbm", didx_b, t_id, "GB/s"), kernel="ki_decode_scan_kernel+ki_decode_select_kernel"),
-        "sparse_decode": dict(roofline("hbm", dmain_b, t_sd, "GB/s"), kernel="kd_kernel+kd_merge_kernel"),
+        "index_decode": dict(roofline("hbm", didx_b, t_id, "GB/s", "index_decode"),
+                             kernel="ki_decode_scan_kernel+ki_decode_select_kernel"),
+        "sparse_decode": dict(roofline("hbm", dmain_b, t_sd, "GB/s", "sparse_decode"),
+                              kernel="kd_kernel+kd_merge_kernel"),
     }
     for k_, ms_ in (("index_prefill", t_ip), ("sparse_prefill", t_sp), ("index_decode", t_id), ("sparse_decode", t_sd)):
         rl[k_]["ms"] = round(ms_, 4)

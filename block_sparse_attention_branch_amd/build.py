@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# per-file extras: the index kernel reads its MFMA accumulators with VALU max
+# operations, so they are kept in VGPRs (no accumulator-register copies)
+FILE_FLAGS = {"msa_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -36,7 +39,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     for src in SOURCES:
         obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
         if r.returncode != 0:

@@ -199,14 +199,6 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
   }
 }
 
-// Keeps the scheduler from hoisting every unrolled LDS fragment load to the
-// top of a loop nest (which costs registers and forces spills).
-#ifndef MSA_NO_SCHED_FENCE
-#define MSA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define MSA_SCHED_FENCE() do {} while (0)
-#endif
-
 // Store 8 consecutive values (one 16-byte store for bf16, two for fp32).
 template <typename T>
 __device__ __forceinline__ void store8(T* dst, const f32x16& o, int base) {

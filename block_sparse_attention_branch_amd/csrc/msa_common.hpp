@@ -105,18 +105,19 @@ __device__ __forceinline__ float key_score(uint64_t k) {
 }
 
 // Insert v into the descending list `keys` (capacity L, unique keys).
-// The caller checks v > keys[L-1]; the last entry falls off.
+// The caller checks v > keys[L-1]; the last entry falls off.  Slot s becomes
+// max(keys[s], min(keys[s-1], v)): entries above v stay, v lands where the
+// first smaller entry was, and the smaller ones shift down by one.  Every
+// slot is computed from the old list, so there is no serial chain.
 template <int L>
 __device__ __forceinline__ void list_insert(uint64_t (&keys)[L], uint64_t v) {
-  bool prev_better = true;
-  uint64_t prev = 0;
+  uint64_t prev = ~0ull;
 #pragma unroll
   for (int s = 0; s < L; ++s) {
     const uint64_t cur = keys[s];
-    const bool better = cur > v;
-    keys[s] = better ? cur : (prev_better ? v : prev);
+    const uint64_t m = prev < v ? prev : v;
+    keys[s] = cur > m ? cur : m;
     prev = cur;
-    prev_better = better;
   }
 }
 
@@ -161,6 +162,15 @@ __device__ __forceinline__ U scalar_load(const U* p, int64_t i) {
   typedef const __attribute__((address_space(4))) U* CP;
   return ((CP)p)[i];
 }
+
+// Keeps the scheduler from hoisting every unrolled LDS fragment load (or
+// every MFMA of a loop nest) to the top, which costs registers and forces
+// spills or accumulator-register traffic.
+#ifndef MSA_NO_SCHED_FENCE
+#define MSA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define MSA_SCHED_FENCE() do {} while (0)
+#endif
 
 // --------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_xor_f32(float x, int mask) { return __shfl_xor(x, mask, 64); }

@@ -137,7 +137,9 @@ __global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a)
     const char* K = lds[buf];
     const bool masked = b >= min_diag;
     float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
+    // not unrolled: an unrolled nest keeps every tile's addresses and mask
+    // constants live and halves the occupancy
+#pragma unroll 1
     for (int kt = 0; kt < 4; ++kt) {
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
