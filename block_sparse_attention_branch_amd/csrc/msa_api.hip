@@ -194,6 +194,8 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   a.n_kv = kv->n_kv;
   a.chunk_blocks = p.chunk_blocks;
   a.n_chunks = p.n_chunks;
+  a.grid_chunks = p.grid_chunks;
+  a.xcd_major = p.xcd_major;
   a.n_tiles = p.n_tiles;
   a.idx_scale = idx_scale;
   a.force_local = s.force_local;

@@ -25,6 +25,8 @@
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
 
+#include <cstdlib>
+
 namespace msa {
 
 constexpr int kKiThreads = 256;
@@ -38,6 +40,7 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
   if (p.n_tiles == 0) {
     p.chunk_blocks = 1;
     p.n_chunks = 1;
+    p.grid_chunks = 1;
     return p;
   }
   // blocks that need scoring in the last (longest) tile, and in total
@@ -48,10 +51,27 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
   const int64_t hi_last = hi_of(p.n_tiles - 1);
   const int64_t hi_first = hi_of(0);
   const int64_t work = (hi_first + hi_last) * p.n_tiles / 2 + 1;
+  // Blocks per chunk: long enough to amortise a workgroup's set-up and its
+  // partial list, short enough for ~`target` workgroups in all.
+  const char* env = getenv("MSA_KI_WORK");
+  const int64_t target = (env && atoi(env) > 0) ? atoi(env) : 512;
   int64_t cb = std::max<int64_t>(8, (hi_last + 63) / 64);
-  cb = std::max<int64_t>(cb, (work + 4095) / 4096);
+  cb = std::max<int64_t>(cb, (work + target - 1) / target);
+  int64_t nch = std::max<int64_t>(1, (hi_last + cb - 1) / cb);
+  if (nch >= 8) {
+    // one chunk per XCD at a time: the tiles of a chunk share its K_idx
+    // range in that XCD's L2
+    nch = (nch + 7) & ~int64_t(7);
+    cb = (hi_last + nch - 1) / nch;
+    nch = (hi_last + cb - 1) / cb;
+    p.xcd_major = 1;
+    p.grid_chunks = static_cast<int32_t>((nch + 7) & ~int64_t(7));
+  } else {
+    p.xcd_major = 0;
+    p.grid_chunks = static_cast<int32_t>(nch);
+  }
   p.chunk_blocks = static_cast<int32_t>(cb);
-  p.n_chunks = static_cast<int32_t>(std::max<int64_t>(1, (hi_last + cb - 1) / cb));
+  p.n_chunks = static_cast<int32_t>(nch);
   return p;
 }
 
@@ -66,8 +86,18 @@ __global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a)
   static_assert(LOADS >= 1 && (128 * CHUNKS_PER_ROW) % kKiThreads == 0, "staging split");
   __shared__ __attribute__((aligned(16))) char lds[2][128 * LDS_STRIDE];
 
-  const int tile = a.n_tiles - 1 - (int)blockIdx.y;  // longest tiles first
-  const int chunk = blockIdx.x;
+  // Workgroups run chunk-major, so the tiles scoring one K_idx range run
+  // together; with xcd_major, chunk c's workgroups all land on XCD c % 8.
+  int chunk, tile_i;
+  if (a.xcd_major) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    chunk = x + 8 * (k / a.n_tiles);
+    tile_i = k % a.n_tiles;
+  } else {
+    chunk = blockIdx.x / a.n_tiles;
+    tile_i = blockIdx.x % a.n_tiles;
+  }
+  const int tile = a.n_tiles - 1 - tile_i;  // longest tiles first
   const int row0 = tile * kKiRowsPerTile;
   const int row_last = min(row0 + kKiRowsPerTile - 1, a.n_rows - 1);
   const int min_diag = (a.q_start + row0 / a.h_kv) >> 7;
@@ -375,7 +405,7 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
 // ----------------------------------------------------------------- launch
 template <typename T, int DIDX>
 static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
-  dim3 grid(a.n_chunks, a.n_tiles);
+  const dim3 grid((unsigned)((int64_t)a.grid_chunks * a.n_tiles));
   hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX>), grid, dim3(kKiThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;

@@ -20,7 +20,9 @@ struct KiPrefillArgs {
   int32_t q_start;
   int32_t n_kv;
   int32_t chunk_blocks;
-  int32_t n_chunks;         // chunks of the longest tile (grid.x)
+  int32_t n_chunks;         // chunks of the longest tile
+  int32_t grid_chunks;      // chunk slots in the grid (n_chunks rounded up to 8 when xcd_major)
+  int32_t xcd_major;        // chunk c runs on XCD c % 8 (all its tiles share that L2)
   int32_t n_tiles;
   float idx_scale;
   int32_t force_local;
@@ -53,7 +55,7 @@ struct KiDecodeArgs {
 // Host-side tiling rule of the prefill index kernel, shared with the
 // workspace-size query so both agree.
 struct KiPlan {
-  int32_t n_rows, n_tiles, chunk_blocks, n_chunks;
+  int32_t n_rows, n_tiles, chunk_blocks, n_chunks, grid_chunks, xcd_major;
 };
 KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_diag);
 
