@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import msa_oracle as orc
-from synth import MODEL_SHAPE, TINY_SHAPE, gen_decode_paged, gen_prefill
+from synth import MODEL_SHAPE, TINY_SHAPE, gen_decode_paged, gen_long_context, gen_prefill
 from synth.inputs import HeadShape
 
 from _helpers import compare_index_rows, compare_lse, compare_out, np64
@@ -245,3 +245,144 @@ def test_full_size_prefill_32k_sampled_rows():
     o_ref = np.stack([orc.sparse_attention(q_rows[t:t + 1], k64, v64, g_ids[t:t + 1], int(i))[0][0]
                       for t, i in enumerate(rows)])
     compare_out(o[torch.from_numpy(rows).to(DEV)], o_ref, torch.bfloat16)
+
+
+def test_full_size_decode_64x128k_sampled_sequences():
+    """Decode step at the benchmark shape (64 x 131072 paged, random page
+    table), in the benchmark's launch configuration; 3 sequences checked."""
+    msa = _msa()
+    shape = MODEL_SHAPE
+    inp = gen_decode_paged(64, 131072, shape, seed=3, device=DEV)
+    _say("decode 64 x 128K full size")
+    q_idx = inp["q_idx"][0].contiguous()
+    q = inp["q"][0].contiguous()
+    bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=16, page_table=inp["page_table"],
+                          seq_lens=inp["seq_lens"])
+    o, lse = msa.sparse_decode(q, inp["k_pages"], inp["v_pages"], inp["page_table"], inp["seq_lens"], bidx,
+                               with_lse=True)
+    torch.cuda.synchronize()
+    g_ids = bidx.cpu().numpy()
+    L = 131072
+    local_pt = np.arange(L // 128)[None, :]
+    for s in (0, 21, 63):
+        pages = inp["page_table"][s].long()
+        kp = np64(inp["k_pages"][pages])
+        vp = np64(inp["v_pages"][pages])
+        ip = np64(inp["k_idx_pages"][pages])
+        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx[s:s + 1]), ip, local_pt, [L], 16)
+        compare_index_rows(g_ids[s:s + 1], o_ids, pooled, [(L - 1) // 128])
+        o_ref, lse_ref = orc.sparse_decode(np64(q[s:s + 1]), kp, vp, local_pt, [L], g_ids[s:s + 1])
+        compare_out(o[s:s + 1], o_ref, torch.bfloat16)
+        compare_lse(lse[s:s + 1], lse_ref, torch.bfloat16)
+
+
+def test_full_size_prefill_128k_planted():
+    """131072-token prefill with planted index keys: every designated query
+    of every group retrieves its 3 planted blocks; sampled rows match the
+    oracle (index lists and outputs)."""
+    from synth import gen_planted_prefill
+    msa = _msa()
+    shape = MODEL_SHAPE
+    n = 131072
+    inp = gen_planted_prefill(n, shape, device=DEV)
+    _say("128K planted prefill full size")
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx)
+    torch.cuda.synchronize()
+    g_ids = bidx.cpu().numpy()
+    des = inp["designated"].numpy()
+    for r in range(shape.h_kv):
+        planted = set(inp["planted_blocks"][r].tolist())
+        for i in des:
+            assert planted <= set(g_ids[i, r].tolist()), (r, int(i), g_ids[i, r], planted)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([des[:6], rng.choice(n, 12, replace=False), [0, 129, n - 1]]))
+    o_ids, _, pooled = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), 0, 16, rows=rows)
+    compare_index_rows(g_ids[rows], o_ids, pooled, rows // 128)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    k64, v64 = np64(inp["k"]), np64(inp["v"])
+    q_rows = np64(inp["q"][rows_t])
+    o_ref = np.stack([orc.sparse_attention(q_rows[t:t + 1], k64, v64, g_ids[rows][t:t + 1], int(i))[0][0]
+                      for t, i in enumerate(rows)])
+    compare_out(o[rows_t], o_ref, torch.bfloat16)
+
+
+def _selected_tokens(k_pages, v_pages, page_row, ids_row, p, r):
+    """Keys/values of group r over the listed blocks (ascending), visible up
+    to position p, gathered from a paged cache, and the query position
+    inside that gathered run.  Eq. (8) reads nothing else, so attending over
+    this run equals attending over the whole sequence with the same list."""
+    blocks = sorted(int(b) for b in set(ids_row.tolist()) if b >= 0 and b * 128 <= p)
+    pages = torch.tensor([int(page_row[b]) for b in blocks], dtype=torch.long, device=k_pages.device)
+    kb = np64(k_pages[pages, r].reshape(-1, k_pages.shape[-1]))   # [nb * 128, d]
+    vb = np64(v_pages[pages, r].reshape(-1, v_pages.shape[-1]))
+    n_vis = 128 * (len(blocks) - 1) + (p - 128 * blocks[-1]) + 1
+    return kb[:n_vis], vb[:n_vis], len(blocks)
+
+
+def _oracle_rows_paged(q_rows, k_pages, v_pages, page_row, ids_rows, positions, h_kv):
+    """orc.sparse_attention per (row, group) on the gathered selected run."""
+    h_q = q_rows.shape[1]
+    G = h_q // h_kv
+    o_all = np.empty(q_rows.shape)
+    lse_all = np.empty(q_rows.shape[:2])
+    for t, p in enumerate(positions):
+        for r in range(h_kv):
+            kb, vb, nb = _selected_tokens(k_pages, v_pages, page_row, ids_rows[t, r], int(p), r)
+            local = np.arange(nb, dtype=np.int64)[None, None, :]
+            qg = q_rows[t:t + 1, r * G:(r + 1) * G]
+            o, lse = orc.sparse_attention(qg, kb[:, None, :], vb[:, None, :], local, kb.shape[0] - 1)
+            o_all[t, r * G:(r + 1) * G] = o[0]
+            lse_all[t, r * G:(r + 1) * G] = lse[0]
+    return o_all, lse_all
+
+
+def test_long_context_1m_chunked_prefill_and_decode_sampled():
+    """1,048,576-token paged cache: chunked prefill of the last 8192 queries
+    (sampled rows checked) and the first two decode steps, each appending
+    its token first (both checked)."""
+    msa = _msa()
+    shape = MODEL_SHAPE
+    lc = gen_long_context(device=DEV)
+    n_ctx, q_start = lc["n_ctx"], lc["q_start"]
+    pt = lc["page_table"]
+    _say("1M chunked prefill + decode")
+    bidx = msa.index_topk(lc["chunk_q_idx"], lc["k_idx_pages"], top_k=16, q_start=q_start, page_table=pt[0],
+                          n_kv=n_ctx)
+    o = msa.sparse_prefill(lc["chunk_q"], lc["k_pages"], lc["v_pages"], bidx, q_start=q_start, page_table=pt[0],
+                           n_kv=n_ctx)
+    torch.cuda.synchronize()
+    g_ids = bidx.cpu().numpy()
+    pt_row = pt[0].cpu().numpy()
+    seq = orc.gather_sequence(pt_row, n_ctx, k_idx_pages=lc["k_idx_pages"].float().cpu().numpy())
+    rng = np.random.default_rng(5)
+    nq = lc["chunk_q"].shape[0]
+    rows = np.unique(np.concatenate([rng.choice(nq, 10, replace=False), [0, 1, 127, nq - 1]]))
+    o_ids, _, pooled = orc.index_topk(np64(lc["chunk_q_idx"]), seq["k_idx"], q_start, 16, rows=rows)
+    compare_index_rows(g_ids[rows], o_ids, pooled, (q_start + rows) // 128)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    o_ref, _ = _oracle_rows_paged(np64(lc["chunk_q"][rows_t]), lc["k_pages"], lc["v_pages"], pt_row,
+                                  g_ids[rows], q_start + rows, shape.h_kv)
+    compare_out(o[rows_t], o_ref, torch.bfloat16)
+    # two decode steps
+    seq_lens = torch.tensor([n_ctx], dtype=torch.int32, device=DEV)
+    k_idx_host = seq["k_idx"]
+    for t in range(2):
+        pos = n_ctx + t
+        page = pt[0, pos // 128].long()
+        lc["k_pages"][page, :, pos % 128] = lc["step_k"][t]
+        lc["v_pages"][page, :, pos % 128] = lc["step_v"][t]
+        lc["k_idx_pages"][page, pos % 128] = lc["step_k_idx"][t]
+        seq_lens.fill_(pos + 1)
+        db = msa.index_topk(lc["step_q_idx"][t], lc["k_idx_pages"], top_k=16, page_table=pt, seq_lens=seq_lens)
+        do, dl = msa.sparse_decode(lc["step_q"][t], lc["k_pages"], lc["v_pages"], pt, seq_lens, db,
+                                   with_lse=True)
+        torch.cuda.synchronize()
+        k_idx_host = np.concatenate([k_idx_host, np64(lc["step_k_idx"][t:t + 1])])
+        d_ids = db.cpu().numpy()
+        oi, _, dp = orc.index_topk(np64(lc["step_q_idx"][t][0:1]), k_idx_host, pos, 16)
+        compare_index_rows(d_ids, oi, dp, [pos // 128])
+        d_ref, l_ref = _oracle_rows_paged(np64(lc["step_q"][t]), lc["k_pages"], lc["v_pages"], pt_row,
+                                          d_ids, [pos], shape.h_kv)
+        compare_out(do, d_ref, torch.bfloat16)
+        compare_lse(dl, l_ref, torch.bfloat16)
