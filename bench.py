@@ -224,8 +224,20 @@ def bench_copy(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(1, args.steps)
+    # a read-only stream of 4 GiB (torch's sum), for the achievable read rate
+    big = torch.ones(4 * COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    big.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(max(1, args.steps)):
+        big.sum(dtype=torch.float32)
+    e1.record()
+    torch.cuda.synchronize()
+    rms = e0.elapsed_time(e1) / max(1, args.steps)
     print(json.dumps({"workload": "copy", "bytes": COPY_BYTES, "ms": round(ms, 4),
-                      "read_plus_write_GBs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}))
+                      "read_plus_write_GBs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1),
+                      "read_only_bytes": 4 * COPY_BYTES, "read_only_ms": round(rms, 4),
+                      "read_only_GBs": round(4 * COPY_BYTES / (rms * 1e-3) / 1e9, 1)}))
 
 
 # ------------------------------------------------------------ CPU baseline
