@@ -54,7 +54,7 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
   // Blocks per chunk: long enough to amortise a workgroup's set-up and its
   // partial list, short enough for ~`target` workgroups in all.
   const char* env = getenv("MSA_KI_WORK");
-  const int64_t target = (env && atoi(env) > 0) ? atoi(env) : 512;
+  const int64_t target = (env && atoi(env) > 0) ? atoi(env) : 1024;
   int64_t cb = std::max<int64_t>(8, (hi_last + 63) / 64);
   cb = std::max<int64_t>(cb, (work + target - 1) / target);
   int64_t nch = std::max<int64_t>(1, (hi_last + cb - 1) / cb);
@@ -77,7 +77,7 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
 
 // ----------------------------------------------------------- prefill kernel
 template <typename T, int DIDX>
-__global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a) {
+__global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs a) {
   constexpr int KS = DIDX / 16;                       // 16-wide contraction steps
   constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
   constexpr int LDS_STRIDE = ROW_BYTES + 16;          // padded row, bytes
@@ -135,35 +135,51 @@ __global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a)
   for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
   float diag_score = -__builtin_inff();
 
-  u32x4 pre[LOADS];
-  auto load_block = [&](int b) {
-    const int64_t base_tok = a.page_table ? (int64_t)a.page_table[b] * kBlock : (int64_t)b * kBlock;
+  // K_idx blocks are staged global -> registers -> LDS two blocks ahead.
+  // Thread i of the workgroup copies 16-byte pieces at fixed offsets of a
+  // block; only the partial last block of a contiguous cache clamps its rows
+  // (those keys lie after every query, so the causal mask drops them).
+  uint32_t toff[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + kKiThreads * i;
-      const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
-      const bool ok = a.page_table != nullptr || ((int64_t)b * kBlock + j < a.n_kv);
-      const char* src = reinterpret_cast<const char*>(k_idx + (base_tok + j) * DIDX) + c * 16;
-      pre[i] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < LOADS; ++i) {
+    const int u = tid + kKiThreads * i;
+    toff[i] = (uint32_t)((u / CHUNKS_PER_ROW) * ROW_BYTES + (u % CHUNKS_PER_ROW) * 16);
+  }
+  u32x4 pre0[LOADS], pre1[LOADS];
+  auto load_block = [&](u32x4 (&dst)[LOADS], int b) {
+    const int64_t base_tok = a.page_table ? (int64_t)scalar_load(a.page_table, b) * kBlock : (int64_t)b * kBlock;
+    const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX);
+    if (a.page_table || (int64_t)b * kBlock + kBlock <= a.n_kv) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dst[i] = *reinterpret_cast<const u32x4*>(base + toff[i]);
+    } else {
+      const uint32_t last = (uint32_t)(a.n_kv - 1 - b * kBlock);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t row = min(toff[i] / ROW_BYTES, last);
+        dst[i] = *reinterpret_cast<const u32x4*>(base + row * ROW_BYTES + toff[i] % ROW_BYTES);
+      }
     }
   };
-  auto store_block = [&](int buf) {
+  auto store_block = [&](const u32x4 (&src)[LOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int u = tid + kKiThreads * i;
       const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
-      *reinterpret_cast<u32x4*>(&lds[buf][j * LDS_STRIDE + c * 16]) = pre[i];
+      *reinterpret_cast<u32x4*>(&lds[buf][j * LDS_STRIDE + c * 16]) = src[i];
     }
   };
 
   if (b_begin < b_end) {
-    load_block(b_begin);
-    store_block(0);
+    load_block(pre0, b_begin);
+    store_block(pre0, 0);
   }
+  if (b_begin + 1 < b_end) load_block(pre0, b_begin + 1);
   __syncthreads();
-  for (int b = b_begin; b < b_end; ++b) {
+  // one block: `cur` holds block b + 1, `nxt` receives block b + 2
+  auto block_step = [&](int b, u32x4 (&cur)[LOADS], u32x4 (&nxt)[LOADS]) {
     const int buf = (b - b_begin) & 1;
-    if (b + 1 < b_end) load_block(b + 1);
+    if (b + 2 < b_end) load_block(nxt, b + 2);
     const char* K = lds[buf];
     const bool masked = b >= min_diag;
     float m0 = -__builtin_inff(), m1 = -__builtin_inff();
@@ -206,8 +222,13 @@ __global__ __launch_bounds__(kKiThreads) void ki_prefill_kernel(KiPrefillArgs a)
       }
       if (b == my_diag) diag_score = pooled;
     }
-    if (b + 1 < b_end) store_block(buf ^ 1);
+    if (b + 1 < b_end) store_block(cur, buf ^ 1);
     __syncthreads();
+  };
+  // unrolled by two so the register stages swap roles without copies
+  for (int b = b_begin; b < b_end; b += 2) {
+    block_step(b, pre0, pre1);
+    if (b + 1 < b_end) block_step(b + 1, pre1, pre0);
   }
 
   if (!my_valid) return;
