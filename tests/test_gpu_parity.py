@@ -132,6 +132,13 @@ def test_prefill_d64_group4_bf16():
     _prefill_case(HeadShape(8, 2, 64, 32, 4), 1300, 1300, torch.bfloat16, 11)
 
 
+def test_prefill_groups_of_1_2_and_8():
+    # every supported head-to-group ratio besides 4 and 16, both dtypes
+    _prefill_case(HeadShape(4, 4, 128, 64, 5), 1700, 1700, torch.bfloat16, 15)
+    _prefill_case(HeadShape(4, 2, 64, 32, 3), 900, 600, torch.float32, 16)
+    _prefill_case(HeadShape(16, 2, 128, 64, 16), 1400, 1400, torch.bfloat16, 17, use_gpu_index=True)
+
+
 def test_prefill_full_coverage_equals_dense():
     msa = _msa()
     shape = HeadShape(16, 2, 128, 64, 16)
@@ -218,6 +225,11 @@ def test_decode_mixed_lengths():
 
 def test_decode_batch_many_short():
     _decode_case(HeadShape(32, 4, 128, 64, 16), [700 + 37 * i for i in range(40)], 21)
+
+
+def test_decode_groups_of_1_and_8_d64():
+    _decode_case(HeadShape(4, 4, 128, 64, 7), [900, 129, 1], 23)
+    _decode_case(HeadShape(16, 2, 64, 32, 16), [5000, 2500], 24)
 
 
 def test_decode_single_long_sequence():
