@@ -156,6 +156,18 @@ def traffic_bytes(workload, call):
     return None if rec is None else rec["bytes"]
 
 
+def kernel_traffic(workload, kernel):
+    """Measured HBM bytes per launch of `kernel`, or None (see traffic_bytes)."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        return None
+    rec = t.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if rec is None else rec["bytes_per_launch"]
+
+
 def _pmc_rows(path, counter):
     import csv
     out = []
@@ -201,11 +213,22 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
         with open(TRAFFIC_JSON) as fh:
             t = json.load(fh)
     if t.get("source_hash") != source_hash():
-        t = {"workloads": {}}
+        t = {"workloads": {}, "kernels": {}}
     t["source_hash"] = source_hash()
     t["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_read": fk, "write_kib_read": wk,
                              "fetch_factor": ff, "write_factor": wf}
     t["workloads"][workload] = res
+    kres = {}
+    for kname in ("ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "kd_kernel"):
+        rec = {}
+        for key, path, counter, fac in (("fetch", fetch_csv, "FETCH_SIZE", ff), ("write", write_csv, "WRITE_SIZE", wf)):
+            vals = [v for n, v in per_dispatch(path, counter) if kname in n and "merge" not in n]
+            if vals:
+                rec[key] = float(np.mean(vals)) * 1024.0 * fac
+        if len(rec) == 2:
+            kres[kname] = {"fetch_bytes_per_launch": round(rec["fetch"]), "write_bytes_per_launch": round(rec["write"]),
+                           "bytes_per_launch": round(rec["fetch"] + rec["write"])}
+    t.setdefault("kernels", {})[workload] = kres
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(t, fh, indent=1)
@@ -238,6 +261,22 @@ def bench_copy(args):
                       "read_plus_write_GBs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1),
                       "read_only_bytes": 4 * COPY_BYTES, "read_only_ms": round(rms, 4),
                       "read_only_GBs": round(4 * COPY_BYTES / (rms * 1e-3) / 1e9, 1)}))
+
+
+def kernel_roofline(kern, main_flops, call_rl):
+    """Roofline of the dominant kernel, kp_kernel (the KV-outer pass of
+    msa_sparse_prefill, which does all of the main branch's MFMA work):
+    achieved = the call's algorithmic FLOPs per launch / its mean launch time,
+    both from HIP events recorded around each launch on its stream."""
+    k = kern.get("kp_kernel")
+    if not k:
+        return dict(call_rl, name="msa_sparse_prefill")
+    per_launch = main_flops / k["launches_per_step"]
+    achieved = per_launch / (k["avg_launch_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic("step", "kp_kernel"),
+            "name": "kp_kernel", "avg_launch_ms": k["avg_launch_ms"], "launches_per_step": k["launches_per_step"],
+            "flops_per_launch": per_launch}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -304,6 +343,8 @@ def main():
     ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the per-kernel event timing pass (ABI-call events only)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                              "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json for --workload from rocprofv3 counter CSVs (no GPU)")
@@ -381,6 +422,26 @@ def bench_step(msa, args):
     wall = time.perf_counter() - t0
     timer.collect(evs)
     print(f"[bench] {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+    # Kernel timing: the same steps again, with every launch of the hot kernels
+    # bracketed by HIP events on its stream.  Run after the timed region above
+    # because the extra events add gaps between launches (they would inflate
+    # the call times that `value` is computed from).
+    kern = {}
+    if not args.no_kernel_timing:
+        kern_names = ("ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "kd_kernel")
+        for k in kern_names:
+            msa.profile_read(k)
+        msa.profile_enable(True)
+        for s in range(args.steps):
+            for fn in calls(s):
+                fn()
+        torch.cuda.synchronize()
+        msa.profile_enable(False)
+        for k in kern_names:
+            tot, cnt = msa.profile_read(k)
+            if cnt:
+                kern[k] = {"launches_per_step": cnt / args.steps, "avg_launch_ms": round(tot / cnt, 5),
+                           "ms_per_step": round(tot / args.steps, 4)}
 
     ms_step = wall * 1e3 / args.steps
     t_ip, t_sp = timer.mean_ms("index_prefill"), timer.mean_ms("sparse_prefill")
@@ -446,8 +507,9 @@ def bench_step(msa, args):
                    "parallelism": "single GPU"},
         "prefill_ms": round(prefill_ms, 4),
         "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
-        "roofline": dict(rl["sparse_prefill"], name="msa_sparse_prefill"),
+        "roofline": kernel_roofline(kern, main_fl, rl["sparse_prefill"]),
         "rooflines": rl,
+        "kernels": kern,
         "dense_gqa": dense,
         "cpu_baseline": cpu,
     }

@@ -11,6 +11,7 @@
 
 #include <cstdlib>
 #include "msa_internal.hpp"
+#include "msa_profile.hpp"
 
 namespace {
 
@@ -84,6 +85,22 @@ constexpr int32_t kMaxDecodePages = 16384;
 extern "C" {
 
 int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+msa_status msa_profile_enable(int32_t on) {
+  msa::profile_set(on != 0);
+  return ok();
+}
+
+msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(MSA_ERR_INVALID_ARG, "total_ms and launches must not be NULL");
+  const int k = msa::profile_kernel_id(kernel);
+  if (k < 0) return fail(MSA_ERR_INVALID_ARG, "unknown kernel name '%s'", kernel ? kernel : "(null)");
+  long long n = 0;
+  const hipError_t e = msa::profile_collect(static_cast<msa::ProfKernel>(k), total_ms, &n);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "profile_collect: %s", hipGetErrorString(e));
+  *launches = n;
+  return ok();
+}
 
 const char* msa_status_string(msa_status st) {
   switch (st) {

@@ -25,6 +25,7 @@
 // The dense kernel (Eq. (1), §2.2) is the Q-outer comparison path.
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
+#include "msa_profile.hpp"
 
 namespace msa {
 
@@ -1321,11 +1322,15 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     kp.w = w;
     int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kp_wgs_per_cu<T, D>());
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
+    const int pk = profile_begin(PK_KP, st);
     hipLaunchKernelGGL((kp_kernel<T, D>), dim3(grid), dim3(kKpThreads), 0, st, kp);
+    profile_end(pk, st);
     km.w = w;
     const int64_t pairs = (int64_t)tok * a.h_kv;
+    const int pm = profile_begin(PK_KM, st);
     hipLaunchKernelGGL((km_kernel<T, D>), dim3((unsigned)((pairs + km.pairs_per_wg - 1) / km.pairs_per_wg)),
                        dim3(256), 0, st, km);
+    profile_end(pm, st);
   }
   return hipGetLastError();
 }
@@ -1411,7 +1416,9 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.max_pages = a.max_pages;
   k.split = pl.split;
   k.sm_scale = a.sm_scale;
+  const int pd = profile_begin(PK_KD, st);
   hipLaunchKernelGGL((kd_kernel<D, kKdWaves>), dim3(a.batch * a.h_kv * pl.split), dim3(kKdWaves * 64), 0, st, k);
+  profile_end(pd, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.split == 1) return e;
   hipLaunchKernelGGL((kd_merge_kernel<D>), dim3(a.batch * a.h_kv * a.group), dim3(D), 0, st, k);

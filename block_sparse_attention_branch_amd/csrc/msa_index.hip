@@ -24,6 +24,7 @@
 // and LDS bitonic sorts.
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
+#include "msa_profile.hpp"
 
 #include <cstdlib>
 
@@ -427,7 +428,9 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
 template <typename T, int DIDX>
 static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.grid_chunks * a.n_tiles));
+  const int pi = profile_begin(PK_KI_PREFILL, st);
   hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX>), grid, dim3(kKiThreads), 0, st, a);
+  profile_end(pi, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   hipLaunchKernelGGL(ki_merge_kernel, dim3((a.n_rows + 255) / 256), dim3(256), 0, st, a);
@@ -437,7 +440,9 @@ static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
 template <typename T, int DIDX>
 static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
   dim3 grid((a.max_pages + a.pages_per_wg - 1) / a.pages_per_wg, a.batch);
+  const int ps = profile_begin(PK_KI_DECODE_SCAN, st);
   hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX>), grid, dim3(256), 0, st, a);
+  profile_end(ps, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ki_decode_select_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, st, a);

@@ -45,7 +45,8 @@ class KV(ctypes.Structure):
 _lib = None
 
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
-           "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version"]
+           "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
+           "msa_profile_enable", "msa_profile_read"]
 
 
 def lib() -> ctypes.CDLL:
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.msa_last_error.argtypes = []
         L.msa_last_error.restype = ctypes.c_char_p
         L.msa_abi_version.restype = ctypes.c_int32
+        L.msa_profile_enable.argtypes = [i32]
+        L.msa_profile_enable.restype = ctypes.c_int
+        L.msa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(ctypes.c_int64)]
+        L.msa_profile_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -124,6 +129,21 @@ def _workspace(nbytes: int, device, ws):
     if ws is not None and ws.numel() >= nbytes:
         return ws
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- timing
+
+def profile_enable(on: bool = True) -> None:
+    """msa_profile_enable: bracket every launch of the timed kernels with HIP
+    events on the launch stream (measurement only)."""
+    _check(lib().msa_profile_enable(1 if on else 0))
+
+
+def profile_read(kernel: str):
+    """msa_profile_read: (summed GPU ms, launches) of `kernel` since the last read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().msa_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 # ---------------------------------------------------------------- calls

@@ -172,6 +172,22 @@ const char* msa_last_error(void);
 /* MSA_ABI_VERSION of the built library.                                 */
 int32_t msa_abi_version(void);
 
+/* Kernel timing, for measurement (not part of the method).
+ * msa_profile_enable(1): from now on every launch of a timed kernel is
+ *   bracketed by two HIP events recorded on the call's stream (the library
+ *   creates the events on first use and keeps them for reuse; no device
+ *   memory is allocated).  msa_profile_enable(0) stops recording.
+ * msa_profile_read(kernel, &total_ms, &launches): waits for the recorded
+ *   launches of `kernel`, returns their summed GPU time and count, and
+ *   forgets them.  Kernel names: "ki_prefill_kernel" (msa_index_topk,
+ *   prefill), "kp_kernel" and "km_kernel" (msa_sparse_prefill, KV-outer
+ *   pass and merge, one launch each per window of queries),
+ *   "ki_decode_scan_kernel" (msa_index_topk, decode), "kd_kernel"
+ *   (msa_sparse_decode).  Unknown names or NULL outputs: MSA_ERR_INVALID_ARG.
+ * Not meant to be used while calls are being enqueued from other threads. */
+msa_status msa_profile_enable(int32_t on);
+msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

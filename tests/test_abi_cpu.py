@@ -116,3 +116,13 @@ def test_workspace_size_queries():
     assert msa.workspace_size(msa.OP_DENSE, s, n_q=100, n_kv=100) == 0
     with pytest.raises(msa.MsaError):
         msa.workspace_size(9, s)
+
+
+def test_profile_api_host_side():
+    msa.profile_enable(True)
+    msa.profile_enable(False)
+    ms, n = msa.profile_read("kp_kernel")          # nothing recorded: no HIP call needed
+    assert ms == 0.0 and n == 0
+    with pytest.raises(msa.MsaError) as e:
+        msa.profile_read("no_such_kernel")
+    assert e.value.status == 1
