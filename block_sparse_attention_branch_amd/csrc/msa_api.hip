@@ -58,6 +58,19 @@ msa_status check_shape(const msa_shape* s, bool need_idx, bool need_attn) {
   return MSA_OK;
 }
 
+bool fp8_cache(const msa_shape& s) { return s.cache_dtype == MSA_FP8_E4M3; }
+
+// e4m3 caches: bf16 compute only, and only the paged decode calls.
+msa_status check_cache_dtype(const msa_shape& s, bool decode_call) {
+  if (!fp8_cache(s)) return MSA_OK;
+  if (s.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches need dtype MSA_BF16");
+  if (!decode_call) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches are built for the decode calls only");
+  return MSA_OK;
+}
+
+// Kernel dispatch code: 0 bf16, 1 fp32, 2 bf16 with e4m3 caches.
+int kernel_dtype(const msa_shape& s) { return fp8_cache(s) ? 2 : s.dtype; }
+
 msa_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return MSA_OK;
   if (!ws) return fail(MSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -122,6 +135,7 @@ size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int
     return 0;
   }
   if (check_shape(shape, op == 0 || op == 4, op >= 1 && op <= 3) != MSA_OK) return 0;
+  if (check_cache_dtype(*shape, op == 2 || op == 4) != MSA_OK) return 0;
   if (batch < 0 || n_q < 0 || q_start < 0 || n_kv < 0 || max_pages < 0) {
     fail(MSA_ERR_INVALID_ARG, "negative size");
     return 0;
@@ -158,6 +172,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   const float idx_scale = idx_scale_of(s);
   const int need_diag = (block_score != nullptr) ? 1 : 0;
 
+  if ((st = check_cache_dtype(s, kv->seq_lens != nullptr)) != MSA_OK) return st;
   if (kv->seq_lens) {  // decode mode
     if (n_q != 1) return fail(MSA_ERR_INVALID_ARG, "decode mode (seq_lens given) needs n_q == 1, got %d", n_q);
     if (!kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs a page_table");
@@ -187,7 +202,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
     a.scores = static_cast<float*>(workspace);
     a.block_idx = block_idx;
     a.block_score = block_score;
-    return hip_status(msa::launch_ki_decode(s.dtype, s.d_idx, a, stream), "msa_index_topk(decode)");
+    return hip_status(msa::launch_ki_decode(kernel_dtype(s), s.d_idx, a, stream), "msa_index_topk(decode)");
   }
 
   if (batch != 1) return fail(MSA_ERR_INVALID_ARG, "prefill mode handles one sequence: batch must be 1, got %d", batch);
@@ -235,6 +250,7 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   msa_status st = check_shape(shape, false, true);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
+  if ((st = check_cache_dtype(s, false)) != MSA_OK) return st;
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
   if (kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_prefill takes one sequence: seq_lens must be NULL");
   if (n_q < 0 || q_start < 0) return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d", n_q, q_start);
@@ -279,7 +295,8 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
   msa_status st = check_shape(shape, false, true);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
-  if (!msa::decode_supported(s.dtype, s.d_h)) return fail(MSA_ERR_UNSUPPORTED, "decode is built for bf16 only");
+  if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
+  if (!msa::decode_supported(kernel_dtype(s), s.d_h)) return fail(MSA_ERR_UNSUPPORTED, "decode is built for bf16 only");
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
   if (!kv->page_table || !kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "decode needs a paged cache with seq_lens");
   if (kv->max_pages < 1) return fail(MSA_ERR_INVALID_ARG, "max_pages=%d", kv->max_pages);
@@ -308,7 +325,7 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
   a.sm_scale = sm_scale_of(s);
   a.ws = workspace;
   a.ws_bytes = ws_bytes;
-  return hip_status(msa::launch_sparse_decode(s.dtype, s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
+  return hip_status(msa::launch_sparse_decode(kernel_dtype(s), s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
                     "msa_sparse_decode");
 }
 
@@ -320,6 +337,7 @@ msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_star
   msa_status st = check_shape(shape, false, true);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
+  if ((st = check_cache_dtype(s, false)) != MSA_OK) return st;
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
   if (kv->page_table || kv->seq_lens) return fail(MSA_ERR_UNSUPPORTED, "dense prefill takes a contiguous cache");
   if (n_q < 0 || q_start < 0 || (int64_t)q_start + n_q > kv->n_kv)

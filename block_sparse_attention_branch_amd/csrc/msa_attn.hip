@@ -933,32 +933,65 @@ constexpr int kKdWaves = 8;              // waves per decode workgroup  // bytes
 // One 32-key unit of a selected page for one wave: K rows as 16x16x32 B
 // fragments (keys on the MFMA rows) and V rows as raw 16-byte pieces, to be
 // transposed through LDS.
-template <int D>
+template <int D, typename TC>
 struct KdUnit {
-  Frag<bf16_t> kf[2][D / 32];
-  u32x4 vx[D / 32], vy[D / 32];
+  Raw<TC> kf[2][D / 32];
+  Raw<TC> vx[D / 32], vy[D / 32];
 };
+
+// Contraction-index / V-chunk maps.  16-bit caches: step ks of lane group q4
+// covers dims ks*32 + 8*q4 + e, and V chunk it of q4 is chunk q4 + 4*it.  e4m3
+// caches: q4 owns the contiguous run q4*(D/4) .. +D/4 (dims q4*(D/4) + 8*ks + e,
+// V chunks (D/32)*q4 + it), so each load moves 16 contiguous bytes per lane.
+template <typename TC, int D>
+__device__ __forceinline__ int kd_dim(int q4, int ks) {
+  return sizeof(TC) == 1 ? q4 * (D / 4) + 8 * ks : ks * 32 + 8 * q4;
+}
+template <typename TC, int D>
+__device__ __forceinline__ int kd_vchunk(int q4, int it) {
+  return sizeof(TC) == 1 ? (D / 32) * q4 + it : q4 + 4 * it;
+}
 
 // `pages` holds, in lane j, the physical page of slot j (read once per
 // workgroup), so a unit's address needs no dependent load.
-template <int D>
-__device__ __forceinline__ void kd_load_unit(KdUnit<D>& x, const KdArgs& a, int pages, int r, int u) {
-  typedef bf16_t T;
+template <int D, typename TC>
+__device__ __forceinline__ void kd_load_unit(KdUnit<D, TC>& x, const KdArgs& a, int pages, int r, int u) {
   const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
   const int j = u >> 2, qq = u & 3;
   const int page = __builtin_amdgcn_readlane(pages, j);
   const size_t base = (((size_t)page * a.h_kv + r) * kBlock + qq * 32) * D;
-  const T* kb = static_cast<const T*>(a.k) + base;
-  const T* vb = static_cast<const T*>(a.v) + base;
+  const TC* kb = static_cast<const TC*>(a.k) + base;
+  const TC* vb = static_cast<const TC*>(a.v) + base;
+  if constexpr (sizeof(TC) == 1) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) x.kf[tt][ks] = load_frag<T>(kb + (tt * 16 + l16) * D + ks * 32 + q4 * 8);
+      for (int ks = 0; ks < D / 32; ks += 2) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(kb + (tt * 16 + l16) * D + kd_dim<TC, D>(q4, ks));
+        x.kf[tt][ks] = u32x2{w[0], w[1]};
+        x.kf[tt][ks + 1] = u32x2{w[2], w[3]};
+      }
 #pragma unroll
-  for (int it = 0; it < D / 32; ++it) {
-    const int dc = q4 + 4 * it;
-    x.vx[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16) * D + 8 * dc);
-    x.vy[it] = *reinterpret_cast<const u32x4*>(vb + (2 * l16 + 1) * D + 8 * dc);
+    for (int it = 0; it < D / 32; it += 2) {
+      const int c = 8 * kd_vchunk<TC, D>(q4, it);
+      const u32x4 wx = *reinterpret_cast<const u32x4*>(vb + (2 * l16) * D + c);
+      const u32x4 wy = *reinterpret_cast<const u32x4*>(vb + (2 * l16 + 1) * D + c);
+      x.vx[it] = u32x2{wx[0], wx[1]};
+      x.vx[it + 1] = u32x2{wx[2], wx[3]};
+      x.vy[it] = u32x2{wy[0], wy[1]};
+      x.vy[it + 1] = u32x2{wy[2], wy[3]};
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) x.kf[tt][ks] = load_raw<TC>(kb + (tt * 16 + l16) * D + kd_dim<TC, D>(q4, ks));
+#pragma unroll
+    for (int it = 0; it < D / 32; ++it) {
+      const int c = 8 * kd_vchunk<TC, D>(q4, it);
+      x.vx[it] = load_raw<TC>(vb + (2 * l16) * D + c);
+      x.vy[it] = load_raw<TC>(vb + (2 * l16 + 1) * D + c);
+    }
   }
 }
 
@@ -981,7 +1014,7 @@ __device__ __forceinline__ uint32_t used_slots_s(const int32_t* row, int top_k, 
 // units with the next unit's loads in flight while the current one is
 // computed; the NW waves are then combined in LDS, and the splits by
 // kd_merge_kernel.
-template <int D, int NW>
+template <int D, int NW, typename TC>
 __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   typedef bf16_t T;
   constexpr int kVtBytes = D * kKdVtStride;
@@ -1008,7 +1041,7 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   Frag<T> qf[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = (l16 < G) ? load_frag<T>(qp + (size_t)l16 * D + ks * 32 + q4 * 8) : zero_frag<T>();
+    qf[ks] = (l16 < G) ? load_frag<T>(qp + (size_t)l16 * D + kd_dim<TC, D>(q4, ks)) : zero_frag<T>();
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
@@ -1018,19 +1051,19 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   const int step = a.split * NW;
   int u = sp * NW + wave;
   while (u < n_units && !((used >> (u >> 2)) & 1u)) u += step;
-  KdUnit<D> cur, nxt;
-  if (u < n_units) kd_load_unit<D>(cur, a, pages, r, u);
+  KdUnit<D, TC> cur, nxt;
+  if (u < n_units) kd_load_unit<D, TC>(cur, a, pages, r, u);
   while (u < n_units) {
     int un = u + step;
     while (un < n_units && !((used >> (un >> 2)) & 1u)) un += step;
-    if (un < n_units) kd_load_unit<D>(nxt, a, pages, r, un);
+    if (un < n_units) kd_load_unit<D, TC>(nxt, a, pages, r, un);
     const int b = __builtin_amdgcn_readlane(bl, u >> 2);
     f32x4 sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       sc[tt] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], cur.kf[tt][ks], qf[ks]);
+      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], widen<T, TC>(cur.kf[tt][ks]), qf[ks]);
     }
     // sc[tt][v]: key (u%4)*32 + tt*16 + 4*q4 + v of block b, head l16
     const int key0 = b * kBlock + (u & 3) * 32;
@@ -1048,11 +1081,13 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int it = 0; it < D / 32; ++it) {
-      const int dc = q4 + 4 * it;
+      const int dc = kd_vchunk<TC, D>(q4, it);
+      const u32x4 vx = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vx[it]));
+      const u32x4 vy = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vy[it]));
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
-        const uint32_t lo = (cur.vx[it][t2] & 0xffffu) | (cur.vy[it][t2] << 16);
-        const uint32_t hi = (cur.vx[it][t2] >> 16) | (cur.vy[it][t2] & 0xffff0000u);
+        const uint32_t lo = (vx[t2] & 0xffffu) | (vy[t2] << 16);
+        const uint32_t hi = (vx[t2] >> 16) | (vy[t2] & 0xffff0000u);
         *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2) * kKdVtStride + l16 * 4) = lo;
         *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t2 + 1) * kKdVtStride + l16 * 4) = hi;
       }
@@ -1240,7 +1275,7 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
 
 bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (d_h == 64 || d_h == 128); }
 bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
-bool decode_supported(int dtype, int d_h) { return dtype == 0 && (d_h == 64 || d_h == 128); }
+bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 2) && (d_h == 64 || d_h == 128); }
 
 template <typename T, int D>
 static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
@@ -1394,7 +1429,7 @@ DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, in
   return p;
 }
 
-template <int D>
+template <int D, typename TC>
 static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStream_t st) {
   KdArgs k{};
   k.q = a.q;
@@ -1417,7 +1452,7 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.split = pl.split;
   k.sm_scale = a.sm_scale;
   const int pd = profile_begin(PK_KD, st);
-  hipLaunchKernelGGL((kd_kernel<D, kKdWaves>), dim3(a.batch * a.h_kv * pl.split), dim3(kKdWaves * 64), 0, st, k);
+  hipLaunchKernelGGL((kd_kernel<D, kKdWaves, TC>), dim3(a.batch * a.h_kv * pl.split), dim3(kKdWaves * 64), 0, st, k);
   profile_end(pd, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.split == 1) return e;
@@ -1427,9 +1462,13 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
 
 hipError_t launch_sparse_decode(int dtype, int d_h, const AttnArgs& a, const DecodePlan& pl,
                                 hipStream_t st) {
-  if (dtype != 0) return hipErrorInvalidValue;
-  if (d_h == 128) return decode_typed<128>(a, pl, st);
-  if (d_h == 64) return decode_typed<64>(a, pl, st);
+  if (dtype == 0) {
+    if (d_h == 128) return decode_typed<128, bf16_t>(a, pl, st);
+    if (d_h == 64) return decode_typed<64, bf16_t>(a, pl, st);
+  } else if (dtype == 2) {  // bf16 queries, e4m3 cached keys and values
+    if (d_h == 128) return decode_typed<128, fp8_t>(a, pl, st);
+    if (d_h == 64) return decode_typed<64, fp8_t>(a, pl, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -81,6 +81,44 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 8-bit cache entries: OCP e4m3 ("fn": bias 7, no infinities), 1 byte each,
+// used as stored (no scale).  Every e4m3 value is exactly a bf16 value, so
+// widening to bf16 loses nothing.
+typedef uint8_t fp8_t;
+
+// Eight e4m3 codes (byte e of the pair of dwords = element e) to bf16.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], true);
+  return bf16x8{static_cast<bf16_t>(a[0]), static_cast<bf16_t>(a[1]), static_cast<bf16_t>(b[0]),
+                static_cast<bf16_t>(b[1]), static_cast<bf16_t>(c[0]), static_cast<bf16_t>(c[1]),
+                static_cast<bf16_t>(d[0]), static_cast<bf16_t>(d[1])};
+}
+
+// A cache fragment as loaded: 8 elements of the cache type, kept raw until
+// the math needs them (so converting never waits on loads in flight).
+template <typename TC> struct RawT;
+template <> struct RawT<bf16_t> { typedef bf16x8 type; };
+template <> struct RawT<float> { typedef f32x8 type; };
+template <> struct RawT<fp8_t> { typedef u32x2 type; };
+template <typename TC> using Raw = typename RawT<TC>::type;
+
+template <typename TC>
+__device__ __forceinline__ Raw<TC> load_raw(const TC* p) {
+  return *reinterpret_cast<const Raw<TC>*>(p);
+}
+// Raw fragment -> compute fragment (T = bf16 for fp8 caches).
+template <typename T, typename TC>
+__device__ __forceinline__ Frag<T> widen(const Raw<TC>& r) {
+  if constexpr (sizeof(TC) == 1) {
+    return fp8x8_to_bf16(r);
+  } else {
+    return r;
+  }
+}
+
 // ------------------------------------------------------------ top-k keys
 // A candidate block is packed into one 64-bit key whose unsigned order is the
 // selection order: pooled score descending, then block index ascending.

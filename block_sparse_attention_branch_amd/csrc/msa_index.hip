@@ -277,16 +277,38 @@ __global__ __launch_bounds__(256) void ki_merge_kernel(KiPrefillArgs a) {
 // ------------------------------------------------------------ decode kernels
 // One 128-key page of index keys as 16x16x32 B fragments: kt-th 16-key
 // slice, keys on the MFMA columns.
-template <typename T, int DIDX>
-__device__ __forceinline__ void ki_load_page(Frag<T> (&f)[8][DIDX / 32], const T* kp) {
-  const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-    for (int ks = 0; ks < DIDX / 32; ++ks) f[kt][ks] = load_frag<T>(kp + (kt * 16 + l16) * DIDX + ks * 32 + q4 * 8);
+// Contraction-index map: for 16-bit caches lane group q4 holds dims
+// ks*32 + 8*q4 + e of step ks; for e4m3 caches it holds the contiguous run
+// q4*(DIDX/4) + 8*ks + e, so one 16-byte load covers two steps and a load
+// instruction reads whole 64-byte rows.  (The query fragments use the same map.)
+template <typename TC, int DIDX>
+__device__ __forceinline__ int ki_dim(int q4, int ks) {
+  return sizeof(TC) == 1 ? q4 * (DIDX / 4) + 8 * ks : ks * 32 + 8 * q4;
 }
 
-template <typename T, int DIDX>
+template <typename TC, int DIDX>
+__device__ __forceinline__ void ki_load_page(Raw<TC> (&f)[8][DIDX / 32], const TC* kp) {
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    if constexpr (sizeof(TC) == 1 && DIDX >= 64) {
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 32; ks += 2) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(kp + (kt * 16 + l16) * DIDX + ki_dim<TC, DIDX>(q4, ks));
+        f[kt][ks] = u32x2{w[0], w[1]};
+        f[kt][ks + 1] = u32x2{w[2], w[3]};
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 32; ++ks)
+        f[kt][ks] = load_raw<TC>(kp + (kt * 16 + l16) * DIDX + ki_dim<TC, DIDX>(q4, ks));
+    }
+  }
+}
+
+// T: dtype of q_idx and of the MFMA; TC: dtype of the cached k_idx (T, or
+// e4m3 widened to bf16 after loading).
+template <typename T, int DIDX, typename TC>
 __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   constexpr int KS = DIDX / 32;
   const int s = blockIdx.y;
@@ -300,30 +322,30 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, l16 = lane & 15;
   const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
-  const T* __restrict__ k_idx = static_cast<const T*>(a.k_idx);
+  const TC* __restrict__ k_idx = static_cast<const TC*>(a.k_idx);
   Frag<T> qa[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ks * 32 + q4 * 8)
+    qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ki_dim<TC, DIDX>(q4, ks))
                             : zero_frag<T>();
   const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
   // For rows of up to 128 bytes the next page's index keys are loaded while
   // the current page is scored (wider rows would not fit two pages).
-  constexpr bool kPipe = sizeof(T) * DIDX <= 128;
-  Frag<T> cur[8][KS], nxt[8][KS];
+  constexpr bool kPipe = sizeof(TC) * DIDX <= 128;
+  Raw<TC> cur[8][KS], nxt[8][KS];
   int pg = pg_begin + wave;
-  if (kPipe && pg < pg_end) ki_load_page<T, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
+  if (kPipe && pg < pg_end) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
   for (; pg < pg_end; pg += 4) {
-    if (!kPipe) ki_load_page<T, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
+    if (!kPipe) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
     if (kPipe && pg + 4 < pg_end)
-      ki_load_page<T, DIDX>(nxt, k_idx + (size_t)scalar_load(pt, pg + 4) * kBlock * DIDX);
+      ki_load_page<TC, DIDX>(nxt, k_idx + (size_t)scalar_load(pt, pg + 4) * kBlock * DIDX);
     float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
     const bool masked = (pg == nb - 1);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], cur[kt][ks]);
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], widen<T, TC>(cur[kt][ks]));
       const bool vis = !masked || (pg * kBlock + kt * 16 + l16 <= p);
 #pragma unroll
       for (int v = 0; v < 4; ++v) m[v] = fmaxf(m[v], vis ? acc[v] : -__builtin_inff());
@@ -437,11 +459,11 @@ static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int DIDX>
+template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
   dim3 grid((a.max_pages + a.pages_per_wg - 1) / a.pages_per_wg, a.batch);
   const int ps = profile_begin(PK_KI_DECODE_SCAN, st);
-  hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX, TC>), grid, dim3(256), 0, st, a);
   profile_end(ps, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -471,6 +493,12 @@ hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipSt
   MSA_KI_DISPATCH(ki_prefill_typed, a, st);
 }
 hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st) {
+  if (dtype == 2) {  // bf16 queries, e4m3 cached index keys
+    if (d_idx == 32) return ki_decode_typed<bf16_t, 32, fp8_t>(a, st);
+    if (d_idx == 64) return ki_decode_typed<bf16_t, 64, fp8_t>(a, st);
+    if (d_idx == 128) return ki_decode_typed<bf16_t, 128, fp8_t>(a, st);
+    return hipErrorInvalidValue;
+  }
   MSA_KI_DISPATCH(ki_decode_typed, a, st);
 }
 

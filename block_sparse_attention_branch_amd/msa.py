@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_BF16, MSA_FP32 = 0, 1
+MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
 OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE = 0, 1, 2, 3, 4
 BLOCK = 128
 
@@ -33,7 +33,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("force_local", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -109,9 +109,17 @@ def _stream(stream) -> int | None:
 
 
 def make_shape(h_q, h_kv, d_h, d_idx, top_k, dtype_code, *, force_local=True,
-               sm_scale=0.0, idx_scale=0.0) -> Shape:
+               sm_scale=0.0, idx_scale=0.0, cache_dtype=None) -> Shape:
+    cd = int(dtype_code) if cache_dtype is None else int(cache_dtype)
     return Shape(int(h_q), int(h_kv), int(d_h), int(d_idx), BLOCK, int(top_k),
-                 1 if force_local else 0, float(sm_scale), float(idx_scale), int(dtype_code))
+                 1 if force_local else 0, float(sm_scale), float(idx_scale), int(dtype_code), cd)
+
+
+def _cache_code(t: torch.Tensor, compute_code: int) -> int:
+    """Cache dtype of a k/v/k_idx tensor: e4m3 (float8_e4m3fn) or the call's dtype."""
+    if t is not None and t.dtype == torch.float8_e4m3fn:
+        return MSA_FP8_E4M3
+    return compute_code
 
 
 def workspace_size(op: int, shape: Shape, *, batch=1, n_q=0, q_start=0, n_kv=0, max_pages=0) -> int:
@@ -173,7 +181,7 @@ def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale
         mp = int(max_pages)
     dt = _dtype_code(q_idx)
     shape = make_shape(h_q or h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local,
-                       idx_scale=idx_scale)
+                       idx_scale=idx_scale, cache_dtype=_cache_code(k_idx, dt))
     dev = q_idx.device
     bidx = out if out is not None else torch.empty((rows, h_kv, top_k), dtype=torch.int32, device=dev)
     scores = torch.empty((rows, h_kv, top_k), dtype=torch.float32, device=dev) if with_scores else None
@@ -215,7 +223,8 @@ def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *, sm_sc
     int32 [batch, h_kv, top_k].  Returns o [batch, h_q, d_h] (and lse)."""
     batch, h_q, d_h = q.shape
     h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
-    shape = make_shape(h_q, h_kv, d_h, 64, top_k, _dtype_code(q), sm_scale=sm_scale)
+    dt = _dtype_code(q)
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale, cache_dtype=_cache_code(k_pages, dt))
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((batch, h_q), dtype=torch.float32, device=q.device) if with_lse else None
     nws = workspace_size(OP_DECODE, shape, batch=batch, n_q=1)

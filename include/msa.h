@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 #define MSA_BLOCK_SIZE 128
 #define MSA_MAX_TOP_K 16
 
@@ -64,7 +64,9 @@ typedef enum msa_status {
   MSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
 } msa_status;
 
-typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1 } msa_dtype;
+/* MSA_FP8_E4M3: OCP 8-bit float e4m3 ("fn": bias 7, no infinities), one
+ * byte per element, used as stored (no scale).  Only for the caches. */
+typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2 } msa_dtype;
 
 /* Head shapes and method hyper-parameters.
  *   h_q, h_kv    query heads and KV heads (GQA groups); h_q % h_kv == 0 and
@@ -78,11 +80,17 @@ typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1 } msa_dtype;
  *                k slots ([P1] §4.2); 0: plain top-k over visible blocks.
  *   sm_scale     softmax scale of Eq. (8); 0 means 1/sqrt(d_h).
  *   idx_scale    score scale of Eq. (6); 0 means 1/sqrt(d_idx).
- *   dtype        msa_dtype of every float tensor of the call.            */
+ *   dtype        msa_dtype (BF16 or FP32) of every float tensor of the call.
+ *   cache_dtype  MSA_FP8_E4M3: the caches k, v and k_idx hold e4m3 codes
+ *                (paged decode calls with dtype MSA_BF16 only: msa_index_topk
+ *                in decode mode and msa_sparse_decode); they are widened
+ *                exactly to bf16 before use.  Any other value: the caches
+ *                have type `dtype`.                                       */
 typedef struct msa_shape {
   int32_t h_q, h_kv, d_h, d_idx, block_size, top_k, force_local;
   float sm_scale, idx_scale;
   int32_t dtype;
+  int32_t cache_dtype;
 } msa_shape;
 
 /* The KV side of a call.

@@ -269,6 +269,27 @@ def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *,
 
 
 # --------------------------------------------------------------------------
+# 8-bit caches (scope table, next step: e4m3 K/V and K_idx caches; the MXFP8
+# KV cache of the zhichai.net key points)
+# --------------------------------------------------------------------------
+
+def decode_e4m3(codes):
+    """Values of OCP FP8 E4M3 ("fn") codes, written from the format's
+    definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 is subnormal (m/8 * 2^-6), the code S.1111.111 is NaN
+    and there are no infinities.  ``codes`` is any uint8 array; returns
+    float64 of the same shape."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = sign * np.ldexp(m / 8.0, -6)
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, out)
+
+
+# --------------------------------------------------------------------------
 # FLOP model ([P1] §5.2 Eq. (12))
 # --------------------------------------------------------------------------
 

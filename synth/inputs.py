@@ -90,15 +90,18 @@ def gen_prefill(n_kv: int, shape: HeadShape = MODEL_SHAPE, *, n_q: int | None = 
 def gen_decode_paged(batch: int, seq_len: int, shape: HeadShape = MODEL_SHAPE, *,
                      dtype=torch.bfloat16, seed: int = 3, device="cpu",
                      extra_tokens: int = 0, n_query_sets: int = 1,
-                     seq_lens=None) -> dict:
+                     seq_lens=None, cache_dtype=None) -> dict:
     """A paged KV cache of ``batch`` sequences with 128-token pages.
 
     Physical pages are a seeded random permutation: page_table [batch, max_pages]
     int32.  k/v pages [num_pages, h_kv, 128, d_h] (head-major inside a page),
     k_idx pages [num_pages, 128, d_idx].  ``seq_lens`` [batch] int32 counts the
     tokens held, the newest token included.  Queries: q [sets, batch, h_q, d_h],
-    q_idx [sets, batch, h_kv, d_idx].  Everything N(0,1).
+    q_idx [sets, batch, h_kv, d_idx].  Everything N(0,1).  ``cache_dtype``
+    (default ``dtype``) is the storage type of the three caches, e.g.
+    torch.float8_e4m3fn (the N(0,1) draws rounded once to that format).
     """
+    cdt = dtype if cache_dtype is None else cache_dtype
     if seq_lens is None:
         seq_lens = [seq_len] * batch
     max_pages = -(-(max(seq_lens) + extra_tokens) // BLOCK)
@@ -109,9 +112,9 @@ def gen_decode_paged(batch: int, seq_len: int, shape: HeadShape = MODEL_SHAPE, *
     out = {
         "page_table": perm.view(batch, max_pages).contiguous().to(device),
         "seq_lens": torch.tensor(seq_lens, dtype=torch.int32).to(device),
-        "k_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, dtype),
-        "v_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, dtype),
-        "k_idx_pages": _randn((num_pages, BLOCK, shape.d_idx), g, device, dtype),
+        "k_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt),
+        "v_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt),
+        "k_idx_pages": _randn((num_pages, BLOCK, shape.d_idx), g, device, cdt),
         "q": _randn((n_query_sets, batch, shape.h_q, shape.d_h), g, device, dtype),
         "q_idx": _randn((n_query_sets, batch, shape.h_kv, shape.d_idx), g, device, dtype),
         "max_pages": max_pages,

@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     L = msa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.msa_abi_version() == 1
+    assert L.msa_abi_version() == 2
     for st in range(5):
         assert L.msa_status_string(st).decode().startswith("MSA_")
 

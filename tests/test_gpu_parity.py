@@ -194,11 +194,19 @@ def test_prefill_deterministic_and_chunked_equals_one_shot():
 
 # ------------------------------------------------------------------ decode
 
-def _decode_case(shape, seq_lens, seed, n_sets=1):
+def _cache_host(t):
+    """Host float64 copy of a cache tensor; e4m3 codes go through the oracle's decoder."""
+    if t.dtype == torch.float8_e4m3fn:
+        return orc.decode_e4m3(t.view(torch.uint8).cpu().numpy())
+    return t.cpu().double().numpy()
+
+
+def _decode_case(shape, seq_lens, seed, n_sets=1, cache_dtype=None):
     msa = _msa()
     batch = len(seq_lens)
-    inp = gen_decode_paged(batch, max(seq_lens), shape, seed=seed, device=DEV, seq_lens=seq_lens)
-    _say("decode", shape, seq_lens, seed)
+    inp = gen_decode_paged(batch, max(seq_lens), shape, seed=seed, device=DEV, seq_lens=seq_lens,
+                           cache_dtype=cache_dtype)
+    _say("decode", shape, seq_lens, seed, cache_dtype)
     q_idx = inp["q_idx"][0].contiguous()
     q = inp["q"][0].contiguous()
     bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=shape.top_k, page_table=inp["page_table"],
@@ -207,14 +215,13 @@ def _decode_case(shape, seq_lens, seed, n_sets=1):
                                with_lse=True)
     torch.cuda.synchronize()
     pt = inp["page_table"].cpu().numpy()
-    kp = inp["k_pages"].cpu()
-    vp = inp["v_pages"].cpu()
-    ip = inp["k_idx_pages"].cpu()
-    o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), ip.double().numpy(), pt, seq_lens, shape.top_k)
+    kp = _cache_host(inp["k_pages"])
+    vp = _cache_host(inp["v_pages"])
+    ip = _cache_host(inp["k_idx_pages"])
+    o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), ip, pt, seq_lens, shape.top_k)
     diags = (np.asarray(seq_lens) - 1) // 128
     compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, diags)
-    o_ref, lse_ref = orc.sparse_decode(np64(q), kp.double().numpy(), vp.double().numpy(), pt, seq_lens,
-                                       bidx.cpu().numpy())
+    o_ref, lse_ref = orc.sparse_decode(np64(q), kp, vp, pt, seq_lens, bidx.cpu().numpy())
     compare_out(o, o_ref, torch.bfloat16)
     compare_lse(lse, lse_ref, torch.bfloat16)
 
@@ -230,6 +237,23 @@ def test_decode_batch_many_short():
 def test_decode_groups_of_1_and_8_d64():
     _decode_case(HeadShape(4, 4, 128, 64, 7), [900, 129, 1], 23)
     _decode_case(HeadShape(16, 2, 64, 32, 16), [5000, 2500], 24)
+
+
+def test_decode_e4m3_caches():
+    # e4m3 K, V and K_idx pages, bf16 queries: mixed lengths, d_h 128 and 64
+    f8 = torch.float8_e4m3fn
+    _decode_case(MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049], 25, cache_dtype=f8)
+    _decode_case(HeadShape(16, 2, 64, 32, 16), [5000, 2500, 700], 26, cache_dtype=f8)
+    _decode_case(HeadShape(16, 4, 128, 128, 8), [1500, 9000], 27, cache_dtype=f8)
+
+
+def test_decode_e4m3_rejected_for_prefill_calls():
+    msa = _msa()
+    inp = gen_prefill(300, MODEL_SHAPE, dtype=torch.bfloat16, seed=28, device=DEV)
+    k8 = inp["k_idx"].to(torch.float8_e4m3fn)
+    with pytest.raises(msa.MsaError) as e:
+        msa.index_topk(inp["q_idx"], k8, top_k=16)
+    assert "e4m3" in str(e.value)
 
 
 def test_decode_single_long_sequence():
@@ -281,6 +305,34 @@ def test_full_size_decode_64x128k_sampled_sequences():
         kp = np64(inp["k_pages"][pages])
         vp = np64(inp["v_pages"][pages])
         ip = np64(inp["k_idx_pages"][pages])
+        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx[s:s + 1]), ip, local_pt, [L], 16)
+        compare_index_rows(g_ids[s:s + 1], o_ids, pooled, [(L - 1) // 128])
+        o_ref, lse_ref = orc.sparse_decode(np64(q[s:s + 1]), kp, vp, local_pt, [L], g_ids[s:s + 1])
+        compare_out(o[s:s + 1], o_ref, torch.bfloat16)
+        compare_lse(lse[s:s + 1], lse_ref, torch.bfloat16)
+
+
+def test_full_size_decode_64x128k_e4m3_sampled_sequences():
+    """The 64 x 131072 decode step with e4m3 caches; 2 sequences checked."""
+    msa = _msa()
+    shape = MODEL_SHAPE
+    inp = gen_decode_paged(64, 131072, shape, seed=3, device=DEV, cache_dtype=torch.float8_e4m3fn)
+    _say("decode 64 x 128K e4m3 full size")
+    q_idx = inp["q_idx"][0].contiguous()
+    q = inp["q"][0].contiguous()
+    bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=16, page_table=inp["page_table"],
+                          seq_lens=inp["seq_lens"])
+    o, lse = msa.sparse_decode(q, inp["k_pages"], inp["v_pages"], inp["page_table"], inp["seq_lens"], bidx,
+                               with_lse=True)
+    torch.cuda.synchronize()
+    g_ids = bidx.cpu().numpy()
+    L = 131072
+    local_pt = np.arange(L // 128)[None, :]
+    for s in (5, 60):
+        pages = inp["page_table"][s].long()
+        kp = _cache_host(inp["k_pages"][pages])
+        vp = _cache_host(inp["v_pages"][pages])
+        ip = _cache_host(inp["k_idx_pages"][pages])
         o_ids, _, pooled = orc.index_topk_decode(np64(q_idx[s:s + 1]), ip, local_pt, [L], 16)
         compare_index_rows(g_ids[s:s + 1], o_ids, pooled, [(L - 1) // 128])
         o_ref, lse_ref = orc.sparse_decode(np64(q[s:s + 1]), kp, vp, local_pt, [L], g_ids[s:s + 1])

@@ -360,3 +360,33 @@ def test_paged_oracles_equal_contiguous():
         o_c, l_c = orc.sparse_attention(q[s:s + 1], kc, vc, ids_c, L - 1)
         np.testing.assert_allclose(o[s], o_c[0], rtol=1e-13)
         np.testing.assert_allclose(lse[s], l_c[0], rtol=1e-13)
+
+
+# ------------------------------------------------------------------ e4m3 decoder
+
+def test_e4m3_decoder_closed_forms():
+    # values fixed by the format's definition (sign, 4-bit exponent bias 7,
+    # 3-bit mantissa, subnormals at exponent 0, S.1111.111 = NaN)
+    cases = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0,
+             0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x0F: 1.875 * 2.0 ** -6, 0x77: 240.0}
+    got = orc.decode_e4m3(np.array(list(cases), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(cases.values())))
+    nan = orc.decode_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.all(np.isnan(nan))
+    assert np.signbit(orc.decode_e4m3(np.array([0x80], dtype=np.uint8)))[0]
+
+
+def test_e4m3_decoder_is_monotone_and_symmetric():
+    pos = orc.decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    neg = orc.decode_e4m3(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(neg, -pos)
+
+
+def test_e4m3_decoder_matches_torch_float8_e4m3fn():
+    # an independent implementation of the same format
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.decode_e4m3(codes.numpy())
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
