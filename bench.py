@@ -56,14 +56,16 @@ def prefill_counts(n_q, q_start, shape=MODEL_SHAPE):
     return idx_flops, main_flops, dense_flops
 
 
-def decode_bytes(seq_lens, shape=MODEL_SHAPE, esz=2):
+def decode_bytes(seq_lens, shape=MODEL_SHAPE, esz=2, cache_esz=None):
     """Algorithmic HBM bytes of one decode step: the index keys of every past
-    page (index scan) and the visible keys/values of the k selected pages."""
+    page (index scan) and the visible keys/values of the k selected pages.
+    ``cache_esz``: bytes per cached element (default ``esz``; 1 for e4m3)."""
+    cesz = esz if cache_esz is None else cache_esz
     L = np.asarray(seq_lens, dtype=np.int64)
     diag = (L - 1) // BLOCK
-    idx_bytes = float((BLOCK * diag * shape.d_idx * esz).sum())
+    idx_bytes = float((BLOCK * diag * shape.d_idx * cesz).sum())
     vis = BLOCK * np.minimum(shape.top_k - 1, diag) + (L - 1) % BLOCK + 1
-    main_bytes = float((vis * shape.h_kv * shape.d_h * esz * 2).sum())
+    main_bytes = float((vis * shape.h_kv * shape.d_h * cesz * 2).sum())
     main_bytes += float(len(L) * shape.h_q * shape.d_h * esz * 2)  # q in, o out
     dense_bytes = float((L * shape.h_kv * shape.d_h * esz * 2).sum())
     return idx_bytes, main_bytes, dense_bytes
@@ -340,7 +342,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "copy"])
+    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -365,6 +367,8 @@ def main():
         bench_copy(args)
     elif args.workload == "step":
         bench_step(msa, args)
+    elif args.workload == "decode_fp8":
+        bench_decode_fp8(msa, args)
     elif args.workload == "prefill128k":
         bench_prefill_only(msa, args, planted=True)
     else:
@@ -514,6 +518,46 @@ def bench_step(msa, args):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def bench_decode_fp8(msa, args):
+    """The 64 x 131072 paged decode step with e4m3 K, V and K_idx caches
+    (bf16 queries and outputs), 4 rotating query sets."""
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    B, L = 64, 131072
+    dec = gen_decode_paged(B, L, shape, seed=3, device=dev, n_query_sets=4, cache_dtype=torch.float8_e4m3fn)
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16,
+                           cache_dtype=msa.MSA_FP8_E4M3)
+    mp = dec["page_table"].shape[1]
+    dbidx = [torch.empty((B, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev) for _ in range(4)]
+    do = torch.empty((B, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
+    ws_di = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX_DECODE, s_idx, batch=B, n_q=1, max_pages=mp)),
+                        dtype=torch.uint8, device=dev)
+    ws_dd = torch.empty(max(1, msa.workspace_size(msa.OP_DECODE, s_idx, batch=B, n_q=1)), dtype=torch.uint8,
+                        device=dev)
+    qsets = [dec["q"][i].contiguous() for i in range(4)]
+    qisets = [dec["q_idx"][i].contiguous() for i in range(4)]
+
+    def calls(j):
+        return [lambda: msa.index_topk(qisets[j], dec["k_idx_pages"], top_k=16, page_table=dec["page_table"],
+                                       seq_lens=dec["seq_lens"], out=dbidx[j], workspace=ws_di),
+                lambda: msa.sparse_decode(qsets[j], dec["k_pages"], dec["v_pages"], dec["page_table"],
+                                          dec["seq_lens"], dbidx[j], out=do, workspace=ws_dd)]
+    timer = CallTimer(["index_decode", "sparse_decode"])
+    for w in range(args.warmup):
+        for f in calls(w % 4):
+            f()
+    torch.cuda.synchronize()
+    evs = [timer.step(calls(i % 4)) for i in range(args.steps)]
+    timer.collect(evs)
+    t_id, t_sd = timer.mean_ms("index_decode"), timer.mean_ms("sparse_decode")
+    didx_b, dmain_b, _ = decode_bytes([L] * B, shape, cache_esz=1)
+    print(json.dumps({"workload": "decode 64 x 131072 paged, e4m3 K/V/K_idx caches, bf16 queries",
+                      "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
+                      "index_us": round(t_id * 1e3, 2), "sparse_us": round(t_sd * 1e3, 2),
+                      "index_roofline": roofline("hbm", didx_b, t_id, "GB/s"),
+                      "sparse_roofline": roofline("hbm", dmain_b, t_sd, "GB/s")}))
 
 
 def bench_prefill_only(msa, args, planted=True):
