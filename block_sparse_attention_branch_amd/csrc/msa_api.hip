@@ -60,11 +60,11 @@ msa_status check_shape(const msa_shape* s, bool need_idx, bool need_attn) {
 
 bool fp8_cache(const msa_shape& s) { return s.cache_dtype == MSA_FP8_E4M3; }
 
-// e4m3 caches: bf16 compute only, and only the paged decode calls.
-msa_status check_cache_dtype(const msa_shape& s, bool decode_call) {
+// e4m3 caches: bf16 compute only; every call but the dense comparison.
+msa_status check_cache_dtype(const msa_shape& s, bool allowed) {
   if (!fp8_cache(s)) return MSA_OK;
   if (s.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches need dtype MSA_BF16");
-  if (!decode_call) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches are built for the decode calls only");
+  if (!allowed) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches are not built for the dense comparison call");
   return MSA_OK;
 }
 
@@ -135,7 +135,7 @@ size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int
     return 0;
   }
   if (check_shape(shape, op == 0 || op == 4, op >= 1 && op <= 3) != MSA_OK) return 0;
-  if (check_cache_dtype(*shape, op == 2 || op == 4) != MSA_OK) return 0;
+  if (check_cache_dtype(*shape, op != 3) != MSA_OK) return 0;
   if (batch < 0 || n_q < 0 || q_start < 0 || n_kv < 0 || max_pages < 0) {
     fail(MSA_ERR_INVALID_ARG, "negative size");
     return 0;
@@ -172,7 +172,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   const float idx_scale = idx_scale_of(s);
   const int need_diag = (block_score != nullptr) ? 1 : 0;
 
-  if ((st = check_cache_dtype(s, kv->seq_lens != nullptr)) != MSA_OK) return st;
+  if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
   if (kv->seq_lens) {  // decode mode
     if (n_q != 1) return fail(MSA_ERR_INVALID_ARG, "decode mode (seq_lens given) needs n_q == 1, got %d", n_q);
     if (!kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs a page_table");
@@ -241,7 +241,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
     a.part_keys = reinterpret_cast<uint64_t*>(ws);
     a.part_diag = reinterpret_cast<float*>(ws + keys);
   }
-  return hip_status(msa::launch_ki_prefill(s.dtype, s.d_idx, a, stream), "msa_index_topk(prefill)");
+  return hip_status(msa::launch_ki_prefill(kernel_dtype(s), s.d_idx, a, stream), "msa_index_topk(prefill)");
 }
 
 msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
@@ -250,7 +250,7 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   msa_status st = check_shape(shape, false, true);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
-  if ((st = check_cache_dtype(s, false)) != MSA_OK) return st;
+  if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
   if (kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_prefill takes one sequence: seq_lens must be NULL");
   if (n_q < 0 || q_start < 0) return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d", n_q, q_start);
@@ -285,7 +285,7 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   a.sm_scale = sm_scale_of(s);
   a.ws = workspace;
   a.ws_bytes = ws_bytes;
-  return hip_status(msa::launch_sparse_prefill(s.dtype, s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
+  return hip_status(msa::launch_sparse_prefill(kernel_dtype(s), s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
                     "msa_sparse_prefill");
 }
 

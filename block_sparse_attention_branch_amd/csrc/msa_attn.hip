@@ -27,6 +27,8 @@
 #include "msa_internal.hpp"
 #include "msa_profile.hpp"
 
+#include <type_traits>
+
 namespace msa {
 
 // ----------------------------------------------------------------- LDS tile
@@ -40,15 +42,19 @@ struct KvLds {
 
 // Two-phase staging for double buffering: global -> registers (issued before
 // the current block's math) and registers -> LDS (after it).  NT threads.
-template <typename T, int D, int NT>
+// TC is the cache type; with e4m3 caches (T = bf16) each 16-byte bf16 chunk
+// arrives as 8 bytes and is widened when stored to LDS.
+template <typename T, int D, int NT, typename TC = T>
 struct StageRegs {
+  typedef typename std::conditional<sizeof(TC) == 1, u32x2, u32x4>::type Chunk;
+  static constexpr int CB = 16 * (int)sizeof(TC) / (int)sizeof(T);          // cache bytes per 16-B LDS chunk
   static constexpr int CPR = D * (int)sizeof(T) / 16;
   static constexpr int KL = 128 * CPR / NT;                                  // K chunks per thread
   static constexpr int VU = (sizeof(T) == 2 ? 64 * (D / 8) : 128 * (D / 4)) / NT;  // V units per thread
   static constexpr int VW = sizeof(T) == 2 ? 2 : 1;                          // loads per V unit
   static_assert(KL >= 1 && VU >= 1, "staging split");
-  u32x4 k[KL];
-  u32x4 v[VU][VW];
+  Chunk k[KL];
+  Chunk v[VU][VW];
   uint32_t zero_mask;  // bit i: K load i past the end; bit 16 + 2u + w: V load (u, w)
 };
 
@@ -80,12 +86,13 @@ __device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, cons
   return p;
 }
 
-template <typename T, int D, int NT>
-__device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPtr& p) {
+template <typename T, int D, int NT, typename TC = T>
+__device__ __forceinline__ void stage_load(StageRegs<T, D, NT, TC>& g, const BlockPtr& p) {
   // Every load is issued unconditionally (rows past the end of a contiguous
   // cache read the last valid row); the values are zeroed only when stored to
   // LDS, so nothing here waits for the loads to land.
-  using S = StageRegs<T, D, NT>;
+  using S = StageRegs<T, D, NT, TC>;
+  typedef typename S::Chunk C;
   static_assert(S::KL <= 16 && S::VU * S::VW <= 16, "zero mask layout");
   const int last = p.valid - 1;
   uint32_t zm = 0;
@@ -93,7 +100,7 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPt
   for (int i = 0; i < S::KL; ++i) {
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
-    g.k[i] = *reinterpret_cast<const u32x4*>(p.k + (size_t)min(j, last) * p.stride + c * 16);
+    g.k[i] = *reinterpret_cast<const C*>(p.k + (size_t)min(j, last) * p.stride + c * S::CB);
     zm |= (j > last ? 1u : 0u) << i;
   }
   if constexpr (sizeof(T) == 2) {
@@ -103,8 +110,8 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPt
       const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      g.v[i][0] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(2 * kp, last) * p.stride + dc * 16);
-      g.v[i][1] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(2 * kp + 1, last) * p.stride + dc * 16);
+      g.v[i][0] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp, last) * p.stride + dc * S::CB);
+      g.v[i][1] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp + 1, last) * p.stride + dc * S::CB);
       zm |= (2 * kp > last ? 1u : 0u) << (16 + 2 * i);
       zm |= (2 * kp + 1 > last ? 1u : 0u) << (17 + 2 * i);
     }
@@ -115,23 +122,32 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT>& g, const BlockPt
       const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
-      g.v[i][0] = *reinterpret_cast<const u32x4*>(p.v + (size_t)min(key, last) * p.stride + dc * 16);
+      g.v[i][0] = *reinterpret_cast<const C*>(p.v + (size_t)min(key, last) * p.stride + dc * S::CB);
       zm |= (key > last ? 1u : 0u) << (16 + 2 * i);
     }
   }
   g.zero_mask = zm;
 }
 
-template <typename T, int D, int NT>
-__device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* lds) {
-  using S = StageRegs<T, D, NT>;
+template <typename T, typename C>
+__device__ __forceinline__ u32x4 stage_widen(const C& c) {
+  if constexpr (sizeof(C) == 8) {
+    return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c));
+  } else {
+    return c;
+  }
+}
+
+template <typename T, int D, int NT, typename TC = T>
+__device__ __forceinline__ void stage_store(const StageRegs<T, D, NT, TC>& g, char* lds) {
+  using S = StageRegs<T, D, NT, TC>;
   using L = KvLds<T, D>;
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < S::KL; ++i) {
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
-    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = ((g.zero_mask >> i) & 1u) ? z : g.k[i];
+    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = ((g.zero_mask >> i) & 1u) ? z : stage_widen<T>(g.k[i]);
   }
   char* vt = lds + L::K_BYTES;
   if constexpr (sizeof(T) == 2) {
@@ -141,8 +157,8 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* 
       const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : g.v[i][0];
-      const u32x4 y = ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : g.v[i][1];
+      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
+      const u32x4 y = ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][1]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
@@ -158,7 +174,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT>& g, char* 
       const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : g.v[i][0];
+      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
     }
@@ -665,7 +681,7 @@ __device__ __forceinline__ KpItem kp_item_s(const KpArgs& a, int it) {
 // nsub, ...  Each item is two passes of 256 rows.  The next item's K/V and
 // token entries are prefetched into registers at the start of an item, the
 // next pass's queries while the current pass runs P.V.
-template <typename T, int D>
+template <typename T, int D, typename TC = T>
 __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
   using L = KvLds<T, D>;
   constexpr int NT = kKpThreads;
@@ -683,11 +699,11 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
   const int rho0 = wave * 32 + l32;                 // this lane's row in pass 0; pass 1 is + 256
   const int tid = threadIdx.x;
 
-  StageRegs<T, D, NT> pre;
+  StageRegs<T, D, NT, TC> pre;
   KpItem cur = kp_item_s<T, D>(a, it);
-  stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv));
+  stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv));
   int pre_ent = a.entries[cur.e_begin + min(tid, cur.e_end - cur.e_begin - 1)];
-  stage_store<T, D, NT>(pre, lds[0]);
+  stage_store<T, D, NT, TC>(pre, lds[0]);
   reinterpret_cast<int*>(lds[0] + L::BYTES)[tid] = pre_ent;
   __syncthreads();
   KpPass<T, D> ps;
@@ -700,7 +716,7 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
     int nxt_ent = 0;
     if (has_next) {
       nxt = kp_item_s<T, D>(a, nx);
-      stage_load<T, D, NT>(pre, block_ptr<T, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv));
+      stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv));
       const int ne = nxt.e_end - nxt.e_begin;
       pre_ent = a.entries[nxt.e_begin + min(tid, ne - 1)];
       nxt_ent = a.entries[nxt.e_begin + min(rho0 >> a.g_shift, ne - 1)];
@@ -731,7 +747,7 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
     if (!has_next) break;
     if (NB == 1) __syncthreads();
     char* dst = lds[NB == 2 ? (buf ^ 1) : 0];
-    stage_store<T, D, NT>(pre, dst);
+    stage_store<T, D, NT, TC>(pre, dst);
     reinterpret_cast<int*>(dst + L::BYTES)[tid] = pre_ent;
     __syncthreads();
     it = nx;
@@ -1277,7 +1293,7 @@ bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (
 bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
 bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 2) && (d_h == 64 || d_h == 128); }
 
-template <typename T, int D>
+template <typename T, int D, typename TC = T>
 static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
   char* ws = static_cast<char*>(a.ws);
   SchedArgs s{};
@@ -1358,7 +1374,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kp_wgs_per_cu<T, D>());
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
     const int pk = profile_begin(PK_KP, st);
-    hipLaunchKernelGGL((kp_kernel<T, D>), dim3(grid), dim3(kKpThreads), 0, st, kp);
+    hipLaunchKernelGGL((kp_kernel<T, D, TC>), dim3(grid), dim3(kKpThreads), 0, st, kp);
     profile_end(pk, st);
     km.w = w;
     const int64_t pairs = (int64_t)tok * a.h_kv;
@@ -1372,6 +1388,8 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
 
 hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const PrefillPlan& pl,
                                  hipStream_t st) {
+  if (dtype == 2 && d_h == 128) return sparse_prefill_typed<bf16_t, 128, fp8_t>(a, pl, st);
+  if (dtype == 2 && d_h == 64) return sparse_prefill_typed<bf16_t, 64, fp8_t>(a, pl, st);
   if (dtype == 0 && d_h == 128) return sparse_prefill_typed<bf16_t, 128>(a, pl, st);
   if (dtype == 0 && d_h == 64) return sparse_prefill_typed<bf16_t, 64>(a, pl, st);
   if (dtype == 1 && d_h == 128) return sparse_prefill_typed<float, 128>(a, pl, st);

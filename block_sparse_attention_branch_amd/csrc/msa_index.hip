@@ -27,6 +27,7 @@
 #include "msa_profile.hpp"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace msa {
 
@@ -77,7 +78,7 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
 }
 
 // ----------------------------------------------------------- prefill kernel
-template <typename T, int DIDX>
+template <typename T, int DIDX, typename TC = T>
 __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs a) {
   constexpr int KS = DIDX / 16;                       // 16-wide contraction steps
   constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
-  const T* __restrict__ k_idx = static_cast<const T*>(a.k_idx);
+  const TC* __restrict__ k_idx = static_cast<const TC*>(a.k_idx);
 
   const int my_row = row0 + wave * 64 + lane;  // row whose list this lane owns
   const bool my_valid = my_row < a.n_rows;
@@ -140,34 +141,45 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   // Thread i of the workgroup copies 16-byte pieces at fixed offsets of a
   // block; only the partial last block of a contiguous cache clamps its rows
   // (those keys lie after every query, so the causal mask drops them).
+  // With e4m3 caches each 16-byte (8-element) LDS chunk arrives as 8 bytes
+  // and is widened to bf16 when stored.
+  typedef typename std::conditional<sizeof(TC) == 1 && sizeof(T) == 2, u32x2, u32x4>::type Chunk;
+  constexpr int G_ROW = DIDX * (int)sizeof(TC);                   // cache bytes per key row
+  constexpr int G_CHUNK = 16 * (int)sizeof(TC) / (int)sizeof(T);  // cache bytes per LDS chunk
   uint32_t toff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int u = tid + kKiThreads * i;
-    toff[i] = (uint32_t)((u / CHUNKS_PER_ROW) * ROW_BYTES + (u % CHUNKS_PER_ROW) * 16);
+    toff[i] = (uint32_t)((u / CHUNKS_PER_ROW) * G_ROW + (u % CHUNKS_PER_ROW) * G_CHUNK);
   }
-  u32x4 pre0[LOADS], pre1[LOADS];
-  auto load_block = [&](u32x4 (&dst)[LOADS], int b) {
+  Chunk pre0[LOADS], pre1[LOADS];
+  auto load_block = [&](Chunk (&dst)[LOADS], int b) {
     const int64_t base_tok = a.page_table ? (int64_t)scalar_load(a.page_table, b) * kBlock : (int64_t)b * kBlock;
     const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX);
     if (a.page_table || (int64_t)b * kBlock + kBlock <= a.n_kv) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dst[i] = *reinterpret_cast<const u32x4*>(base + toff[i]);
+      for (int i = 0; i < LOADS; ++i) dst[i] = *reinterpret_cast<const Chunk*>(base + toff[i]);
     } else {
       const uint32_t last = (uint32_t)(a.n_kv - 1 - b * kBlock);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint32_t row = min(toff[i] / ROW_BYTES, last);
-        dst[i] = *reinterpret_cast<const u32x4*>(base + row * ROW_BYTES + toff[i] % ROW_BYTES);
+        const uint32_t row = min(toff[i] / G_ROW, last);
+        dst[i] = *reinterpret_cast<const Chunk*>(base + row * G_ROW + toff[i] % G_ROW);
       }
     }
   };
-  auto store_block = [&](const u32x4 (&src)[LOADS], int buf) {
+  auto store_block = [&](const Chunk (&src)[LOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int u = tid + kKiThreads * i;
       const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
-      *reinterpret_cast<u32x4*>(&lds[buf][j * LDS_STRIDE + c * 16]) = src[i];
+      u32x4 w;
+      if constexpr (sizeof(Chunk) == 8) {
+        w = __builtin_bit_cast(u32x4, fp8x8_to_bf16(src[i]));
+      } else {
+        w = src[i];
+      }
+      *reinterpret_cast<u32x4*>(&lds[buf][j * LDS_STRIDE + c * 16]) = w;
     }
   };
 
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   if (b_begin + 1 < b_end) load_block(pre0, b_begin + 1);
   __syncthreads();
   // one block: `cur` holds block b + 1, `nxt` receives block b + 2
-  auto block_step = [&](int b, u32x4 (&cur)[LOADS], u32x4 (&nxt)[LOADS]) {
+  auto block_step = [&](int b, Chunk (&cur)[LOADS], Chunk (&nxt)[LOADS]) {
     const int buf = (b - b_begin) & 1;
     if (b + 2 < b_end) load_block(nxt, b + 2);
     const char* K = lds[buf];
@@ -447,11 +459,11 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
 }
 
 // ----------------------------------------------------------------- launch
-template <typename T, int DIDX>
+template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.grid_chunks * a.n_tiles));
   const int pi = profile_begin(PK_KI_PREFILL, st);
-  hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX>), grid, dim3(kKiThreads), 0, st, a);
+  hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX, TC>), grid, dim3(kKiThreads), 0, st, a);
   profile_end(pi, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
@@ -490,6 +502,12 @@ bool ki_supported(int dtype, int d_idx) {
   } while (0)
 
 hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipStream_t st) {
+  if (dtype == 2) {  // bf16 queries, e4m3 cached index keys
+    if (d_idx == 32) return ki_prefill_typed<bf16_t, 32, fp8_t>(a, st);
+    if (d_idx == 64) return ki_prefill_typed<bf16_t, 64, fp8_t>(a, st);
+    if (d_idx == 128) return ki_prefill_typed<bf16_t, 128, fp8_t>(a, st);
+    return hipErrorInvalidValue;
+  }
   MSA_KI_DISPATCH(ki_prefill_typed, a, st);
 }
 hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st) {

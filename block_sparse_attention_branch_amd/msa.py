@@ -205,7 +205,8 @@ def sparse_prefill(q, k, v, block_idx, *, q_start=0, sm_scale=0.0, page_table=No
     h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
     nkv = int(n_kv) if n_kv is not None else k.shape[0]
     mp = page_table.numel() if page_table is not None else 0
-    shape = make_shape(h_q, h_kv, d_h, 64, top_k, _dtype_code(q), sm_scale=sm_scale)
+    dt = _dtype_code(q)
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale, cache_dtype=_cache_code(k, dt))
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((n_q, h_q), dtype=torch.float32, device=q.device) if with_lse else None
     nws = workspace_size(OP_PREFILL, shape, n_q=n_q, q_start=int(q_start), n_kv=nkv)

@@ -82,10 +82,9 @@ typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2 } msa_dtyp
  *   idx_scale    score scale of Eq. (6); 0 means 1/sqrt(d_idx).
  *   dtype        msa_dtype (BF16 or FP32) of every float tensor of the call.
  *   cache_dtype  MSA_FP8_E4M3: the caches k, v and k_idx hold e4m3 codes
- *                (paged decode calls with dtype MSA_BF16 only: msa_index_topk
- *                in decode mode and msa_sparse_decode); they are widened
- *                exactly to bf16 before use.  Any other value: the caches
- *                have type `dtype`.                                       */
+ *                (with dtype MSA_BF16; every call except
+ *                msa_dense_prefill); they are widened exactly to bf16
+ *                before use.  Any other value: the caches have type `dtype`. */
 typedef struct msa_shape {
   int32_t h_q, h_kv, d_h, d_idx, block_size, top_k, force_local;
   float sm_scale, idx_scale;

@@ -64,23 +64,25 @@ def _randn(shape, gen, device, dtype, scale=1.0, rows_per_chunk=None):
 
 def gen_prefill(n_kv: int, shape: HeadShape = MODEL_SHAPE, *, n_q: int | None = None,
                 dtype=torch.bfloat16, seed: int = 1, device="cpu",
-                scaled: bool = True) -> dict:
+                scaled: bool = True, cache_dtype=None) -> dict:
     """One contiguous sequence: K/V/K_idx for ``n_kv`` tokens and queries for the
     last ``n_q`` positions (``q_start = n_kv - n_q``).
 
     Layouts: q [n_q, h_q, d_h], k/v [n_kv, h_kv, d_h], q_idx [n_q, h_kv, d_idx],
     k_idx [n_kv, d_idx].  With ``scaled`` every tensor is N(0,1)/sqrt(last dim),
-    otherwise N(0,1).
+    otherwise N(0,1).  ``cache_dtype`` (default ``dtype``) is the storage type
+    of k, v and k_idx, e.g. torch.float8_e4m3fn.
     """
+    cdt = dtype if cache_dtype is None else cache_dtype
     n_q = n_kv if n_q is None else n_q
     g = _gen(seed, device)
     sh = lambda d: (1.0 / math.sqrt(d)) if scaled else 1.0  # noqa: E731
     out = {
         "q": _randn((n_q, shape.h_q, shape.d_h), g, device, dtype, sh(shape.d_h)),
-        "k": _randn((n_kv, shape.h_kv, shape.d_h), g, device, dtype, sh(shape.d_h)),
-        "v": _randn((n_kv, shape.h_kv, shape.d_h), g, device, dtype, sh(shape.d_h)),
+        "k": _randn((n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h)),
+        "v": _randn((n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h)),
         "q_idx": _randn((n_q, shape.h_kv, shape.d_idx), g, device, dtype, sh(shape.d_idx)),
-        "k_idx": _randn((n_kv, shape.d_idx), g, device, dtype, sh(shape.d_idx)),
+        "k_idx": _randn((n_kv, shape.d_idx), g, device, cdt, sh(shape.d_idx)),
     }
     out["q_start"] = n_kv - n_q
     out["n_kv"] = n_kv

@@ -126,3 +126,22 @@ def test_profile_api_host_side():
     with pytest.raises(msa.MsaError) as e:
         msa.profile_read("no_such_kernel")
     assert e.value.status == 1
+
+
+def test_e4m3_cache_validation():
+    """e4m3 caches are accepted with bf16 compute by every call but the dense one."""
+    L = msa.lib()
+    f8 = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, cache_dtype=msa.MSA_FP8_E4M3)
+    f8_32 = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_FP32, cache_dtype=msa.MSA_FP8_E4M3)
+    kv = msa.KV(FAKE, FAKE, None, None, None, 256, 0)
+    assert L.msa_dense_prefill(ctypes.byref(f8), 8, 0, FAKE, ctypes.byref(kv), FAKE, None, None, 0, None) == 2
+    assert "dense" in _err()
+    assert L.msa_sparse_prefill(ctypes.byref(f8_32), 8, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0,
+                                None) == 2
+    assert "MSA_BF16" in _err()
+    assert _idx_call(f8_32) == 2 and "MSA_BF16" in _err()
+    # accepted: the call gets as far as the workspace check
+    assert _idx_call(f8, n_q=20000, n_kv=20000) == 3
+    assert msa.workspace_size(msa.OP_PREFILL, f8, n_q=8, n_kv=256) > 0
+    assert msa.lib().msa_workspace_size(msa.OP_DENSE, ctypes.byref(f8), 1, 8, 0, 8, 0) == 0
+    assert "dense" in _err()

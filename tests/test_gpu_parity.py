@@ -139,6 +139,49 @@ def test_prefill_groups_of_1_2_and_8():
     _prefill_case(HeadShape(16, 2, 128, 64, 16), 1400, 1400, torch.bfloat16, 17, use_gpu_index=True)
 
 
+def _e4m3_prefill_case(shape, n_kv, n_q, seed, paged):
+    msa = _msa()
+    f8 = torch.float8_e4m3fn
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV, cache_dtype=f8)
+    q_start = inp["q_start"]
+    _say("e4m3 prefill", shape, n_kv, n_q, seed, "paged" if paged else "contiguous")
+    k, v, ki = inp["k"], inp["v"], inp["k_idx"]
+    kw = {}
+    if paged:
+        # the same tokens in head-major 128-token pages placed by a random permutation
+        nb = -(-n_kv // 128)
+        pad = nb * 128 - n_kv
+        perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+        def pages(t):
+            u8 = t.view(torch.uint8)
+            u8 = torch.cat([u8, torch.zeros((pad,) + u8.shape[1:], dtype=torch.uint8, device=DEV)])
+            u8 = u8.view((nb, 128) + u8.shape[1:])
+            if u8.dim() == 4:
+                u8 = u8.permute(0, 2, 1, 3)
+            out = torch.empty_like(u8.contiguous())
+            out[perm.long().to(DEV)] = u8.contiguous()
+            return out.view(f8)
+        k, v, ki = pages(k), pages(v), pages(ki)
+        kw = dict(page_table=perm.to(DEV), n_kv=n_kv)
+    bidx = msa.index_topk(inp["q_idx"], ki, top_k=shape.top_k, q_start=q_start, **kw)
+    o, lse = msa.sparse_prefill(inp["q"], k, v, bidx, q_start=q_start, with_lse=True, **kw)
+    torch.cuda.synchronize()
+    k64 = orc.decode_e4m3(inp["k"].view(torch.uint8).cpu().numpy())
+    v64 = orc.decode_e4m3(inp["v"].view(torch.uint8).cpu().numpy())
+    ki64 = orc.decode_e4m3(inp["k_idx"].view(torch.uint8).cpu().numpy())
+    o_ids, _, pooled = orc.index_topk(np64(inp["q_idx"]), ki64, q_start, shape.top_k)
+    compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, (q_start + np.arange(n_q)) // 128)
+    o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), k64, v64, bidx.cpu().numpy(), q_start)
+    compare_out(o, o_ref, torch.bfloat16)
+    compare_lse(lse, lse_ref, torch.bfloat16)
+
+
+def test_prefill_e4m3_caches_contiguous_and_paged():
+    _e4m3_prefill_case(MODEL_SHAPE, 2300, 2300, 29, paged=False)
+    _e4m3_prefill_case(HeadShape(16, 2, 64, 32, 6), 1700, 900, 30, paged=True)
+    _e4m3_prefill_case(HeadShape(16, 4, 128, 128, 16), 1300, 1300, 31, paged=True)
+
+
 def test_prefill_full_coverage_equals_dense():
     msa = _msa()
     shape = HeadShape(16, 2, 128, 64, 16)
@@ -245,15 +288,6 @@ def test_decode_e4m3_caches():
     _decode_case(MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049], 25, cache_dtype=f8)
     _decode_case(HeadShape(16, 2, 64, 32, 16), [5000, 2500, 700], 26, cache_dtype=f8)
     _decode_case(HeadShape(16, 4, 128, 128, 8), [1500, 9000], 27, cache_dtype=f8)
-
-
-def test_decode_e4m3_rejected_for_prefill_calls():
-    msa = _msa()
-    inp = gen_prefill(300, MODEL_SHAPE, dtype=torch.bfloat16, seed=28, device=DEV)
-    k8 = inp["k_idx"].to(torch.float8_e4m3fn)
-    with pytest.raises(msa.MsaError) as e:
-        msa.index_topk(inp["q_idx"], k8, top_k=16)
-    assert "e4m3" in str(e.value)
 
 
 def test_decode_single_long_sequence():
