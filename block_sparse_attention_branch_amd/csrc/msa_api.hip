@@ -91,8 +91,6 @@ size_t ki_prefill_ws(const msa_shape& s, int32_t n_q, int32_t q_start, int need_
   return ((keys + 255) & ~size_t(255)) + (((size_t)p.n_rows * 4 + 255) & ~size_t(255));
 }
 
-constexpr int32_t kMaxDecodePages = 16384;
-
 }  // namespace
 
 extern "C" {
@@ -176,8 +174,8 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   if (kv->seq_lens) {  // decode mode
     if (n_q != 1) return fail(MSA_ERR_INVALID_ARG, "decode mode (seq_lens given) needs n_q == 1, got %d", n_q);
     if (!kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs a page_table");
-    if (kv->max_pages < 1 || kv->max_pages > kMaxDecodePages)
-      return fail(MSA_ERR_UNSUPPORTED, "max_pages=%d not in [1,%d]", kv->max_pages, kMaxDecodePages);
+    if (kv->max_pages < 1 || kv->max_pages > msa::kMaxDecodePages)
+      return fail(MSA_ERR_UNSUPPORTED, "max_pages=%d not in [1,%d]", kv->max_pages, msa::kMaxDecodePages);
     if (batch == 0) return ok();
     if (!q_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "q_idx/block_idx is NULL");
     const size_t need = (size_t)batch * s.h_kv * kv->max_pages * 4;

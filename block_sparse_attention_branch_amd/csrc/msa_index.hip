@@ -394,8 +394,32 @@ constexpr int kSelectMaxSurvivors = 1024;  // 16 threads x up to 64 candidates e
 //  2) every key >= T survives (only those 16 threads hold any);
 //  3) each survivor's rank among the survivors places the best 16 in order.
 // Ranks are counted against values in LDS, so the selection needs no sort
-// and only a few barriers.
+// and only a few barriers.  The row is read from global memory once, eight
+// independent loads per thread at a time, and kept in LDS for step 2.
+// Copies the row's scores into LDS (U independent loads per thread in
+// flight) and returns this thread's largest key.
+template <int U>
+__device__ __forceinline__ uint64_t select_load_row(const float* sc, int ncand, float* row_s) {
+  uint64_t tmax = 0;
+  for (int b0 = threadIdx.x; b0 < ncand; b0 += 256 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = sc[min(b0 + 256 * u, ncand - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = b0 + 256 * u;
+      if (b < ncand) {
+        row_s[b] = v[u];
+        const uint64_t k = make_key(v[u], b);
+        tmax = k > tmax ? k : tmax;
+      }
+    }
+  }
+  return tmax;
+}
+
 __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
+  __shared__ float row_s[kMaxDecodePages];
   __shared__ uint64_t tm[256];
   __shared__ uint64_t surv[kSelectMaxSurvivors];
   __shared__ uint64_t top[kMaxTopK];
@@ -404,15 +428,11 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
   const int L = scalar_load(a.seq_lens, s);
   const int diag = (L - 1) / kBlock;
-  const int ncand = a.force_local ? diag : diag + 1;
+  const int ncand = min(a.force_local ? diag : diag + 1, a.max_pages);
   const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
   const int tid = threadIdx.x;
 
-  uint64_t tmax = 0;
-  for (int b = tid; b < ncand; b += 256) {
-    const uint64_t k = make_key(sc[b], b);
-    tmax = k > tmax ? k : tmax;
-  }
+  const uint64_t tmax = ncand > 256 * 8 ? select_load_row<32>(sc, ncand, row_s) : select_load_row<8>(sc, ncand, row_s);
   tm[tid] = tmax;
   if (tid == 0) {
     count = 0;
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
   const uint64_t thr = thr_s;
   if (tmax >= thr && tmax != 0) {
     for (int b = tid; b < ncand; b += 256) {
-      const uint64_t k = make_key(sc[b], b);
+      const uint64_t k = make_key(row_s[b], b);
       if (k >= thr) {
         const int pos = atomicAdd(&count, 1);
         if (pos < kSelectMaxSurvivors) surv[pos] = k;
@@ -445,16 +465,40 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
     if (rk < kMaxTopK) top[rk] = k;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint64_t keys[kMaxTopK];
-#pragma unroll
-    for (int t = 0; t < kMaxTopK; ++t) keys[t] = top[t];
-    float dscore = -__builtin_inff();
-    if (a.force_local && a.need_diag) dscore = sc[diag];
+  // Assemble the row on wave 0: lane e < 16 holds the e-th best key (used if
+  // e < n_take and non-empty), lane 16 the forced diagonal block; a valid
+  // entry's rank by block id is its output slot, and the slots past the
+  // valid entries get the -1 / -inf padding.
+  if (tid < 64) {
     const int n_take = a.top_k - (a.force_local ? 1 : 0);
+    int id = 0x7fffffff;
+    float scv = 0.0f;
+    if (tid < kMaxTopK) {
+      const uint64_t k = top[tid];
+      if (tid < n_take && k != 0ull) {
+        id = key_block(k);
+        scv = key_score(k);
+      }
+    } else if (tid == kMaxTopK && a.force_local) {
+      id = diag;
+      scv = a.need_diag ? sc[diag] : -__builtin_inff();
+    }
+    int rk = 0;
+#pragma unroll
+    for (int j = 0; j <= kMaxTopK; ++j) rk += __shfl(id, j, 64) < id ? 1 : 0;
+    const bool valid = id != 0x7fffffff;
+    const int n_valid = __popcll(__ballot(valid));
     const size_t row = (size_t)s * a.h_kv + r;
-    write_row_list(keys, n_take, a.force_local ? diag : -1, dscore, a.top_k,
-                   a.block_idx + row * a.top_k, a.block_score ? a.block_score + row * a.top_k : nullptr);
+    int32_t* idx_out = a.block_idx + row * a.top_k;
+    float* sc_out = a.block_score ? a.block_score + row * a.top_k : nullptr;
+    if (valid) {
+      idx_out[rk] = id;
+      if (sc_out) sc_out[rk] = scv;
+    }
+    if (tid >= n_valid && tid < a.top_k) {
+      idx_out[tid] = -1;
+      if (sc_out) sc_out[tid] = -__builtin_inff();
+    }
   }
 }
 

@@ -8,6 +8,9 @@
 
 namespace msa {
 
+// Largest page-table width (pages per sequence) the decode calls accept.
+constexpr int kMaxDecodePages = 16384;
+
 // ---------------------------------------------------------------- index
 // Tiles of 256 (query, group) rows; the block range [0, hi) of a tile is cut
 // into chunks of `chunk_blocks` blocks; every (tile, chunk) is one workgroup.
