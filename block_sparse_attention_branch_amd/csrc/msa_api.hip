@@ -51,6 +51,8 @@ msa_status check_shape(const msa_shape* s, bool need_idx, bool need_attn) {
   if (s->force_local != 0 && s->force_local != 1) return fail(MSA_ERR_INVALID_ARG, "force_local=%d must be 0 or 1", s->force_local);
   if (!(s->sm_scale >= 0.f) || !(s->idx_scale >= 0.f))
     return fail(MSA_ERR_INVALID_ARG, "sm_scale=%g idx_scale=%g must be >= 0 (0 = default)", s->sm_scale, s->idx_scale);
+  if (need_idx && s->pool != MSA_POOL_MAX && s->pool != MSA_POOL_MEAN)
+    return fail(MSA_ERR_INVALID_ARG, "pool=%d is not a msa_pool", s->pool);
   if (need_idx && !msa::ki_supported(s->dtype, s->d_idx))
     return fail(MSA_ERR_UNSUPPORTED, "d_idx=%d not in {32,64,128}", s->d_idx);
   if (need_attn && !msa::attn_supported(s->dtype, s->d_h))
@@ -195,6 +197,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
     }
     a.idx_scale = idx_scale;
     a.force_local = s.force_local;
+    a.pool = s.pool;
     a.top_k = s.top_k;
     a.need_diag = need_diag;
     a.scores = static_cast<float*>(workspace);
@@ -229,6 +232,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   a.n_tiles = p.n_tiles;
   a.idx_scale = idx_scale;
   a.force_local = s.force_local;
+  a.pool = s.pool;
   a.top_k = s.top_k;
   a.need_diag = need_diag;
   a.block_idx = block_idx;

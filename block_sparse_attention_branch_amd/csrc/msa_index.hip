@@ -4,7 +4,9 @@
 // titansim.online, §4.2 Eq. (6) and §4.4.1; tensor shapes per the 163.com
 // commentary, "Step 1 Index Attention"):
 //   S_j = q_idx^(r) . k_idx_j * idx_scale        (keys j <= p)
-//   M_b = max_{j in block b, j <= p} S_j          (block max-pool)
+//   M_b = max_{j in block b, j <= p} S_j          (block max-pool; as an
+//         ablation the mean over the same keys, the block scoring the
+//         163.com commentary attributes to MoBA)
 //   I   = top-k of M on the raw scores (no exp / softmax: the order is the
 //         same), ties to the lower block, diagonal block kept if forced.
 //
@@ -21,7 +23,7 @@
 // Decode: a paged scan writes M for every page of each sequence (HBM-bound,
 // one query per group, 16x16x32 MFMA with the groups as rows), then one
 // workgroup per (sequence, group) selects the top-k with a threshold filter
-// and LDS bitonic sorts.
+// and rank counting (no sort).
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
 #include "msa_profile.hpp"
@@ -78,7 +80,8 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
 }
 
 // ----------------------------------------------------------- prefill kernel
-template <typename T, int DIDX, typename TC = T>
+// POOL: 0 block max-pool (the method), 1 block mean-pool.
+template <typename T, int DIDX, typename TC, int POOL>
 __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs a) {
   constexpr int KS = DIDX / 16;                       // 16-wide contraction steps
   constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
     if (b + 2 < b_end) load_block(nxt, b + 2);
     const char* K = lds[buf];
     const bool masked = b >= min_diag;
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+    constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
+    float m0 = kDrop, m1 = kDrop;
     // not unrolled: an unrolled nest keeps every tile's addresses and mask
     // constants live and halves the occupancy
 #pragma unroll 1
@@ -212,21 +216,32 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key > col_pos[0]) acc0[v] = -__builtin_inff();
-          if (key > col_pos[1]) acc1[v] = -__builtin_inff();
+          if (key > col_pos[0]) acc0[v] = kDrop;
+          if (key > col_pos[1]) acc1[v] = kDrop;
         }
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        m0 = fmaxf(m0, acc0[v]);
-        m1 = fmaxf(m1, acc1[v]);
+        if constexpr (POOL == 0) {
+          m0 = fmaxf(m0, acc0[v]);
+          m1 = fmaxf(m1, acc1[v]);
+        } else {
+          m0 += acc0[v];
+          m1 += acc1[v];
+        }
       }
     }
     // lanes l and l+32 hold the two key halves of rows l and 32+l: swap so
     // that lane L ends with the whole-block max of wave row L
     const float send = half ? m0 : m1;
     const float recv = __shfl_xor(send, 32, 64);
-    const float pooled = fmaxf(half ? m1 : m0, recv) * a.idx_scale;
+    float pooled;
+    if constexpr (POOL == 0) {
+      pooled = fmaxf(half ? m1 : m0, recv) * a.idx_scale;
+    } else {  // mean over the keys of block b visible from this lane's row
+      const int cnt = min(kBlock, a.q_start + (my_valid ? my_row : row_last) / a.h_kv - b * kBlock + 1);
+      pooled = cnt > 0 ? ((half ? m1 : m0) + recv) * a.idx_scale / (float)cnt : -__builtin_inff();
+    }
     if (my_valid) {
       const bool cand = a.force_local ? (b < my_diag) : (b <= my_diag);
       if (cand) {
@@ -320,7 +335,7 @@ __device__ __forceinline__ void ki_load_page(Raw<TC> (&f)[8][DIDX / 32], const T
 
 // T: dtype of q_idx and of the MFMA; TC: dtype of the cached k_idx (T, or
 // e4m3 widened to bf16 after loading).
-template <typename T, int DIDX, typename TC>
+template <typename T, int DIDX, typename TC, int POOL>
 __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   constexpr int KS = DIDX / 32;
   const int s = blockIdx.y;
@@ -351,7 +366,8 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     if (!kPipe) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
     if (kPipe && pg + 4 < pg_end)
       ki_load_page<TC, DIDX>(nxt, k_idx + (size_t)scalar_load(pt, pg + 4) * kBlock * DIDX);
-    float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
+    float m[4] = {kDrop, kDrop, kDrop, kDrop};
     const bool masked = (pg == nb - 1);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
@@ -360,18 +376,34 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
       for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], widen<T, TC>(cur[kt][ks]));
       const bool vis = !masked || (pg * kBlock + kt * 16 + l16 <= p);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) m[v] = fmaxf(m[v], vis ? acc[v] : -__builtin_inff());
+      for (int v = 0; v < 4; ++v) {
+        if constexpr (POOL == 0) {
+          m[v] = fmaxf(m[v], vis ? acc[v] : kDrop);
+        } else {
+          m[v] += vis ? acc[v] : kDrop;
+        }
+      }
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) m[v] = fmaxf(m[v], __shfl_xor(m[v], off, 64));
+      for (int off = 1; off < 16; off <<= 1) {
+        if constexpr (POOL == 0) {
+          m[v] = fmaxf(m[v], __shfl_xor(m[v], off, 64));
+        } else {
+          m[v] += __shfl_xor(m[v], off, 64);
+        }
+      }
     }
+    // mean-pool: the page's visible keys (all 128 but on the last page)
+    const float inv_cnt = POOL == 0 ? 1.0f : 1.0f / (float)(masked ? p - pg * kBlock + 1 : kBlock);
     if (l16 == 0) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int g = 4 * q4 + v;
-        if (g < a.h_kv) a.scores[((size_t)s * a.h_kv + g) * a.max_pages + pg] = m[v] * a.idx_scale;
+        if (g < a.h_kv)
+          a.scores[((size_t)s * a.h_kv + g) * a.max_pages + pg] =
+              POOL == 0 ? m[v] * a.idx_scale : m[v] * a.idx_scale * inv_cnt;
       }
     }
     if (kPipe) {
@@ -507,7 +539,10 @@ template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.grid_chunks * a.n_tiles));
   const int pi = profile_begin(PK_KI_PREFILL, st);
-  hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX, TC>), grid, dim3(kKiThreads), 0, st, a);
+  if (a.pool == 1)
+    hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX, TC, 1>), grid, dim3(kKiThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((ki_prefill_kernel<T, DIDX, TC, 0>), grid, dim3(kKiThreads), 0, st, a);
   profile_end(pi, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
@@ -519,7 +554,10 @@ template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
   dim3 grid((a.max_pages + a.pages_per_wg - 1) / a.pages_per_wg, a.batch);
   const int ps = profile_begin(PK_KI_DECODE_SCAN, st);
-  hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX, TC>), grid, dim3(256), 0, st, a);
+  if (a.pool == 1)
+    hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX, TC, 1>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX, TC, 0>), grid, dim3(256), 0, st, a);
   profile_end(ps, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -29,6 +29,7 @@ struct KiPrefillArgs {
   int32_t n_tiles;
   float idx_scale;
   int32_t force_local;
+  int32_t pool;             // msa_pool: 0 max, 1 mean
   int32_t top_k;
   int32_t need_diag;        // diagonal block must be scored
   int32_t* block_idx;       // [n_rows, top_k]
@@ -48,6 +49,7 @@ struct KiDecodeArgs {
   int32_t pages_per_wg;
   float idx_scale;
   int32_t force_local;
+  int32_t pool;             // msa_pool: 0 max, 1 mean
   int32_t top_k;
   int32_t need_diag;
   float* scores;            // workspace [batch, h_kv, max_pages]

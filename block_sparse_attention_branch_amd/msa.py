@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
+MSA_POOL_MAX, MSA_POOL_MEAN = 0, 1
 OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE = 0, 1, 2, 3, 4
 BLOCK = 128
 
@@ -33,7 +34,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("d_idx", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("force_local", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
+                ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
+                ("pool", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -109,10 +111,19 @@ def _stream(stream) -> int | None:
 
 
 def make_shape(h_q, h_kv, d_h, d_idx, top_k, dtype_code, *, force_local=True,
-               sm_scale=0.0, idx_scale=0.0, cache_dtype=None) -> Shape:
+               sm_scale=0.0, idx_scale=0.0, cache_dtype=None, pool=None) -> Shape:
     cd = int(dtype_code) if cache_dtype is None else int(cache_dtype)
     return Shape(int(h_q), int(h_kv), int(d_h), int(d_idx), BLOCK, int(top_k),
-                 1 if force_local else 0, float(sm_scale), float(idx_scale), int(dtype_code), cd)
+                 1 if force_local else 0, float(sm_scale), float(idx_scale), int(dtype_code), cd,
+                 _pool_code(pool))
+
+
+def _pool_code(pool) -> int:
+    if pool is None or pool == "max":
+        return MSA_POOL_MAX
+    if pool == "mean":
+        return MSA_POOL_MEAN
+    return int(pool)
 
 
 def _cache_code(t: torch.Tensor, compute_code: int) -> int:
@@ -158,8 +169,8 @@ def profile_read(kernel: str):
 
 def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale=0.0,
                page_table=None, n_kv=None, seq_lens=None, max_pages=None, h_q=None,
-               with_scores=False, out=None, workspace=None, stream=None):
-    """msa_index_topk.  Prefill mode: q_idx [n_q, h_kv, d_idx], k_idx
+               with_scores=False, out=None, workspace=None, stream=None, pool="max"):
+    """msa_index_topk (``pool``: "max", the method's block max-pool, or "mean").  Prefill mode: q_idx [n_q, h_kv, d_idx], k_idx
     [n_kv, d_idx] (or pages [*, 128, d_idx] with ``page_table``).  Decode mode
     (``seq_lens`` given): q_idx [batch, h_kv, d_idx], one query per sequence.
     Returns block_idx int32 [rows, h_kv, top_k] (and fp32 scores)."""
@@ -181,7 +192,7 @@ def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale
         mp = int(max_pages)
     dt = _dtype_code(q_idx)
     shape = make_shape(h_q or h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local,
-                       idx_scale=idx_scale, cache_dtype=_cache_code(k_idx, dt))
+                       idx_scale=idx_scale, cache_dtype=_cache_code(k_idx, dt), pool=pool)
     dev = q_idx.device
     bidx = out if out is not None else torch.empty((rows, h_kv, top_k), dtype=torch.int32, device=dev)
     scores = torch.empty((rows, h_kv, top_k), dtype=torch.float32, device=dev) if with_scores else None

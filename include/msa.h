@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 #define MSA_BLOCK_SIZE 128
 #define MSA_MAX_TOP_K 16
 
@@ -67,6 +67,12 @@ typedef enum msa_status {
 /* MSA_FP8_E4M3: OCP 8-bit float e4m3 ("fn": bias 7, no infinities), one
  * byte per element, used as stored (no scale).  Only for the caches. */
 typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2 } msa_dtype;
+
+/* Block scoring of the index branch.  MSA_POOL_MAX is the method's max-pool
+ * ([P1] §4.2 Eq. (6)); MSA_POOL_MEAN averages the visible token scores of a
+ * block instead, the block scoring the [P5] commentary ("Step 1 Index
+ * Attention") contrasts MSA with (MoBA), kept as an ablation. */
+typedef enum msa_pool { MSA_POOL_MAX = 0, MSA_POOL_MEAN = 1 } msa_pool;
 
 /* Head shapes and method hyper-parameters.
  *   h_q, h_kv    query heads and KV heads (GQA groups); h_q % h_kv == 0 and
@@ -84,12 +90,15 @@ typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2 } msa_dtyp
  *   cache_dtype  MSA_FP8_E4M3: the caches k, v and k_idx hold e4m3 codes
  *                (with dtype MSA_BF16; every call except
  *                msa_dense_prefill); they are widened exactly to bf16
- *                before use.  Any other value: the caches have type `dtype`. */
+ *                before use.  Any other value: the caches have type `dtype`.
+ *   pool         msa_pool: block scoring of msa_index_topk (other calls
+ *                ignore it). */
 typedef struct msa_shape {
   int32_t h_q, h_kv, d_h, d_idx, block_size, top_k, force_local;
   float sm_scale, idx_scale;
   int32_t dtype;
   int32_t cache_dtype;
+  int32_t pool;
 } msa_shape;
 
 /* The KV side of a call.
@@ -111,7 +120,8 @@ typedef struct msa_kv {
 /* Index branch: [P1] §4.2 Eq. (6) and §4.4.1; shapes from [P5] Step 1.
  * For every query and KV group r:
  *   S_j  = q_idx^(r) . k_idx_j * idx_scale           for keys j <= p
- *   M_b  = max over visible j in block b of S_j      (block max-pool)
+ *   M_b  = max over visible j in block b of S_j      (block max-pool; with
+ *          pool == MSA_POOL_MEAN the mean over the same keys)
  *   I    = exp-free top-k of M (ties: lower block wins), diagonal block
  *          kept when force_local.
  * Two modes, chosen by kv->seq_lens:

@@ -12,7 +12,9 @@ Sources (the pages this follows):
        §4.4.1 exp-free selection; §5.2 Eq. (12) FLOP model; §3.1 shapes.
   [P5] 163.com commentary on MSA, "Step 1 Index Attention": one index query
        per GQA group, one shared index key (Q_idx in R^{n x h x d},
-       K_idx in R^{n x 1 x d}); max-pool rather than mean-pool.
+       K_idx in R^{n x 1 x d}); max-pool rather than mean-pool (the mean
+       over a block's tokens is the block scoring it attributes to MoBA;
+       kept here as an ablation, ``pool="mean"``).
 
 Readings taken where the pages are silent:
   * query i of a call sits at absolute position p = q_start + i;
@@ -73,6 +75,27 @@ def block_max_pool(scores, p, block=BLOCK):
     return out
 
 
+def block_mean_pool(scores, p, block=BLOCK):
+    """Ablation of Eq. (6): the mean of S_j over the visible keys j <= p of
+    block b instead of their max ([P5] "Step 1 Index Attention" contrasts
+    the two).  ``scores`` [h_kv, p + 1].  Returns [h_kv, p // block + 1]."""
+    s = _f64(scores)
+    nb = p // block + 1
+    out = np.empty((s.shape[0], nb))
+    for b in range(nb):
+        lo, hi = b * block, min(b * block + block, p + 1)
+        out[:, b] = s[:, lo:hi].sum(axis=1) / (hi - lo)
+    return out
+
+
+def _pool(scores, p, pool, block):
+    if pool == "max":
+        return block_max_pool(scores, p, block)
+    if pool == "mean":
+        return block_mean_pool(scores, p, block)
+    raise ValueError(f"pool must be 'max' or 'mean', got {pool!r}")
+
+
 def select_blocks(m_row, diag, top_k, force_local=True):
     """Exp-free causal top-k over one row of pooled scores ([P1] §4.2, §4.4.1).
 
@@ -103,7 +126,7 @@ def select_blocks(m_row, diag, top_k, force_local=True):
 
 
 def index_topk(q_idx, k_idx, q_start, top_k, *, force_local=True, idx_scale=None,
-               rows=None, block=BLOCK):
+               rows=None, block=BLOCK, pool="max"):
     """Index branch for one contiguous sequence.
 
     ``q_idx`` [n_q, h_kv, d_idx], ``k_idx`` [n_kv, d_idx].  Query i sits at
@@ -120,7 +143,7 @@ def index_topk(q_idx, k_idx, q_start, top_k, *, force_local=True, idx_scale=None
     for i in rows:
         p = q_start + int(i)
         s = index_token_scores(q_idx[i], k_idx, p, idx_scale)
-        m = block_max_pool(s, p, block)
+        m = _pool(s, p, pool, block)
         diag = p // block
         ids = np.stack([select_blocks(m[r], diag, top_k, force_local) for r in range(h_kv)])
         sc = np.where(ids >= 0, np.take_along_axis(m, np.maximum(ids, 0), axis=1), -np.inf)
@@ -234,7 +257,7 @@ def gather_sequence(page_table_row, seq_len, k_pages=None, v_pages=None,
 
 
 def index_topk_decode(q_idx, k_idx_pages, page_table, seq_lens, top_k, *,
-                      force_local=True, idx_scale=None, seqs=None, block=BLOCK):
+                      force_local=True, idx_scale=None, seqs=None, block=BLOCK, pool="max"):
     """Decode-time index branch: one query per sequence at position
     seq_len - 1 over its paged index keys.  ``q_idx`` [batch, h_kv, d_idx].
     Returns (block_idx [n, h_kv, k], block_score [n, h_kv, k], pooled list)."""
@@ -244,7 +267,8 @@ def index_topk_decode(q_idx, k_idx_pages, page_table, seq_lens, top_k, *,
         L = int(seq_lens[s])
         seq = gather_sequence(page_table[s], L, k_idx_pages=k_idx_pages, block=block)
         i_s, sc_s, m_s = index_topk(_f64(q_idx)[s:s + 1], seq["k_idx"], L - 1, top_k,
-                                    force_local=force_local, idx_scale=idx_scale, block=block)
+                                    force_local=force_local, idx_scale=idx_scale, block=block,
+                                    pool=pool)
         ids.append(i_s[0])
         scs.append(sc_s[0])
         pooled.append(m_s[0])

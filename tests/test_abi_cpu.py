@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     L = msa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.msa_abi_version() == 2
+    assert L.msa_abi_version() == 3
     for st in range(5):
         assert L.msa_status_string(st).decode().startswith("MSA_")
 
@@ -145,3 +145,16 @@ def test_e4m3_cache_validation():
     assert msa.workspace_size(msa.OP_PREFILL, f8, n_q=8, n_kv=256) > 0
     assert msa.lib().msa_workspace_size(msa.OP_DENSE, ctypes.byref(f8), 1, 8, 0, 8, 0) == 0
     assert "dense" in _err()
+
+
+def test_pool_mode_validation():
+    s = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, pool=7)
+    assert _idx_call(s) == 1 and "pool" in _err()
+    s = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, pool="mean")
+    assert s.pool == msa.MSA_POOL_MEAN
+    assert _idx_call(s, n_q=0) == 0
+    # the attention calls ignore the index branch's pool mode
+    kv = msa.KV(FAKE, FAKE, None, None, None, 256, 0)
+    bad = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, pool=7)
+    assert msa.lib().msa_sparse_prefill(ctypes.byref(bad), 0, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0,
+                                        None) == 0

@@ -34,17 +34,19 @@ def _say(*a):
 
 # ------------------------------------------------------------------ index branch
 
-def _index_case(shape, n_kv, n_q, dtype, seed, *, force_local=True, with_scores=False, scaled=True):
+def _index_case(shape, n_kv, n_q, dtype, seed, *, force_local=True, with_scores=False, scaled=True, pool="max",
+                cache_dtype=None):
     msa = _msa()
-    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=dtype, seed=seed, device=DEV, scaled=scaled)
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=dtype, seed=seed, device=DEV, scaled=scaled,
+                      cache_dtype=cache_dtype)
     q_start = inp["q_start"]
-    _say("index_topk", shape, n_kv, n_q, dtype, seed, force_local)
+    _say("index_topk", shape, n_kv, n_q, dtype, seed, force_local, pool, cache_dtype)
     out = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k, q_start=q_start,
-                         force_local=force_local, with_scores=with_scores)
+                         force_local=force_local, with_scores=with_scores, pool=pool)
     torch.cuda.synchronize()
     ids, sc = out if with_scores else (out, None)
-    o_ids, o_sc, pooled = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q_start, shape.top_k,
-                                         force_local=force_local)
+    o_ids, o_sc, pooled = orc.index_topk(np64(inp["q_idx"]), _cache_host(inp["k_idx"]), q_start, shape.top_k,
+                                         force_local=force_local, pool=pool)
     diags = (q_start + np.arange(n_q)) // 128
     n_exact, n_exc = compare_index_rows(ids.cpu().numpy(), o_ids, pooled, diags, force_local)
     if sc is not None:
@@ -89,6 +91,46 @@ def test_index_short_sequences():
     _index_case(MODEL_SHAPE, 130, 130, torch.bfloat16, 6)
     _index_case(MODEL_SHAPE, 1, 1, torch.bfloat16, 7)
     _index_case(MODEL_SHAPE, 500, 1, torch.bfloat16, 8)
+
+
+def test_index_mean_pool_prefill():
+    # the mean-pool ablation: ragged tail, chunked unaligned start, no forced
+    # block, fp32, d_idx 32 and 128, e4m3 index keys
+    _index_case(MODEL_SHAPE, 2300, 2300, torch.bfloat16, 40, pool="mean", with_scores=True)
+    _index_case(MODEL_SHAPE, 3000, 700, torch.bfloat16, 41, pool="mean")
+    _index_case(HeadShape(8, 2, 64, 64, 5), 1500, 1500, torch.bfloat16, 42, force_local=False, pool="mean",
+                with_scores=True)
+    _index_case(TINY_SHAPE, 2048, 2048, torch.float32, 43, scaled=False, pool="mean")
+    _index_case(HeadShape(16, 4, 128, 128, 3), 1100, 1100, torch.bfloat16, 44, pool="mean")
+    _index_case(HeadShape(16, 4, 128, 32, 16), 900, 900, torch.bfloat16, 45, pool="mean",
+                cache_dtype=torch.float8_e4m3fn)
+
+
+def test_index_mean_pool_decode():
+    msa = _msa()
+    for shape, seq_lens, seed, cdt in ((MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049, 40000], 46, None),
+                                       (HeadShape(16, 2, 64, 32, 16), [5000, 700, 129], 47, torch.float8_e4m3fn),
+                                       (HeadShape(16, 4, 128, 128, 8), [1500, 9000], 48, None)):
+        inp = gen_decode_paged(len(seq_lens), max(seq_lens), shape, seed=seed, device=DEV, seq_lens=seq_lens,
+                               cache_dtype=cdt)
+        _say("decode index mean-pool", shape, seq_lens, seed, cdt)
+        q_idx = inp["q_idx"][0].contiguous()
+        bidx, bsc = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=shape.top_k, page_table=inp["page_table"],
+                                   seq_lens=inp["seq_lens"], pool="mean", with_scores=True)
+        torch.cuda.synchronize()
+        pt = inp["page_table"].cpu().numpy()
+        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), _cache_host(inp["k_idx_pages"]), pt, seq_lens,
+                                                 shape.top_k, pool="mean")
+        diags = (np.asarray(seq_lens) - 1) // 128
+        compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, diags)
+        g, gs = bidx.cpu().numpy(), bsc.cpu().numpy().astype(np.float64)
+        for t in range(len(seq_lens)):
+            for r in range(shape.h_kv):
+                for j in range(shape.top_k):
+                    b = g[t, r, j]
+                    if b >= 0:
+                        ref = pooled[t][r][b]
+                        assert abs(gs[t, r, j] - ref) <= 1e-5 * max(1.0, abs(ref)), (t, r, b)
 
 
 # ------------------------------------------------------------------ main branch

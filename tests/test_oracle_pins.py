@@ -390,3 +390,67 @@ def test_e4m3_decoder_matches_torch_float8_e4m3fn():
     got = orc.decode_e4m3(codes.numpy())
     both_nan = np.isnan(ref) & np.isnan(got)
     assert np.all(both_nan | (ref == got))
+
+
+# ------------------------------------------------- mean-pool ablation ([P5])
+
+def test_mean_pool_equals_score_of_mean_key():
+    # linearity: the mean of q.k_j over a block's visible keys is q . (mean of
+    # those keys), computed here without forming any token score
+    rng = np.random.default_rng(11)
+    d, h_kv, n_kv = 32, 3, 700
+    q = rng.standard_normal((h_kv, d))
+    k = rng.standard_normal((n_kv, d))
+    for p in (0, 5, 127, 128, 300, 699):
+        m = orc.block_mean_pool(orc.index_token_scores(q, k, p), p)
+        for b in range(p // 128 + 1):
+            lo, hi = 128 * b, min(128 * b + 128, p + 1)
+            kbar = k[lo:hi].mean(axis=0)
+            np.testing.assert_allclose(m[:, b], q @ kbar / math.sqrt(d), rtol=1e-12, atol=1e-13)
+
+
+def test_mean_pool_brute_force_and_constant_block():
+    rng = np.random.default_rng(12)
+    s = rng.standard_normal((2, 400))
+    p = 399
+    m = orc.block_mean_pool(s, p)
+    for r in range(2):
+        for b in range(p // 128 + 1):
+            vals = [s[r, j] for j in range(128 * b, min(128 * b + 128, p + 1))]
+            tot = 0.0
+            for v in vals:
+                tot += v
+            assert m[r, b] == pytest.approx(tot / len(vals), rel=1e-13)
+    # a block whose visible scores are all equal has mean = max = that score
+    c = np.full((1, 300), 0.75)
+    np.testing.assert_array_equal(orc.block_mean_pool(c, 299), orc.block_max_pool(c, 299))
+
+
+def test_mean_and_max_pool_select_differently_by_construction():
+    # block 1: one spike of 5 and 127 keys at -1 (max 5, mean (5-127)/128);
+    # block 2: every key at 0.5 (max 0.5, mean 0.5); block 0 and 3: -2.
+    # With one free slot (k = 2 with the diagonal block 3 forced) max-pool
+    # takes block 1 and mean-pool takes block 2.
+    d = 4
+    k = np.zeros((4 * 128, d))
+    k[:, 0] = -2.0
+    k[128:256, 0] = -1.0
+    k[128 + 17, 0] = 5.0
+    k[256:384, 0] = 0.5
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = math.sqrt(d)  # makes S_j = k_j[0]
+    p = 4 * 128 - 1
+    ids_max, sc_max, _ = orc.index_topk(q, k, p, 2)
+    ids_mean, sc_mean, _ = orc.index_topk(q, k, p, 2, pool="mean")
+    assert ids_max[0, 0].tolist() == [1, 3]
+    assert ids_mean[0, 0].tolist() == [2, 3]
+    assert sc_max[0, 0, 0] == pytest.approx(5.0, rel=1e-14)
+    assert sc_mean[0, 0, 0] == pytest.approx(0.5, rel=1e-14)
+    # the diagonal block's mean uses only the keys j <= p
+    _, _, pooled = orc.index_topk(q, k, 3 * 128 + 9, 2, pool="mean")
+    assert pooled[0][0, 3] == pytest.approx(-2.0, rel=1e-14)
+
+
+def test_mean_pool_rejects_unknown_mode():
+    with pytest.raises(ValueError):
+        orc.index_topk(np.zeros((1, 1, 4)), np.zeros((10, 4)), 9, 2, pool="median")
