@@ -30,6 +30,12 @@ Readings taken where the pages are silent:
     a decode query sits at position seq_len - 1 and the cache already holds it.
 
 Every input array is upcast to float64 before any arithmetic.
+
+Training path (readings): the KL-alignment loss of [P1] §4.5 compares, per
+query and group over the visible keys of the selected blocks, the mean over
+the group's heads of the main-branch softmax (the target, detached) with the
+softmax of the index scores (the prediction); KL(target || prediction),
+summed over (query, group) and multiplied by a caller-given weight.
 """
 from __future__ import annotations
 
@@ -296,6 +302,100 @@ def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *,
 # 8-bit caches (scope table, next step: e4m3 K/V and K_idx caches; the MXFP8
 # KV cache of the zhichai.net key points)
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# Training path ([P1] §4.5): gradients of Eq. (8) over the selected blocks, and
+# the KL-alignment loss between the index branch and the group-averaged main
+# branch, with the main-branch side detached.
+# --------------------------------------------------------------------------
+
+def _visible_tokens(row_blocks, p, block=BLOCK):
+    """Token positions j <= p of the listed blocks (entries < 0 ignored)."""
+    blocks = sorted(set(int(b) for b in row_blocks if b >= 0))
+    parts = [np.arange(b * block, min(b * block + block, p + 1)) for b in blocks if b * block <= p]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None, block=BLOCK):
+    """Gradients of Eq. (8) for one contiguous sequence, given dO.
+
+    For query i (position p) and head h of group r, with T the visible keys of
+    the group's selected blocks, s_j = q.k_j * scale, P = softmax_T(s),
+    O = sum_j P_j v_j:
+        dv_j += P_j dO
+        dP_j  = dO . v_j,   ds_j = P_j (dP_j - sum_t P_t dP_t)
+        dq    = scale * sum_j ds_j k_j,   dk_j += scale * ds_j q.
+    Returns (dq [n_q, h_q, d_h], dk [n_kv, h_kv, d_h], dv [n_kv, h_kv, d_h]).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n_q, h_q, d_h = q.shape
+    h_kv = k.shape[1]
+    g = h_q // h_kv
+    scale = 1.0 / math.sqrt(d_h) if sm_scale is None else float(sm_scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in range(n_q):
+        p = q_start + i
+        for r in range(h_kv):
+            toks = _visible_tokens(block_idx[i, r], p, block)
+            if toks.size == 0:
+                continue
+            kt, vt = k[toks, r], v[toks, r]
+            for h in range(r * g, (r + 1) * g):
+                s = kt @ q[i, h] * scale
+                w = np.exp(s - s.max())
+                pr = w / w.sum()
+                dpr = vt @ do[i, h]
+                ds = pr * (dpr - pr @ dpr)
+                dq[i, h] = scale * (ds @ kt)
+                dk[toks, r] += scale * np.outer(ds, q[i, h])
+                dv[toks, r] += np.outer(pr, do[i, h])
+    return dq, dk, dv
+
+
+def kl_alignment(q_idx, k_idx, q, k, block_idx, q_start, *, sm_scale=None, idx_scale=None,
+                 kl_scale=1.0, block=BLOCK):
+    """KL-alignment loss of the index branch ([P1] §4.5; [P4] key points).
+
+    For query i and group r, over the visible keys T of the group's selected
+    blocks:
+      target    p_main(j) = mean over the group's heads h of softmax_T(q_h.k_j * sm_scale)
+      predicted p_idx(j)  = softmax_T(q_idx^(r).k_idx_j * idx_scale)
+      KL_{i,r}  = sum_j p_main(j) (log p_main(j) - log p_idx(j)).
+    The loss is L = kl_scale * sum_{i,r} KL_{i,r}.  p_main is detached (no
+    gradient reaches q or k), so dL/dS_idx(j) = kl_scale (p_idx(j) - p_main(j))
+    and the gradients go to q_idx and k_idx only.
+    Returns (kl [n_q, h_kv], dq_idx [n_q, h_kv, d_idx], dk_idx [n_kv, d_idx]).
+    """
+    q_idx, k_idx, q, k = _f64(q_idx), _f64(k_idx), _f64(q), _f64(k)
+    n_q, h_kv, d_idx = q_idx.shape
+    h_q, d_h = q.shape[1], q.shape[2]
+    g = h_q // h_kv
+    sc = 1.0 / math.sqrt(d_h) if sm_scale is None else float(sm_scale)
+    isc = 1.0 / math.sqrt(d_idx) if idx_scale is None else float(idx_scale)
+    kl = np.zeros((n_q, h_kv))
+    dq_idx = np.zeros_like(q_idx)
+    dk_idx = np.zeros_like(k_idx)
+    for i in range(n_q):
+        p = q_start + i
+        for r in range(h_kv):
+            toks = _visible_tokens(block_idx[i, r], p, block)
+            if toks.size == 0:
+                continue
+            s = (q[i, r * g:(r + 1) * g] @ k[toks, r].T) * sc          # [G, T]
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            p_main = (w / w.sum(axis=1, keepdims=True)).mean(axis=0)   # [T]
+            si = k_idx[toks] @ q_idx[i, r] * isc                       # [T]
+            log_p_idx = si - (si.max() + np.log(np.exp(si - si.max()).sum()))
+            p_idx = np.exp(log_p_idx)
+            pos = p_main > 0
+            kl[i, r] = np.sum(p_main[pos] * (np.log(p_main[pos]) - log_p_idx[pos]))
+            dsi = kl_scale * (p_idx - p_main)
+            dq_idx[i, r] = isc * (dsi @ k_idx[toks])
+            dk_idx[toks] += isc * np.outer(dsi, q_idx[i, r])
+    return kl, dq_idx, dk_idx
+
 
 def decode_e4m3(codes):
     """Values of OCP FP8 E4M3 ("fn") codes, written from the format's

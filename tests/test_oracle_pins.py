@@ -454,3 +454,142 @@ def test_mean_and_max_pool_select_differently_by_construction():
 def test_mean_pool_rejects_unknown_mode():
     with pytest.raises(ValueError):
         orc.index_topk(np.zeros((1, 1, 4)), np.zeros((10, 4)), 9, 2, pool="median")
+
+
+# ---------------------------------------------- training path ([P1] §4.5)
+
+def _rand_training_case(seed, n=300, h_q=4, h_kv=2, d_h=16, d_idx=8, top_k=2):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, h_q, d_h))
+    k = rng.standard_normal((n, h_kv, d_h))
+    v = rng.standard_normal((n, h_kv, d_h))
+    do = rng.standard_normal((n, h_q, d_h))
+    q_idx = rng.standard_normal((n, h_kv, d_idx))
+    k_idx = rng.standard_normal((n, d_idx))
+    ids, _, _ = orc.index_topk(q_idx, k_idx, 0, top_k)
+    return q, k, v, do, q_idx, k_idx, ids
+
+
+def _visible_mask(ids, n, h_q, h_kv, q_start=0, n_kv=None):
+    n_kv = n if n_kv is None else n_kv
+    g = h_q // h_kv
+    m = np.zeros((n, h_q, n_kv), dtype=bool)
+    for i in range(n):
+        p = q_start + i
+        for r in range(h_kv):
+            for b in ids[i, r]:
+                if b >= 0:
+                    lo, hi = 128 * b, min(128 * b + 128, p + 1)
+                    m[i, r * g:(r + 1) * g, lo:hi] = True
+    return m
+
+
+def test_backward_matches_torch_autograd_of_masked_attention():
+    # autograd differentiates the masked softmax attention; the oracle's
+    # gradient formulas are hand-derived
+    q, k, v, do, _, _, ids = _rand_training_case(20)
+    n, h_q, d = q.shape
+    h_kv = k.shape[1]
+    g = h_q // h_kv
+    mask = torch.from_numpy(_visible_mask(ids, n, h_q, h_kv))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ke = tk.repeat_interleave(g, dim=1)
+    ve = tv.repeat_interleave(g, dim=1)
+    s = torch.einsum("ihd,jhd->ihj", tq, ke) / math.sqrt(d)
+    s = s.masked_fill(~mask, float("-inf"))
+    o = torch.einsum("ihj,jhd->ihd", torch.softmax(s, dim=-1), ve)
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = orc.sparse_attention_backward(q, k, v, ids, 0, do)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_backward_full_coverage_equals_sdpa_backward():
+    # k covering every block: the gradient of dense causal attention (torch SDPA)
+    rng = np.random.default_rng(21)
+    n, h_q, h_kv, d = 260, 4, 1, 16
+    q = rng.standard_normal((n, h_q, d))
+    k = rng.standard_normal((n, h_kv, d))
+    v = rng.standard_normal((n, h_kv, d))
+    do = rng.standard_normal((n, h_q, d))
+    ids, _, _ = orc.index_topk(rng.standard_normal((n, h_kv, 8)), rng.standard_normal((n, 8)), 0, 4)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(0, 1), tk.expand(n, h_q, d).transpose(0, 1), tv.expand(n, h_q, d).transpose(0, 1),
+        is_causal=True)
+    (o.transpose(0, 1) * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = orc.sparse_attention_backward(q, k, v, ids, 0, do)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    q, k, v, do, _, _, ids = _rand_training_case(22, n=200)
+
+    def loss(q_, k_, v_):
+        o, _ = orc.sparse_attention(q_, k_, v_, ids, 0)
+        return float(np.sum(o * do))
+
+    dq, dk, dv = orc.sparse_attention_backward(q, k, v, ids, 0, do)
+    rng = np.random.default_rng(0)
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for _ in range(5):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            plus, minus = [x.copy() for x in (q, k, v)], [x.copy() for x in (q, k, v)]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert fd == pytest.approx(grad[idx], rel=1e-5, abs=1e-7), (which, idx)
+
+
+def _torch_kl(q_idx, k_idx, q, k, ids, kl_scale):
+    n, h_kv, d_idx = q_idx.shape
+    h_q, d = q.shape[1], q.shape[2]
+    g = h_q // h_kv
+    mask = torch.from_numpy(_visible_mask(ids, n, h_q, h_kv))
+    with torch.no_grad():
+        s = torch.einsum("ihd,jhd->ihj", torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(g, dim=1))
+        s = (s / math.sqrt(d)).masked_fill(~mask, float("-inf"))
+        p_main = torch.softmax(s, dim=-1).view(n, h_kv, g, n).mean(dim=2)   # [n, h_kv, n]
+    tqi = torch.tensor(q_idx, requires_grad=True)
+    tki = torch.tensor(k_idx, requires_grad=True)
+    si = torch.einsum("ird,jd->irj", tqi, tki) / math.sqrt(d_idx)
+    gmask = mask.view(n, h_kv, g, n)[:, :, 0]
+    log_p_idx = torch.log_softmax(si.masked_fill(~gmask, float("-inf")), dim=-1)
+    # library KL per row: sum p_main (log p_main - log p_idx) over visible keys
+    kl_rows = torch.nn.functional.kl_div(log_p_idx.masked_fill(~gmask, 0.0), p_main, reduction="none").sum(-1)
+    (kl_scale * kl_rows.sum()).backward()
+    return kl_rows.detach().numpy(), tqi.grad.numpy(), tki.grad.numpy()
+
+
+def test_kl_alignment_matches_torch_kl_div_and_autograd():
+    q, k, _, _, q_idx, k_idx, ids = _rand_training_case(23)
+    kl, dqi, dki = orc.kl_alignment(q_idx, k_idx, q, k, ids, 0, kl_scale=0.37)
+    t_kl, t_dqi, t_dki = _torch_kl(q_idx, k_idx, q, k, ids, 0.37)
+    np.testing.assert_allclose(kl, t_kl, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dqi, t_dqi, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dki, t_dki, rtol=1e-9, atol=1e-12)
+    assert np.all(kl >= -1e-15)
+
+
+def test_kl_alignment_zero_when_index_branch_equals_main_branch():
+    # one head per group, q_idx = q, k_idx = k, equal scales: the two
+    # distributions coincide, so the loss and its gradients vanish
+    rng = np.random.default_rng(24)
+    n, d = 300, 16
+    q = rng.standard_normal((n, 1, d))
+    k = rng.standard_normal((n, 1, d))
+    ids, _, _ = orc.index_topk(rng.standard_normal((n, 1, 8)), rng.standard_normal((n, 8)), 0, 2)
+    kl, dqi, dki = orc.kl_alignment(q, k[:, 0], q, k, ids, 0)
+    assert np.max(np.abs(kl)) < 1e-13
+    assert np.max(np.abs(dqi)) < 1e-12 and np.max(np.abs(dki)) < 1e-12
+    # scaling the loss weight scales the gradients only
+    q2, k2, _, _, qi2, ki2, ids2 = _rand_training_case(25)
+    a = orc.kl_alignment(qi2, ki2, q2, k2, ids2, 0, kl_scale=1.0)
+    b = orc.kl_alignment(qi2, ki2, q2, k2, ids2, 0, kl_scale=2.5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_allclose(b[1], 2.5 * a[1], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(b[2], 2.5 * a[2], rtol=1e-12, atol=1e-15)
