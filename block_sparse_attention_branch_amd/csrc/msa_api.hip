@@ -130,12 +130,12 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int32_t n_q, int32_t q_start,
                           int32_t n_kv, int32_t max_pages) {
-  if (op < 0 || op > 4) {
-    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..4", op);
+  if (op < 0 || op > 5) {
+    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..5", op);
     return 0;
   }
-  if (check_shape(shape, op == 0 || op == 4, op >= 1 && op <= 3) != MSA_OK) return 0;
-  if (check_cache_dtype(*shape, op != 3) != MSA_OK) return 0;
+  if (check_shape(shape, op == 0 || op == 4, (op >= 1 && op <= 3) || op == 5) != MSA_OK) return 0;
+  if (check_cache_dtype(*shape, op != 3 && op != 5) != MSA_OK) return 0;
   if (batch < 0 || n_q < 0 || q_start < 0 || n_kv < 0 || max_pages < 0) {
     fail(MSA_ERR_INVALID_ARG, "negative size");
     return 0;
@@ -153,6 +153,9 @@ size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int
       return msa::prefill_plan(s.dtype, n_q, q_start, n_kv, s.h_q, s.h_kv, s.d_h, s.top_k).total;
     case 2:
       return msa::decode_plan(batch, s.h_q, s.h_kv, s.d_h, s.top_k).total;
+    case 5:
+      if (n_q == 0) return 0;
+      return msa::backward_plan(n_q, q_start, n_kv, s.h_q, s.h_kv, s.d_h, s.top_k).total;
     default:
       return 0;
   }
@@ -289,6 +292,59 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   a.ws_bytes = ws_bytes;
   return hip_status(msa::launch_sparse_prefill(kernel_dtype(s), s.d_h, a, pl, static_cast<hipStream_t>(hip_stream)),
                     "msa_sparse_prefill");
+}
+
+msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
+                                       const msa_kv* kv, const int32_t* block_idx, const void* o, const float* lse,
+                                       const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t ws_bytes, void* hip_stream) {
+  msa_status st = check_shape(shape, false, true);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if ((st = check_cache_dtype(s, false)) != MSA_OK) return st;
+  if (!msa::backward_supported(s.dtype, s.d_h))
+    return fail(MSA_ERR_UNSUPPORTED, "the backward is built for dtype MSA_BF16 and d_h 64/128");
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->seq_lens || kv->page_table)
+    return fail(MSA_ERR_UNSUPPORTED, "the backward takes one contiguous sequence (no page_table, no seq_lens)");
+  if (n_q < 0 || q_start < 0 || kv->n_kv < 0) return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d", n_q, q_start);
+  if ((int64_t)q_start + n_q > kv->n_kv)
+    return fail(MSA_ERR_INVALID_ARG, "q_start + n_q = %lld exceeds n_kv = %d", (long long)q_start + n_q, kv->n_kv);
+  if ((int64_t)n_q * s.h_kv * s.top_k >= (int64_t(1) << 27)) return fail(MSA_ERR_UNSUPPORTED, "n_q too large");
+  if (kv->n_kv > 0 && (!dk || !dv)) return fail(MSA_ERR_INVALID_ARG, "dk/dv is NULL");
+  if (n_q > 0 && (!q || !kv->k || !kv->v || !block_idx || !o || !lse || !d_o || !dq))
+    return fail(MSA_ERR_INVALID_ARG, "q/k/v/block_idx/o/lse/d_o/dq is NULL");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(MSA_ERR_INVALID_ARG, "q/k/v/o/d_o/dq/dk/dv must be 16-byte aligned");
+  if (kv->n_kv == 0) return ok();
+  const msa::BackwardPlan pl = msa::backward_plan(n_q, q_start, kv->n_kv, s.h_q, s.h_kv, s.d_h, s.top_k);
+  if (n_q > 0 && (st = check_ws(workspace, ws_bytes, pl.total)) != MSA_OK) return st;
+  msa::BackwardArgs b{};
+  msa::AttnArgs& a = b.attn;
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.block_idx = block_idx;
+  a.o = const_cast<void*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.n_q = n_q;
+  a.q_start = q_start;
+  a.n_kv = kv->n_kv;
+  a.batch = 1;
+  a.h_q = s.h_q;
+  a.h_kv = s.h_kv;
+  a.group = s.h_q / s.h_kv;
+  a.top_k = s.top_k;
+  a.sm_scale = sm_scale_of(s);
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  b.d_o = d_o;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  return hip_status(msa::launch_sparse_prefill_backward(s.d_h, b, pl, static_cast<hipStream_t>(hip_stream)),
+                    "msa_sparse_prefill_backward");
 }
 
 msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* q, const msa_kv* kv,

@@ -25,378 +25,12 @@
 // The dense kernel (Eq. (1), §2.2) is the Q-outer comparison path.
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
+#include "msa_kvouter.hpp"
 #include "msa_profile.hpp"
 
 #include <type_traits>
 
 namespace msa {
-
-// ----------------------------------------------------------------- LDS tile
-template <typename T, int D>
-struct KvLds {
-  static constexpr int KS = D * (int)sizeof(T) + 16;                        // bytes per key row
-  static constexpr int VS = 128 * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // bytes per d row of V^T
-  static constexpr int K_BYTES = 128 * KS;
-  static constexpr int BYTES = K_BYTES + D * VS;
-};
-
-// Two-phase staging for double buffering: global -> registers (issued before
-// the current block's math) and registers -> LDS (after it).  NT threads.
-// TC is the cache type; with e4m3 caches (T = bf16) each 16-byte bf16 chunk
-// arrives as 8 bytes and is widened when stored to LDS.
-template <typename T, int D, int NT, typename TC = T>
-struct StageRegs {
-  typedef typename std::conditional<sizeof(TC) == 1, u32x2, u32x4>::type Chunk;
-  static constexpr int CB = 16 * (int)sizeof(TC) / (int)sizeof(T);          // cache bytes per 16-B LDS chunk
-  static constexpr int CPR = D * (int)sizeof(T) / 16;
-  static constexpr int KL = 128 * CPR / NT;                                  // K chunks per thread
-  static constexpr int VU = (sizeof(T) == 2 ? 64 * (D / 8) : 128 * (D / 4)) / NT;  // V units per thread
-  static constexpr int VW = sizeof(T) == 2 ? 2 : 1;                          // loads per V unit
-  static_assert(KL >= 1 && VU >= 1, "staging split");
-  Chunk k[KL];
-  Chunk v[VU][VW];
-  uint32_t zero_mask;  // bit i: K load i past the end; bit 16 + 2u + w: V load (u, w)
-};
-
-
-// Base addresses of block b of KV group r: row j of K is k + j * stride.
-struct BlockPtr {
-  const char* k;
-  const char* v;
-  int stride;  // bytes between consecutive key rows
-  int valid;   // rows that exist (a contiguous cache may end inside the block)
-};
-
-template <typename T, int D>
-__device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, const int32_t* pt, int b, int r,
-                                              int h_kv, int n_kv) {
-  BlockPtr p;
-  size_t off;
-  if (pt) {
-    off = (((size_t)scalar_load(pt, b) * h_kv + r) * kBlock) * D * sizeof(T);
-    p.stride = D * (int)sizeof(T);
-    p.valid = kBlock;
-  } else {
-    off = (((size_t)b * kBlock) * h_kv + r) * D * sizeof(T);
-    p.stride = h_kv * D * (int)sizeof(T);
-    p.valid = min(kBlock, n_kv - b * kBlock);
-  }
-  p.k = static_cast<const char*>(k) + off;
-  p.v = static_cast<const char*>(v) + off;
-  return p;
-}
-
-template <typename T, int D, int NT, typename TC = T>
-__device__ __forceinline__ void stage_load(StageRegs<T, D, NT, TC>& g, const BlockPtr& p) {
-  // Every load is issued unconditionally (rows past the end of a contiguous
-  // cache read the last valid row); the values are zeroed only when stored to
-  // LDS, so nothing here waits for the loads to land.
-  using S = StageRegs<T, D, NT, TC>;
-  typedef typename S::Chunk C;
-  static_assert(S::KL <= 16 && S::VU * S::VW <= 16, "zero mask layout");
-  const int last = p.valid - 1;
-  uint32_t zm = 0;
-#pragma unroll
-  for (int i = 0; i < S::KL; ++i) {
-    const int u = threadIdx.x + NT * i;
-    const int j = u / S::CPR, c = u % S::CPR;
-    g.k[i] = *reinterpret_cast<const C*>(p.k + (size_t)min(j, last) * p.stride + c * S::CB);
-    zm |= (j > last ? 1u : 0u) << i;
-  }
-  if constexpr (sizeof(T) == 2) {
-    constexpr int DC = D / 8;
-#pragma unroll
-    for (int i = 0; i < S::VU; ++i) {
-      const int u = threadIdx.x + NT * i;
-      const int kp = (u & 15) + 16 * (u / (16 * DC));
-      const int dc = (u >> 4) % DC;
-      g.v[i][0] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp, last) * p.stride + dc * S::CB);
-      g.v[i][1] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp + 1, last) * p.stride + dc * S::CB);
-      zm |= (2 * kp > last ? 1u : 0u) << (16 + 2 * i);
-      zm |= (2 * kp + 1 > last ? 1u : 0u) << (17 + 2 * i);
-    }
-  } else {
-    constexpr int DC = D / 4;
-#pragma unroll
-    for (int i = 0; i < S::VU; ++i) {
-      const int u = threadIdx.x + NT * i;
-      const int key = (u & 31) + 32 * (u / (32 * DC));
-      const int dc = (u >> 5) % DC;
-      g.v[i][0] = *reinterpret_cast<const C*>(p.v + (size_t)min(key, last) * p.stride + dc * S::CB);
-      zm |= (key > last ? 1u : 0u) << (16 + 2 * i);
-    }
-  }
-  g.zero_mask = zm;
-}
-
-template <typename T, typename C>
-__device__ __forceinline__ u32x4 stage_widen(const C& c) {
-  if constexpr (sizeof(C) == 8) {
-    return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c));
-  } else {
-    return c;
-  }
-}
-
-template <typename T, int D, int NT, typename TC = T>
-__device__ __forceinline__ void stage_store(const StageRegs<T, D, NT, TC>& g, char* lds) {
-  using S = StageRegs<T, D, NT, TC>;
-  using L = KvLds<T, D>;
-  const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < S::KL; ++i) {
-    const int u = threadIdx.x + NT * i;
-    const int j = u / S::CPR, c = u % S::CPR;
-    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = ((g.zero_mask >> i) & 1u) ? z : stage_widen<T>(g.k[i]);
-  }
-  char* vt = lds + L::K_BYTES;
-  if constexpr (sizeof(T) == 2) {
-    constexpr int DC = D / 8;
-#pragma unroll
-    for (int i = 0; i < S::VU; ++i) {
-      const int u = threadIdx.x + NT * i;
-      const int kp = (u & 15) + 16 * (u / (16 * DC));
-      const int dc = (u >> 4) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
-      const u32x4 y = ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][1]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
-        const uint32_t hi = (x[t] >> 16) | (y[t] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t) * L::VS + kp * 4) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (8 * dc + 2 * t + 1) * L::VS + kp * 4) = hi;
-      }
-    }
-  } else {
-    constexpr int DC = D / 4;
-#pragma unroll
-    for (int i = 0; i < S::VU; ++i) {
-      const int u = threadIdx.x + NT * i;
-      const int key = (u & 31) + 32 * (u / (32 * DC));
-      const int dc = (u >> 5) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
-    }
-  }
-}
-
-// A fragment of V^T: row d, elements 0..3 = keys ka..ka+3, 4..7 = keys kb..kb+3.
-template <typename T>
-__device__ __forceinline__ Frag<T> vt_frag(const char* vt, int vs, int d, int ka, int kb) {
-  Frag<T> f;
-  if constexpr (sizeof(T) == 2) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(vt + d * vs + ka * 2);
-    const bf16x4 y = *reinterpret_cast<const bf16x4*>(vt + d * vs + kb * 2);
-    f = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  } else {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(vt + d * vs + ka * 4);
-    const f32x4 y = *reinterpret_cast<const f32x4*>(vt + d * vs + kb * 4);
-    f = f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  }
-  return f;
-}
-
-template <typename T>
-__device__ __forceinline__ Frag<T> to_frag(float a0, float a1, float a2, float a3, float a4, float a5,
-                                           float a6, float a7) {
-  Frag<T> f;
-  f[0] = from_f32<T>(a0); f[1] = from_f32<T>(a1); f[2] = from_f32<T>(a2); f[3] = from_f32<T>(a3);
-  f[4] = from_f32<T>(a4); f[5] = from_f32<T>(a5); f[6] = from_f32<T>(a6); f[7] = from_f32<T>(a7);
-  return f;
-}
-
-// Store 4 consecutive values (d .. d+3) of one output row.
-template <typename T>
-__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<bf16x4*>(dst) = bf16x4{from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
-  }
-}
-
-// Store 8 consecutive values (one 16-byte store for bf16, two for fp32).
-template <typename T>
-__device__ __forceinline__ void store8(T* dst, const f32x16& o, int base) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<bf16x8*>(dst) =
-        bf16x8{from_f32<T>(o[base]), from_f32<T>(o[base + 1]), from_f32<T>(o[base + 2]), from_f32<T>(o[base + 3]),
-               from_f32<T>(o[base + 4]), from_f32<T>(o[base + 5]), from_f32<T>(o[base + 6]), from_f32<T>(o[base + 7])};
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{o[base], o[base + 1], o[base + 2], o[base + 3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[base + 4], o[base + 5], o[base + 6], o[base + 7]};
-  }
-}
-
-// ------------------------------------------------------------ row tile math
-// One wave processes RT tiles of 32 (token, head) rows against the staged
-// block.  S^T = K . Q^T puts keys on the MFMA rows: lane l holds 16 keys of
-// row (l % 32) per 32-key tile, so softmax reductions are in-lane plus one
-// exchange between lanes l and l+32.
-template <typename T, int D, int RT>
-struct TileRegs {
-  Frag<T> qf[RT][D / 16];
-  f32x16 s[RT][4];
-  Frag<T> pf[RT][4][2];   // P^T fragments (keys kt*32 + 16*h2 + ...)
-  f32x16 o[RT][D / 32];
-  int pos[RT];
-};
-
-template <typename T, int D, int RT>
-__device__ __forceinline__ Frag<T> k_frag(const char* lds, int step) {
-  using L = KvLds<T, D>;
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int kt = step / (D / 16), ks = step % (D / 16);
-  return *reinterpret_cast<const Frag<T>*>(lds + (kt * 32 + l32) * L::KS + (ks * 16 + half * 8) * (int)sizeof(T));
-}
-
-// S^T = K . Q^T for the staged block; fragments are read two steps ahead.
-template <typename T, int D, int RT>
-__device__ __forceinline__ void tile_scores(TileRegs<T, D, RT>& t, const char* lds, int b, bool mask) {
-  constexpr int KS = D / 16, NS = 4 * KS;
-  const int lane = threadIdx.x & 63, half = lane >> 5;
-  Frag<T> f0 = k_frag<T, D, RT>(lds, 0), f1 = k_frag<T, D, RT>(lds, 1);
-#pragma unroll
-  for (int step = 0; step < NS; ++step) {
-    const int kt = step / KS, ks = step % KS;
-    Frag<T> f2;
-    if (step + 2 < NS) f2 = k_frag<T, D, RT>(lds, step + 2);
-    if (ks == 0) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) t.s[rt][kt] = f32x16{};
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mma32(t.s[rt][kt], f0, t.qf[rt][ks]);
-    f0 = f1;
-    f1 = f2;
-    MSA_SCHED_FENCE();
-  }
-  if (mask) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key > t.pos[rt]) t.s[rt][kt][v] = -__builtin_inff();
-        }
-  }
-}
-
-// Pack the exponentiated scores of row tile rt into P^T fragments.
-template <typename T, int D, int RT>
-__device__ __forceinline__ void tile_pack_p(TileRegs<T, D, RT>& t, int rt) {
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const f32x16& p = t.s[rt][kt];
-      const int o = 8 * h2;
-      t.pf[rt][kt][h2] = to_frag<T>(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
-    }
-}
-
-// O^T += V^T . P^T; V^T fragments are read two steps ahead.
-template <typename T, int D, int RT>
-__device__ __forceinline__ Frag<T> v_frag(const char* lds, int step) {
-  using L = KvLds<T, D>;
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int kt = step / (2 * (D / 32)), h2 = (step / (D / 32)) & 1, dt = step % (D / 32);
-  const int base = kt * 32 + h2 * 16;
-  return vt_frag<T>(lds + L::K_BYTES, L::VS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half);
-}
-
-template <typename T, int D, int RT>
-__device__ __forceinline__ void tile_pv(TileRegs<T, D, RT>& t, const char* lds) {
-  constexpr int DT = D / 32, NS = 4 * 2 * DT;
-  Frag<T> f0 = v_frag<T, D, RT>(lds, 0), f1 = v_frag<T, D, RT>(lds, 1);
-#pragma unroll
-  for (int step = 0; step < NS; ++step) {
-    const int kt = step / (2 * DT), h2 = (step / DT) & 1, dt = step % DT;
-    Frag<T> f2;
-    if (step + 2 < NS) f2 = v_frag<T, D, RT>(lds, step + 2);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mma32(t.o[rt][dt], f0, t.pf[rt][kt][h2]);
-    f0 = f1;
-    f1 = f2;
-    MSA_SCHED_FENCE();
-  }
-}
-
-// ====================================================================
-// Prefill schedule: invert block lists into per-(window, group, block)
-// token lists.  Slot j of row (i, r) is used iff its block is >= 0, causal
-// (<= diag) and larger than the previous used block of the row.
-// ====================================================================
-struct SchedArgs {
-  const int32_t* block_idx;
-  int32_t n_q, q_start, h_kv, top_k, n_blocks, window, chunk;
-  int64_t n_cells;
-  int32_t* count;     // [n_cells]
-  int32_t* fill;      // [n_cells]
-  int32_t* cell_off;  // [n_cells + 1]
-  int32_t* item_off;  // [n_cells + 1]
-  int32_t* entries;   // [n_q * h_kv * top_k]
-  i32x4* items;       // [max_items] {b, r, e_begin, e_end}
-  int32_t* scan;      // [4 * n_scan_tiles]
-  int32_t n_scan_tiles;
-};
-
-// Cells are the (window, group, block) token lists.  Within a window they are
-// numbered XCD-major, and the KV-outer workgroups running on XCD x take
-// exactly XCD x's cells.  A group's blocks are spread over S = 8 / h_kv XCDs
-// (by b mod S), so each XCD gathers the queries of one group only (they stay
-// in its L2 while the window's items run) and reads each KV block of its
-// cells from one L2 across windows.  nbp = blocks rounded up to 8.
-__device__ __forceinline__ int64_t cell_key(int w, int r, int b, int nbp, int h_kv) {
-  const int n_l = h_kv * nbp, per = n_l >> 3;
-  int x, pos;
-  if (h_kv <= 8 && (8 % h_kv) == 0) {
-    const int S = 8 / h_kv;
-    x = r * S + b % S;
-    pos = b / S;
-  } else if ((h_kv & 7) == 0) {
-    x = r & 7;
-    pos = (r >> 3) * nbp + b;
-  } else {  // any other head count: interleave all cells over the XCDs
-    const int cl = r * nbp + b;
-    x = cl & 7;
-    pos = cl >> 3;
-  }
-  return (int64_t)w * n_l + (int64_t)x * per + pos;
-}
-__device__ __forceinline__ void cell_rb(int64_t k, int nbp, int h_kv, int& r, int& b) {
-  const int n_l = h_kv * nbp, per = n_l >> 3;
-  const int kl = (int)(k % n_l);
-  const int x = kl / per, pos = kl % per;
-  if (h_kv <= 8 && (8 % h_kv) == 0) {
-    const int S = 8 / h_kv;
-    r = x / S;
-    b = pos * S + x % S;
-  } else if ((h_kv & 7) == 0) {
-    r = (pos / nbp) * 8 + x;
-    b = pos % nbp;
-  } else {
-    const int cl = pos * 8 + x;
-    r = cl / nbp;
-    b = cl % nbp;
-  }
-}
-
-__device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
-  uint32_t m = 0;
-  int prev = -1;
-  for (int j = 0; j < top_k; ++j) {
-    const int b = row[j];
-    if (b > prev && b <= diag) {
-      m |= 1u << j;
-      prev = b;
-    }
-  }
-  return m;
-}
 
 __global__ void ks_zero_kernel(SchedArgs a) {
   for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < a.n_cells; c += (int64_t)gridDim.x * 256) {
@@ -416,9 +50,6 @@ __global__ void ks_count_kernel(SchedArgs a) {
   for (int j = 0; j < a.top_k; ++j)
     if (m & (1u << j)) atomicAdd(&a.count[cell_key(w, r, br[j], a.n_blocks, a.h_kv)], 1);
 }
-
-constexpr int kScanPerThread = 16;
-constexpr int kScanTile = 256 * kScanPerThread;
 
 __device__ __forceinline__ void block_excl_scan2(int& x, int& y, int* sh) {
   // sh: 512 ints
@@ -543,6 +174,52 @@ __global__ void ks_items_kernel(SchedArgs a) {
   }
 }
 
+// Ordered mode: a cell's token list in increasing token order whatever the
+// order the threads run in.  Each used (row, slot) sets its token's bit in
+// the cell's bitmap; one workgroup per cell then writes the set bits out in
+// order at the cell's offset.
+__global__ void ks_bits_zero_kernel(SchedArgs a) {
+  const int64_t n = a.n_cells * a.words;
+  for (int64_t x = blockIdx.x * 256ll + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) a.bitmap[x] = 0u;
+}
+
+__global__ void ks_bits_set_kernel(SchedArgs a) {
+  const int64_t row = blockIdx.x * 256ll + threadIdx.x;  // (i, r)
+  if (row >= (int64_t)a.n_q * a.h_kv) return;
+  const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
+  const int diag = (a.q_start + i) >> 7;
+  const int32_t* br = a.block_idx + row * a.top_k;
+  const uint32_t m = used_slots(br, a.top_k, diag);
+  const int w = i / a.window, il = i - w * a.window;
+  for (int j = 0; j < a.top_k; ++j)
+    if (m & (1u << j)) {
+      const int64_t cell = cell_key(w, r, br[j], a.n_blocks, a.h_kv);
+      atomicOr(&a.bitmap[cell * a.words + (il >> 5)], 1u << (il & 31));
+    }
+}
+
+__global__ __launch_bounds__(256) void ks_bits_extract_kernel(SchedArgs a) {
+  __shared__ int sh[512];
+  const int64_t cell = blockIdx.x;
+  const int per = (a.words + 255) / 256;
+  const int w0 = threadIdx.x * per, w1 = min(w0 + per, a.words);
+  const uint32_t* bits = a.bitmap + cell * a.words;
+  int n = 0;
+  for (int x = w0; x < w1; ++x) n += __builtin_popcount(bits[x]);
+  int pos = n, dummy = 0;
+  block_excl_scan2(pos, dummy, sh);
+  pos += a.cell_off[cell];
+  const int w = (int)(cell / ((int64_t)a.h_kv * a.n_blocks));
+  for (int x = w0; x < w1; ++x) {
+    uint32_t b = bits[x];
+    while (b) {
+      const int bit = __builtin_ctz(b);
+      b &= b - 1u;
+      a.entries[pos++] = (w * a.window + x * 32 + bit) << 4;
+    }
+  }
+}
+
 // ====================================================================
 // KV-outer sparse attention (one window of query tokens)
 // ====================================================================
@@ -563,11 +240,6 @@ struct KpArgs {
 };
 
 
-// One KV-outer work item: (group r, block b) and a run of the tokens that
-// selected b.  The K/V block is staged once in LDS and shared by all rows.
-struct KpItem {
-  int b, r, e_begin, e_end;
-};
 
 
 // Query rows of one pass (one 32-row tile per wave) of one item.
@@ -636,16 +308,6 @@ __device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) t.o[0][dt] = f32x16{};
   tile_pv<T, D, 1>(t, lds);
-}
-
-// Partial layout.  The partial of (token, slot) is a region of G * D values
-// stored in the order the MFMA accumulators hold them: 8-value chunks indexed
-// ((dt * 2 + p) * 2 + half) * G + head hold d = dt*32 + 16p + 4half + {0..3}
-// and the same + 8.  A store instruction then writes, for each token of the
-// tile, 2 * G chunks back to back (full cache lines) instead of 64 scattered
-// 8-byte pieces.
-__device__ __forceinline__ int part_chunk(int dt, int p, int half, int head, int G) {
-  return ((dt * 2 + p) * 2 + half) * G + head;
 }
 
 template <typename T, int D>
@@ -1227,7 +889,7 @@ static int env_int(const char* name, int dflt) {
 }
 
 // Compute units of the current device (cached per device).
-static int num_cus() {
+int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1245,12 +907,34 @@ static int kp_wgs_per_cu() {
   return e > 0 ? e : 1;
 }
 
+void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv, int32_t top_k, int32_t window,
+                     int32_t chunk, bool ordered) {
+  p.n_blocks = (int32_t)((((int64_t)q_start + n_q - 1) / kBlock + 1 + 7) & ~int64_t(7));
+  p.window = window;
+  p.n_windows = (int32_t)((n_q + window - 1) / window);
+  p.chunk = chunk;
+  p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
+  const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
+  p.max_items = n_entries / p.chunk + p.n_cells + 1;
+  const int64_t n_scan_tiles = (p.n_cells + kScanTile - 1) / kScanTile;
+  size_t off = 0;
+  p.off_count = off; off = align_up(off + p.n_cells * 4);
+  p.off_fill = off; off = align_up(off + p.n_cells * 4);
+  p.off_cell_off = off; off = align_up(off + (p.n_cells + 1) * 4);
+  p.off_item_off = off; off = align_up(off + (p.n_cells + 1) * 4);
+  p.off_entries = off; off = align_up(off + n_entries * 4);
+  p.off_items = off; off = align_up(off + p.max_items * 16);
+  p.off_scan = off; off = align_up(off + 4 * n_scan_tiles * 4);
+  p.bitmap_words = ordered ? (window + 31) / 32 : 0;
+  p.off_bitmap = off; off = align_up(off + (size_t)p.n_cells * p.bitmap_words * 4);
+  p.total = off;
+}
+
 PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
                          int32_t h_kv, int32_t d_h, int32_t top_k) {
   PrefillPlan p{};
   const size_t esz = dtype == 0 ? 2 : 4;
   const int G = h_q / h_kv;
-  p.n_blocks = (int32_t)((((int64_t)q_start + n_q - 1) / kBlock + 1 + 7) & ~int64_t(7));
   (void)n_kv;
   const size_t per_token = (size_t)h_kv * top_k * G * (d_h * esz + 8);
   // Window of query tokens per KV-outer pass.  Its partials should stay in
@@ -1268,20 +952,8 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   w = std::max<int64_t>(64, ((w + 63) / 64) * 64);
   w = std::min<int64_t>(w, std::max<int32_t>(n_q, 1));
   p.window = (int32_t)w;
-  p.n_windows = (int32_t)((n_q + w - 1) / w);
-  p.chunk = 512 / G;  // tokens per KV-outer item: 512 (token, head) rows
-  p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
-  const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
-  p.max_items = n_entries / p.chunk + p.n_cells + 1;
-  const int64_t n_scan_tiles = (p.n_cells + kScanTile - 1) / kScanTile;
-  size_t off = 0;
-  p.off_count = off; off = align_up(off + p.n_cells * 4);
-  p.off_fill = off; off = align_up(off + p.n_cells * 4);
-  p.off_cell_off = off; off = align_up(off + (p.n_cells + 1) * 4);
-  p.off_item_off = off; off = align_up(off + (p.n_cells + 1) * 4);
-  p.off_entries = off; off = align_up(off + n_entries * 4);
-  p.off_items = off; off = align_up(off + p.max_items * 16);
-  p.off_scan = off; off = align_up(off + 4 * n_scan_tiles * 4);
+  schedule_layout(p, n_q, q_start, h_kv, top_k, (int32_t)w, 512 / G);  // items of 512 (token, head) rows
+  size_t off = p.total;
   const size_t prow = ((size_t)p.window * h_kv * top_k + 2) * G;  // + two trash slots
   p.off_part_o = off; off = align_up(off + prow * d_h * esz);
   p.off_part_lse = off; off = align_up(off + prow * 8);
@@ -1293,10 +965,9 @@ bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (
 bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
 bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 2) && (d_h == 64 || d_h == 128); }
 
-template <typename T, int D, typename TC = T>
-static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
+hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st) {
   char* ws = static_cast<char*>(a.ws);
-  SchedArgs s{};
+  s = SchedArgs{};
   s.block_idx = a.block_idx;
   s.n_q = a.n_q;
   s.q_start = a.q_start;
@@ -1314,6 +985,8 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   s.items = reinterpret_cast<i32x4*>(ws + pl.off_items);
   s.scan = reinterpret_cast<int32_t*>(ws + pl.off_scan);
   s.n_scan_tiles = (int32_t)((pl.n_cells + kScanTile - 1) / kScanTile);
+  s.words = pl.bitmap_words;
+  s.bitmap = pl.bitmap_words > 0 ? reinterpret_cast<uint32_t*>(ws + pl.off_bitmap) : nullptr;
   const int64_t rows = (int64_t)a.n_q * a.h_kv;
   const unsigned row_blocks = (unsigned)((rows + 255) / 256);
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
@@ -1322,9 +995,24 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   hipLaunchKernelGGL(ks_scan_a_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
   hipLaunchKernelGGL(ks_scan_b_kernel, dim3(1), dim3(256), 0, st, s);
   hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+  if (s.bitmap) {
+    const int64_t nw = pl.n_cells * s.words;
+    hipLaunchKernelGGL(ks_bits_zero_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 8192)), dim3(256), 0,
+                       st, s);
+    hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
+  } else {
+    hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+  }
   hipLaunchKernelGGL(ks_items_kernel, dim3(cell_blocks), dim3(256), 0, st, s);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <typename T, int D, typename TC = T>
+static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
+  char* ws = static_cast<char*>(a.ws);
+  SchedArgs s;
+  hipError_t e = launch_prefill_schedule(a, pl, s, st);
   if (e != hipSuccess) return e;
 
   KpArgs kp{};

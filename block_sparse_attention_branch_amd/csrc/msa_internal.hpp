@@ -96,9 +96,18 @@ struct PrefillPlan {
   size_t off_count, off_fill, off_cell_off, off_item_off, off_entries, off_items,
       off_part_o, off_part_lse, off_scan, total;
   int64_t max_items;
+  size_t off_bitmap;        // ordered schedules only
+  int32_t bitmap_words;     // 0: entries are scattered in arrival order
 };
 PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
                          int32_t h_kv, int32_t d_h, int32_t top_k);
+// Schedule arrays only (windows of `window` tokens, items of at most `chunk`
+// tokens); `total` ends after them.  `ordered`: each cell lists its tokens in
+// increasing order (built through a per-cell token bitmap), so that sums over
+// a cell's rows do not depend on thread timing; the slot field of such
+// entries is 0.
+void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv, int32_t top_k, int32_t window,
+                     int32_t chunk, bool ordered = false);
 hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const PrefillPlan& pl,
                                  hipStream_t st);
 bool attn_supported(int dtype, int d_h);
@@ -113,6 +122,24 @@ hipError_t launch_sparse_decode(int dtype, int d_h, const AttnArgs& a, const Dec
 bool decode_supported(int dtype, int d_h);
 
 hipError_t launch_dense_prefill(int dtype, int d_h, const AttnArgs& a, hipStream_t st);
+
+// ------------------------------------------------------- training path
+struct BackwardArgs {
+  AttnArgs attn;            // q, k, v, block_idx, o (the forward's output), lse, workspace
+  const void* d_o;          // [n_q, h_q, d]
+  void* dq;                 // [n_q, h_q, d]
+  void* dk;                 // [n_kv, h_kv, d]
+  void* dv;
+};
+struct BackwardPlan {
+  PrefillPlan q;            // dQ pass schedule (windows), at off_q
+  PrefillPlan kv;           // dK/dV pass schedule (one window), at off_kv
+  size_t off_q, off_kv, off_dsum, off_part_dq, off_part_dkv, total;
+};
+BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q, int32_t h_kv, int32_t d_h,
+                           int32_t top_k);
+hipError_t launch_sparse_prefill_backward(int d_h, const BackwardArgs& a, const BackwardPlan& pl, hipStream_t st);
+bool backward_supported(int dtype, int d_h);
 bool dense_supported(int dtype, int d_h);
 
 }  // namespace msa

@@ -18,8 +18,8 @@ std::mutex g_mu;
 bool g_on = false;
 std::vector<Rec> g_recs;   // events are kept for reuse once collected
 
-const char* kNames[PK_COUNT] = {"ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel",
-                                "kd_kernel"};
+const char* kNames[PK_COUNT] = {"ki_prefill_kernel", "kp_kernel",  "km_kernel",  "ki_decode_scan_kernel",
+                                "kd_kernel",         "kbq_kernel", "kbkv_kernel"};
 
 }  // namespace
 

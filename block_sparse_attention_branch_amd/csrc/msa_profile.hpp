@@ -11,7 +11,7 @@
 
 namespace msa {
 
-enum ProfKernel { PK_KI_PREFILL = 0, PK_KP, PK_KM, PK_KI_DECODE_SCAN, PK_KD, PK_COUNT };
+enum ProfKernel { PK_KI_PREFILL = 0, PK_KP, PK_KM, PK_KI_DECODE_SCAN, PK_KD, PK_KBQ, PK_KBKV, PK_COUNT };
 
 bool profile_on();
 void profile_set(bool on);

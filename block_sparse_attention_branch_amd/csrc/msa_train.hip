@@ -1,0 +1,684 @@
+// msa_train.hip - training path of the main branch on gfx950.
+//
+// Gradients of Eq. (8) of the "MiniMax Sparse Attention" digest
+// (titansim.online, §4.3) over the selected blocks, for the training of §4.5.
+// Per (token, head) row with P = softmax over the visible keys of the
+// group's selected blocks, dP = dO.V^T and D = rowsum(dO * O):
+//   dS = P * (dP - D),  dQ = scale * dS.K,  dK = scale * dS^T.Q,  dV = P^T.dO.
+// P is recomputed from the forward's lse.  Both passes are KV-outer like the
+// forward (§4.4.2) and run on the forward's schedule kernels:
+//  * dQ pass (windows of query tokens): an item is one (group, block) and up
+//    to 512 of the rows that selected it; S^T = K.Q^T, dP^T = V.dO^T and
+//    dQ^T = K^T.dS^T on v_mfma_f32_32x32x16_bf16 with keys on the MFMA rows.
+//    Each (token, head, slot) writes an fp32 partial dQ and a merge kernel
+//    sums a row's partials (the two-stage merge without rescaling).
+//  * dK/dV pass (one window over all queries): an item keeps its block's
+//    dK^T and dV^T in registers (four waves of 32 keys) while it sweeps its
+//    rows 32 at a time: S = Q.K^T, dP = dO.V^T, dV^T += dO^T.P,
+//    dK^T += Q^T.dS.  A (group, block) cell split over several items writes
+//    fp32 partials that a reduce kernel sums; unselected blocks get zeros.
+// No floating-point atomics: results are bitwise reproducible.
+#include "msa_common.hpp"
+#include "msa_internal.hpp"
+#include "msa_kvouter.hpp"
+#include "msa_profile.hpp"
+
+namespace msa {
+
+struct KbArgs {
+  const void* q;            // [n_q, h_q, D]
+  const void* k;            // [n_kv, h_kv, D]
+  const void* v;
+  const void* o;            // [n_q, h_q, D]
+  const float* lse;         // [n_q, h_q]
+  const void* d_o;          // [n_q, h_q, D]
+  void* dq;                 // [n_q, h_q, D]
+  void* dk;                 // [n_kv, h_kv, D]
+  void* dv;
+  float* dsum;              // [n_q, h_q]  rowsum(dO * O)
+  const int32_t* block_idx; // [n_q, h_kv, top_k]
+  const int32_t* item_off;
+  const int32_t* entries;
+  const i32x4* items;
+  float* part_dq;           // dQ pass: [window * h_kv * top_k + 2 trash, G, D]
+  float* part_dkv;          // dK/dV pass: [max_items, 2, 128, D]
+  int32_t n_q, q_start, n_kv, h_q, h_kv, group, g_shift, top_k, n_blocks, window, w;
+  size_t trash_slot;
+  float sm_scale;
+};
+
+// ------------------------------------------------------------- D = rowsum
+template <int D>
+__global__ __launch_bounds__(256) void kb_dsum_kernel(KbArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 values each
+  const int64_t t = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int c = (int)(t % LPR);
+  const bool ok = row < (int64_t)a.n_q * a.h_q;
+  float s = 0.0f;
+  if (ok) {
+    const bf16x8 x = load_frag<bf16_t>(static_cast<const bf16_t*>(a.o) + row * D + c * 8);
+    const bf16x8 y = load_frag<bf16_t>(static_cast<const bf16_t*>(a.d_o) + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(to_f32(x[e]), to_f32(y[e]), s);
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off, 64);
+  if (ok && c == 0) a.dsum[row] = s;
+}
+
+// ----------------------------------------------------- K/V block staging
+// The dQ pass needs K with keys on rows (for S^T = K.Q^T), V with keys on
+// rows (dP^T = V.dO^T) and K^T with d on rows (dQ^T = K^T.dS^T).  K is
+// loaded as pairs of adjacent keys so both layouts come from one load.
+template <int D>
+struct KbqLds {
+  static constexpr int KS = D * 2 + 16;   // bytes per key row
+  static constexpr int TS = 128 * 2 + 8;  // bytes per d row of K^T
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 128 * KS;
+  static constexpr int KT_OFF = 2 * 128 * KS;
+  static constexpr int ENT_OFF = KT_OFF + D * TS;
+  static constexpr int BYTES = ENT_OFF + 512 * 4;  // token entries of an item (at most 512)
+};
+
+template <int D, int NT>
+struct KbStage {
+  static constexpr int DC = D / 8;
+  static constexpr int KU = 64 * DC / NT;   // (key pair, chunk) units of K per thread
+  static constexpr int VL = 128 * DC / NT;  // key-row chunks of V per thread
+  static_assert(KU >= 1 && VL >= 1, "staging split");
+  u32x4 k[KU][2];
+  u32x4 v[VL];
+  uint32_t zk, zv;  // bit set: that row lies past n_kv (stored as zeros)
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void kb_stage_load(KbStage<D, NT>& g, const KbArgs& a, int b, int r) {
+  using S = KbStage<D, NT>;
+  const int stride = a.h_kv * D * 2;
+  const char* kb = static_cast<const char*>(a.k) + (((size_t)b * kBlock) * a.h_kv + r) * D * 2;
+  const char* vb = static_cast<const char*>(a.v) + (((size_t)b * kBlock) * a.h_kv + r) * D * 2;
+  const int last = min(kBlock, a.n_kv - b * kBlock) - 1;
+  uint32_t zk = 0, zv = 0;
+#pragma unroll
+  for (int i = 0; i < S::KU; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int dc = u % S::DC, kp = u / S::DC;
+    g.k[i][0] = *reinterpret_cast<const u32x4*>(kb + (size_t)min(2 * kp, last) * stride + dc * 16);
+    g.k[i][1] = *reinterpret_cast<const u32x4*>(kb + (size_t)min(2 * kp + 1, last) * stride + dc * 16);
+    zk |= (2 * kp > last ? 1u : 0u) << (2 * i);
+    zk |= (2 * kp + 1 > last ? 1u : 0u) << (2 * i + 1);
+  }
+#pragma unroll
+  for (int i = 0; i < S::VL; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int dc = u % S::DC, j = u / S::DC;
+    g.v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)min(j, last) * stride + dc * 16);
+    zv |= (j > last ? 1u : 0u) << i;
+  }
+  g.zk = zk;
+  g.zv = zv;
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void kb_stage_store(const KbStage<D, NT>& g, char* lds) {
+  using S = KbStage<D, NT>;
+  using L = KbqLds<D>;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < S::KU; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int dc = u % S::DC, kp = u / S::DC;
+    const u32x4 x = ((g.zk >> (2 * i)) & 1u) ? z : g.k[i][0];
+    const u32x4 y = ((g.zk >> (2 * i + 1)) & 1u) ? z : g.k[i][1];
+    *reinterpret_cast<u32x4*>(lds + L::K_OFF + (2 * kp) * L::KS + dc * 16) = x;
+    *reinterpret_cast<u32x4*>(lds + L::K_OFF + (2 * kp + 1) * L::KS + dc * 16) = y;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // K^T: d rows, each 32-bit word = keys (2kp, 2kp + 1)
+      const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
+      const uint32_t hi = (x[t] >> 16) | (y[t] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(lds + L::KT_OFF + (8 * dc + 2 * t) * L::TS + kp * 4) = lo;
+      *reinterpret_cast<uint32_t*>(lds + L::KT_OFF + (8 * dc + 2 * t + 1) * L::TS + kp * 4) = hi;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < S::VL; ++i) {
+    const int u = threadIdx.x + NT * i;
+    const int dc = u % S::DC, j = u / S::DC;
+    *reinterpret_cast<u32x4*>(lds + L::V_OFF + j * L::KS + dc * 16) = ((g.zv >> i) & 1u) ? z : g.v[i];
+  }
+}
+
+// ---------------------------------------------------------------- dQ pass
+constexpr int kKbqThreads = 512;      // 8 waves, 32 rows each per pass
+constexpr int kKbqRowsPerPass = 256;
+
+template <int D>
+struct KbqPass {
+  bf16x8 qf[D / 16];
+  bf16x8 df[D / 16];
+  float lse2, dsum;
+  int pos, slot, head;
+  bool ok;
+};
+
+// Row `rho` of item m (entries in LDS); rows past the item's end load a valid
+// row and are flagged !ok.
+template <int D>
+__device__ __forceinline__ void kbq_load_pass(KbqPass<D>& ps, const KbArgs& a, const KpItem& m, int rho,
+                                              const int* ent_lds) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const int G = a.group;
+  const int n_tok = m.e_end - m.e_begin;
+  ps.ok = rho < n_tok * G;
+  const int ent = ent_lds[min(rho >> a.g_shift, n_tok - 1)];
+  const int i = ent >> 4, j = ent & 15;
+  ps.head = rho & (G - 1);
+  ps.slot = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
+  ps.pos = ps.ok ? a.q_start + i : -1;
+  const size_t row = (size_t)i * a.h_q + m.r * G + ps.head;
+  const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + row * D + half * 8;
+  const bf16_t* drow = static_cast<const bf16_t*>(a.d_o) + row * D + half * 8;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    ps.qf[ks] = load_frag<bf16_t>(qrow + ks * 16);
+    ps.df[ks] = load_frag<bf16_t>(drow + ks * 16);
+  }
+  ps.lse2 = a.lse[row] * kLog2e;
+  ps.dsum = a.dsum[row];
+}
+
+// dQ^T of the wave's 32 rows against the staged block, one 32-key tile at a
+// time to bound the live accumulators.
+template <int D>
+__device__ __forceinline__ void kbq_math(const KbArgs& a, int b, const KbqPass<D>& ps, const char* lds,
+                                         f32x16 (&dq)[D / 32]) {
+  using L = KbqLds<D>;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const float c2 = a.sm_scale * kLog2e;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dq[dt] = f32x16{};
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int off = (kt * 32 + l32) * L::KS + (ks * 16 + half * 8) * 2;
+      mma32(s, *reinterpret_cast<const bf16x8*>(lds + L::K_OFF + off), ps.qf[ks]);
+      mma32(dp, *reinterpret_cast<const bf16x8*>(lds + L::V_OFF + off), ps.df[ks]);
+    }
+    float dsv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      const float pv = key > ps.pos ? 0.0f : fast_exp2(fmaf(s[v], c2, -ps.lse2));
+      dsv[v] = pv * (dp[v] - ps.dsum);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int o = 8 * h2, base = kt * 32 + h2 * 16;
+      const bf16x8 dsf = to_frag<bf16_t>(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5],
+                                         dsv[o + 6], dsv[o + 7]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        mma32(dq[dt], vt_frag<bf16_t>(lds + L::KT_OFF, L::TS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half),
+              dsf);
+    }
+    MSA_SCHED_FENCE();
+  }
+}
+
+// fp32 partial of (token, slot): [G][D] in natural order; rows past the item
+// write the trash slot so the store count never depends on the data.
+template <int D>
+__device__ __forceinline__ void kbq_store(const KbArgs& a, const KbqPass<D>& ps, const f32x16 (&dq)[D / 32]) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const size_t slot = ps.ok ? (size_t)ps.slot : a.trash_slot;
+  float* dst = a.part_dq + (slot * a.group + ps.head) * D;
+  const float sc = a.sm_scale;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<f32x4*>(dst + dt * 32 + 8 * c + 4 * half) =
+          f32x4{dq[dt][4 * c] * sc, dq[dt][4 * c + 1] * sc, dq[dt][4 * c + 2] * sc, dq[dt][4 * c + 3] * sc};
+}
+
+// Persistent over this XCD's items of window w (the forward's item order):
+// workgroup g runs on XCD g % 8 and takes items sub, sub + nsub, ...  The next
+// item's K/V are loaded into registers while the current item computes.
+template <int D>
+__global__ __launch_bounds__(kKbqThreads) void kbq_kernel(KbArgs a) {
+  using L = KbqLds<D>;
+  constexpr int NT = kKbqThreads;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int x = blockIdx.x & 7, sub = blockIdx.x >> 3, nsub = gridDim.x >> 3;
+  const int64_t n_l = (int64_t)a.h_kv * a.n_blocks, per = n_l >> 3;
+  const int64_t k0 = (int64_t)a.w * n_l + x * per;
+  const int item_begin = scalar_load(a.item_off, k0);
+  const int item_end = scalar_load(a.item_off, k0 + per);
+  int it = item_begin + sub;
+  if (it >= item_end) return;
+  const int tid = threadIdx.x, wave = tid >> 6, l32 = tid & 31;
+  int* ent_lds = reinterpret_cast<int*>(lds + L::ENT_OFF);
+
+  KbStage<D, NT> pre;
+  i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
+  KpItem cur{d[0], d[1], d[2], d[3]};
+  kb_stage_load<D, NT>(pre, a, cur.b, cur.r);
+  int pre_ent = a.entries[cur.e_begin + min(tid, cur.e_end - cur.e_begin - 1)];
+  for (;;) {
+    kb_stage_store<D, NT>(pre, lds);
+    ent_lds[tid] = pre_ent;
+    __syncthreads();
+    const int nx = it + nsub;
+    const bool has_next = nx < item_end;
+    KpItem nxt = cur;
+    if (has_next) {
+      d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(nx));
+      nxt = KpItem{d[0], d[1], d[2], d[3]};
+      kb_stage_load<D, NT>(pre, a, nxt.b, nxt.r);
+      pre_ent = a.entries[nxt.e_begin + min(tid, nxt.e_end - nxt.e_begin - 1)];
+    }
+    const int rows = (cur.e_end - cur.e_begin) * a.group;
+    for (int p0 = 0; p0 < rows; p0 += kKbqRowsPerPass) {
+      KbqPass<D> ps;
+      kbq_load_pass<D>(ps, a, cur, p0 + wave * 32 + l32, ent_lds);
+      if (__any(ps.ok)) {
+        f32x16 dq[D / 32];
+        kbq_math<D>(a, cur.b, ps, lds, dq);
+        kbq_store<D>(a, ps, dq);
+      }
+    }
+    if (!has_next) break;
+    __syncthreads();  // every wave is done with this item's LDS
+    it = nx;
+    cur = nxt;
+  }
+}
+
+// Second stage of dQ: the sum of a row's per-slot partials.
+template <int D>
+__global__ __launch_bounds__(256) void kbq_merge_kernel(KbArgs a) {
+  constexpr int DC = D / 8;
+  const int64_t t = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t rl = t / DC;  // il * h_q + h
+  const int c = (int)(t % DC);
+  const int il = (int)(rl / a.h_q), h = (int)(rl % a.h_q);
+  const int i = a.w * a.window + il;
+  if (il >= a.window || i >= a.n_q) return;
+  const int G = a.group, r = h / G, g = h % G;
+  const int diag = (a.q_start + i) >> 7;
+  const uint32_t used = used_slots(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, diag);
+  const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.top_k; ++j) {
+    if (!((used >> j) & 1u)) continue;
+    const float* src = a.part_dq + ((slot0 + j) * G + g) * D + c * 8;
+    s0 += *reinterpret_cast<const f32x4*>(src);
+    s1 += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  bf16_t* dst = static_cast<bf16_t*>(a.dq) + ((size_t)i * a.h_q + h) * D + c * 8;
+  *reinterpret_cast<bf16x8*>(dst) = bf16x8{from_f32<bf16_t>(s0[0]), from_f32<bf16_t>(s0[1]), from_f32<bf16_t>(s0[2]),
+                                           from_f32<bf16_t>(s0[3]), from_f32<bf16_t>(s1[0]), from_f32<bf16_t>(s1[1]),
+                                           from_f32<bf16_t>(s1[2]), from_f32<bf16_t>(s1[3])};
+}
+
+// ------------------------------------------------------------ dK/dV pass
+constexpr int kKbkvThreads = 256;  // 4 waves, 32 keys each
+
+template <int D>
+struct KbkvLds {
+  static constexpr int KS = D * 2 + 16;   // bytes per key row / query row
+  static constexpr int TS = 32 * 2 + 8;   // bytes per d row of a 32-row Q^T / dO^T tile
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 128 * KS;
+  // one row tile: Q rows, dO rows, Q^T, dO^T, then lse2, dsum, pos per row
+  static constexpr int Q_R = 0;
+  static constexpr int D_R = 32 * KS;
+  static constexpr int Q_T = 2 * 32 * KS;
+  static constexpr int D_T = Q_T + D * TS;
+  static constexpr int SC = D_T + D * TS;
+  static constexpr int TILE = SC + 3 * 32 * 4;
+  static constexpr int T_OFF = 2 * 128 * KS;
+  static constexpr int ENT_OFF = T_OFF + 2 * TILE;
+  static constexpr int ENT_CAP = 2048;  // token entries of an item
+  static constexpr int BYTES = ENT_OFF + ENT_CAP * 4;
+};
+
+// Row tile staging: unit u = (row pair rp, 16-byte chunk dc) of Q and dO.
+template <int D>
+struct KbkvTileRegs {
+  u32x4 q0, q1, d0, d1;
+  float lse2, dsum;
+  int pos;
+};
+
+template <int D>
+__device__ __forceinline__ void kbkv_tile_load(KbkvTileRegs<D>& g, const KbArgs& a, const KpItem& m, int row0,
+                                               const int* ent_lds) {
+  constexpr int DC = D / 8;
+  const int tid = threadIdx.x;
+  const int G = a.group, n_tok = m.e_end - m.e_begin, rows = n_tok * G;
+  if (tid < 16 * DC) {
+    const int dc = tid % DC, rp = tid / DC;
+    const int ra = row0 + 2 * rp, rb = ra + 1;
+    const int ea = ent_lds[min(ra >> a.g_shift, n_tok - 1)], eb = ent_lds[min(rb >> a.g_shift, n_tok - 1)];
+    const size_t xa = ((size_t)(ea >> 4) * a.h_q + m.r * G + (ra & (G - 1))) * D + dc * 8;
+    const size_t xb = ((size_t)(eb >> 4) * a.h_q + m.r * G + (rb & (G - 1))) * D + dc * 8;
+    g.q0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xa);
+    g.q1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xb);
+    g.d0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xa);
+    g.d1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xb);
+  }
+  if (tid < 32) {
+    const int rr = row0 + tid;
+    const bool ok = rr < rows;
+    const int e = ent_lds[min(rr >> a.g_shift, n_tok - 1)];
+    const size_t x = (size_t)(e >> 4) * a.h_q + m.r * G + (rr & (G - 1));
+    g.lse2 = ok ? a.lse[x] * kLog2e : 0.0f;
+    g.dsum = ok ? a.dsum[x] : 0.0f;
+    g.pos = ok ? a.q_start + (e >> 4) : -1;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kbkv_tile_store(const KbkvTileRegs<D>& g, char* tile) {
+  using L = KbkvLds<D>;
+  constexpr int DC = D / 8;
+  const int tid = threadIdx.x;
+  if (tid < 16 * DC) {
+    const int dc = tid % DC, rp = tid / DC;
+    *reinterpret_cast<u32x4*>(tile + L::Q_R + (2 * rp) * L::KS + dc * 16) = g.q0;
+    *reinterpret_cast<u32x4*>(tile + L::Q_R + (2 * rp + 1) * L::KS + dc * 16) = g.q1;
+    *reinterpret_cast<u32x4*>(tile + L::D_R + (2 * rp) * L::KS + dc * 16) = g.d0;
+    *reinterpret_cast<u32x4*>(tile + L::D_R + (2 * rp + 1) * L::KS + dc * 16) = g.d1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // d rows; each 32-bit word = rows (2rp, 2rp + 1)
+      *reinterpret_cast<uint32_t*>(tile + L::Q_T + (8 * dc + 2 * t) * L::TS + rp * 4) =
+          (g.q0[t] & 0xffffu) | (g.q1[t] << 16);
+      *reinterpret_cast<uint32_t*>(tile + L::Q_T + (8 * dc + 2 * t + 1) * L::TS + rp * 4) =
+          (g.q0[t] >> 16) | (g.q1[t] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(tile + L::D_T + (8 * dc + 2 * t) * L::TS + rp * 4) =
+          (g.d0[t] & 0xffffu) | (g.d1[t] << 16);
+      *reinterpret_cast<uint32_t*>(tile + L::D_T + (8 * dc + 2 * t + 1) * L::TS + rp * 4) =
+          (g.d0[t] >> 16) | (g.d1[t] & 0xffff0000u);
+    }
+  }
+  if (tid < 32) {
+    float* sc = reinterpret_cast<float*>(tile + L::SC);
+    sc[tid] = g.lse2;
+    sc[32 + tid] = g.dsum;
+    reinterpret_cast<int*>(sc + 64)[tid] = g.pos;
+  }
+}
+
+// Items of all (group, block) cells, round-robin over a persistent grid.
+// Each wave owns keys 32*wave .. 32*wave + 31 of the item's block.
+template <int D>
+__global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
+  using L = KbkvLds<D>;
+  constexpr int NT = kKbkvThreads;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int n_items = scalar_load(a.item_off, (int64_t)a.h_kv * a.n_blocks);
+  int* ent_lds = reinterpret_cast<int*>(lds + L::ENT_OFF);
+  const float c2 = a.sm_scale * kLog2e;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
+    const KpItem m{d[0], d[1], d[2], d[3]};
+    const int n_tok = m.e_end - m.e_begin;
+    const int rows = n_tok * a.group;
+    __syncthreads();  // the previous item's readers are done
+    // K and V rows of the block (zeros past n_kv)
+    {
+      constexpr int DC = D / 8;
+      const int stride = a.h_kv * D * 2;
+      const size_t base = (((size_t)m.b * kBlock) * a.h_kv + m.r) * D * 2;
+      const int last = min(kBlock, a.n_kv - m.b * kBlock) - 1;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 128 * DC / NT; ++i) {
+        const int u = tid + NT * i;
+        const int dc = u % DC, j = u / DC;
+        const size_t off = base + (size_t)min(j, last) * stride + dc * 16;
+        const u32x4 kx = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k) + off);
+        const u32x4 vx = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v) + off);
+        *reinterpret_cast<u32x4*>(lds + L::K_OFF + j * L::KS + dc * 16) = j > last ? z : kx;
+        *reinterpret_cast<u32x4*>(lds + L::V_OFF + j * L::KS + dc * 16) = j > last ? z : vx;
+      }
+      for (int e = tid; e < n_tok; e += NT) ent_lds[e] = a.entries[m.e_begin + e];
+    }
+    __syncthreads();
+    KbkvTileRegs<D> g;
+    kbkv_tile_load<D>(g, a, m, 0, ent_lds);
+    kbkv_tile_store<D>(g, lds + L::T_OFF);
+    __syncthreads();
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      dk[dt] = f32x16{};
+      dv[dt] = f32x16{};
+    }
+    const int key_abs = m.b * kBlock + wave * 32 + l32;
+    const int n_pass = (rows + 31) / 32;
+    for (int ps = 0; ps < n_pass; ++ps) {
+      const char* tile = lds + L::T_OFF + (ps & 1) * L::TILE;
+      const bool more = ps + 1 < n_pass;
+      if (more) kbkv_tile_load<D>(g, a, m, (ps + 1) * 32, ent_lds);
+      // S = Q.K^T and dP = dO.V^T for the tile's 32 rows x this wave's 32 keys
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int roff = l32 * L::KS + (ks * 16 + half * 8) * 2;
+        const int koff = (wave * 32 + l32) * L::KS + (ks * 16 + half * 8) * 2;
+        mma32(s, *reinterpret_cast<const bf16x8*>(tile + L::Q_R + roff),
+              *reinterpret_cast<const bf16x8*>(lds + L::K_OFF + koff));
+        mma32(dp, *reinterpret_cast<const bf16x8*>(tile + L::D_R + roff),
+              *reinterpret_cast<const bf16x8*>(lds + L::V_OFF + koff));
+      }
+      const float* sc = reinterpret_cast<const float*>(tile + L::SC);
+      const int* pos = reinterpret_cast<const int*>(sc + 64);
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+        const float pr = key_abs > pos[row] ? 0.0f : fast_exp2(fmaf(s[v], c2, -sc[row]));
+        pv[v] = pr;
+        dsv[v] = pr * (dp[v] - sc[32 + row]);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int o = 8 * h2;
+        const bf16x8 pf = to_frag<bf16_t>(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6],
+                                          pv[o + 7]);
+        const bf16x8 dsf = to_frag<bf16_t>(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5],
+                                           dsv[o + 6], dsv[o + 7]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dd = dt * 32 + l32;
+          mma32(dv[dt], vt_frag<bf16_t>(tile + L::D_T, L::TS, dd, 16 * h2 + 4 * half, 16 * h2 + 8 + 4 * half), pf);
+          mma32(dk[dt], vt_frag<bf16_t>(tile + L::Q_T, L::TS, dd, 16 * h2 + 4 * half, 16 * h2 + 8 + 4 * half), dsf);
+        }
+      }
+      if (more) kbkv_tile_store<D>(g, lds + L::T_OFF + ((ps + 1) & 1) * L::TILE);
+      __syncthreads();
+    }
+    // dK = scale * (dS^T.Q), dV = P^T.dO for key `key_abs`: lane holds d =
+    // dt*32 + 8c + 4*half + {0..3}
+    const int64_t cell = cell_key(0, m.r, m.b, a.n_blocks, a.h_kv);
+    const int ib = scalar_load(a.item_off, cell), ie = scalar_load(a.item_off, cell + 1);
+    if (ie - ib == 1) {
+      if (key_abs < a.n_kv) {
+        bf16_t* pk = static_cast<bf16_t*>(a.dk) + ((size_t)key_abs * a.h_kv + m.r) * D;
+        bf16_t* pv2 = static_cast<bf16_t*>(a.dv) + ((size_t)key_abs * a.h_kv + m.r) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int d0 = dt * 32 + 8 * c + 4 * half;
+            store4<bf16_t>(pk + d0, dk[dt][4 * c] * a.sm_scale, dk[dt][4 * c + 1] * a.sm_scale,
+                           dk[dt][4 * c + 2] * a.sm_scale, dk[dt][4 * c + 3] * a.sm_scale);
+            store4<bf16_t>(pv2 + d0, dv[dt][4 * c], dv[dt][4 * c + 1], dv[dt][4 * c + 2], dv[dt][4 * c + 3]);
+          }
+      }
+    } else {
+      float* pk = a.part_dkv + (((size_t)it * 2 + 0) * kBlock + wave * 32 + l32) * D;
+      float* pv2 = a.part_dkv + (((size_t)it * 2 + 1) * kBlock + wave * 32 + l32) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = dt * 32 + 8 * c + 4 * half;
+          *reinterpret_cast<f32x4*>(pk + d0) = f32x4{dk[dt][4 * c] * a.sm_scale, dk[dt][4 * c + 1] * a.sm_scale,
+                                                     dk[dt][4 * c + 2] * a.sm_scale, dk[dt][4 * c + 3] * a.sm_scale};
+          *reinterpret_cast<f32x4*>(pv2 + d0) = f32x4{dv[dt][4 * c], dv[dt][4 * c + 1], dv[dt][4 * c + 2],
+                                                      dv[dt][4 * c + 3]};
+        }
+    }
+  }
+}
+
+// dK/dV of every (block, group): the sum of a split cell's item partials, or
+// zeros for blocks no query selected.  Single-item cells were written by the
+// pass itself.
+template <int D>
+__global__ __launch_bounds__(256) void kbkv_reduce_kernel(KbArgs a) {
+  const int b = blockIdx.x, r = blockIdx.y;
+  int ib = 0, ie = 0;
+  if (b < a.n_blocks) {
+    const int64_t cell = cell_key(0, r, b, a.n_blocks, a.h_kv);
+    ib = a.item_off[cell];
+    ie = a.item_off[cell + 1];
+  }
+  if (ie - ib == 1) return;
+  for (int e = threadIdx.x; e < kBlock * D / 4; e += 256) {
+    const int key = e / (D / 4), d0 = 4 * (e % (D / 4));
+    const int key_abs = b * kBlock + key;
+    if (key_abs >= a.n_kv) continue;
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int it = ib; it < ie; ++it) {
+      sk += *reinterpret_cast<const f32x4*>(a.part_dkv + (((size_t)it * 2 + 0) * kBlock + key) * D + d0);
+      sv += *reinterpret_cast<const f32x4*>(a.part_dkv + (((size_t)it * 2 + 1) * kBlock + key) * D + d0);
+    }
+    const size_t o = ((size_t)key_abs * a.h_kv + r) * D + d0;
+    store4<bf16_t>(static_cast<bf16_t*>(a.dk) + o, sk[0], sk[1], sk[2], sk[3]);
+    store4<bf16_t>(static_cast<bf16_t*>(a.dv) + o, sv[0], sv[1], sv[2], sv[3]);
+  }
+}
+
+// ------------------------------------------------------------------- host
+bool backward_supported(int dtype, int d_h) { return dtype == 0 && (d_h == 64 || d_h == 128); }
+
+BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q, int32_t h_kv, int32_t d_h,
+                           int32_t top_k) {
+  BackwardPlan p{};
+  const int G = h_q / h_kv;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  // dQ pass: the forward's windows (its partials are fp32 here)
+  p.q = prefill_plan(1, n_q, q_start, n_kv, h_q, h_kv, d_h, top_k);
+  p.q.total = p.q.off_part_o;  // schedule arrays only
+  // dK/dV pass: one window; items of up to KbkvLds::ENT_CAP tokens
+  schedule_layout(p.kv, n_q, q_start, h_kv, top_k, std::max<int32_t>(n_q, 1), KbkvLds<128>::ENT_CAP,
+                  /*ordered=*/true);
+  size_t off = 0;
+  p.off_q = off; off = align(off + p.q.total);
+  p.off_kv = off; off = align(off + p.kv.total);
+  p.off_dsum = off; off = align(off + (size_t)n_q * h_q * 4);
+  p.off_part_dq = off; off = align(off + ((size_t)p.q.window * h_kv * top_k + 2) * G * d_h * 4);
+  p.off_part_dkv = off; off = align(off + (size_t)p.kv.max_items * 2 * kBlock * d_h * 4);
+  p.total = off;
+  return p;
+}
+
+template <int D>
+static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl, hipStream_t st) {
+  const AttnArgs& a = ba.attn;
+  char* ws = static_cast<char*>(a.ws);
+  KbArgs k{};
+  k.q = a.q;
+  k.k = a.k;
+  k.v = a.v;
+  k.o = a.o;
+  k.lse = a.lse;
+  k.d_o = ba.d_o;
+  k.dq = ba.dq;
+  k.dk = ba.dk;
+  k.dv = ba.dv;
+  k.dsum = reinterpret_cast<float*>(ws + pl.off_dsum);
+  k.block_idx = a.block_idx;
+  k.part_dq = reinterpret_cast<float*>(ws + pl.off_part_dq);
+  k.part_dkv = reinterpret_cast<float*>(ws + pl.off_part_dkv);
+  k.n_q = a.n_q;
+  k.q_start = a.q_start;
+  k.n_kv = a.n_kv;
+  k.h_q = a.h_q;
+  k.h_kv = a.h_kv;
+  k.group = a.group;
+  k.g_shift = __builtin_ctz((unsigned)a.group);
+  k.top_k = a.top_k;
+  k.sm_scale = a.sm_scale;
+
+  const unsigned nb_kv = (unsigned)((a.n_kv + kBlock - 1) / kBlock);
+  if (a.n_q == 0) {  // no query attends: dK = dV = 0
+    k.n_blocks = 0;
+    if (nb_kv > 0) hipLaunchKernelGGL(kbkv_reduce_kernel<D>, dim3(nb_kv, (unsigned)a.h_kv), dim3(256), 0, st, k);
+    return hipGetLastError();
+  }
+  const int64_t rows = (int64_t)a.n_q * a.h_q;
+  hipLaunchKernelGGL(kb_dsum_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, k);
+
+  // dQ: windows of the forward's schedule
+  AttnArgs aq = a;
+  aq.ws = ws + pl.off_q;
+  SchedArgs sq;
+  hipError_t e = launch_prefill_schedule(aq, pl.q, sq, st);
+  if (e != hipSuccess) return e;
+  k.item_off = sq.item_off;
+  k.entries = sq.entries;
+  k.items = sq.items;
+  k.n_blocks = pl.q.n_blocks;
+  k.window = pl.q.window;
+  k.trash_slot = (size_t)pl.q.window * a.h_kv * a.top_k;
+  const int n_cu = num_cus();
+  for (int w = 0; w < pl.q.n_windows; ++w) {
+    const int tok = std::min<int>(pl.q.window, a.n_q - w * pl.q.window);
+    const int64_t bound = (int64_t)tok * a.h_kv * a.top_k / pl.q.chunk + (int64_t)a.h_kv * pl.q.n_blocks + 1;
+    const int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu);
+    const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
+    k.w = w;
+    const int pk = profile_begin(PK_KBQ, st);
+    hipLaunchKernelGGL(kbq_kernel<D>, dim3(grid), dim3(kKbqThreads), 0, st, k);
+    profile_end(pk, st);
+    const int64_t mrows = (int64_t)tok * a.h_q;
+    hipLaunchKernelGGL(kbq_merge_kernel<D>, dim3((unsigned)((mrows * (D / 8) + 255) / 256)), dim3(256), 0, st, k);
+  }
+
+  // dK/dV: one window over all queries
+  AttnArgs akv = a;
+  akv.ws = ws + pl.off_kv;
+  SchedArgs skv;
+  e = launch_prefill_schedule(akv, pl.kv, skv, st);
+  if (e != hipSuccess) return e;
+  k.item_off = skv.item_off;
+  k.entries = skv.entries;
+  k.items = skv.items;
+  k.n_blocks = pl.kv.n_blocks;
+  k.window = pl.kv.window;
+  k.w = 0;
+  const int pk = profile_begin(PK_KBKV, st);
+  hipLaunchKernelGGL(kbkv_kernel<D>, dim3((unsigned)n_cu), dim3(kKbkvThreads), 0, st, k);
+  profile_end(pk, st);
+  if (nb_kv > 0)
+    hipLaunchKernelGGL(kbkv_reduce_kernel<D>, dim3(nb_kv, (unsigned)a.h_kv), dim3(256), 0, st, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_prefill_backward(int d_h, const BackwardArgs& a, const BackwardPlan& pl, hipStream_t st) {
+  if (d_h == 128) return backward_typed<128>(a, pl, st);
+  if (d_h == 64) return backward_typed<64>(a, pl, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_POOL_MAX, MSA_POOL_MEAN = 0, 1
-OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE = 0, 1, 2, 3, 4
+OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE, OP_PREFILL_BACKWARD = 0, 1, 2, 3, 4, 5
 BLOCK = 128
 
 
@@ -47,6 +47,7 @@ class KV(ctypes.Structure):
 _lib = None
 
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
+           "msa_sparse_prefill_backward",
            "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
            "msa_profile_enable", "msa_profile_read"]
 
@@ -65,7 +66,10 @@ def lib() -> ctypes.CDLL:
         L.msa_sparse_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_sparse_decode.argtypes = [P(Shape), i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
-        for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill"):
+        L.msa_sparse_prefill_backward.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  sz, vp]
+        for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
+                  "msa_sparse_prefill_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_workspace_size.argtypes = [i32, P(Shape), i32, i32, i32, i32, i32]
         L.msa_workspace_size.restype = sz
@@ -245,6 +249,26 @@ def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *, sm_sc
     _check(lib().msa_sparse_decode(ctypes.byref(shape), batch, _ptr(q), ctypes.byref(kv), _ptr(block_idx),
                                    _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(stream)))
     return (o, lse) if with_lse else o
+
+
+def sparse_prefill_backward(q, k, v, block_idx, o, lse, d_o, *, q_start=0, sm_scale=0.0, top_k=None,
+                            out=None, workspace=None, stream=None):
+    """msa_sparse_prefill_backward: gradients (dq, dk, dv) of msa_sparse_prefill
+    for one contiguous sequence, given the forward's o and lse and d_o.
+    q, o, d_o [n_q, h_q, d_h]; k, v [n_kv, h_kv, d_h]; block_idx int32
+    [n_q, h_kv, k]; lse fp32 [n_q, h_q]."""
+    n_q, h_q, d_h = q.shape
+    n_kv, h_kv = k.shape[0], k.shape[1]
+    tk = int(top_k) if top_k is not None else block_idx.shape[-1]
+    shape = make_shape(h_q, h_kv, d_h, 64, tk, _dtype_code(q), sm_scale=sm_scale)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    nws = workspace_size(OP_PREFILL_BACKWARD, shape, n_q=n_q, q_start=int(q_start), n_kv=n_kv)
+    ws = _workspace(nws, q.device, workspace)
+    kv = KV(_ptr(k), _ptr(v), None, None, None, n_kv, 0)
+    _check(lib().msa_sparse_prefill_backward(ctypes.byref(shape), n_q, int(q_start), _ptr(q), ctypes.byref(kv),
+                                             _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
+                                             _ptr(dv), _ptr(ws), nws, _stream(stream)))
+    return dq, dk, dv
 
 
 def dense_prefill(q, k, v, *, q_start=0, sm_scale=0.0, with_lse=False, out=None, stream=None):

@@ -162,6 +162,26 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
                              float* lse, void* workspace, size_t ws_bytes,
                              void* hip_stream);
 
+/* Training path: gradients of msa_sparse_prefill ([P1] §4.3 Eq. (8), for
+ * the training of §4.5) for one contiguous sequence.  With P the softmax of
+ * a (token, head) row over the visible keys of its group's selected blocks
+ * (recomputed from the forward's lse), dP = d_o.V^T and D = rowsum(d_o*o):
+ *   dS = P*(dP - D),  dq = sm_scale dS.K,  dk = sm_scale dS^T.Q,  dv = P^T.d_o.
+ *   q, o, d_o, dq   [n_q, h_q, d_h]      o and lse are the forward's outputs
+ *   lse             [n_q, h_q] fp32      (natural log, as msa_sparse_prefill)
+ *   kv->k, kv->v    [n_kv, h_kv, d_h]    contiguous (page_table and seq_lens
+ *                                        NULL); block_idx as in the forward
+ *   dk, dv          [n_kv, h_kv, d_h]    written in full: keys no query
+ *                                        attends get 0
+ * Built for dtype MSA_BF16 (bf16 caches) and d_h 64/128; other shapes
+ * return MSA_ERR_UNSUPPORTED.  Accumulation is fp32 without atomics, so
+ * results are bitwise reproducible.  Workspace: msa_workspace_size(5, ...). */
+msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int32_t q_start,
+                                       const void* q, const msa_kv* kv, const int32_t* block_idx,
+                                       const void* o, const float* lse, const void* d_o, void* dq,
+                                       void* dk, void* dv, void* workspace, size_t ws_bytes,
+                                       void* hip_stream);
+
 /* Dense causal GQA attention, [P1] §2.2 Eq. (1): the comparison kernel.
  *   Same arguments as msa_sparse_prefill without block_idx; contiguous cache
  *   only.  top_k, force_local and the index fields of `shape` are ignored. */
@@ -171,7 +191,8 @@ msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_star
 
 /* Workspace bytes a call needs.  op: 0 = msa_index_topk in prefill mode,
  * 1 = msa_sparse_prefill, 2 = msa_sparse_decode, 3 = msa_dense_prefill,
- * 4 = msa_index_topk in decode mode.  Pass the same shape, batch, n_q,
+ * 4 = msa_index_topk in decode mode, 5 = msa_sparse_prefill_backward.
+ * Pass the same shape, batch, n_q,
  * q_start and cache geometry (n_kv; max_pages for decode mode) as the
  * call.  Returns 0 when no workspace is needed or for an invalid request
  * (then msa_last_error() is non-empty).                                 */
@@ -200,7 +221,9 @@ int32_t msa_abi_version(void);
  *   prefill), "kp_kernel" and "km_kernel" (msa_sparse_prefill, KV-outer
  *   pass and merge, one launch each per window of queries),
  *   "ki_decode_scan_kernel" (msa_index_topk, decode), "kd_kernel"
- *   (msa_sparse_decode).  Unknown names or NULL outputs: MSA_ERR_INVALID_ARG.
+ *   (msa_sparse_decode), "kbq_kernel" (dq pass of msa_sparse_prefill_backward,
+ *   one launch per window) and "kbkv_kernel" (its dk/dv pass).  Unknown
+ *   names or NULL outputs: MSA_ERR_INVALID_ARG.
  * Not meant to be used while calls are being enqueued from other threads. */
 msa_status msa_profile_enable(int32_t on);
 msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches);

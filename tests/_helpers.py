@@ -78,3 +78,23 @@ def compare_lse(l_gpu, l_ref, dtype):
     err = np.abs(lg - lr)
     assert float(err.max()) <= tol, f"lse: max-abs {float(err.max()):.3e} > {tol}"
     return float(err.max())
+
+
+# Gradients (bf16 outputs of fp32 accumulations whose operands P and dS are
+# rounded to bf16 for the MFMA): relative to the gradient's own scale.
+GRAD_TOL = {"max_rel_to_max": 1e-2, "rel_l2": 1e-2}
+
+
+def compare_grad(g_gpu, g_ref, what="grad"):
+    gg = np64(g_gpu) if isinstance(g_gpu, torch.Tensor) else np.asarray(g_gpu, np.float64)
+    gr = np.asarray(g_ref, np.float64)
+    assert gg.shape == gr.shape, (gg.shape, gr.shape)
+    assert np.all(np.isfinite(gg)), f"{what}: non-finite values"
+    scale = float(np.abs(gr).max()) if gr.size else 0.0
+    err = np.abs(gg - gr)
+    max_err = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(gg - gr) / max(np.linalg.norm(gr), 1e-30))
+    assert max_err <= GRAD_TOL["max_rel_to_max"] * max(scale, 1e-30), \
+        f"{what}: max error {max_err:.3e} > {GRAD_TOL['max_rel_to_max']} x max|ref| {scale:.3e}"
+    assert rel <= GRAD_TOL["rel_l2"], f"{what}: relative L2 {rel:.3e} > {GRAD_TOL['rel_l2']}"
+    return max_err / max(scale, 1e-30), rel

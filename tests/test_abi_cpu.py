@@ -158,3 +158,23 @@ def test_pool_mode_validation():
     bad = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, pool=7)
     assert msa.lib().msa_sparse_prefill(ctypes.byref(bad), 0, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0,
                                         None) == 0
+
+
+def test_backward_validation():
+    L = msa.lib()
+    s = _shape()
+    kv = msa.KV(FAKE, FAKE, None, None, None, 256, 0)
+    args = lambda shp, n_q=8, q_start=0, kv_=kv, dq=FAKE: (ctypes.byref(shp), n_q, q_start, FAKE, ctypes.byref(kv_),
+                                                          FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, None, 0, None)
+    assert L.msa_sparse_prefill_backward(*args(_shape(dtype_code=1))) == 2 and "MSA_BF16" in _err()
+    assert L.msa_sparse_prefill_backward(*args(_shape(d_h=96))) == 2
+    paged = msa.KV(FAKE, FAKE, None, FAKE, None, 256, 2)
+    assert L.msa_sparse_prefill_backward(*args(s, kv_=paged)) == 2 and "contiguous" in _err()
+    assert L.msa_sparse_prefill_backward(*args(s, n_q=300)) == 1 and "exceeds" in _err()
+    assert L.msa_sparse_prefill_backward(*args(s, dq=None)) == 1 and "NULL" in _err()
+    assert L.msa_sparse_prefill_backward(*args(s)) == 3 and "workspace" in _err()
+    f8 = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, cache_dtype=msa.MSA_FP8_E4M3)
+    assert L.msa_sparse_prefill_backward(*args(f8)) == 2 and "e4m3" in _err()
+    need = msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=8, n_kv=256)
+    assert need > msa.workspace_size(msa.OP_PREFILL, s, n_q=8, n_kv=256)
+    assert msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=0, n_kv=256) == 0

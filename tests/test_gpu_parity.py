@@ -13,7 +13,7 @@ from oracle import msa_oracle as orc
 from synth import MODEL_SHAPE, TINY_SHAPE, gen_decode_paged, gen_long_context, gen_prefill
 from synth.inputs import HeadShape
 
-from _helpers import compare_index_rows, compare_lse, compare_out, np64
+from _helpers import compare_grad, compare_index_rows, compare_lse, compare_out, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -526,3 +526,84 @@ def test_long_context_1m_chunked_prefill_and_decode_sampled():
                                           d_ids, [pos], shape.h_kv)
         compare_out(do, d_ref, torch.bfloat16)
         compare_lse(dl, l_ref, torch.bfloat16)
+
+
+# ------------------------------------------------------------- training path
+
+def _backward_case(shape, n_kv, n_q, seed, *, all_blocks=False):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV)
+    q_start = inp["q_start"]
+    _say("backward", shape, n_kv, n_q, seed, "all blocks" if all_blocks else "")
+    top_k = shape.top_k
+    if all_blocks:
+        # every query keeps the first k - 1 blocks ("sink" blocks) and its own
+        bidx = torch.full((n_q, shape.h_kv, top_k), -1, dtype=torch.int32)
+        for i in range(n_q):
+            d = (q_start + i) // 128
+            ids = sorted(set(range(min(top_k - 1, d))) | {d})
+            bidx[i, :, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        bidx = bidx.to(DEV)
+    else:
+        bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=top_k, q_start=q_start)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1000)
+    d_o = torch.randn(inp["q"].shape, generator=g).to(torch.bfloat16).to(DEV)
+    dq, dk, dv = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o, q_start=q_start)
+    torch.cuda.synchronize()
+    ids = bidx.cpu().numpy()
+    rq, rk, rv = orc.sparse_attention_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start,
+                                               np64(d_o))
+    compare_grad(dq, rq, "dq")
+    compare_grad(dk, rk, "dk")
+    compare_grad(dv, rv, "dv")
+    return dq, dk, dv
+
+
+def test_backward_model_shape_ragged():
+    _backward_case(MODEL_SHAPE, 2300, 2300, 50)
+
+
+def test_backward_chunked_q_start_and_untouched_keys():
+    # queries over the last 700 of 3000 keys: keys no query selected get 0
+    dq, dk, dv = _backward_case(MODEL_SHAPE, 3000, 700, 51)
+    assert torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+
+
+def test_backward_head_ratios_and_d64():
+    _backward_case(HeadShape(16, 2, 64, 32, 6), 1700, 1700, 52)
+    _backward_case(HeadShape(16, 16, 128, 64, 8), 900, 900, 53)
+    _backward_case(HeadShape(64, 8, 128, 64, 16), 1300, 1300, 54)
+
+
+def test_backward_hot_block_split_over_items():
+    # every query selects the same 15 sink blocks: those cells hold 4500
+    # tokens, more than one item takes, so their dK/dV go through the
+    # split-cell reduction
+    _backward_case(HeadShape(16, 1, 128, 64, 16), 4500, 4500, 55, all_blocks=True)
+
+
+def test_backward_deterministic():
+    msa = _msa()
+    inp = gen_prefill(1500, MODEL_SHAPE, dtype=torch.bfloat16, seed=56, device=DEV)
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, with_lse=True)
+    d_o = torch.randn(inp["q"].shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
+    a = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o)
+    b = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_no_queries_zero_fills():
+    msa = _msa()
+    inp = gen_prefill(600, MODEL_SHAPE, n_q=1, dtype=torch.bfloat16, seed=57, device=DEV)
+    q0 = inp["q"][:0]
+    bidx = torch.empty((0, 4, 16), dtype=torch.int32, device=DEV)
+    dk = torch.full_like(inp["k"], 3.0)
+    dv = torch.full_like(inp["v"], 3.0)
+    msa.sparse_prefill_backward(q0, inp["k"], inp["v"], bidx, q0, torch.empty((0, 64), device=DEV), q0,
+                                q_start=600, out=(q0, dk, dv))
+    torch.cuda.synchronize()
+    assert not dk.any() and not dv.any()
