@@ -12,7 +12,12 @@ the stream it is launched on; ``roofline`` covers the dominant call
 GQA kernel is timed at the prefill shape for comparison, outside the step.
 The float64 oracle is timed on a bounded sample on the host (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload step|prefill128k|long1m]
+Other workloads print their own JSON line: prefill128k (planted), long1m,
+decode_fp8 (e4m3 caches), backward32k (the training path's gradient call at
+the 32K prefill shape) and copy (bandwidth calibration).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+                       [--workload step|prefill128k|long1m|decode_fp8|backward32k|copy]
 """
 from __future__ import annotations
 
@@ -342,7 +347,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "copy"])
+    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "backward32k",
+                                                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -371,6 +377,8 @@ def main():
         bench_decode_fp8(msa, args)
     elif args.workload == "prefill128k":
         bench_prefill_only(msa, args, planted=True)
+    elif args.workload == "backward32k":
+        bench_backward(msa, args)
     else:
         bench_long(msa, args)
 
@@ -591,6 +599,52 @@ def bench_prefill_only(msa, args, planted=True):
                       "index_roofline": roofline("mfma", idx_fl, t_ip, "TFLOP/s"),
                       "sparse_roofline": roofline("mfma", main_fl, t_sp, "TFLOP/s"),
                       "planted_blocks_retrieved": bool(hit)}))
+
+
+def bench_backward(msa, args):
+    """msa_sparse_prefill_backward at the 32K prefill shape.  Algorithmic work:
+    five d_h-wide products per (query head, visible selected key) -- S, dP,
+    dV, dK, dQ -- i.e. 10 * d_h FLOPs, 2.5x the forward's main branch."""
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    n = 32768
+    inp = gen_prefill(n, shape, dtype=torch.bfloat16, seed=1, device=dev)
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, with_lse=True)
+    d_o = torch.randn(inp["q"].shape, generator=torch.Generator(device=dev).manual_seed(2), device=dev,
+                      dtype=torch.float32).to(torch.bfloat16)
+    s = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+    ws = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=n, n_kv=n)), dtype=torch.uint8,
+                     device=dev)
+    outs = (torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]))
+    fn = [lambda: msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o, out=outs,
+                                              workspace=ws)]
+    timer = CallTimer(["backward"])
+    for _ in range(args.warmup):
+        fn[0]()
+    torch.cuda.synchronize()
+    evs = [timer.step(fn) for _ in range(args.steps)]
+    timer.collect(evs)
+    t = timer.mean_ms("backward")
+    kern = {}
+    if not args.no_kernel_timing:
+        msa.profile_enable(True)
+        for _ in range(min(args.steps, 5)):
+            fn[0]()
+        torch.cuda.synchronize()
+        msa.profile_enable(False)
+        for k_ in ("kbq_kernel", "kbkv_kernel"):
+            tot, cnt = msa.profile_read(k_)
+            if cnt:
+                kern[k_] = {"launches_per_call": cnt / min(args.steps, 5), "avg_launch_ms": round(tot / cnt, 5),
+                            "ms_per_call": round(tot / min(args.steps, 5), 4)}
+    _, main_fl, _ = prefill_counts(n, 0, shape)
+    bwd_fl = 2.5 * main_fl
+    print(json.dumps({"workload": "backward 1x32768 (dq, dk, dv of the sparse prefill), 64 q / 4 kv heads, "
+                                  "d_h 128, k 16, bf16", "ms": round(t, 3),
+                      "p10_ms": round(timer.pct("backward", 10), 3), "p90_ms": round(timer.pct("backward", 90), 3),
+                      "tokens_per_s": round(n / (t * 1e-3), 1), "flops": bwd_fl,
+                      "roofline": roofline("mfma", bwd_fl, t, "TFLOP/s"), "kernels": kern}))
 
 
 def bench_long(msa, args):

@@ -179,6 +179,7 @@ __global__ void ks_items_kernel(SchedArgs a) {
 // the cell's bitmap; one workgroup per cell then writes the set bits out in
 // order at the cell's offset.
 __global__ void ks_bits_zero_kernel(SchedArgs a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.fill[0] = 0;  // work-queue head of the consumer
   const int64_t n = a.n_cells * a.words;
   for (int64_t x = blockIdx.x * 256ll + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) a.bitmap[x] = 0u;
 }
@@ -196,6 +197,21 @@ __global__ void ks_bits_set_kernel(SchedArgs a) {
       const int64_t cell = cell_key(w, r, br[j], a.n_blocks, a.h_kv);
       atomicOr(&a.bitmap[cell * a.words + (il >> 5)], 1u << (il & 31));
     }
+}
+
+// Ordered mode's cell sizes: the popcount of each cell's bitmap (no atomics
+// on a few hot counters).
+__global__ __launch_bounds__(256) void ks_bits_count_kernel(SchedArgs a) {
+  __shared__ int red[4];
+  const int64_t cell = blockIdx.x;
+  const uint32_t* bits = a.bitmap + cell * a.words;
+  int n = 0;
+  for (int x = threadIdx.x; x < a.words; x += 256) n += __builtin_popcount(bits[x]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) a.count[cell] = red[0] + red[1] + red[2] + red[3];
 }
 
 __global__ __launch_bounds__(256) void ks_bits_extract_kernel(SchedArgs a) {
@@ -990,20 +1006,23 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   const int64_t rows = (int64_t)a.n_q * a.h_kv;
   const unsigned row_blocks = (unsigned)((rows + 255) / 256);
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
-  hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(ks_count_kernel, dim3(row_blocks), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(ks_scan_a_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(ks_scan_b_kernel, dim3(1), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
-  if (s.bitmap) {
+  if (s.bitmap) {  // ordered: bitmap -> counts -> offsets -> token lists in order
     const int64_t nw = pl.n_cells * s.words;
     hipLaunchKernelGGL(ks_bits_zero_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 8192)), dim3(256), 0,
                        st, s);
     hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
-    hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(ks_bits_count_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
   } else {
-    hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(ks_count_kernel, dim3(row_blocks), dim3(256), 0, st, s);
   }
+  hipLaunchKernelGGL(ks_scan_a_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scan_b_kernel, dim3(1), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
+  if (s.bitmap)
+    hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
+  else
+    hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
   hipLaunchKernelGGL(ks_items_kernel, dim3(cell_blocks), dim3(256), 0, st, s);
   return hipGetLastError();
 }

@@ -40,6 +40,7 @@ struct KbArgs {
   const int32_t* item_off;
   const int32_t* entries;
   const i32x4* items;
+  int32_t* queue;           // dK/dV pass: next item to take (zeroed by the schedule)
   float* part_dq;           // dQ pass: [window * h_kv * top_k + 2 trash, G, D]
   float* part_dkv;          // dK/dV pass: [max_items, 2, 128, D]
   int32_t n_q, q_start, n_kv, h_q, h_kv, group, g_shift, top_k, n_blocks, window, w;
@@ -355,32 +356,37 @@ struct KbkvTileRegs {
   int pos;
 };
 
+// Every thread issues the same loads whatever its index (the last units and
+// the per-row scalars are duplicated across threads and only some threads
+// store them), so no load sits under a divergent branch: the compiler then
+// never has to drain the loads of the passes in flight to resolve one.
+// Pass `ps` of an item with `n_pass` passes; passes past the end re-read the
+// last one's rows but flag every row invalid (pos -1), so they add nothing.
 template <int D>
-__device__ __forceinline__ void kbkv_tile_load(KbkvTileRegs<D>& g, const KbArgs& a, const KpItem& m, int row0,
-                                               const int* ent_lds) {
+__device__ __forceinline__ void kbkv_tile_load(KbkvTileRegs<D>& g, const KbArgs& a, const KpItem& m, int ps,
+                                               int n_pass, const int* ent_lds) {
   constexpr int DC = D / 8;
   const int tid = threadIdx.x;
   const int G = a.group, n_tok = m.e_end - m.e_begin, rows = n_tok * G;
-  if (tid < 16 * DC) {
-    const int dc = tid % DC, rp = tid / DC;
-    const int ra = row0 + 2 * rp, rb = ra + 1;
-    const int ea = ent_lds[min(ra >> a.g_shift, n_tok - 1)], eb = ent_lds[min(rb >> a.g_shift, n_tok - 1)];
-    const size_t xa = ((size_t)(ea >> 4) * a.h_q + m.r * G + (ra & (G - 1))) * D + dc * 8;
-    const size_t xb = ((size_t)(eb >> 4) * a.h_q + m.r * G + (rb & (G - 1))) * D + dc * 8;
-    g.q0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xa);
-    g.q1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xb);
-    g.d0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xa);
-    g.d1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xb);
-  }
-  if (tid < 32) {
-    const int rr = row0 + tid;
-    const bool ok = rr < rows;
-    const int e = ent_lds[min(rr >> a.g_shift, n_tok - 1)];
-    const size_t x = (size_t)(e >> 4) * a.h_q + m.r * G + (rr & (G - 1));
-    g.lse2 = ok ? a.lse[x] * kLog2e : 0.0f;
-    g.dsum = ok ? a.dsum[x] : 0.0f;
-    g.pos = ok ? a.q_start + (e >> 4) : -1;
-  }
+  const int row0 = min(ps, n_pass - 1) * 32;
+  const int u = tid % (16 * DC);
+  const int dc = u % DC, rp = u / DC;
+  const int ra = row0 + 2 * rp, rb = ra + 1;
+  const int ea = ent_lds[min(ra >> a.g_shift, n_tok - 1)], eb = ent_lds[min(rb >> a.g_shift, n_tok - 1)];
+  const size_t xa = ((size_t)(ea >> 4) * a.h_q + m.r * G + (ra & (G - 1))) * D + dc * 8;
+  const size_t xb = ((size_t)(eb >> 4) * a.h_q + m.r * G + (rb & (G - 1))) * D + dc * 8;
+  g.q0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xa);
+  g.q1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + xb);
+  g.d0 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xa);
+  g.d1 = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.d_o) + xb);
+  const int rr = row0 + (tid & 31);
+  const bool ok = ps * 32 + (tid & 31) < rows;
+  const int e = ent_lds[min(rr >> a.g_shift, n_tok - 1)];
+  const size_t x = (size_t)(e >> 4) * a.h_q + m.r * G + (rr & (G - 1));
+  const float l = a.lse[x], ds = a.dsum[x];
+  g.lse2 = ok ? l * kLog2e : 0.0f;
+  g.dsum = ok ? ds : 0.0f;
+  g.pos = ok ? a.q_start + (e >> 4) : -1;
 }
 
 template <int D>
@@ -414,8 +420,9 @@ __device__ __forceinline__ void kbkv_tile_store(const KbkvTileRegs<D>& g, char* 
   }
 }
 
-// Items of all (group, block) cells, round-robin over a persistent grid.
-// Each wave owns keys 32*wave .. 32*wave + 31 of the item's block.
+// Items of all (group, block) cells taken from a work queue by a persistent
+// grid (items run in cell order, which puts the most-selected early blocks
+// first).  Each wave owns keys 32*wave .. 32*wave + 31 of the item's block.
 template <int D>
 __global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
   using L = KbkvLds<D>;
@@ -425,7 +432,12 @@ __global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
   const int n_items = scalar_load(a.item_off, (int64_t)a.h_kv * a.n_blocks);
   int* ent_lds = reinterpret_cast<int*>(lds + L::ENT_OFF);
   const float c2 = a.sm_scale * kLog2e;
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+  __shared__ int next_item;
+  for (;;) {
+    if (tid == 0) next_item = atomicAdd(a.queue, 1);
+    __syncthreads();
+    const int it = next_item;
+    if (it >= n_items) break;
     const i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
     const KpItem m{d[0], d[1], d[2], d[3]};
     const int n_tok = m.e_end - m.e_begin;
@@ -451,10 +463,6 @@ __global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
       for (int e = tid; e < n_tok; e += NT) ent_lds[e] = a.entries[m.e_begin + e];
     }
     __syncthreads();
-    KbkvTileRegs<D> g;
-    kbkv_tile_load<D>(g, a, m, 0, ent_lds);
-    kbkv_tile_store<D>(g, lds + L::T_OFF);
-    __syncthreads();
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -463,30 +471,52 @@ __global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
     }
     const int key_abs = m.b * kBlock + wave * 32 + l32;
     const int n_pass = (rows + 31) / 32;
-    for (int ps = 0; ps < n_pass; ++ps) {
+    // this wave's 32 keys of K and V stay in registers for the whole item
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int koff = (wave * 32 + l32) * L::KS + (ks * 16 + half * 8) * 2;
+      kf[ks] = *reinterpret_cast<const bf16x8*>(lds + L::K_OFF + koff);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(lds + L::V_OFF + koff);
+    }
+    // Row tiles are gathered three passes ahead through a ring of register
+    // sets (x: the next pass's tile, y: the one after, z: free) and stored to
+    // the LDS buffer the pass after next reads.
+    KbkvTileRegs<D> ga, gb, gc;
+    // (loads are unconditional: past the last pass they re-read it, so the
+    // number of loads in flight never depends on the data)
+    kbkv_tile_load<D>(ga, a, m, 0, n_pass, ent_lds);
+    kbkv_tile_load<D>(gb, a, m, 1, n_pass, ent_lds);
+    kbkv_tile_load<D>(gc, a, m, 2, n_pass, ent_lds);
+    kbkv_tile_store<D>(ga, lds + L::T_OFF);
+    __syncthreads();
+    auto pass = [&](int ps, KbkvTileRegs<D>& gx, KbkvTileRegs<D>& gz) {
       const char* tile = lds + L::T_OFF + (ps & 1) * L::TILE;
-      const bool more = ps + 1 < n_pass;
-      if (more) kbkv_tile_load<D>(g, a, m, (ps + 1) * 32, ent_lds);
+      kbkv_tile_load<D>(gz, a, m, ps + 3, n_pass, ent_lds);
       // S = Q.K^T and dP = dO.V^T for the tile's 32 rows x this wave's 32 keys
-      f32x16 s = {}, dp = {};
+      f32x16 sa = {}, dpa = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const int roff = l32 * L::KS + (ks * 16 + half * 8) * 2;
-        const int koff = (wave * 32 + l32) * L::KS + (ks * 16 + half * 8) * 2;
-        mma32(s, *reinterpret_cast<const bf16x8*>(tile + L::Q_R + roff),
-              *reinterpret_cast<const bf16x8*>(lds + L::K_OFF + koff));
-        mma32(dp, *reinterpret_cast<const bf16x8*>(tile + L::D_R + roff),
-              *reinterpret_cast<const bf16x8*>(lds + L::V_OFF + koff));
+        mma32(sa, *reinterpret_cast<const bf16x8*>(tile + L::Q_R + roff), kf[ks]);
+        mma32(dpa, *reinterpret_cast<const bf16x8*>(tile + L::D_R + roff), vf[ks]);
       }
+      // per-row lse, D and position of this lane's 16 rows (4 runs of 4)
       const float* sc = reinterpret_cast<const float*>(tile + L::SC);
-      const int* pos = reinterpret_cast<const int*>(sc + 64);
       float pv[16], dsv[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * half + (v & 3);
-        const float pr = key_abs > pos[row] ? 0.0f : fast_exp2(fmaf(s[v], c2, -sc[row]));
-        pv[v] = pr;
-        dsv[v] = pr * (dp[v] - sc[32 + row]);
+      for (int c = 0; c < 4; ++c) {
+        const int r0 = 8 * c + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sc + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sc + 32 + r0);
+        const i32x4 p4 = *reinterpret_cast<const i32x4*>(sc + 64 + r0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = 4 * c + q;
+          const float pr = fast_exp2(key_abs > p4[q] ? -__builtin_inff() : fmaf(sa[v], c2, -l4[q]));
+          pv[v] = pr;
+          dsv[v] = pr * (dpa[v] - d4[q]);
+        }
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -502,8 +532,17 @@ __global__ __launch_bounds__(kKbkvThreads) void kbkv_kernel(KbArgs a) {
           mma32(dk[dt], vt_frag<bf16_t>(tile + L::Q_T, L::TS, dd, 16 * h2 + 4 * half, 16 * h2 + 8 + 4 * half), dsf);
         }
       }
-      if (more) kbkv_tile_store<D>(g, lds + L::T_OFF + ((ps + 1) & 1) * L::TILE);
+      kbkv_tile_store<D>(gx, lds + L::T_OFF + ((ps + 1) & 1) * L::TILE);
       __syncthreads();
+    };
+    // ring rotation: pass ps stores the set holding pass ps + 1 and refills
+    // the free set with pass ps + 3.  The body always runs three passes (up
+    // to two of them past the end, adding zeros) so no branch splits the
+    // loads in flight.
+    for (int ps = 0; ps < n_pass; ps += 3) {
+      pass(ps, gb, ga);
+      pass(ps + 1, gc, gb);
+      pass(ps + 2, ga, gc);
     }
     // dK = scale * (dS^T.Q), dV = P^T.dO for key `key_abs`: lane holds d =
     // dt*32 + 8c + 4*half + {0..3}
@@ -664,6 +703,7 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
   k.item_off = skv.item_off;
   k.entries = skv.entries;
   k.items = skv.items;
+  k.queue = skv.fill;
   k.n_blocks = pl.kv.n_blocks;
   k.window = pl.kv.window;
   k.w = 0;
