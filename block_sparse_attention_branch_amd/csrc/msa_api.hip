@@ -130,12 +130,12 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int32_t n_q, int32_t q_start,
                           int32_t n_kv, int32_t max_pages) {
-  if (op < 0 || op > 5) {
-    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..5", op);
+  if (op < 0 || op > 6) {
+    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..6", op);
     return 0;
   }
-  if (check_shape(shape, op == 0 || op == 4, (op >= 1 && op <= 3) || op == 5) != MSA_OK) return 0;
-  if (check_cache_dtype(*shape, op != 3 && op != 5) != MSA_OK) return 0;
+  if (check_shape(shape, op == 0 || op == 4 || op == 6, (op >= 1 && op <= 3) || op >= 5) != MSA_OK) return 0;
+  if (check_cache_dtype(*shape, op != 3 && op < 5) != MSA_OK) return 0;
   if (batch < 0 || n_q < 0 || q_start < 0 || n_kv < 0 || max_pages < 0) {
     fail(MSA_ERR_INVALID_ARG, "negative size");
     return 0;
@@ -154,8 +154,9 @@ size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int
     case 2:
       return msa::decode_plan(batch, s.h_q, s.h_kv, s.d_h, s.top_k).total;
     case 5:
+    case 6:
       if (n_q == 0) return 0;
-      return msa::backward_plan(n_q, q_start, n_kv, s.h_q, s.h_kv, s.d_h, s.top_k).total;
+      return msa::backward_plan(n_q, q_start, n_kv, s.h_q, s.h_kv, s.d_h, s.top_k, s.d_idx, op == 6).total;
     default:
       return 0;
   }
@@ -296,9 +297,9 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
 
 msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
                                        const msa_kv* kv, const int32_t* block_idx, const void* o, const float* lse,
-                                       const void* d_o, void* dq, void* dk, void* dv, void* workspace,
-                                       size_t ws_bytes, void* hip_stream) {
-  msa_status st = check_shape(shape, false, true);
+                                       const void* d_o, void* dq, void* dk, void* dv, const msa_kl* kl,
+                                       void* workspace, size_t ws_bytes, void* hip_stream) {
+  msa_status st = check_shape(shape, kl != nullptr, true);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
   if ((st = check_cache_dtype(s, false)) != MSA_OK) return st;
@@ -317,8 +318,16 @@ msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int3
   if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o) || !aligned16(d_o) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(MSA_ERR_INVALID_ARG, "q/k/v/o/d_o/dq/dk/dv must be 16-byte aligned");
+  if (kl) {
+    if ((kv->n_kv > 0 && !kl->dk_idx) || (n_q > 0 && (!kl->q_idx || !kl->k_idx || !kl->dq_idx)))
+      return fail(MSA_ERR_INVALID_ARG, "kl: q_idx/k_idx/dq_idx/dk_idx is NULL");
+    if (!aligned16(kl->q_idx) || !aligned16(kl->k_idx) || !aligned16(kl->dq_idx) || !aligned16(kl->dk_idx))
+      return fail(MSA_ERR_INVALID_ARG, "kl: q_idx/k_idx/dq_idx/dk_idx must be 16-byte aligned");
+    if (!(kl->kl_scale == kl->kl_scale)) return fail(MSA_ERR_INVALID_ARG, "kl: kl_scale is NaN");
+  }
   if (kv->n_kv == 0) return ok();
-  const msa::BackwardPlan pl = msa::backward_plan(n_q, q_start, kv->n_kv, s.h_q, s.h_kv, s.d_h, s.top_k);
+  const msa::BackwardPlan pl =
+      msa::backward_plan(n_q, q_start, kv->n_kv, s.h_q, s.h_kv, s.d_h, s.top_k, s.d_idx, kl != nullptr);
   if (n_q > 0 && (st = check_ws(workspace, ws_bytes, pl.total)) != MSA_OK) return st;
   msa::BackwardArgs b{};
   msa::AttnArgs& a = b.attn;
@@ -343,6 +352,17 @@ msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int3
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
+  if (kl) {
+    b.kl = 1;
+    b.d_idx = s.d_idx;
+    b.q_idx = kl->q_idx;
+    b.k_idx = kl->k_idx;
+    b.idx_scale = s.idx_scale > 0.f ? s.idx_scale : 1.0f / sqrtf((float)s.d_idx);
+    b.kl_scale = kl->kl_scale;
+    b.kl_out = kl->kl_out;
+    b.dq_idx = kl->dq_idx;
+    b.dk_idx = kl->dk_idx;
+  }
   return hip_status(msa::launch_sparse_prefill_backward(s.d_h, b, pl, static_cast<hipStream_t>(hip_stream)),
                     "msa_sparse_prefill_backward");
 }

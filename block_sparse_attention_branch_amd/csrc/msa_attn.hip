@@ -179,7 +179,7 @@ __global__ void ks_items_kernel(SchedArgs a) {
 // the cell's bitmap; one workgroup per cell then writes the set bits out in
 // order at the cell's offset.
 __global__ void ks_bits_zero_kernel(SchedArgs a) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.fill[0] = 0;  // work-queue head of the consumer
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.fill[threadIdx.x] = 0;  // work-queue heads of the consumers
   const int64_t n = a.n_cells * a.words;
   for (int64_t x = blockIdx.x * 256ll + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) a.bitmap[x] = 0u;
 }

@@ -130,14 +130,24 @@ struct BackwardArgs {
   void* dq;                 // [n_q, h_q, d]
   void* dk;                 // [n_kv, h_kv, d]
   void* dv;
+  // KL-alignment term: kl != 0 asks for it
+  int32_t kl, d_idx;
+  const void* q_idx;        // [n_q, h_kv, d_idx]
+  const void* k_idx;        // [n_kv, d_idx]
+  float idx_scale, kl_scale;
+  float* kl_out;            // [n_q, h_kv], nullable
+  void* dq_idx;             // [n_q, h_kv, d_idx]
+  void* dk_idx;             // [n_kv, d_idx]
 };
 struct BackwardPlan {
   PrefillPlan q;            // dQ pass schedule (windows), at off_q
   PrefillPlan kv;           // dK/dV pass schedule (one window), at off_kv
-  size_t off_q, off_kv, off_dsum, off_part_dq, off_part_dkv, total;
+  size_t off_q, off_kv, off_dsum, off_part_dq, off_part_dkv;
+  size_t off_pmain, off_part_kl, off_lse_idx, off_part_dki;  // with the KL term only
+  size_t total;
 };
 BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q, int32_t h_kv, int32_t d_h,
-                           int32_t top_k);
+                           int32_t top_k, int32_t d_idx, bool with_kl);
 hipError_t launch_sparse_prefill_backward(int d_h, const BackwardArgs& a, const BackwardPlan& pl, hipStream_t st);
 bool backward_supported(int dtype, int d_h);
 bool dense_supported(int dtype, int d_h);

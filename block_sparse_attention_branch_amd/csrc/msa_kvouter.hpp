@@ -323,7 +323,7 @@ struct SchedArgs {
   int32_t* scan;      // [4 * n_scan_tiles]
   int32_t n_scan_tiles;
   uint32_t* bitmap;   // ordered mode: [n_cells, words] token bits of each cell; NULL otherwise
-                      // (fill[0] is then zeroed as a work-queue head for the consumer)
+                      // (fill[0] and fill[1] are then zeroed as work-queue heads for the consumers)
   int32_t words;      // 32-bit words per cell (window / 32, rounded up)
 };
 

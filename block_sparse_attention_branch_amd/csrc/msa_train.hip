@@ -46,6 +46,17 @@ struct KbArgs {
   int32_t n_q, q_start, n_kv, h_q, h_kv, group, g_shift, top_k, n_blocks, window, w;
   size_t trash_slot;
   float sm_scale;
+  // KL-alignment term (pmain == NULL: not requested)
+  float* pmain;             // [n_q, h_kv, top_k, 128] group-mean main-branch probabilities per selected key
+  const void* q_idx;        // [n_q, h_kv, d_idx]
+  const void* k_idx;        // [n_kv, d_idx]
+  float idx_scale, kl_scale;
+  float* part_kl;           // index pass: [window * h_kv * top_k + 1 trash, 4 + 2 d_idx]
+  float* lse_idx;           // [n_q, h_kv]
+  float* kl;                // [n_q, h_kv], nullable
+  void* dq_idx;             // [n_q, h_kv, d_idx]
+  void* dk_idx;             // [n_kv, d_idx]
+  float* part_dki;          // dk_idx pass: [max_items, 128, d_idx]
 };
 
 // ------------------------------------------------------------- D = rowsum
@@ -161,6 +172,7 @@ struct KbqPass {
   bf16x8 df[D / 16];
   float lse2, dsum;
   int pos, slot, head;
+  int64_t slot_g;  // (token, group, slot) over the whole call; rows past the item: a trash slot
   bool ok;
 };
 
@@ -177,6 +189,7 @@ __device__ __forceinline__ void kbq_load_pass(KbqPass<D>& ps, const KbArgs& a, c
   const int i = ent >> 4, j = ent & 15;
   ps.head = rho & (G - 1);
   ps.slot = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
+  ps.slot_g = ps.ok ? ((int64_t)i * a.h_kv + m.r) * a.top_k + j : (int64_t)a.n_q * a.h_kv * a.top_k;
   ps.pos = ps.ok ? a.q_start + i : -1;
   const size_t row = (size_t)i * a.h_q + m.r * G + ps.head;
   const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + row * D + half * 8;
@@ -192,7 +205,7 @@ __device__ __forceinline__ void kbq_load_pass(KbqPass<D>& ps, const KbArgs& a, c
 
 // dQ^T of the wave's 32 rows against the staged block, one 32-key tile at a
 // time to bound the live accumulators.
-template <int D>
+template <int D, bool KL>
 __device__ __forceinline__ void kbq_math(const KbArgs& a, int b, const KbqPass<D>& ps, const char* lds,
                                          f32x16 (&dq)[D / 32]) {
   using L = KbqLds<D>;
@@ -209,12 +222,29 @@ __device__ __forceinline__ void kbq_math(const KbArgs& a, int b, const KbqPass<D
       mma32(s, *reinterpret_cast<const bf16x8*>(lds + L::K_OFF + off), ps.qf[ks]);
       mma32(dp, *reinterpret_cast<const bf16x8*>(lds + L::V_OFF + off), ps.df[ks]);
     }
-    float dsv[16];
+    float dsv[16], pm[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      const float pv = key > ps.pos ? 0.0f : fast_exp2(fmaf(s[v], c2, -ps.lse2));
+      const float pv = fast_exp2(key > ps.pos ? -__builtin_inff() : fmaf(s[v], c2, -ps.lse2));
       dsv[v] = pv * (dp[v] - ps.dsum);
+      pm[v] = pv;
+    }
+    if constexpr (KL) {
+      // group mean of P over the token's heads (lanes token * G + head of
+      // this half), written by all of them (same values, same addresses)
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1)
+        if (off < a.group) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) pm[v] += __shfl_xor(pm[v], off, 64);
+        }
+      const float inv_g = 1.0f / (float)a.group;
+      float* dst = a.pmain + ((size_t)ps.slot_g * kBlock + kt * 32 + 4 * half);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4*>(dst + 8 * c) =
+            f32x4{pm[4 * c] * inv_g, pm[4 * c + 1] * inv_g, pm[4 * c + 2] * inv_g, pm[4 * c + 3] * inv_g};
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -249,7 +279,7 @@ __device__ __forceinline__ void kbq_store(const KbArgs& a, const KbqPass<D>& ps,
 // Persistent over this XCD's items of window w (the forward's item order):
 // workgroup g runs on XCD g % 8 and takes items sub, sub + nsub, ...  The next
 // item's K/V are loaded into registers while the current item computes.
-template <int D>
+template <int D, bool KL>
 __global__ __launch_bounds__(kKbqThreads) void kbq_kernel(KbArgs a) {
   using L = KbqLds<D>;
   constexpr int NT = kKbqThreads;
@@ -288,7 +318,7 @@ __global__ __launch_bounds__(kKbqThreads) void kbq_kernel(KbArgs a) {
       kbq_load_pass<D>(ps, a, cur, p0 + wave * 32 + l32, ent_lds);
       if (__any(ps.ok)) {
         f32x16 dq[D / 32];
-        kbq_math<D>(a, cur.b, ps, lds, dq);
+        kbq_math<D, KL>(a, cur.b, ps, lds, dq);
         kbq_store<D>(a, ps, dq);
       }
     }
@@ -607,11 +637,361 @@ __global__ __launch_bounds__(256) void kbkv_reduce_kernel(KbArgs a) {
   }
 }
 
+// ------------------------------------------------------ KL-alignment term
+// For each query and group over the visible keys T of its selected blocks:
+//   target p_main(j)  (group mean of the main-branch softmax, written in fp32
+//                      by the dQ pass), prediction p_idx(j) = softmax_T(S_idx),
+//   S_idx(j) = q_idx . k_idx_j * idx_scale,
+//   KL = sum_j p_main (ln p_main - S_idx + lse_idx),
+//   dS_idx(j) = kl_scale (p_idx(j) - p_main(j)),
+//   dq_idx = idx_scale sum_j dS_idx(j) k_idx_j,  dk_idx_j = idx_scale sum dS_idx q_idx.
+// Every per-key quantity is formed in fp32 before it is summed (p_idx and
+// p_main nearly coincide when the branches agree, so the gradient and the
+// KL are small differences and must not be taken between large sums).
+// Index passes (KV-outer over the dQ pass's windows, one wave per item, 32
+// tokens per MFMA tile): phase 0 writes each (token, slot)'s block max and
+// sum of exp(S_idx - max), merged into lse_idx; phase 1 writes the block's
+// KL terms and U = sum_j (p_idx - p_main) k_idx_j, merged into KL and dq_idx.
+// A third pass (ordered single-window schedule, keys on lanes) accumulates
+// dk_idx per block; a reduce sums a block's items over all groups (k_idx is
+// shared by the groups).
+constexpr int kKlWaves = 4;
+
+template <int DI>
+struct KlLds {
+  static constexpr int TS = 128 * 2 + 8;  // bytes per d row of K_idx^T
+  static constexpr int WAVE = DI * TS;
+};
+
+template <int DI>
+__device__ __forceinline__ float* kl_part(const KbArgs& a, size_t slot) {
+  return a.part_kl + slot * (8 + DI);
+}
+
+template <int DI, int PHASE>
+__global__ __launch_bounds__(kKlWaves * 64) void kl_index_kernel(KbArgs a) {
+  using L = KlLds<DI>;
+  __shared__ __attribute__((aligned(16))) char lds[PHASE == 1 ? kKlWaves : 1][PHASE == 1 ? L::WAVE : 16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  char* kt_lds = lds[PHASE == 1 ? wave : 0];
+  const int64_t n_l = (int64_t)a.h_kv * a.n_blocks;
+  const int item_begin = scalar_load(a.item_off, (int64_t)a.w * n_l);
+  const int item_end = scalar_load(a.item_off, (int64_t)(a.w + 1) * n_l);
+  const bf16_t* kidx = static_cast<const bf16_t*>(a.k_idx);
+  const bf16_t* qidx = static_cast<const bf16_t*>(a.q_idx);
+  for (int it = item_begin + blockIdx.x * kKlWaves + wave; it < item_end; it += gridDim.x * kKlWaves) {
+    const i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
+    const int b = d[0], r = d[1], e0 = d[2], n_tok = d[3] - d[2];
+    const int last = min(kBlock, a.n_kv - b * kBlock) - 1;
+    if constexpr (PHASE == 1) {
+      // K_idx^T of block b into this wave's LDS: pairs of keys interleaved
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < DI / 8; ++i) {
+        const int u = lane + 64 * i;
+        const int dc = u % (DI / 8), kp = u / (DI / 8);
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(kidx + ((size_t)b * kBlock + min(2 * kp, last)) * DI + dc * 8);
+        const u32x4 y0 =
+            *reinterpret_cast<const u32x4*>(kidx + ((size_t)b * kBlock + min(2 * kp + 1, last)) * DI + dc * 8);
+        const u32x4 x = 2 * kp > last ? z : x0;
+        const u32x4 y = 2 * kp + 1 > last ? z : y0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          *reinterpret_cast<uint32_t*>(kt_lds + (8 * dc + 2 * t) * L::TS + kp * 4) = (x[t] & 0xffffu) | (y[t] << 16);
+          *reinterpret_cast<uint32_t*>(kt_lds + (8 * dc + 2 * t + 1) * L::TS + kp * 4) =
+              (x[t] >> 16) | (y[t] & 0xffff0000u);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    for (int t0 = 0; t0 < n_tok; t0 += 32) {
+      const bool ok = t0 + l32 < n_tok;
+      const int ent = a.entries[e0 + min(t0 + l32, n_tok - 1)];
+      const int i = ent >> 4, j = ent & 15;
+      const int pos = ok ? a.q_start + i : -1;
+      const size_t slot = ok ? ((size_t)(i - a.w * a.window) * a.h_kv + r) * a.top_k + j : a.trash_slot;
+      bf16x8 qf[DI / 16];
+#pragma unroll
+      for (int ks = 0; ks < DI / 16; ++ks)
+        qf[ks] = load_frag<bf16_t>(qidx + ((size_t)i * a.h_kv + r) * DI + ks * 16 + half * 8);
+      // S_idx^T = K_idx . q_idx^T (keys on the MFMA rows, tokens on lanes);
+      // this lane holds keys kt*32 + 8c + 4*half + q of its token
+      f32x16 sc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sc[kt] = f32x16{};
+        const bf16_t* krow = kidx + ((size_t)b * kBlock + min(kt * 32 + l32, last)) * DI + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < DI / 16; ++ks) mma32(sc[kt], load_frag<bf16_t>(krow + ks * 16), qf[ks]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          sc[kt][v] = key > pos ? -__builtin_inff() : sc[kt][v] * a.idx_scale;
+        }
+      }
+      float* dst = kl_part<DI>(a, slot);
+      if constexpr (PHASE == 0) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mc = mx == -__builtin_inff() ? 0.0f : mx;
+        float sl = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sl += fast_exp2((sc[kt][v] - mc) * kLog2e);
+        sl += __shfl_xor(sl, 32, 64);
+        *reinterpret_cast<f32x2*>(dst) = f32x2{mx, sl};
+      } else {
+        const float lse = a.lse_idx[(size_t)i * a.h_kv + r];
+        const float* pmrow = a.pmain + (((size_t)i * a.h_kv + r) * a.top_k + j) * kBlock + 4 * half;
+        float klt = 0.f;
+        bf16x8 df[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float dv[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(pmrow + kt * 32 + 8 * c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int v = 4 * c + q;
+              const float lp = sc[kt][v] - lse;  // ln p_idx (-inf where masked)
+              const float pi = fast_exp2(lp * kLog2e);
+              const float pm = ok ? p4[q] : 0.0f;
+              dv[v] = pi - pm;
+              klt += pm > 0.0f ? pm * (__logf(pm) - lp) : 0.0f;
+            }
+          }
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int o = 8 * h2;
+            df[kt][h2] = to_frag<bf16_t>(dv[o], dv[o + 1], dv[o + 2], dv[o + 3], dv[o + 4], dv[o + 5], dv[o + 6],
+                                         dv[o + 7]);
+          }
+        }
+        klt += __shfl_xor(klt, 32, 64);
+        // U^T = K_idx^T . (p_idx - p_main)^T (d_idx on the MFMA rows)
+        f32x16 u[DI / 32];
+#pragma unroll
+        for (int dt = 0; dt < DI / 32; ++dt) u[dt] = f32x16{};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int base = kt * 32 + h2 * 16;
+#pragma unroll
+            for (int dt = 0; dt < DI / 32; ++dt)
+              mma32(u[dt], vt_frag<bf16_t>(kt_lds, L::TS, dt * 32 + l32, base + 4 * half, base + 8 + 4 * half),
+                    df[kt][h2]);
+          }
+        dst[0] = klt;
+#pragma unroll
+        for (int dt = 0; dt < DI / 32; ++dt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int d0 = dt * 32 + 8 * c + 4 * half;
+            *reinterpret_cast<f32x4*>(dst + 8 + d0) =
+                f32x4{u[dt][4 * c], u[dt][4 * c + 1], u[dt][4 * c + 2], u[dt][4 * c + 3]};
+          }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // this wave's LDS is rewritten for its next item
+  }
+}
+
+// Row merges of window w.  Phase 0: lse_idx of every (token, group).
+// Phase 1: KL and dq_idx.
+template <int DI, int PHASE>
+__global__ __launch_bounds__(256) void kl_merge_kernel(KbArgs a) {
+  constexpr int DC = PHASE == 0 ? 1 : DI / 8;
+  const int64_t t = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t rl = t / DC;  // il * h_kv + r
+  const int c = (int)(t % DC);
+  const int il = (int)(rl / a.h_kv), r = (int)(rl % a.h_kv);
+  const int i = a.w * a.window + il;
+  if (il >= a.window || i >= a.n_q) return;
+  const int diag = (a.q_start + i) >> 7;
+  const uint32_t used = used_slots(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, diag);
+  const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
+  if constexpr (PHASE == 0) {
+    float mm = -__builtin_inff();
+    for (int j = 0; j < a.top_k; ++j)
+      if ((used >> j) & 1u) mm = fmaxf(mm, kl_part<DI>(a, slot0 + j)[0]);
+    float ll = 0.f;
+    for (int j = 0; j < a.top_k; ++j)
+      if ((used >> j) & 1u) {
+        const float* p = kl_part<DI>(a, slot0 + j);
+        ll += p[1] * __expf(p[0] - mm);
+      }
+    a.lse_idx[(size_t)i * a.h_kv + r] = used ? mm + __logf(ll) : 0.0f;
+  } else {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float klv = 0.f;
+    for (int j = 0; j < a.top_k; ++j)
+      if ((used >> j) & 1u) {
+        const float* p = kl_part<DI>(a, slot0 + j);
+        klv += p[0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += p[8 + c * 8 + e];
+      }
+    const float g = a.idx_scale * a.kl_scale;
+    bf16_t* dst = static_cast<bf16_t*>(a.dq_idx) + ((size_t)i * a.h_kv + r) * DI + c * 8;
+    *reinterpret_cast<bf16x8*>(dst) =
+        bf16x8{from_f32<bf16_t>(g * acc[0]), from_f32<bf16_t>(g * acc[1]), from_f32<bf16_t>(g * acc[2]),
+               from_f32<bf16_t>(g * acc[3]), from_f32<bf16_t>(g * acc[4]), from_f32<bf16_t>(g * acc[5]),
+               from_f32<bf16_t>(g * acc[6]), from_f32<bf16_t>(g * acc[7])};
+    if (c == 0 && a.kl) a.kl[(size_t)i * a.h_kv + r] = klv;
+  }
+}
+
+// dk_idx pass: items of the ordered single-window schedule from a work queue;
+// wave w owns keys 32w .. 32w + 31 of the block, tokens go in tiles of 32.
+template <int DI>
+struct KlDkLds {
+  static constexpr int QS = DI * 2 + 16;   // bytes per token row of q_idx
+  static constexpr int TS = 32 * 2 + 8;    // bytes per d row of a 32-token q_idx^T tile
+  static constexpr int Q_R = 0;
+  static constexpr int Q_T = 32 * QS;
+  static constexpr int SC = Q_T + DI * TS;     // lse_idx, pos, pmain row (int64 as 2 ints) per token
+  static constexpr int BYTES = SC + 32 * 16;
+  static constexpr int ENT_OFF = BYTES;
+  static constexpr int TOTAL = ENT_OFF + 2048 * 4;
+};
+
+template <int DI>
+__global__ __launch_bounds__(256) void kl_dk_kernel(KbArgs a) {
+  using L = KlDkLds<DI>;
+  __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
+  __shared__ int next_item;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int n_items = scalar_load(a.item_off, (int64_t)a.h_kv * a.n_blocks);
+  int* ent_lds = reinterpret_cast<int*>(lds + L::ENT_OFF);
+  const bf16_t* kidx = static_cast<const bf16_t*>(a.k_idx);
+  const bf16_t* qidx = static_cast<const bf16_t*>(a.q_idx);
+  for (;;) {
+    if (tid == 0) next_item = atomicAdd(a.queue + 1, 1);
+    __syncthreads();
+    const int it = next_item;
+    if (it >= n_items) break;
+    const i32x4 d = scalar_load(a.items, __builtin_amdgcn_readfirstlane(it));
+    const int b = d[0], r = d[1], e0 = d[2], n_tok = d[3] - d[2];
+    for (int e = tid; e < n_tok; e += 256) ent_lds[e] = a.entries[e0 + e] >> 4;
+    const int last = min(kBlock, a.n_kv - b * kBlock) - 1;
+    const int key_l = wave * 32 + l32;
+    const int key_abs = b * kBlock + key_l;
+    bf16x8 kf[DI / 16];
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks)
+      kf[ks] = load_frag<bf16_t>(kidx + ((size_t)b * kBlock + min(key_l, last)) * DI + ks * 16 + half * 8);
+    f32x16 dk[DI / 32];
+#pragma unroll
+    for (int dt = 0; dt < DI / 32; ++dt) dk[dt] = f32x16{};
+    __syncthreads();
+    for (int t0 = 0; t0 < n_tok; t0 += 32) {
+      // stage the tile: q_idx rows and q_idx^T, and per token lse_idx, pos, pmain row
+      {
+        constexpr int DC = DI / 8;
+        for (int u = tid; u < 16 * DC; u += 256) {
+          const int dc = u % DC, rp = u / DC;
+          const int ia = ent_lds[min(t0 + 2 * rp, n_tok - 1)], ib = ent_lds[min(t0 + 2 * rp + 1, n_tok - 1)];
+          const u32x4 x = *reinterpret_cast<const u32x4*>(qidx + ((size_t)ia * a.h_kv + r) * DI + dc * 8);
+          const u32x4 y = *reinterpret_cast<const u32x4*>(qidx + ((size_t)ib * a.h_kv + r) * DI + dc * 8);
+          *reinterpret_cast<u32x4*>(lds + L::Q_R + (2 * rp) * L::QS + dc * 16) = x;
+          *reinterpret_cast<u32x4*>(lds + L::Q_R + (2 * rp + 1) * L::QS + dc * 16) = y;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            *reinterpret_cast<uint32_t*>(lds + L::Q_T + (8 * dc + 2 * t) * L::TS + rp * 4) = (x[t] & 0xffffu) | (y[t] << 16);
+            *reinterpret_cast<uint32_t*>(lds + L::Q_T + (8 * dc + 2 * t + 1) * L::TS + rp * 4) =
+                (x[t] >> 16) | (y[t] & 0xffff0000u);
+          }
+        }
+        if (tid < 32) {
+          const bool ok = t0 + tid < n_tok;
+          const int i = ent_lds[min(t0 + tid, n_tok - 1)];
+          const int32_t* br = a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k;
+          int j = 0;
+          for (int s = 0; s < a.top_k; ++s) j = br[s] == b ? s : j;
+          int* sc = reinterpret_cast<int*>(lds + L::SC) + 4 * tid;
+          reinterpret_cast<float*>(sc)[0] = a.lse_idx[(size_t)i * a.h_kv + r];
+          sc[1] = ok ? a.q_start + i : -1;
+          const int64_t row = ((int64_t)i * a.h_kv + r) * a.top_k + j;
+          sc[2] = (int)(row & 0xffffffff);
+          sc[3] = (int)(row >> 32);
+        }
+      }
+      __syncthreads();
+      // S_idx = q_idx . K_idx^T (tokens on the MFMA rows, this wave's keys on lanes)
+      f32x16 s = {};
+#pragma unroll
+      for (int ks = 0; ks < DI / 16; ++ks)
+        mma32(s, *reinterpret_cast<const bf16x8*>(lds + L::Q_R + l32 * L::QS + (ks * 16 + half * 8) * 2), kf[ks]);
+      float dsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+        const int* sc = reinterpret_cast<const int*>(lds + L::SC) + 4 * row;
+        const float lse = reinterpret_cast<const float*>(sc)[0];
+        const int pos = sc[1];
+        const int64_t prow = (int64_t)(uint32_t)sc[2] | ((int64_t)sc[3] << 32);
+        const bool vis = key_abs <= pos;
+        const float pi = fast_exp2(vis ? (s[v] * a.idx_scale - lse) * kLog2e : -__builtin_inff());
+        const float pm = a.pmain[prow * kBlock + key_l];
+        dsv[v] = vis ? a.kl_scale * (pi - pm) : 0.0f;
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int o = 8 * h2;
+        const bf16x8 f = to_frag<bf16_t>(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5],
+                                         dsv[o + 6], dsv[o + 7]);
+#pragma unroll
+        for (int dt = 0; dt < DI / 32; ++dt)
+          mma32(dk[dt], vt_frag<bf16_t>(lds + L::Q_T, L::TS, dt * 32 + l32, 16 * h2 + 4 * half, 16 * h2 + 8 + 4 * half),
+                f);
+      }
+      __syncthreads();
+    }
+    float* dst = a.part_dki + ((size_t)it * kBlock + key_l) * DI;
+#pragma unroll
+    for (int dt = 0; dt < DI / 32; ++dt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = dt * 32 + 8 * c + 4 * half;
+        *reinterpret_cast<f32x4*>(dst + d0) = f32x4{dk[dt][4 * c] * a.idx_scale, dk[dt][4 * c + 1] * a.idx_scale,
+                                                    dk[dt][4 * c + 2] * a.idx_scale, dk[dt][4 * c + 3] * a.idx_scale};
+      }
+  }
+}
+
+// dk_idx of block b: the sum of the items of every group's cell (b, r).
+template <int DI>
+__global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KbArgs a) {
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < kBlock * DI / 4; e += 256) {
+    const int key = e / (DI / 4), d0 = 4 * (e % (DI / 4));
+    const int key_abs = b * kBlock + key;
+    if (key_abs >= a.n_kv) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (b < a.n_blocks)
+      for (int r = 0; r < a.h_kv; ++r) {
+        const int64_t cell = cell_key(0, r, b, a.n_blocks, a.h_kv);
+        const int ib = a.item_off[cell], ie = a.item_off[cell + 1];
+        for (int it = ib; it < ie; ++it)
+          acc += *reinterpret_cast<const f32x4*>(a.part_dki + ((size_t)it * kBlock + key) * DI + d0);
+      }
+    store4<bf16_t>(static_cast<bf16_t*>(a.dk_idx) + (size_t)key_abs * DI + d0, acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
 // ------------------------------------------------------------------- host
 bool backward_supported(int dtype, int d_h) { return dtype == 0 && (d_h == 64 || d_h == 128); }
 
 BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q, int32_t h_kv, int32_t d_h,
-                           int32_t top_k) {
+                           int32_t top_k, int32_t d_idx, bool with_kl) {
   BackwardPlan p{};
   const int G = h_q / h_kv;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -627,8 +1007,47 @@ BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h
   p.off_dsum = off; off = align(off + (size_t)n_q * h_q * 4);
   p.off_part_dq = off; off = align(off + ((size_t)p.q.window * h_kv * top_k + 2) * G * d_h * 4);
   p.off_part_dkv = off; off = align(off + (size_t)p.kv.max_items * 2 * kBlock * d_h * 4);
+  if (with_kl) {
+    p.off_pmain = off; off = align(off + ((size_t)n_q * h_kv * top_k + 1) * kBlock * 4);
+    p.off_part_kl = off; off = align(off + ((size_t)p.q.window * h_kv * top_k + 1) * (8 + d_idx) * 4);
+    p.off_lse_idx = off; off = align(off + (size_t)n_q * h_kv * 4);
+    p.off_part_dki = off; off = align(off + (size_t)p.kv.max_items * kBlock * d_idx * 4);
+  }
   p.total = off;
   return p;
+}
+
+template <int DI>
+static void launch_kl_index_typed(const KbArgs& k, unsigned grid, int64_t rows, hipStream_t st) {
+  hipLaunchKernelGGL((kl_index_kernel<DI, 0>), dim3(grid), dim3(kKlWaves * 64), 0, st, k);
+  hipLaunchKernelGGL((kl_merge_kernel<DI, 0>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, k);
+  hipLaunchKernelGGL((kl_index_kernel<DI, 1>), dim3(grid), dim3(kKlWaves * 64), 0, st, k);
+  hipLaunchKernelGGL((kl_merge_kernel<DI, 1>), dim3((unsigned)((rows * (DI / 8) + 255) / 256)), dim3(256), 0, st, k);
+}
+
+static void launch_kl_index(int d_idx, const KbArgs& k, unsigned grid, int64_t rows, hipStream_t st) {
+  if (d_idx == 32) launch_kl_index_typed<32>(k, grid, rows, st);
+  else if (d_idx == 64) launch_kl_index_typed<64>(k, grid, rows, st);
+  else launch_kl_index_typed<128>(k, grid, rows, st);
+}
+
+static void launch_kl_dk(int d_idx, const KbArgs& k, unsigned grid, unsigned nb_kv, hipStream_t st) {
+  if (d_idx == 32) {
+    hipLaunchKernelGGL(kl_dk_kernel<32>, dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL(kl_dk_reduce_kernel<32>, dim3(nb_kv), dim3(256), 0, st, k);
+  } else if (d_idx == 64) {
+    hipLaunchKernelGGL(kl_dk_kernel<64>, dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL(kl_dk_reduce_kernel<64>, dim3(nb_kv), dim3(256), 0, st, k);
+  } else {
+    hipLaunchKernelGGL(kl_dk_kernel<128>, dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL(kl_dk_reduce_kernel<128>, dim3(nb_kv), dim3(256), 0, st, k);
+  }
+}
+
+static void launch_kl_dk_reduce(int d_idx, const KbArgs& k, unsigned nb_kv, hipStream_t st) {
+  if (d_idx == 32) hipLaunchKernelGGL(kl_dk_reduce_kernel<32>, dim3(nb_kv), dim3(256), 0, st, k);
+  else if (d_idx == 64) hipLaunchKernelGGL(kl_dk_reduce_kernel<64>, dim3(nb_kv), dim3(256), 0, st, k);
+  else hipLaunchKernelGGL(kl_dk_reduce_kernel<128>, dim3(nb_kv), dim3(256), 0, st, k);
 }
 
 template <int D>
@@ -649,6 +1068,19 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
   k.block_idx = a.block_idx;
   k.part_dq = reinterpret_cast<float*>(ws + pl.off_part_dq);
   k.part_dkv = reinterpret_cast<float*>(ws + pl.off_part_dkv);
+  if (ba.kl) {
+    k.pmain = reinterpret_cast<float*>(ws + pl.off_pmain);
+    k.part_kl = reinterpret_cast<float*>(ws + pl.off_part_kl);
+    k.lse_idx = reinterpret_cast<float*>(ws + pl.off_lse_idx);
+    k.part_dki = reinterpret_cast<float*>(ws + pl.off_part_dki);
+    k.q_idx = ba.q_idx;
+    k.k_idx = ba.k_idx;
+    k.kl = ba.kl_out;
+    k.dq_idx = ba.dq_idx;
+    k.dk_idx = ba.dk_idx;
+    k.idx_scale = ba.idx_scale;
+    k.kl_scale = ba.kl_scale;
+  }
   k.n_q = a.n_q;
   k.q_start = a.q_start;
   k.n_kv = a.n_kv;
@@ -660,9 +1092,12 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
   k.sm_scale = a.sm_scale;
 
   const unsigned nb_kv = (unsigned)((a.n_kv + kBlock - 1) / kBlock);
-  if (a.n_q == 0) {  // no query attends: dK = dV = 0
+  if (a.n_q == 0) {  // no query attends: dK = dV = 0 (and dk_idx = 0)
     k.n_blocks = 0;
-    if (nb_kv > 0) hipLaunchKernelGGL(kbkv_reduce_kernel<D>, dim3(nb_kv, (unsigned)a.h_kv), dim3(256), 0, st, k);
+    if (nb_kv > 0) {
+      hipLaunchKernelGGL(kbkv_reduce_kernel<D>, dim3(nb_kv, (unsigned)a.h_kv), dim3(256), 0, st, k);
+      if (ba.kl) launch_kl_dk_reduce(ba.d_idx, k, nb_kv, st);
+    }
     return hipGetLastError();
   }
   const int64_t rows = (int64_t)a.n_q * a.h_q;
@@ -688,10 +1123,17 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
     k.w = w;
     const int pk = profile_begin(PK_KBQ, st);
-    hipLaunchKernelGGL(kbq_kernel<D>, dim3(grid), dim3(kKbqThreads), 0, st, k);
+    if (k.pmain)
+      hipLaunchKernelGGL((kbq_kernel<D, true>), dim3(grid), dim3(kKbqThreads), 0, st, k);
+    else
+      hipLaunchKernelGGL((kbq_kernel<D, false>), dim3(grid), dim3(kKbqThreads), 0, st, k);
     profile_end(pk, st);
     const int64_t mrows = (int64_t)tok * a.h_q;
     hipLaunchKernelGGL(kbq_merge_kernel<D>, dim3((unsigned)((mrows * (D / 8) + 255) / 256)), dim3(256), 0, st, k);
+    if (ba.kl) {
+      k.trash_slot = (size_t)pl.q.window * a.h_kv * a.top_k;
+      launch_kl_index(ba.d_idx, k, (unsigned)(2 * n_cu), (int64_t)tok * a.h_kv, st);
+    }
   }
 
   // dK/dV: one window over all queries
@@ -712,6 +1154,7 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
   profile_end(pk, st);
   if (nb_kv > 0)
     hipLaunchKernelGGL(kbkv_reduce_kernel<D>, dim3(nb_kv, (unsigned)a.h_kv), dim3(256), 0, st, k);
+  if (ba.kl && nb_kv > 0) launch_kl_dk(ba.d_idx, k, (unsigned)(2 * n_cu), nb_kv, st);
   return hipGetLastError();
 }
 

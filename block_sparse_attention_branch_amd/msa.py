@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_POOL_MAX, MSA_POOL_MEAN = 0, 1
-OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE, OP_PREFILL_BACKWARD = 0, 1, 2, 3, 4, 5
+OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE, OP_PREFILL_BACKWARD, OP_PREFILL_BACKWARD_KL = \
+    0, 1, 2, 3, 4, 5, 6
 BLOCK = 128
 
 
@@ -36,6 +37,11 @@ class Shape(ctypes.Structure):
                 ("force_local", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("idx_scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
                 ("pool", ctypes.c_int32)]
+
+
+class KL(ctypes.Structure):
+    _fields_ = [("q_idx", ctypes.c_void_p), ("k_idx", ctypes.c_void_p), ("kl_scale", ctypes.c_float),
+                ("kl_out", ctypes.c_void_p), ("dq_idx", ctypes.c_void_p), ("dk_idx", ctypes.c_void_p)]
 
 
 class KV(ctypes.Structure):
@@ -66,8 +72,8 @@ def lib() -> ctypes.CDLL:
         L.msa_sparse_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_sparse_decode.argtypes = [P(Shape), i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
-        L.msa_sparse_prefill_backward.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, vp, vp, vp, vp,
-                                                  sz, vp]
+        L.msa_sparse_prefill_backward.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, vp, vp, vp,
+                                                  P(KL), vp, sz, vp]
         for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
                   "msa_sparse_prefill_backward"):
             getattr(L, f).restype = ctypes.c_int
@@ -252,22 +258,37 @@ def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *, sm_sc
 
 
 def sparse_prefill_backward(q, k, v, block_idx, o, lse, d_o, *, q_start=0, sm_scale=0.0, top_k=None,
-                            out=None, workspace=None, stream=None):
+                            out=None, workspace=None, stream=None, q_idx=None, k_idx=None, kl_scale=1.0,
+                            idx_scale=0.0, kl_out=True):
     """msa_sparse_prefill_backward: gradients (dq, dk, dv) of msa_sparse_prefill
     for one contiguous sequence, given the forward's o and lse and d_o.
     q, o, d_o [n_q, h_q, d_h]; k, v [n_kv, h_kv, d_h]; block_idx int32
-    [n_q, h_kv, k]; lse fp32 [n_q, h_q]."""
+    [n_q, h_kv, k]; lse fp32 [n_q, h_q].  With q_idx [n_q, h_kv, d_idx] and
+    k_idx [n_kv, d_idx] also the KL-alignment term: returns (dq, dk, dv, kl,
+    dq_idx, dk_idx) with kl fp32 [n_q, h_kv] (None when kl_out is False)."""
     n_q, h_q, d_h = q.shape
     n_kv, h_kv = k.shape[0], k.shape[1]
     tk = int(top_k) if top_k is not None else block_idx.shape[-1]
-    shape = make_shape(h_q, h_kv, d_h, 64, tk, _dtype_code(q), sm_scale=sm_scale)
+    with_kl = q_idx is not None
+    d_idx = q_idx.shape[-1] if with_kl else 64
+    shape = make_shape(h_q, h_kv, d_h, d_idx, tk, _dtype_code(q), sm_scale=sm_scale, idx_scale=idx_scale)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    nws = workspace_size(OP_PREFILL_BACKWARD, shape, n_q=n_q, q_start=int(q_start), n_kv=n_kv)
+    op = OP_PREFILL_BACKWARD_KL if with_kl else OP_PREFILL_BACKWARD
+    nws = workspace_size(op, shape, n_q=n_q, q_start=int(q_start), n_kv=n_kv)
     ws = _workspace(nws, q.device, workspace)
     kv = KV(_ptr(k), _ptr(v), None, None, None, n_kv, 0)
+    klp = None
+    kl = dq_idx = dk_idx = None
+    if with_kl:
+        kl = torch.empty((n_q, h_kv), dtype=torch.float32, device=q.device) if kl_out else None
+        dq_idx = torch.empty_like(q_idx)
+        dk_idx = torch.empty_like(k_idx)
+        klp = ctypes.byref(KL(_ptr(q_idx), _ptr(k_idx), float(kl_scale), _ptr(kl), _ptr(dq_idx), _ptr(dk_idx)))
     _check(lib().msa_sparse_prefill_backward(ctypes.byref(shape), n_q, int(q_start), _ptr(q), ctypes.byref(kv),
                                              _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
-                                             _ptr(dv), _ptr(ws), nws, _stream(stream)))
+                                             _ptr(dv), klp, _ptr(ws), nws, _stream(stream)))
+    if with_kl:
+        return dq, dk, dv, kl, dq_idx, dk_idx
     return dq, dk, dv
 
 

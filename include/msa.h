@@ -175,12 +175,36 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
  *                                        attends get 0
  * Built for dtype MSA_BF16 (bf16 caches) and d_h 64/128; other shapes
  * return MSA_ERR_UNSUPPORTED.  Accumulation is fp32 without atomics, so
- * results are bitwise reproducible.  Workspace: msa_workspace_size(5, ...). */
+ * results are bitwise reproducible.
+ *
+ * kl (nullable): also the KL-alignment term of [P1] §4.5 and the [P4] key
+ * points, in the same pass over the selected blocks.  For each query and
+ * group over the same visible keys T:
+ *   target     p_main(j) = mean over the group's heads of P (detached)
+ *   prediction p_idx(j)  = softmax over T of S_idx(j) = q_idx.k_idx_j * idx_scale
+ *   KL_row = sum_j p_main(j) (ln p_main(j) - ln p_idx(j));
+ *   L = kl_scale * sum over rows of KL_row, differentiated only in q_idx and
+ *   k_idx: dq_idx = idx_scale sum_j dS_idx(j) k_idx_j, dk_idx_j = idx_scale
+ *   sum over rows of dS_idx(j) q_idx, dS_idx = kl_scale (p_idx - p_main).
+ *   kl->q_idx [n_q, h_kv, d_idx], kl->k_idx [n_kv, d_idx] (bf16, contiguous);
+ *   kl->kl_out [n_q, h_kv] fp32 (nullable); kl->dq_idx, kl->dk_idx (bf16,
+ *   shapes of q_idx, k_idx; dk_idx written in full).  idx_scale comes from
+ *   the shape (0 -> 1/sqrt(d_idx)).
+ * Workspace: msa_workspace_size(5, ...) without kl, (6, ...) with kl.       */
+typedef struct msa_kl {
+  const void* q_idx;
+  const void* k_idx;
+  float kl_scale;
+  float* kl_out;
+  void* dq_idx;
+  void* dk_idx;
+} msa_kl;
+
 msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int32_t q_start,
                                        const void* q, const msa_kv* kv, const int32_t* block_idx,
                                        const void* o, const float* lse, const void* d_o, void* dq,
-                                       void* dk, void* dv, void* workspace, size_t ws_bytes,
-                                       void* hip_stream);
+                                       void* dk, void* dv, const msa_kl* kl, void* workspace,
+                                       size_t ws_bytes, void* hip_stream);
 
 /* Dense causal GQA attention, [P1] §2.2 Eq. (1): the comparison kernel.
  *   Same arguments as msa_sparse_prefill without block_idx; contiguous cache
@@ -191,7 +215,8 @@ msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_star
 
 /* Workspace bytes a call needs.  op: 0 = msa_index_topk in prefill mode,
  * 1 = msa_sparse_prefill, 2 = msa_sparse_decode, 3 = msa_dense_prefill,
- * 4 = msa_index_topk in decode mode, 5 = msa_sparse_prefill_backward.
+ * 4 = msa_index_topk in decode mode, 5 = msa_sparse_prefill_backward,
+ * 6 = msa_sparse_prefill_backward with the KL-alignment term.
  * Pass the same shape, batch, n_q,
  * q_start and cache geometry (n_kv; max_pages for decode mode) as the
  * call.  Returns 0 when no workspace is needed or for an invalid request

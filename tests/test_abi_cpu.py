@@ -164,8 +164,9 @@ def test_backward_validation():
     L = msa.lib()
     s = _shape()
     kv = msa.KV(FAKE, FAKE, None, None, None, 256, 0)
-    args = lambda shp, n_q=8, q_start=0, kv_=kv, dq=FAKE: (ctypes.byref(shp), n_q, q_start, FAKE, ctypes.byref(kv_),
-                                                          FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, None, 0, None)
+    args = lambda shp, n_q=8, q_start=0, kv_=kv, dq=FAKE, kl=None: (
+        ctypes.byref(shp), n_q, q_start, FAKE, ctypes.byref(kv_), FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, kl, None, 0,
+        None)
     assert L.msa_sparse_prefill_backward(*args(_shape(dtype_code=1))) == 2 and "MSA_BF16" in _err()
     assert L.msa_sparse_prefill_backward(*args(_shape(d_h=96))) == 2
     paged = msa.KV(FAKE, FAKE, None, FAKE, None, 256, 2)
@@ -178,3 +179,10 @@ def test_backward_validation():
     need = msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=8, n_kv=256)
     assert need > msa.workspace_size(msa.OP_PREFILL, s, n_q=8, n_kv=256)
     assert msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=0, n_kv=256) == 0
+    # with the KL-alignment term
+    assert msa.workspace_size(msa.OP_PREFILL_BACKWARD_KL, s, n_q=8, n_kv=256) > need
+    bad_kl = msa.KL(FAKE, None, 1.0, None, FAKE, FAKE)
+    assert L.msa_sparse_prefill_backward(*args(s, kl=ctypes.byref(bad_kl))) == 1 and "kl" in _err()
+    good_kl = msa.KL(FAKE, FAKE, 1.0, None, FAKE, FAKE)
+    assert L.msa_sparse_prefill_backward(*args(s, kl=ctypes.byref(good_kl))) == 3
+    assert L.msa_sparse_prefill_backward(*args(_shape(d_idx=48), kl=ctypes.byref(good_kl))) == 2

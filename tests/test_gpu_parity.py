@@ -607,3 +607,75 @@ def test_backward_no_queries_zero_fills():
                                 q_start=600, out=(q0, dk, dv))
     torch.cuda.synchronize()
     assert not dk.any() and not dv.any()
+
+
+def _kl_case(shape, n_kv, n_q, seed, *, kl_scale=1.0, sinks=False):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV)
+    q_start = inp["q_start"]
+    _say("kl alignment", shape, n_kv, n_q, seed, kl_scale, "sinks" if sinks else "")
+    if sinks:
+        bidx = torch.full((n_q, shape.h_kv, shape.top_k), -1, dtype=torch.int32)
+        for i in range(n_q):
+            d = (q_start + i) // 128
+            ids = sorted(set(range(min(shape.top_k - 1, d))) | {d})
+            bidx[i, :, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        bidx = bidx.to(DEV)
+    else:
+        bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k, q_start=q_start)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
+    d_o = torch.randn(inp["q"].shape, generator=torch.Generator().manual_seed(seed + 7)).to(torch.bfloat16).to(DEV)
+    dq, dk, dv, kl, dqi, dki = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o,
+                                                           q_start=q_start, q_idx=inp["q_idx"], k_idx=inp["k_idx"],
+                                                           kl_scale=kl_scale)
+    torch.cuda.synchronize()
+    ids = bidx.cpu().numpy()
+    r_kl, r_dqi, r_dki = orc.kl_alignment(np64(inp["q_idx"]), np64(inp["k_idx"]), np64(inp["q"]), np64(inp["k"]),
+                                          ids, q_start, kl_scale=kl_scale)
+    g_kl = kl.cpu().double().numpy()
+    err = np.abs(g_kl - r_kl)
+    assert err.max() <= 2e-2 * max(1.0, float(np.abs(r_kl).max())), ("kl", float(err.max()))
+    assert np.linalg.norm(g_kl - r_kl) <= 1e-2 * max(np.linalg.norm(r_kl), 1e-30), "kl relative L2"
+    compare_grad(dqi, r_dqi, "dq_idx")
+    compare_grad(dki, r_dki, "dk_idx")
+    # the attention gradients are unchanged by asking for the KL term
+    rq, rk, rv = orc.sparse_attention_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start,
+                                               np64(d_o))
+    compare_grad(dq, rq, "dq")
+    compare_grad(dk, rk, "dk")
+    compare_grad(dv, rv, "dv")
+
+
+def test_kl_alignment_model_shape_ragged():
+    _kl_case(MODEL_SHAPE, 2300, 2300, 60, kl_scale=0.5)
+
+
+def test_kl_alignment_head_ratios_d_idx_and_chunked_start():
+    _kl_case(HeadShape(16, 2, 64, 32, 6), 1700, 1700, 61)
+    _kl_case(HeadShape(8, 8, 128, 128, 8), 900, 900, 62, kl_scale=2.0)
+    _kl_case(MODEL_SHAPE, 3000, 700, 63)
+
+
+def test_kl_alignment_hot_blocks():
+    _kl_case(HeadShape(16, 1, 128, 64, 16), 4500, 4500, 64, sinks=True)
+
+
+def test_kl_alignment_vanishes_when_branches_agree():
+    # one KV group with one head, d_idx = d_h, q_idx = q, k_idx = k and equal
+    # scales: the two distributions coincide, so KL and its gradients are ~0
+    msa = _msa()
+    shape = HeadShape(1, 1, 64, 64, 4)
+    inp = gen_prefill(900, shape, dtype=torch.bfloat16, seed=65, device=DEV)
+    q, k = inp["q"], inp["k"]
+    k_idx = k[:, 0].contiguous()
+    bidx = msa.index_topk(q, k_idx, top_k=4)
+    o, lse = msa.sparse_prefill(q, k, inp["v"], bidx, with_lse=True)
+    out = msa.sparse_prefill_backward(q, k, inp["v"], bidx, o, lse, torch.zeros_like(q), q_idx=q, k_idx=k_idx)
+    torch.cuda.synchronize()
+    kl, dqi, dki = out[3].cpu(), out[4].cpu().float(), out[5].cpu().float()
+    assert kl.abs().max().item() < 5e-3
+    # the gradients are small next to those of an unrelated index branch
+    ref = msa.sparse_prefill_backward(q, k, inp["v"], bidx, o, lse, torch.zeros_like(q), q_idx=inp["q_idx"],
+                                      k_idx=k_idx)
+    torch.cuda.synchronize()
+    assert dqi.abs().max().item() < 0.05 * max(ref[4].cpu().float().abs().max().item(), 1e-6)
