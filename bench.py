@@ -602,9 +602,10 @@ def bench_prefill_only(msa, args, planted=True):
 
 
 def bench_backward(msa, args):
-    """msa_sparse_prefill_backward at the 32K prefill shape.  Algorithmic work:
-    five d_h-wide products per (query head, visible selected key) -- S, dP,
-    dV, dK, dQ -- i.e. 10 * d_h FLOPs, 2.5x the forward's main branch."""
+    """msa_sparse_prefill_backward at the 32K prefill shape, without and with
+    the KL-alignment term.  Algorithmic work of the attention gradients: five
+    d_h-wide products per (query head, visible selected key) -- S, dP, dV, dK,
+    dQ -- i.e. 10 * d_h FLOPs, 2.5x the forward's main branch."""
     dev = "cuda"
     shape = MODEL_SHAPE
     n = 32768
@@ -614,35 +615,41 @@ def bench_backward(msa, args):
     d_o = torch.randn(inp["q"].shape, generator=torch.Generator(device=dev).manual_seed(2), device=dev,
                       dtype=torch.float32).to(torch.bfloat16)
     s = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
-    ws = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL_BACKWARD, s, n_q=n, n_kv=n)), dtype=torch.uint8,
+    ws = torch.empty(max(1, msa.workspace_size(msa.OP_PREFILL_BACKWARD_KL, s, n_q=n, n_kv=n)), dtype=torch.uint8,
                      device=dev)
     outs = (torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]))
-    fn = [lambda: msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o, out=outs,
-                                              workspace=ws)]
-    timer = CallTimer(["backward"])
+    fns = [lambda: msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o, out=outs,
+                                               workspace=ws),
+           lambda: msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o, out=outs,
+                                               workspace=ws, q_idx=inp["q_idx"], k_idx=inp["k_idx"],
+                                               kl_scale=1.0 / (n * shape.h_kv))]
+    timer = CallTimer(["backward", "backward_kl"])
     for _ in range(args.warmup):
-        fn[0]()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
-    evs = [timer.step(fn) for _ in range(args.steps)]
+    evs = [timer.step(fns) for _ in range(args.steps)]
     timer.collect(evs)
-    t = timer.mean_ms("backward")
+    t, t_kl = timer.mean_ms("backward"), timer.mean_ms("backward_kl")
     kern = {}
     if not args.no_kernel_timing:
+        reps = min(args.steps, 5)
         msa.profile_enable(True)
-        for _ in range(min(args.steps, 5)):
-            fn[0]()
+        for _ in range(reps):
+            fns[0]()
         torch.cuda.synchronize()
         msa.profile_enable(False)
         for k_ in ("kbq_kernel", "kbkv_kernel"):
             tot, cnt = msa.profile_read(k_)
             if cnt:
-                kern[k_] = {"launches_per_call": cnt / min(args.steps, 5), "avg_launch_ms": round(tot / cnt, 5),
-                            "ms_per_call": round(tot / min(args.steps, 5), 4)}
+                kern[k_] = {"launches_per_call": cnt / reps, "avg_launch_ms": round(tot / cnt, 5),
+                            "ms_per_call": round(tot / reps, 4)}
     _, main_fl, _ = prefill_counts(n, 0, shape)
     bwd_fl = 2.5 * main_fl
     print(json.dumps({"workload": "backward 1x32768 (dq, dk, dv of the sparse prefill), 64 q / 4 kv heads, "
-                                  "d_h 128, k 16, bf16", "ms": round(t, 3),
+                                  "d_h 128, d_idx 64, k 16, bf16", "ms": round(t, 3),
                       "p10_ms": round(timer.pct("backward", 10), 3), "p90_ms": round(timer.pct("backward", 90), 3),
+                      "ms_with_kl_alignment": round(t_kl, 3),
                       "tokens_per_s": round(n / (t * 1e-3), 1), "flops": bwd_fl,
                       "roofline": roofline("mfma", bwd_fl, t, "TFLOP/s"), "kernels": kern}))
 

@@ -162,6 +162,21 @@ __device__ __forceinline__ void kb_stage_store(const KbStage<D, NT>& g, char* ld
   }
 }
 
+// Sum over aligned runs of n lanes (n = 1, 2, 4, 8 or 16) with DPP moves on
+// the VALU: quad permutations for 2 and 4, then the half-row and row
+// mirrors, which pair the remaining quads and half-rows of a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_group_sum(float x, int n) {
+  if (n >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  if (n >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if (n >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+  if (n >= 16) x += dpp_f32<0x140>(x); // row_mirror
+  return x;
+}
+
 // ---------------------------------------------------------------- dQ pass
 constexpr int kKbqThreads = 512;      // 8 waves, 32 rows each per pass
 constexpr int kKbqRowsPerPass = 256;
@@ -232,13 +247,10 @@ __device__ __forceinline__ void kbq_math(const KbArgs& a, int b, const KbqPass<D
     }
     if constexpr (KL) {
       // group mean of P over the token's heads (lanes token * G + head of
-      // this half), written by all of them (same values, same addresses)
+      // this half, an aligned run of G <= 16 lanes), written by all of them
+      // (same values, same addresses)
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1)
-        if (off < a.group) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) pm[v] += __shfl_xor(pm[v], off, 64);
-        }
+      for (int v = 0; v < 16; ++v) pm[v] = lane_group_sum(pm[v], a.group);
       const float inv_g = 1.0f / (float)a.group;
       float* dst = a.pmain + ((size_t)ps.slot_g * kBlock + kt * 32 + 4 * half);
 #pragma unroll
