@@ -295,6 +295,46 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
                     "msa_sparse_prefill");
 }
 
+msa_status msa_index_project(const msa_shape* shape, int32_t n_tok, int32_t d_model, const void* x,
+                             const void* w_q_idx, const void* w_k_idx, int32_t rope_dim, float rope_base,
+                             const int32_t* positions, const int32_t* seq, const msa_kv* kv, void* q_idx_out,
+                             void* hip_stream) {
+  msa_status st = check_shape(shape, true, false);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (s.dtype != MSA_BF16 || fp8_cache(s)) return fail(MSA_ERR_UNSUPPORTED, "msa_index_project is built for bf16");
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (n_tok < 0) return fail(MSA_ERR_INVALID_ARG, "n_tok=%d", n_tok);
+  if (d_model <= 0 || d_model % 16 != 0) return fail(MSA_ERR_INVALID_ARG, "d_model=%d must be a positive multiple of 16", d_model);
+  if (rope_dim != 0 && rope_dim != 32 && rope_dim != 64 && rope_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "rope_dim=%d not in {0,32,64,128}", rope_dim);
+  if (rope_dim > s.d_idx) return fail(MSA_ERR_INVALID_ARG, "rope_dim=%d exceeds d_idx=%d", rope_dim, s.d_idx);
+  if (rope_dim > 0 && !(rope_base > 1.0f)) return fail(MSA_ERR_INVALID_ARG, "rope_base must be > 1");
+  if (kv->page_table && kv->max_pages < 1) return fail(MSA_ERR_INVALID_ARG, "max_pages=%d", kv->max_pages);
+  if (n_tok == 0) return ok();
+  if (!x || !w_q_idx || !w_k_idx || !positions || !kv->k_idx || !q_idx_out)
+    return fail(MSA_ERR_INVALID_ARG, "x/w_q_idx/w_k_idx/positions/k_idx/q_idx_out is NULL");
+  if (!aligned16(x) || !aligned16(w_q_idx) || !aligned16(w_k_idx) || !aligned16(kv->k_idx) || !aligned16(q_idx_out))
+    return fail(MSA_ERR_INVALID_ARG, "x/w_q_idx/w_k_idx/k_idx/q_idx_out must be 16-byte aligned");
+  msa::KxArgs a{};
+  a.x = x;
+  a.w_q = w_q_idx;
+  a.w_k = w_k_idx;
+  a.positions = positions;
+  a.seq = seq;
+  a.page_table = kv->page_table;
+  a.k_cache = const_cast<void*>(kv->k_idx);
+  a.q_out = q_idx_out;
+  a.n_tok = n_tok;
+  a.d_model = d_model;
+  a.h_kv = s.h_kv;
+  a.rope_dim = rope_dim;
+  a.n_kv = kv->n_kv;
+  a.max_pages = kv->max_pages;
+  a.rope_base = rope_base;
+  return hip_status(msa::launch_index_project(s.d_idx, a, static_cast<hipStream_t>(hip_stream)), "msa_index_project");
+}
+
 msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int32_t q_start, const void* q,
                                        const msa_kv* kv, const int32_t* block_idx, const void* o, const float* lse,
                                        const void* d_o, void* dq, void* dk, void* dv, const msa_kl* kl,

@@ -64,6 +64,21 @@ struct KiPlan {
 };
 KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_diag);
 
+// Index projections + RoPE + index-key cache append.
+struct KxArgs {
+  const void* x;            // [n_tok, d_model]
+  const void* w_q;          // [h_kv, d_idx, d_model]
+  const void* w_k;          // [d_idx, d_model]
+  const int32_t* positions; // [n_tok]
+  const int32_t* seq;       // [n_tok] nullable (paged: page_table row of each token)
+  const int32_t* page_table;
+  void* k_cache;            // contiguous [n_kv, d_idx] or pages [*, 128, d_idx]
+  void* q_out;              // [n_tok, h_kv, d_idx]
+  int32_t n_tok, d_model, h_kv, rope_dim, n_kv, max_pages;
+  float rope_base;
+};
+hipError_t launch_index_project(int d_idx, const KxArgs& a, hipStream_t st);
+
 hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipStream_t st);
 hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st);
 bool ki_supported(int dtype, int d_idx);

@@ -53,7 +53,7 @@ class KV(ctypes.Structure):
 _lib = None
 
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
-           "msa_sparse_prefill_backward",
+           "msa_sparse_prefill_backward", "msa_index_project",
            "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
            "msa_profile_enable", "msa_profile_read"]
 
@@ -74,8 +74,9 @@ def lib() -> ctypes.CDLL:
         L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
         L.msa_sparse_prefill_backward.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, vp, vp, vp,
                                                   P(KL), vp, sz, vp]
+        L.msa_index_project.argtypes = [P(Shape), i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, P(KV), vp, vp]
         for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
-                  "msa_sparse_prefill_backward"):
+                  "msa_sparse_prefill_backward", "msa_index_project"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_workspace_size.argtypes = [i32, P(Shape), i32, i32, i32, i32, i32]
         L.msa_workspace_size.restype = sz
@@ -290,6 +291,25 @@ def sparse_prefill_backward(q, k, v, block_idx, o, lse, d_o, *, q_start=0, sm_sc
     if with_kl:
         return dq, dk, dv, kl, dq_idx, dk_idx
     return dq, dk, dv
+
+
+def index_project(x, w_q_idx, w_k_idx, positions, k_idx_cache, *, rope_dim=64, rope_base=10000.0, page_table=None,
+                  seq=None, n_kv=None, out=None, stream=None):
+    """msa_index_project: q_idx [n_tok, h_kv, d_idx] = RoPE(W_q_idx[r] x) for every
+    group, and RoPE(W_k_idx x) appended to ``k_idx_cache`` (contiguous [n_kv,
+    d_idx] or pages [*, 128, d_idx] with ``page_table``) at each token's
+    position.  Returns q_idx."""
+    n_tok, d_model = x.shape
+    h_kv, d_idx = w_q_idx.shape[0], w_q_idx.shape[1]
+    shape = make_shape(h_kv, h_kv, 128, d_idx, 16, _dtype_code(x))
+    q_out = out if out is not None else torch.empty((n_tok, h_kv, d_idx), dtype=x.dtype, device=x.device)
+    nkv = int(n_kv) if n_kv is not None else (k_idx_cache.shape[0] if page_table is None else 0)
+    mp = page_table.shape[-1] if page_table is not None else 0
+    kv = KV(None, None, _ptr(k_idx_cache), _ptr(page_table), None, nkv, mp)
+    _check(lib().msa_index_project(ctypes.byref(shape), n_tok, d_model, _ptr(x), _ptr(w_q_idx), _ptr(w_k_idx),
+                                   int(rope_dim), float(rope_base), _ptr(positions), _ptr(seq), ctypes.byref(kv),
+                                   _ptr(q_out), _stream(stream)))
+    return q_out
 
 
 def dense_prefill(q, k, v, *, q_start=0, sm_scale=0.0, with_lse=False, out=None, stream=None):

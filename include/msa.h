@@ -206,6 +206,28 @@ msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int3
                                        void* dk, void* dv, const msa_kl* kl, void* workspace,
                                        size_t ws_bytes, void* hip_stream);
 
+/* The steps before the index branch ([P1] §4.2: one index-query projection
+ * per GQA group and one shared index-key projection; §3.1: RoPE on 64 dims):
+ * for each of n_tok tokens with hidden state x_t at position positions[t],
+ *   q_idx[t, r] = RoPE(W_q_idx[r] . x_t, positions[t]),  r < h_kv
+ *   k_idx_t     = RoPE(W_k_idx . x_t, positions[t])
+ * RoPE turns the pair of dims (i, i + rope_dim/2), i < rope_dim/2, by the
+ * angle positions[t] * rope_base^(-2i/rope_dim) (rope_dim 0, 32, 64 or 128,
+ * at most d_idx; dims from rope_dim on are left as they are).
+ *   x        [n_tok, d_model] bf16; d_model a positive multiple of 16
+ *   w_q_idx  [h_kv, d_idx, d_model] bf16; w_k_idx [d_idx, d_model] bf16
+ *   positions, seq  device int32 [n_tok]; seq nullable (row 0)
+ *   q_idx_out [n_tok, h_kv, d_idx] bf16
+ * k_idx_t is appended to the index-key cache kv->k_idx in place: contiguous
+ * (page_table NULL) at row positions[t] if it is in [0, n_kv); paged at row
+ * positions[t] % 128 of page page_table[seq[t] * max_pages + positions[t] /
+ * 128] if positions[t] / 128 < max_pages.  Rows out of range are skipped.
+ * bf16 only (dtype MSA_BF16, bf16 cache).                                   */
+msa_status msa_index_project(const msa_shape* shape, int32_t n_tok, int32_t d_model, const void* x,
+                             const void* w_q_idx, const void* w_k_idx, int32_t rope_dim, float rope_base,
+                             const int32_t* positions, const int32_t* seq, const msa_kv* kv,
+                             void* q_idx_out, void* hip_stream);
+
 /* Dense causal GQA attention, [P1] §2.2 Eq. (1): the comparison kernel.
  *   Same arguments as msa_sparse_prefill without block_idx; contiguous cache
  *   only.  top_k, force_local and the index fields of `shape` are ignored. */

@@ -397,6 +397,40 @@ def kl_alignment(q_idx, k_idx, q, k, block_idx, q_start, *, sm_scale=None, idx_s
     return kl, dq_idx, dk_idx
 
 
+# --------------------------------------------------------------------------
+# The steps before the index branch ([P1] §4.2: one index-query projection
+# per GQA group and one shared index-key projection; §3.1: RoPE on 64 dims)
+# --------------------------------------------------------------------------
+
+def rope(v, positions, rope_dim, base=10000.0):
+    """Rotary position embedding on the first ``rope_dim`` dims of the last
+    axis, "rotate half" pairing: dim i < rope_dim/2 pairs with i + rope_dim/2
+    and the pair turns by the angle p * base^(-2i/rope_dim).  ``v`` [n, ..., d],
+    ``positions`` [n]."""
+    v = _f64(v).copy()
+    if rope_dim == 0:
+        return v
+    h = rope_dim // 2
+    theta = base ** (-2.0 * np.arange(h) / rope_dim)
+    ang = np.asarray(positions, np.float64).reshape((-1,) + (1,) * (v.ndim - 1)) * theta
+    c, s_ = np.cos(ang), np.sin(ang)
+    x1, x2 = v[..., :h].copy(), v[..., h:rope_dim].copy()
+    v[..., :h] = x1 * c - x2 * s_
+    v[..., h:rope_dim] = x2 * c + x1 * s_
+    return v
+
+
+def index_projection(x, w_q_idx, w_k_idx, positions, *, rope_dim=64, rope_base=10000.0):
+    """q_idx^(r) = W_q^idx,(r) x for each group r and k_idx = W_k^idx x, then
+    RoPE at each token's position.  ``x`` [n, d_model], ``w_q_idx`` [h_kv,
+    d_idx, d_model], ``w_k_idx`` [d_idx, d_model].  Returns (q_idx [n, h_kv,
+    d_idx], k_idx [n, d_idx])."""
+    x = _f64(x)
+    q = np.einsum("nm,rdm->nrd", x, _f64(w_q_idx))
+    k = x @ _f64(w_k_idx).T
+    return rope(q, positions, rope_dim, rope_base), rope(k, positions, rope_dim, rope_base)
+
+
 def decode_e4m3(codes):
     """Values of OCP FP8 E4M3 ("fn") codes, written from the format's
     definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;

@@ -186,3 +186,18 @@ def test_backward_validation():
     good_kl = msa.KL(FAKE, FAKE, 1.0, None, FAKE, FAKE)
     assert L.msa_sparse_prefill_backward(*args(s, kl=ctypes.byref(good_kl))) == 3
     assert L.msa_sparse_prefill_backward(*args(_shape(d_idx=48), kl=ctypes.byref(good_kl))) == 2
+
+
+def test_index_project_validation():
+    L = msa.lib()
+    s = msa.make_shape(4, 4, 128, 64, 16, msa.MSA_BF16)
+    kv = msa.KV(None, None, FAKE, None, None, 1000, 0)
+    call = lambda shp=s, n=8, dm=256, rope=64, base=10000.0, kv_=kv, x=FAKE: L.msa_index_project(
+        ctypes.byref(shp), n, dm, x, FAKE, FAKE, rope, base, FAKE, None, ctypes.byref(kv_), FAKE, None)
+    assert call(dm=100) == 1 and "d_model" in _err()
+    assert call(rope=48) == 2 and "rope_dim" in _err()
+    assert call(rope=128) == 1 and "exceeds" in _err()
+    assert call(base=1.0) == 1 and "rope_base" in _err()
+    assert call(x=None) == 1 and "NULL" in _err()
+    assert call(shp=msa.make_shape(4, 4, 128, 64, 16, msa.MSA_FP32)) == 2
+    assert call(n=0) == 0 and _err() == ""

@@ -679,3 +679,71 @@ def test_kl_alignment_vanishes_when_branches_agree():
                                       k_idx=k_idx)
     torch.cuda.synchronize()
     assert dqi.abs().max().item() < 0.05 * max(ref[4].cpu().float().abs().max().item(), 1e-6)
+
+
+# ------------------------------------------ index projections, RoPE, append
+
+def _project_case(n_tok, d_model, h_kv, d_idx, rope_dim, seed, *, paged, positions=None):
+    msa = _msa()
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16)
+    wq = (torch.randn(h_kv, d_idx, d_model, generator=g) * (0.5 / d_model ** 0.5)).to(torch.bfloat16)
+    wk = (torch.randn(d_idx, d_model, generator=g) * (0.5 / d_model ** 0.5)).to(torch.bfloat16)
+    _say("index_project", n_tok, d_model, h_kv, d_idx, rope_dim, "paged" if paged else "contiguous")
+    if paged:
+        # decode-like: token t is the new token of sequence t
+        pos = positions if positions is not None else torch.randint(0, 1 << 20, (n_tok,), generator=g)
+        max_pages = int(pos.max().item()) // 128 + 1
+        # every logical page of sequence t maps to physical page perm[t] (only
+        # the page holding the new token is written)
+        perm = torch.randperm(n_tok + 3, generator=g)[:n_tok].to(torch.int32)
+        pt = perm[:, None].expand(n_tok, max_pages).contiguous()
+        cache = torch.randn(n_tok + 3, 128, d_idx, generator=g).to(torch.bfloat16)
+        before = cache.clone()
+        q = msa.index_project(x.to(DEV), wq.to(DEV), wk.to(DEV), pos.to(torch.int32).to(DEV), c := cache.to(DEV),
+                              rope_dim=rope_dim, page_table=pt.to(DEV), seq=torch.arange(n_tok, dtype=torch.int32).to(DEV))
+    else:
+        q_start = 5000
+        pos = torch.arange(q_start, q_start + n_tok)
+        cache = torch.randn(q_start + n_tok + 7, d_idx, generator=g).to(torch.bfloat16)
+        before = cache.clone()
+        q = msa.index_project(x.to(DEV), wq.to(DEV), wk.to(DEV), pos.to(torch.int32).to(DEV), c := cache.to(DEV),
+                              rope_dim=rope_dim)
+    torch.cuda.synchronize()
+    rq, rk = orc.index_projection(np64(x), np64(wq), np64(wk), pos.numpy(), rope_dim=rope_dim)
+    compare_out(q, rq, torch.bfloat16, "q_idx")
+    got = c.cpu()
+    expect = before.clone()
+    if paged:
+        for t in range(n_tok):
+            p = int(pos[t])
+            expect[pt[t, p // 128], p % 128] = torch.from_numpy(rk[t]).to(torch.bfloat16)
+            compare_out(got[pt[t, p // 128], p % 128][None], rk[t][None], torch.bfloat16, "k_idx row")
+        written = torch.zeros(got.shape[:2], dtype=torch.bool)
+        for t in range(n_tok):
+            p = int(pos[t])
+            written[pt[t, p // 128], p % 128] = True
+        assert torch.equal(got[~written], before[~written]), "rows other than the appended ones changed"
+    else:
+        compare_out(got[pos], rk, torch.bfloat16, "k_idx rows")
+        keep = torch.ones(got.shape[0], dtype=torch.bool)
+        keep[pos] = False
+        assert torch.equal(got[keep], before[keep]), "rows other than the appended ones changed"
+
+
+def test_index_project_decode_paged_rope64():
+    _project_case(64, 1024, 4, 64, 64, 70, paged=True)
+
+
+def test_index_project_prefill_contiguous_variants():
+    _project_case(1000, 512, 4, 64, 64, 71, paged=False)
+    _project_case(300, 256, 2, 32, 32, 72, paged=False)
+    _project_case(200, 768, 8, 128, 64, 73, paged=False)
+    _project_case(150, 256, 1, 128, 128, 74, paged=False)
+    _project_case(97, 256, 4, 64, 0, 75, paged=False)
+
+
+def test_index_project_large_positions_paged():
+    # positions near 2^20 + 255: the angle must be formed without fp32 rounding
+    pos = torch.tensor([1048575, 1048831, 1048576, 0, 127, 128, 999999, 524288], dtype=torch.int64)
+    _project_case(8, 256, 4, 64, 64, 76, paged=True, positions=pos)

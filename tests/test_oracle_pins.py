@@ -593,3 +593,58 @@ def test_kl_alignment_zero_when_index_branch_equals_main_branch():
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_allclose(b[1], 2.5 * a[1], rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(b[2], 2.5 * a[2], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------- index projections and RoPE ([P1] §3.1, §4.2)
+
+def test_rope_closed_form_angles():
+    # a unit vector on dim i turns into (cos a, sin a) on dims (i, i + 32) with
+    # a = p * 10000^(-2i/64)
+    d = 64
+    for i, p in ((0, 1), (0, 5), (16, 1), (31, 1000), (7, 123456)):
+        v = np.zeros((1, d))
+        v[0, i] = 1.0
+        out = orc.rope(v, [p], 64)
+        a = p * 10000.0 ** (-2.0 * i / 64)
+        expect = np.zeros(d)
+        expect[i] = math.cos(a)
+        expect[i + 32] = math.sin(a)
+        np.testing.assert_allclose(out[0], expect, atol=1e-12)
+    # position 0 is the identity; dims past rope_dim are untouched
+    rng = np.random.default_rng(30)
+    v = rng.standard_normal((3, 128))
+    np.testing.assert_array_equal(orc.rope(v, [0, 0, 0], 64), v)
+    np.testing.assert_array_equal(orc.rope(v, [5, 9, 77], 64)[:, 64:], v[:, 64:])
+
+
+def test_rope_is_a_rotation_with_relative_positions():
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+    np.testing.assert_allclose(np.linalg.norm(orc.rope(q, [987654], 64)), np.linalg.norm(q), rtol=1e-12)
+    # the score of a rotated pair depends only on the position difference
+    for p1, p2, sft in ((10, 3, 100), (5000, 4990, 1 << 20), (0, 0, 77)):
+        a = orc.rope(q, [p1], 64) @ orc.rope(k, [p2], 64).T
+        b = orc.rope(q, [p1 + sft], 64) @ orc.rope(k, [p2 + sft], 64).T
+        assert a[0, 0] == pytest.approx(b[0, 0], rel=1e-9, abs=1e-9)
+
+
+def test_index_projection_groups_and_shared_key():
+    rng = np.random.default_rng(32)
+    n, dm, h_kv, di = 5, 48, 3, 32
+    x = rng.standard_normal((n, dm))
+    wq = rng.standard_normal((h_kv, di, dm))
+    wk = rng.standard_normal((di, dm))
+    pos = np.array([0, 1, 2, 300, 70000])
+    q, k = orc.index_projection(x, wq, wk, pos, rope_dim=0)
+    for r in range(h_kv):
+        np.testing.assert_allclose(q[:, r], x @ wq[r].T, rtol=1e-12)
+    np.testing.assert_allclose(k, x @ wk.T, rtol=1e-12)
+    # group r's query depends on W_q[r] only
+    wq2 = wq.copy()
+    wq2[1] += 1.0
+    q2, _ = orc.index_projection(x, wq2, wk, pos, rope_dim=32)
+    q1, _ = orc.index_projection(x, wq, wk, pos, rope_dim=32)
+    np.testing.assert_array_equal(q2[:, 0], q1[:, 0])
+    np.testing.assert_array_equal(q2[:, 2], q1[:, 2])
+    assert not np.allclose(q2[:, 1], q1[:, 1])
