@@ -348,7 +348,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "backward32k",
-                                                             "copy"])
+                                                             "project", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -379,6 +379,8 @@ def main():
         bench_prefill_only(msa, args, planted=True)
     elif args.workload == "backward32k":
         bench_backward(msa, args)
+    elif args.workload == "project":
+        bench_project(msa, args)
     else:
         bench_long(msa, args)
 
@@ -652,6 +654,47 @@ def bench_backward(msa, args):
                       "ms_with_kl_alignment": round(t_kl, 3),
                       "tokens_per_s": round(n / (t * 1e-3), 1), "flops": bwd_fl,
                       "roofline": roofline("mfma", bwd_fl, t, "TFLOP/s"), "kernels": kern}))
+
+
+def bench_project(msa, args):
+    """msa_index_project (index projections + RoPE + index-key append) for a
+    64-sequence decode step and a 32768-token prefill, at d_model 6144 (the
+    pages give no hidden size; 6144 is an assumed width), 4 groups, d_idx 64,
+    RoPE on 64 dims.  Work: 2 * d_model * (h_kv + 1) * d_idx FLOPs per token;
+    bytes: the weights once plus x, q_idx and the appended keys."""
+    dev = "cuda"
+    dm, h_kv, di = 6144, 4, 64
+    g = torch.Generator(device=dev).manual_seed(5)
+    wq = (torch.randn(h_kv, di, dm, generator=g, device=dev) / dm ** 0.5).to(torch.bfloat16)
+    wk = (torch.randn(di, dm, generator=g, device=dev) / dm ** 0.5).to(torch.bfloat16)
+    res = {}
+    for name, n in (("decode64", 64), ("prefill32k", 32768)):
+        x = torch.randn(n, dm, generator=g, device=dev).to(torch.bfloat16)
+        if name == "decode64":
+            pos = torch.full((n,), 131071, dtype=torch.int32, device=dev)
+            cache = torch.zeros(65536, 128, di, dtype=torch.bfloat16, device=dev)
+            pt = torch.randperm(65536, device=dev).to(torch.int32).view(64, 1024)
+            seq = torch.arange(n, dtype=torch.int32, device=dev)
+            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, page_table=pt, seq=seq, out=qo)]
+        else:
+            pos = torch.arange(n, dtype=torch.int32, device=dev)
+            cache = torch.zeros(n, di, dtype=torch.bfloat16, device=dev)
+            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, out=qo)]
+        qo = torch.empty(n, h_kv, di, dtype=torch.bfloat16, device=dev)
+        timer = CallTimer([name])
+        for _ in range(args.warmup):
+            fn[0]()
+        torch.cuda.synchronize()
+        evs = [timer.step(fn) for _ in range(args.steps)]
+        timer.collect(evs)
+        t = timer.mean_ms(name)
+        fl = 2.0 * n * dm * (h_kv + 1) * di
+        byts = (h_kv + 1) * di * dm * 2 + n * dm * 2 + n * (h_kv + 1) * di * 2
+        res[name] = {"tokens": n, "us": round(t * 1e3, 2), "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "gbs": round(byts / (t * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    print(json.dumps({"workload": "index projections + RoPE + k_idx append, d_model 6144 (assumed), 4 groups, d_idx 64, "
+                                  "RoPE 64", "results": res}))
 
 
 def bench_long(msa, args):

@@ -542,12 +542,18 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
 // a RoPE pair (i, i + R/2) sits in one lane; angles in double precision (the
 // position times the frequency must stay exact for positions up to 2^20 and
 // beyond).  The key projection is appended to the index-key cache in place.
+// A workgroup takes 32 tokens and one projection; its 8 waves split d_model
+// (16-wide steps dealt round-robin) and their sums are added in a fixed tree
+// through LDS, so short calls (a decode step) still spread over many waves.
+constexpr int kKxWaves = 8;
+
 template <int DI>
-__global__ __launch_bounds__(256) void kx_project_kernel(KxArgs a) {
+__global__ __launch_bounds__(kKxWaves * 64) void kx_project_kernel(KxArgs a) {
   constexpr int FT = DI / 32;
+  __shared__ f32x4 red[kKxWaves / 2][FT * 4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   const int hd = blockIdx.y;  // 0 .. h_kv - 1: query projections; h_kv: the key projection
-  const int t_raw = (blockIdx.x * 4 + wave) * 32 + l32;
+  const int t_raw = blockIdx.x * 32 + l32;
   const bool ok = t_raw < a.n_tok;
   const int t = min(t_raw, a.n_tok - 1);
   const bf16_t* w = static_cast<const bf16_t*>(hd < a.h_kv ? a.w_q : a.w_k) +
@@ -557,12 +563,38 @@ __global__ __launch_bounds__(256) void kx_project_kernel(KxArgs a) {
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x16{};
 #pragma unroll 4
-  for (int k0 = 0; k0 < a.d_model; k0 += 16) {
+  for (int k0 = wave * 16; k0 < a.d_model; k0 += kKxWaves * 16) {
     const bf16x8 xb = load_frag<bf16_t>(xr + k0);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
       mma32(acc[ft], load_frag<bf16_t>(w + (size_t)(ft * 32 + l32) * a.d_model + k0 + half * 8), xb);
   }
+  // tree: the upper half of the live waves hands its sums to the lower half
+#pragma unroll
+  for (int live = kKxWaves; live > 1; live >>= 1) {
+    const int h = live >> 1;
+    if (wave >= h && wave < live) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          red[wave - h][ft * 4 + c][lane] =
+              f32x4{acc[ft][4 * c], acc[ft][4 * c + 1], acc[ft][4 * c + 2], acc[ft][4 * c + 3]};
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 o = red[wave][ft * 4 + c][lane];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[ft][4 * c + q] += o[q];
+        }
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
   // RoPE: feature f = ft*32 + 8*(v/4) + 4*half + (v%4) of this lane's token
   const int R = a.rope_dim;
   const double pos = (double)a.positions[t];
@@ -621,10 +653,11 @@ __global__ __launch_bounds__(256) void kx_project_kernel(KxArgs a) {
 
 hipError_t launch_index_project(int d_idx, const KxArgs& a, hipStream_t st) {
   if (a.n_tok == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_tok + 127) / 128), (unsigned)(a.h_kv + 1));
-  if (d_idx == 32) hipLaunchKernelGGL(kx_project_kernel<32>, grid, dim3(256), 0, st, a);
-  else if (d_idx == 64) hipLaunchKernelGGL(kx_project_kernel<64>, grid, dim3(256), 0, st, a);
-  else if (d_idx == 128) hipLaunchKernelGGL(kx_project_kernel<128>, grid, dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.n_tok + 31) / 32), (unsigned)(a.h_kv + 1));
+  const dim3 block(kKxWaves * 64);
+  if (d_idx == 32) hipLaunchKernelGGL(kx_project_kernel<32>, grid, block, 0, st, a);
+  else if (d_idx == 64) hipLaunchKernelGGL(kx_project_kernel<64>, grid, block, 0, st, a);
+  else if (d_idx == 128) hipLaunchKernelGGL(kx_project_kernel<128>, grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
