@@ -10,7 +10,7 @@
 //  * dQ pass (windows of query tokens): an item is one (group, block) and up
 //    to 512 of the rows that selected it; S^T = K.Q^T, dP^T = V.dO^T and
 //    dQ^T = K^T.dS^T on v_mfma_f32_32x32x16_bf16 with keys on the MFMA rows.
-//    Each (token, head, slot) writes an fp32 partial dQ and a merge kernel
+//    Each (token, head, slot) writes a bf16 partial dQ and a merge kernel
 //    sums a row's partials (the two-stage merge without rescaling).
 //  * dK/dV pass (one window over all queries): an item keeps its block's
 //    dK^T and dV^T in registers (four waves of 32 keys) while it sweeps its
@@ -41,7 +41,7 @@ struct KbArgs {
   const int32_t* entries;
   const i32x4* items;
   int32_t* queue;           // dK/dV pass: next item to take (zeroed by the schedule)
-  float* part_dq;           // dQ pass: [window * h_kv * top_k + 2 trash, G, D]
+  bf16_t* part_dq;          // dQ pass: [window * h_kv * top_k + 2 trash, G, D]
   float* part_dkv;          // dK/dV pass: [max_items, 2, 128, D]
   int32_t n_q, q_start, n_kv, h_q, h_kv, group, g_shift, top_k, n_blocks, window, w;
   size_t trash_slot;
@@ -272,20 +272,21 @@ __device__ __forceinline__ void kbq_math(const KbArgs& a, int b, const KbqPass<D
   }
 }
 
-// fp32 partial of (token, slot): [G][D] in natural order; rows past the item
-// write the trash slot so the store count never depends on the data.
+// bf16 partial of (token, slot) (like the forward's partial O): [G][D] in
+// natural order; rows past the item write the trash slot so the store count
+// never depends on the data.
 template <int D>
 __device__ __forceinline__ void kbq_store(const KbArgs& a, const KbqPass<D>& ps, const f32x16 (&dq)[D / 32]) {
   const int half = (threadIdx.x & 63) >> 5;
   const size_t slot = ps.ok ? (size_t)ps.slot : a.trash_slot;
-  float* dst = a.part_dq + (slot * a.group + ps.head) * D;
+  bf16_t* dst = a.part_dq + (slot * a.group + ps.head) * D;
   const float sc = a.sm_scale;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<f32x4*>(dst + dt * 32 + 8 * c + 4 * half) =
-          f32x4{dq[dt][4 * c] * sc, dq[dt][4 * c + 1] * sc, dq[dt][4 * c + 2] * sc, dq[dt][4 * c + 3] * sc};
+      store4<bf16_t>(dst + dt * 32 + 8 * c + 4 * half, dq[dt][4 * c] * sc, dq[dt][4 * c + 1] * sc,
+                     dq[dt][4 * c + 2] * sc, dq[dt][4 * c + 3] * sc);
 }
 
 // Persistent over this XCD's items of window w (the forward's item order):
@@ -358,9 +359,9 @@ __global__ __launch_bounds__(256) void kbq_merge_kernel(KbArgs a) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < a.top_k; ++j) {
     if (!((used >> j) & 1u)) continue;
-    const float* src = a.part_dq + ((slot0 + j) * G + g) * D + c * 8;
-    s0 += *reinterpret_cast<const f32x4*>(src);
-    s1 += *reinterpret_cast<const f32x4*>(src + 4);
+    const bf16x8 x = load_frag<bf16_t>(a.part_dq + ((slot0 + j) * G + g) * D + c * 8);
+    s0 += f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+    s1 += f32x4{to_f32(x[4]), to_f32(x[5]), to_f32(x[6]), to_f32(x[7])};
   }
   bf16_t* dst = static_cast<bf16_t*>(a.dq) + ((size_t)i * a.h_q + h) * D + c * 8;
   *reinterpret_cast<bf16x8*>(dst) = bf16x8{from_f32<bf16_t>(s0[0]), from_f32<bf16_t>(s0[1]), from_f32<bf16_t>(s0[2]),
@@ -1017,7 +1018,7 @@ BackwardPlan backward_plan(int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h
   p.off_q = off; off = align(off + p.q.total);
   p.off_kv = off; off = align(off + p.kv.total);
   p.off_dsum = off; off = align(off + (size_t)n_q * h_q * 4);
-  p.off_part_dq = off; off = align(off + ((size_t)p.q.window * h_kv * top_k + 2) * G * d_h * 4);
+  p.off_part_dq = off; off = align(off + ((size_t)p.q.window * h_kv * top_k + 2) * G * d_h * 2);
   p.off_part_dkv = off; off = align(off + (size_t)p.kv.max_items * 2 * kBlock * d_h * 4);
   if (with_kl) {
     p.off_pmain = off; off = align(off + ((size_t)n_q * h_kv * top_k + 1) * kBlock * 4);
@@ -1078,7 +1079,7 @@ static hipError_t backward_typed(const BackwardArgs& ba, const BackwardPlan& pl,
   k.dv = ba.dv;
   k.dsum = reinterpret_cast<float*>(ws + pl.off_dsum);
   k.block_idx = a.block_idx;
-  k.part_dq = reinterpret_cast<float*>(ws + pl.off_part_dq);
+  k.part_dq = reinterpret_cast<bf16_t*>(ws + pl.off_part_dq);
   k.part_dkv = reinterpret_cast<float*>(ws + pl.off_part_dkv);
   if (ba.kl) {
     k.pmain = reinterpret_cast<float*>(ws + pl.off_pmain);
