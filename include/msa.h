@@ -2,13 +2,15 @@
  * msa.h - C ABI of libmsa, the MI355X (gfx950) hot path of MiniMax Sparse
  * Attention (MSA): the index branch (block scoring and exp-free causal top-k)
  * and the main branch (exact softmax attention over the selected blocks) for
- * prefill and paged decode.
+ * prefill and paged decode; around it the index projections with RoPE and
+ * the training path (gradients of the main branch and the KL-alignment term).
  *
  * Sources:
  *   [P1] "MiniMax Sparse Attention" digest, titansim.online blog:
  *        §2.2 Eq. (1), §3.1 (shapes), §4.2 Eq. (6), §4.3 Eq. (8),
  *        §4.4.1 (exp-free top-k), §4.4.2 (KV-outer traversal, tile chunking
- *        with a two-stage merge), §5.2 Eq. (12).
+ *        with a two-stage merge), §4.5 (KL alignment, gradient detach),
+ *        §5.2 Eq. (12).
  *   [P4] "MiniMax Sparse Attention: Block-Level Top-K for Affordable
  *        Million-Token Contexts", zhichai.net, key points (block size 128,
  *        k = 16, 128-token-aligned memory transfers).
@@ -24,7 +26,8 @@
  *   - Calls are asynchronous and stream ordered on `hip_stream` (a
  *     hipStream_t; NULL = the null stream).  They never synchronise the host.
  *   - Every float tensor of a call has the dtype `shape->dtype` (bf16 or
- *     fp32); outputs `o` use it too; `lse` and `block_score` are fp32.
+ *     fp32), except the caches when `shape->cache_dtype` is MSA_FP8_E4M3;
+ *     outputs use `shape->dtype`; `lse`, `block_score` and KL values are fp32.
  *   - Arguments are validated on the host before anything is launched.  On
  *     an error the call returns a non-zero msa_status, launches nothing and
  *     leaves every output untouched; msa_last_error() then describes it.
