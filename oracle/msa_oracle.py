@@ -316,7 +316,7 @@ def _visible_tokens(row_blocks, p, block=BLOCK):
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
-def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None, block=BLOCK):
+def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None, block=BLOCK, rows=None):
     """Gradients of Eq. (8) for one contiguous sequence, given dO.
 
     For query i (position p) and head h of group r, with T the visible keys of
@@ -326,6 +326,9 @@ def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None,
         dP_j  = dO . v_j,   ds_j = P_j (dP_j - sum_t P_t dP_t)
         dq    = scale * sum_j ds_j k_j,   dk_j += scale * ds_j q.
     Returns (dq [n_q, h_q, d_h], dk [n_kv, h_kv, d_h], dv [n_kv, h_kv, d_h]).
+    With ``rows``, only those queries are taken: their dq rows, and the
+    parts of dk and dv they contribute (the whole of dk/dv for any key whose
+    block only those queries selected).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     n_q, h_q, d_h = q.shape
@@ -335,8 +338,8 @@ def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None,
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i in range(n_q):
-        p = q_start + i
+    for i in (range(n_q) if rows is None else rows):
+        p = q_start + int(i)
         for r in range(h_kv):
             toks = _visible_tokens(block_idx[i, r], p, block)
             if toks.size == 0:
@@ -355,7 +358,7 @@ def sparse_attention_backward(q, k, v, block_idx, q_start, do, *, sm_scale=None,
 
 
 def kl_alignment(q_idx, k_idx, q, k, block_idx, q_start, *, sm_scale=None, idx_scale=None,
-                 kl_scale=1.0, block=BLOCK):
+                 kl_scale=1.0, block=BLOCK, rows=None):
     """KL-alignment loss of the index branch ([P1] §4.5; [P4] key points).
 
     For query i and group r, over the visible keys T of the group's selected
@@ -366,7 +369,8 @@ def kl_alignment(q_idx, k_idx, q, k, block_idx, q_start, *, sm_scale=None, idx_s
     The loss is L = kl_scale * sum_{i,r} KL_{i,r}.  p_main is detached (no
     gradient reaches q or k), so dL/dS_idx(j) = kl_scale (p_idx(j) - p_main(j))
     and the gradients go to q_idx and k_idx only.
-    Returns (kl [n_q, h_kv], dq_idx [n_q, h_kv, d_idx], dk_idx [n_kv, d_idx]).
+    Returns (kl [n_q, h_kv], dq_idx [n_q, h_kv, d_idx], dk_idx [n_kv, d_idx]);
+    with ``rows`` only those queries are taken (as in sparse_attention_backward).
     """
     q_idx, k_idx, q, k = _f64(q_idx), _f64(k_idx), _f64(q), _f64(k)
     n_q, h_kv, d_idx = q_idx.shape
@@ -377,8 +381,8 @@ def kl_alignment(q_idx, k_idx, q, k, block_idx, q_start, *, sm_scale=None, idx_s
     kl = np.zeros((n_q, h_kv))
     dq_idx = np.zeros_like(q_idx)
     dk_idx = np.zeros_like(k_idx)
-    for i in range(n_q):
-        p = q_start + i
+    for i in (range(n_q) if rows is None else rows):
+        p = q_start + int(i)
         for r in range(h_kv):
             toks = _visible_tokens(block_idx[i, r], p, block)
             if toks.size == 0:

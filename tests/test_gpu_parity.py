@@ -747,3 +747,69 @@ def test_index_project_large_positions_paged():
     # positions near 2^20 + 255: the angle must be formed without fp32 rounding
     pos = torch.tensor([1048575, 1048831, 1048576, 0, 127, 128, 999999, 524288], dtype=torch.int64)
     _project_case(8, 256, 4, 64, 64, 76, paged=True, positions=pos)
+
+
+# ------------------------------------------------ full sizes, sampled outputs
+
+def test_full_size_backward_and_kl_32k_sampled():
+    """The 32K prefill shape as bench.py times it (backward with the KL term):
+    dq, KL and dq_idx on sampled query rows (a row's values depend on that row
+    only); dk, dv on sampled (group, block) cells and dk_idx on sampled blocks,
+    from the oracle run on exactly the queries that selected them."""
+    msa = _msa()
+    n = 32768
+    inp = gen_prefill(n, MODEL_SHAPE, dtype=torch.bfloat16, seed=1, device=DEV)
+    _say("backward + KL 32K full size")
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, with_lse=True)
+    d_o = torch.randn(inp["q"].shape, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).to(DEV)
+    kl_scale = 1.0 / (n * 4)
+    dq, dk, dv, kl, dqi, dki = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o,
+                                                           q_idx=inp["q_idx"], k_idx=inp["k_idx"], kl_scale=kl_scale)
+    torch.cuda.synchronize()
+    ids = bidx.cpu().numpy()
+    q64, k64, v64, do64 = np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), np64(d_o)
+    qi64, ki64 = np64(inp["q_idx"]), np64(inp["k_idx"])
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 127, 128, 4095, n - 1] + rng.integers(0, n, 27).tolist()))
+    rq, _, _ = orc.sparse_attention_backward(q64, k64, v64, ids, 0, do64, rows=rows)
+    compare_grad(np64(dq)[rows], rq[rows], "dq rows")
+    r_kl, r_dqi, _ = orc.kl_alignment(qi64, ki64, q64, k64, ids, 0, kl_scale=kl_scale, rows=rows)
+    g_kl = kl.cpu().double().numpy()[rows]
+    assert np.abs(g_kl - r_kl[rows]).max() <= 2e-2 * max(1.0, float(np.abs(r_kl[rows]).max())), "kl rows"
+    compare_grad(np64(dqi)[rows], r_dqi[rows], "dq_idx rows")
+    for r, b in ((1, 200), (3, 255), (0, 180)):
+        sel = np.nonzero((ids[:, r, :] == b).any(axis=1))[0]
+        sub = np.full_like(ids, -1)
+        sub[sel, r] = ids[sel, r]
+        _, rk, rv = orc.sparse_attention_backward(q64, k64, v64, sub, 0, do64, rows=sel)
+        keys = slice(b * 128, min(b * 128 + 128, n))
+        compare_grad(np64(dk)[keys, r], rk[keys, r], f"dk block {b} group {r}")
+        compare_grad(np64(dv)[keys, r], rv[keys, r], f"dv block {b} group {r}")
+    for b in (240, 255):
+        sel = np.nonzero((ids == b).any(axis=(1, 2)))[0]
+        _, _, rki = orc.kl_alignment(qi64, ki64, q64, k64, ids, 0, kl_scale=kl_scale, rows=sel)
+        keys = slice(b * 128, min(b * 128 + 128, n))
+        compare_grad(np64(dki)[keys], rki[keys], f"dk_idx block {b}")
+
+
+def test_full_size_index_project_32k_and_decode64_sampled():
+    """bench.py's projection shapes: 32768 tokens at d_model 6144 (sampled rows)
+    and a 64-sequence paged decode step (all rows)."""
+    msa = _msa()
+    dm, h_kv, di = 6144, 4, 64
+    g = torch.Generator().manual_seed(5)
+    wq = (torch.randn(h_kv, di, dm, generator=g) / dm ** 0.5).to(torch.bfloat16)
+    wk = (torch.randn(di, dm, generator=g) / dm ** 0.5).to(torch.bfloat16)
+    n = 32768
+    _say("index_project 32K x 6144")
+    x = torch.randn(n, dm, generator=g).to(torch.bfloat16)
+    pos = torch.arange(n, dtype=torch.int32)
+    cache = torch.zeros(n, di, dtype=torch.bfloat16, device=DEV)
+    q = msa.index_project(x.to(DEV), wq.to(DEV), wk.to(DEV), pos.to(DEV), cache)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 4096, 20000, n - 1]
+    rq, rk = orc.index_projection(np64(x[rows]), np64(wq), np64(wk), pos[rows].numpy())
+    compare_out(q.cpu()[rows], rq, torch.bfloat16, "q_idx rows")
+    compare_out(cache.cpu()[rows], rk, torch.bfloat16, "k_idx rows")
+    _project_case(64, dm, h_kv, di, 64, 77, paged=True, positions=torch.full((64,), 131071, dtype=torch.int64))

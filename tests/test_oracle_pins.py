@@ -648,3 +648,25 @@ def test_index_projection_groups_and_shared_key():
     np.testing.assert_array_equal(q2[:, 0], q1[:, 0])
     np.testing.assert_array_equal(q2[:, 2], q1[:, 2])
     assert not np.allclose(q2[:, 1], q1[:, 1])
+
+
+def test_training_oracle_rows_subset_is_the_restriction():
+    # taking a subset of queries equals the full computation for their rows,
+    # and for a block that only those queries selected
+    q, k, v, do, q_idx, k_idx, ids = _rand_training_case(26)
+    rows = [5, 131, 200, 299]
+    dq_a, dk_a, dv_a = orc.sparse_attention_backward(q, k, v, ids, 0, do)
+    dq_s, dk_s, dv_s = orc.sparse_attention_backward(q, k, v, ids, 0, do, rows=rows)
+    np.testing.assert_allclose(dq_s[rows], dq_a[rows], rtol=1e-12)
+    assert not dq_s[[0, 1, 2]].any()
+    sub = np.zeros_like(ids) - 1
+    sub[rows] = ids[rows]
+    dq_b, dk_b, dv_b = orc.sparse_attention_backward(q, k, v, sub, 0, do)
+    np.testing.assert_allclose(dk_s, dk_b, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv_s, dv_b, rtol=1e-12, atol=1e-14)
+    kl_a, dqi_a, _ = orc.kl_alignment(q_idx, k_idx, q, k, ids, 0)
+    kl_s, dqi_s, dki_s = orc.kl_alignment(q_idx, k_idx, q, k, ids, 0, rows=rows)
+    np.testing.assert_allclose(kl_s[rows], kl_a[rows], rtol=1e-12)
+    np.testing.assert_allclose(dqi_s[rows], dqi_a[rows], rtol=1e-12)
+    _, _, dki_b = orc.kl_alignment(q_idx, k_idx, q, k, sub, 0)
+    np.testing.assert_allclose(dki_s, dki_b, rtol=1e-12, atol=1e-14)
