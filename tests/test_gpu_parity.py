@@ -277,6 +277,88 @@ def test_prefill_deterministic_and_chunked_equals_one_shot():
     assert torch.equal(torch.cat(parts_o), o1)
 
 
+# ------------------------------------------------- more prefill shapes
+# Group counts with 16 heads each (1, 3 and 8 groups), paged bf16 and e4m3
+# caches, single-token and 17-token query counts, scores tens of nats
+# apart, and bitwise repeatability.
+
+def _pages(t, perm, n_kv):
+    """[n_kv, h_kv, ...] cache -> head-major 128-token pages [nb, h_kv, 128, ...] placed by perm."""
+    nb = perm.numel()
+    u8 = t.contiguous().view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t.contiguous()
+    pad = nb * 128 - n_kv
+    u8 = torch.cat([u8, torch.zeros((pad,) + tuple(u8.shape[1:]), dtype=u8.dtype, device=u8.device)])
+    u8 = u8.view((nb, 128) + tuple(u8.shape[1:])).permute(0, 2, 1, 3).contiguous()
+    out = torch.empty_like(u8)
+    out[perm.long().to(u8.device)] = u8
+    return out.view(torch.float8_e4m3fn) if t.dtype == torch.float8_e4m3fn else out
+
+
+def _shape_case(shape, n_kv, n_q, seed, *, paged=False, cache_dtype=None, boost=None, repeats=1):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV, cache_dtype=cache_dtype)
+    q_start = inp["q_start"]
+    k, v = inp["k"], inp["v"]
+    if boost is not None:
+        # one block's keys scaled up: its scores lie tens of nats above the
+        # rest of each row
+        blk, f = boost
+        k = k.clone()
+        k[blk * 128:(blk + 1) * 128] *= f
+    if cache_dtype == torch.float8_e4m3fn:
+        k64 = orc.decode_e4m3(k.view(torch.uint8).cpu().numpy())
+        v64 = orc.decode_e4m3(v.view(torch.uint8).cpu().numpy())
+        ki64 = orc.decode_e4m3(inp["k_idx"].view(torch.uint8).cpu().numpy())
+    else:
+        k64, v64, ki64 = np64(k), np64(v), np64(inp["k_idx"])
+    ids, _, _ = orc.index_topk(np64(inp["q_idx"]), ki64, q_start, shape.top_k)
+    bidx = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+    kw = {}
+    if paged:
+        nb = -(-n_kv // 128)
+        perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+        k, v = _pages(k, perm, n_kv), _pages(v, perm, n_kv)
+        kw = dict(page_table=perm.to(DEV), n_kv=n_kv)
+    o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), k64, v64, ids, q_start)
+    outs = []
+    for _ in range(repeats):
+        _say("prefill shape", shape, n_kv, n_q, seed, "paged" if paged else "contiguous", cache_dtype, boost)
+        o, lse = msa.sparse_prefill(inp["q"], k, v, bidx, q_start=q_start, with_lse=True, **kw)
+        torch.cuda.synchronize()
+        compare_out(o, o_ref, torch.bfloat16)
+        compare_lse(lse, lse_ref, torch.bfloat16)
+        outs.append(o)
+    return outs
+
+
+def test_prefill_model_shape_query_counts():
+    _shape_case(MODEL_SHAPE, 2125, 2125, 41)          # ragged last block
+    _shape_case(MODEL_SHAPE, 3001, 1013, 42)          # q_start 1988, unaligned
+    _shape_case(MODEL_SHAPE, 777, 1, 43)              # one query
+    _shape_case(MODEL_SHAPE, 300, 17, 44)             # 17 queries, q_start 283
+
+
+def test_prefill_sixteen_head_groups():
+    # 16 heads per group with 1, 3 and 8 groups, and small k
+    _shape_case(HeadShape(16, 1, 128, 64, 16), 1500, 1500, 45)
+    _shape_case(HeadShape(48, 3, 128, 64, 16), 900, 900, 46)
+    _shape_case(HeadShape(128, 8, 128, 64, 8), 1100, 700, 47)
+    _shape_case(HeadShape(32, 2, 128, 64, 2), 800, 800, 48)
+
+
+def test_prefill_paged_bf16_and_e4m3_model_shape():
+    _shape_case(MODEL_SHAPE, 1700, 1700, 49, paged=True)
+    _shape_case(MODEL_SHAPE, 1300, 1100, 50, paged=True, cache_dtype=torch.float8_e4m3fn)
+    _shape_case(MODEL_SHAPE, 1500, 1500, 51, cache_dtype=torch.float8_e4m3fn)
+
+
+def test_prefill_far_apart_scores_and_determinism():
+    # block 2 scores tens of nats above the rest of the rows that select it
+    _shape_case(MODEL_SHAPE, 1200, 1200, 52, boost=(2, 3000.0))
+    a, b = _shape_case(MODEL_SHAPE, 1400, 1400, 53, repeats=2)
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ decode
 
 def _cache_host(t):
