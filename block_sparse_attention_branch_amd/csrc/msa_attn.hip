@@ -689,19 +689,6 @@ __device__ __forceinline__ void kd_load_unit(KdUnit<D, TC>& x, const KdArgs& a, 
   }
 }
 
-__device__ __forceinline__ uint32_t used_slots_s(const int32_t* row, int top_k, int diag) {
-  uint32_t m = 0;
-  int prev = -1;
-  for (int j = 0; j < top_k; ++j) {
-    const int b = scalar_load(row, j);
-    if (b > prev && b <= diag) {
-      m |= 1u << j;
-      prev = b;
-    }
-  }
-  return m;
-}
-
 // Workgroup (sequence s, group r, split sp) of NW waves.  The selected keys
 // are cut into 32-key units (4 per page); wave w of split sp takes units
 // sp*NW + w, + NW*split, ...  Each wave keeps an online softmax over its
@@ -721,15 +708,36 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   const int sp = blockIdx.x % a.split;
   const int sr = blockIdx.x / a.split;
   const int s = sr / a.h_kv, r = sr % a.h_kv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+  // the wave index is made uniform so that the unit loop below is scalar
+  // control flow: loads under per-lane branches make the compiler wait for
+  // every load in flight (the prefetched unit included) before the next use
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
   const int G = a.group;
   const int L = scalar_load(a.seq_lens, s);
   const int p = L - 1, diag = p >> 7;
   const int32_t* br = a.block_idx + ((size_t)s * a.h_kv + r) * a.top_k;
-  const uint32_t used = used_slots_s(br, a.top_k, diag);
-  // lane j: block and physical page of slot j
-  const int bl = (lane < a.top_k && ((used >> lane) & 1u)) ? br[lane] : 0;
-  const int pages = (lane < a.top_k && ((used >> lane) & 1u)) ? a.page_table[(size_t)s * a.max_pages + bl] : 0;
+  // lane j: block and physical page of slot j.  The list and the page ids are
+  // two vector loads issued before the slots are vetted (a clamped index keeps
+  // the page-table read in the row), so the start-up waits on two loads, not
+  // on one load per slot.
+  const int bv = lane < a.top_k ? br[lane] : -1;
+  const int pall = lane < a.top_k ? a.page_table[(size_t)s * a.max_pages + min(max(bv, 0), a.max_pages - 1)] : 0;
+  uint32_t used = 0;
+  {
+    int prev = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int b = __builtin_amdgcn_readlane(bv, j);
+      if (j < a.top_k && b > prev && b <= diag) {
+        used |= 1u << j;
+        prev = b;
+      }
+    }
+  }
+  const bool mine = lane < a.top_k && ((used >> lane) & 1u);
+  const int bl = mine ? bv : 0;
+  const int pages = mine ? pall : 0;
   const float c2 = a.sm_scale * kLog2e;
   const T* __restrict__ qp = static_cast<const T*>(a.q) + ((size_t)s * a.h_q + r * G) * D;
   Frag<T> qf[D / 32];
@@ -750,7 +758,10 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   while (u < n_units) {
     int un = u + step;
     while (un < n_units && !((used >> (un >> 2)) & 1u)) un += step;
-    if (un < n_units) kd_load_unit<D, TC>(nxt, a, pages, r, un);
+    // unconditional, so the wait before the math below covers the current
+    // unit only; past the last unit it reloads the current one (an L2 hit)
+    kd_load_unit<D, TC>(nxt, a, pages, r, un < n_units ? un : u);
+    MSA_SCHED_FENCE();  // keep the prefetch ahead of the math
     const int b = __builtin_amdgcn_readlane(bl, u >> 2);
     f32x4 sc[2];
 #pragma unroll

@@ -356,56 +356,56 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ki_dim<TC, DIDX>(q4, ks))
                             : zero_frag<T>();
   const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
+  // Lane j holds the physical page of this wave's j-th page (at most 64: a
+  // workgroup covers at most 256 pages), read with one vector load, so no
+  // page's loads wait on a page-table read of their own.
+  const int my_pg = pg_begin + wave + 4 * lane;
+  const int pid = my_pg < pg_end ? pt[my_pg] : 0;
   // For rows of up to 128 bytes the next page's index keys are loaded while
   // the current page is scored (wider rows would not fit two pages).
   constexpr bool kPipe = sizeof(TC) * DIDX <= 128;
   Raw<TC> cur[8][KS], nxt[8][KS];
   int pg = pg_begin + wave;
-  if (kPipe && pg < pg_end) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
-  for (; pg < pg_end; pg += 4) {
-    if (!kPipe) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)scalar_load(pt, pg) * kBlock * DIDX);
+  int j = 0;
+  if (kPipe && pg < pg_end)
+    ki_load_page<TC, DIDX>(cur, k_idx + (size_t)__builtin_amdgcn_readlane(pid, 0) * kBlock * DIDX);
+  for (; pg < pg_end; pg += 4, ++j) {
+    if (!kPipe) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)__builtin_amdgcn_readlane(pid, j) * kBlock * DIDX);
     if (kPipe && pg + 4 < pg_end)
-      ki_load_page<TC, DIDX>(nxt, k_idx + (size_t)scalar_load(pt, pg + 4) * kBlock * DIDX);
+      ki_load_page<TC, DIDX>(nxt, k_idx + (size_t)__builtin_amdgcn_readlane(pid, j + 1) * kBlock * DIDX);
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
-    float m[4] = {kDrop, kDrop, kDrop, kDrop};
+    // keys on the MFMA rows, groups on the columns: acc[v] of lane (q4, l16)
+    // is key kt*16 + 4*q4 + v against group l16, so the pool over the page's
+    // keys is in-lane plus one exchange across the four lane groups
+    float m = kDrop;
     const bool masked = (pg == nb - 1);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16(acc, qa[ks], widen<T, TC>(cur[kt][ks]));
-      const bool vis = !masked || (pg * kBlock + kt * 16 + l16 <= p);
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, widen<T, TC>(cur[kt][ks]), qa[ks]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
+        const bool vis = !masked || (pg * kBlock + kt * 16 + 4 * q4 + v <= p);
         if constexpr (POOL == 0) {
-          m[v] = fmaxf(m[v], vis ? acc[v] : kDrop);
+          m = fmaxf(m, vis ? acc[v] : kDrop);
         } else {
-          m[v] += vis ? acc[v] : kDrop;
+          m += vis ? acc[v] : kDrop;
         }
       }
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        if constexpr (POOL == 0) {
-          m[v] = fmaxf(m[v], __shfl_xor(m[v], off, 64));
-        } else {
-          m[v] += __shfl_xor(m[v], off, 64);
-        }
-      }
+    if constexpr (POOL == 0) {
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+    } else {
+      m += __shfl_xor(m, 16, 64);
+      m += __shfl_xor(m, 32, 64);
     }
     // mean-pool: the page's visible keys (all 128 but on the last page)
     const float inv_cnt = POOL == 0 ? 1.0f : 1.0f / (float)(masked ? p - pg * kBlock + 1 : kBlock);
-    if (l16 == 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int g = 4 * q4 + v;
-        if (g < a.h_kv)
-          a.scores[((size_t)s * a.h_kv + g) * a.max_pages + pg] =
-              POOL == 0 ? m[v] * a.idx_scale : m[v] * a.idx_scale * inv_cnt;
-      }
-    }
+    if (q4 == 0 && l16 < a.h_kv)
+      a.scores[((size_t)s * a.h_kv + l16) * a.max_pages + pg] =
+          POOL == 0 ? m * a.idx_scale : m * a.idx_scale * inv_cnt;
     if (kPipe) {
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt)
