@@ -161,6 +161,61 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
     }
 }
 
+// The same two steps with the counters in LDS: one workgroup per (window,
+// group), whose rows only ever touch that (window, group)'s cells.  Global
+// atomics on hot cells (every token of a query block lists its own block)
+// serialise; LDS atomics do not leave the CU.  Used while a window's blocks
+// fit in LDS.
+constexpr int kSchedLdsBlocks = 16384;
+
+// Slot vetting of a row as in used_slots, on a register copy of the row read
+// with independent loads.
+__device__ __forceinline__ uint32_t row_used(const int32_t* br, int top_k, int diag, int (&b)[kMaxTopK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) b[j] = br[min(j, top_k - 1)];
+  uint32_t m = 0;
+  int prev = -1;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < top_k && b[j] > prev && b[j] <= diag) {
+      m |= 1u << j;
+      prev = b[j];
+    }
+  return m;
+}
+
+__global__ __launch_bounds__(256) void ks_count_lds_kernel(SchedArgs a) {
+  extern __shared__ int cnt[];  // [n_blocks]
+  const int w = blockIdx.x, r = blockIdx.y;
+  for (int b = threadIdx.x; b < a.n_blocks; b += 256) cnt[b] = 0;
+  __syncthreads();
+  const int i1 = min((w + 1) * a.window, a.n_q);
+  for (int i = w * a.window + threadIdx.x; i < i1; i += 256) {
+    int b[kMaxTopK];
+    const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (m & (1u << j)) atomicAdd(&cnt[b[j]], 1);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.n_blocks; b += 256) a.count[cell_key(w, r, b, a.n_blocks, a.h_kv)] = cnt[b];
+}
+
+__global__ __launch_bounds__(256) void ks_scatter_lds_kernel(SchedArgs a) {
+  extern __shared__ int fill[];  // [n_blocks] next free entry of each cell
+  const int w = blockIdx.x, r = blockIdx.y;
+  for (int b = threadIdx.x; b < a.n_blocks; b += 256) fill[b] = a.cell_off[cell_key(w, r, b, a.n_blocks, a.h_kv)];
+  __syncthreads();
+  const int i1 = min((w + 1) * a.window, a.n_q);
+  for (int i = w * a.window + threadIdx.x; i < i1; i += 256) {
+    int b[kMaxTopK];
+    const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (m & (1u << j)) a.entries[atomicAdd(&fill[b[j]], 1)] = (i << 4) | j;
+  }
+}
+
 __global__ void ks_items_kernel(SchedArgs a) {
   const int64_t cell = blockIdx.x * 256ll + threadIdx.x;
   if (cell >= a.n_cells) return;
@@ -1023,6 +1078,9 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
                        st, s);
     hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
     hipLaunchKernelGGL(ks_bits_count_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
+  } else if (pl.n_blocks <= kSchedLdsBlocks) {
+    hipLaunchKernelGGL(ks_count_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
+                       (size_t)pl.n_blocks * 4, st, s);
   } else {
     hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
     hipLaunchKernelGGL(ks_count_kernel, dim3(row_blocks), dim3(256), 0, st, s);
@@ -1032,6 +1090,9 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
   if (s.bitmap)
     hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
+  else if (pl.n_blocks <= kSchedLdsBlocks)
+    hipLaunchKernelGGL(ks_scatter_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
+                       (size_t)pl.n_blocks * 4, st, s);
   else
     hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);
   hipLaunchKernelGGL(ks_items_kernel, dim3(cell_blocks), dim3(256), 0, st, s);

@@ -286,13 +286,27 @@ __global__ __launch_bounds__(256) void ki_merge_kernel(KiPrefillArgs a) {
   uint64_t keys[kMaxTopK];
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
-  const uint64_t* src = a.part_keys + (size_t)row * a.n_chunks * kMaxTopK;
+  // A chunk's list (128 bytes) is read with 8 independent 16-byte loads, and
+  // the next chunk's while the current one is inserted (the load is issued
+  // unconditionally, the last chunk again at the end, so that the compiler's
+  // wait before the inserts covers the current chunk only).
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  const u64x2* src = reinterpret_cast<const u64x2*>(a.part_keys + (size_t)row * a.n_chunks * kMaxTopK);
+  u64x2 cur[kMaxTopK / 2], nxt[kMaxTopK / 2];
+#pragma unroll
+  for (int q = 0; q < kMaxTopK / 2; ++q) cur[q] = src[q];
   for (int c = 0; c < nch; ++c) {
+    const int cn = min(c + 1, nch - 1);
+#pragma unroll
+    for (int q = 0; q < kMaxTopK / 2; ++q) nxt[q] = src[cn * (kMaxTopK / 2) + q];
+#pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) {
-      const uint64_t k = src[c * kMaxTopK + s];
+      const uint64_t k = cur[s >> 1][s & 1];
       if (k <= keys[kMaxTopK - 1]) break;  // lists are descending
       list_insert(keys, k);
     }
+#pragma unroll
+    for (int q = 0; q < kMaxTopK / 2; ++q) cur[q] = nxt[q];
   }
   const float dscore = (a.need_diag && a.force_local) ? a.part_diag[row] : -__builtin_inff();
   const int n_take = a.top_k - (a.force_local ? 1 : 0);
