@@ -130,12 +130,14 @@ COPY_BYTES = 1 << 30
 # kernels of each ABI call (substring of the kernel name)
 CALL_KERNELS = {
     "index_prefill": ["ki_prefill_kernel", "ki_merge_kernel"],
-    "sparse_prefill": ["ks_zero_kernel", "ks_count_kernel", "ks_scan_a_kernel", "ks_scan_b_kernel",
-                       "ks_scan_c_kernel", "ks_scatter_kernel", "ks_items_kernel", "kp_kernel", "km_kernel"],
+    # name prefixes: the schedule counts and scatters in LDS (ks_*_lds_kernel) or
+    # with global atomics (ks_zero + ks_count/ks_scatter) depending on the size
+    "sparse_prefill": ["ks_zero", "ks_count", "ks_scan_a", "ks_scan_b", "ks_scan_c", "ks_scatter", "ks_items",
+                       "kp_kernel", "km_kernel"],
     "index_decode": ["ki_decode_scan_kernel", "ki_decode_select_kernel"],
     "sparse_decode": ["kd_kernel", "kd_merge_kernel"],
 }
-CALL_FIRST = {"index_prefill": "ki_prefill_kernel", "sparse_prefill": "ks_zero_kernel",
+CALL_FIRST = {"index_prefill": "ki_prefill_kernel", "sparse_prefill": "ks_count",
               "index_decode": "ki_decode_scan_kernel", "sparse_decode": "kd_kernel"}
 
 

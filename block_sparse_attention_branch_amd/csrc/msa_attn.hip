@@ -1026,7 +1026,7 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   // `cell_tokens` tokens on average (bounded by a hard memory cap).
   const size_t budget = (size_t)env_int("MSA_PARTIAL_BUDGET_MB", 128) << 20;
   const size_t cap = (size_t)env_int("MSA_PARTIAL_CAP_MB", 4096) << 20;
-  const int64_t cell_tokens = env_int("MSA_CELL_TOKENS", 32);
+  const int64_t cell_tokens = env_int("MSA_CELL_TOKENS", 40);
   const int64_t blocks_seen = ((int64_t)q_start + n_q - 1) / kBlock + 1;
   int64_t w = (int64_t)(budget / per_token);
   const int64_t w_occ = (cell_tokens * blocks_seen + std::max(1, top_k - 1) - 1) / std::max(1, top_k - 1);
