@@ -1071,6 +1071,9 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   s.bitmap = pl.bitmap_words > 0 ? reinterpret_cast<uint32_t*>(ws + pl.off_bitmap) : nullptr;
   const int64_t rows = (int64_t)a.n_q * a.h_kv;
   const unsigned row_blocks = (unsigned)((rows + 255) / 256);
+  // LDS counters while a window's blocks fit (the threshold can be lowered
+  // through the environment, which is how the global-atomic path is tested)
+  const bool lds_sched = pl.n_blocks <= std::min(kSchedLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kSchedLdsBlocks));
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
   if (s.bitmap) {  // ordered: bitmap -> counts -> offsets -> token lists in order
     const int64_t nw = pl.n_cells * s.words;
@@ -1078,7 +1081,7 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
                        st, s);
     hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
     hipLaunchKernelGGL(ks_bits_count_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
-  } else if (pl.n_blocks <= kSchedLdsBlocks) {
+  } else if (lds_sched) {
     hipLaunchKernelGGL(ks_count_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
                        (size_t)pl.n_blocks * 4, st, s);
   } else {
@@ -1090,7 +1093,7 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   hipLaunchKernelGGL(ks_scan_c_kernel, dim3(s.n_scan_tiles), dim3(256), 0, st, s);
   if (s.bitmap)
     hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
-  else if (pl.n_blocks <= kSchedLdsBlocks)
+  else if (lds_sched)
     hipLaunchKernelGGL(ks_scatter_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
                        (size_t)pl.n_blocks * 4, st, s);
   else

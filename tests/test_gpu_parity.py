@@ -359,6 +359,33 @@ def test_prefill_far_apart_scores_and_determinism():
     assert torch.equal(a, b)
 
 
+def test_prefill_schedule_lds_and_global_counters_agree(monkeypatch):
+    # The schedule counts and scatters each (window, group) in LDS while its
+    # blocks fit there, else with global atomics; MSA_SCHED_LDS_BLOCKS=0 forces
+    # the latter.  Each (token, block) partial is computed the same way whatever
+    # item holds it, so the outputs are bitwise equal.
+    msa = _msa()
+    for shape, n_kv, n_q, seed in ((MODEL_SHAPE, 1800, 1800, 54), (HeadShape(32, 2, 128, 64, 8), 2500, 700, 55)):
+        inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV)
+        q_start = inp["q_start"]
+        ids, _, _ = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q_start, shape.top_k)
+        bidx = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+        outs = []
+        for thr in (None, "0"):
+            if thr is None:
+                monkeypatch.delenv("MSA_SCHED_LDS_BLOCKS", raising=False)
+            else:
+                monkeypatch.setenv("MSA_SCHED_LDS_BLOCKS", thr)
+            _say("prefill schedule", "lds" if thr is None else "global atomics", shape, n_kv, n_q, seed)
+            o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
+            torch.cuda.synchronize()
+            outs.append((o, lse))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+        o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start)
+        compare_out(outs[1][0], o_ref, torch.bfloat16)
+        compare_lse(outs[1][1], lse_ref, torch.bfloat16)
+
+
 # ------------------------------------------------------------------ decode
 
 def _cache_host(t):
