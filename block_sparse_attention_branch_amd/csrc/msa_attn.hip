@@ -44,11 +44,12 @@ __global__ void ks_count_kernel(SchedArgs a) {
   if (row >= (int64_t)a.n_q * a.h_kv) return;
   const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
   const int diag = (a.q_start + i) >> 7;
-  const int32_t* br = a.block_idx + row * a.top_k;
-  const uint32_t m = used_slots(br, a.top_k, diag);
+  int b[kMaxTopK];
+  const uint32_t m = row_used(a.block_idx + row * a.top_k, a.top_k, diag, b);
   const int w = i / a.window;
-  for (int j = 0; j < a.top_k; ++j)
-    if (m & (1u << j)) atomicAdd(&a.count[cell_key(w, r, br[j], a.n_blocks, a.h_kv)], 1);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (m & (1u << j)) atomicAdd(&a.count[cell_key(w, r, b[j], a.n_blocks, a.h_kv)], 1);
 }
 
 __device__ __forceinline__ void block_excl_scan2(int& x, int& y, int* sh) {
@@ -150,12 +151,13 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
   if (row >= (int64_t)a.n_q * a.h_kv) return;
   const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
   const int diag = (a.q_start + i) >> 7;
-  const int32_t* br = a.block_idx + row * a.top_k;
-  const uint32_t m = used_slots(br, a.top_k, diag);
+  int b[kMaxTopK];
+  const uint32_t m = row_used(a.block_idx + row * a.top_k, a.top_k, diag, b);
   const int w = i / a.window;
-  for (int j = 0; j < a.top_k; ++j)
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
     if (m & (1u << j)) {
-      const int64_t cell = cell_key(w, r, br[j], a.n_blocks, a.h_kv);
+      const int64_t cell = cell_key(w, r, b[j], a.n_blocks, a.h_kv);
       const int pos = a.cell_off[cell] + atomicAdd(&a.fill[cell], 1);
       a.entries[pos] = (i << 4) | j;
     }
@@ -167,22 +169,6 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
 // serialise; LDS atomics do not leave the CU.  Used while a window's blocks
 // fit in LDS.
 constexpr int kSchedLdsBlocks = 16384;
-
-// Slot vetting of a row as in used_slots, on a register copy of the row read
-// with independent loads.
-__device__ __forceinline__ uint32_t row_used(const int32_t* br, int top_k, int diag, int (&b)[kMaxTopK]) {
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) b[j] = br[min(j, top_k - 1)];
-  uint32_t m = 0;
-  int prev = -1;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < top_k && b[j] > prev && b[j] <= diag) {
-      m |= 1u << j;
-      prev = b[j];
-    }
-  return m;
-}
 
 __global__ __launch_bounds__(256) void ks_count_lds_kernel(SchedArgs a) {
   extern __shared__ int cnt[];  // [n_blocks]
@@ -244,12 +230,13 @@ __global__ void ks_bits_set_kernel(SchedArgs a) {
   if (row >= (int64_t)a.n_q * a.h_kv) return;
   const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
   const int diag = (a.q_start + i) >> 7;
-  const int32_t* br = a.block_idx + row * a.top_k;
-  const uint32_t m = used_slots(br, a.top_k, diag);
+  int b[kMaxTopK];
+  const uint32_t m = row_used(a.block_idx + row * a.top_k, a.top_k, diag, b);
   const int w = i / a.window, il = i - w * a.window;
-  for (int j = 0; j < a.top_k; ++j)
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
     if (m & (1u << j)) {
-      const int64_t cell = cell_key(w, r, br[j], a.n_blocks, a.h_kv);
+      const int64_t cell = cell_key(w, r, b[j], a.n_blocks, a.h_kv);
       atomicOr(&a.bitmap[cell * a.words + (il >> 5)], 1u << (il & 31));
     }
 }
@@ -502,10 +489,23 @@ struct KmArgs {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
   constexpr int DC = D / 8;
+  // the (max, sum) of every (pair, head, slot) of the workgroup, read once
+  // ([pair][head][slot]); each is needed by the DC threads of its head
+  __shared__ float2 ml_s[256 * kMaxTopK / DC];
   const int G = a.group;
   const int per_pair = G * DC;                 // one 8-value chunk per thread
   const int sub = threadIdx.x / per_pair;
   const int c = threadIdx.x % per_pair;        // chunk index within a (token, slot) region
+  for (int e = threadIdx.x; e < a.pairs_per_wg * G * kMaxTopK; e += 256) {
+    const int j = e % kMaxTopK, gg = (e / kMaxTopK) % G, sb = e / (kMaxTopK * G);
+    const int64_t pr = (int64_t)blockIdx.x * a.pairs_per_wg + sb;
+    const int il2 = (int)(pr / a.h_kv), r2 = (int)(pr % a.h_kv);
+    float2 v = float2{-__builtin_inff(), 0.0f};
+    if (il2 < a.window && a.w * a.window + il2 < a.n_q && j < a.top_k)
+      v = a.part_ml[(((size_t)il2 * a.h_kv + r2) * a.top_k + j) * G + gg];
+    ml_s[e] = v;
+  }
+  __syncthreads();
   if (sub >= a.pairs_per_wg) return;
   const int64_t pair = (int64_t)blockIdx.x * a.pairs_per_wg + sub;  // (i_local, r)
   const int il = (int)(pair / a.h_kv), r = (int)(pair % a.h_kv);
@@ -514,19 +514,19 @@ __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
   const int g = c % G, half = (c / G) & 1, p = (c / (2 * G)) & 1, dt = c / (4 * G);
   const int d0 = dt * 32 + 16 * p + 4 * half;  // chunk holds d0..d0+3 and d0+8..d0+11
   const int diag = (a.q_start + i) >> 7;
-  const int32_t* br = a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k;
-  const uint32_t used = used_slots(br, a.top_k, diag);
+  int bl[kMaxTopK];
+  const uint32_t used = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, diag, bl);
   const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
   const T* po = static_cast<const T*>(a.part_o);
+  const float2* mls = ml_s + (sub * G + g) * kMaxTopK;
   float2 ml[kMaxTopK];
   Frag<T> x[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     const bool u = (used >> j) & 1u;
     const size_t sj = slot0 + (u ? j : 0);
-    ml[j] = a.part_ml[sj * G + g];
     x[j] = load_frag<T>(po + (sj * G * D + (size_t)c * 8));
-    if (!u) ml[j] = float2{-__builtin_inff(), 0.0f};
+    ml[j] = u ? mls[j] : float2{-__builtin_inff(), 0.0f};
   }
   float mx = -__builtin_inff();
 #pragma unroll

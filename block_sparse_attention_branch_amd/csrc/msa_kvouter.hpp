@@ -368,17 +368,27 @@ __device__ __forceinline__ void cell_rb(int64_t k, int nbp, int h_kv, int& r, in
   }
 }
 
-__device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
+// The slots of a block list that count: an entry is used when it is above
+// every earlier used entry and not past the row's own block (so duplicates,
+// out-of-order entries, -1 padding and future blocks are skipped).  The row is
+// read into registers with independent loads (clamped index) before the
+// serial vetting, so a thread waits for one load latency, not top_k of them.
+__device__ __forceinline__ uint32_t row_used(const int32_t* row, int top_k, int diag, int (&b)[kMaxTopK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) b[j] = row[min(j, top_k - 1)];
   uint32_t m = 0;
   int prev = -1;
-  for (int j = 0; j < top_k; ++j) {
-    const int b = row[j];
-    if (b > prev && b <= diag) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < top_k && b[j] > prev && b[j] <= diag) {
       m |= 1u << j;
-      prev = b;
+      prev = b[j];
     }
-  }
   return m;
+}
+__device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
+  int b[kMaxTopK];
+  return row_used(row, top_k, diag, b);
 }
 
 constexpr int kScanPerThread = 16;
