@@ -241,6 +241,35 @@ __global__ void ks_bits_set_kernel(SchedArgs a) {
     }
 }
 
+// The same with the bits of 256 consecutive tokens (8 words per cell) built in
+// LDS: workgroup (window, token tile, group) owns those words of every cell
+// of its group, so it writes them out whole, without atomics (the tokens of a
+// query block all set bits in the same word of their own block's cell).
+constexpr int kBitsLdsBlocks = 2048;
+
+__global__ __launch_bounds__(256) void ks_bits_set_lds_kernel(SchedArgs a) {
+  extern __shared__ uint32_t lb[];  // [n_blocks][8]
+  const int tiles = (a.window + 255) / 256;
+  const int w = blockIdx.x / tiles, t = blockIdx.x % tiles, r = blockIdx.y;
+  if (blockIdx.x == 0 && r == 0 && threadIdx.x < 2) a.fill[threadIdx.x] = 0;  // work-queue heads of the consumers
+  for (int x = threadIdx.x; x < a.n_blocks * 8; x += 256) lb[x] = 0u;
+  __syncthreads();
+  const int il = t * 256 + threadIdx.x, i = w * a.window + il;
+  if (il < a.window && i < a.n_q) {
+    int b[kMaxTopK];
+    const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (m & (1u << j)) atomicOr(&lb[b[j] * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+  }
+  __syncthreads();
+  const int nw = min(8, a.words - 8 * t);
+  for (int x = threadIdx.x; x < a.n_blocks * 8; x += 256) {
+    const int bb = x >> 3, k = x & 7;
+    if (k < nw) a.bitmap[cell_key(w, r, bb, a.n_blocks, a.h_kv) * a.words + 8 * t + k] = lb[x];
+  }
+}
+
 // Ordered mode's cell sizes: the popcount of each cell's bitmap (no atomics
 // on a few hot counters).
 __global__ __launch_bounds__(256) void ks_bits_count_kernel(SchedArgs a) {
@@ -1076,10 +1105,16 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   const bool lds_sched = pl.n_blocks <= std::min(kSchedLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kSchedLdsBlocks));
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
   if (s.bitmap) {  // ordered: bitmap -> counts -> offsets -> token lists in order
-    const int64_t nw = pl.n_cells * s.words;
-    hipLaunchKernelGGL(ks_bits_zero_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 8192)), dim3(256), 0,
-                       st, s);
-    hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+    if (pl.n_blocks <= std::min(kBitsLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kBitsLdsBlocks))) {
+      const unsigned tiles = (unsigned)((pl.window + 255) / 256);
+      hipLaunchKernelGGL(ks_bits_set_lds_kernel, dim3((unsigned)pl.n_windows * tiles, (unsigned)a.h_kv), dim3(256),
+                         (size_t)pl.n_blocks * 8 * 4, st, s);
+    } else {
+      const int64_t nw = pl.n_cells * s.words;
+      hipLaunchKernelGGL(ks_bits_zero_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 8192)), dim3(256),
+                         0, st, s);
+      hipLaunchKernelGGL(ks_bits_set_kernel, dim3(row_blocks), dim3(256), 0, st, s);
+    }
     hipLaunchKernelGGL(ks_bits_count_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
   } else if (lds_sched) {
     hipLaunchKernelGGL(ks_count_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),

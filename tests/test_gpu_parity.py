@@ -386,6 +386,36 @@ def test_prefill_schedule_lds_and_global_counters_agree(monkeypatch):
         compare_lse(outs[1][1], lse_ref, torch.bfloat16)
 
 
+def test_backward_bitmap_lds_and_global_agree(monkeypatch):
+    # The ordered schedule of the dK/dV pass builds its per-cell token bitmaps
+    # in LDS (256 tokens per workgroup) while a window's blocks fit there, else
+    # with global atomics; both give the same bits, so the gradients are
+    # bitwise equal (and match the oracle).
+    msa = _msa()
+    shape = MODEL_SHAPE
+    inp = gen_prefill(1700, shape, dtype=torch.bfloat16, seed=56, device=DEV)
+    ids, _, _ = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), 0, shape.top_k)
+    bidx = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, with_lse=True)
+    d_o = torch.randn(o.shape, generator=torch.Generator(device="cpu").manual_seed(57)).to(torch.bfloat16).to(DEV)
+    grads = []
+    for thr in (None, "0"):
+        if thr is None:
+            monkeypatch.delenv("MSA_SCHED_LDS_BLOCKS", raising=False)
+        else:
+            monkeypatch.setenv("MSA_SCHED_LDS_BLOCKS", thr)
+        _say("backward bitmaps", "lds" if thr is None else "global atomics")
+        grads.append(msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o))
+        torch.cuda.synchronize()
+    for a, b in zip(grads[0], grads[1]):
+        assert torch.equal(a, b)
+    dq_ref, dk_ref, dv_ref = orc.sparse_attention_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, 0,
+                                                           np64(d_o))
+    compare_grad(grads[0][0], dq_ref, "dq")
+    compare_grad(grads[0][1], dk_ref, "dk")
+    compare_grad(grads[0][2], dv_ref, "dv")
+
+
 # ------------------------------------------------------------------ decode
 
 def _cache_host(t):
