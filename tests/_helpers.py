@@ -72,10 +72,13 @@ def compare_out(o_gpu, o_ref, dtype, what="o"):
 
 
 def compare_lse(l_gpu, l_ref, dtype):
+    """lse within the tolerance; rows with no visible key must be -inf on both sides."""
     tol = TOL[dtype]["lse"]
     lg = np64(l_gpu)
     lr = np.asarray(l_ref, np.float64)
-    err = np.abs(lg - lr)
+    empty = np.isneginf(lr)
+    assert np.array_equal(np.isneginf(lg), empty), "lse: -inf rows differ"
+    err = np.abs(np.where(empty, 0.0, lg - lr))
     assert float(err.max()) <= tol, f"lse: max-abs {float(err.max()):.3e} > {tol}"
     return float(err.max())
 

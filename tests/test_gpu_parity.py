@@ -416,6 +416,58 @@ def test_backward_bitmap_lds_and_global_agree(monkeypatch):
     compare_grad(grads[0][2], dv_ref, "dv")
 
 
+def _irregular_lists(n_rows, h_kv, top_k, diags, seed):
+    """Ascending block lists within the ABI's contract but unlike the index
+    branch's output: repeated entries, -1 between entries, blocks past the
+    row's own block at the end, short lists, and some empty rows."""
+    rng = np.random.default_rng(seed)
+    out = np.full((n_rows, h_kv, top_k), -1, dtype=np.int32)
+    for t in range(n_rows):
+        d = int(diags[t])
+        for r in range(h_kv):
+            kind = rng.integers(0, 6)
+            if kind == 0:
+                continue                                  # empty row: o = 0, lse = -inf
+            m = int(rng.integers(1, top_k + 1))
+            picks = np.sort(rng.integers(0, d + 3, size=m))  # may repeat, may pass d
+            row = []
+            for b in picks:
+                row.append(int(b))
+                if rng.random() < 0.2 and len(row) < top_k:
+                    row.append(-1 if rng.random() < 0.5 else int(b))   # a gap or a repeat
+            out[t, r, :min(top_k, len(row))] = row[:top_k]
+    return out
+
+
+def test_prefill_and_decode_irregular_block_lists():
+    msa = _msa()
+    shape = MODEL_SHAPE
+    inp = gen_prefill(1500, shape, n_q=1100, dtype=torch.bfloat16, seed=58, device=DEV)
+    q_start = inp["q_start"]
+    ids = _irregular_lists(1100, shape.h_kv, shape.top_k, (q_start + np.arange(1100)) // 128, 59)
+    _say("irregular block lists: prefill")
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], torch.from_numpy(ids).to(DEV), q_start=q_start,
+                                with_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start)
+    compare_out(o, o_ref, torch.bfloat16)
+    compare_lse(lse, lse_ref, torch.bfloat16)
+    assert np.all(np.isneginf(lse.cpu().numpy()[np.repeat(np.all(ids < 0, axis=2), shape.h_q // shape.h_kv, 1)]))
+
+    seq_lens = [3000, 129, 777, 4096, 1, 2500]
+    dec = gen_decode_paged(len(seq_lens), max(seq_lens), shape, seed=60, device=DEV, seq_lens=seq_lens)
+    dids = _irregular_lists(len(seq_lens), shape.h_kv, shape.top_k, (np.asarray(seq_lens) - 1) // 128, 61)
+    _say("irregular block lists: decode")
+    q = dec["q"][0].contiguous()
+    od, ld = msa.sparse_decode(q, dec["k_pages"], dec["v_pages"], dec["page_table"], dec["seq_lens"],
+                               torch.from_numpy(dids).to(DEV), with_lse=True)
+    torch.cuda.synchronize()
+    od_ref, ld_ref = orc.sparse_decode(np64(q), _cache_host(dec["k_pages"]), _cache_host(dec["v_pages"]),
+                                       dec["page_table"].cpu().numpy(), seq_lens, dids)
+    compare_out(od, od_ref, torch.bfloat16)
+    compare_lse(ld, ld_ref, torch.bfloat16)
+
+
 # ------------------------------------------------------------------ decode
 
 def _cache_host(t):
