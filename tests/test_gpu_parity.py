@@ -453,6 +453,17 @@ def test_prefill_and_decode_irregular_block_lists():
     compare_out(o, o_ref, torch.bfloat16)
     compare_lse(lse, lse_ref, torch.bfloat16)
     assert np.all(np.isneginf(lse.cpu().numpy()[np.repeat(np.all(ids < 0, axis=2), shape.h_q // shape.h_kv, 1)]))
+    # the training path on the same lists (empty rows get dq = 0)
+    d_o = torch.randn(o.shape, generator=torch.Generator(device="cpu").manual_seed(62)).to(torch.bfloat16).to(DEV)
+    _say("irregular block lists: backward")
+    dq, dk, dv = msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], torch.from_numpy(ids).to(DEV), o, lse, d_o,
+                                             q_start=q_start)
+    torch.cuda.synchronize()
+    rq, rk, rv = orc.sparse_attention_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start,
+                                               np64(d_o))
+    compare_grad(dq, rq, "dq")
+    compare_grad(dk, rk, "dk")
+    compare_grad(dv, rv, "dv")
 
     seq_lens = [3000, 129, 777, 4096, 1, 2500]
     dec = gen_decode_paged(len(seq_lens), max(seq_lens), shape, seed=60, device=DEV, seq_lens=seq_lens)
