@@ -78,7 +78,8 @@ def compare_lse(l_gpu, l_ref, dtype):
     lr = np.asarray(l_ref, np.float64)
     empty = np.isneginf(lr)
     assert np.array_equal(np.isneginf(lg), empty), "lse: -inf rows differ"
-    err = np.abs(np.where(empty, 0.0, lg - lr))
+    err = np.zeros_like(lr)
+    err[~empty] = np.abs(lg[~empty] - lr[~empty])
     assert float(err.max()) <= tol, f"lse: max-abs {float(err.max()):.3e} > {tol}"
     return float(err.max())
 
