@@ -170,13 +170,19 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
 // fit in LDS.
 constexpr int kSchedLdsBlocks = 16384;
 
-__global__ __launch_bounds__(256) void ks_count_lds_kernel(SchedArgs a) {
-  extern __shared__ int cnt[];  // [n_blocks]
-  const int w = blockIdx.x, r = blockIdx.y;
+// Workgroup (window w, slice s, group r) takes tokens [t0, t1) of window w.
+__device__ __forceinline__ void ks_slice(const SchedArgs& a, int& w, int& t0, int& t1) {
+  w = blockIdx.x / a.split;
+  const int s = blockIdx.x % a.split, per = (a.window + a.split - 1) / a.split;
+  t0 = w * a.window + s * per;
+  t1 = min(min(t0 + per, (w + 1) * a.window), a.n_q);
+}
+
+// Counts a slice's entries per block of group r into cnt (LDS, zeroed here).
+__device__ __forceinline__ void ks_slice_counts(const SchedArgs& a, int r, int t0, int t1, int* cnt) {
   for (int b = threadIdx.x; b < a.n_blocks; b += 256) cnt[b] = 0;
   __syncthreads();
-  const int i1 = min((w + 1) * a.window, a.n_q);
-  for (int i = w * a.window + threadIdx.x; i < i1; i += 256) {
+  for (int i = t0 + threadIdx.x; i < t1; i += 256) {
     int b[kMaxTopK];
     const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
 #pragma unroll
@@ -184,21 +190,55 @@ __global__ __launch_bounds__(256) void ks_count_lds_kernel(SchedArgs a) {
       if (m & (1u << j)) atomicAdd(&cnt[b[j]], 1);
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < a.n_blocks; b += 256) a.count[cell_key(w, r, b, a.n_blocks, a.h_kv)] = cnt[b];
 }
 
+// With one slice per (window, group) the counts are stored whole; with more,
+// each slice adds its nonzero counts (count zeroed beforehand): one global
+// atomic per (slice, cell) instead of one per entry.
+__global__ __launch_bounds__(256) void ks_count_lds_kernel(SchedArgs a) {
+  extern __shared__ int cnt[];  // [n_blocks]
+  const int r = blockIdx.y;
+  int w, t0, t1;
+  ks_slice(a, w, t0, t1);
+  ks_slice_counts(a, r, t0, t1, cnt);
+  for (int b = threadIdx.x; b < a.n_blocks; b += 256) {
+    const int64_t cell = cell_key(w, r, b, a.n_blocks, a.h_kv);
+    if (a.split == 1)
+      a.count[cell] = cnt[b];
+    else if (cnt[b] > 0)
+      atomicAdd(&a.count[cell], cnt[b]);
+  }
+}
+
+// Scatter: a slice reserves a contiguous run of each cell's entries (one
+// global atomic on fill per nonzero cell; fill zeroed beforehand when split),
+// then places its entries with LDS atomics.  The order of the slices' runs
+// within a cell depends on timing; no result depends on that order.
 __global__ __launch_bounds__(256) void ks_scatter_lds_kernel(SchedArgs a) {
-  extern __shared__ int fill[];  // [n_blocks] next free entry of each cell
-  const int w = blockIdx.x, r = blockIdx.y;
-  for (int b = threadIdx.x; b < a.n_blocks; b += 256) fill[b] = a.cell_off[cell_key(w, r, b, a.n_blocks, a.h_kv)];
-  __syncthreads();
-  const int i1 = min((w + 1) * a.window, a.n_q);
-  for (int i = w * a.window + threadIdx.x; i < i1; i += 256) {
+  extern __shared__ int pos[];  // [n_blocks] next free entry of each cell
+  const int r = blockIdx.y;
+  int w, t0, t1;
+  ks_slice(a, w, t0, t1);
+  if (a.split == 1) {
+    for (int b = threadIdx.x; b < a.n_blocks; b += 256) pos[b] = a.cell_off[cell_key(w, r, b, a.n_blocks, a.h_kv)];
+    __syncthreads();
+  } else {
+    ks_slice_counts(a, r, t0, t1, pos);
+    for (int b = threadIdx.x; b < a.n_blocks; b += 256) {
+      const int n = pos[b];
+      if (n > 0) {
+        const int64_t cell = cell_key(w, r, b, a.n_blocks, a.h_kv);
+        pos[b] = a.cell_off[cell] + atomicAdd(&a.fill[cell], n);
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = t0 + threadIdx.x; i < t1; i += 256) {
     int b[kMaxTopK];
     const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
-      if (m & (1u << j)) a.entries[atomicAdd(&fill[b[j]], 1)] = (i << 4) | j;
+      if (m & (1u << j)) a.entries[atomicAdd(&pos[b[j]], 1)] = (i << 4) | j;
   }
 }
 
@@ -552,9 +592,13 @@ __global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
   Frag<T> x[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
+    // every load is issued (an unused slot reads slot 0 again), but an unused
+    // slot's values are zeroed: a weight of 0 must not meet stale workspace
+    // contents (0 * inf), e.g. in a row with no used slot at all
     const bool u = (used >> j) & 1u;
     const size_t sj = slot0 + (u ? j : 0);
-    x[j] = load_frag<T>(po + (sj * G * D + (size_t)c * 8));
+    const Frag<T> xl = load_frag<T>(po + (sj * G * D + (size_t)c * 8));
+    x[j] = u ? xl : zero_frag<T>();
     ml[j] = u ? mls[j] : float2{-__builtin_inff(), 0.0f};
   }
   float mx = -__builtin_inff();
@@ -1103,6 +1147,15 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   // LDS counters while a window's blocks fit (the threshold can be lowered
   // through the environment, which is how the global-atomic path is tested)
   const bool lds_sched = pl.n_blocks <= std::min(kSchedLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kSchedLdsBlocks));
+  // With few (window, group) pairs (one long window, as in a chunked prefill
+  // at long context) each is split into token slices, enough to fill the
+  // chip, of at least 128 tokens; otherwise one workgroup per pair (slices
+  // would count every entry twice and add global atomics)
+  {
+    const int64_t wg = (int64_t)pl.n_windows * a.h_kv;
+    const int64_t want = wg * 2 < num_cus() ? (2LL * num_cus() + wg - 1) / wg : 1;
+    s.split = (int32_t)std::max<int64_t>(1, std::min<int64_t>(want, pl.window / 128));
+  }
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
   if (s.bitmap) {  // ordered: bitmap -> counts -> offsets -> token lists in order
     if (pl.n_blocks <= std::min(kBitsLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kBitsLdsBlocks))) {
@@ -1117,7 +1170,9 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
     }
     hipLaunchKernelGGL(ks_bits_count_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
   } else if (lds_sched) {
-    hipLaunchKernelGGL(ks_count_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
+    if (s.split > 1)
+      hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(ks_count_lds_kernel, dim3((unsigned)(pl.n_windows * s.split), (unsigned)a.h_kv), dim3(256),
                        (size_t)pl.n_blocks * 4, st, s);
   } else {
     hipLaunchKernelGGL(ks_zero_kernel, dim3(std::min<unsigned>(cell_blocks, 4096u)), dim3(256), 0, st, s);
@@ -1129,7 +1184,7 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   if (s.bitmap)
     hipLaunchKernelGGL(ks_bits_extract_kernel, dim3((unsigned)pl.n_cells), dim3(256), 0, st, s);
   else if (lds_sched)
-    hipLaunchKernelGGL(ks_scatter_lds_kernel, dim3((unsigned)pl.n_windows, (unsigned)a.h_kv), dim3(256),
+    hipLaunchKernelGGL(ks_scatter_lds_kernel, dim3((unsigned)(pl.n_windows * s.split), (unsigned)a.h_kv), dim3(256),
                        (size_t)pl.n_blocks * 4, st, s);
   else
     hipLaunchKernelGGL(ks_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, s);

@@ -325,6 +325,7 @@ struct SchedArgs {
   uint32_t* bitmap;   // ordered mode: [n_cells, words] token bits of each cell; NULL otherwise
                       // (fill[0] and fill[1] are then zeroed as work-queue heads for the consumers)
   int32_t words;      // 32-bit words per cell (window / 32, rounded up)
+  int32_t split;      // LDS count/scatter: workgroups per (window, group), each over a slice of the window's tokens
 };
 
 // Cells are the (window, group, block) token lists.  Within a window they are
