@@ -513,6 +513,55 @@ def _decode_case(shape, seq_lens, seed, n_sets=1, cache_dtype=None):
     compare_lse(lse, lse_ref, torch.bfloat16)
 
 
+def test_decode_step_graph_replays_match_eager():
+    # The decode step (index top-k, then the sparse gather) captured once in a
+    # HIP graph and replayed with new queries and longer sequences written
+    # into the captured buffers between replays (eager work and syncs in
+    # between); every replay must equal the eager calls bitwise.
+    msa = _msa()
+    shape = MODEL_SHAPE
+    seq_lens = [3000, 700, 5000, 129]
+    dec = gen_decode_paged(len(seq_lens), max(seq_lens), shape, seed=63, device=DEV, seq_lens=seq_lens,
+                           extra_tokens=300, n_query_sets=4)
+    B = len(seq_lens)
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    qb = dec["q"][0].clone()
+    qib = dec["q_idx"][0].clone()
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+    mp = dec["page_table"].shape[1]
+    ws_i = torch.empty(msa.workspace_size(msa.OP_INDEX_DECODE, s_idx, batch=B, n_q=1, max_pages=mp),
+                       dtype=torch.uint8, device=DEV)
+    ws_d = torch.empty(max(1, msa.workspace_size(msa.OP_DECODE, s_idx, batch=B, n_q=1)), dtype=torch.uint8,
+                       device=DEV)
+    bidx = torch.empty((B, shape.h_kv, shape.top_k), dtype=torch.int32, device=DEV)
+    o = torch.empty((B, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=DEV)
+
+    def step(q, qi, out_b, out_o):
+        msa.index_topk(qi, dec["k_idx_pages"], top_k=shape.top_k, page_table=dec["page_table"], seq_lens=sl,
+                       out=out_b, workspace=ws_i)
+        msa.sparse_decode(q, dec["k_pages"], dec["v_pages"], dec["page_table"], sl, out_b, out=out_o, workspace=ws_d)
+
+    step(qb, qib, bidx, o)       # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(qb, qib, bidx, o)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        qb.copy_(dec["q"][rep])
+        qib.copy_(dec["q_idx"][rep])
+        sl.add_(37 * rep)                       # the sequences grow between steps
+        torch.cuda.synchronize()
+        _say("decode graph replay", rep, sl.tolist())
+        g.replay()
+        torch.cuda.synchronize()
+        eb = torch.empty_like(bidx)
+        eo = torch.empty_like(o)
+        step(dec["q"][rep].contiguous(), dec["q_idx"][rep].contiguous(), eb, eo)
+        torch.cuda.synchronize()
+        assert torch.equal(bidx, eb) and torch.equal(o, eo), rep
+
+
 def test_decode_mixed_lengths():
     _decode_case(MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049], 20)
 
