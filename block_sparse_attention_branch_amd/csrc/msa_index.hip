@@ -434,71 +434,75 @@ constexpr int kSelectMaxSurvivors = 1024;  // 16 threads x up to 64 candidates e
 // Top-k of one (sequence, group) row of pooled page scores.  Keys are the
 // order-preserving bits of the score with the inverted block id below them,
 // so they are unique and "larger" means better (ties to the lower block).
-//  1) each thread takes the maximum of its candidates; the 16th largest of
-//     the 256 maxima T is a lower bound of the answer: the 16 threads whose
-//     maxima are >= T each hold a key >= T, so the 16 best keys are all >= T;
-//  2) every key >= T survives (only those 16 threads hold any);
+//  1) each thread loads its U candidates (pages tid + 256 u) into registers
+//     and takes their maximum; the 16th largest of the 256 maxima, T, is a
+//     lower bound of the answer: the 16 threads whose maxima are >= T each
+//     hold a key >= T, so the 16 best keys are all >= T.  Every wave finds T
+//     on its own with a bitwise search over the maxima (64 steps of a ballot
+//     count), so no barrier follows;
+//  2) every key >= T survives (only those 16 threads hold any); a thread
+//     counts its survivors in registers and reserves their places with one
+//     LDS atomic;
 //  3) each survivor's rank among the survivors places the best 16 in order.
-// Ranks are counted against values in LDS, so the selection needs no sort
-// and only a few barriers.  The row is read from global memory once, eight
-// independent loads per thread at a time, and kept in LDS for step 2.
-// Copies the row's scores into LDS (U independent loads per thread in
-// flight) and returns this thread's largest key.
 template <int U>
-__device__ __forceinline__ uint64_t select_load_row(const float* sc, int ncand, float* row_s) {
-  uint64_t tmax = 0;
-  for (int b0 = threadIdx.x; b0 < ncand; b0 += 256 * U) {
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = sc[min(b0 + 256 * u, ncand - 1)];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = b0 + 256 * u;
-      if (b < ncand) {
-        row_s[b] = v[u];
-        const uint64_t k = make_key(v[u], b);
-        tmax = k > tmax ? k : tmax;
-      }
-    }
-  }
-  return tmax;
-}
-
 __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
-  __shared__ float row_s[kMaxDecodePages];
   __shared__ uint64_t tm[256];
   __shared__ uint64_t surv[kSelectMaxSurvivors];
   __shared__ uint64_t top[kMaxTopK];
-  __shared__ uint64_t thr_s;
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
   const int L = scalar_load(a.seq_lens, s);
   const int diag = (L - 1) / kBlock;
   const int ncand = min(a.force_local ? diag : diag + 1, a.max_pages);
   const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
 
-  const uint64_t tmax = ncand > 256 * 8 ? select_load_row<32>(sc, ncand, row_s) : select_load_row<8>(sc, ncand, row_s);
-  tm[tid] = tmax;
-  if (tid == 0) {
-    count = 0;
-    thr_s = 0;
+  // Candidates past the row's end read a clamped (in-bounds) entry and are
+  // dropped by the b < ncand test; with no candidates, entry 0 of the row
+  // (max_pages >= 1) is read and dropped.
+  float v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = sc[max(min(tid + 256 * u, ncand - 1), 0)];
+  uint64_t tmax = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = tid + 256 * u;
+    const uint64_t k = b < ncand ? make_key(v[u], b) : 0ull;
+    tmax = k > tmax ? k : tmax;
   }
+  tm[tid] = tmax;
+  if (tid == 0) count = 0;
   if (tid < kMaxTopK) top[tid] = 0;
   __syncthreads();
-  int rank = 0;
-  for (int i = 0; i < 256; ++i) rank += tm[i] > tmax ? 1 : 0;
-  // With fewer than 16 non-empty threads nobody (or only empty threads, with
-  // key 0) has rank 15 and the bound stays 0: every candidate survives.
-  if (rank == kMaxTopK - 1) thr_s = tmax;
-  __syncthreads();
-  const uint64_t thr = thr_s;
+  // T: the largest value with at least 16 maxima >= it, i.e. the 16th
+  // largest maximum; 0 when fewer than 16 threads hold a candidate (then
+  // every candidate survives).
+  uint64_t mx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mx[j] = tm[lane + 64 * j];
+  uint64_t thr = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = thr | (1ull << bit);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(mx[j] >= cand));
+    if (c >= kMaxTopK) thr = cand;
+  }
   if (tmax >= thr && tmax != 0) {
-    for (int b = tid; b < ncand; b += 256) {
-      const uint64_t k = make_key(row_s[b], b);
-      if (k >= thr) {
-        const int pos = atomicAdd(&count, 1);
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = tid + 256 * u;
+      c += (b < ncand && make_key(v[u], b) >= thr) ? 1 : 0;
+    }
+    int pos = atomicAdd(&count, c);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = tid + 256 * u;
+      const uint64_t k = make_key(v[u], b);
+      if (b < ncand && k >= thr) {
         if (pos < kSelectMaxSurvivors) surv[pos] = k;
+        ++pos;
       }
     }
   }
@@ -703,7 +707,15 @@ static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
   profile_end(ps, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ki_decode_select_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, st, a);
+  const dim3 sg((unsigned)(a.batch * a.h_kv));
+  const int per = (a.max_pages + 255) / 256;  // candidates per thread
+  if (per <= 4) hipLaunchKernelGGL(ki_decode_select_kernel<4>, sg, dim3(256), 0, st, a);
+  else if (per <= 8) hipLaunchKernelGGL(ki_decode_select_kernel<8>, sg, dim3(256), 0, st, a);
+  else if (per <= 16) hipLaunchKernelGGL(ki_decode_select_kernel<16>, sg, dim3(256), 0, st, a);
+  else if (per <= 32) hipLaunchKernelGGL(ki_decode_select_kernel<32>, sg, dim3(256), 0, st, a);
+  else if (per <= 40) hipLaunchKernelGGL(ki_decode_select_kernel<40>, sg, dim3(256), 0, st, a);
+  else if (per <= 48) hipLaunchKernelGGL(ki_decode_select_kernel<48>, sg, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(ki_decode_select_kernel<64>, sg, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
