@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "msa_index.hip", "msa_attn.hip", "msa_train.hip", "msa_profile.hip"]
+SOURCES = ["msa_api.hip", "msa_index.hip", "msa_project.hip", "msa_attn.hip", "msa_train.hip", "msa_profile.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

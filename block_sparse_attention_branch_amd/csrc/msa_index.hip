@@ -552,134 +552,6 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
   }
 }
 
-// ------------------------------------------- index projections and RoPE
-// The steps before the index branch ("MiniMax Sparse Attention" digest,
-// §4.2: one index-query projection per GQA group, one shared index-key
-// projection; §3.1: RoPE on 64 dims).  C^T = W . x^T on 32x32x16 bf16 MFMA
-// with the projected features on the MFMA rows and 32 tokens on the lanes, so
-// a RoPE pair (i, i + R/2) sits in one lane; angles in double precision (the
-// position times the frequency must stay exact for positions up to 2^20 and
-// beyond).  The key projection is appended to the index-key cache in place.
-// A workgroup takes 32 tokens and one projection; its 8 waves split d_model
-// (16-wide steps dealt round-robin) and their sums are added in a fixed tree
-// through LDS, so short calls (a decode step) still spread over many waves.
-constexpr int kKxWaves = 8;
-
-template <int DI>
-__global__ __launch_bounds__(kKxWaves * 64) void kx_project_kernel(KxArgs a) {
-  constexpr int FT = DI / 32;
-  __shared__ f32x4 red[kKxWaves / 2][FT * 4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int hd = blockIdx.y;  // 0 .. h_kv - 1: query projections; h_kv: the key projection
-  const int t_raw = blockIdx.x * 32 + l32;
-  const bool ok = t_raw < a.n_tok;
-  const int t = min(t_raw, a.n_tok - 1);
-  const bf16_t* w = static_cast<const bf16_t*>(hd < a.h_kv ? a.w_q : a.w_k) +
-                    (hd < a.h_kv ? (size_t)hd * DI * a.d_model : 0);
-  const bf16_t* xr = static_cast<const bf16_t*>(a.x) + (size_t)t * a.d_model + half * 8;
-  f32x16 acc[FT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x16{};
-#pragma unroll 4
-  for (int k0 = wave * 16; k0 < a.d_model; k0 += kKxWaves * 16) {
-    const bf16x8 xb = load_frag<bf16_t>(xr + k0);
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-      mma32(acc[ft], load_frag<bf16_t>(w + (size_t)(ft * 32 + l32) * a.d_model + k0 + half * 8), xb);
-  }
-  // tree: the upper half of the live waves hands its sums to the lower half
-#pragma unroll
-  for (int live = kKxWaves; live > 1; live >>= 1) {
-    const int h = live >> 1;
-    if (wave >= h && wave < live) {
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          red[wave - h][ft * 4 + c][lane] =
-              f32x4{acc[ft][4 * c], acc[ft][4 * c + 1], acc[ft][4 * c + 2], acc[ft][4 * c + 3]};
-    }
-    __syncthreads();
-    if (wave < h) {
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 o = red[wave][ft * 4 + c][lane];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[ft][4 * c + q] += o[q];
-        }
-    }
-    __syncthreads();
-  }
-  if (wave != 0) return;
-  // RoPE: feature f = ft*32 + 8*(v/4) + 4*half + (v%4) of this lane's token
-  const int R = a.rope_dim;
-  const double pos = (double)a.positions[t];
-  const double lb = log2((double)a.rope_base);
-  // turns the pair (acc[fa][va], acc[fb][vb]) by the angle of pair index i
-  auto turn = [&](int fa, int va, int fb, int vb, int i) {
-    double sn, cs;
-    sincos(pos * exp2(-2.0 * i / R * lb), &sn, &cs);
-    const float c = (float)cs, s_ = (float)sn;
-    const float x1 = acc[fa][va], x2 = acc[fb][vb];
-    acc[fa][va] = x1 * c - x2 * s_;
-    acc[fb][vb] = x2 * c + x1 * s_;
-  };
-  if (R == 32) {
-#pragma unroll
-    for (int v = 0; v < 8; ++v) turn(0, v, 0, v + 8, 8 * (v >> 2) + 4 * half + (v & 3));
-  }
-  if constexpr (FT >= 2) {
-    if (R == 64) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) turn(0, v, 1, v, 8 * (v >> 2) + 4 * half + (v & 3));
-    }
-  }
-  if constexpr (FT >= 4) {
-    if (R == 128) {
-#pragma unroll
-      for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) turn(ft, v, ft + 2, v, ft * 32 + 8 * (v >> 2) + 4 * half + (v & 3));
-    }
-  }
-  bf16_t* dst = nullptr;
-  if (hd < a.h_kv) {
-    dst = static_cast<bf16_t*>(a.q_out) + ((size_t)t * a.h_kv + hd) * DI;
-  } else {
-    const int p = a.positions[t];
-    if (a.page_table) {
-      const int sq = a.seq ? a.seq[t] : 0;
-      if (p >= 0 && (p >> 7) < a.max_pages)
-        dst = static_cast<bf16_t*>(a.k_cache) +
-              ((size_t)a.page_table[(size_t)sq * a.max_pages + (p >> 7)] * kBlock + (p & (kBlock - 1))) * DI;
-    } else if (p >= 0 && p < a.n_kv) {
-      dst = static_cast<bf16_t*>(a.k_cache) + (size_t)p * DI;
-    }
-  }
-  if (ok && dst) {
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<bf16x4*>(dst + ft * 32 + 8 * c + 4 * half) =
-            bf16x4{from_f32<bf16_t>(acc[ft][4 * c]), from_f32<bf16_t>(acc[ft][4 * c + 1]),
-                   from_f32<bf16_t>(acc[ft][4 * c + 2]), from_f32<bf16_t>(acc[ft][4 * c + 3])};
-  }
-}
-
-hipError_t launch_index_project(int d_idx, const KxArgs& a, hipStream_t st) {
-  if (a.n_tok == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_tok + 31) / 32), (unsigned)(a.h_kv + 1));
-  const dim3 block(kKxWaves * 64);
-  if (d_idx == 32) hipLaunchKernelGGL(kx_project_kernel<32>, grid, block, 0, st, a);
-  else if (d_idx == 64) hipLaunchKernelGGL(kx_project_kernel<64>, grid, block, 0, st, a);
-  else if (d_idx == 128) hipLaunchKernelGGL(kx_project_kernel<128>, grid, block, 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 // ----------------------------------------------------------------- launch
 template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {

@@ -994,6 +994,20 @@ def test_index_project_prefill_contiguous_variants():
     _project_case(97, 256, 4, 64, 0, 75, paged=False)
 
 
+def test_index_project_long_call_tiles():
+    # calls of 256 tokens and more take the tiled kernel: d_idx 32 / 64 / 128,
+    # d_model with a 16-wide tail past the last 64-wide chunk, token counts
+    # that end inside a tile, projections split over several workgroups with
+    # an idle wave in the last (h_kv 16: 17 projections as 6 + 6 + 5), and a
+    # paged cache
+    _project_case(1000, 784, 8, 128, 64, 78, paged=False)
+    _project_case(600, 528, 1, 128, 128, 79, paged=False)
+    _project_case(513, 1040, 4, 32, 32, 80, paged=False)
+    _project_case(700, 256, 16, 64, 64, 81, paged=False)
+    _project_case(256, 272, 4, 64, 0, 82, paged=False)
+    _project_case(300, 512, 4, 64, 64, 83, paged=True)
+
+
 def test_index_project_large_positions_paged():
     # positions near 2^20 + 255: the angle must be formed without fp32 rounding
     pos = torch.tensor([1048575, 1048831, 1048576, 0, 127, 128, 999999, 524288], dtype=torch.int64)
