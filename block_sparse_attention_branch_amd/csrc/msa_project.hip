@@ -178,6 +178,8 @@ __global__ __launch_bounds__(kKxWaves * 64) void kx_project_kernel(KxArgs a) {
 // the layout of the short kernel's (features on the MFMA rows, tokens on the
 // lanes) and goes through the same RoPE and store.
 constexpr int kKxChunk = 64;
+constexpr int kKxSteps = kKxChunk / 16;    // MFMA k-steps per chunk
+constexpr int kKxRowPieces = kKxChunk / 8;  // 16-byte pieces per row and chunk
 constexpr int kKxRowBytes = kKxChunk * 2 + 16;
 constexpr int kKxTileMinTokens = 256;
 constexpr int kKxTileWaves = 8;
@@ -188,12 +190,12 @@ template <int DI>
 constexpr int kx_tile_tt() { return DI >= 128 ? 1 : 4; }
 // x pieces (16 bytes) per staging thread and chunk, with at least 3 staging waves
 template <int DI>
-constexpr int kx_tile_npt() { return (kx_tile_tt<DI>() * 32 * (kKxChunk / 8) + 64 * (kKxTileWaves - kKxMaxCompute) - 1) / (64 * (kKxTileWaves - kKxMaxCompute)); }
+constexpr int kx_tile_npt() { return (kx_tile_tt<DI>() * 32 * kKxRowPieces + 64 * (kKxTileWaves - kKxMaxCompute) - 1) / (64 * (kKxTileWaves - kKxMaxCompute)); }
 
 template <int DI>
 __global__ __launch_bounds__(kKxTileWaves * 64) void kx_tile_kernel(KxArgs a, int proj_per_wg) {
   constexpr int FT = DI / 32, TT = kx_tile_tt<DI>(), ROWS = TT * 32, NPT = kx_tile_npt<DI>();
-  constexpr int PIECES = ROWS * (kKxChunk / 8);  // 16-byte pieces of x per chunk
+  constexpr int PIECES = ROWS * kKxRowPieces;  // 16-byte pieces of x per chunk
   __shared__ __align__(16) unsigned char xs[3][ROWS * kKxRowBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
@@ -213,17 +215,17 @@ __global__ __launch_bounds__(kKxTileWaves * 64) void kx_tile_kernel(KxArgs a, in
 #pragma unroll
       for (int j = 0; j < NPT; ++j) {
         const int p = min(sid + j * nst, PIECES - 1);
-        const int tok = min(tok0 + (p >> 3), a.n_tok - 1);
-        r[j] = load_frag<bf16_t>(x + (size_t)tok * D + min(c * kKxChunk + 8 * (p & 7), D - 8));
+        const int tok = min(tok0 + p / kKxRowPieces, a.n_tok - 1);
+        r[j] = load_frag<bf16_t>(x + (size_t)tok * D + min(c * kKxChunk + 8 * (p % kKxRowPieces), D - 8));
       }
     };
     auto x_store = [&](const bf16x8(&r)[NPT], int buf, int c) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j) {
         const int p = sid + j * nst;
-        const bool in = c * kKxChunk + 8 * (p & 7) < D;
+        const bool in = c * kKxChunk + 8 * (p % kKxRowPieces) < D;
         if (p < PIECES)
-          *reinterpret_cast<bf16x8*>(&xs[buf][(p >> 3) * kKxRowBytes + (p & 7) * 16]) = in ? r[j] : zero_frag<bf16_t>();
+          *reinterpret_cast<bf16x8*>(&xs[buf][(p / kKxRowPieces) * kKxRowBytes + (p % kKxRowPieces) * 16]) = in ? r[j] : zero_frag<bf16_t>();
       }
     };
     bf16x8 r0[NPT], r1[NPT], r2[NPT];
@@ -268,11 +270,11 @@ __global__ __launch_bounds__(kKxTileWaves * 64) void kx_tile_kernel(KxArgs a, in
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) acc[tt][ft] = f32x16{};
-  bf16x8 wa[FT][4];
+  bf16x8 wa[FT][kKxSteps];
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-    for (int st = 0; st < 4; ++st) wa[ft][st] = w_frag(ft, st, 0);
+    for (int st = 0; st < kKxSteps; ++st) wa[ft][st] = w_frag(ft, st, 0);
   __syncthreads();
   auto chunk = [&](int c, int buf) __attribute__((always_inline)) {
     const int cn = c + 1;
@@ -283,8 +285,8 @@ __global__ __launch_bounds__(kKxTileWaves * 64) void kx_tile_kernel(KxArgs a, in
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) bx[tt] = *reinterpret_cast<const bf16x8*>(xb + tt * 32 * kKxRowBytes);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st < 3) {
+    for (int st = 0; st < kKxSteps; ++st) {
+      if (st < kKxSteps - 1) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           bn[tt] = *reinterpret_cast<const bf16x8*>(xb + tt * 32 * kKxRowBytes + 32 * (st + 1));
