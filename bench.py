@@ -14,10 +14,11 @@ The float64 oracle is timed on a bounded sample on the host (cpu_baseline).
 
 Other workloads print their own JSON line: prefill128k (planted), long1m,
 decode_fp8 (e4m3 caches), backward32k (the training path's gradient call at
-the 32K prefill shape) and copy (bandwidth calibration).
+the 32K prefill shape), project (index projections + RoPE), copy (bandwidth
+calibration) and peak (achievable MFMA rate and copy bandwidth).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                       [--workload step|prefill128k|long1m|decode_fp8|backward32k|copy]
+                       [--workload step|prefill128k|long1m|decode_fp8|backward32k|project|copy|peak]
 """
 from __future__ import annotations
 
@@ -272,6 +273,29 @@ def bench_copy(args):
                       "read_only_GBs": round(4 * COPY_BYTES / (rms * 1e-3) / 1e9, 1)}))
 
 
+def bench_peak(msa, args):
+    """Achievable peaks next to the published ones: a dense bf16 MFMA loop
+    (msa_probe_mfma on 4 workgroups of 4 waves per CU) and the copy above."""
+    n_wg, iters = 4 * 256, 4000
+    out = torch.empty(n_wg, dtype=torch.float32, device="cuda")
+    msa.probe_mfma(n_wg, 100, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(max(3, args.steps)):
+        e0.record()
+        msa.probe_mfma(n_wg, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2]
+    fl = n_wg * 4.0 * iters * 8 * 32768
+    tf = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({"workload": "peak", "mfma_bf16_tflops": round(tf, 1), "mfma_spec_tflops": PEAK_BF16_TFLOPS,
+                      "mfma_frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4), "mfma_ms": round(ms, 4)}))
+    bench_copy(args)
+
+
 def kernel_roofline(kern, main_flops, call_rl):
     """Roofline of the dominant kernel, kp_kernel (the KV-outer pass of
     msa_sparse_prefill, which does all of the main branch's MFMA work):
@@ -350,7 +374,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "backward32k",
-                                                             "project", "copy"])
+                                                             "project", "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -373,6 +397,8 @@ def main():
     msa.lib()
     if args.workload == "copy":
         bench_copy(args)
+    elif args.workload == "peak":
+        bench_peak(msa, args)
     elif args.workload == "step":
         bench_step(msa, args)
     elif args.workload == "decode_fp8":

@@ -104,6 +104,12 @@ msa_status msa_profile_enable(int32_t on) {
   return ok();
 }
 
+msa_status msa_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* hip_stream) {
+  if (n_wg < 1 || iters < 1) return fail(MSA_ERR_INVALID_ARG, "n_wg=%d iters=%d must be >= 1", n_wg, iters);
+  if (!out) return fail(MSA_ERR_INVALID_ARG, "out is NULL");
+  return hip_status(msa::launch_mfma_probe(n_wg, iters, out, static_cast<hipStream_t>(hip_stream)), "msa_probe_mfma");
+}
+
 msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return fail(MSA_ERR_INVALID_ARG, "total_ms and launches must not be NULL");
   const int k = msa::profile_kernel_id(kernel);

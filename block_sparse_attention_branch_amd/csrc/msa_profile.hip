@@ -1,6 +1,8 @@
 // msa_profile.hip - event pairs around timed kernel launches (diagnostics).
 #include "msa_profile.hpp"
 
+#include "msa_common.hpp"
+
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -86,6 +88,38 @@ hipError_t profile_collect(ProfKernel k, double* total_ms, long long* launches) 
   *total_ms = tot;
   *launches = n;
   return hipSuccess;
+}
+
+// Dense bf16 MFMA throughput probe (measurement of the achievable peak): each
+// wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 chains on
+// operands made from the lane index (unknown at compile time); one sum per
+// workgroup is written so that the work is kept.
+__global__ __launch_bounds__(256) void kprobe_mfma_kernel(int32_t iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = from_f32<bf16_t>((float)(lane + e) * 1e-3f);
+    b[e] = from_f32<bf16_t>((float)(3 * lane + e) * 1e-3f);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mma32(acc[j], a, b);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[j][v];
+  if (threadIdx.x == 0) out[blockIdx.x] = sum;
+}
+
+hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(kprobe_mfma_kernel, dim3((unsigned)n_wg), dim3(256), 0, st, iters, out);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -21,5 +21,7 @@ void profile_end(int slot, hipStream_t st);
 int profile_kernel_id(const char* name);
 // Sums the recorded durations of kernel k and forgets them.
 hipError_t profile_collect(ProfKernel k, double* total_ms, long long* launches);
+// n_wg workgroups of 4 waves, each wave `iters` rounds of 8 bf16 32x32x16 MFMAs.
+hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t st);
 
 }  // namespace msa

@@ -55,7 +55,7 @@ _lib = None
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
            "msa_sparse_prefill_backward", "msa_index_project",
            "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
-           "msa_profile_enable", "msa_profile_read"]
+           "msa_profile_enable", "msa_profile_read", "msa_probe_mfma"]
 
 
 def lib() -> ctypes.CDLL:
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.msa_profile_enable.restype = ctypes.c_int
         L.msa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(ctypes.c_int64)]
         L.msa_profile_read.restype = ctypes.c_int
+        L.msa_probe_mfma.argtypes = [i32, i32, P(ctypes.c_float), ctypes.c_void_p]
+        L.msa_probe_mfma.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -167,6 +169,13 @@ def profile_enable(on: bool = True) -> None:
     """msa_profile_enable: bracket every launch of the timed kernels with HIP
     events on the launch stream (measurement only)."""
     _check(lib().msa_profile_enable(1 if on else 0))
+
+
+def probe_mfma(n_wg: int, iters: int, out, stream=None) -> None:
+    """msa_probe_mfma: n_wg * 4 * iters * 8 bf16 32x32x16 MFMAs (measurement only);
+    ``out`` is a float32 device tensor of n_wg elements."""
+    _check(lib().msa_probe_mfma(int(n_wg), int(iters), ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_float)),
+                                _stream(stream)))
 
 
 def profile_read(kernel: str):

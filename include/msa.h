@@ -278,6 +278,15 @@ int32_t msa_abi_version(void);
 msa_status msa_profile_enable(int32_t on);
 msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 
+/* Achievable dense bf16 MFMA rate, for measurement (not part of the method):
+ * n_wg workgroups of 4 waves; each wave runs `iters` rounds of 8 independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands, i.e.
+ * n_wg * 4 * iters * 8 * 32768 FLOPs, and one float per workgroup is written
+ * to `out` (device, n_wg floats, caller-owned) so the work is not removed.
+ * Asynchronous on hip_stream; the caller times it.  n_wg or iters < 1, or out
+ * NULL: MSA_ERR_INVALID_ARG.                                               */
+msa_status msa_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,3 +201,12 @@ def test_index_project_validation():
     assert call(x=None) == 1 and "NULL" in _err()
     assert call(shp=msa.make_shape(4, 4, 128, 64, 16, msa.MSA_FP32)) == 2
     assert call(n=0) == 0 and _err() == ""
+
+
+def test_mfma_probe_validation():
+    # argument checks of the measurement probe run on the host, before any launch
+    L = msa.lib()
+    fp = ctypes.cast(FAKE, ctypes.POINTER(ctypes.c_float))
+    assert L.msa_probe_mfma(0, 10, fp, None) == 1 and "n_wg" in _err()
+    assert L.msa_probe_mfma(4, 0, fp, None) == 1 and "iters" in _err()
+    assert L.msa_probe_mfma(4, 10, None, None) == 1 and "NULL" in _err()
