@@ -204,7 +204,8 @@ __global__ __launch_bounds__(kKxTileWaves * 64) void kx_tile_kernel(KxArgs a, in
   const int nch3 = ((D + kKxChunk - 1) / kKxChunk + 2) / 3 * 3;
 
   if (wave >= proj_per_wg) {
-    // ---- staging waves: piece p = row * 8 + col, 16 bytes at k = 64 c + 8 col
+    // ---- staging waves: piece p = row * kKxRowPieces + col, 16 bytes at
+    // k = c * kKxChunk + 8 col
     const int sid = threadIdx.x - proj_per_wg * 64, nst = (kKxTileWaves - proj_per_wg) * 64;
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
     // d_model is a multiple of 16, so an 8-wide piece is wholly inside or
