@@ -619,7 +619,22 @@ def bench_prefill_only(msa, args, planted=True):
     evs = [timer.step(fns) for _ in range(args.steps)]
     timer.collect(evs)
     t_ip, t_sp = timer.mean_ms("index_prefill"), timer.mean_ms("sparse_prefill")
-    idx_fl, main_fl, _ = prefill_counts(n, 0, shape)
+    idx_fl, main_fl, dense_fl = prefill_counts(n, 0, shape)
+    dense = None
+    if not args.no_dense:
+        # the dense comparison kernel at the same shape, for the speedup at 128K
+        od = torch.empty_like(inp["q"])
+        msa.dense_prefill(inp["q"], inp["k"], inp["v"], out=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        msa.dense_prefill(inp["q"], inp["k"], inp["v"], out=od)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1)
+        dense = {"ms": round(dms, 2), "tflops": round(dense_fl / (dms * 1e-3) / 1e12, 1),
+                 "speedup_msa_prefill_vs_dense": round(dms / (t_ip + t_sp), 2)}
+        del od
     got = bidx.cpu()
     des = inp["designated"]
     hit = all(set(inp["planted_blocks"][r].tolist()) <= set(got[int(i), r].tolist())
@@ -628,7 +643,7 @@ def bench_prefill_only(msa, args, planted=True):
                       "sparse_ms": round(t_sp, 3), "tokens_per_s": round(n / ((t_ip + t_sp) * 1e-3), 1),
                       "index_roofline": roofline("mfma", idx_fl, t_ip, "TFLOP/s"),
                       "sparse_roofline": roofline("mfma", main_fl, t_sp, "TFLOP/s"),
-                      "planted_blocks_retrieved": bool(hit)}))
+                      "planted_blocks_retrieved": bool(hit), "dense_gqa": dense}))
 
 
 def bench_backward(msa, args):
