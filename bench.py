@@ -718,12 +718,15 @@ def bench_project(msa, args):
             cache = torch.zeros(65536, 128, di, dtype=torch.bfloat16, device=dev)
             pt = torch.randperm(65536, device=dev).to(torch.int32).view(64, 1024)
             seq = torch.arange(n, dtype=torch.int32, device=dev)
-            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, page_table=pt, seq=seq, out=qo)]
+            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, page_table=pt, seq=seq, out=qo, workspace=ws)]
         else:
             pos = torch.arange(n, dtype=torch.int32, device=dev)
             cache = torch.zeros(n, di, dtype=torch.bfloat16, device=dev)
-            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, out=qo)]
+            fn = [lambda: msa.index_project(x, wq, wk, pos, cache, out=qo, workspace=ws)]
         qo = torch.empty(n, h_kv, di, dtype=torch.bfloat16, device=dev)
+        shp = msa.make_shape(h_kv, h_kv, 128, di, 16, msa.MSA_BF16)
+        ws = torch.empty(max(1, msa.workspace_size(msa.OP_INDEX_PROJECT, shp, n_q=n, n_kv=dm)), dtype=torch.uint8,
+                         device=dev)
         timer = CallTimer([name])
         for _ in range(args.warmup):
             fn[0]()

@@ -136,9 +136,18 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 size_t msa_workspace_size(int32_t op, const msa_shape* shape, int32_t batch, int32_t n_q, int32_t q_start,
                           int32_t n_kv, int32_t max_pages) {
-  if (op < 0 || op > 6) {
-    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..6", op);
+  if (op < 0 || op > 7) {
+    fail(MSA_ERR_INVALID_ARG, "op=%d not in 0..7", op);
     return 0;
+  }
+  if (op == 7) {  // msa_index_project: n_q = n_tok, n_kv = d_model
+    if (check_shape(shape, true, false) != MSA_OK) return 0;
+    if (n_q < 0 || n_kv < 0) {
+      fail(MSA_ERR_INVALID_ARG, "negative size");
+      return 0;
+    }
+    ok();
+    return msa::kx_plan(n_q, n_kv, shape->h_kv, shape->d_idx).total;
   }
   if (check_shape(shape, op == 0 || op == 4 || op == 6, (op >= 1 && op <= 3) || op >= 5) != MSA_OK) return 0;
   if (check_cache_dtype(*shape, op != 3 && op < 5) != MSA_OK) return 0;
@@ -304,7 +313,7 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
 msa_status msa_index_project(const msa_shape* shape, int32_t n_tok, int32_t d_model, const void* x,
                              const void* w_q_idx, const void* w_k_idx, int32_t rope_dim, float rope_base,
                              const int32_t* positions, const int32_t* seq, const msa_kv* kv, void* q_idx_out,
-                             void* hip_stream) {
+                             void* workspace, size_t ws_bytes, void* hip_stream) {
   msa_status st = check_shape(shape, true, false);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
@@ -338,6 +347,11 @@ msa_status msa_index_project(const msa_shape* shape, int32_t n_tok, int32_t d_mo
   a.n_kv = kv->n_kv;
   a.max_pages = kv->max_pages;
   a.rope_base = rope_base;
+  const msa::KxPlan pl = msa::kx_plan(n_tok, d_model, s.h_kv, s.d_idx);
+  if ((st = check_ws(workspace, ws_bytes, pl.total)) != MSA_OK) return st;
+  a.split = pl.split;
+  a.k_per_split = pl.k_per_split;
+  a.part = pl.split > 1 ? static_cast<float*>(workspace) : nullptr;
   return hip_status(msa::launch_index_project(s.d_idx, a, static_cast<hipStream_t>(hip_stream)), "msa_index_project");
 }
 

@@ -76,7 +76,16 @@ struct KxArgs {
   void* q_out;              // [n_tok, h_kv, d_idx]
   int32_t n_tok, d_model, h_kv, rope_dim, n_kv, max_pages;
   float rope_base;
+  float* part;              // split > 1: fp32 partial sums [split, n_tok, h_kv + 1, d_idx]
+  int32_t split, k_per_split;
 };
+// Short calls split d_model over `split` slices of k_per_split (a multiple of
+// 16) so that enough workgroups stream the weights; total = workspace bytes.
+struct KxPlan {
+  int32_t split, k_per_split;
+  size_t total;
+};
+KxPlan kx_plan(int32_t n_tok, int32_t d_model, int32_t h_kv, int32_t d_idx);
 hipError_t launch_index_project(int d_idx, const KxArgs& a, hipStream_t st);
 
 hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipStream_t st);

@@ -3,6 +3,8 @@
 // projection, with the index key appended to the cache in place).  Built
 // without the VGPR-form MFMA option of the index kernels, so the long-call
 // kernel's accumulators can live in the accumulation registers.
+#include <algorithm>
+
 #include "msa_common.hpp"
 #include "msa_internal.hpp"
 
@@ -16,11 +18,48 @@ namespace msa {
 // a RoPE pair (i, i + R/2) sits in one lane; angles in double precision (the
 // position times the frequency must stay exact for positions up to 2^20 and
 // beyond).  The key projection is appended to the index-key cache in place.
-// Short calls (a decode step): a workgroup takes 32 tokens and one
-// projection; its 8 waves split d_model (16-wide steps dealt round-robin) and
-// their sums are added in a fixed tree through LDS, so a few tokens still
-// spread over many waves.  Long calls use kx_tile_kernel below.
+// Short calls (a decode step): a workgroup takes 32 tokens, one projection
+// and one slice of d_model (blockIdx.z; the whole of it when the call is not
+// split); its 8 waves split the slice (16-wide steps dealt round-robin) and
+// their sums are added in a fixed tree through LDS.  Unsplit, wave 0 applies
+// RoPE and stores; split, it writes the slice's fp32 sums and kx_reduce_kernel
+// adds the slices in order, applies RoPE and stores.  Long calls use
+// kx_tile_kernel below.
 constexpr int kKxWaves = 8;
+
+// cos and sin of the angle pos * f.  The angle is formed in double and
+// reduced modulo 2 pi there (Cody and Waite's method, 2 pi split into three
+// parts; the first two have 24 significant bits, so k times either is exact
+// for |k| < 2^29, i.e. every int32 position); sine and cosine of the reduced
+// angle are taken in fp32.
+__device__ __forceinline__ void rope_cos_sin(double pos, double f, float& c, float& s) {
+  const double th = pos * f;
+  const double k = rint(th * 0.15915494309189535);
+  double red = fma(-k, 0x1.921fb4p+2, th);
+  red = fma(-k, 0x1.4442d0p-22, red);
+  red = fma(-k, 0x1.8469898cc5170p-46, red);
+  sincosf((float)red, &s, &c);
+}
+
+// Destination row of token t's projection hd (d_idx values): hd < h_kv, the
+// query projection in q_out; hd == h_kv, the token's row of the index-key
+// cache (contiguous at row positions[t] if in [0, n_kv), paged at row
+// positions[t] % 128 of page page_table[seq[t], positions[t] / 128] if that
+// page index is below max_pages); nullptr if the row is out of range.
+template <int DI>
+__device__ __forceinline__ bf16_t* kx_dst(const KxArgs& a, int t, int hd) {
+  if (hd < a.h_kv) return static_cast<bf16_t*>(a.q_out) + ((size_t)t * a.h_kv + hd) * DI;
+  const int p = a.positions[t];
+  if (a.page_table) {
+    const int sq = a.seq ? a.seq[t] : 0;
+    if (p >= 0 && (p >> 7) < a.max_pages)
+      return static_cast<bf16_t*>(a.k_cache) +
+             ((size_t)a.page_table[(size_t)sq * a.max_pages + (p >> 7)] * kBlock + (p & (kBlock - 1))) * DI;
+  } else if (p >= 0 && p < a.n_kv) {
+    return static_cast<bf16_t*>(a.k_cache) + (size_t)p * DI;
+  }
+  return nullptr;
+}
 
 // RoPE and store of one 32-token tile of one projection held as the MFMA
 // result C^T: lane (half, l32) has token t, acc[ft][v] = feature
@@ -48,19 +87,10 @@ __device__ __forceinline__ void kx_rope_store(f32x16 (&acc)[DI / 32], int t, boo
       row *= r8;
     }
   }
-  // turns the pair (acc[fa][va], acc[fb][vb]) by the angle pos * f.  The
-  // angle is formed in double and reduced modulo 2 pi there (Cody and
-  // Waite's method, 2 pi split into three parts; the first two have 24
-  // significant bits, so k times either is exact for |k| < 2^29, i.e. every
-  // int32 position); sine and cosine of the reduced angle are taken in fp32.
+  // turns the pair (acc[fa][va], acc[fb][vb]) by the angle pos * f
   auto turn = [&](int fa, int va, int fb, int vb, double f) __attribute__((always_inline)) {
-    const double th = pos * f;
-    const double k = rint(th * 0.15915494309189535);
-    double red = fma(-k, 0x1.921fb4p+2, th);
-    red = fma(-k, 0x1.4442d0p-22, red);
-    red = fma(-k, 0x1.8469898cc5170p-46, red);
     float c, s_;
-    sincosf((float)red, &s_, &c);
+    rope_cos_sin(pos, f, c, s_);
     const float x1 = acc[fa][va], x2 = acc[fb][vb];
     acc[fa][va] = x1 * c - x2 * s_;
     acc[fb][vb] = x2 * c + x1 * s_;
@@ -87,20 +117,7 @@ __device__ __forceinline__ void kx_rope_store(f32x16 (&acc)[DI / 32], int t, boo
       for (int v = 0; v < 16; ++v) turn(1, v, 3, v, fq[v] * r32);
     }
   }
-  bf16_t* dst = nullptr;
-  if (hd < a.h_kv) {
-    dst = static_cast<bf16_t*>(a.q_out) + ((size_t)t * a.h_kv + hd) * DI;
-  } else {
-    const int p = a.positions[t];
-    if (a.page_table) {
-      const int sq = a.seq ? a.seq[t] : 0;
-      if (p >= 0 && (p >> 7) < a.max_pages)
-        dst = static_cast<bf16_t*>(a.k_cache) +
-              ((size_t)a.page_table[(size_t)sq * a.max_pages + (p >> 7)] * kBlock + (p & (kBlock - 1))) * DI;
-    } else if (p >= 0 && p < a.n_kv) {
-      dst = static_cast<bf16_t*>(a.k_cache) + (size_t)p * DI;
-    }
-  }
+  bf16_t* dst = kx_dst<DI>(a, t, hd);
   if (ok && dst) {
 #pragma unroll
     for (int ft = 0; ft < DI / 32; ++ft)
@@ -124,11 +141,12 @@ __global__ __launch_bounds__(kKxWaves * 64) void kx_project_kernel(KxArgs a) {
   const bf16_t* w = static_cast<const bf16_t*>(hd < a.h_kv ? a.w_q : a.w_k) +
                     (hd < a.h_kv ? (size_t)hd * DI * a.d_model : 0);
   const bf16_t* xr = static_cast<const bf16_t*>(a.x) + (size_t)t * a.d_model + half * 8;
+  const int k_lo = blockIdx.z * a.k_per_split, k_hi = min(a.d_model, k_lo + a.k_per_split);
   f32x16 acc[FT];
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x16{};
 #pragma unroll 4
-  for (int k0 = wave * 16; k0 < a.d_model; k0 += kKxWaves * 16) {
+  for (int k0 = k_lo + wave * 16; k0 < k_hi; k0 += kKxWaves * 16) {
     const bf16x8 xb = load_frag<bf16_t>(xr + k0);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
@@ -160,7 +178,66 @@ __global__ __launch_bounds__(kKxWaves * 64) void kx_project_kernel(KxArgs a) {
     __syncthreads();
   }
   if (wave != 0) return;
+  if (a.split > 1) {
+    // acc[ft][4c .. 4c+3] are features ft*32 + 8c + 4*half + 0..3
+    if (ok) {
+      float* dst = a.part + (((size_t)blockIdx.z * a.n_tok + t) * (a.h_kv + 1) + hd) * DI;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<f32x4*>(dst + ft * 32 + 8 * c + 4 * half) =
+              f32x4{acc[ft][4 * c], acc[ft][4 * c + 1], acc[ft][4 * c + 2], acc[ft][4 * c + 3]};
+    }
+    return;
+  }
   kx_rope_store<DI>(acc, t, ok, hd, a);
+}
+
+// Sum of the split slices (in slice order) for one (token, projection): item
+// j < R/2 is the RoPE pair (j, j + R/2), turned by the angle of pair j; items
+// from R/2 on are the dims past rope_dim, stored as they are.  One thread per
+// item, so every partial is read once.
+template <int DI>
+__global__ __launch_bounds__(256) void kx_reduce_kernel(KxArgs a) {
+  const int nproj = a.h_kv + 1;
+  const int R = a.rope_dim, H = R / 2, NI = DI - H;  // items per (token, projection)
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.n_tok * nproj * NI) return;
+  const int j = (int)(idx % NI);
+  const int hd = (int)((idx / NI) % nproj);
+  const int t = (int)(idx / ((int64_t)NI * nproj));
+  const bool pair = j < H;
+  const int f1 = pair ? j : j + H, f2 = pair ? j + H : f1;
+  const size_t stride = (size_t)a.n_tok * nproj * DI;
+  const float* src = a.part + ((size_t)t * nproj + hd) * DI;
+  // slices in groups of 8 independent loads (clamped past the last slice,
+  // which then adds zero), summed in slice order
+  float x = 0.0f, y = 0.0f;
+  for (int z0 = 0; z0 < a.split; z0 += 8) {
+    float vx[8], vy[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t o = (size_t)min(z0 + u, a.split - 1) * stride;
+      vx[u] = src[o + f1];
+      vy[u] = src[o + f2];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      x += z0 + u < a.split ? vx[u] : 0.0f;
+      y += z0 + u < a.split ? vy[u] : 0.0f;
+    }
+  }
+  bf16_t* dst = kx_dst<DI>(a, t, hd);
+  if (!dst) return;
+  if (pair) {
+    float c, s;
+    rope_cos_sin((double)a.positions[t], exp2(-2.0 * j / R * log2((double)a.rope_base)), c, s);
+    dst[f1] = from_f32<bf16_t>(x * c - y * s);
+    dst[f2] = from_f32<bf16_t>(y * c + x * s);
+  } else {
+    dst[f1] = from_f32<bf16_t>(x);
+  }
 }
 
 // Long calls: a workgroup of 8 waves takes 32*TT tokens (128 at d_idx 32 and
@@ -348,12 +425,35 @@ hipError_t launch_index_project(int d_idx, const KxArgs& a, hipStream_t st) {
     else kx_tile_launch<128>(a, st);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((a.n_tok + 31) / 32), (unsigned)(a.h_kv + 1));
+  const dim3 grid((unsigned)((a.n_tok + 31) / 32), (unsigned)(a.h_kv + 1), (unsigned)std::max(1, a.split));
   const dim3 block(kKxWaves * 64);
   if (d_idx == 32) hipLaunchKernelGGL(kx_project_kernel<32>, grid, block, 0, st, a);
   else if (d_idx == 64) hipLaunchKernelGGL(kx_project_kernel<64>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(kx_project_kernel<128>, grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split <= 1) return e;
+  const int64_t n = (int64_t)a.n_tok * (a.h_kv + 1) * (d_idx - a.rope_dim / 2);
+  const dim3 rg((unsigned)((n + 255) / 256));
+  if (d_idx == 32) hipLaunchKernelGGL(kx_reduce_kernel<32>, rg, dim3(256), 0, st, a);
+  else if (d_idx == 64) hipLaunchKernelGGL(kx_reduce_kernel<64>, rg, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(kx_reduce_kernel<128>, rg, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+KxPlan kx_plan(int32_t n_tok, int32_t d_model, int32_t h_kv, int32_t d_idx) {
+  KxPlan p{1, d_model, 0};
+  if (n_tok <= 0 || n_tok >= kKxTileMinTokens || d_model <= 0) return p;
+  // aim for >= 256 workgroups; every slice keeps >= 2 steps of 16 per wave
+  const int64_t wg = (int64_t)((n_tok + 31) / 32) * (h_kv + 1);
+  const int64_t want = (256 + wg - 1) / wg;
+  const int64_t most = std::max<int64_t>(1, d_model / (kKxWaves * 32));
+  const int64_t split = std::min(want, most);
+  if (split <= 1) return p;
+  const int32_t kps = (int32_t)(((d_model + split - 1) / split + 15) / 16 * 16);
+  p.k_per_split = kps;
+  p.split = (d_model + kps - 1) / kps;
+  p.total = (size_t)p.split * n_tok * (h_kv + 1) * d_idx * sizeof(float);
+  return p;
 }
 
 }  // namespace msa

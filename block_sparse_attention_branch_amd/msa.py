@@ -18,6 +18,7 @@ MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
 MSA_POOL_MAX, MSA_POOL_MEAN = 0, 1
 OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE, OP_PREFILL_BACKWARD, OP_PREFILL_BACKWARD_KL = \
     0, 1, 2, 3, 4, 5, 6
+OP_INDEX_PROJECT = 7
 BLOCK = 128
 
 
@@ -74,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
         L.msa_sparse_prefill_backward.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, vp, vp, vp,
                                                   P(KL), vp, sz, vp]
-        L.msa_index_project.argtypes = [P(Shape), i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, P(KV), vp, vp]
+        L.msa_index_project.argtypes = [P(Shape), i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, P(KV), vp, vp,
+                                        ctypes.c_size_t, vp]
         for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
                   "msa_sparse_prefill_backward", "msa_index_project"):
             getattr(L, f).restype = ctypes.c_int
@@ -303,7 +305,7 @@ def sparse_prefill_backward(q, k, v, block_idx, o, lse, d_o, *, q_start=0, sm_sc
 
 
 def index_project(x, w_q_idx, w_k_idx, positions, k_idx_cache, *, rope_dim=64, rope_base=10000.0, page_table=None,
-                  seq=None, n_kv=None, out=None, stream=None):
+                  seq=None, n_kv=None, out=None, workspace=None, stream=None):
     """msa_index_project: q_idx [n_tok, h_kv, d_idx] = RoPE(W_q_idx[r] x) for every
     group, and RoPE(W_k_idx x) appended to ``k_idx_cache`` (contiguous [n_kv,
     d_idx] or pages [*, 128, d_idx] with ``page_table``) at each token's
@@ -315,9 +317,11 @@ def index_project(x, w_q_idx, w_k_idx, positions, k_idx_cache, *, rope_dim=64, r
     nkv = int(n_kv) if n_kv is not None else (k_idx_cache.shape[0] if page_table is None else 0)
     mp = page_table.shape[-1] if page_table is not None else 0
     kv = KV(None, None, _ptr(k_idx_cache), _ptr(page_table), None, nkv, mp)
+    nws = workspace_size(OP_INDEX_PROJECT, shape, n_q=n_tok, n_kv=d_model)
+    ws = _workspace(nws, x.device, workspace)
     _check(lib().msa_index_project(ctypes.byref(shape), n_tok, d_model, _ptr(x), _ptr(w_q_idx), _ptr(w_k_idx),
                                    int(rope_dim), float(rope_base), _ptr(positions), _ptr(seq), ctypes.byref(kv),
-                                   _ptr(q_out), _stream(stream)))
+                                   _ptr(q_out), _ptr(ws), nws, _stream(stream)))
     return q_out
 
 

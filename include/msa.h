@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 #define MSA_BLOCK_SIZE 128
 #define MSA_MAX_TOP_K 16
 
@@ -225,11 +225,15 @@ msa_status msa_sparse_prefill_backward(const msa_shape* shape, int32_t n_q, int3
  * (page_table NULL) at row positions[t] if it is in [0, n_kv); paged at row
  * positions[t] % 128 of page page_table[seq[t] * max_pages + positions[t] /
  * 128] if positions[t] / 128 < max_pages.  Rows out of range are skipped.
- * bf16 only (dtype MSA_BF16, bf16 cache).                                   */
+ * bf16 only (dtype MSA_BF16, bf16 cache).
+ * Workspace: msa_workspace_size(7, shape, 0, n_tok, 0, d_model, 0) bytes
+ *   (d_model passed in the n_kv slot); non-zero only for short calls (fewer
+ *   than 256 tokens), which split d_model over workgroups and add the fp32
+ *   partial sums in a second kernel.                                      */
 msa_status msa_index_project(const msa_shape* shape, int32_t n_tok, int32_t d_model, const void* x,
                              const void* w_q_idx, const void* w_k_idx, int32_t rope_dim, float rope_base,
                              const int32_t* positions, const int32_t* seq, const msa_kv* kv,
-                             void* q_idx_out, void* hip_stream);
+                             void* q_idx_out, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Dense causal GQA attention, [P1] §2.2 Eq. (1): the comparison kernel.
  *   Same arguments as msa_sparse_prefill without block_idx; contiguous cache
@@ -241,7 +245,8 @@ msa_status msa_dense_prefill(const msa_shape* shape, int32_t n_q, int32_t q_star
 /* Workspace bytes a call needs.  op: 0 = msa_index_topk in prefill mode,
  * 1 = msa_sparse_prefill, 2 = msa_sparse_decode, 3 = msa_dense_prefill,
  * 4 = msa_index_topk in decode mode, 5 = msa_sparse_prefill_backward,
- * 6 = msa_sparse_prefill_backward with the KL-alignment term.
+ * 6 = msa_sparse_prefill_backward with the KL-alignment term,
+ * 7 = msa_index_project (n_q = n_tok, n_kv = d_model).
  * Pass the same shape, batch, n_q,
  * q_start and cache geometry (n_kv; max_pages for decode mode) as the
  * call.  Returns 0 when no workspace is needed or for an invalid request

@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     L = msa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.msa_abi_version() == 3
+    assert L.msa_abi_version() == 4
     for st in range(5):
         assert L.msa_status_string(st).decode().startswith("MSA_")
 
@@ -192,8 +192,8 @@ def test_index_project_validation():
     L = msa.lib()
     s = msa.make_shape(4, 4, 128, 64, 16, msa.MSA_BF16)
     kv = msa.KV(None, None, FAKE, None, None, 1000, 0)
-    call = lambda shp=s, n=8, dm=256, rope=64, base=10000.0, kv_=kv, x=FAKE: L.msa_index_project(
-        ctypes.byref(shp), n, dm, x, FAKE, FAKE, rope, base, FAKE, None, ctypes.byref(kv_), FAKE, None)
+    call = lambda shp=s, n=8, dm=256, rope=64, base=10000.0, kv_=kv, x=FAKE, ws=None, wsb=0: L.msa_index_project(
+        ctypes.byref(shp), n, dm, x, FAKE, FAKE, rope, base, FAKE, None, ctypes.byref(kv_), FAKE, ws, wsb, None)
     assert call(dm=100) == 1 and "d_model" in _err()
     assert call(rope=48) == 2 and "rope_dim" in _err()
     assert call(rope=128) == 1 and "exceeds" in _err()
@@ -201,6 +201,13 @@ def test_index_project_validation():
     assert call(x=None) == 1 and "NULL" in _err()
     assert call(shp=msa.make_shape(4, 4, 128, 64, 16, msa.MSA_FP32)) == 2
     assert call(n=0) == 0 and _err() == ""
+    # short calls split d_model and need a workspace (none at d_model 256 with 8 tokens: too short to split)
+    need = L.msa_workspace_size(7, ctypes.byref(s), 0, 64, 0, 6144, 0)
+    assert need == 24 * 64 * 5 * 64 * 4  # 24 slices of 256 dims, fp32 sums per (token, projection, dim)
+    assert L.msa_workspace_size(7, ctypes.byref(s), 0, 8, 0, 256, 0) == 0
+    assert L.msa_workspace_size(7, ctypes.byref(s), 0, 4096, 0, 6144, 0) == 0  # long calls: tiled, no split
+    assert call(n=64, dm=6144) == 3 and "workspace" in _err()
+    assert call(n=64, dm=6144, ws=FAKE, wsb=need - 1) == 3
 
 
 def test_mfma_probe_validation():

@@ -1008,6 +1008,16 @@ def test_index_project_long_call_tiles():
     _project_case(300, 512, 4, 64, 64, 83, paged=True)
 
 
+def test_index_project_short_call_splits():
+    # calls under 256 tokens split d_model over workgroups and add the fp32
+    # slices in a second kernel: RoPE pairs only (rope_dim = d_idx), pairs and
+    # plain dims (d_idx 128, RoPE 64), no RoPE, d_idx 32, paged and contiguous
+    _project_case(40, 1024, 2, 32, 0, 84, paged=False)      # 4 slices, no RoPE
+    _project_case(100, 2048, 4, 32, 32, 85, paged=True)     # 8 slices
+    _project_case(33, 4096, 4, 128, 64, 86, paged=False)    # 16 slices, 64 rotated + 64 plain dims
+    _project_case(255, 784, 4, 64, 64, 87, paged=False)     # 3 slices of 272
+
+
 def test_index_project_large_positions_paged():
     # positions near 2^20 + 255: the angle must be formed without fp32 rounding
     pos = torch.tensor([1048575, 1048831, 1048576, 0, 127, 128, 999999, 524288], dtype=torch.int64)
