@@ -513,6 +513,31 @@ def _decode_case(shape, seq_lens, seed, n_sets=1, cache_dtype=None):
     compare_lse(lse, lse_ref, torch.bfloat16)
 
 
+def test_decode_index_at_maximum_page_counts():
+    # The decode select's largest candidate counts per thread: 16384 pages (a
+    # 2M-token sequence, the most the library accepts: 64 per thread) and
+    # 12000 pages (48 per thread).  Only the index-key pages are made (N(0,1)
+    # keys and queries); the oracle scores every key of each sequence.
+    msa = _msa()
+    shape = MODEL_SHAPE
+    g = torch.Generator(device=DEV).manual_seed(88)
+    for seq_lens in ([2097152], [1536000, 700]):
+        B = len(seq_lens)
+        mp = -(-max(seq_lens) // 128)
+        npg = B * mp
+        pt = torch.randperm(npg, generator=torch.Generator().manual_seed(89)).to(torch.int32).view(B, mp).to(DEV)
+        kp = torch.randn((npg, 128, shape.d_idx), generator=g, device=DEV).to(torch.bfloat16)
+        qi = torch.randn((B, shape.h_kv, shape.d_idx), generator=g, device=DEV).to(torch.bfloat16)
+        sl = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+        _say("decode index at maximum page counts", seq_lens, mp)
+        bidx = msa.index_topk(qi, kp, top_k=shape.top_k, page_table=pt, seq_lens=sl)
+        torch.cuda.synchronize()
+        o_ids, _, pooled = orc.index_topk_decode(np64(qi), kp.cpu().double().numpy(), pt.cpu().numpy(), seq_lens,
+                                                 shape.top_k)
+        compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, (np.asarray(seq_lens) - 1) // 128)
+        del kp
+
+
 def test_decode_step_graph_replays_match_eager():
     # The decode step (index top-k, then the sparse gather) captured once in a
     # HIP graph and replayed with new queries and longer sequences written
