@@ -217,3 +217,56 @@ def test_mfma_probe_validation():
     assert L.msa_probe_mfma(0, 10, fp, None) == 1 and "n_wg" in _err()
     assert L.msa_probe_mfma(4, 0, fp, None) == 1 and "iters" in _err()
     assert L.msa_probe_mfma(4, 10, None, None) == 1 and "NULL" in _err()
+
+
+def test_bench_refuses_several_gpus():
+    # bench.py measures one GPU; a request for more exits with status 2 and says why
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+
+
+def test_bench_summarizes_traffic_without_gpu(tmp_path, monkeypatch):
+    # The counter summary is host logic: per-dispatch FETCH_SIZE / WRITE_SIZE
+    # rows of rocprofv3 CSVs (several rows of one dispatch add up), scaled by
+    # the ratio of the calibration copy's known bytes to what the same counter
+    # read for it, divided by the calls in the run.  Checked on made-up CSVs.
+    import csv
+    import importlib.util
+    import json
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "traffic.json"))
+
+    def write(path, counter, rows):
+        with open(path, "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for did, name, val in rows:
+                w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+
+    copy_kib = bench.COPY_BYTES / 1024.0
+    # the copy reads half its bytes on FETCH_SIZE (factor 2) and all of them on WRITE_SIZE (factor 1),
+    # each dispatch reported as two rows
+    write(tmp_path / "cf.csv", "FETCH_SIZE", [(1, "copyBuffer", copy_kib / 4), (1, "copyBuffer", copy_kib / 4)])
+    write(tmp_path / "cw.csv", "WRITE_SIZE", [(1, "copyBuffer", copy_kib / 2), (1, "copyBuffer", copy_kib / 2)])
+    # two sparse-decode calls: kd_kernel 100 KiB fetched / 4 written, kd_merge_kernel 10 / 1
+    fetch = [(10, "msa::kd_kernel<128>", 100), (11, "msa::kd_merge_kernel<128>", 10),
+             (12, "msa::kd_kernel<128>", 100), (13, "msa::kd_merge_kernel<128>", 10)]
+    wr = [(10, "msa::kd_kernel<128>", 4), (11, "msa::kd_merge_kernel<128>", 1),
+          (12, "msa::kd_kernel<128>", 4), (13, "msa::kd_merge_kernel<128>", 1)]
+    write(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    write(tmp_path / "w.csv", "WRITE_SIZE", wr)
+    bench.summarize_traffic("step", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                            str(tmp_path / "cw.csv"))
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["source_hash"] == bench.source_hash()
+    call = t["workloads"]["step"]["sparse_decode"]
+    assert call["fetch_bytes"] == round(110 * 1024 * 2.0) and call["write_bytes"] == round(5 * 1024 * 1.0)
+    kd = t["kernels"]["step"]["kd_kernel"]  # per launch, the merge kernel excluded
+    assert kd["fetch_bytes_per_launch"] == 100 * 1024 * 2 and kd["write_bytes_per_launch"] == 4 * 1024
+    assert "index_prefill" not in t["workloads"]["step"]  # no dispatch of that call in the run
