@@ -270,3 +270,29 @@ def test_bench_summarizes_traffic_without_gpu(tmp_path, monkeypatch):
     kd = t["kernels"]["step"]["kd_kernel"]  # per launch, the merge kernel excluded
     assert kd["fetch_bytes_per_launch"] == 100 * 1024 * 2 and kd["write_bytes_per_launch"] == 4 * 1024
     assert "index_prefill" not in t["workloads"]["step"]  # no dispatch of that call in the run
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # the boundary is usable from C: the header compiles as C99 (-pedantic) and a C
+    # program links against libmsa.so and calls its host-only entry points
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    msa.lib()  # the library must be built
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <string.h>\n#include "msa.h"\n'
+        "int main(void) {\n"
+        "  if (msa_abi_version() != MSA_ABI_VERSION) return 1;\n"
+        '  if (strcmp(msa_status_string(MSA_ERR_WORKSPACE), "") == 0) return 2;\n'
+        "  if (msa_probe_mfma(0, 1, NULL, NULL) != MSA_ERR_INVALID_ARG) return 3;\n"
+        '  if (strstr(msa_last_error(), "n_wg") == NULL) return 4;\n'
+        '  printf("ok %d\\n", msa_abi_version());\n  return 0;\n}\n')
+    libdir = os.path.join(ROOT, "block_sparse_attention_branch_amd")
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-l:libmsa.so", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == "ok 4"
