@@ -140,6 +140,12 @@ CALL_KERNELS = {
 }
 CALL_FIRST = {"index_prefill": "ki_prefill_kernel", "sparse_prefill": "ks_count",
               "index_decode": "ki_decode_scan_kernel", "sparse_decode": "kd_kernel"}
+# Legs of the default step, in launch order: two prefill legs (each starts with
+# an index prefill launch) and two decode legs (each decode call starts with an
+# index scan launch; the 64 x 128K step once, then LONG_DECODE_STEPS steps at 1M).
+STEP_PREFILL_LEGS = ("prefill128k", "prefill1m")
+LONG_DECODE_STEPS = 256
+TRAFFIC_KERNELS = ("ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "kd_kernel")
 
 
 def source_hash():
@@ -155,12 +161,19 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_bytes(workload, call):
-    if call is None or not os.path.exists(TRAFFIC_JSON):
+def _traffic():
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     with open(TRAFFIC_JSON) as fh:
         t = json.load(fh)
-    if t.get("source_hash") != source_hash():
+    return t if t.get("source_hash") == source_hash() else None
+
+
+def traffic_bytes(workload, call):
+    """Measured HBM bytes per call of `call` in `workload` (a workload or a leg
+    of the default step), or None when not measured for the current sources."""
+    t = _traffic()
+    if call is None or t is None:
         return None
     rec = t.get("workloads", {}).get(workload, {}).get(call)
     return None if rec is None else rec["bytes"]
@@ -168,11 +181,8 @@ def traffic_bytes(workload, call):
 
 def kernel_traffic(workload, kernel):
     """Measured HBM bytes per launch of `kernel`, or None (see traffic_bytes)."""
-    if not os.path.exists(TRAFFIC_JSON):
-        return None
-    with open(TRAFFIC_JSON) as fh:
-        t = json.load(fh)
-    if t.get("source_hash") != source_hash():
+    t = _traffic()
+    if t is None:
         return None
     rec = t.get("kernels", {}).get(workload, {}).get(kernel)
     return None if rec is None else rec["bytes_per_launch"]
@@ -188,13 +198,40 @@ def _pmc_rows(path, counter):
     return out
 
 
+def step_legs(names):
+    """Leg of each dispatch of a default-step run, from the launch order:
+    an index-prefill launch opens the next prefill leg (128K, 1M, 128K, ...);
+    an index-scan launch opens a decode leg, the first after the 1M prefill
+    being the 64 x 128K step and the rest the 1M steps.  Kernels that belong to
+    no call (cache appends, the dense comparison, copies) get None."""
+    legs = []
+    leg, n_pre, n_dec = None, 0, 0
+    mine = [k for ks in CALL_KERNELS.values() for k in ks]
+    for n in names:
+        if "ki_prefill_kernel" in n:
+            leg = STEP_PREFILL_LEGS[n_pre % 2]
+            n_pre += 1
+            n_dec = 0
+        elif "ki_decode_scan_kernel" in n:
+            leg = "decode64x128k" if n_dec == 0 else "decode1m"
+            n_dec += 1
+        legs.append(leg if any(k in n for k in mine) else None)
+    return legs
+
+
 def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
-    """Per-call HBM bytes from rocprofv3 counter CSVs; writes profiles/traffic.json."""
+    """Per-call HBM bytes from rocprofv3 counter CSVs; writes profiles/traffic.json.
+
+    FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB; several rows of one
+    dispatch add up) and scaled by the ratio of a plain copy's known bytes to
+    what the same counter read for it.  For the default step ("step") each
+    dispatch is attributed to its leg (step_legs) and a call's bytes are
+    averaged over that leg's occurrences; other workloads are one leg."""
     def per_dispatch(path, counter):
         d = {}
         for name, did, v in _pmc_rows(path, counter):
             d[did] = (name, d.get(did, (name, 0.0))[1] + v)
-        return list(d.values())
+        return [d[k] for k in sorted(d)]
 
     def copy_factor(path, counter):
         vals = [v for n, v in per_dispatch(path, counter) if "copy" in n.lower()]
@@ -205,34 +242,33 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
 
     ff, fk = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     wf, wk = copy_factor(copy_write_csv, "WRITE_SIZE")
-    res = {}
-    for call, kernels in CALL_KERNELS.items():
-        tot = {}
-        for key, path, counter, fac in (("fetch", fetch_csv, "FETCH_SIZE", ff), ("write", write_csv, "WRITE_SIZE", wf)):
-            rows = per_dispatch(path, counter)
-            n_calls = sum(1 for n, _ in rows if CALL_FIRST[call] in n)
-            if n_calls == 0:
-                break
-            kib = sum(v for n, v in rows if any(k in n for k in kernels))
-            tot[key] = kib * 1024.0 * fac / n_calls
-        if len(tot) == 2:
-            res[call] = {"fetch_bytes": round(tot["fetch"]), "write_bytes": round(tot["write"]),
-                         "bytes": round(tot["fetch"] + tot["write"])}
-    t = {}
-    if os.path.exists(TRAFFIC_JSON):
-        with open(TRAFFIC_JSON) as fh:
-            t = json.load(fh)
-    if t.get("source_hash") != source_hash():
-        t = {"workloads": {}, "kernels": {}}
+    runs = {"fetch": (per_dispatch(fetch_csv, "FETCH_SIZE"), ff), "write": (per_dispatch(write_csv, "WRITE_SIZE"), wf)}
+    t = _traffic() or {"workloads": {}, "kernels": {}}
     t["source_hash"] = source_hash()
     t["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_read": fk, "write_kib_read": wk,
                              "fetch_factor": ff, "write_factor": wf}
-    t["workloads"][workload] = res
+    leg_names = ([workload] if workload != "step" else list(STEP_PREFILL_LEGS) + ["decode64x128k", "decode1m"])
+    for leg_name in leg_names:
+        res = {}
+        for call, kernels in CALL_KERNELS.items():
+            tot = {}
+            for key, (rows, fac) in runs.items():
+                legs = step_legs([n for n, _ in rows]) if workload == "step" else [workload] * len(rows)
+                sel = [(n, v) for (n, v), lg in zip(rows, legs) if lg == leg_name]
+                n_calls = sum(1 for n, _ in sel if CALL_FIRST[call] in n)
+                if n_calls == 0:
+                    break
+                kib = sum(v for n, v in sel if any(k in n for k in kernels))
+                tot[key] = kib * 1024.0 * fac / n_calls
+            if len(tot) == 2:
+                res[call] = {"fetch_bytes": round(tot["fetch"]), "write_bytes": round(tot["write"]),
+                             "bytes": round(tot["fetch"] + tot["write"])}
+        t["workloads"][leg_name] = res
     kres = {}
-    for kname in ("ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "kd_kernel"):
+    for kname in TRAFFIC_KERNELS:
         rec = {}
-        for key, path, counter, fac in (("fetch", fetch_csv, "FETCH_SIZE", ff), ("write", write_csv, "WRITE_SIZE", wf)):
-            vals = [v for n, v in per_dispatch(path, counter) if kname in n and "merge" not in n]
+        for key, (rows, fac) in runs.items():
+            vals = [v for n, v in rows if kname in n and "merge" not in n]
             if vals:
                 rec[key] = float(np.mean(vals)) * 1024.0 * fac
         if len(rec) == 2:
@@ -296,28 +332,57 @@ def bench_peak(msa, args):
     bench_copy(args)
 
 
-def kernel_roofline(kern, main_flops, call_rl):
+def kernel_roofline(kern, main_flops, call_rl, workload="step"):
     """Roofline of the dominant kernel, kp_kernel (the KV-outer pass of
     msa_sparse_prefill, which does all of the main branch's MFMA work):
-    achieved = the call's algorithmic FLOPs per launch / its mean launch time,
-    both from HIP events recorded around each launch on its stream."""
+    achieved = the main branch's algorithmic FLOPs per step / launches per step
+    (FLOPs per launch) / the kernel's mean launch time, both from HIP events
+    recorded around each launch on its stream.  ``call`` repeats the figure for
+    the whole msa_sparse_prefill call (schedule, KV-outer pass and merge)."""
     k = kern.get("kp_kernel")
     if not k:
         return dict(call_rl, name="msa_sparse_prefill")
     per_launch = main_flops / k["launches_per_step"]
     achieved = per_launch / (k["avg_launch_ms"] * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic("step", "kp_kernel"),
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic(workload, "kp_kernel"),
             "name": "kp_kernel", "avg_launch_ms": k["avg_launch_ms"], "launches_per_step": k["launches_per_step"],
-            "flops_per_launch": per_launch}
+            "flops_per_launch": per_launch,
+            "call": {"name": "msa_sparse_prefill", "achieved": call_rl["achieved"], "frac": call_rl["frac"]}}
 
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline_prefill(inp, shape, budget_s=12.0, seed=0):
-    """Time the float64 oracle on sampled query rows of the prefill input."""
+def host_info():
+    """CPU model, logical CPUs and the BLAS threads the oracle runs with."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": int(threads)}
 
+
+def _time_rows(fn, rows, budget_s):
+    """Run fn(row) over rows until budget_s has passed (at least 4 rows); returns (rows done, seconds)."""
+    t0 = time.perf_counter()
+    done = 0
+    for i in rows:
+        fn(int(i))
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 4:
+            break
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline_prefill(inp, shape, budget_s=12.0, seed=0):
+    """Time the float64 oracle on sampled query rows of one contiguous prefill input."""
     from oracle import msa_oracle as orc
     q_idx = inp["q_idx"].double().cpu().numpy()
     k_idx = inp["k_idx"].double().cpu().numpy()
@@ -325,22 +390,44 @@ def cpu_baseline_prefill(inp, shape, budget_s=12.0, seed=0):
     v = inp["v"].double().cpu().numpy()
     q = inp["q"]
     n = q.shape[0]
-    rng = np.random.default_rng(seed)
-    order = rng.permutation(n)
-    t0 = time.perf_counter()
-    done = 0
-    for i in order:
-        i = int(i)
+
+    def row(i):
         ids, _, _ = orc.index_topk(q_idx[i:i + 1], k_idx, i, shape.top_k)
         orc.sparse_attention(q[i:i + 1].double().cpu().numpy(), k, v, ids, i)
-        done += 1
-        if time.perf_counter() - t0 > budget_s and done >= 8:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} random query rows of the 32768-token prefill (index top-k + sparse attention, "
-                      f"all 4 groups / 64 heads), {dt:.1f} s; BLAS threads {threads}, one Python thread"}
+
+    done, dt = _time_rows(row, np.random.default_rng(seed).permutation(n), budget_s)
+    return done, dt
+
+
+def cpu_baseline_chunk_1m(lc, shape, budget_s=8.0, seed=0):
+    """Time the float64 oracle on sampled query rows of the 1M-context chunk.
+    The oracle's index branch reads the whole contiguous index-key sequence
+    (gathered from the pages once, outside the timing).  Its main branch reads
+    only the selected blocks, so each row is handed the selected blocks of its
+    four groups packed in ascending order (block ids renumbered to that packed
+    sequence, which keeps them ascending and the diagonal block last)."""
+    from oracle import msa_oracle as orc
+    n_ctx, q_start = lc["n_ctx"], lc["q_start"]
+    pt = lc["page_table"][0]
+    nb = -(-n_ctx // BLOCK)
+    k_idx = lc["k_idx_pages"][pt[:nb].long()].reshape(nb * BLOCK, -1)[:n_ctx].double().cpu().numpy()
+    q_idx = lc["chunk_q_idx"].double().cpu().numpy()
+    nq = q_idx.shape[0]
+
+    def row(i):
+        ids, _, _ = orc.index_topk(q_idx, k_idx, q_start, shape.top_k, rows=[i])
+        p = q_start + i
+        blocks = sorted(set(int(b) for b in ids[0].ravel() if b >= 0))
+        pages = pt[torch.tensor(blocks, device=pt.device)].long()
+        kk = lc["k_pages"][pages].transpose(1, 2).reshape(len(blocks) * BLOCK, shape.h_kv, shape.d_h)
+        vv = lc["v_pages"][pages].transpose(1, 2).reshape(len(blocks) * BLOCK, shape.h_kv, shape.d_h)
+        pos = {b: j for j, b in enumerate(blocks)}
+        ids_c = np.where(ids >= 0, np.vectorize(lambda b: pos.get(int(b), -1))(ids), -1)
+        p_c = pos[p // BLOCK] * BLOCK + p % BLOCK
+        orc.sparse_attention(lc["chunk_q"][i:i + 1].double().cpu().numpy(), kk.double().cpu().numpy(),
+                             vv.double().cpu().numpy(), ids_c, p_c)
+
+    return _time_rows(row, np.random.default_rng(seed).permutation(nq), budget_s)
 
 
 def cpu_baseline_decode(dec, shape, n_seqs=2):
@@ -373,8 +460,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="step", choices=["step", "prefill128k", "long1m", "decode_fp8", "backward32k",
-                                                             "project", "copy", "peak"])
+    ap.add_argument("--workload", default="step", choices=["step", "step32k", "prefill128k", "long1m", "decode_fp8",
+                                                             "backward32k", "project", "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -401,6 +488,8 @@ def main():
         bench_peak(msa, args)
     elif args.workload == "step":
         bench_step(msa, args)
+    elif args.workload == "step32k":
+        bench_step32k(msa, args)
     elif args.workload == "decode_fp8":
         bench_decode_fp8(msa, args)
     elif args.workload == "prefill128k":
@@ -414,6 +503,284 @@ def main():
 
 
 def bench_step(msa, args):
+    """The default step: every hot-path call at 128K and 1M context.
+
+    Legs, in launch order:
+      prefill128k    planted 131072-token causal prefill (contiguous cache):
+                     msa_index_topk + msa_sparse_prefill over all queries;
+      prefill1m      chunked prefill of the last 8192 queries of a 1,048,576-token
+                     paged cache: msa_index_topk + msa_sparse_prefill;
+      decode64x128k  one decode step of 64 sequences x 131072 tokens, paged,
+                     4 rotating query sets: msa_index_topk + msa_sparse_decode;
+      decode1m       256 decode steps of the 1M sequence (batch 1), each after
+                     appending its token to the caches; every step is launched
+                     from an idle GPU and timed on its own (p50 / p99).
+    ``value`` = prefill tokens of the step / the GPU time of the four prefill
+    calls (HIP events on the launch stream)."""
+    dev = "cuda"
+    shape = MODEL_SHAPE
+    B, L_dec = 64, 131072
+    t_gen = time.perf_counter()
+    big = gen_planted_prefill(131072, shape, device=dev)
+    lc = gen_long_context(device=dev)
+    dec = gen_decode_paged(B, L_dec, shape, seed=3, device=dev, n_query_sets=4)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16)
+
+    def wsz(op, **kw):
+        return torch.empty(max(1, msa.workspace_size(op, s_idx, **kw)), dtype=torch.uint8, device=dev)
+
+    # leg prefill128k
+    n_a = big["q"].shape[0]
+    bidx_a = torch.empty((n_a, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o_a = torch.empty_like(big["q"])
+    ws_ia, ws_pa = wsz(msa.OP_INDEX, n_q=n_a, n_kv=n_a), wsz(msa.OP_PREFILL, n_q=n_a, n_kv=n_a)
+    # leg prefill1m
+    n_ctx, q_start = lc["n_ctx"], lc["q_start"]
+    n_b = lc["chunk_q"].shape[0]
+    pt_l = lc["page_table"]
+    bidx_b = torch.empty((n_b, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o_b = torch.empty_like(lc["chunk_q"])
+    ws_ib = wsz(msa.OP_INDEX, n_q=n_b, q_start=q_start, n_kv=n_ctx)
+    ws_pb = wsz(msa.OP_PREFILL, n_q=n_b, q_start=q_start, n_kv=n_ctx)
+    # leg decode64x128k
+    mp_c = dec["page_table"].shape[1]
+    bidx_c = [torch.empty((B, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev) for _ in range(4)]
+    o_c = torch.empty((B, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
+    ws_ic, ws_dc = wsz(msa.OP_INDEX_DECODE, batch=B, n_q=1, max_pages=mp_c), wsz(msa.OP_DECODE, batch=B, n_q=1)
+    qsets = [dec["q"][i].contiguous() for i in range(4)]
+    qisets = [dec["q_idx"][i].contiguous() for i in range(4)]
+    # leg decode1m
+    n_dec = lc["step_q"].shape[0]
+    sl_d = torch.tensor([n_ctx], dtype=torch.int32, device=dev)
+    bidx_d = torch.empty((1, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev)
+    o_d = torch.empty((1, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
+    ws_id = wsz(msa.OP_INDEX_DECODE, batch=1, n_q=1, max_pages=pt_l.shape[1])
+    ws_dd = wsz(msa.OP_DECODE, batch=1, n_q=1)
+    app_page = [int(pt_l[0, (n_ctx + t) // BLOCK]) for t in range(n_dec)]
+
+    prefill_calls = [
+        lambda: msa.index_topk(big["q_idx"], big["k_idx"], top_k=16, out=bidx_a, workspace=ws_ia),
+        lambda: msa.sparse_prefill(big["q"], big["k"], big["v"], bidx_a, out=o_a, workspace=ws_pa),
+        lambda: msa.index_topk(lc["chunk_q_idx"], lc["k_idx_pages"], top_k=16, q_start=q_start, page_table=pt_l[0],
+                               n_kv=n_ctx, out=bidx_b, workspace=ws_ib),
+        lambda: msa.sparse_prefill(lc["chunk_q"], lc["k_pages"], lc["v_pages"], bidx_b, q_start=q_start,
+                                   page_table=pt_l[0], n_kv=n_ctx, out=o_b, workspace=ws_pb),
+    ]
+
+    def decode_c(j):
+        return [lambda: msa.index_topk(qisets[j], dec["k_idx_pages"], top_k=16, page_table=dec["page_table"],
+                                       seq_lens=dec["seq_lens"], out=bidx_c[j], workspace=ws_ic),
+                lambda: msa.sparse_decode(qsets[j], dec["k_pages"], dec["v_pages"], dec["page_table"],
+                                          dec["seq_lens"], bidx_c[j], out=o_c, workspace=ws_dc)]
+
+    def append(t):
+        # the new token's K, V and index key go into the cache before its step
+        pg, row = app_page[t], (n_ctx + t) % BLOCK
+        lc["k_pages"][pg, :, row] = lc["step_k"][t]
+        lc["v_pages"][pg, :, row] = lc["step_v"][t]
+        lc["k_idx_pages"][pg, row] = lc["step_k_idx"][t]
+        sl_d.fill_(n_ctx + t + 1)
+
+    def decode_1m(t):
+        return [lambda: msa.index_topk(lc["step_q_idx"][t], lc["k_idx_pages"], top_k=16, page_table=pt_l,
+                                       seq_lens=sl_d, out=bidx_d, workspace=ws_id),
+                lambda: msa.sparse_decode(lc["step_q"][t], lc["k_pages"], lc["v_pages"], pt_l, sl_d, bidx_d,
+                                          out=o_d, workspace=ws_dd)]
+
+    names = ["prefill128k_index", "prefill128k_sparse", "prefill1m_index", "prefill1m_sparse",
+             "decode64x128k_index", "decode64x128k_sparse"]
+    timer = CallTimer(names)
+    d1m = CallTimer(["decode1m_index", "decode1m_sparse"])
+
+    def run_step(s, timed):
+        ev = timer.step(prefill_calls + decode_c(s % 4)) if timed else [f() for f in prefill_calls + decode_c(s % 4)]
+        evd = []
+        for t in range(n_dec):
+            append(t)
+            if timed:
+                torch.cuda.synchronize()
+                evd.append(d1m.step(decode_1m(t)))
+            else:
+                for f in decode_1m(t):
+                    f()
+        return ev, evd
+
+    for w in range(args.warmup):
+        run_step(w, False)
+    torch.cuda.synchronize()
+    evs, evds = [], []
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev, evd = run_step(s, True)
+        evs.append(ev)
+        evds.extend(evd)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect(evs)
+    d1m.collect(evds)
+    print(f"[bench] {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+    # Kernel timing: steps again with every launch of the hot kernels bracketed
+    # by HIP events on its stream (after the timed region: the extra events add
+    # gaps between launches that would inflate the call times).
+    kern = {}
+    if not args.no_kernel_timing:
+        reps = min(args.steps, 5)
+        for k in TRAFFIC_KERNELS:
+            msa.profile_read(k)
+        msa.profile_enable(True)
+        for s in range(reps):
+            run_step(s, False)
+        torch.cuda.synchronize()
+        msa.profile_enable(False)
+        for k in TRAFFIC_KERNELS:
+            tot, cnt = msa.profile_read(k)
+            if cnt:
+                kern[k] = {"launches_per_step": cnt / reps, "avg_launch_ms": round(tot / cnt, 5),
+                           "ms_per_step": round(tot / reps, 4)}
+    # the 1M decode steps replayed from a captured HIP graph (new queries and the
+    # sequence length written into the captured buffers before each replay)
+    qb, qib = lc["step_q"][0].clone(), lc["step_q_idx"][0].clone()
+
+    def dstep():
+        msa.index_topk(qib, lc["k_idx_pages"], top_k=16, page_table=pt_l, seq_lens=sl_d, out=bidx_d, workspace=ws_id)
+        msa.sparse_decode(qb, lc["k_pages"], lc["v_pages"], pt_l, sl_d, bidx_d, out=o_d, workspace=ws_dd)
+
+    sl_d.fill_(n_ctx + 1)
+    dstep()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dstep()
+    torch.cuda.synchronize()
+    graph_ms = []
+    for t in range(n_dec):
+        qb.copy_(lc["step_q"][t])
+        qib.copy_(lc["step_q_idx"][t])
+        sl_d.fill_(n_ctx + t + 1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms.append(e0.elapsed_time(e1))
+    graph_us = np.array(graph_ms) * 1e3
+    del graph
+
+    t = {n: timer.mean_ms(n) for n in names}
+    dstep_us = (np.array(d1m.records["decode1m_index"]) + np.array(d1m.records["decode1m_sparse"])) * 1e3
+    t1m_i, t1m_s = d1m.mean_ms("decode1m_index"), d1m.mean_ms("decode1m_sparse")
+    prefill_ms = t["prefill128k_index"] + t["prefill128k_sparse"] + t["prefill1m_index"] + t["prefill1m_sparse"]
+    fa = prefill_counts(n_a, 0, shape)
+    fb = prefill_counts(n_b, q_start, shape)
+    dc = decode_bytes([L_dec] * B, shape)
+    dd = decode_bytes([n_ctx + n_dec // 2], shape)  # mid-run length of the 1M decode steps
+    kd = {"prefill128k": ("ki_prefill_kernel+ki_merge_kernel", "ks_* schedule + kp_kernel + km_kernel"),
+          "prefill1m": ("ki_prefill_kernel+ki_merge_kernel", "ks_* schedule + kp_kernel + km_kernel"),
+          "decode64x128k": ("ki_decode_scan_kernel+ki_decode_select_kernel", "kd_kernel(+kd_merge_kernel)"),
+          "decode1m": ("ki_decode_scan_kernel+ki_decode_select_kernel", "kd_kernel+kd_merge_kernel")}
+    rl = {}
+    for leg, (bound, unit, wi, ws, ti, ts, recs) in {
+            "prefill128k": ("mfma", "TFLOP/s", fa[0], fa[1], "prefill128k_index", "prefill128k_sparse", timer),
+            "prefill1m": ("mfma", "TFLOP/s", fb[0], fb[1], "prefill1m_index", "prefill1m_sparse", timer),
+            "decode64x128k": ("hbm", "GB/s", dc[0], dc[1], "decode64x128k_index", "decode64x128k_sparse", timer),
+            "decode1m": ("hbm", "GB/s", dd[0], dd[1], "decode1m_index", "decode1m_sparse", d1m)}.items():
+        for call, work, nm, kn in (("index", wi, ti, kd[leg][0]), ("sparse", ws, ts, kd[leg][1])):
+            ms_ = recs.mean_ms(nm)
+            abi = ("index_prefill" if leg.startswith("prefill") else "index_decode") if call == "index" else \
+                ("sparse_prefill" if leg.startswith("prefill") else "sparse_decode")
+            rl[f"{leg}_{call}"] = dict(roofline(bound, work, ms_, unit, abi, leg), kernel=kn, ms=round(ms_, 4),
+                                       p10_ms=round(recs.pct(nm, 10), 4), p90_ms=round(recs.pct(nm, 90), 4))
+    legs = {
+        "prefill128k": {"tokens": n_a, "ms": round(t["prefill128k_index"] + t["prefill128k_sparse"], 4),
+                        "tokens_per_s": round(n_a / ((t["prefill128k_index"] + t["prefill128k_sparse"]) * 1e-3), 1)},
+        "prefill1m": {"tokens": n_b, "ctx": n_ctx, "ms": round(t["prefill1m_index"] + t["prefill1m_sparse"], 4),
+                      "tokens_per_s": round(n_b / ((t["prefill1m_index"] + t["prefill1m_sparse"]) * 1e-3), 1)},
+        "decode64x128k": {"us_per_step": round((t["decode64x128k_index"] + t["decode64x128k_sparse"]) * 1e3, 2)},
+        "decode1m": {"us_p50": round(float(np.percentile(dstep_us, 50)), 1),
+                     "us_p99": round(float(np.percentile(dstep_us, 99)), 1),
+                     "us_mean": round(float(dstep_us.mean()), 1), "steps_timed": int(dstep_us.size),
+                     "graph_us_p50": round(float(np.percentile(graph_us, 50)), 1),
+                     "graph_us_p99": round(float(np.percentile(graph_us, 99)), 1)},
+    }
+    # retrieval check of the planted workload (a property of the output, not timed)
+    got = bidx_a.cpu()
+    des = big["designated"]
+    legs["prefill128k"]["planted_blocks_retrieved"] = bool(all(
+        set(big["planted_blocks"][r].tolist()) <= set(got[int(i), r].tolist())
+        for i in des[:256] for r in range(shape.h_kv)))
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(big["q"])
+        msa.dense_prefill(big["q"], big["k"], big["v"], out=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        msa.dense_prefill(big["q"], big["k"], big["v"], out=od)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1)
+        ta = t["prefill128k_index"] + t["prefill128k_sparse"]
+        dense = {"workload": "prefill 1x131072", "ms": round(dms, 3), "tflops": round(fa[2] / (dms * 1e-3) / 1e12, 1),
+                 "speedup_msa_prefill_vs_dense": round(dms / ta, 2), "kernel": "kg_kernel (Q-outer, Eq. (1))"}
+        del od
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        na_done, na_s = cpu_baseline_prefill(big, shape, budget_s=10.0)
+        nb_done, nb_s = cpu_baseline_chunk_1m(lc, shape, budget_s=8.0)
+        sec_a, sec_b = na_s / na_done, nb_s / nb_done
+        hi = host_info()
+        cpu = {"value": round((n_a + n_b) / (n_a * sec_a + n_b * sec_b), 3), "unit": "tokens/s",
+               "cores": hi["blas_threads"], "kind": "oracle",
+               "sample": f"{na_done} random query rows of the 131072-token planted prefill ({na_s:.1f} s) and "
+                         f"{nb_done} random rows of the 8192-query chunk at 1M context ({nb_s:.1f} s), each row "
+                         f"the index top-k and sparse attention of all 4 groups / 64 heads; per-row times scaled to "
+                         f"the step's {n_a} + {n_b} prefill tokens",
+               "host": hi, "decode": cpu_baseline_decode(dec, shape)}
+
+    main_fl = fa[1] + fb[1]
+    line = {
+        "metric": "MSA prefill tok/s + decode us/step at 128K/1M ctx; % MFMA / HBM roofline",
+        "value": round((n_a + n_b) / (prefill_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic, seeded (planted-needle index keys at 128K, N(0,1) elsewhere); no weights",
+        "config": {"workload": "prefill 1x131072 planted (whole causal prefill) + prefill chunk of the last 8192 "
+                               "queries at 1048576 ctx (paged) + decode step 64x131072 paged + 256 decode steps "
+                               "(batch 1) at 1048576 ctx; 64 q / 4 kv heads, d_h 128, d_idx 64, B_k 128, k 16, "
+                               "diagonal block kept",
+                   "prefill_tokens_per_step": n_a + n_b, "seq_len": n_a, "long_ctx": n_ctx, "decode_batch": B,
+                   "decode_ctx": L_dec, "long_decode_steps": n_dec, "parallelism": "single GPU"},
+        "prefill_ms": round(prefill_ms, 4),
+        "decode_us_per_step": legs["decode64x128k"]["us_per_step"],
+        "decode_1m_us_p50": legs["decode1m"]["us_p50"],
+        "decode_1m_us_p99": legs["decode1m"]["us_p99"],
+        "legs": legs,
+        "roofline": kernel_roofline(kern, main_fl, roofline("mfma", main_fl, t["prefill128k_sparse"]
+                                                             + t["prefill1m_sparse"], "TFLOP/s"), "step"),
+        "rooflines": rl,
+        "kernels": kern,
+        "dense_gqa": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def bench_step32k(msa, args):
+    """The 32K prefill + 64 x 128K decode step (the smaller prefill configuration)."""
     dev = "cuda"
     shape = MODEL_SHAPE
     n = 32768
@@ -492,13 +859,13 @@ def bench_step(msa, args):
     idx_fl, main_fl, dense_fl = prefill_counts(n, 0, shape)
     didx_b, dmain_b, ddense_b = decode_bytes([131072] * B, shape)
     rl = {
-        "index_prefill": dict(roofline("mfma", idx_fl, t_ip, "TFLOP/s", "index_prefill"),
+        "index_prefill": dict(roofline("mfma", idx_fl, t_ip, "TFLOP/s", "index_prefill", "step32k"),
                               kernel="ki_prefill_kernel+ki_merge_kernel"),
-        "sparse_prefill": dict(roofline("mfma", main_fl, t_sp, "TFLOP/s", "sparse_prefill"),
+        "sparse_prefill": dict(roofline("mfma", main_fl, t_sp, "TFLOP/s", "sparse_prefill", "step32k"),
                                kernel="ks_* schedule + kp_kernel + km_kernel (per window)"),
-        "index_decode": dict(roofline("hbm", didx_b, t_id, "GB/s", "index_decode"),
+        "index_decode": dict(roofline("hbm", didx_b, t_id, "GB/s", "index_decode", "step32k"),
                              kernel="ki_decode_scan_kernel+ki_decode_select_kernel"),
-        "sparse_decode": dict(roofline("hbm", dmain_b, t_sd, "GB/s", "sparse_decode"),
+        "sparse_decode": dict(roofline("hbm", dmain_b, t_sd, "GB/s", "sparse_decode", "step32k"),
                               kernel="kd_kernel+kd_merge_kernel"),
     }
     for k_, ms_ in (("index_prefill", t_ip), ("sparse_prefill", t_sp), ("index_decode", t_id), ("sparse_decode", t_sd)):
@@ -527,11 +894,15 @@ def bench_step(msa, args):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_prefill(pre, shape)
-        cpu["decode"] = cpu_baseline_decode(dec, shape)
+        done, dt = cpu_baseline_prefill(pre, shape)
+        hi = host_info()
+        cpu = {"value": round(done / dt, 3), "unit": "tokens/s", "cores": hi["blas_threads"], "kind": "oracle",
+               "sample": f"{done} random query rows of the 32768-token prefill (index top-k + sparse attention, "
+                         f"all 4 groups / 64 heads), {dt:.1f} s", "host": hi,
+               "decode": cpu_baseline_decode(dec, shape)}
 
     line = {
-        "metric": "MSA prefill tok/s + decode us/step; % MFMA / HBM roofline",
+        "metric": "MSA prefill tok/s + decode us/step (32K prefill variant); % MFMA / HBM roofline",
         "value": round(n / (prefill_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -549,7 +920,7 @@ def bench_step(msa, args):
                    "parallelism": "single GPU"},
         "prefill_ms": round(prefill_ms, 4),
         "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
-        "roofline": kernel_roofline(kern, main_fl, rl["sparse_prefill"]),
+        "roofline": kernel_roofline(kern, main_fl, rl["sparse_prefill"], "step32k"),
         "rooflines": rl,
         "kernels": kern,
         "dense_gqa": dense,

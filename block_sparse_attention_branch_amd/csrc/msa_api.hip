@@ -93,6 +93,34 @@ size_t ki_prefill_ws(const msa_shape& s, int32_t n_q, int32_t q_start, int need_
   return ((keys + 255) & ~size_t(255)) + (((size_t)p.n_rows * 4 + 255) & ~size_t(255));
 }
 
+// Decode mode of msa_index_topk after its checks: the paged scan writes the
+// pooled score of every page to `scores` [batch, h_kv, max_pages], then the
+// select reads them back.
+msa_status launch_index_decode(const msa_shape& s, int32_t batch, const void* q_idx, const msa_kv* kv,
+                               int32_t* block_idx, float* block_score, float* scores, hipStream_t stream,
+                               const char* what) {
+  msa::KiDecodeArgs a{};
+  a.q_idx = q_idx;
+  a.k_idx = kv->k_idx;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.batch = batch;
+  a.h_kv = s.h_kv;
+  a.max_pages = kv->max_pages;
+  a.pages_per_wg = msa::kKiDecodePagesPerWg;
+  a.idx_scale = idx_scale_of(s);
+  a.force_local = s.force_local;
+  a.pool = s.pool;
+  a.top_k = s.top_k;
+  // the diagonal block is scored when its pooled score is reported or when it
+  // competes as an ordinary candidate
+  a.need_diag = (block_score != nullptr || !s.force_local) ? 1 : 0;
+  a.scores = scores;
+  a.block_idx = block_idx;
+  a.block_score = block_score;
+  return hip_status(msa::launch_ki_decode(kernel_dtype(s), s.d_idx, a, stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +136,11 @@ msa_status msa_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* hip_str
   if (n_wg < 1 || iters < 1) return fail(MSA_ERR_INVALID_ARG, "n_wg=%d iters=%d must be >= 1", n_wg, iters);
   if (!out) return fail(MSA_ERR_INVALID_ARG, "out is NULL");
   return hip_status(msa::launch_mfma_probe(n_wg, iters, out, static_cast<hipStream_t>(hip_stream)), "msa_probe_mfma");
+}
+
+msa_status msa_test_schedule_lds_limit(int32_t max_blocks) {
+  msa::set_schedule_lds_limit(max_blocks);
+  return ok();
 }
 
 msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
@@ -189,7 +222,9 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   if (!aligned16(q_idx) || !aligned16(kv->k_idx)) return fail(MSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float idx_scale = idx_scale_of(s);
-  const int need_diag = (block_score != nullptr) ? 1 : 0;
+  // The diagonal block must be scored when its pooled score is reported, and
+  // when it competes as an ordinary candidate (no forced local block).
+  const int need_diag = (block_score != nullptr || !s.force_local) ? 1 : 0;
 
   if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
   if (kv->seq_lens) {  // decode mode
@@ -201,28 +236,8 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
     if (!q_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "q_idx/block_idx is NULL");
     const size_t need = (size_t)batch * s.h_kv * kv->max_pages * 4;
     if ((st = check_ws(workspace, ws_bytes, need)) != MSA_OK) return st;
-    msa::KiDecodeArgs a{};
-    a.q_idx = q_idx;
-    a.k_idx = kv->k_idx;
-    a.page_table = kv->page_table;
-    a.seq_lens = kv->seq_lens;
-    a.batch = batch;
-    a.h_kv = s.h_kv;
-    a.max_pages = kv->max_pages;
-    {
-      const char* e = getenv("MSA_KI_PAGES_PER_WG");
-      const int v = e ? atoi(e) : 0;
-      a.pages_per_wg = (v >= 4 && v <= 256) ? v : 16;
-    }
-    a.idx_scale = idx_scale;
-    a.force_local = s.force_local;
-    a.pool = s.pool;
-    a.top_k = s.top_k;
-    a.need_diag = need_diag;
-    a.scores = static_cast<float*>(workspace);
-    a.block_idx = block_idx;
-    a.block_score = block_score;
-    return hip_status(msa::launch_ki_decode(kernel_dtype(s), s.d_idx, a, stream), "msa_index_topk(decode)");
+    return launch_index_decode(s, batch, q_idx, kv, block_idx, block_score, static_cast<float*>(workspace), stream,
+                               "msa_index_topk(decode)");
   }
 
   if (batch != 1) return fail(MSA_ERR_INVALID_ARG, "prefill mode handles one sequence: batch must be 1, got %d", batch);

@@ -28,6 +28,7 @@
 #include "msa_kvouter.hpp"
 #include "msa_profile.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace msa {
@@ -1037,10 +1038,13 @@ __global__ __launch_bounds__(D) void kd_merge_kernel(KdArgs a) {
 // ====================================================================
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-static int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
+// Largest block count whose schedule counters live in LDS; a test hook can
+// lower it (to 0) so that the tests run the global-atomic path too.
+static std::atomic<int> g_sched_lds_limit{-1};
+void set_schedule_lds_limit(int max_blocks) { g_sched_lds_limit.store(max_blocks < 0 ? -1 : max_blocks); }
+static int sched_lds_limit(int dflt) {
+  const int v = g_sched_lds_limit.load();
+  return v < 0 ? dflt : std::min(v, dflt);
 }
 
 // Compute units of the current device (cached per device).
@@ -1056,11 +1060,9 @@ int num_cus() {
   return cached[dev];
 }
 
-template <typename T, int D>
-static int kp_wgs_per_cu() {
-  const int e = env_int("MSA_KP_WG_PER_CU", 0);
-  return e > 0 ? e : 1;
-}
+// KV-outer workgroups per CU: one 512-thread workgroup with two 64 KB K/V
+// buffers fills a CU's LDS.
+constexpr int kKpWgPerCu = 1;
 
 void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv, int32_t top_k, int32_t window,
                      int32_t chunk, bool ordered) {
@@ -1085,6 +1087,13 @@ void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv,
   p.total = off;
 }
 
+// Window sizing of the sparse prefill (measured optima, see prefill_plan):
+// partial bytes a window may use at least and at most, and the average tokens
+// per (group, block) cell the window is grown to.
+constexpr size_t kPartialBudgetBytes = size_t(128) << 20;
+constexpr size_t kPartialCapBytes = size_t(4096) << 20;
+constexpr int64_t kCellTokens = 40;
+
 PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
                          int32_t h_kv, int32_t d_h, int32_t top_k) {
   PrefillPlan p{};
@@ -1097,9 +1106,9 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   // small window leaves few tokens per (group, block) cell and the items
   // mostly empty, so the window grows until a cell holds about
   // `cell_tokens` tokens on average (bounded by a hard memory cap).
-  const size_t budget = (size_t)env_int("MSA_PARTIAL_BUDGET_MB", 128) << 20;
-  const size_t cap = (size_t)env_int("MSA_PARTIAL_CAP_MB", 4096) << 20;
-  const int64_t cell_tokens = env_int("MSA_CELL_TOKENS", 40);
+  const size_t budget = kPartialBudgetBytes;
+  const size_t cap = kPartialCapBytes;
+  const int64_t cell_tokens = kCellTokens;
   const int64_t blocks_seen = ((int64_t)q_start + n_q - 1) / kBlock + 1;
   int64_t w = (int64_t)(budget / per_token);
   const int64_t w_occ = (cell_tokens * blocks_seen + std::max(1, top_k - 1) - 1) / std::max(1, top_k - 1);
@@ -1146,7 +1155,7 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   const unsigned row_blocks = (unsigned)((rows + 255) / 256);
   // LDS counters while a window's blocks fit (the threshold can be lowered
   // through the environment, which is how the global-atomic path is tested)
-  const bool lds_sched = pl.n_blocks <= std::min(kSchedLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kSchedLdsBlocks));
+  const bool lds_sched = pl.n_blocks <= sched_lds_limit(kSchedLdsBlocks);
   // With few (window, group) pairs (one long window, as in a chunked prefill
   // at long context) each is split into token slices, enough to fill the
   // chip, of at least 128 tokens; otherwise one workgroup per pair (slices
@@ -1158,7 +1167,7 @@ hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, Sch
   }
   const unsigned cell_blocks = (unsigned)((pl.n_cells + 255) / 256);
   if (s.bitmap) {  // ordered: bitmap -> counts -> offsets -> token lists in order
-    if (pl.n_blocks <= std::min(kBitsLdsBlocks, env_int("MSA_SCHED_LDS_BLOCKS", kBitsLdsBlocks))) {
+    if (pl.n_blocks <= sched_lds_limit(kBitsLdsBlocks)) {
       const unsigned tiles = (unsigned)((pl.window + 255) / 256);
       hipLaunchKernelGGL(ks_bits_set_lds_kernel, dim3((unsigned)pl.n_windows * tiles, (unsigned)a.h_kv), dim3(256),
                          (size_t)pl.n_blocks * 8 * 4, st, s);
@@ -1243,7 +1252,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     const int tok = std::min<int>(pl.window, a.n_q - w * pl.window);
     const int64_t bound = (int64_t)tok * a.h_kv * a.top_k / pl.chunk + (int64_t)a.h_kv * pl.n_blocks + 1;
     kp.w = w;
-    int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kp_wgs_per_cu<T, D>());
+    int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kKpWgPerCu);
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
     const int pk = profile_begin(PK_KP, st);
     hipLaunchKernelGGL((kp_kernel<T, D, TC>), dim3(grid), dim3(kKpThreads), 0, st, kp);
@@ -1308,8 +1317,6 @@ DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, in
   // workgroups of kKdWaves waves; aim for >= 256 of them (one per CU) while
   // every wave keeps at least one 32-key unit
   while (split * kKdWaves < top_k * 4 && (int64_t)pairs * split < 256) split <<= 1;
-  const int env = env_int("MSA_KD_SPLIT", 0);
-  if (env > 0) split = std::min(16, env);
   p.split = split;
   const int G = h_q / h_kv;
   size_t off = 0;

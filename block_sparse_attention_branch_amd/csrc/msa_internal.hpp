@@ -10,6 +10,8 @@ namespace msa {
 
 // Largest page-table width (pages per sequence) the decode calls accept.
 constexpr int kMaxDecodePages = 16384;
+// Pages of one sequence scored by one workgroup of the decode index scan.
+constexpr int kKiDecodePagesPerWg = 16;
 
 // ---------------------------------------------------------------- index
 // Tiles of 256 (query, group) rows; the block range [0, hi) of a tile is cut
@@ -134,6 +136,9 @@ void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv,
                      int32_t chunk, bool ordered = false);
 hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const PrefillPlan& pl,
                                  hipStream_t st);
+// Test hook: largest block count whose schedule counters are kept in LDS
+// (< 0 restores the built-in limits; 0 forces the global-atomic path).
+void set_schedule_lds_limit(int max_blocks);
 bool attn_supported(int dtype, int d_h);
 
 struct DecodePlan {

@@ -56,7 +56,7 @@ _lib = None
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
            "msa_sparse_prefill_backward", "msa_index_project",
            "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
-           "msa_profile_enable", "msa_profile_read", "msa_probe_mfma"]
+           "msa_profile_enable", "msa_profile_read", "msa_probe_mfma", "msa_test_schedule_lds_limit"]
 
 
 def lib() -> ctypes.CDLL:
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.msa_profile_read.restype = ctypes.c_int
         L.msa_probe_mfma.argtypes = [i32, i32, P(ctypes.c_float), ctypes.c_void_p]
         L.msa_probe_mfma.restype = ctypes.c_int
+        L.msa_test_schedule_lds_limit.argtypes = [i32]
+        L.msa_test_schedule_lds_limit.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -178,6 +180,13 @@ def probe_mfma(n_wg: int, iters: int, out, stream=None) -> None:
     ``out`` is a float32 device tensor of n_wg elements."""
     _check(lib().msa_probe_mfma(int(n_wg), int(iters), ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_float)),
                                 _stream(stream)))
+
+
+def test_schedule_lds_limit(max_blocks: int) -> None:
+    """msa_test_schedule_lds_limit (test hook): cap the block count whose
+    prefill schedule counters live in LDS (0 forces global atomics, < 0
+    restores the built-in limits)."""
+    _check(lib().msa_test_schedule_lds_limit(int(max_blocks)))
 
 
 def profile_read(kernel: str):

@@ -292,6 +292,15 @@ msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launc
  * NULL: MSA_ERR_INVALID_ARG.                                               */
 msa_status msa_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* hip_stream);
 
+/* Test hook (not part of the method): the prefill schedule keeps its
+ * per-(group, block) counters in LDS while a call has at most a built-in
+ * number of KV blocks (16384; 2048 for the backward's ordered schedule) and
+ * uses global atomics beyond that.  msa_test_schedule_lds_limit(n), n >= 0,
+ * lowers that number to min(n, built-in) for every later call in the process
+ * (0 forces the global-atomic path); n < 0 restores the built-in numbers.
+ * Results do not depend on the path.  Always MSA_OK.                       */
+msa_status msa_test_schedule_lds_limit(int32_t max_blocks);
+
 #ifdef __cplusplus
 }
 #endif

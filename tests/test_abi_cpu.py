@@ -254,22 +254,55 @@ def test_bench_summarizes_traffic_without_gpu(tmp_path, monkeypatch):
     # each dispatch reported as two rows
     write(tmp_path / "cf.csv", "FETCH_SIZE", [(1, "copyBuffer", copy_kib / 4), (1, "copyBuffer", copy_kib / 4)])
     write(tmp_path / "cw.csv", "WRITE_SIZE", [(1, "copyBuffer", copy_kib / 2), (1, "copyBuffer", copy_kib / 2)])
-    # two sparse-decode calls: kd_kernel 100 KiB fetched / 4 written, kd_merge_kernel 10 / 1
+    # a one-leg workload: two sparse-decode calls, kd_kernel 100 KiB fetched / 4 written, kd_merge_kernel 10 / 1
     fetch = [(10, "msa::kd_kernel<128>", 100), (11, "msa::kd_merge_kernel<128>", 10),
              (12, "msa::kd_kernel<128>", 100), (13, "msa::kd_merge_kernel<128>", 10)]
     wr = [(10, "msa::kd_kernel<128>", 4), (11, "msa::kd_merge_kernel<128>", 1),
           (12, "msa::kd_kernel<128>", 4), (13, "msa::kd_merge_kernel<128>", 1)]
     write(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     write(tmp_path / "w.csv", "WRITE_SIZE", wr)
-    bench.summarize_traffic("step", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
-                            str(tmp_path / "cw.csv"))
+    bench.summarize_traffic("decode_fp8", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                            str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"))
     t = json.load(open(tmp_path / "traffic.json"))
     assert t["source_hash"] == bench.source_hash()
-    call = t["workloads"]["step"]["sparse_decode"]
+    call = t["workloads"]["decode_fp8"]["sparse_decode"]
     assert call["fetch_bytes"] == round(110 * 1024 * 2.0) and call["write_bytes"] == round(5 * 1024 * 1.0)
-    kd = t["kernels"]["step"]["kd_kernel"]  # per launch, the merge kernel excluded
+    kd = t["kernels"]["decode_fp8"]["kd_kernel"]  # per launch, the merge kernel excluded
     assert kd["fetch_bytes_per_launch"] == 100 * 1024 * 2 and kd["write_bytes_per_launch"] == 4 * 1024
-    assert "index_prefill" not in t["workloads"]["step"]  # no dispatch of that call in the run
+    assert "index_prefill" not in t["workloads"]["decode_fp8"]  # no dispatch of that call in the run
+
+    # the default step: its legs are told apart by launch order (prefill 128K, prefill 1M, the
+    # 64 x 128K decode step, then 1M decode steps); a cache-append kernel belongs to no call
+    def step(did0, kp128, kp1m, kd1m):
+        return [(did0, "ki_prefill_kernel", 7), (did0 + 1, "ks_count_lds_kernel", 1),
+                (did0 + 2, "kp_kernel", kp128), (did0 + 3, "km_kernel", 3), (did0 + 4, "kp_kernel", kp128),
+                (did0 + 5, "km_kernel", 3), (did0 + 6, "ki_prefill_kernel", 9), (did0 + 7, "ks_count_lds_kernel", 2),
+                (did0 + 8, "kp_kernel", kp1m), (did0 + 9, "km_kernel", 5), (did0 + 10, "ki_decode_scan_kernel", 50),
+                (did0 + 11, "kd_kernel", 20), (did0 + 12, "index_put_kernel", 99),
+                (did0 + 13, "ki_decode_scan_kernel", 30), (did0 + 14, "kd_kernel", kd1m),
+                (did0 + 15, "index_put_kernel", 99), (did0 + 16, "ki_decode_scan_kernel", 30),
+                (did0 + 17, "kd_kernel", kd1m)]
+    fetch = step(100, 40, 60, 2) + step(200, 40, 60, 2)
+    wr = [(d, n, 1) for d, n, _ in fetch]
+    write(tmp_path / "f2.csv", "FETCH_SIZE", fetch)
+    write(tmp_path / "w2.csv", "WRITE_SIZE", wr)
+    assert bench.step_legs([n for _, n, _ in step(0, 1, 1, 1)]) == (
+        ["prefill128k"] * 6 + ["prefill1m"] * 4 + ["decode64x128k"] * 2 + [None] + ["decode1m"] * 2 + [None]
+        + ["decode1m"] * 2)
+    bench.summarize_traffic("step", str(tmp_path / "f2.csv"), str(tmp_path / "w2.csv"), str(tmp_path / "cf.csv"),
+                            str(tmp_path / "cw.csv"))
+    t = json.load(open(tmp_path / "traffic.json"))
+    w = t["workloads"]
+    assert w["prefill128k"]["index_prefill"]["fetch_bytes"] == 7 * 1024 * 2
+    assert w["prefill128k"]["sparse_prefill"]["fetch_bytes"] == (1 + 2 * 40 + 2 * 3) * 1024 * 2
+    assert w["prefill1m"]["sparse_prefill"]["fetch_bytes"] == (2 + 60 + 5) * 1024 * 2
+    assert w["decode64x128k"]["sparse_decode"]["fetch_bytes"] == 20 * 1024 * 2
+    assert w["decode1m"]["index_decode"]["fetch_bytes"] == 30 * 1024 * 2
+    assert w["decode1m"]["sparse_decode"]["fetch_bytes"] == 2 * 1024 * 2
+    assert w["decode1m"]["sparse_decode"]["write_bytes"] == 1 * 1024
+    # per launch of a kernel over the whole step (3 kp launches per step)
+    assert t["kernels"]["step"]["kp_kernel"]["fetch_bytes_per_launch"] == round((40 + 40 + 60) / 3 * 1024 * 2)
+    assert "decode_fp8" in w  # measurements of other workloads for the same sources are kept
 
 
 def test_header_is_plain_c_and_links(tmp_path):

@@ -81,6 +81,67 @@ def test_index_no_forced_local_block():
     _index_case(HeadShape(8, 2, 64, 64, 5), 1500, 1500, torch.bfloat16, 3, force_local=False, with_scores=True)
 
 
+def test_index_no_forced_local_block_without_scores():
+    # force_local = 0 and no score output: the diagonal block is an ordinary
+    # candidate and must still be scored (one chunk, several chunks, 4 groups)
+    _index_case(HeadShape(8, 2, 64, 64, 5), 900, 900, torch.bfloat16, 60, force_local=False)
+    _index_case(HeadShape(8, 2, 64, 64, 5), 1500, 1500, torch.bfloat16, 61, force_local=False)
+    _index_case(MODEL_SHAPE, 2125, 2125, torch.bfloat16, 62, force_local=False)
+    _index_case(MODEL_SHAPE, 3000, 700, torch.bfloat16, 63, force_local=False)
+
+
+def _closed_form_golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "closed_form_selection.json")) as fh:
+        g = json.load(fh)
+    # d_idx 32: the golden vectors live on coordinate 0, the rest are zero
+    d = 32
+    k_idx = torch.zeros(g["n_kv"], d, dtype=torch.float32)
+    k_idx[:, 0] = -1.0
+    for b, (v, off) in enumerate(zip(g["peak_value"], g["peak_offset"])):
+        k_idx[b * 128 + off, 0] = v
+    q_row = torch.zeros(g["h_kv"], d, dtype=torch.float32)
+    q_row[:, 0] = torch.tensor(g["group_coef"], dtype=torch.float32)
+    return g, k_idx.to(torch.bfloat16), q_row.to(torch.bfloat16)
+
+
+def test_index_exact_ties_closed_form_prefill_and_decode():
+    # The hand-derived closed form (tests/golden/closed_form_selection.json):
+    # group 1 scores every block exactly alike, so its lists are decided by the
+    # tie-break alone (lower block wins); group 0 has distinct peaks (bf16
+    # rounding keeps their order).  The GPU lists must equal the golden lists
+    # exactly, with no near-tie excusal, in prefill mode (one query at
+    # position p) and in decode mode (a paged cache, the query at seq_len - 1).
+    msa = _msa()
+    g, k_idx, q_row = _closed_form_golden()
+    n_kv, h_kv = g["n_kv"], g["h_kv"]
+    kd = k_idx.to(DEV)
+    qd = q_row.to(DEV)
+    n_pages = n_kv // 128
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(64)).to(torch.int32)
+    pages = torch.empty(n_pages, 128, k_idx.shape[1], dtype=torch.bfloat16)
+    pages[perm.long()] = k_idx.view(n_pages, 128, -1)
+    pages = pages.to(DEV)
+    pt = perm.view(1, n_pages).to(DEV)
+    for case in g["cases"]:
+        p, k, fl = case["p"], case["top_k"], case["force_local"]
+        expect = np.asarray(case["expect"], dtype=np.int64)
+        _say("exact ties, prefill", p, k, fl)
+        got = msa.index_topk(qd.view(1, h_kv, -1).contiguous(), kd, top_k=k, q_start=p, force_local=fl)
+        got_s, sc = msa.index_topk(qd.view(1, h_kv, -1).contiguous(), kd, top_k=k, q_start=p, force_local=fl,
+                                   with_scores=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy()[0], expect), (case["why"], got.cpu().numpy()[0], expect)
+        assert np.array_equal(got_s.cpu().numpy()[0], expect), (case["why"], got_s.cpu().numpy()[0], expect)
+        _say("exact ties, decode", p, k, fl)
+        sl = torch.tensor([p + 1], dtype=torch.int32, device=DEV)
+        dec = msa.index_topk(qd.view(1, h_kv, -1).contiguous(), pages, top_k=k, page_table=pt, seq_lens=sl,
+                             force_local=fl)
+        torch.cuda.synchronize()
+        assert np.array_equal(dec.cpu().numpy()[0], expect), (case["why"], dec.cpu().numpy()[0], expect)
+
+
 def test_index_small_k_and_d_idx_128():
     _index_case(HeadShape(16, 4, 128, 128, 3), 1100, 1100, torch.bfloat16, 4)
     _index_case(HeadShape(16, 4, 128, 32, 1), 600, 600, torch.float32, 5)
@@ -359,10 +420,10 @@ def test_prefill_far_apart_scores_and_determinism():
     assert torch.equal(a, b)
 
 
-def test_prefill_schedule_lds_and_global_counters_agree(monkeypatch):
+def test_prefill_schedule_lds_and_global_counters_agree():
     # The schedule counts and scatters each (window, group) in LDS while its
-    # blocks fit there, else with global atomics; MSA_SCHED_LDS_BLOCKS=0 forces
-    # the latter.  Each (token, block) partial is computed the same way whatever
+    # blocks fit there, else with global atomics; the test hook with limit 0
+    # forces the latter.  Each (token, block) partial is computed the same way whatever
     # item holds it, so the outputs are bitwise equal.
     msa = _msa()
     for shape, n_kv, n_q, seed in ((MODEL_SHAPE, 1800, 1800, 54), (HeadShape(32, 2, 128, 64, 8), 2500, 700, 55)):
@@ -371,22 +432,22 @@ def test_prefill_schedule_lds_and_global_counters_agree(monkeypatch):
         ids, _, _ = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q_start, shape.top_k)
         bidx = torch.from_numpy(ids.astype(np.int32)).to(DEV)
         outs = []
-        for thr in (None, "0"):
-            if thr is None:
-                monkeypatch.delenv("MSA_SCHED_LDS_BLOCKS", raising=False)
-            else:
-                monkeypatch.setenv("MSA_SCHED_LDS_BLOCKS", thr)
-            _say("prefill schedule", "lds" if thr is None else "global atomics", shape, n_kv, n_q, seed)
-            o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
-            torch.cuda.synchronize()
-            outs.append((o, lse))
+        try:
+            for thr in (-1, 0):
+                msa.test_schedule_lds_limit(thr)
+                _say("prefill schedule", "lds" if thr < 0 else "global atomics", shape, n_kv, n_q, seed)
+                o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q_start, with_lse=True)
+                torch.cuda.synchronize()
+                outs.append((o, lse))
+        finally:
+            msa.test_schedule_lds_limit(-1)
         assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
         o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, q_start)
         compare_out(outs[1][0], o_ref, torch.bfloat16)
         compare_lse(outs[1][1], lse_ref, torch.bfloat16)
 
 
-def test_backward_bitmap_lds_and_global_agree(monkeypatch):
+def test_backward_bitmap_lds_and_global_agree():
     # The ordered schedule of the dK/dV pass builds its per-cell token bitmaps
     # in LDS (256 tokens per workgroup) while a window's blocks fit there, else
     # with global atomics; both give the same bits, so the gradients are
@@ -399,14 +460,14 @@ def test_backward_bitmap_lds_and_global_agree(monkeypatch):
     o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, with_lse=True)
     d_o = torch.randn(o.shape, generator=torch.Generator(device="cpu").manual_seed(57)).to(torch.bfloat16).to(DEV)
     grads = []
-    for thr in (None, "0"):
-        if thr is None:
-            monkeypatch.delenv("MSA_SCHED_LDS_BLOCKS", raising=False)
-        else:
-            monkeypatch.setenv("MSA_SCHED_LDS_BLOCKS", thr)
-        _say("backward bitmaps", "lds" if thr is None else "global atomics")
-        grads.append(msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o))
-        torch.cuda.synchronize()
+    try:
+        for thr in (-1, 0):
+            msa.test_schedule_lds_limit(thr)
+            _say("backward bitmaps", "lds" if thr < 0 else "global atomics")
+            grads.append(msa.sparse_prefill_backward(inp["q"], inp["k"], inp["v"], bidx, o, lse, d_o))
+            torch.cuda.synchronize()
+    finally:
+        msa.test_schedule_lds_limit(-1)
     for a, b in zip(grads[0], grads[1]):
         assert torch.equal(a, b)
     dq_ref, dk_ref, dv_ref = orc.sparse_attention_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), ids, 0,
