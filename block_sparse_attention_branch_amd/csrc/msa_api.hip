@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "msa.h"
@@ -123,7 +124,71 @@ msa_status launch_index_decode(const msa_shape& s, int32_t batch, const void* q_
 
 }  // namespace
 
+// --------------------------------------------------- allocation-free variant
+// msa_index_topk_decode_static keeps the pooled page scores of the decode
+// index call in this array instead of a caller workspace: every GPU the
+// library runs on holds its own copy (16 MiB) until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static constexpr size_t kScratchFloats = size_t(1) << 22;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current).
+msa_status scratch_address(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d: only devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+msa_status msa_index_topk_decode_static(const msa_shape* shape, int32_t batch, const void* q_idx, const msa_kv* kv,
+                                        int32_t* block_idx, float* block_score, void* hip_stream) {
+  msa_status st = check_shape(shape, true, false);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch=%d", batch);
+  if (!kv->k_idx) return fail(MSA_ERR_INVALID_ARG, "kv->k_idx is NULL");
+  if (!aligned16(q_idx) || !aligned16(kv->k_idx)) return fail(MSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned");
+  if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
+  if (!kv->seq_lens || !kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs seq_lens and a page_table");
+  if (kv->max_pages < 1 || kv->max_pages > msa::kMaxDecodePages)
+    return fail(MSA_ERR_UNSUPPORTED, "max_pages=%d not in [1,%d]", kv->max_pages, msa::kMaxDecodePages);
+  const size_t need = (size_t)batch * s.h_kv * kv->max_pages;
+  if (need > kScratchFloats)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "batch * h_kv * max_pages = %zu exceeds the %zu page scores of the built-in scratch; "
+                "use msa_index_topk with a workspace", need, kScratchFloats);
+  if (batch == 0) return ok();
+  if (!q_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "q_idx/block_idx is NULL");
+  float* scores = nullptr;
+  if ((st = scratch_address(&scores)) != MSA_OK) return st;
+  return launch_index_decode(s, batch, q_idx, kv, block_idx, block_score, scores, static_cast<hipStream_t>(hip_stream),
+                             "msa_index_topk_decode_static");
+}
+
 
 int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
 

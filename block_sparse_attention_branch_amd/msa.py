@@ -56,7 +56,8 @@ _lib = None
 EXPORTS = ["msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
            "msa_sparse_prefill_backward", "msa_index_project",
            "msa_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
-           "msa_profile_enable", "msa_profile_read", "msa_probe_mfma", "msa_test_schedule_lds_limit"]
+           "msa_profile_enable", "msa_profile_read", "msa_probe_mfma", "msa_test_schedule_lds_limit",
+           "msa_index_topk_decode_static"]
 
 
 def lib() -> ctypes.CDLL:
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         P = ctypes.POINTER
         L.msa_index_topk.argtypes = [P(Shape), i32, i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
+        L.msa_index_topk_decode_static.argtypes = [P(Shape), i32, vp, P(KV), vp, vp, vp]
         L.msa_sparse_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_sparse_decode.argtypes = [P(Shape), i32, vp, P(KV), vp, vp, vp, vp, sz, vp]
         L.msa_dense_prefill.argtypes = [P(Shape), i32, i32, vp, P(KV), vp, vp, vp, sz, vp]
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
                                                   P(KL), vp, sz, vp]
         L.msa_index_project.argtypes = [P(Shape), i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, P(KV), vp, vp,
                                         ctypes.c_size_t, vp]
-        for f in ("msa_index_topk", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
+        for f in ("msa_index_topk", "msa_index_topk_decode_static", "msa_sparse_prefill", "msa_sparse_decode", "msa_dense_prefill",
                   "msa_sparse_prefill_backward", "msa_index_project"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_workspace_size.argtypes = [i32, P(Shape), i32, i32, i32, i32, i32]
@@ -235,6 +237,29 @@ def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale
     kv = KV(None, None, _ptr(k_idx), _ptr(page_table), _ptr(seq_lens), nkv, mp)
     _check(lib().msa_index_topk(ctypes.byref(shape), batch, n_q, qs, _ptr(q_idx), ctypes.byref(kv),
                                 _ptr(bidx), _ptr(scores), _ptr(ws), nws, _stream(stream)))
+    return (bidx, scores) if with_scores else bidx
+
+
+def index_topk_decode_static(q_idx, k_idx_pages, page_table, seq_lens, *, top_k=16, force_local=True,
+                             idx_scale=0.0, with_scores=False, out=None, out_scores=None, stream=None, pool="max"):
+    """msa_index_topk_decode_static: msa_index_topk in decode mode with the
+    library's own scratch instead of a workspace (nothing is allocated but the
+    outputs, and those only when ``out`` / ``out_scores`` are not given).
+    q_idx [batch, h_kv, d_idx]; k_idx pages [*, 128, d_idx]; page_table int32
+    [batch, max_pages]; seq_lens int32 [batch]."""
+    batch, h_kv, d_idx = q_idx.shape
+    dt = _dtype_code(q_idx)
+    shape = make_shape(h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local, idx_scale=idx_scale,
+                       cache_dtype=_cache_code(k_idx_pages, dt), pool=pool)
+    dev = q_idx.device
+    bidx = out if out is not None else torch.empty((batch, h_kv, top_k), dtype=torch.int32, device=dev)
+    scores = None
+    if with_scores:
+        scores = out_scores if out_scores is not None else torch.empty((batch, h_kv, top_k), dtype=torch.float32,
+                                                                       device=dev)
+    kv = KV(None, None, _ptr(k_idx_pages), _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1])
+    _check(lib().msa_index_topk_decode_static(ctypes.byref(shape), batch, _ptr(q_idx), ctypes.byref(kv), _ptr(bidx),
+                                              _ptr(scores), _stream(stream)))
     return (bidx, scores) if with_scores else bidx
 
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 4
+#define MSA_ABI_VERSION 5
 #define MSA_BLOCK_SIZE 128
 #define MSA_MAX_TOP_K 16
 
@@ -291,6 +291,21 @@ msa_status msa_profile_read(const char* kernel, double* total_ms, int64_t* launc
  * Asynchronous on hip_stream; the caller times it.  n_wg or iters < 1, or out
  * NULL: MSA_ERR_INVALID_ARG.                                               */
 msa_status msa_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* hip_stream);
+
+/* msa_index_topk in decode mode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation).  Arguments, outputs and errors as msa_index_topk with
+ * kv->seq_lens != NULL and n_q = 1.  The pooled page scores go to a device
+ * array of 2^22 floats (16 MiB) that the library holds on each GPU it runs
+ * on until the process ends, so batch * h_kv * max_pages must be at most
+ * 4194304 (MSA_ERR_UNSUPPORTED otherwise; e.g. 64 sequences x 4 groups x
+ * 16384 pages).  Nothing is allocated and nothing needs clearing: every score
+ * the call reads is written earlier in the same call.  All calls on one GPU
+ * share that array, so calls that may overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.                    */
+msa_status msa_index_topk_decode_static(const msa_shape* shape, int32_t batch, const void* q_idx,
+                                        const msa_kv* kv, int32_t* block_idx, float* block_score,
+                                        void* hip_stream);
 
 /* Test hook (not part of the method): the prefill schedule keeps its
  * per-(group, block) counters in LDS while a call has at most a built-in

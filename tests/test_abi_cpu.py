@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     L = msa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.msa_abi_version() == 4
+    assert L.msa_abi_version() == 5
     for st in range(5):
         assert L.msa_status_string(st).decode().startswith("MSA_")
 
@@ -219,6 +219,28 @@ def test_mfma_probe_validation():
     assert L.msa_probe_mfma(4, 10, None, None) == 1 and "NULL" in _err()
 
 
+def test_decode_static_argument_validation():
+    # the allocation-free decode index call checks everything on the host,
+    # its scratch limit included, before it looks at the device
+    L = msa.lib()
+    s = _shape()
+
+    def call(batch=2, max_pages=1024, seq_lens=FAKE, page_table=FAKE, q_idx=FAKE, out=FAKE, shape=s):
+        kv = msa.KV(None, None, FAKE, page_table, seq_lens, 0, max_pages)
+        return L.msa_index_topk_decode_static(ctypes.byref(shape), batch, q_idx, ctypes.byref(kv), out, None, None)
+
+    assert call(seq_lens=None) == 1 and "seq_lens" in _err()
+    assert call(page_table=None) == 1 and "page_table" in _err()
+    assert call(max_pages=0) == 2 and "max_pages" in _err()
+    assert call(batch=-1) == 1 and "batch" in _err()
+    # 2^22 page scores: 64 sequences x 4 groups x 16384 pages fit, one more sequence does not
+    assert call(batch=65, max_pages=16384) == 2 and "scratch" in _err()
+    assert call(batch=4097, max_pages=1024) == 2 and "scratch" in _err()
+    assert call(batch=0) == 0
+    assert call(out=None) == 1 and "NULL" in _err()
+    assert call(shape=_shape(d_idx=48)) == 2 and "d_idx" in _err()
+
+
 def test_bench_refuses_several_gpus():
     # bench.py measures one GPU; a request for more exits with status 2 and says why
     import subprocess
@@ -328,4 +350,4 @@ def test_header_is_plain_c_and_links(tmp_path):
                     str(src), "-o", str(exe), "-L", libdir, "-l:libmsa.so", f"-Wl,-rpath,{libdir}"], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
-    assert r.stdout.strip() == "ok 4"
+    assert r.stdout.strip() == "ok 5"
