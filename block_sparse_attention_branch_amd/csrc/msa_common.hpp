@@ -210,6 +210,21 @@ __device__ __forceinline__ U scalar_load(const U* p, int64_t i) {
 #define MSA_SCHED_FENCE() do {} while (0)
 #endif
 
+// Waits here, once, for the load that produced `x`: an empty asm statement
+// that reads it makes the compiler put the wait in front of it.  Without it
+// the wait lands before x's first use inside a loop, and that wait then also
+// drains, in every iteration, the prefetches issued earlier in the iteration.
+template <typename V>
+__device__ __forceinline__ void settle(const V& x) {
+  static_assert(sizeof(V) % 4 == 0, "whole dwords");
+  struct Words {
+    uint32_t w[sizeof(V) / 4];
+  };
+  const Words d = __builtin_bit_cast(Words, x);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(V) / 4); ++i) asm volatile("" ::"v"(d.w[i]));
+}
+
 // --------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_xor_f32(float x, int mask) { return __shfl_xor(x, mask, 64); }
 

@@ -135,11 +135,28 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
     for (int ks = 0; ks < KS; ++ks)
       qf[rt][ks] = ok ? load_frag<T>(q_idx + (size_t)r * DIDX + ks * 16 + half * 8) : zero_frag<T>();
   }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qf[rt][ks]);
 
   uint64_t keys[kMaxTopK];
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
   float diag_score = -__builtin_inff();
+  constexpr int kPending = 3;
+  uint64_t pend[kPending];
+#pragma unroll
+  for (int p = 0; p < kPending; ++p) pend[p] = 0ull;
+  int n_pend = 0;
+  // Inserts the pending candidates that still beat the list's last entry
+  // (inserting one raises that bound for the next).
+  auto absorb = [&]() {
+#pragma unroll
+    for (int p = 0; p < kPending; ++p)
+      if (p < n_pend && pend[p] > keys[kMaxTopK - 1]) list_insert(keys, pend[p]);
+    n_pend = 0;
+  };
 
   // K_idx blocks are staged global -> registers -> LDS two blocks ahead.
   // Thread i of the workgroup copies 16-byte pieces at fixed offsets of a
@@ -150,26 +167,25 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   typedef typename std::conditional<sizeof(TC) == 1 && sizeof(T) == 2, u32x2, u32x4>::type Chunk;
   constexpr int G_ROW = DIDX * (int)sizeof(TC);                   // cache bytes per key row
   constexpr int G_CHUNK = 16 * (int)sizeof(TC) / (int)sizeof(T);  // cache bytes per LDS chunk
-  uint32_t toff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int u = tid + kKiThreads * i;
-    toff[i] = (uint32_t)((u / CHUNKS_PER_ROW) * G_ROW + (u % CHUNKS_PER_ROW) * G_CHUNK);
-  }
+  // thread tid copies, for i < LOADS, the chunk at row srow = tid / CHUNKS_PER_ROW
+  // + i * ROWS_PER_PASS, column tid % CHUNKS_PER_ROW (the same offsets for every block)
+  static_assert(kKiThreads % CHUNKS_PER_ROW == 0, "staging rows");
+  constexpr int ROWS_PER_PASS = kKiThreads / CHUNKS_PER_ROW;
+  const uint32_t srow = tid / CHUNKS_PER_ROW;
+  const uint32_t col_off = (tid % CHUNKS_PER_ROW) * G_CHUNK;
   Chunk pre0[LOADS], pre1[LOADS];
   auto load_block = [&](Chunk (&dst)[LOADS], int b) {
     const int64_t base_tok = a.page_table ? (int64_t)scalar_load(a.page_table, b) * kBlock : (int64_t)b * kBlock;
-    const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX);
+    const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX) + col_off;
     if (a.page_table || (int64_t)b * kBlock + kBlock <= a.n_kv) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dst[i] = *reinterpret_cast<const Chunk*>(base + toff[i]);
+      for (int i = 0; i < LOADS; ++i)
+        dst[i] = *reinterpret_cast<const Chunk*>(base + (srow + i * ROWS_PER_PASS) * G_ROW);
     } else {
       const uint32_t last = (uint32_t)(a.n_kv - 1 - b * kBlock);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const uint32_t row = min(toff[i] / G_ROW, last);
-        dst[i] = *reinterpret_cast<const Chunk*>(base + row * G_ROW + toff[i] % G_ROW);
-      }
+      for (int i = 0; i < LOADS; ++i)
+        dst[i] = *reinterpret_cast<const Chunk*>(base + min(srow + (uint32_t)(i * ROWS_PER_PASS), last) * G_ROW);
     }
   };
   auto store_block = [&](const Chunk (&src)[LOADS], int buf) {
@@ -196,7 +212,10 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   // one block: `cur` holds block b + 1, `nxt` receives block b + 2
   auto block_step = [&](int b, Chunk (&cur)[LOADS], Chunk (&nxt)[LOADS]) {
     const int buf = (b - b_begin) & 1;
-    if (b + 2 < b_end) load_block(nxt, b + 2);
+    // unconditional (past the end it reloads the last block, an L2 hit), so
+    // that the wait before storing `cur` below covers `cur` only and the
+    // loads of block b + 2 stay in flight through this block's math
+    load_block(nxt, min(b + 2, b_end - 1));
     const char* K = lds[buf];
     const bool masked = b >= min_diag;
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
@@ -243,13 +262,20 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
       const int cnt = min(kBlock, a.q_start + (my_valid ? my_row : row_last) / a.h_kv - b * kBlock + 1);
       pooled = cnt > 0 ? ((half ? m1 : m0) + recv) * a.idx_scale / (float)cnt : -__builtin_inff();
     }
-    if (my_valid) {
-      const bool cand = a.force_local ? (b < my_diag) : (b <= my_diag);
-      if (cand) {
-        const uint64_t k = make_key(pooled, b);
-        if (k > keys[kMaxTopK - 1]) list_insert(keys, k);
-      }
-      if (b == my_diag) diag_score = pooled;
+    // A candidate that beats the list's last entry is set aside in this
+    // lane's pending slots; the list absorbs them when some lane of the wave
+    // has filled its slots (and once at the end).  An insertion costs the
+    // whole wave when any lane needs one, and with one insertion per block
+    // that would be almost every block.
+    {
+      const bool cand = my_valid && (a.force_local ? (b < my_diag) : (b <= my_diag));
+      const uint64_t k = make_key(pooled, b);
+      const bool want = cand && k > keys[kMaxTopK - 1];
+#pragma unroll
+      for (int p = 0; p < kPending; ++p) pend[p] = (want && n_pend == p) ? k : pend[p];
+      n_pend += want ? 1 : 0;
+      if (__any(n_pend == kPending)) absorb();
+      if (my_valid && b == my_diag) diag_score = pooled;
     }
     if (b + 1 < b_end) store_block(cur, buf ^ 1);
     __syncthreads();
@@ -259,6 +285,7 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
     block_step(b, pre0, pre1);
     if (b + 1 < b_end) block_step(b + 1, pre1, pre0);
   }
+  absorb();
 
   if (!my_valid) return;
   if (a.n_chunks == 1) {
