@@ -750,8 +750,9 @@ struct KdArgs {
   float sm_scale;
 };
 
-constexpr int kKdVtStride = 32 * 2 + 8;
-constexpr int kKdWaves = 8;              // waves per decode workgroup  // bytes per d row of a 32-key V^T slice (bf16)
+constexpr int kKdVtStride = 32 * 2 + 8;  // bytes per d row of a 32-key V^T slice (bf16)
+constexpr int kKdWaves = 8;       // waves per decode workgroup
+constexpr int kKdWavesSplit = 4;  // waves per workgroup when the keys are split over workgroups
 
 // One 32-key unit of a selected page for one wave: K rows as 16x16x32 B
 // fragments (keys on the MFMA rows) and V rows as raw 16-byte pieces, to be
@@ -1312,12 +1313,18 @@ hipError_t launch_dense_prefill(int dtype, int d_h, const AttnArgs& a, hipStream
 DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, int32_t top_k) {
   DecodePlan p{};
   const int pairs = batch * h_kv;
-  int split = 1;
-  // aim for >= ~1024 workgroups of 4 waves; each wave takes whole 32-key units
-  // workgroups of kKdWaves waves; aim for >= 256 of them (one per CU) while
-  // every wave keeps at least one 32-key unit
-  while (split * kKdWaves < top_k * 4 && (int64_t)pairs * split < 256) split <<= 1;
+  int split = 1, waves = kKdWaves;
+  // One workgroup of 8 waves per (sequence, group) while that gives one per
+  // CU or more; with fewer pairs the selected keys are split over workgroups
+  // of 4 waves (more, smaller workgroups start their loads sooner), aiming at
+  // >= 256 workgroups while every wave keeps at least one 32-key unit.  The
+  // splits are combined by kd_merge_kernel.
+  if (pairs < 256) {
+    waves = kKdWavesSplit;
+    while (split * waves < top_k * 4 && (int64_t)pairs * split < 256) split <<= 1;
+  }
   p.split = split;
+  p.waves = waves;
   const int G = h_q / h_kv;
   size_t off = 0;
   p.off_part_o = off; off = align_up(off + (size_t)pairs * split * G * d_h * 4);
@@ -1349,7 +1356,11 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.split = pl.split;
   k.sm_scale = a.sm_scale;
   const int pd = profile_begin(PK_KD, st);
-  hipLaunchKernelGGL((kd_kernel<D, kKdWaves, TC>), dim3(a.batch * a.h_kv * pl.split), dim3(kKdWaves * 64), 0, st, k);
+  const dim3 grid((unsigned)(a.batch * a.h_kv * pl.split));
+  if (pl.waves == kKdWavesSplit)
+    hipLaunchKernelGGL((kd_kernel<D, kKdWavesSplit, TC>), grid, dim3(kKdWavesSplit * 64), 0, st, k);
+  else
+    hipLaunchKernelGGL((kd_kernel<D, kKdWaves, TC>), grid, dim3(kKdWaves * 64), 0, st, k);
   profile_end(pd, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.split == 1) return e;

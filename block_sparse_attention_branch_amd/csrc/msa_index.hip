@@ -457,25 +457,66 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   }
 }
 
-constexpr int kSelectMaxSurvivors = 1024;  // 16 threads x up to 64 candidates each
+// Writes one (sequence, group) row from `top` (its best keys, descending, 0 =
+// empty); run by the 64 lanes of one wave.  Lane e < 16 holds the e-th best
+// key (used if e < n_take and non-empty), lane 16 the forced diagonal block;
+// a valid entry's rank by block id is its output slot, and the slots past the
+// valid entries get the -1 / -inf padding.
+__device__ __forceinline__ void select_write_row(const KiDecodeArgs& a, int s, int r, int diag, const float* sc,
+                                                 const uint64_t* top) {
+  const int tid = threadIdx.x & 63;
+  const int n_take = a.top_k - (a.force_local ? 1 : 0);
+  int id = 0x7fffffff;
+  float scv = 0.0f;
+  if (tid < kMaxTopK) {
+    const uint64_t k = top[tid];
+    if (tid < n_take && k != 0ull) {
+      id = key_block(k);
+      scv = key_score(k);
+    }
+  } else if (tid == kMaxTopK && a.force_local) {
+    id = diag;
+    scv = a.need_diag ? sc[diag] : -__builtin_inff();
+  }
+  int rk = 0;
+#pragma unroll
+  for (int j = 0; j <= kMaxTopK; ++j) rk += __shfl(id, j, 64) < id ? 1 : 0;
+  const bool valid = id != 0x7fffffff;
+  const int n_valid = __popcll(__ballot(valid));
+  const size_t row = (size_t)s * a.h_kv + r;
+  int32_t* idx_out = a.block_idx + row * a.top_k;
+  float* sc_out = a.block_score ? a.block_score + row * a.top_k : nullptr;
+  if (valid) {
+    idx_out[rk] = id;
+    if (sc_out) sc_out[rk] = scv;
+  }
+  if (tid >= n_valid && tid < a.top_k) {
+    idx_out[tid] = -1;
+    if (sc_out) sc_out[tid] = -__builtin_inff();
+  }
+}
 
-// Top-k of one (sequence, group) row of pooled page scores.  Keys are the
-// order-preserving bits of the score with the inverted block id below them,
-// so they are unique and "larger" means better (ties to the lower block).
-//  1) each thread loads its U candidates (pages tid + 256 u) into registers
-//     and takes their maximum; the 16th largest of the 256 maxima, T, is a
-//     lower bound of the answer: the 16 threads whose maxima are >= T each
-//     hold a key >= T, so the 16 best keys are all >= T.  Every wave finds T
-//     on its own with a bitwise search over the maxima (64 steps of a ballot
-//     count), so no barrier follows;
-//  2) every key >= T survives (only those 16 threads hold any); a thread
-//     counts its survivors in registers and reserves their places with one
-//     LDS atomic;
+// Top-k of one (sequence, group) row of pooled page scores, one workgroup of
+// NT threads per row, thread t holding the candidates t + NT u, u < U.  Keys
+// are the order-preserving bits of the score with the inverted block id below
+// them, so they are unique and "larger" means better (ties to the lower block).
+//  1) each thread takes the maximum of its keys (0: no candidate).  Each wave
+//     finds t_w, the 16th largest of its 64 thread maxima (0 when fewer than
+//     16 lanes hold a candidate), by counting for every lane the maxima above
+//     its own (the wave's maxima are read from LDS as broadcasts);
+//     T = max_w t_w bounds the answer from below: the wave that attains it
+//     holds 16 keys >= T;
+//  2) every key >= T survives.  In a wave at most 16 lanes have a maximum
+//     >= T (t_w <= T), so at most 16 * (NT / 64) threads hold survivors and at
+//     most 16 * (NT / 64) * U keys survive: the LDS buffer holds them all;
 //  3) each survivor's rank among the survivors places the best 16 in order.
-template <int U>
-__global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
-  __shared__ uint64_t tm[256];
-  __shared__ uint64_t surv[kSelectMaxSurvivors];
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
+  constexpr int NW = NT / 64;
+  constexpr int kCap = kMaxTopK * NW * U;
+  __shared__ uint64_t tm[NT];
+  __shared__ uint64_t wthr[NW];
+  __shared__ uint64_t surv[kCap];
   __shared__ uint64_t top[kMaxTopK];
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
@@ -483,101 +524,68 @@ __global__ __launch_bounds__(256) void ki_decode_select_kernel(KiDecodeArgs a) {
   const int diag = (L - 1) / kBlock;
   const int ncand = min(a.force_local ? diag : diag + 1, a.max_pages);
   const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
-  const int tid = threadIdx.x, lane = tid & 63;
-
-  // Candidates past the row's end read a clamped (in-bounds) entry and are
-  // dropped by the b < ncand test; with no candidates, entry 0 of the row
-  // (max_pages >= 1) is read and dropped.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Candidates past the row's end read a clamped (in-bounds) entry and get
+  // key 0.  All loads are issued before any is used: settle() keeps the
+  // compiler from moving each load under its own branch, one round trip at a
+  // time.
   float v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) v[u] = sc[max(min(tid + 256 * u, ncand - 1), 0)];
+  for (int u = 0; u < U; ++u) v[u] = sc[max(min(tid + NT * u, ncand - 1), 0)];
+#pragma unroll
+  for (int u = 0; u < U; ++u) settle(v[u]);
+  uint64_t k[U];
   uint64_t tmax = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int b = tid + 256 * u;
-    const uint64_t k = b < ncand ? make_key(v[u], b) : 0ull;
-    tmax = k > tmax ? k : tmax;
+    const int b = tid + NT * u;
+    k[u] = b < ncand ? make_key(v[u], b) : 0ull;
+    tmax = k[u] > tmax ? k[u] : tmax;
   }
   tm[tid] = tmax;
   if (tid == 0) count = 0;
   if (tid < kMaxTopK) top[tid] = 0;
   __syncthreads();
-  // T: the largest value with at least 16 maxima >= it, i.e. the 16th
-  // largest maximum; 0 when fewer than 16 threads hold a candidate (then
-  // every candidate survives).
-  uint64_t mx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mx[j] = tm[lane + 64 * j];
-  uint64_t thr = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const uint64_t cand = thr | (1ull << bit);
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(mx[j] >= cand));
-    if (c >= kMaxTopK) thr = cand;
-  }
-  if (tmax >= thr && tmax != 0) {
-    int c = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = tid + 256 * u;
-      c += (b < ncand && make_key(v[u], b) >= thr) ? 1 : 0;
+  {
+    // gt / ge: the wave's maxima above / at least this lane's
+    const uint64_t* wm = tm + wave * 64;
+    int gt = 0, ge = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; j += 2) {
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+      const u64x2 p = *reinterpret_cast<const u64x2*>(wm + j);
+      gt += (p[0] > tmax ? 1 : 0) + (p[1] > tmax ? 1 : 0);
+      ge += (p[0] >= tmax ? 1 : 0) + (p[1] >= tmax ? 1 : 0);
     }
+    // the lane holding the 16th largest value (all lanes holding it when it
+    // is 0, which then is the answer)
+    const uint64_t hit = __ballot(gt < kMaxTopK && ge >= kMaxTopK);
+    const uint64_t t = hit ? __shfl(tmax, __builtin_ctzll(hit), 64) : 0ull;  // hit is wave-uniform
+    if (lane == 0) wthr[wave] = t;
+  }
+  __syncthreads();
+  uint64_t T = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) T = wthr[w] > T ? wthr[w] : T;
+  if (tmax >= T && tmax != 0) {
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) c += (k[u] != 0ull && k[u] >= T) ? 1 : 0;
     int pos = atomicAdd(&count, c);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = tid + 256 * u;
-      const uint64_t k = make_key(v[u], b);
-      if (b < ncand && k >= thr) {
-        if (pos < kSelectMaxSurvivors) surv[pos] = k;
-        ++pos;
-      }
-    }
+    for (int u = 0; u < U; ++u)
+      if (k[u] != 0ull && k[u] >= T) surv[pos++] = k[u];
   }
   __syncthreads();
-  const int n = min(count, kSelectMaxSurvivors);
-  for (int i = tid; i < n; i += 256) {
-    const uint64_t k = surv[i];
+  const int n = count;
+  for (int i = tid; i < n; i += NT) {
+    const uint64_t ki = surv[i];
     int rk = 0;
-    for (int j = 0; j < n; ++j) rk += surv[j] > k ? 1 : 0;
-    if (rk < kMaxTopK) top[rk] = k;
+    for (int j = 0; j < n; ++j) rk += surv[j] > ki ? 1 : 0;
+    if (rk < kMaxTopK) top[rk] = ki;
   }
   __syncthreads();
-  // Assemble the row on wave 0: lane e < 16 holds the e-th best key (used if
-  // e < n_take and non-empty), lane 16 the forced diagonal block; a valid
-  // entry's rank by block id is its output slot, and the slots past the
-  // valid entries get the -1 / -inf padding.
-  if (tid < 64) {
-    const int n_take = a.top_k - (a.force_local ? 1 : 0);
-    int id = 0x7fffffff;
-    float scv = 0.0f;
-    if (tid < kMaxTopK) {
-      const uint64_t k = top[tid];
-      if (tid < n_take && k != 0ull) {
-        id = key_block(k);
-        scv = key_score(k);
-      }
-    } else if (tid == kMaxTopK && a.force_local) {
-      id = diag;
-      scv = a.need_diag ? sc[diag] : -__builtin_inff();
-    }
-    int rk = 0;
-#pragma unroll
-    for (int j = 0; j <= kMaxTopK; ++j) rk += __shfl(id, j, 64) < id ? 1 : 0;
-    const bool valid = id != 0x7fffffff;
-    const int n_valid = __popcll(__ballot(valid));
-    const size_t row = (size_t)s * a.h_kv + r;
-    int32_t* idx_out = a.block_idx + row * a.top_k;
-    float* sc_out = a.block_score ? a.block_score + row * a.top_k : nullptr;
-    if (valid) {
-      idx_out[rk] = id;
-      if (sc_out) sc_out[rk] = scv;
-    }
-    if (tid >= n_valid && tid < a.top_k) {
-      idx_out[tid] = -1;
-      if (sc_out) sc_out[tid] = -__builtin_inff();
-    }
-  }
+  if (tid < 64) select_write_row(a, s, r, diag, sc, top);
 }
 
 // ----------------------------------------------------------------- launch
@@ -608,14 +616,15 @@ static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sg((unsigned)(a.batch * a.h_kv));
-  const int per = (a.max_pages + 255) / 256;  // candidates per thread
-  if (per <= 4) hipLaunchKernelGGL(ki_decode_select_kernel<4>, sg, dim3(256), 0, st, a);
-  else if (per <= 8) hipLaunchKernelGGL(ki_decode_select_kernel<8>, sg, dim3(256), 0, st, a);
-  else if (per <= 16) hipLaunchKernelGGL(ki_decode_select_kernel<16>, sg, dim3(256), 0, st, a);
-  else if (per <= 32) hipLaunchKernelGGL(ki_decode_select_kernel<32>, sg, dim3(256), 0, st, a);
-  else if (per <= 40) hipLaunchKernelGGL(ki_decode_select_kernel<40>, sg, dim3(256), 0, st, a);
-  else if (per <= 48) hipLaunchKernelGGL(ki_decode_select_kernel<48>, sg, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(ki_decode_select_kernel<64>, sg, dim3(256), 0, st, a);
+  // 256 threads per row up to 2048 pages (8 candidates each), 1024 beyond
+  static_assert(kMaxDecodePages <= 16 * 1024, "the select holds at most 16 candidates per thread");
+  const int mp = a.max_pages;
+  if (mp <= 256 * 4) hipLaunchKernelGGL((ki_decode_select_kernel<256, 4>), sg, dim3(256), 0, st, a);
+  else if (mp <= 256 * 8) hipLaunchKernelGGL((ki_decode_select_kernel<256, 8>), sg, dim3(256), 0, st, a);
+  else if (mp <= 1024 * 4) hipLaunchKernelGGL((ki_decode_select_kernel<1024, 4>), sg, dim3(1024), 0, st, a);
+  else if (mp <= 1024 * 8) hipLaunchKernelGGL((ki_decode_select_kernel<1024, 8>), sg, dim3(1024), 0, st, a);
+  else if (mp <= 1024 * 12) hipLaunchKernelGGL((ki_decode_select_kernel<1024, 12>), sg, dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL((ki_decode_select_kernel<1024, 16>), sg, dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

@@ -143,6 +143,7 @@ bool attn_supported(int dtype, int d_h);
 
 struct DecodePlan {
   int32_t split;            // workgroups per (sequence, group)
+  int32_t waves;            // waves per workgroup (8, or 4 when the keys are split)
   size_t off_part_o, off_part_lse, total;
 };
 DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, int32_t top_k);
