@@ -46,7 +46,7 @@ __global__ void ks_count_kernel(SchedArgs a) {
   const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
   const int diag = (a.q_start + i) >> 7;
   int b[kMaxTopK];
-  const uint32_t m = row_used(a.block_idx + row * a.top_k, a.top_k, diag, b);
+  const uint32_t m = sched_used(a.block_idx + row * a.top_k, a.top_k, diag, a.skip_diag, b);
   const int w = i / a.window;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
@@ -153,7 +153,7 @@ __global__ void ks_scatter_kernel(SchedArgs a) {
   const int i = (int)(row / a.h_kv), r = (int)(row % a.h_kv);
   const int diag = (a.q_start + i) >> 7;
   int b[kMaxTopK];
-  const uint32_t m = row_used(a.block_idx + row * a.top_k, a.top_k, diag, b);
+  const uint32_t m = sched_used(a.block_idx + row * a.top_k, a.top_k, diag, a.skip_diag, b);
   const int w = i / a.window;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
@@ -185,7 +185,8 @@ __device__ __forceinline__ void ks_slice_counts(const SchedArgs& a, int r, int t
   __syncthreads();
   for (int i = t0 + threadIdx.x; i < t1; i += 256) {
     int b[kMaxTopK];
-    const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
+    const uint32_t m =
+        sched_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, a.skip_diag, b);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
       if (m & (1u << j)) atomicAdd(&cnt[b[j]], 1);
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(256) void ks_scatter_lds_kernel(SchedArgs a) {
   }
   for (int i = t0 + threadIdx.x; i < t1; i += 256) {
     int b[kMaxTopK];
-    const uint32_t m = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, b);
+    const uint32_t m =
+        sched_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, (a.q_start + i) >> 7, a.skip_diag, b);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
       if (m & (1u << j)) a.entries[atomicAdd(&pos[b[j]], 1)] = (i << 4) | j;
@@ -405,14 +407,15 @@ __device__ __forceinline__ int kp_entry(const KpItem& m, int rho, int g_shift, c
 // Scores, softmax and P.V for the rows in `ps`, then the partial stores.  The
 // math is skipped when no row of the wave is valid; the stores are not (rows
 // past the end write a trash row), keeping the memory-op count fixed.
+// One 32-row tile of a wave against the block b staged in `lds`: scores
+// (keys after the row's position masked), the block-local softmax with max
+// `mx` (raw score) and sum `l`, and the un-normalised P.V in t.o.  The query
+// fragments and the position are already in t.qf[0] / t.pos[0].
 template <typename T, int D>
-__device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, D>& ps, const char* lds,
-                                        TileRegs<T, D, 1>& t, float& mx, float& l) {
-  const float c2 = a.sm_scale * kLog2e;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) t.qf[0][ks] = ps.qf[ks];
-  t.pos[0] = ps.pos;
-  const bool need_mask = ps.ok && (b * kBlock + kBlock - 1 > ps.pos);
+__device__ __forceinline__ void block_tile_math(float sm_scale, int b, bool ok, const char* lds,
+                                                TileRegs<T, D, 1>& t, float& mx, float& l) {
+  const float c2 = sm_scale * kLog2e;
+  const bool need_mask = ok && (b * kBlock + kBlock - 1 > t.pos[0]);
   tile_scores<T, D, 1>(t, lds, b, __any(need_mask));
   float mm = -__builtin_inff();
 #pragma unroll
@@ -436,6 +439,15 @@ __device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) t.o[0][dt] = f32x16{};
   tile_pv<T, D, 1>(t, lds);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, D>& ps, const char* lds,
+                                        TileRegs<T, D, 1>& t, float& mx, float& l) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) t.qf[0][ks] = ps.qf[ks];
+  t.pos[0] = ps.pos;
+  block_tile_math<T, D>(a.sm_scale, b, ps.ok, lds, t, mx, l);
 }
 
 template <typename T, int D>
@@ -546,81 +558,212 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
   }
 }
 
-// Second stage: log-sum-exp merge of a token's per-block partials.
+// Second stage: the diagonal block and the log-sum-exp merge ("MiniMax Sparse
+// Attention" digest, §4.4.2: the query's own block as a causal tile, combined
+// with the partials of its other selected blocks).  A workgroup of 4 waves
+// owns the 128 (token, head) rows of one group whose positions lie in one
+// aligned run of 128/G positions, so all its rows share their diagonal block.
+//  A) the block's K and V^T are staged in LDS and the causal tile is computed
+//     on MFMA (one 32-row tile per wave, as in the KV-outer pass); its
+//     un-normalised output goes to LDS in the partial layout (part_chunk),
+//     with its (max, sum), next to the (max, sum) of every (row, slot);
+//  B) the merge streams the partials like a plain merge: a thread owns one
+//     8-value chunk of a (token, head) row at a time, loads that chunk of all
+//     the row's partial slots at once (the next chunk's loads issued before
+//     the current one is combined) and writes O and lse.
+// The schedule left the diagonal blocks out of the KV-outer pass, so no
+// partial of them exists.  A row whose list lacks its diagonal block
+// (force_local = 0, or a caller's list) gives the tile weight 0.
 struct KmArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
   const int32_t* block_idx;
   const void* part_o;
   const float2* part_ml;
   void* o;
   float* lse;
-  int32_t n_q, q_start, h_q, h_kv, group, top_k, window, w, pairs_per_wg;
+  int32_t n_q, q_start, n_kv, h_q, h_kv, group, g_shift, top_k, window, w;
+  int32_t tile0;        // first run of this window: position / tile_tokens
+  int32_t n_runs;       // runs of this window; the grid is n_runs * h_kv
+  int32_t tile_tokens;  // 128 / G
+  float sm_scale;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void km_kernel(KmArgs a) {
-  constexpr int DC = D / 8;
-  // the (max, sum) of every (pair, head, slot) of the workgroup, read once
-  // ([pair][head][slot]); each is needed by the DC threads of its head
-  __shared__ float2 ml_s[256 * kMaxTopK / DC];
-  const int G = a.group;
-  const int per_pair = G * DC;                 // one 8-value chunk per thread
-  const int sub = threadIdx.x / per_pair;
-  const int c = threadIdx.x % per_pair;        // chunk index within a (token, slot) region
-  for (int e = threadIdx.x; e < a.pairs_per_wg * G * kMaxTopK; e += 256) {
-    const int j = e % kMaxTopK, gg = (e / kMaxTopK) % G, sb = e / (kMaxTopK * G);
-    const int64_t pr = (int64_t)blockIdx.x * a.pairs_per_wg + sb;
-    const int il2 = (int)(pr / a.h_kv), r2 = (int)(pr % a.h_kv);
-    float2 v = float2{-__builtin_inff(), 0.0f};
-    if (il2 < a.window && a.w * a.window + il2 < a.n_q && j < a.top_k)
-      v = a.part_ml[(((size_t)il2 * a.h_kv + r2) * a.top_k + j) * G + gg];
-    ml_s[e] = v;
+constexpr int kKmThreads = 256;  // 4 waves x 32 rows
+constexpr int kKmRows = 128;
+
+template <typename T, int D, typename TC = T>
+__global__ __launch_bounds__(kKmThreads, 2) void km_kernel(KmArgs a) {
+  using L = KvLds<T, D>;
+  constexpr int DT = D / 32, DC = D / 8;
+  constexpr int kPasses = kKmRows * DC / kKmThreads;  // chunks per thread in phase B
+  static_assert(kPasses % 2 == 0, "phase B runs passes in pairs");
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  // phase B's use of the same LDS
+  T* od_s = reinterpret_cast<T*>(lds);                                              // [rows / G][G * D]
+  float2* mld_s = reinterpret_cast<float2*>(lds + (size_t)kKmRows * D * sizeof(T));  // [rows]
+  float2* ml_s = mld_s + kKmRows;                                                   // [rows][16 slots]
+  uint32_t* parts_s = reinterpret_cast<uint32_t*>(ml_s + kKmRows * kMaxTopK);      // [rows / G]
+  static_assert((size_t)kKmRows * D * sizeof(T) + kKmRows * 8 * (1 + kMaxTopK) + kKmRows * 4 <= (size_t)L::BYTES,
+                "phase B fits the K/V area");
+  // Workgroup L is dispatched to XCD L % 8; each XCD takes a contiguous range of
+  // (group, run) ids, so the 128 / tile_tokens runs of one diagonal block read
+  // its K/V through one L2.
+  int r, run;
+  {
+    const int n = gridDim.x, L = blockIdx.x, xcd = L & 7, q8 = n >> 3, rem = n & 7;
+    const int m = xcd * q8 + min(xcd, rem) + (L >> 3);
+    r = m / a.n_runs;
+    run = a.tile0 + (m - r * a.n_runs);
   }
-  __syncthreads();
-  if (sub >= a.pairs_per_wg) return;
-  const int64_t pair = (int64_t)blockIdx.x * a.pairs_per_wg + sub;  // (i_local, r)
-  const int il = (int)(pair / a.h_kv), r = (int)(pair % a.h_kv);
-  const int i = a.w * a.window + il;
-  if (il >= a.window || i >= a.n_q) return;
-  const int g = c % G, half = (c / G) & 1, p = (c / (2 * G)) & 1, dt = c / (4 * G);
-  const int d0 = dt * 32 + 16 * p + 4 * half;  // chunk holds d0..d0+3 and d0+8..d0+11
+  const int G = a.group;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int rho = (tid >> 6) * 32 + l32;
+  const int head = rho & (G - 1), tl = rho >> a.g_shift;
+  const int p_lo = a.q_start + a.w * a.window;
+  const int p_hi = a.q_start + min((a.w + 1) * a.window, a.n_q);  // exclusive
+  // token (local index tt in the run) -> window row: rows outside the window
+  // compute on a valid token and store nothing
+  auto tok = [&](int tt, bool& ok) {
+    const int pos = run * a.tile_tokens + tt;
+    ok = pos >= p_lo && pos < p_hi;
+    return min(max(pos, p_lo), p_hi - 1) - a.q_start;
+  };
+  bool ok;
+  const int i = tok(tl, ok);
   const int diag = (a.q_start + i) >> 7;
+  const int bdiag = (run * a.tile_tokens) >> 7;  // the same for every row of the run
+
+  // ---- phase A: the diagonal tile
+  StageRegs<T, D, kKmThreads, TC> g;
+  stage_load<T, D, kKmThreads, TC>(g, block_ptr<TC, D>(a.k, a.v, a.page_table, bdiag, r, a.h_kv, a.n_kv));
   int bl[kMaxTopK];
   const uint32_t used = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, diag, bl);
-  const size_t slot0 = ((size_t)il * a.h_kv + r) * a.top_k;
+  uint32_t parts = used;
+  bool has_diag = false;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (bl[j] == diag && ((used >> j) & 1u)) {
+      has_diag = true;
+      parts &= ~(1u << j);
+    }
+  // (max, sum) of every (row, slot), entries tid + 256 e, read now and put in
+  // LDS after the tile (the slot index is clamped; unused slots are masked)
+  constexpr int kMlPerThread = kKmRows * kMaxTopK / kKmThreads;
+  float2 mlr[kMlPerThread];
+#pragma unroll
+  for (int e = 0; e < kMlPerThread; ++e) {
+    const int x = tid + kKmThreads * e, row = x / kMaxTopK, j = x % kMaxTopK;
+    bool okr;
+    const int ir = tok(row >> a.g_shift, okr);
+    const size_t slot = ((size_t)(ir - a.w * a.window) * a.h_kv + r) * a.top_k + min(j, a.top_k - 1);
+    mlr[e] = a.part_ml[slot * G + (row & (G - 1))];
+  }
+  TileRegs<T, D, 1> t;
+  {
+    const T* qrow = static_cast<const T*>(a.q) + ((size_t)i * a.h_q + r * G + head) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) t.qf[0][ks] = load_frag<T>(qrow + ks * 16);
+  }
+  t.pos[0] = a.q_start + i;
+  stage_store<T, D, kKmThreads, TC>(g, lds);
+  __syncthreads();
+  float mx_d, l_d;
+  block_tile_math<T, D>(a.sm_scale, bdiag, ok, lds, t, mx_d, l_d);
+  __syncthreads();  // every wave is done with K and V^T
+  {
+    T* region = od_s + (size_t)tl * G * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) store8<T>(region + (size_t)part_chunk(dt, p, half, head, G) * 8, t.o[0][dt], 8 * p);
+    if (half == 0) mld_s[rho] = has_diag ? float2{mx_d * a.sm_scale, l_d} : float2{-__builtin_inff(), 0.0f};
+    if (half == 0 && head == 0) parts_s[tl] = parts;
+  }
+#pragma unroll
+  for (int e = 0; e < kMlPerThread; ++e) ml_s[tid + kKmThreads * e] = mlr[e];
+  __syncthreads();
+
+  // ---- phase B: merge, one 8-value chunk c of token tt per thread and pass
+  const int per_tok = G * DC;
   const T* po = static_cast<const T*>(a.part_o);
-  const float2* mls = ml_s + (sub * G + g) * kMaxTopK;
-  float2 ml[kMaxTopK];
-  Frag<T> x[kMaxTopK];
+  auto issue = [&](Frag<T> (&x)[kMaxTopK], int pass) {
+    const int u = pass * kKmThreads + tid, tt = u / per_tok, c = u % per_tok;
+    bool okp;
+    const int ip = tok(tt, okp);
+    const uint32_t pm = parts_s[tt];
+    const size_t slot0 = ((size_t)(ip - a.w * a.window) * a.h_kv + r) * a.top_k;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    // every load is issued (an unused slot reads slot 0 again), but an unused
-    // slot's values are zeroed: a weight of 0 must not meet stale workspace
-    // contents (0 * inf), e.g. in a row with no used slot at all
-    const bool u = (used >> j) & 1u;
-    const size_t sj = slot0 + (u ? j : 0);
-    const Frag<T> xl = load_frag<T>(po + (sj * G * D + (size_t)c * 8));
-    x[j] = u ? xl : zero_frag<T>();
-    ml[j] = u ? mls[j] : float2{-__builtin_inff(), 0.0f};
+    for (int j = 0; j < kMaxTopK; ++j) {
+      // every load is issued (an unused slot reads slot 0 again) so that the
+      // number in flight is fixed; an unused slot's values are zeroed below
+      const size_t sj = slot0 + (((pm >> j) & 1u) ? j : 0);
+      x[j] = load_frag<T>(po + sj * G * D + (size_t)c * 8);
+    }
+  };
+  auto finish = [&](const Frag<T> (&x)[kMaxTopK], int pass) {
+    const int u = pass * kKmThreads + tid, tt = u / per_tok, c = u % per_tok;
+    bool okp;
+    const int ip = tok(tt, okp);
+    const uint32_t pm = parts_s[tt];
+    const int gg = c % G, hf = (c / G) & 1, pp = (c / (2 * G)) & 1, dt = c / (4 * G);
+    const int d0 = dt * 32 + 16 * pp + 4 * hf;  // the chunk holds d0..d0+3 and d0+8..d0+11
+    const int row = tt * G + gg;
+    const float2 md = mld_s[row];
+    float2 ml[kMaxTopK];
+    float mx = md.x;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      ml[j] = ((pm >> j) & 1u) ? ml_s[row * kMaxTopK + j] : float2{-__builtin_inff(), 0.0f};
+      mx = fmaxf(mx, ml[j].x);
+    }
+    const float mref = mx == -__builtin_inff() ? 0.0f : mx;
+    const float wd = fast_exp2((md.x - mref) * kLog2e);
+    float den = wd * md.y;
+    const Frag<T> xd = load_frag<T>(od_s + (size_t)tt * G * D + (size_t)c * 8);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = wd * to_f32(xd[e]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      // a zero weight must not meet stale workspace contents (0 * inf)
+      const Frag<T> xj = ((pm >> j) & 1u) ? x[j] : zero_frag<T>();
+      const float w = fast_exp2((ml[j].x - mref) * kLog2e);
+      den = fmaf(w, ml[j].y, den);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(xj[e]), acc[e]);
+    }
+    if (!okp) return;
+    T* out = static_cast<T*>(a.o) + ((size_t)ip * a.h_q + r * G + gg) * D;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    store4<T>(out + d0, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    store4<T>(out + d0 + 8, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (a.lse && c < G)
+      a.lse[(size_t)ip * a.h_q + r * G + gg] = den > 0.0f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
+  };
+  if constexpr (sizeof(T) == 2) {
+    // two buffers: the next chunk's 16 loads are in flight while one is combined
+    Frag<T> xa[kMaxTopK], xb[kMaxTopK];
+    issue(xa, 0);
+#pragma unroll
+    for (int pass = 0; pass < kPasses; pass += 2) {
+      issue(xb, pass + 1);
+      finish(xa, pass);
+      MSA_SCHED_FENCE();
+      if (pass + 2 < kPasses) issue(xa, pass + 2);
+      finish(xb, pass + 1);
+      MSA_SCHED_FENCE();
+    }
+  } else {
+    // fp32 fragments are twice as wide: one buffer
+    Frag<T> xa[kMaxTopK];
+    for (int pass = 0; pass < kPasses; ++pass) {
+      issue(xa, pass);
+      finish(xa, pass);
+    }
   }
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) mx = fmaxf(mx, ml[j].x);
-  const float mref = mx == -__builtin_inff() ? 0.0f : mx;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float den = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    const float w = fast_exp2((ml[j].x - mref) * kLog2e);
-    den = fmaf(w, ml[j].y, den);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, to_f32(x[j][e]), acc[e]);
-  }
-  T* out = static_cast<T*>(a.o) + ((size_t)i * a.h_q + r * G + g) * D;
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  store4<T>(out + d0, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  store4<T>(out + d0 + 8, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse && c < G)
-    a.lse[(size_t)i * a.h_q + r * G + g] = den > 0.0f ? mx + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
 }
 
 // ====================================================================
@@ -1130,9 +1273,11 @@ bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (
 bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
 bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 2) && (d_h == 64 || d_h == 128); }
 
-hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st) {
+hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st,
+                                   bool skip_diag) {
   char* ws = static_cast<char*>(a.ws);
   s = SchedArgs{};
+  s.skip_diag = skip_diag ? 1 : 0;
   s.block_idx = a.block_idx;
   s.n_q = a.n_q;
   s.q_start = a.q_start;
@@ -1206,7 +1351,7 @@ template <typename T, int D, typename TC = T>
 static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl, hipStream_t st) {
   char* ws = static_cast<char*>(a.ws);
   SchedArgs s;
-  hipError_t e = launch_prefill_schedule(a, pl, s, st);
+  hipError_t e = launch_prefill_schedule(a, pl, s, st, /*skip_diag=*/true);
   if (e != hipSuccess) return e;
 
   KpArgs kp{};
@@ -1234,6 +1379,10 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   kp.sm_scale = a.sm_scale;
 
   KmArgs km{};
+  km.q = a.q;
+  km.k = a.k;
+  km.v = a.v;
+  km.page_table = a.page_table;
   km.block_idx = a.block_idx;
   km.part_o = kp.part_o;
   km.part_ml = kp.part_ml;
@@ -1241,12 +1390,15 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   km.lse = a.lse;
   km.n_q = a.n_q;
   km.q_start = a.q_start;
+  km.n_kv = a.n_kv;
   km.h_q = a.h_q;
   km.h_kv = a.h_kv;
   km.group = a.group;
+  km.g_shift = kp.g_shift;
   km.top_k = a.top_k;
   km.window = pl.window;
-  km.pairs_per_wg = std::max(1, 256 / (a.group * (D / 8)));
+  km.tile_tokens = kKmRows / a.group;
+  km.sm_scale = a.sm_scale;
 
   const int n_cu = num_cus();
   for (int w = 0; w < pl.n_windows; ++w) {
@@ -1259,10 +1411,12 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     hipLaunchKernelGGL((kp_kernel<T, D, TC>), dim3(grid), dim3(kKpThreads), 0, st, kp);
     profile_end(pk, st);
     km.w = w;
-    const int64_t pairs = (int64_t)tok * a.h_kv;
+    // aligned runs of tile_tokens positions that meet the window's positions
+    const int p0 = a.q_start + w * pl.window, p1 = p0 + tok;
+    km.tile0 = p0 / km.tile_tokens;
+    km.n_runs = (p1 - 1) / km.tile_tokens - km.tile0 + 1;
     const int pm = profile_begin(PK_KM, st);
-    hipLaunchKernelGGL((km_kernel<T, D>), dim3((unsigned)((pairs + km.pairs_per_wg - 1) / km.pairs_per_wg)),
-                       dim3(256), 0, st, km);
+    hipLaunchKernelGGL((km_kernel<T, D, TC>), dim3((unsigned)(km.n_runs * a.h_kv)), dim3(kKmThreads), 0, st, km);
     profile_end(pm, st);
   }
   return hipGetLastError();

@@ -326,6 +326,7 @@ struct SchedArgs {
                       // (fill[0] and fill[1] are then zeroed as work-queue heads for the consumers)
   int32_t words;      // 32-bit words per cell (window / 32, rounded up)
   int32_t split;      // LDS count/scatter: workgroups per (window, group), each over a slice of the window's tokens
+  int32_t skip_diag;  // leave each row's own (diagonal) block out of the cells: the merge computes it
 };
 
 // Cells are the (window, group, block) token lists.  Within a window they are
@@ -387,6 +388,18 @@ __device__ __forceinline__ uint32_t row_used(const int32_t* row, int top_k, int 
     }
   return m;
 }
+// The slots a schedule places in cells: the used ones, without the row's
+// diagonal block when the merge kernel computes that block itself.
+__device__ __forceinline__ uint32_t sched_used(const int32_t* row, int top_k, int diag, int skip_diag,
+                                               int (&b)[kMaxTopK]) {
+  uint32_t m = row_used(row, top_k, diag, b);
+  if (skip_diag) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (b[j] == diag) m &= ~(1u << j);
+  }
+  return m;
+}
 __device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int diag) {
   int b[kMaxTopK];
   return row_used(row, top_k, diag, b);
@@ -413,7 +426,10 @@ struct KpItem {
 
 // Builds the schedule of plan `pl` for the block lists of `a` in the
 // workspace: per-cell token lists (`entries`) and work items.
-hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st);
+// With `skip_diag` each row's diagonal block is left out (the forward's merge
+// kernel computes it); the backward's schedules keep every used slot.
+hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st,
+                                   bool skip_diag = false);
 
 // Compute units of the current device.
 int num_cus();
