@@ -887,9 +887,9 @@ struct KdArgs {
   const int32_t* block_idx;  // [batch, h_kv, top_k]
   void* o;
   float* lse;
-  float* part_o;             // [batch, h_kv, split, G, D] (split > 1)
-  float* part_lse;           // [batch, h_kv, split, G]
-  int32_t batch, h_q, h_kv, group, top_k, max_pages, split;
+  float* part_o;             // [batch, h_kv, split * waves, G, D] (split > 1), un-normalised
+  float2* part_ml;           // [batch, h_kv, split * waves, G]: (scaled max, sum)
+  int32_t batch, h_q, h_kv, group, top_k, max_pages, split, waves;
   float sm_scale;
 };
 
@@ -966,8 +966,10 @@ __device__ __forceinline__ void kd_load_unit(KdUnit<D, TC>& x, const KdArgs& a, 
 // are cut into 32-key units (4 per page); wave w of split sp takes units
 // sp*NW + w, + NW*split, ...  Each wave keeps an online softmax over its
 // units with the next unit's loads in flight while the current one is
-// computed; the NW waves are then combined in LDS, and the splits by
-// kd_merge_kernel.
+// computed.  Without a split the NW waves are then combined in LDS; with one,
+// every wave writes its own partial (un-normalised output and its max and
+// sum), and kd_merge_kernel combines all of a (sequence, group)'s partials,
+// so no wave waits on the others.
 template <int D, int NW, typename TC>
 __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   typedef bf16_t T;
@@ -1100,8 +1102,18 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
     cur = nxt;
     u = un;
   }
-  // o[dt][v]: d = dt*16 + 4*q4 + v, head l16.  Combine the NW waves in LDS
-  // (each wave's slab now holds its output rows).
+  // o[dt][v]: d = dt*16 + 4*q4 + v, head l16.
+  if (a.split > 1) {
+    const size_t pidx = (((size_t)sr * a.split + sp) * NW + wave) * G + l16;
+    if (l16 < G) {
+      float* po = a.part_o + pidx * D + 4 * q4;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+      if (q4 == 0) a.part_ml[pidx] = float2{lrun > 0.0f ? mrun * a.sm_scale : -__builtin_inff(), lrun};
+    }
+    return;
+  }
+  // Combine the NW waves in LDS (each wave's slab now holds its output rows).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1129,52 +1141,69 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
         wsum += ww;
       }
     }
-    const float lse_all = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
-    if (a.split == 1) {
-      T* out = static_cast<T*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
-      *out = from_f32<T>(wsum > 0.0f ? acc / wsum : 0.0f);
-      if (a.lse && d == 0) a.lse[(size_t)s * a.h_q + r * G + g] = lse_all;
-    } else {
-      const size_t pidx = ((size_t)sr * a.split + sp) * G + g;
-      a.part_o[pidx * D + d] = wsum > 0.0f ? acc / wsum : 0.0f;
-      if (d == 0) a.part_lse[pidx] = lse_all;
-    }
+    T* out = static_cast<T*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
+    *out = from_f32<T>(wsum > 0.0f ? acc / wsum : 0.0f);
+    if (a.lse && d == 0)
+      a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
   }
 }
 
-// LSE merge of the splits: one workgroup of D threads per (sequence, group,
-// head); every split's lse and value are loaded up front.
+// Merge of the per-wave partials of a split decode: one workgroup per
+// (sequence, group, head).  With M the largest partial max,
+//   o = sum_k e^(m_k - M) o_k / sum_k e^(m_k - M) l_k,  lse = M + ln(sum_k e^(m_k - M) l_k).
+// Lane k of wave 0 holds partial k's (max, sum): M and the denominator are
+// wave reductions and the weights go to LDS.  Thread (quarter qq, dim d) sums
+// partials 16 qq .. 16 qq + 15 of dim d, all loaded before any is used (a
+// clamped index keeps the loads unconditional; the weight of a partial past
+// the last is 0), and the four quarters are added in LDS.
+constexpr int kKdMaxParts = 64;  // split (a power of two, at most 16 for top_k <= 16) * 4 waves
+constexpr int kKdMergeQuarter = kKdMaxParts / 4;
 template <int D>
-__global__ __launch_bounds__(D) void kd_merge_kernel(KdArgs a) {
+__global__ __launch_bounds__(4 * D) void kd_merge_kernel(KdArgs a) {
+  __shared__ __attribute__((aligned(16))) float w_s[kKdMaxParts];
+  __shared__ float acc_s[4][D];
+  __shared__ float2 md_s;  // (M, denominator)
   const int G = a.group;
   const int sr = blockIdx.x / G, g = blockIdx.x % G;
   const int s = sr / a.h_kv, r = sr % a.h_kv;
-  const int d = threadIdx.x;
-  const size_t base = (size_t)sr * a.split * G + g;   // + k * G for split k
-  float l[kMaxTopK], x[kMaxTopK];
+  const int d = threadIdx.x % D, qq = threadIdx.x / D;
+  const int np = a.split * a.waves;
+  const size_t base = (size_t)sr * np * G + g;  // + k * G for partial k
+  float x[kKdMergeQuarter];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    l[k] = -__builtin_inff();
-    x[k] = 0.0f;
-    if (k < a.split) {
-      l[k] = scalar_load(a.part_lse, (int64_t)(base + (size_t)k * G));
-      x[k] = a.part_o[(base + (size_t)k * G) * D + d];
-    }
+  for (int e = 0; e < kKdMergeQuarter; ++e)
+    x[e] = a.part_o[(base + (size_t)min(qq * kKdMergeQuarter + e, np - 1) * G) * D + d];
+  if (threadIdx.x < 64) {
+    const int k = threadIdx.x;
+    const float2 ml = k < np ? a.part_ml[base + (size_t)k * G] : float2{-__builtin_inff(), 0.0f};
+    float mx = ml.x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float mref = mx == -__builtin_inff() ? 0.0f : mx;
+    const float w = fast_exp2((ml.x - mref) * kLog2e);  // 0 for an empty or missing partial
+    float den = w * ml.y;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
+    w_s[k] = w;
+    if (k == 0) md_s = float2{mref, den};
   }
-  float mx = -__builtin_inff();
+  __syncthreads();
+  float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) mx = fmaxf(mx, l[k]);
-  float acc = 0.0f, wsum = 0.0f;
+  for (int e = 0; e < kKdMergeQuarter; e += 4) {
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(w_s + qq * kKdMergeQuarter + e);
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    const float ww = (l[k] == -__builtin_inff()) ? 0.0f : fast_exp2((l[k] - mx) * kLog2e);
-    acc = fmaf(ww, x[k], acc);
-    wsum += ww;
+    for (int t = 0; t < 4; ++t) acc = fmaf(w4[t], x[e + t], acc);
   }
+  acc_s[qq][d] = acc;
+  __syncthreads();
+  if (qq != 0) return;
+  const float mref = md_s.x, den = md_s.y;
+  acc = acc_s[0][d] + acc_s[1][d] + acc_s[2][d] + acc_s[3][d];
   bf16_t* out = static_cast<bf16_t*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
-  *out = from_f32<bf16_t>(wsum > 0.0f ? acc / wsum : 0.0f);
+  *out = from_f32<bf16_t>(den > 0.0f ? acc / den : 0.0f);
   if (a.lse && d == 0)
-    a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+    a.lse[(size_t)s * a.h_q + r * G + g] = den > 0.0f ? mref + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
 }
 
 // ====================================================================
@@ -1480,9 +1509,10 @@ DecodePlan decode_plan(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_h, in
   p.split = split;
   p.waves = waves;
   const int G = h_q / h_kv;
+  const size_t parts = (size_t)pairs * split * waves * G;  // one partial per wave and head
   size_t off = 0;
-  p.off_part_o = off; off = align_up(off + (size_t)pairs * split * G * d_h * 4);
-  p.off_part_lse = off; off = align_up(off + (size_t)pairs * split * G * 4);
+  p.off_part_o = off; off = align_up(off + parts * d_h * 4);
+  p.off_part_lse = off; off = align_up(off + parts * 8);
   p.total = split > 1 ? off : 0;
   return p;
 }
@@ -1500,7 +1530,7 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.lse = a.lse;
   char* ws = static_cast<char*>(a.ws);
   k.part_o = pl.split > 1 ? reinterpret_cast<float*>(ws + pl.off_part_o) : nullptr;
-  k.part_lse = pl.split > 1 ? reinterpret_cast<float*>(ws + pl.off_part_lse) : nullptr;
+  k.part_ml = pl.split > 1 ? reinterpret_cast<float2*>(ws + pl.off_part_lse) : nullptr;
   k.batch = a.batch;
   k.h_q = a.h_q;
   k.h_kv = a.h_kv;
@@ -1508,7 +1538,9 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.top_k = a.top_k;
   k.max_pages = a.max_pages;
   k.split = pl.split;
+  k.waves = pl.waves;
   k.sm_scale = a.sm_scale;
+  if (pl.split > 1 && pl.split * pl.waves > kKdMaxParts) return hipErrorInvalidValue;
   const int pd = profile_begin(PK_KD, st);
   const dim3 grid((unsigned)(a.batch * a.h_kv * pl.split));
   if (pl.waves == kKdWavesSplit)
@@ -1518,7 +1550,7 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   profile_end(pd, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.split == 1) return e;
-  hipLaunchKernelGGL((kd_merge_kernel<D>), dim3(a.batch * a.h_kv * a.group), dim3(D), 0, st, k);
+  hipLaunchKernelGGL((kd_merge_kernel<D>), dim3(a.batch * a.h_kv * a.group), dim3(4 * D), 0, st, k);
   return hipGetLastError();
 }
 
