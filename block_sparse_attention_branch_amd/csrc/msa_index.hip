@@ -500,24 +500,27 @@ __device__ __forceinline__ void select_write_row(const KiDecodeArgs& a, int s, i
 // NT threads per row, thread t holding the candidates t + NT u, u < U.  Keys
 // are the order-preserving bits of the score with the inverted block id below
 // them, so they are unique and "larger" means better (ties to the lower block).
-//  1) each thread takes the maximum of its keys (0: no candidate).  Each wave
-//     finds t_w, the 16th largest of its 64 thread maxima (0 when fewer than
-//     16 lanes hold a candidate), by counting for every lane the maxima above
-//     its own (the wave's maxima are read from LDS as broadcasts);
-//     T = max_w t_w bounds the answer from below: the wave that attains it
-//     holds 16 keys >= T;
-//  2) every key >= T survives.  In a wave at most 16 lanes have a maximum
-//     >= T (t_w <= T), so at most 16 * (NT / 64) threads hold survivors and at
-//     most 16 * (NT / 64) * U keys survive: the LDS buffer holds them all;
+//  1) each thread takes the maximum of its keys (0: no candidate).  Every lane
+//     counts the maxima of its wave above its own (read from LDS as
+//     broadcasts); as the nonzero maxima are unique, the lane that counts
+//     j - 1 holds the wave's j-th largest maximum t_w(j), j = 1, 2, 4, 8, 16
+//     (0 when fewer than j lanes hold a candidate);
+//  2) a lower bound T of the 16th best key: for m = 16 / j, m waves each hold
+//     j keys >= their t_w(j), so the m-th largest t_w(j) over the waves is
+//     one; T is the largest of these bounds.  T >= max_w t_w(16), so in every
+//     wave at most 16 lanes hold a maximum >= T, and at most 16 * NW * U keys
+//     are >= T: the LDS buffer holds every survivor;
 //  3) each survivor's rank among the survivors places the best 16 in order.
 template <int NT, int U>
 __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kCap = kMaxTopK * NW * U;
+  constexpr int kLevels = 5;  // j = 16 >> e
   __shared__ uint64_t tm[NT];
-  __shared__ uint64_t wthr[NW];
+  __shared__ uint64_t wthr[kLevels][NW];
   __shared__ uint64_t surv[kCap];
   __shared__ uint64_t top[kMaxTopK];
+  __shared__ uint64_t thr;
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
   const int L = scalar_load(a.seq_lens, s);
@@ -547,26 +550,42 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
   if (tid < kMaxTopK) top[tid] = 0;
   __syncthreads();
   {
-    // gt / ge: the wave's maxima above / at least this lane's
     const uint64_t* wm = tm + wave * 64;
-    int gt = 0, ge = 0;
+    int gt = 0;
 #pragma unroll 8
     for (int j = 0; j < 64; j += 2) {
       typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
       const u64x2 p = *reinterpret_cast<const u64x2*>(wm + j);
       gt += (p[0] > tmax ? 1 : 0) + (p[1] > tmax ? 1 : 0);
-      ge += (p[0] >= tmax ? 1 : 0) + (p[1] >= tmax ? 1 : 0);
     }
-    // the lane holding the 16th largest value (all lanes holding it when it
-    // is 0, which then is the answer)
-    const uint64_t hit = __ballot(gt < kMaxTopK && ge >= kMaxTopK);
-    const uint64_t t = hit ? __shfl(tmax, __builtin_ctzll(hit), 64) : 0ull;  // hit is wave-uniform
-    if (lane == 0) wthr[wave] = t;
+#pragma unroll
+    for (int e = 0; e < kLevels; ++e) {
+      const uint64_t hit = __ballot(tmax != 0ull && gt == (16 >> e) - 1);
+      const uint64_t t = hit ? __shfl(tmax, __builtin_ctzll(hit), 64) : 0ull;  // hit is wave-uniform
+      if (lane == 0) wthr[e][wave] = t;
+    }
   }
   __syncthreads();
-  uint64_t T = 0;
+  if (wave == 0) {
+    // lane w < NW holds t_w(j); the m-th largest over the waves is the value
+    // with m - 1 larger ones (nonzero values are unique keys)
+    uint64_t T = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) T = wthr[w] > T ? wthr[w] : T;
+    for (int e = 0; e < kLevels; ++e) {
+      const int m = 1 << e;
+      if (m > NW) break;
+      const uint64_t x = lane < NW ? wthr[e][lane] : 0ull;
+      int g = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) g += wthr[e][w] > x ? 1 : 0;
+      const uint64_t hit = __ballot(x != 0ull && g == m - 1);
+      const uint64_t t = hit ? __shfl(x, __builtin_ctzll(hit), 64) : 0ull;
+      T = t > T ? t : T;
+    }
+    if (lane == 0) thr = T;
+  }
+  __syncthreads();
+  const uint64_t T = thr;
   if (tmax >= T && tmax != 0) {
     int c = 0;
 #pragma unroll
