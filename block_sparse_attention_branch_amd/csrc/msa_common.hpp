@@ -228,4 +228,12 @@ __device__ __forceinline__ void settle(const V& x) {
 // --------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_xor_f32(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// x of lane `lane`, which must be the same in every lane (v_readlane; a
+// shuffle would go through LDS).
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 }  // namespace msa

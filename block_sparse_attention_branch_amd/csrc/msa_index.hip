@@ -480,7 +480,7 @@ __device__ __forceinline__ void select_write_row(const KiDecodeArgs& a, int s, i
   }
   int rk = 0;
 #pragma unroll
-  for (int j = 0; j <= kMaxTopK; ++j) rk += __shfl(id, j, 64) < id ? 1 : 0;
+  for (int j = 0; j <= kMaxTopK; ++j) rk += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
   const bool valid = id != 0x7fffffff;
   const int n_valid = __popcll(__ballot(valid));
   const size_t row = (size_t)s * a.h_kv + r;
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < kLevels; ++e) {
       const uint64_t hit = __ballot(tmax != 0ull && gt == (16 >> e) - 1);
-      const uint64_t t = hit ? __shfl(tmax, __builtin_ctzll(hit), 64) : 0ull;  // hit is wave-uniform
+      const uint64_t t = hit ? readlane_u64(tmax, __builtin_ctzll(hit)) : 0ull;  // hit is wave-uniform
       if (lane == 0) wthr[e][wave] = t;
     }
   }
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) g += wthr[e][w] > x ? 1 : 0;
       const uint64_t hit = __ballot(x != 0ull && g == m - 1);
-      const uint64_t t = hit ? __shfl(x, __builtin_ctzll(hit), 64) : 0ull;
+      const uint64_t t = hit ? readlane_u64(x, __builtin_ctzll(hit)) : 0ull;
       T = t > T ? t : T;
     }
     if (lane == 0) thr = T;
