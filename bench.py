@@ -140,11 +140,11 @@ CALL_KERNELS = {
 }
 CALL_FIRST = {"index_prefill": "ki_prefill_kernel", "sparse_prefill": "ks_count",
               "index_decode": "ki_decode_scan_kernel", "sparse_decode": "kd_kernel"}
-# Legs of the default step, in launch order: two prefill legs (each starts with
-# an index prefill launch) and two decode legs (each decode call starts with an
-# index scan launch; the 64 x 128K step once, then LONG_DECODE_STEPS steps at 1M).
+# Legs of the default run, in launch order: two prefill legs (each starts with
+# an index prefill launch), then the 64 x 128K decode step (its index scan is the
+# first after the 1M prefill); the 1M decode steps of the latency probe follow
+# the last step, so every later index scan belongs to them.
 STEP_PREFILL_LEGS = ("prefill128k", "prefill1m")
-LONG_DECODE_STEPS = 256
 TRAFFIC_KERNELS = ("ki_prefill_kernel", "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "kd_kernel")
 
 
@@ -505,16 +505,20 @@ def main():
 def bench_step(msa, args):
     """The default step: every hot-path call at 128K and 1M context.
 
-    Legs, in launch order:
+    Legs of a timed step, in launch order:
       prefill128k    planted 131072-token causal prefill (contiguous cache):
                      msa_index_topk + msa_sparse_prefill over all queries;
       prefill1m      chunked prefill of the last 8192 queries of a 1,048,576-token
                      paged cache: msa_index_topk + msa_sparse_prefill;
       decode64x128k  one decode step of 64 sequences x 131072 tokens, paged,
-                     4 rotating query sets: msa_index_topk + msa_sparse_decode;
-      decode1m       256 decode steps of the 1M sequence (batch 1), each after
-                     appending its token to the caches; every step is launched
-                     from an idle GPU and timed on its own (p50 / p99).
+                     4 rotating query sets: msa_index_topk + msa_sparse_decode.
+    After the timed steps, a latency probe:
+      decode1m       256 decode steps of the 1M sequence (batch 1) per timed
+                     step, each after appending its token to the caches; every
+                     step is launched on an idle GPU and timed on its own
+                     (p50 / p99), then 256 replays of the step from a HIP graph.
+    The probe runs outside the timed steps because its idle gaps let the GPU
+    clock down, which would slow the prefill launched after it.
     ``value`` = prefill tokens of the step / the GPU time of the four prefill
     calls (HIP events on the launch stream)."""
     dev = "cuda"
@@ -596,31 +600,19 @@ def bench_step(msa, args):
     d1m = CallTimer(["decode1m_index", "decode1m_sparse"])
 
     def run_step(s, timed):
-        ev = timer.step(prefill_calls + decode_c(s % 4)) if timed else [f() for f in prefill_calls + decode_c(s % 4)]
-        evd = []
-        for t in range(n_dec):
-            append(t)
-            if timed:
-                torch.cuda.synchronize()
-                evd.append(d1m.step(decode_1m(t)))
-            else:
-                for f in decode_1m(t):
-                    f()
-        return ev, evd
+        calls = prefill_calls + decode_c(s % 4)
+        return timer.step(calls) if timed else [f() for f in calls]
 
     for w in range(args.warmup):
         run_step(w, False)
     torch.cuda.synchronize()
-    evs, evds = [], []
+    evs = []
     t0 = time.perf_counter()
     for s in range(args.steps):
-        ev, evd = run_step(s, True)
-        evs.append(ev)
-        evds.extend(evd)
+        evs.append(run_step(s, True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer.collect(evs)
-    d1m.collect(evds)
     print(f"[bench] {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
     # Kernel timing: steps again with every launch of the hot kernels bracketed
     # by HIP events on its stream (after the timed region: the extra events add
@@ -640,7 +632,20 @@ def bench_step(msa, args):
             if cnt:
                 kern[k] = {"launches_per_step": cnt / reps, "avg_launch_ms": round(tot / cnt, 5),
                            "ms_per_step": round(tot / reps, 4)}
-    # the 1M decode steps replayed from a captured HIP graph (new queries and the
+    # latency probe: the 1M decode steps, each launched on an idle GPU
+    for t in range(16):
+        append(t)
+        for f in decode_1m(t):
+            f()
+    evds = []
+    for s in range(args.steps):
+        for t in range(n_dec):
+            append(t)
+            torch.cuda.synchronize()
+            evds.append(d1m.step(decode_1m(t)))
+    d1m.collect(evds)
+    print(f"[bench] {len(evds)} decode steps at 1M timed", file=sys.stderr, flush=True)
+    # the same steps replayed from a captured HIP graph (new queries and the
     # sequence length written into the captured buffers before each replay)
     qb, qib = lc["step_q"][0].clone(), lc["step_q_idx"][0].clone()
 
@@ -758,10 +763,11 @@ def bench_step(msa, args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic, seeded (planted-needle index keys at 128K, N(0,1) elsewhere); no weights",
-        "config": {"workload": "prefill 1x131072 planted (whole causal prefill) + prefill chunk of the last 8192 "
-                               "queries at 1048576 ctx (paged) + decode step 64x131072 paged + 256 decode steps "
-                               "(batch 1) at 1048576 ctx; 64 q / 4 kv heads, d_h 128, d_idx 64, B_k 128, k 16, "
-                               "diagonal block kept",
+        "config": {"workload": "step = prefill 1x131072 planted (whole causal prefill) + prefill chunk of the "
+                               "last 8192 queries at 1048576 ctx (paged) + decode step 64x131072 paged; after the "
+                               "timed steps, 256 decode steps (batch 1) at 1048576 ctx per step, each launched on "
+                               "an idle GPU; 64 q / 4 kv heads, d_h 128, d_idx 64, B_k 128, k 16, diagonal block "
+                               "kept",
                    "prefill_tokens_per_step": n_a + n_b, "seq_len": n_a, "long_ctx": n_ctx, "decode_batch": B,
                    "decode_ctx": L_dec, "long_decode_steps": n_dec, "parallelism": "single GPU"},
         "prefill_ms": round(prefill_ms, 4),
