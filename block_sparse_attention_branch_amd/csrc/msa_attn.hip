@@ -978,8 +978,8 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   constexpr int kSlab = kVtBytes > kOBytes ? kVtBytes : kOBytes;
   // per wave: the V^T slice while units run, then its output rows
   __shared__ __attribute__((aligned(16))) char slab[NW][kSlab];
-  __shared__ float llds[NW][16];
-  __shared__ float lrs[NW][16];
+  __shared__ float2 mls[NW][16];  // per wave and head: (scaled max, sum)
+  __shared__ float cw[NW][16];    // per wave and head: e^(m_w - M) / denominator
   const int sp = blockIdx.x % a.split;
   const int sr = blockIdx.x / a.split;
   const int s = sr / a.h_kv, r = sr % a.h_kv;
@@ -1113,7 +1113,10 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
     }
     return;
   }
-  // Combine the NW waves in LDS (each wave's slab now holds its output rows).
+  // Combine the NW waves: each wave's slab now holds its un-normalised output
+  // rows and mls its (max, sum) per head.  The weights e^(m_w - M) / den are
+  // formed once per (wave, head); then every thread sums 4 consecutive dims of
+  // one head over the waves.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1122,29 +1125,39 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) ow[l16 * (D + 1) + dt * 16 + 4 * q4 + v] = o[dt][v];
-  if (q4 == 0) {
-    llds[wave][l16] = (lrun > 0.0f) ? mrun * a.sm_scale + __builtin_amdgcn_logf(lrun) * kLn2 : -__builtin_inff();
-    lrs[wave][l16] = lrun;
-  }
+  if (q4 == 0) mls[wave][l16] = float2{lrun > 0.0f ? mrun * a.sm_scale : -__builtin_inff(), lrun};
   __syncthreads();
-  for (int x = threadIdx.x; x < G * D; x += NW * 64) {
-    const int g = x / D, d = x % D;
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, llds[w][g]);
-    float acc = 0.0f, wsum = 0.0f;
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mls[w][g].x);
+    const float mref = mx == -__builtin_inff() ? 0.0f : mx;
+    float e[NW];
+    float den = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      if (lrs[w][g] > 0.0f) {
-        const float ww = fast_exp2((llds[w][g] - mx) * kLog2e);
-        acc += ww * reinterpret_cast<const float*>(slab[w])[g * (D + 1) + d] / lrs[w][g];
-        wsum += ww;
-      }
+      e[w] = fast_exp2((mls[w][g].x - mref) * kLog2e);  // 0 for a wave without keys
+      den = fmaf(e[w], mls[w][g].y, den);
     }
-    T* out = static_cast<T*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d;
-    *out = from_f32<T>(wsum > 0.0f ? acc / wsum : 0.0f);
-    if (a.lse && d == 0)
-      a.lse[(size_t)s * a.h_q + r * G + g] = wsum > 0.0f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cw[w][g] = e[w] * inv;
+    if (a.lse)
+      a.lse[(size_t)s * a.h_q + r * G + g] = den > 0.0f ? mref + __builtin_amdgcn_logf(den) * kLn2 : -__builtin_inff();
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * (D / 4); x += NW * 64) {
+    const int g = x / (D / 4), d0 = (x % (D / 4)) * 4;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = cw[w][g];
+      const float* src = reinterpret_cast<const float*>(slab[w]) + g * (D + 1) + d0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = fmaf(c, src[t], acc[t]);
+    }
+    store4<T>(static_cast<T*>(a.o) + ((size_t)s * a.h_q + r * G + g) * D + d0, acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
