@@ -451,6 +451,29 @@ def decode_e4m3(codes):
     return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, out)
 
 
+def decode_e8m0(codes):
+    """Values of OCP E8M0 codes, the shared scale of the MX block formats
+    (the MXFP8 cache format named on the zhichai.net key points page,
+    Limitations): an 8-bit biased exponent with no sign and no mantissa,
+    value 2^(code - 127); the code 0xFF is NaN.  Returns float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 0xFF, np.nan, np.ldexp(1.0, c - 127))
+
+
+def decode_mxfp8(codes, scales, block=32):
+    """Values of an MXFP8 (E4M3 elements) tensor: along the last axis, every
+    run of ``block`` = 32 consecutive elements shares one E8M0 scale, and an
+    element's value is its E4M3 value times that scale.  ``codes`` [..., d]
+    uint8, ``scales`` [..., d / 32] uint8; returns float64 [..., d]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8)
+    d = c.shape[-1]
+    assert d % block == 0 and s.shape == c.shape[:-1] + (d // block,)
+    elem = decode_e4m3(c)
+    scale = np.repeat(decode_e8m0(s), block, axis=-1)
+    return elem * scale
+
+
 # --------------------------------------------------------------------------
 # FLOP model ([P1] §5.2 Eq. (12))
 # --------------------------------------------------------------------------

@@ -62,6 +62,64 @@ def _randn(shape, gen, device, dtype, scale=1.0, rows_per_chunk=None):
     return out
 
 
+MX_BLOCK = 32        # elements per shared scale of the MX formats
+MXFP8 = "mxfp8"      # cache_dtype value: E4M3 codes plus one E8M0 scale per 32 elements
+
+
+def mx_encode(x: torch.Tensor):
+    """OCP MXFP8 (E4M3 elements) encoding of ``x`` along its last dim.
+
+    Every run of 32 consecutive elements gets shared_exp = floor(log2(max |x|))
+    - 8 (8 = the largest E4M3 exponent), clamped to [-127, 127] (an all-zero
+    run gets -127); its elements x / 2^shared_exp are rounded to E4M3 (nearest
+    even, saturating at +-448) and its scale byte is shared_exp + 127.
+    Returns (codes as torch.float8_e4m3fn, scales uint8 [..., d / 32])."""
+    d = x.shape[-1]
+    assert d % MX_BLOCK == 0
+    xb = x.to(torch.float32).reshape(*x.shape[:-1], d // MX_BLOCK, MX_BLOCK)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.floor(torch.log2(amax.clamp_min(torch.finfo(torch.float32).tiny))) - 8.0
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127.0, 127.0)
+    q = (xb / torch.exp2(e).unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.reshape(x.shape), (e + 127.0).to(torch.uint8)
+
+
+def _randn_mx(shape, gen, device, scale=1.0, rows_per_chunk=None):
+    """MXFP8 cache tensor: N(0, scale^2) draws in which every 32-element run of
+    the last dim is multiplied by 2^u, u uniform in {-4..4} (so neighbouring
+    runs get different shared scales), then encoded with ``mx_encode``.
+    Returns (codes float8_e4m3fn ``shape``, scales uint8 ``shape[:-1] + (d/32,)``)."""
+    shape = tuple(int(s) for s in shape)
+    codes = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    scales = torch.empty(shape[:-1] + (shape[-1] // MX_BLOCK,), dtype=torch.uint8, device=device)
+    if codes.numel() == 0:
+        return codes, scales
+    per_row = max(1, codes[0].numel())
+    if rows_per_chunk is None:
+        rows_per_chunk = max(1, (1 << 25) // per_row)
+    for s in range(0, shape[0], rows_per_chunk):
+        e = min(shape[0], s + rows_per_chunk)
+        x = torch.randn((e - s,) + shape[1:], generator=gen, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        u = torch.randint(-4, 5, (e - s,) + shape[1:-1] + (shape[-1] // MX_BLOCK, 1), generator=gen,
+                          device=device, dtype=torch.int32)
+        x = (x.reshape((e - s,) + shape[1:-1] + (shape[-1] // MX_BLOCK, MX_BLOCK)) * torch.exp2(u.float()))
+        c, sc = mx_encode(x.reshape((e - s,) + shape[1:]))
+        codes[s:e].copy_(c)
+        scales[s:e].copy_(sc)
+    return codes, scales
+
+
+def _cache(out: dict, name: str, shape, gen, device, cdt, scale=1.0):
+    """Cache tensor ``name`` in storage type ``cdt`` (a torch dtype, or MXFP8:
+    E4M3 codes in ``name`` and their scales in ``name + '_scale'``)."""
+    if cdt == MXFP8:
+        out[name], out[name + "_scale"] = _randn_mx(shape, gen, device, scale)
+    else:
+        out[name] = _randn(shape, gen, device, cdt, scale)
+
+
 def gen_prefill(n_kv: int, shape: HeadShape = MODEL_SHAPE, *, n_q: int | None = None,
                 dtype=torch.bfloat16, seed: int = 1, device="cpu",
                 scaled: bool = True, cache_dtype=None) -> dict:
@@ -71,19 +129,18 @@ def gen_prefill(n_kv: int, shape: HeadShape = MODEL_SHAPE, *, n_q: int | None = 
     Layouts: q [n_q, h_q, d_h], k/v [n_kv, h_kv, d_h], q_idx [n_q, h_kv, d_idx],
     k_idx [n_kv, d_idx].  With ``scaled`` every tensor is N(0,1)/sqrt(last dim),
     otherwise N(0,1).  ``cache_dtype`` (default ``dtype``) is the storage type
-    of k, v and k_idx, e.g. torch.float8_e4m3fn.
+    of k, v and k_idx, e.g. torch.float8_e4m3fn, or MXFP8 (then ``k_scale``,
+    ``v_scale`` and ``k_idx_scale`` hold the E8M0 scales, see ``_randn_mx``).
     """
     cdt = dtype if cache_dtype is None else cache_dtype
     n_q = n_kv if n_q is None else n_q
     g = _gen(seed, device)
     sh = lambda d: (1.0 / math.sqrt(d)) if scaled else 1.0  # noqa: E731
-    out = {
-        "q": _randn((n_q, shape.h_q, shape.d_h), g, device, dtype, sh(shape.d_h)),
-        "k": _randn((n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h)),
-        "v": _randn((n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h)),
-        "q_idx": _randn((n_q, shape.h_kv, shape.d_idx), g, device, dtype, sh(shape.d_idx)),
-        "k_idx": _randn((n_kv, shape.d_idx), g, device, cdt, sh(shape.d_idx)),
-    }
+    out = {"q": _randn((n_q, shape.h_q, shape.d_h), g, device, dtype, sh(shape.d_h))}
+    _cache(out, "k", (n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h))
+    _cache(out, "v", (n_kv, shape.h_kv, shape.d_h), g, device, cdt, sh(shape.d_h))
+    out["q_idx"] = _randn((n_q, shape.h_kv, shape.d_idx), g, device, dtype, sh(shape.d_idx))
+    _cache(out, "k_idx", (n_kv, shape.d_idx), g, device, cdt, sh(shape.d_idx))
     out["q_start"] = n_kv - n_q
     out["n_kv"] = n_kv
     return out
@@ -114,13 +171,13 @@ def gen_decode_paged(batch: int, seq_len: int, shape: HeadShape = MODEL_SHAPE, *
     out = {
         "page_table": perm.view(batch, max_pages).contiguous().to(device),
         "seq_lens": torch.tensor(seq_lens, dtype=torch.int32).to(device),
-        "k_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt),
-        "v_pages": _randn((num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt),
-        "k_idx_pages": _randn((num_pages, BLOCK, shape.d_idx), g, device, cdt),
-        "q": _randn((n_query_sets, batch, shape.h_q, shape.d_h), g, device, dtype),
-        "q_idx": _randn((n_query_sets, batch, shape.h_kv, shape.d_idx), g, device, dtype),
-        "max_pages": max_pages,
     }
+    _cache(out, "k_pages", (num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt)
+    _cache(out, "v_pages", (num_pages, shape.h_kv, BLOCK, shape.d_h), g, device, cdt)
+    _cache(out, "k_idx_pages", (num_pages, BLOCK, shape.d_idx), g, device, cdt)
+    out["q"] = _randn((n_query_sets, batch, shape.h_q, shape.d_h), g, device, dtype)
+    out["q_idx"] = _randn((n_query_sets, batch, shape.h_kv, shape.d_idx), g, device, dtype)
+    out["max_pages"] = max_pages
     return out
 
 

@@ -392,6 +392,74 @@ def test_e4m3_decoder_matches_torch_float8_e4m3fn():
     assert np.all(both_nan | (ref == got))
 
 
+# ------------------------------------------------------- MXFP8 (E8M0 scales)
+
+def test_e8m0_decoder_closed_forms_and_torch():
+    # the scale format's definition: 2^(code - 127), 0xFF = NaN, no sign
+    cases = {127: 1.0, 128: 2.0, 126: 0.5, 0: 2.0 ** -127, 1: 2.0 ** -126, 254: 2.0 ** 127, 137: 1024.0}
+    got = orc.decode_e8m0(np.array(list(cases), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(cases.values())))
+    assert np.isnan(orc.decode_e8m0(np.array([255], dtype=np.uint8)))[0]
+    # an independent implementation of the same format, every code
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = orc.decode_e8m0(codes.numpy())
+    assert np.all((np.isnan(ref) & np.isnan(got)) | (ref == got))
+
+
+def test_mxfp8_decoder_unit_scale_and_block_mapping():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(3, 2, 128), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    unit = np.full((3, 2, 4), 127, dtype=np.uint8)
+    # unit scales reduce to the element format
+    assert np.array_equal(orc.decode_mxfp8(codes, unit), orc.decode_e4m3(codes))
+    # one scale byte moves exactly its own 32 elements, by its power of two
+    base = orc.decode_mxfp8(codes, unit)
+    for (i, j, q, de) in ((0, 0, 0, 1), (2, 1, 3, -3), (1, 0, 2, 10)):
+        sc = unit.copy()
+        sc[i, j, q] = 127 + de
+        got = orc.decode_mxfp8(codes, sc)
+        want = base.copy()
+        want[i, j, 32 * q:32 * q + 32] *= 2.0 ** de
+        assert np.array_equal(got, want)
+    # closed forms: 1.0 at scale 2^3, 448 at 2^10, -2^-9 at 2^-5
+    c = np.zeros((1, 96), dtype=np.uint8)
+    c[0, 5], c[0, 40], c[0, 70] = 0x38, 0x7E, 0x81
+    v = orc.decode_mxfp8(c, np.array([[130, 137, 122]], dtype=np.uint8))
+    assert v[0, 5] == 8.0 and v[0, 40] == 448.0 * 1024 and v[0, 70] == -(2.0 ** -14)
+
+
+def test_mx_encoder_round_trip_through_the_oracle_decoder():
+    # values an MXFP8 block holds exactly (E4M3 values whose block maximum
+    # lies in [256, 448], times a power of two per block) come back exactly;
+    # arbitrary values come back within half an E4M3 step of their block
+    from synth.inputs import mx_encode
+    g = torch.Generator().manual_seed(3)
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    e4 = e4[torch.isfinite(e4)]
+    x = e4[torch.randint(0, e4.numel(), (6, 4, 32), generator=g)]
+    x[..., 0] = 256.0 + 32.0 * torch.randint(0, 6, (6, 4), generator=g).float()  # block max in [256, 416]
+    x = x * torch.exp2(torch.randint(-20, 20, (6, 4, 1), generator=g).float())
+    codes, scales = mx_encode(x.reshape(6, 128))
+    back = orc.decode_mxfp8(codes.view(torch.uint8).numpy(), scales.numpy())
+    assert np.array_equal(back, x.reshape(6, 128).double().numpy())
+    y = torch.randn(64, 256, generator=g) * torch.exp2(torch.randint(-8, 8, (64, 8), generator=g).float()).repeat_interleave(32, 1)
+    codes, scales = mx_encode(y)
+    back = orc.decode_mxfp8(codes.view(torch.uint8).numpy(), scales.numpy())
+    yd = y.double().numpy()
+    X = np.repeat(orc.decode_e8m0(scales.numpy()), 32, axis=1)
+    # the block maximum scales into [256, 512): elements past the largest E4M3
+    # value, 448, saturate to it; the others keep 3 mantissa bits (relative
+    # error <= 2^-4), down to the subnormal step 2^-9 (absolute error <= 2^-10)
+    assert np.all((np.abs(yd).reshape(64, 8, 32).max(-1) / X[:, ::32] >= 256.0))
+    sat = np.abs(yd) > 448.0 * X
+    assert np.array_equal(back[sat], np.sign(yd[sat]) * 448.0 * X[sat])
+    err = np.abs(back - yd)[~sat]
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(yd[~sat]), 2.0 ** -10 * X[~sat]))
+    assert scales.dtype == torch.uint8 and codes.dtype == torch.float8_e4m3fn
+
+
 # ------------------------------------------------- mean-pool ablation ([P5])
 
 def test_mean_pool_equals_score_of_mean_key():
