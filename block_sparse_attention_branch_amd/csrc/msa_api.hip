@@ -61,18 +61,32 @@ msa_status check_shape(const msa_shape* s, bool need_idx, bool need_attn) {
   return MSA_OK;
 }
 
-bool fp8_cache(const msa_shape& s) { return s.cache_dtype == MSA_FP8_E4M3; }
+bool mx_cache(const msa_shape& s) { return s.cache_dtype == MSA_MXFP8_E4M3; }
+bool fp8_cache(const msa_shape& s) { return s.cache_dtype == MSA_FP8_E4M3 || mx_cache(s); }
 
-// e4m3 caches: bf16 compute only; every call but the dense comparison.
+// 8-bit caches (e4m3, MXFP8): bf16 compute only; every call but the dense
+// comparison, the backward and the projections.
 msa_status check_cache_dtype(const msa_shape& s, bool allowed) {
   if (!fp8_cache(s)) return MSA_OK;
-  if (s.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches need dtype MSA_BF16");
-  if (!allowed) return fail(MSA_ERR_UNSUPPORTED, "e4m3 caches are not built for the dense comparison call");
+  if (s.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "8-bit (e4m3, MXFP8) caches need dtype MSA_BF16");
+  if (!allowed)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "8-bit (e4m3, MXFP8) caches are not built for the dense comparison, the backward or the projections");
   return MSA_OK;
 }
 
-// Kernel dispatch code: 0 bf16, 1 fp32, 2 bf16 with e4m3 caches.
-int kernel_dtype(const msa_shape& s) { return fp8_cache(s) ? 2 : s.dtype; }
+// MXFP8 caches: the scale arrays the call reads must be given.
+msa_status check_scales(const msa_shape& s, const msa_kv* kv, bool need_idx, bool need_kv) {
+  if (!mx_cache(s)) return MSA_OK;
+  if (need_idx && !kv->k_idx_scale) return fail(MSA_ERR_INVALID_ARG, "MXFP8 caches: kv->k_idx_scale is NULL");
+  if (need_kv && (!kv->k_scale || !kv->v_scale))
+    return fail(MSA_ERR_INVALID_ARG, "MXFP8 caches: kv->k_scale/v_scale is NULL");
+  return MSA_OK;
+}
+
+// Kernel dispatch code: 0 bf16, 1 fp32, 2 bf16 with e4m3 caches, 3 bf16 with
+// MXFP8 caches.
+int kernel_dtype(const msa_shape& s) { return mx_cache(s) ? 3 : (fp8_cache(s) ? 2 : s.dtype); }
 
 msa_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return MSA_OK;
@@ -103,6 +117,7 @@ msa_status launch_index_decode(const msa_shape& s, int32_t batch, const void* q_
   msa::KiDecodeArgs a{};
   a.q_idx = q_idx;
   a.k_idx = kv->k_idx;
+  a.k_idx_scale = mx_cache(s) ? kv->k_idx_scale : nullptr;
   a.page_table = kv->page_table;
   a.seq_lens = kv->seq_lens;
   a.batch = batch;
@@ -173,6 +188,7 @@ msa_status msa_index_topk_decode_static(const msa_shape* shape, int32_t batch, c
   if (!kv->k_idx) return fail(MSA_ERR_INVALID_ARG, "kv->k_idx is NULL");
   if (!aligned16(q_idx) || !aligned16(kv->k_idx)) return fail(MSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned");
   if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
+  if ((st = check_scales(s, kv, true, false)) != MSA_OK) return st;
   if (!kv->seq_lens || !kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs seq_lens and a page_table");
   if (kv->max_pages < 1 || kv->max_pages > msa::kMaxDecodePages)
     return fail(MSA_ERR_UNSUPPORTED, "max_pages=%d not in [1,%d]", kv->max_pages, msa::kMaxDecodePages);
@@ -292,6 +308,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   const int need_diag = (block_score != nullptr || !s.force_local) ? 1 : 0;
 
   if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
+  if ((st = check_scales(s, kv, true, false)) != MSA_OK) return st;
   if (kv->seq_lens) {  // decode mode
     if (n_q != 1) return fail(MSA_ERR_INVALID_ARG, "decode mode (seq_lens given) needs n_q == 1, got %d", n_q);
     if (!kv->page_table) return fail(MSA_ERR_INVALID_ARG, "decode mode needs a page_table");
@@ -319,6 +336,7 @@ msa_status msa_index_topk(const msa_shape* shape, int32_t batch, int32_t n_q, in
   msa::KiPrefillArgs a{};
   a.q_idx = q_idx;
   a.k_idx = kv->k_idx;
+  a.k_idx_scale = mx_cache(s) ? kv->k_idx_scale : nullptr;
   a.page_table = kv->page_table;
   a.n_rows = p.n_rows;
   a.h_kv = s.h_kv;
@@ -353,6 +371,7 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   const msa_shape& s = *shape;
   if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if ((st = check_scales(s, kv, false, true)) != MSA_OK) return st;
   if (kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_prefill takes one sequence: seq_lens must be NULL");
   if (n_q < 0 || q_start < 0) return fail(MSA_ERR_INVALID_ARG, "n_q=%d q_start=%d", n_q, q_start);
   if ((int64_t)q_start + n_q > kv->n_kv)
@@ -370,6 +389,8 @@ msa_status msa_sparse_prefill(const msa_shape* shape, int32_t n_q, int32_t q_sta
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
+  a.k_scale = mx_cache(s) ? kv->k_scale : nullptr;
+  a.v_scale = mx_cache(s) ? kv->v_scale : nullptr;
   a.page_table = kv->page_table;
   a.block_idx = block_idx;
   a.o = o;
@@ -516,6 +537,7 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
   if ((st = check_cache_dtype(s, true)) != MSA_OK) return st;
   if (!msa::decode_supported(kernel_dtype(s), s.d_h)) return fail(MSA_ERR_UNSUPPORTED, "decode is built for bf16 only");
   if (!kv) return fail(MSA_ERR_INVALID_ARG, "kv is NULL");
+  if ((st = check_scales(s, kv, false, true)) != MSA_OK) return st;
   if (!kv->page_table || !kv->seq_lens) return fail(MSA_ERR_INVALID_ARG, "decode needs a paged cache with seq_lens");
   if (kv->max_pages < 1) return fail(MSA_ERR_INVALID_ARG, "max_pages=%d", kv->max_pages);
   if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch=%d", batch);
@@ -529,6 +551,8 @@ msa_status msa_sparse_decode(const msa_shape* shape, int32_t batch, const void* 
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
+  a.k_scale = mx_cache(s) ? kv->k_scale : nullptr;
+  a.v_scale = mx_cache(s) ? kv->v_scale : nullptr;
   a.page_table = kv->page_table;
   a.seq_lens = kv->seq_lens;
   a.block_idx = block_idx;

@@ -357,6 +357,8 @@ struct KpArgs {
   const void* q;
   const void* k;
   const void* v;
+  const uint8_t* k_scale;  // MXFP8 caches only
+  const uint8_t* v_scale;
   const int32_t* page_table;
   const int32_t* cell_off;
   const int32_t* item_off;
@@ -503,7 +505,8 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
 
   StageRegs<T, D, NT, TC> pre;
   KpItem cur = kp_item_s<T, D>(a, it);
-  stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv));
+  stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, cur.b, cur.r, a.h_kv, a.n_kv, a.k_scale,
+                                                 a.v_scale));
   int pre_ent = a.entries[cur.e_begin + min(tid, cur.e_end - cur.e_begin - 1)];
   stage_store<T, D, NT, TC>(pre, lds[0]);
   reinterpret_cast<int*>(lds[0] + L::BYTES)[tid] = pre_ent;
@@ -518,7 +521,8 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
     int nxt_ent = 0;
     if (has_next) {
       nxt = kp_item_s<T, D>(a, nx);
-      stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv));
+      stage_load<T, D, NT, TC>(pre, block_ptr<TC, D>(a.k, a.v, a.page_table, nxt.b, nxt.r, a.h_kv, a.n_kv,
+                                                     a.k_scale, a.v_scale));
       const int ne = nxt.e_end - nxt.e_begin;
       pre_ent = a.entries[nxt.e_begin + min(tid, ne - 1)];
       nxt_ent = a.entries[nxt.e_begin + min(rho0 >> a.g_shift, ne - 1)];
@@ -578,6 +582,8 @@ struct KmArgs {
   const void* q;
   const void* k;
   const void* v;
+  const uint8_t* k_scale;  // MXFP8 caches only
+  const uint8_t* v_scale;
   const int32_t* page_table;
   const int32_t* block_idx;
   const void* part_o;
@@ -638,7 +644,8 @@ __global__ __launch_bounds__(kKmThreads, 2) void km_kernel(KmArgs a) {
 
   // ---- phase A: the diagonal tile
   StageRegs<T, D, kKmThreads, TC> g;
-  stage_load<T, D, kKmThreads, TC>(g, block_ptr<TC, D>(a.k, a.v, a.page_table, bdiag, r, a.h_kv, a.n_kv));
+  stage_load<T, D, kKmThreads, TC>(
+      g, block_ptr<TC, D>(a.k, a.v, a.page_table, bdiag, r, a.h_kv, a.n_kv, a.k_scale, a.v_scale));
   int bl[kMaxTopK];
   const uint32_t used = row_used(a.block_idx + ((size_t)i * a.h_kv + r) * a.top_k, a.top_k, diag, bl);
   uint32_t parts = used;
@@ -882,6 +889,8 @@ struct KdArgs {
   const void* q;             // [batch, h_q, D]
   const void* k;             // pages [*, h_kv, 128, D]
   const void* v;
+  const uint8_t* k_scale;    // MXFP8 caches: [*, h_kv, 128, D / 32]
+  const uint8_t* v_scale;
   const int32_t* page_table; // [batch, max_pages]
   const int32_t* seq_lens;
   const int32_t* block_idx;  // [batch, h_kv, top_k]
@@ -904,6 +913,9 @@ template <int D, typename TC>
 struct KdUnit {
   Raw<TC> kf[2][D / 32];
   Raw<TC> vx[D / 32], vy[D / 32];
+  // MXFP8: the scale bytes of K rows tt*16 + l16 and of V rows 2*l16, 2*l16 + 1
+  // (a lane's dims q4*(D/4) .. +D/4 lie in one 32-element block); 0 otherwise
+  uint32_t ksc[2], vsc[2];
 };
 
 // Contraction-index / V-chunk maps.  16-bit caches: step ks of lane group q4
@@ -929,6 +941,15 @@ __device__ __forceinline__ void kd_load_unit(KdUnit<D, TC>& x, const KdArgs& a, 
   const size_t base = (((size_t)page * a.h_kv + r) * kBlock + qq * 32) * D;
   const TC* kb = static_cast<const TC*>(a.k) + base;
   const TC* vb = static_cast<const TC*>(a.v) + base;
+  if constexpr (kIsMx<TC>) {
+    const size_t sbase = base / kMxBlock + (q4 * (D / 4)) / kMxBlock;
+    x.ksc[0] = a.k_scale[sbase + (size_t)l16 * (D / kMxBlock)];
+    x.ksc[1] = a.k_scale[sbase + (size_t)(16 + l16) * (D / kMxBlock)];
+    x.vsc[0] = a.v_scale[sbase + (size_t)(2 * l16) * (D / kMxBlock)];
+    x.vsc[1] = a.v_scale[sbase + (size_t)(2 * l16 + 1) * (D / kMxBlock)];
+  } else {
+    x.ksc[0] = x.ksc[1] = x.vsc[0] = x.vsc[1] = 0u;
+  }
   if constexpr (sizeof(TC) == 1) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -1043,7 +1064,7 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
     for (int tt = 0; tt < 2; ++tt) {
       sc[tt] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], widen<T, TC>(cur.kf[tt][ks]), qf[ks]);
+      for (int ks = 0; ks < D / 32; ++ks) mma16(sc[tt], widen<T, TC>(cur.kf[tt][ks], cur.ksc[tt]), qf[ks]);
     }
     // sc[tt][v]: key (u%4)*32 + tt*16 + 4*q4 + v of block b, head l16
     const int key0 = b * kBlock + (u & 3) * 32;
@@ -1062,8 +1083,8 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
 #pragma unroll
     for (int it = 0; it < D / 32; ++it) {
       const int dc = kd_vchunk<TC, D>(q4, it);
-      const u32x4 vx = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vx[it]));
-      const u32x4 vy = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vy[it]));
+      const u32x4 vx = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vx[it], cur.vsc[0]));
+      const u32x4 vy = __builtin_bit_cast(u32x4, widen<T, TC>(cur.vy[it], cur.vsc[1]));
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
         const uint32_t lo = (vx[t2] & 0xffffu) | (vy[t2] << 16);
@@ -1313,7 +1334,7 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
 
 bool attn_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 1) && (d_h == 64 || d_h == 128); }
 bool dense_supported(int dtype, int d_h) { return attn_supported(dtype, d_h); }
-bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype == 2) && (d_h == 64 || d_h == 128); }
+bool decode_supported(int dtype, int d_h) { return (dtype == 0 || dtype >= 2) && (d_h == 64 || d_h == 128); }
 
 hipError_t launch_prefill_schedule(const AttnArgs& a, const PrefillPlan& pl, SchedArgs& s, hipStream_t st,
                                    bool skip_diag) {
@@ -1400,6 +1421,8 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   kp.q = a.q;
   kp.k = a.k;
   kp.v = a.v;
+  kp.k_scale = a.k_scale;
+  kp.v_scale = a.v_scale;
   kp.page_table = a.page_table;
   kp.cell_off = s.cell_off;
   kp.item_off = s.item_off;
@@ -1424,6 +1447,8 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   km.q = a.q;
   km.k = a.k;
   km.v = a.v;
+  km.k_scale = a.k_scale;
+  km.v_scale = a.v_scale;
   km.page_table = a.page_table;
   km.block_idx = a.block_idx;
   km.part_o = kp.part_o;
@@ -1468,6 +1493,8 @@ hipError_t launch_sparse_prefill(int dtype, int d_h, const AttnArgs& a, const Pr
                                  hipStream_t st) {
   if (dtype == 2 && d_h == 128) return sparse_prefill_typed<bf16_t, 128, fp8_t>(a, pl, st);
   if (dtype == 2 && d_h == 64) return sparse_prefill_typed<bf16_t, 64, fp8_t>(a, pl, st);
+  if (dtype == 3 && d_h == 128) return sparse_prefill_typed<bf16_t, 128, mx8_t>(a, pl, st);
+  if (dtype == 3 && d_h == 64) return sparse_prefill_typed<bf16_t, 64, mx8_t>(a, pl, st);
   if (dtype == 0 && d_h == 128) return sparse_prefill_typed<bf16_t, 128>(a, pl, st);
   if (dtype == 0 && d_h == 64) return sparse_prefill_typed<bf16_t, 64>(a, pl, st);
   if (dtype == 1 && d_h == 128) return sparse_prefill_typed<float, 128>(a, pl, st);
@@ -1536,6 +1563,8 @@ static hipError_t decode_typed(const AttnArgs& a, const DecodePlan& pl, hipStrea
   k.q = a.q;
   k.k = a.k;
   k.v = a.v;
+  k.k_scale = a.k_scale;
+  k.v_scale = a.v_scale;
   k.page_table = a.page_table;
   k.seq_lens = a.seq_lens;
   k.block_idx = a.block_idx;
@@ -1575,6 +1604,9 @@ hipError_t launch_sparse_decode(int dtype, int d_h, const AttnArgs& a, const Dec
   } else if (dtype == 2) {  // bf16 queries, e4m3 cached keys and values
     if (d_h == 128) return decode_typed<128, fp8_t>(a, pl, st);
     if (d_h == 64) return decode_typed<64, fp8_t>(a, pl, st);
+  } else if (dtype == 3) {  // bf16 queries, MXFP8 cached keys and values
+    if (d_h == 128) return decode_typed<128, mx8_t>(a, pl, st);
+    if (d_h == 64) return decode_typed<64, mx8_t>(a, pl, st);
   }
   return hipErrorInvalidValue;
 }

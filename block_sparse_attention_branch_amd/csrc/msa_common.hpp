@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace msa {
 
@@ -97,12 +98,42 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
                 static_cast<bf16_t>(d[0]), static_cast<bf16_t>(d[1])};
 }
 
+// MXFP8 caches (the OCP microscaling format): E4M3 codes as above, plus one
+// E8M0 scale byte per 32 consecutive elements of a row, value 2^(s - 127)
+// (0xFF is NaN).  An E4M3 value times a power of two has at most 4
+// significant bits, so the scaled value is still exact in bf16 whenever it
+// lies in bf16's range.  mx8_t tags these caches; its codes are laid out and
+// loaded exactly like fp8_t's, and every scale array has the layout of its
+// cache with the last dimension divided by 32.
+struct mx8_t {
+  uint8_t code;
+};
+template <typename TC>
+inline constexpr bool kIsMx = std::is_same<TC, mx8_t>::value;
+constexpr int kMxBlock = 32;
+
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  return s == 0xFFu ? __builtin_nanf("") : (s == 0u ? 0x1p-127f : __builtin_bit_cast(float, s << 23));
+}
+
+// Eight e4m3 codes times one scale, to bf16 (exact, see above).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w, float sc) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], true);
+  return bf16x8{static_cast<bf16_t>(a[0] * sc), static_cast<bf16_t>(a[1] * sc), static_cast<bf16_t>(b[0] * sc),
+                static_cast<bf16_t>(b[1] * sc), static_cast<bf16_t>(c[0] * sc), static_cast<bf16_t>(c[1] * sc),
+                static_cast<bf16_t>(d[0] * sc), static_cast<bf16_t>(d[1] * sc)};
+}
+
 // A cache fragment as loaded: 8 elements of the cache type, kept raw until
 // the math needs them (so converting never waits on loads in flight).
 template <typename TC> struct RawT;
 template <> struct RawT<bf16_t> { typedef bf16x8 type; };
 template <> struct RawT<float> { typedef f32x8 type; };
 template <> struct RawT<fp8_t> { typedef u32x2 type; };
+template <> struct RawT<mx8_t> { typedef u32x2 type; };
 template <typename TC> using Raw = typename RawT<TC>::type;
 
 template <typename TC>
@@ -116,6 +147,16 @@ __device__ __forceinline__ Frag<T> widen(const Raw<TC>& r) {
     return fp8x8_to_bf16(r);
   } else {
     return r;
+  }
+}
+// Raw fragment and the E8M0 byte of its 32-element block -> compute fragment
+// (the scale is ignored for caches without one).
+template <typename T, typename TC>
+__device__ __forceinline__ Frag<T> widen(const Raw<TC>& r, uint32_t scale_byte) {
+  if constexpr (kIsMx<TC>) {
+    return fp8x8_to_bf16(r, e8m0_scale(scale_byte));
+  } else {
+    return widen<T, TC>(r);
   }
 }
 

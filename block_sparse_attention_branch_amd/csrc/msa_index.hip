@@ -163,8 +163,15 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   // block; only the partial last block of a contiguous cache clamps its rows
   // (those keys lie after every query, so the causal mask drops them).
   // With e4m3 caches each 16-byte (8-element) LDS chunk arrives as 8 bytes
-  // and is widened to bf16 when stored.
-  typedef typename std::conditional<sizeof(TC) == 1 && sizeof(T) == 2, u32x2, u32x4>::type Chunk;
+  // and is widened to bf16 when stored; with MXFP8 caches the chunk's scale
+  // byte (its 8 elements lie in one 32-element block) comes with it.
+  struct MxChunk {
+    u32x2 w;
+    uint32_t s;
+  };
+  typedef typename std::conditional<
+      kIsMx<TC>, MxChunk, typename std::conditional<sizeof(TC) == 1 && sizeof(T) == 2, u32x2, u32x4>::type>::type
+      Chunk;
   constexpr int G_ROW = DIDX * (int)sizeof(TC);                   // cache bytes per key row
   constexpr int G_CHUNK = 16 * (int)sizeof(TC) / (int)sizeof(T);  // cache bytes per LDS chunk
   // thread tid copies, for i < LOADS, the chunk at row srow = tid / CHUNKS_PER_ROW
@@ -174,18 +181,27 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   const uint32_t srow = tid / CHUNKS_PER_ROW;
   const uint32_t col_off = (tid % CHUNKS_PER_ROW) * G_CHUNK;
   Chunk pre0[LOADS], pre1[LOADS];
+  // MXFP8: this thread's chunks all sit in scale column (tid % CHUNKS_PER_ROW) / 4
+  const uint32_t scol = (tid % CHUNKS_PER_ROW) * 8 / kMxBlock;
+  auto load_chunk = [&](Chunk& dst, const char* base, const uint8_t* sbase, uint32_t row) {
+    if constexpr (kIsMx<TC>) {
+      dst.w = *reinterpret_cast<const u32x2*>(base + row * G_ROW);
+      dst.s = sbase[row * (DIDX / kMxBlock) + scol];
+    } else {
+      dst = *reinterpret_cast<const Chunk*>(base + row * G_ROW);
+    }
+  };
   auto load_block = [&](Chunk (&dst)[LOADS], int b) {
     const int64_t base_tok = a.page_table ? (int64_t)scalar_load(a.page_table, b) * kBlock : (int64_t)b * kBlock;
     const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX) + col_off;
+    const uint8_t* sbase = kIsMx<TC> ? a.k_idx_scale + base_tok * (DIDX / kMxBlock) : nullptr;
     if (a.page_table || (int64_t)b * kBlock + kBlock <= a.n_kv) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        dst[i] = *reinterpret_cast<const Chunk*>(base + (srow + i * ROWS_PER_PASS) * G_ROW);
+      for (int i = 0; i < LOADS; ++i) load_chunk(dst[i], base, sbase, srow + i * ROWS_PER_PASS);
     } else {
       const uint32_t last = (uint32_t)(a.n_kv - 1 - b * kBlock);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        dst[i] = *reinterpret_cast<const Chunk*>(base + min(srow + (uint32_t)(i * ROWS_PER_PASS), last) * G_ROW);
+      for (int i = 0; i < LOADS; ++i) load_chunk(dst[i], base, sbase, min(srow + (uint32_t)(i * ROWS_PER_PASS), last));
     }
   };
   auto store_block = [&](const Chunk (&src)[LOADS], int buf) {
@@ -194,7 +210,9 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
       const int u = tid + kKiThreads * i;
       const int j = u / CHUNKS_PER_ROW, c = u % CHUNKS_PER_ROW;
       u32x4 w;
-      if constexpr (sizeof(Chunk) == 8) {
+      if constexpr (kIsMx<TC>) {
+        w = __builtin_bit_cast(u32x4, fp8x8_to_bf16(src[i].w, e8m0_scale(src[i].s)));
+      } else if constexpr (sizeof(Chunk) == 8) {
         w = __builtin_bit_cast(u32x4, fp8x8_to_bf16(src[i]));
       } else {
         w = src[i];
@@ -355,9 +373,21 @@ __device__ __forceinline__ int ki_dim(int q4, int ks) {
   return sizeof(TC) == 1 ? q4 * (DIDX / 4) + 8 * ks : ks * 32 + 8 * q4;
 }
 
+// MXFP8 caches: sc[kt] receives the scale byte of key kt*16 + l16 for this
+// lane's dims (q4*(DIDX/4) .. +DIDX/4, inside one 32-element block); `sp` is
+// the page's scale rows.
 template <typename TC, int DIDX>
-__device__ __forceinline__ void ki_load_page(Raw<TC> (&f)[8][DIDX / 32], const TC* kp) {
+__device__ __forceinline__ void ki_load_page(Raw<TC> (&f)[8][DIDX / 32], uint32_t (&sc)[8], const TC* kp,
+                                             const uint8_t* sp) {
   const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
+  if constexpr (kIsMx<TC>) {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+      sc[kt] = sp[(kt * 16 + l16) * (DIDX / kMxBlock) + (q4 * (DIDX / 4)) / kMxBlock];
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) sc[kt] = 0u;
+  }
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
     if constexpr (sizeof(TC) == 1 && DIDX >= 64) {
@@ -407,14 +437,18 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   // the current page is scored (wider rows would not fit two pages).
   constexpr bool kPipe = sizeof(TC) * DIDX <= 128;
   Raw<TC> cur[8][KS], nxt[8][KS];
+  uint32_t csc[8], nsc[8];  // MXFP8 scale bytes of the two pages
+  auto load = [&](Raw<TC>(&f)[8][KS], uint32_t(&sc)[8], int page) {
+    const size_t tok = (size_t)page * kBlock;
+    ki_load_page<TC, DIDX>(f, sc, k_idx + tok * DIDX,
+                           kIsMx<TC> ? a.k_idx_scale + tok * (DIDX / kMxBlock) : nullptr);
+  };
   int pg = pg_begin + wave;
   int j = 0;
-  if (kPipe && pg < pg_end)
-    ki_load_page<TC, DIDX>(cur, k_idx + (size_t)__builtin_amdgcn_readlane(pid, 0) * kBlock * DIDX);
+  if (kPipe && pg < pg_end) load(cur, csc, __builtin_amdgcn_readlane(pid, 0));
   for (; pg < pg_end; pg += 4, ++j) {
-    if (!kPipe) ki_load_page<TC, DIDX>(cur, k_idx + (size_t)__builtin_amdgcn_readlane(pid, j) * kBlock * DIDX);
-    if (kPipe && pg + 4 < pg_end)
-      ki_load_page<TC, DIDX>(nxt, k_idx + (size_t)__builtin_amdgcn_readlane(pid, j + 1) * kBlock * DIDX);
+    if (!kPipe) load(cur, csc, __builtin_amdgcn_readlane(pid, j));
+    if (kPipe && pg + 4 < pg_end) load(nxt, nsc, __builtin_amdgcn_readlane(pid, j + 1));
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
     // keys on the MFMA rows, groups on the columns: acc[v] of lane (q4, l16)
     // is key kt*16 + 4*q4 + v against group l16, so the pool over the page's
@@ -425,7 +459,7 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16(acc, widen<T, TC>(cur[kt][ks]), qa[ks]);
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, widen<T, TC>(cur[kt][ks], csc[kt]), qa[ks]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const bool vis = !masked || (pg * kBlock + kt * 16 + 4 * q4 + v <= p);
@@ -450,9 +484,11 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
           POOL == 0 ? m * a.idx_scale : m * a.idx_scale * inv_cnt;
     if (kPipe) {
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt)
+      for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) cur[kt][ks] = nxt[kt][ks];
+        csc[kt] = nsc[kt];
+      }
     }
   }
 }
@@ -672,6 +708,12 @@ hipError_t launch_ki_prefill(int dtype, int d_idx, const KiPrefillArgs& a, hipSt
     if (d_idx == 128) return ki_prefill_typed<bf16_t, 128, fp8_t>(a, st);
     return hipErrorInvalidValue;
   }
+  if (dtype == 3) {  // bf16 queries, MXFP8 cached index keys
+    if (d_idx == 32) return ki_prefill_typed<bf16_t, 32, mx8_t>(a, st);
+    if (d_idx == 64) return ki_prefill_typed<bf16_t, 64, mx8_t>(a, st);
+    if (d_idx == 128) return ki_prefill_typed<bf16_t, 128, mx8_t>(a, st);
+    return hipErrorInvalidValue;
+  }
   MSA_KI_DISPATCH(ki_prefill_typed, a, st);
 }
 hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStream_t st) {
@@ -679,6 +721,12 @@ hipError_t launch_ki_decode(int dtype, int d_idx, const KiDecodeArgs& a, hipStre
     if (d_idx == 32) return ki_decode_typed<bf16_t, 32, fp8_t>(a, st);
     if (d_idx == 64) return ki_decode_typed<bf16_t, 64, fp8_t>(a, st);
     if (d_idx == 128) return ki_decode_typed<bf16_t, 128, fp8_t>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (dtype == 3) {  // bf16 queries, MXFP8 cached index keys
+    if (d_idx == 32) return ki_decode_typed<bf16_t, 32, mx8_t>(a, st);
+    if (d_idx == 64) return ki_decode_typed<bf16_t, 64, mx8_t>(a, st);
+    if (d_idx == 128) return ki_decode_typed<bf16_t, 128, mx8_t>(a, st);
     return hipErrorInvalidValue;
   }
   MSA_KI_DISPATCH(ki_decode_typed, a, st);

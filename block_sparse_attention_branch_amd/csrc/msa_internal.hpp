@@ -19,6 +19,7 @@ constexpr int kKiDecodePagesPerWg = 16;
 struct KiPrefillArgs {
   const void* q_idx;        // [n_q, h_kv, d_idx]
   const void* k_idx;        // contiguous [n_kv, d_idx] or pages [*, 128, d_idx]
+  const uint8_t* k_idx_scale;  // MXFP8 caches: [n_kv or pages * 128, d_idx / 32]
   const int32_t* page_table;  // NULL or [max_pages] of the one sequence
   int32_t n_rows;           // n_q * h_kv
   int32_t h_kv;
@@ -43,6 +44,7 @@ struct KiPrefillArgs {
 struct KiDecodeArgs {
   const void* q_idx;        // [batch, h_kv, d_idx]
   const void* k_idx;        // pages [*, 128, d_idx]
+  const uint8_t* k_idx_scale;  // MXFP8 caches: [pages, 128, d_idx / 32]
   const int32_t* page_table;  // [batch, max_pages]
   const int32_t* seq_lens;  // [batch]
   int32_t batch;
@@ -99,6 +101,8 @@ struct AttnArgs {
   const void* q;             // prefill [n_q, h_q, d] / decode [batch, h_q, d]
   const void* k;             // contiguous [n_kv, h_kv, d] or pages [*, h_kv, 128, d]
   const void* v;
+  const uint8_t* k_scale;    // MXFP8 caches: E8M0 scales, the cache layout with d / 32 columns
+  const uint8_t* v_scale;
   const int32_t* page_table; // NULL = contiguous
   const int32_t* seq_lens;   // decode only
   const int32_t* block_idx;  // [rows, h_kv, top_k]

@@ -23,7 +23,9 @@ struct KvLds {
 // Two-phase staging for double buffering: global -> registers (issued before
 // the current block's math) and registers -> LDS (after it).  NT threads.
 // TC is the cache type; with e4m3 caches (T = bf16) each 16-byte bf16 chunk
-// arrives as 8 bytes and is widened when stored to LDS.
+// arrives as 8 bytes and is widened when stored to LDS; with MXFP8 caches the
+// chunk's E8M0 scale byte (its 8 elements lie in one 32-element block) comes
+// with it.
 template <typename T, int D, int NT, typename TC = T>
 struct StageRegs {
   typedef typename std::conditional<sizeof(TC) == 1, u32x2, u32x4>::type Chunk;
@@ -35,34 +37,52 @@ struct StageRegs {
   static_assert(KL >= 1 && VU >= 1, "staging split");
   Chunk k[KL];
   Chunk v[VU][VW];
+  uint32_t ksc[KL];      // MXFP8 only: scale byte of K load i
+  uint32_t vsc[VU][VW];  // MXFP8 only: scale byte of V load (u, w)
   uint32_t zero_mask;  // bit i: K load i past the end; bit 16 + 2u + w: V load (u, w)
 };
 
 
 // Base addresses of block b of KV group r: row j of K is k + j * stride.
+// MXFP8 caches: row j's scale bytes start at ks + j * sstride (one per 32
+// elements; the scale arrays have the cache layouts with d / 32 columns).
 struct BlockPtr {
   const char* k;
   const char* v;
   int stride;  // bytes between consecutive key rows
   int valid;   // rows that exist (a contiguous cache may end inside the block)
+  const uint8_t* ks;
+  const uint8_t* vs;
+  int sstride;  // scale bytes between consecutive key rows
 };
 
 template <typename T, int D>
 __device__ __forceinline__ BlockPtr block_ptr(const void* k, const void* v, const int32_t* pt, int b, int r,
-                                              int h_kv, int n_kv) {
+                                              int h_kv, int n_kv, const uint8_t* k_scale = nullptr,
+                                              const uint8_t* v_scale = nullptr) {
   BlockPtr p;
-  size_t off;
+  size_t row0;  // element offset of row 0, in units of D
+  int rstride;  // rows of D elements between consecutive key rows
   if (pt) {
-    off = (((size_t)scalar_load(pt, b) * h_kv + r) * kBlock) * D * sizeof(T);
-    p.stride = D * (int)sizeof(T);
+    row0 = ((size_t)scalar_load(pt, b) * h_kv + r) * kBlock;
+    rstride = 1;
     p.valid = kBlock;
   } else {
-    off = (((size_t)b * kBlock) * h_kv + r) * D * sizeof(T);
-    p.stride = h_kv * D * (int)sizeof(T);
+    row0 = ((size_t)b * kBlock) * h_kv + r;
+    rstride = h_kv;
     p.valid = min(kBlock, n_kv - b * kBlock);
   }
-  p.k = static_cast<const char*>(k) + off;
-  p.v = static_cast<const char*>(v) + off;
+  p.stride = rstride * D * (int)sizeof(T);
+  p.k = static_cast<const char*>(k) + row0 * D * sizeof(T);
+  p.v = static_cast<const char*>(v) + row0 * D * sizeof(T);
+  if constexpr (kIsMx<T>) {
+    p.sstride = rstride * (D / kMxBlock);
+    p.ks = k_scale + row0 * (D / kMxBlock);
+    p.vs = v_scale + row0 * (D / kMxBlock);
+  } else {
+    p.sstride = 0;
+    p.ks = p.vs = nullptr;
+  }
   return p;
 }
 
@@ -81,6 +101,7 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT, TC>& g, const Blo
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
     g.k[i] = *reinterpret_cast<const C*>(p.k + (size_t)min(j, last) * p.stride + c * S::CB);
+    if constexpr (kIsMx<TC>) g.ksc[i] = p.ks[min(j, last) * p.sstride + (c * 8) / kMxBlock];
     zm |= (j > last ? 1u : 0u) << i;
   }
   if constexpr (sizeof(T) == 2) {
@@ -92,6 +113,10 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT, TC>& g, const Blo
       const int dc = (u >> 4) % DC;
       g.v[i][0] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp, last) * p.stride + dc * S::CB);
       g.v[i][1] = *reinterpret_cast<const C*>(p.v + (size_t)min(2 * kp + 1, last) * p.stride + dc * S::CB);
+      if constexpr (kIsMx<TC>) {
+        g.vsc[i][0] = p.vs[min(2 * kp, last) * p.sstride + (dc * 8) / kMxBlock];
+        g.vsc[i][1] = p.vs[min(2 * kp + 1, last) * p.sstride + (dc * 8) / kMxBlock];
+      }
       zm |= (2 * kp > last ? 1u : 0u) << (16 + 2 * i);
       zm |= (2 * kp + 1 > last ? 1u : 0u) << (17 + 2 * i);
     }
@@ -109,9 +134,11 @@ __device__ __forceinline__ void stage_load(StageRegs<T, D, NT, TC>& g, const Blo
   g.zero_mask = zm;
 }
 
-template <typename T, typename C>
-__device__ __forceinline__ u32x4 stage_widen(const C& c) {
-  if constexpr (sizeof(C) == 8) {
+template <typename T, typename TC, typename C>
+__device__ __forceinline__ u32x4 stage_widen(const C& c, uint32_t scale_byte) {
+  if constexpr (kIsMx<TC>) {
+    return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c, e8m0_scale(scale_byte)));
+  } else if constexpr (sizeof(C) == 8) {
     return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c));
   } else {
     return c;
@@ -127,7 +154,8 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT, TC>& g, ch
   for (int i = 0; i < S::KL; ++i) {
     const int u = threadIdx.x + NT * i;
     const int j = u / S::CPR, c = u % S::CPR;
-    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) = ((g.zero_mask >> i) & 1u) ? z : stage_widen<T>(g.k[i]);
+    *reinterpret_cast<u32x4*>(lds + j * L::KS + c * 16) =
+        ((g.zero_mask >> i) & 1u) ? z : stage_widen<T, TC>(g.k[i], kIsMx<TC> ? g.ksc[i] : 0u);
   }
   char* vt = lds + L::K_BYTES;
   if constexpr (sizeof(T) == 2) {
@@ -137,8 +165,10 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT, TC>& g, ch
       const int u = threadIdx.x + NT * i;
       const int kp = (u & 15) + 16 * (u / (16 * DC));
       const int dc = (u >> 4) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
-      const u32x4 y = ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][1]);
+      const u32x4 x =
+          ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T, TC>(g.v[i][0], kIsMx<TC> ? g.vsc[i][0] : 0u);
+      const u32x4 y =
+          ((g.zero_mask >> (17 + 2 * i)) & 1u) ? z : stage_widen<T, TC>(g.v[i][1], kIsMx<TC> ? g.vsc[i][1] : 0u);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t lo = (x[t] & 0xffffu) | (y[t] << 16);
@@ -154,7 +184,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<T, D, NT, TC>& g, ch
       const int u = threadIdx.x + NT * i;
       const int key = (u & 31) + 32 * (u / (32 * DC));
       const int dc = (u >> 5) % DC;
-      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T>(g.v[i][0]);
+      const u32x4 x = ((g.zero_mask >> (16 + 2 * i)) & 1u) ? z : stage_widen<T, TC>(g.v[i][0], 0u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (4 * dc + e) * L::VS + key * 4) = x[e];
     }

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_BF16, MSA_FP32, MSA_FP8_E4M3 = 0, 1, 2
+MSA_BF16, MSA_FP32, MSA_FP8_E4M3, MSA_MXFP8_E4M3 = 0, 1, 2, 3
 MSA_POOL_MAX, MSA_POOL_MEAN = 0, 1
 OP_INDEX, OP_PREFILL, OP_DECODE, OP_DENSE, OP_INDEX_DECODE, OP_PREFILL_BACKWARD, OP_PREFILL_BACKWARD_KL = \
     0, 1, 2, 3, 4, 5, 6
@@ -48,7 +48,8 @@ class KL(ctypes.Structure):
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_idx", ctypes.c_void_p),
                 ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
-                ("n_kv", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+                ("n_kv", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("k_idx_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -145,10 +146,12 @@ def _pool_code(pool) -> int:
     return int(pool)
 
 
-def _cache_code(t: torch.Tensor, compute_code: int) -> int:
-    """Cache dtype of a k/v/k_idx tensor: e4m3 (float8_e4m3fn) or the call's dtype."""
+def _cache_code(t: torch.Tensor, compute_code: int, scale=None) -> int:
+    """Cache dtype of a k/v/k_idx tensor: MXFP8 (float8_e4m3fn codes with a
+    uint8 E8M0 scale tensor), e4m3 (float8_e4m3fn without one) or the call's
+    dtype."""
     if t is not None and t.dtype == torch.float8_e4m3fn:
-        return MSA_FP8_E4M3
+        return MSA_FP8_E4M3 if scale is None else MSA_MXFP8_E4M3
     return compute_code
 
 
@@ -202,11 +205,13 @@ def profile_read(kernel: str):
 
 def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale=0.0,
                page_table=None, n_kv=None, seq_lens=None, max_pages=None, h_q=None,
-               with_scores=False, out=None, workspace=None, stream=None, pool="max"):
+               with_scores=False, out=None, workspace=None, stream=None, pool="max", k_idx_scale=None):
     """msa_index_topk (``pool``: "max", the method's block max-pool, or "mean").  Prefill mode: q_idx [n_q, h_kv, d_idx], k_idx
     [n_kv, d_idx] (or pages [*, 128, d_idx] with ``page_table``).  Decode mode
     (``seq_lens`` given): q_idx [batch, h_kv, d_idx], one query per sequence.
-    Returns block_idx int32 [rows, h_kv, top_k] (and fp32 scores)."""
+    An MXFP8 k_idx is its float8_e4m3fn codes plus ``k_idx_scale`` (uint8,
+    last dim d_idx / 32).  Returns block_idx int32 [rows, h_kv, top_k] (and
+    fp32 scores)."""
     decode = seq_lens is not None
     if decode:
         batch, h_kv, d_idx = q_idx.shape
@@ -225,7 +230,7 @@ def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale
         mp = int(max_pages)
     dt = _dtype_code(q_idx)
     shape = make_shape(h_q or h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local,
-                       idx_scale=idx_scale, cache_dtype=_cache_code(k_idx, dt), pool=pool)
+                       idx_scale=idx_scale, cache_dtype=_cache_code(k_idx, dt, k_idx_scale), pool=pool)
     dev = q_idx.device
     bidx = out if out is not None else torch.empty((rows, h_kv, top_k), dtype=torch.int32, device=dev)
     scores = torch.empty((rows, h_kv, top_k), dtype=torch.float32, device=dev) if with_scores else None
@@ -234,14 +239,15 @@ def index_topk(q_idx, k_idx, *, top_k=16, q_start=0, force_local=True, idx_scale
     else:
         nws = workspace_size(OP_INDEX, shape, n_q=n_q, q_start=qs, n_kv=nkv)
     ws = _workspace(nws, dev, workspace)
-    kv = KV(None, None, _ptr(k_idx), _ptr(page_table), _ptr(seq_lens), nkv, mp)
+    kv = KV(None, None, _ptr(k_idx), _ptr(page_table), _ptr(seq_lens), nkv, mp, None, None, _ptr(k_idx_scale))
     _check(lib().msa_index_topk(ctypes.byref(shape), batch, n_q, qs, _ptr(q_idx), ctypes.byref(kv),
                                 _ptr(bidx), _ptr(scores), _ptr(ws), nws, _stream(stream)))
     return (bidx, scores) if with_scores else bidx
 
 
 def index_topk_decode_static(q_idx, k_idx_pages, page_table, seq_lens, *, top_k=16, force_local=True,
-                             idx_scale=0.0, with_scores=False, out=None, out_scores=None, stream=None, pool="max"):
+                             idx_scale=0.0, with_scores=False, out=None, out_scores=None, stream=None, pool="max",
+                             k_idx_scale=None):
     """msa_index_topk_decode_static: msa_index_topk in decode mode with the
     library's own scratch instead of a workspace (nothing is allocated but the
     outputs, and those only when ``out`` / ``out_scores`` are not given).
@@ -250,54 +256,61 @@ def index_topk_decode_static(q_idx, k_idx_pages, page_table, seq_lens, *, top_k=
     batch, h_kv, d_idx = q_idx.shape
     dt = _dtype_code(q_idx)
     shape = make_shape(h_kv, h_kv, 128, d_idx, top_k, dt, force_local=force_local, idx_scale=idx_scale,
-                       cache_dtype=_cache_code(k_idx_pages, dt), pool=pool)
+                       cache_dtype=_cache_code(k_idx_pages, dt, k_idx_scale), pool=pool)
     dev = q_idx.device
     bidx = out if out is not None else torch.empty((batch, h_kv, top_k), dtype=torch.int32, device=dev)
     scores = None
     if with_scores:
         scores = out_scores if out_scores is not None else torch.empty((batch, h_kv, top_k), dtype=torch.float32,
                                                                        device=dev)
-    kv = KV(None, None, _ptr(k_idx_pages), _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1])
+    kv = KV(None, None, _ptr(k_idx_pages), _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1], None, None,
+            _ptr(k_idx_scale))
     _check(lib().msa_index_topk_decode_static(ctypes.byref(shape), batch, _ptr(q_idx), ctypes.byref(kv), _ptr(bidx),
                                               _ptr(scores), _stream(stream)))
     return (bidx, scores) if with_scores else bidx
 
 
 def sparse_prefill(q, k, v, block_idx, *, q_start=0, sm_scale=0.0, page_table=None, n_kv=None,
-                   with_lse=False, out=None, workspace=None, stream=None):
+                   with_lse=False, out=None, workspace=None, stream=None, k_scale=None, v_scale=None):
     """msa_sparse_prefill.  q [n_q, h_q, d_h]; k/v [n_kv, h_kv, d_h] (or pages
     [*, h_kv, 128, d_h] with ``page_table`` and ``n_kv``); block_idx int32
-    [n_q, h_kv, top_k].  Returns o [n_q, h_q, d_h] (and lse fp32 [n_q, h_q])."""
+    [n_q, h_kv, top_k].  MXFP8 k/v: float8_e4m3fn codes plus ``k_scale`` /
+    ``v_scale`` (uint8, last dim d_h / 32).  Returns o [n_q, h_q, d_h] (and
+    lse fp32 [n_q, h_q])."""
     n_q, h_q, d_h = q.shape
     h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
     nkv = int(n_kv) if n_kv is not None else k.shape[0]
     mp = page_table.numel() if page_table is not None else 0
     dt = _dtype_code(q)
-    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale, cache_dtype=_cache_code(k, dt))
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale, cache_dtype=_cache_code(k, dt, k_scale))
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((n_q, h_q), dtype=torch.float32, device=q.device) if with_lse else None
     nws = workspace_size(OP_PREFILL, shape, n_q=n_q, q_start=int(q_start), n_kv=nkv)
     ws = _workspace(nws, q.device, workspace)
-    kv = KV(_ptr(k), _ptr(v), None, _ptr(page_table), None, nkv, mp)
+    kv = KV(_ptr(k), _ptr(v), None, _ptr(page_table), None, nkv, mp, _ptr(k_scale), _ptr(v_scale), None)
     _check(lib().msa_sparse_prefill(ctypes.byref(shape), n_q, int(q_start), _ptr(q), ctypes.byref(kv),
                                     _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(stream)))
     return (o, lse) if with_lse else o
 
 
 def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, block_idx, *, sm_scale=0.0,
-                  with_lse=False, out=None, workspace=None, stream=None):
+                  with_lse=False, out=None, workspace=None, stream=None, k_scale=None, v_scale=None):
     """msa_sparse_decode.  q [batch, h_q, d_h]; pages [*, h_kv, 128, d_h];
     page_table int32 [batch, max_pages]; seq_lens int32 [batch]; block_idx
-    int32 [batch, h_kv, top_k].  Returns o [batch, h_q, d_h] (and lse)."""
+    int32 [batch, h_kv, top_k].  MXFP8 pages: float8_e4m3fn codes plus
+    ``k_scale`` / ``v_scale`` [*, h_kv, 128, d_h / 32] uint8.  Returns o
+    [batch, h_q, d_h] (and lse)."""
     batch, h_q, d_h = q.shape
     h_kv, top_k = block_idx.shape[1], block_idx.shape[2]
     dt = _dtype_code(q)
-    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale, cache_dtype=_cache_code(k_pages, dt))
+    shape = make_shape(h_q, h_kv, d_h, 64, top_k, dt, sm_scale=sm_scale,
+                       cache_dtype=_cache_code(k_pages, dt, k_scale))
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((batch, h_q), dtype=torch.float32, device=q.device) if with_lse else None
     nws = workspace_size(OP_DECODE, shape, batch=batch, n_q=1)
     ws = _workspace(nws, q.device, workspace)
-    kv = KV(_ptr(k_pages), _ptr(v_pages), None, _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1])
+    kv = KV(_ptr(k_pages), _ptr(v_pages), None, _ptr(page_table), _ptr(seq_lens), 0, page_table.shape[1],
+            _ptr(k_scale), _ptr(v_scale), None)
     _check(lib().msa_sparse_decode(ctypes.byref(shape), batch, _ptr(q), ctypes.byref(kv), _ptr(block_idx),
                                    _ptr(o), _ptr(lse), _ptr(ws), nws, _stream(stream)))
     return (o, lse) if with_lse else o

@@ -26,7 +26,8 @@
  *   - Calls are asynchronous and stream ordered on `hip_stream` (a
  *     hipStream_t; NULL = the null stream).  They never synchronise the host.
  *   - Every float tensor of a call has the dtype `shape->dtype` (bf16 or
- *     fp32), except the caches when `shape->cache_dtype` is MSA_FP8_E4M3;
+ *     fp32), except the caches when `shape->cache_dtype` is MSA_FP8_E4M3 or
+ *     MSA_MXFP8_E4M3;
  *     outputs use `shape->dtype`; `lse`, `block_score` and KL values are fp32.
  *   - Arguments are validated on the host before anything is launched.  On
  *     an error the call returns a non-zero msa_status, launches nothing and
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 5
+#define MSA_ABI_VERSION 6
 #define MSA_BLOCK_SIZE 128
 #define MSA_MAX_TOP_K 16
 
@@ -68,8 +69,15 @@ typedef enum msa_status {
 } msa_status;
 
 /* MSA_FP8_E4M3: OCP 8-bit float e4m3 ("fn": bias 7, no infinities), one
- * byte per element, used as stored (no scale).  Only for the caches. */
-typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2 } msa_dtype;
+ * byte per element, used as stored (no scale).  Only for the caches.
+ * MSA_MXFP8_E4M3: the OCP microscaling format MXFP8 with e4m3 elements, the
+ * 8-bit KV-cache format named on the zhichai.net key points page
+ * (Limitations): the same one-byte e4m3 codes, plus one E8M0 scale byte per
+ * 32 consecutive elements of a row (value 2^(s - 127); 0xFF is NaN).  An
+ * element's value is its e4m3 value times its block's scale.  The scale
+ * arrays are separate tensors (msa_kv k_scale, v_scale, k_idx_scale).  Only
+ * for the caches. */
+typedef enum msa_dtype { MSA_BF16 = 0, MSA_FP32 = 1, MSA_FP8_E4M3 = 2, MSA_MXFP8_E4M3 = 3 } msa_dtype;
 
 /* Block scoring of the index branch.  MSA_POOL_MAX is the method's max-pool
  * ([P1] §4.2 Eq. (6)); MSA_POOL_MEAN averages the visible token scores of a
@@ -92,8 +100,12 @@ typedef enum msa_pool { MSA_POOL_MAX = 0, MSA_POOL_MEAN = 1 } msa_pool;
  *   dtype        msa_dtype (BF16 or FP32) of every float tensor of the call.
  *   cache_dtype  MSA_FP8_E4M3: the caches k, v and k_idx hold e4m3 codes
  *                (with dtype MSA_BF16; every call except
- *                msa_dense_prefill); they are widened exactly to bf16
- *                before use.  Any other value: the caches have type `dtype`.
+ *                msa_dense_prefill, msa_sparse_prefill_backward and
+ *                msa_index_project); they are widened exactly to bf16
+ *                before use.  MSA_MXFP8_E4M3: the same codes times their
+ *                block scales (msa_kv), for the same calls; the scaled
+ *                values are exact in bf16 whenever they lie in bf16's
+ *                range.  Any other value: the caches have type `dtype`.
  *   pool         msa_pool: block scoring of msa_index_topk (other calls
  *                ignore it). */
 typedef struct msa_shape {
@@ -109,7 +121,15 @@ typedef struct msa_shape {
  *   page_table != NULL: paged cache; max_pages = columns of page_table.
  *     seq_lens == NULL: one sequence (batch must be 1) of n_kv tokens.
  *     seq_lens != NULL: device int32 [batch], tokens held per sequence,
- *                       each in [1, 128*max_pages] (decode calls).       */
+ *                       each in [1, 128*max_pages] (decode calls).
+ *   k_scale, v_scale, k_idx_scale: with cache_dtype MSA_MXFP8_E4M3, device
+ *     uint8 E8M0 scales of k, v and k_idx, each laid out like its cache with
+ *     the last dimension divided by 32 (contiguous: [n_kv, h_kv, d_h/32] and
+ *     [n_kv, d_idx/32]; paged: [num_pages, h_kv, 128, d_h/32] and
+ *     [num_pages, 128, d_idx/32]); scale s of row j covers elements
+ *     32 s .. 32 s + 31 of that row.  The index call needs k_idx_scale, the
+ *     attention calls k_scale and v_scale; NULL otherwise (ignored for
+ *     other cache dtypes).                                              */
 typedef struct msa_kv {
   const void* k;
   const void* v;
@@ -118,6 +138,9 @@ typedef struct msa_kv {
   const int32_t* seq_lens;
   int32_t n_kv;
   int32_t max_pages;
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
+  const uint8_t* k_idx_scale;
 } msa_kv;
 
 /* Index branch: [P1] §4.2 Eq. (6) and §4.4.1; shapes from [P5] Step 1.

@@ -57,7 +57,12 @@ def compare_index_rows(gpu_ids, ora_ids, pooled, diags, force_local=True):
     return n_exact, n_excused
 
 
-def compare_out(o_gpu, o_ref, dtype, what="o"):
+def compare_out(o_gpu, o_ref, dtype, what="o", rel_elem=0.0):
+    """Outputs within the tolerance.  ``rel_elem`` adds rel_elem * |o_ref| to
+    the max-abs bound of each element: for inputs whose outputs reach well
+    above 1 (the MXFP8 tests' block scales reach 2^4), a bf16 output carries a
+    rounding error of up to 2^-9 of its own magnitude, which a fixed absolute
+    bound does not cover."""
     tol = TOL[dtype]
     og = np64(o_gpu) if isinstance(o_gpu, torch.Tensor) else np.asarray(o_gpu, np.float64)
     orf = np.asarray(o_ref, np.float64)
@@ -66,6 +71,9 @@ def compare_out(o_gpu, o_ref, dtype, what="o"):
     err = np.abs(og - orf)
     max_abs = float(err.max()) if err.size else 0.0
     rel = float(np.linalg.norm(og - orf) / max(np.linalg.norm(orf), 1e-30))
+    if rel_elem > 0.0:
+        excess = err - rel_elem * np.abs(orf)
+        max_abs = float(excess.max()) if excess.size else 0.0
     assert max_abs <= tol["max_abs"], f"{what}: max-abs {max_abs:.3e} > {tol['max_abs']}"
     assert rel <= tol["rel_l2"], f"{what}: relative L2 {rel:.3e} > {tol['rel_l2']}"
     return max_abs, rel

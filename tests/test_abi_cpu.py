@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     L = msa.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.msa_abi_version() == 5
+    assert L.msa_abi_version() == 6
     for st in range(5):
         assert L.msa_status_string(st).decode().startswith("MSA_")
 
@@ -145,6 +145,42 @@ def test_e4m3_cache_validation():
     assert msa.workspace_size(msa.OP_PREFILL, f8, n_q=8, n_kv=256) > 0
     assert msa.lib().msa_workspace_size(msa.OP_DENSE, ctypes.byref(f8), 1, 8, 0, 8, 0) == 0
     assert "dense" in _err()
+
+
+def test_mxfp8_cache_validation():
+    """MXFP8 caches: the calls that take 8-bit caches accept them when the scale
+    arrays they read are given, and refuse them without (or elsewhere)."""
+    L = msa.lib()
+    mx = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_BF16, cache_dtype=msa.MSA_MXFP8_E4M3)
+    mx32 = msa.make_shape(64, 4, 128, 64, 16, msa.MSA_FP32, cache_dtype=msa.MSA_MXFP8_E4M3)
+    no_sc = msa.KV(FAKE, FAKE, FAKE, None, None, 256, 0)
+    only_idx = msa.KV(FAKE, FAKE, FAKE, None, None, 256, 0, None, None, FAKE)
+    full = msa.KV(FAKE, FAKE, FAKE, None, None, 256, 0, FAKE, FAKE, FAKE)
+    pre = lambda shp, kv: L.msa_sparse_prefill(ctypes.byref(shp), 8, 0, FAKE, ctypes.byref(kv), FAKE, FAKE, None,
+                                               None, 0, None)
+    assert pre(mx, no_sc) == 1 and "k_scale" in _err()
+    assert pre(mx, only_idx) == 1 and "k_scale" in _err()
+    assert pre(mx, full) == 3 and "workspace" in _err()  # accepted up to the workspace check
+    assert pre(mx32, full) == 2 and "MSA_BF16" in _err()
+    idx = lambda shp, kv: L.msa_index_topk(ctypes.byref(shp), 1, 20000, 0, FAKE, ctypes.byref(kv), FAKE, None, None,
+                                           0, None)
+    kv_i = msa.KV(None, None, FAKE, None, None, 20000, 0)
+    assert idx(mx, kv_i) == 1 and "k_idx_scale" in _err()
+    kv_i = msa.KV(None, None, FAKE, None, None, 20000, 0, None, None, FAKE)
+    assert idx(mx, kv_i) == 3
+    dec = lambda kv: L.msa_sparse_decode(ctypes.byref(mx), 2, FAKE, ctypes.byref(kv), FAKE, FAKE, None, None, 0, None)
+    assert dec(msa.KV(FAKE, FAKE, None, FAKE, FAKE, 0, 8)) == 1 and "k_scale" in _err()
+    assert dec(msa.KV(FAKE, FAKE, None, FAKE, FAKE, 0, 8, FAKE, FAKE, None)) == 3
+    st = lambda kv: L.msa_index_topk_decode_static(ctypes.byref(mx), 2, FAKE, ctypes.byref(kv), FAKE, None, None)
+    assert st(msa.KV(None, None, FAKE, FAKE, FAKE, 0, 8)) == 1 and "k_idx_scale" in _err()
+    # not built for MXFP8: the dense comparison and the backward
+    assert L.msa_dense_prefill(ctypes.byref(mx), 8, 0, FAKE, ctypes.byref(full), FAKE, None, None, 0, None) == 2
+    assert msa.lib().msa_workspace_size(msa.OP_DENSE, ctypes.byref(mx), 1, 8, 0, 8, 0) == 0
+    # the binding picks MXFP8 when a scale tensor comes with e4m3 codes
+    import torch
+    t = torch.empty(4, dtype=torch.float8_e4m3fn)
+    assert msa._cache_code(t, msa.MSA_BF16) == msa.MSA_FP8_E4M3
+    assert msa._cache_code(t, msa.MSA_BF16, torch.empty(1, dtype=torch.uint8)) == msa.MSA_MXFP8_E4M3
 
 
 def test_pool_mode_validation():
@@ -350,4 +386,4 @@ def test_header_is_plain_c_and_links(tmp_path):
                     str(src), "-o", str(exe), "-L", libdir, "-l:libmsa.so", f"-Wl,-rpath,{libdir}"], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
-    assert r.stdout.strip() == "ok 5"
+    assert r.stdout.strip() == "ok 6"

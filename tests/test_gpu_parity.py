@@ -11,7 +11,7 @@ import torch
 
 from oracle import msa_oracle as orc
 from synth import MODEL_SHAPE, TINY_SHAPE, gen_decode_paged, gen_long_context, gen_prefill
-from synth.inputs import HeadShape
+from synth.inputs import MXFP8, HeadShape
 
 from _helpers import compare_grad, compare_index_rows, compare_lse, compare_out, np64
 
@@ -285,6 +285,58 @@ def test_prefill_e4m3_caches_contiguous_and_paged():
     _e4m3_prefill_case(HeadShape(16, 4, 128, 128, 16), 1300, 1300, 31, paged=True)
 
 
+def _mx_prefill_case(shape, n_kv, n_q, seed, paged):
+    msa = _msa()
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=seed, device=DEV, cache_dtype=MXFP8)
+    q_start = inp["q_start"]
+    _say("MXFP8 prefill", shape, n_kv, n_q, seed, "paged" if paged else "contiguous")
+    names = ("k", "v", "k_idx", "k_scale", "v_scale", "k_idx_scale")
+    t = {n: inp[n] for n in names}
+    kw = {}
+    if paged:
+        # the same tokens (and their scale rows) in head-major 128-token pages
+        # placed by a random permutation
+        nb = -(-n_kv // 128)
+        pad = nb * 128 - n_kv
+        perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+        def pages(x):
+            u8 = x.view(torch.uint8)
+            u8 = torch.cat([u8, torch.zeros((pad,) + u8.shape[1:], dtype=torch.uint8, device=DEV)])
+            u8 = u8.view((nb, 128) + u8.shape[1:])
+            if u8.dim() == 4:
+                u8 = u8.permute(0, 2, 1, 3)
+            out = torch.empty_like(u8.contiguous())
+            out[perm.long().to(DEV)] = u8.contiguous()
+            return out.view(x.dtype)
+        t = {n: pages(x) for n, x in t.items()}
+        kw = dict(page_table=perm.to(DEV), n_kv=n_kv)
+    bidx = msa.index_topk(inp["q_idx"], t["k_idx"], top_k=shape.top_k, q_start=q_start, k_idx_scale=t["k_idx_scale"],
+                          **kw)
+    o, lse = msa.sparse_prefill(inp["q"], t["k"], t["v"], bidx, q_start=q_start, with_lse=True, k_scale=t["k_scale"],
+                                v_scale=t["v_scale"], **kw)
+    torch.cuda.synchronize()
+    k64 = _cache_host(inp["k"], inp["k_scale"])
+    v64 = _cache_host(inp["v"], inp["v_scale"])
+    ki64 = _cache_host(inp["k_idx"], inp["k_idx_scale"])
+    o_ids, _, pooled = orc.index_topk(np64(inp["q_idx"]), ki64, q_start, shape.top_k)
+    compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, (q_start + np.arange(n_q)) // 128)
+    o_ref, lse_ref = orc.sparse_attention(np64(inp["q"]), k64, v64, bidx.cpu().numpy(), q_start)
+    compare_out(o, o_ref, torch.bfloat16, rel_elem=MX_REL)
+    compare_lse(lse, lse_ref, torch.bfloat16)
+
+
+# MXFP8 test data reach |v| ~ 7 (block scales up to 2^4), so the bf16 output
+# rounding (2^-9 relative) exceeds the fixed 1e-2 bound near the largest
+# outputs: those tests add 2^-7 of each reference value to it (4x the rounding).
+MX_REL = 2.0 ** -7
+
+
+def test_prefill_mxfp8_caches_contiguous_and_paged():
+    _mx_prefill_case(MODEL_SHAPE, 2300, 2300, 129, paged=False)
+    _mx_prefill_case(HeadShape(16, 2, 64, 32, 6), 1700, 900, 130, paged=True)
+    _mx_prefill_case(HeadShape(16, 4, 128, 128, 16), 1300, 1300, 131, paged=True)
+
+
 def test_prefill_full_coverage_equals_dense():
     msa = _msa()
     shape = HeadShape(16, 2, 128, 64, 16)
@@ -542,9 +594,12 @@ def test_prefill_and_decode_irregular_block_lists():
 
 # ------------------------------------------------------------------ decode
 
-def _cache_host(t):
-    """Host float64 copy of a cache tensor; e4m3 codes go through the oracle's decoder."""
+def _cache_host(t, scale=None):
+    """Host float64 copy of a cache tensor; e4m3 codes (with their E8M0 block
+    scales for MXFP8) go through the oracle's decoders."""
     if t.dtype == torch.float8_e4m3fn:
+        if scale is not None:
+            return orc.decode_mxfp8(t.view(torch.uint8).cpu().numpy(), scale.cpu().numpy())
         return orc.decode_e4m3(t.view(torch.uint8).cpu().numpy())
     return t.cpu().double().numpy()
 
@@ -557,20 +612,26 @@ def _decode_case(shape, seq_lens, seed, n_sets=1, cache_dtype=None):
     _say("decode", shape, seq_lens, seed, cache_dtype)
     q_idx = inp["q_idx"][0].contiguous()
     q = inp["q"][0].contiguous()
+    ks, vs, kis = inp.get("k_pages_scale"), inp.get("v_pages_scale"), inp.get("k_idx_pages_scale")
     bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=shape.top_k, page_table=inp["page_table"],
-                          seq_lens=inp["seq_lens"])
+                          seq_lens=inp["seq_lens"], k_idx_scale=kis)
     o, lse = msa.sparse_decode(q, inp["k_pages"], inp["v_pages"], inp["page_table"], inp["seq_lens"], bidx,
-                               with_lse=True)
+                               with_lse=True, k_scale=ks, v_scale=vs)
+    if kis is not None:
+        # the allocation-free entry point reads the same scales
+        b2 = msa.index_topk_decode_static(q_idx, inp["k_idx_pages"], inp["page_table"], inp["seq_lens"],
+                                          top_k=shape.top_k, k_idx_scale=kis)
+        assert torch.equal(b2, bidx)
     torch.cuda.synchronize()
     pt = inp["page_table"].cpu().numpy()
-    kp = _cache_host(inp["k_pages"])
-    vp = _cache_host(inp["v_pages"])
-    ip = _cache_host(inp["k_idx_pages"])
+    kp = _cache_host(inp["k_pages"], ks)
+    vp = _cache_host(inp["v_pages"], vs)
+    ip = _cache_host(inp["k_idx_pages"], kis)
     o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), ip, pt, seq_lens, shape.top_k)
     diags = (np.asarray(seq_lens) - 1) // 128
     compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, diags)
     o_ref, lse_ref = orc.sparse_decode(np64(q), kp, vp, pt, seq_lens, bidx.cpu().numpy())
-    compare_out(o, o_ref, torch.bfloat16)
+    compare_out(o, o_ref, torch.bfloat16, rel_elem=MX_REL if ks is not None else 0.0)
     compare_lse(lse, lse_ref, torch.bfloat16)
 
 
@@ -669,6 +730,16 @@ def test_decode_e4m3_caches():
     _decode_case(HeadShape(16, 4, 128, 128, 8), [1500, 9000], 27, cache_dtype=f8)
 
 
+def test_decode_mxfp8_caches():
+    # MXFP8 K, V and K_idx pages (E4M3 codes, one E8M0 scale per 32 elements,
+    # neighbouring blocks scaled differently), bf16 queries
+    _decode_case(MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049], 125, cache_dtype=MXFP8)
+    _decode_case(HeadShape(16, 2, 64, 32, 16), [5000, 2500, 700], 126, cache_dtype=MXFP8)
+    _decode_case(HeadShape(16, 4, 128, 128, 8), [1500, 9000], 127, cache_dtype=MXFP8)
+    # 64 sequences: no key split in the gather (8-wave workgroups)
+    _decode_case(HeadShape(16, 4, 64, 64, 16), [600 + 37 * i for i in range(64)], 128, cache_dtype=MXFP8)
+
+
 def test_decode_single_long_sequence():
     _decode_case(MODEL_SHAPE, [40000], 22)
 
@@ -750,6 +821,35 @@ def test_full_size_decode_64x128k_e4m3_sampled_sequences():
         compare_index_rows(g_ids[s:s + 1], o_ids, pooled, [(L - 1) // 128])
         o_ref, lse_ref = orc.sparse_decode(np64(q[s:s + 1]), kp, vp, local_pt, [L], g_ids[s:s + 1])
         compare_out(o[s:s + 1], o_ref, torch.bfloat16)
+        compare_lse(lse[s:s + 1], lse_ref, torch.bfloat16)
+
+
+def test_full_size_decode_64x128k_mxfp8_sampled_sequences():
+    """The 64 x 131072 decode step with MXFP8 caches; 2 sequences checked."""
+    msa = _msa()
+    shape = MODEL_SHAPE
+    inp = gen_decode_paged(64, 131072, shape, seed=3, device=DEV, cache_dtype=MXFP8)
+    _say("decode 64 x 128K MXFP8 full size")
+    q_idx = inp["q_idx"][0].contiguous()
+    q = inp["q"][0].contiguous()
+    ks, vs, kis = inp["k_pages_scale"], inp["v_pages_scale"], inp["k_idx_pages_scale"]
+    bidx = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=16, page_table=inp["page_table"],
+                          seq_lens=inp["seq_lens"], k_idx_scale=kis)
+    o, lse = msa.sparse_decode(q, inp["k_pages"], inp["v_pages"], inp["page_table"], inp["seq_lens"], bidx,
+                               with_lse=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    g_ids = bidx.cpu().numpy()
+    L = 131072
+    local_pt = np.arange(L // 128)[None, :]
+    for s in (7, 44):
+        pages = inp["page_table"][s].long()
+        kp = _cache_host(inp["k_pages"][pages], ks[pages])
+        vp = _cache_host(inp["v_pages"][pages], vs[pages])
+        ip = _cache_host(inp["k_idx_pages"][pages], kis[pages])
+        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx[s:s + 1]), ip, local_pt, [L], 16)
+        compare_index_rows(g_ids[s:s + 1], o_ids, pooled, [(L - 1) // 128])
+        o_ref, lse_ref = orc.sparse_decode(np64(q[s:s + 1]), kp, vp, local_pt, [L], g_ids[s:s + 1])
+        compare_out(o[s:s + 1], o_ref, torch.bfloat16, rel_elem=MX_REL)
         compare_lse(lse[s:s + 1], lse_ref, torch.bfloat16)
 
 
