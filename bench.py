@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from synth import MODEL_SHAPE, gen_decode_paged, gen_long_context, gen_planted_prefill, gen_prefill  # noqa: E402
+from synth.inputs import MXFP8  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
@@ -62,11 +63,12 @@ def prefill_counts(n_q, q_start, shape=MODEL_SHAPE):
     return idx_flops, main_flops, dense_flops
 
 
-def decode_bytes(seq_lens, shape=MODEL_SHAPE, esz=2, cache_esz=None):
+def decode_bytes(seq_lens, shape=MODEL_SHAPE, esz=2, cache_esz=None, mx=False):
     """Algorithmic HBM bytes of one decode step: the index keys of every past
     page (index scan) and the visible keys/values of the k selected pages.
-    ``cache_esz``: bytes per cached element (default ``esz``; 1 for e4m3)."""
-    cesz = esz if cache_esz is None else cache_esz
+    ``cache_esz``: bytes per cached element (default ``esz``; 1 for e4m3);
+    ``mx``: MXFP8 caches, one more scale byte per 32 cached elements."""
+    cesz = (esz if cache_esz is None else cache_esz) + (1.0 / 32 if mx else 0.0)
     L = np.asarray(seq_lens, dtype=np.int64)
     diag = (L - 1) // BLOCK
     idx_bytes = float((BLOCK * diag * shape.d_idx * cesz).sum())
@@ -936,14 +938,24 @@ def bench_step32k(msa, args):
 
 
 def bench_decode_fp8(msa, args):
-    """The 64 x 131072 paged decode step with e4m3 K, V and K_idx caches
-    (bf16 queries and outputs), 4 rotating query sets."""
+    """The 64 x 131072 paged decode step with 8-bit K, V and K_idx caches
+    (bf16 queries and outputs), 4 rotating query sets: e4m3 codes used as
+    stored, then MXFP8 (the same codes with one E8M0 scale per 32 elements)."""
+    res = _decode_8bit(msa, args, mx=False)
+    res["mxfp8"] = _decode_8bit(msa, args, mx=True)
+    res["mxfp8"].pop("workload")
+    print(json.dumps(res))
+
+
+def _decode_8bit(msa, args, mx):
     dev = "cuda"
     shape = MODEL_SHAPE
     B, L = 64, 131072
-    dec = gen_decode_paged(B, L, shape, seed=3, device=dev, n_query_sets=4, cache_dtype=torch.float8_e4m3fn)
+    dec = gen_decode_paged(B, L, shape, seed=3, device=dev, n_query_sets=4,
+                           cache_dtype=MXFP8 if mx else torch.float8_e4m3fn)
+    ks, vs, kis = dec.get("k_pages_scale"), dec.get("v_pages_scale"), dec.get("k_idx_pages_scale")
     s_idx = msa.make_shape(shape.h_q, shape.h_kv, shape.d_h, shape.d_idx, shape.top_k, msa.MSA_BF16,
-                           cache_dtype=msa.MSA_FP8_E4M3)
+                           cache_dtype=msa.MSA_MXFP8_E4M3 if mx else msa.MSA_FP8_E4M3)
     mp = dec["page_table"].shape[1]
     dbidx = [torch.empty((B, shape.h_kv, shape.top_k), dtype=torch.int32, device=dev) for _ in range(4)]
     do = torch.empty((B, shape.h_q, shape.d_h), dtype=torch.bfloat16, device=dev)
@@ -956,9 +968,9 @@ def bench_decode_fp8(msa, args):
 
     def calls(j):
         return [lambda: msa.index_topk(qisets[j], dec["k_idx_pages"], top_k=16, page_table=dec["page_table"],
-                                       seq_lens=dec["seq_lens"], out=dbidx[j], workspace=ws_di),
+                                       seq_lens=dec["seq_lens"], out=dbidx[j], workspace=ws_di, k_idx_scale=kis),
                 lambda: msa.sparse_decode(qsets[j], dec["k_pages"], dec["v_pages"], dec["page_table"],
-                                          dec["seq_lens"], dbidx[j], out=do, workspace=ws_dd)]
+                                          dec["seq_lens"], dbidx[j], out=do, workspace=ws_dd, k_scale=ks, v_scale=vs)]
     timer = CallTimer(["index_decode", "sparse_decode"])
     for w in range(args.warmup):
         for f in calls(w % 4):
@@ -967,12 +979,14 @@ def bench_decode_fp8(msa, args):
     evs = [timer.step(calls(i % 4)) for i in range(args.steps)]
     timer.collect(evs)
     t_id, t_sd = timer.mean_ms("index_decode"), timer.mean_ms("sparse_decode")
-    didx_b, dmain_b, _ = decode_bytes([L] * B, shape, cache_esz=1)
-    print(json.dumps({"workload": "decode 64 x 131072 paged, e4m3 K/V/K_idx caches, bf16 queries",
-                      "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
-                      "index_us": round(t_id * 1e3, 2), "sparse_us": round(t_sd * 1e3, 2),
-                      "index_roofline": roofline("hbm", didx_b, t_id, "GB/s"),
-                      "sparse_roofline": roofline("hbm", dmain_b, t_sd, "GB/s")}))
+    didx_b, dmain_b, _ = decode_bytes([L] * B, shape, cache_esz=1, mx=mx)
+    del dec
+    torch.cuda.empty_cache()
+    return {"workload": "decode 64 x 131072 paged, e4m3 K/V/K_idx caches, bf16 queries",
+            "decode_us_per_step": round((t_id + t_sd) * 1e3, 2),
+            "index_us": round(t_id * 1e3, 2), "sparse_us": round(t_sd * 1e3, 2),
+            "index_roofline": roofline("hbm", didx_b, t_id, "GB/s"),
+            "sparse_roofline": roofline("hbm", dmain_b, t_sd, "GB/s")}
 
 
 def bench_prefill_only(msa, args, planted=True):
