@@ -556,7 +556,7 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
   __shared__ uint64_t wthr[kLevels][NW];
   __shared__ uint64_t surv[kCap];
   __shared__ uint64_t top[kMaxTopK];
-  __shared__ uint64_t thr;
+  __shared__ uint64_t thr[kLevels];
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
   const int L = scalar_load(a.seq_lens, s);
@@ -602,26 +602,27 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // lane w < NW holds t_w(j); the m-th largest over the waves is the value
-    // with m - 1 larger ones (nonzero values are unique keys)
-    uint64_t T = 0;
-#pragma unroll
-    for (int e = 0; e < kLevels; ++e) {
-      const int m = 1 << e;
-      if (m > NW) break;
+  // wave e takes level e: lane w < NW holds t_w(j), j = 16 >> e, and the m-th
+  // largest over the waves (m = 2^e) is the value with m - 1 larger ones
+  // (nonzero values are unique keys); levels with m > NW give no bound
+  if (wave < kLevels) {
+    const int e = wave, m = 1 << e;
+    uint64_t t = 0ull;
+    if (m <= NW) {
       const uint64_t x = lane < NW ? wthr[e][lane] : 0ull;
       int g = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) g += wthr[e][w] > x ? 1 : 0;
       const uint64_t hit = __ballot(x != 0ull && g == m - 1);
-      const uint64_t t = hit ? readlane_u64(x, __builtin_ctzll(hit)) : 0ull;
-      T = t > T ? t : T;
+      t = hit ? readlane_u64(x, __builtin_ctzll(hit)) : 0ull;
     }
-    if (lane == 0) thr = T;
+    if (lane == 0) thr[e] = t;
   }
   __syncthreads();
-  const uint64_t T = thr;
+  uint64_t T = 0ull;
+#pragma unroll
+  for (int e = 0; e < kLevels; ++e)
+    if ((1 << e) <= NW) T = thr[e] > T ? thr[e] : T;
   if (tmax >= T && tmax != 0) {
     int c = 0;
 #pragma unroll
