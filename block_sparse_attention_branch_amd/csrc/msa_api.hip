@@ -81,6 +81,8 @@ msa_status check_scales(const msa_shape& s, const msa_kv* kv, bool need_idx, boo
   if (need_idx && !kv->k_idx_scale) return fail(MSA_ERR_INVALID_ARG, "MXFP8 caches: kv->k_idx_scale is NULL");
   if (need_kv && (!kv->k_scale || !kv->v_scale))
     return fail(MSA_ERR_INVALID_ARG, "MXFP8 caches: kv->k_scale/v_scale is NULL");
+  if ((need_idx && !aligned16(kv->k_idx_scale)) || (need_kv && (!aligned16(kv->k_scale) || !aligned16(kv->v_scale))))
+    return fail(MSA_ERR_INVALID_ARG, "MXFP8 caches: scale arrays must be 16-byte aligned");
   return MSA_OK;
 }
 
