@@ -42,11 +42,12 @@ def _index_case(shape, n_kv, n_q, dtype, seed, *, force_local=True, with_scores=
     q_start = inp["q_start"]
     _say("index_topk", shape, n_kv, n_q, dtype, seed, force_local, pool, cache_dtype)
     out = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=shape.top_k, q_start=q_start,
-                         force_local=force_local, with_scores=with_scores, pool=pool)
+                         force_local=force_local, with_scores=with_scores, pool=pool,
+                         k_idx_scale=inp.get("k_idx_scale"))
     torch.cuda.synchronize()
     ids, sc = out if with_scores else (out, None)
-    o_ids, o_sc, pooled = orc.index_topk(np64(inp["q_idx"]), _cache_host(inp["k_idx"]), q_start, shape.top_k,
-                                         force_local=force_local, pool=pool)
+    o_ids, o_sc, pooled = orc.index_topk(np64(inp["q_idx"]), _cache_host(inp["k_idx"], inp.get("k_idx_scale")),
+                                         q_start, shape.top_k, force_local=force_local, pool=pool)
     diags = (q_start + np.arange(n_q)) // 128
     n_exact, n_exc = compare_index_rows(ids.cpu().numpy(), o_ids, pooled, diags, force_local)
     if sc is not None:
@@ -167,20 +168,33 @@ def test_index_mean_pool_prefill():
                 cache_dtype=torch.float8_e4m3fn)
 
 
+def test_index_mxfp8_keys_with_the_index_options():
+    # MXFP8 index keys with every option of the index call: scores reported, no
+    # forced block, mean-pool, a chunked unaligned start, d_idx 32 and 128
+    _index_case(MODEL_SHAPE, 2125, 2125, torch.bfloat16, 140, with_scores=True, cache_dtype=MXFP8)
+    _index_case(HeadShape(8, 2, 64, 64, 5), 1500, 1500, torch.bfloat16, 141, force_local=False, cache_dtype=MXFP8)
+    _index_case(MODEL_SHAPE, 3000, 700, torch.bfloat16, 142, pool="mean", with_scores=True, cache_dtype=MXFP8)
+    _index_case(HeadShape(16, 4, 128, 32, 16), 900, 900, torch.bfloat16, 143, force_local=False, pool="mean",
+                cache_dtype=MXFP8)
+    _index_case(HeadShape(16, 4, 128, 128, 7), 1300, 1300, torch.bfloat16, 144, cache_dtype=MXFP8)
+
+
 def test_index_mean_pool_decode():
     msa = _msa()
     for shape, seq_lens, seed, cdt in ((MODEL_SHAPE, [1, 127, 128, 129, 3000, 2049, 40000], 46, None),
                                        (HeadShape(16, 2, 64, 32, 16), [5000, 700, 129], 47, torch.float8_e4m3fn),
-                                       (HeadShape(16, 4, 128, 128, 8), [1500, 9000], 48, None)):
+                                       (HeadShape(16, 4, 128, 128, 8), [1500, 9000], 48, None),
+                                       (HeadShape(16, 4, 128, 64, 16), [4000, 300, 128], 49, MXFP8)):
         inp = gen_decode_paged(len(seq_lens), max(seq_lens), shape, seed=seed, device=DEV, seq_lens=seq_lens,
                                cache_dtype=cdt)
         _say("decode index mean-pool", shape, seq_lens, seed, cdt)
         q_idx = inp["q_idx"][0].contiguous()
+        kis = inp.get("k_idx_pages_scale")
         bidx, bsc = msa.index_topk(q_idx, inp["k_idx_pages"], top_k=shape.top_k, page_table=inp["page_table"],
-                                   seq_lens=inp["seq_lens"], pool="mean", with_scores=True)
+                                   seq_lens=inp["seq_lens"], pool="mean", with_scores=True, k_idx_scale=kis)
         torch.cuda.synchronize()
         pt = inp["page_table"].cpu().numpy()
-        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), _cache_host(inp["k_idx_pages"]), pt, seq_lens,
+        o_ids, _, pooled = orc.index_topk_decode(np64(q_idx), _cache_host(inp["k_idx_pages"], kis), pt, seq_lens,
                                                  shape.top_k, pool="mean")
         diags = (np.asarray(seq_lens) - 1) // 128
         compare_index_rows(bidx.cpu().numpy(), o_ids, pooled, diags)
