@@ -364,9 +364,10 @@ struct KpArgs {
   const int32_t* item_off;
   const int32_t* entries;
   const i32x4* items;
-  void* part_o;       // [window, h_kv, top_k, G, D]  un-normalised sum_j p_j v_j
-  float2* part_ml;    // [window, h_kv, top_k, G]     (row max * sm_scale, sum_j p_j)
+  void* part_o;       // [span, h_kv, top_k, G, D]  un-normalised sum_j p_j v_j
+  float2* part_ml;    // [span, h_kv, top_k, G]     (row max * sm_scale, sum_j p_j)
   int32_t n_kv, q_start, h_q, h_kv, group, g_shift, top_k, n_blocks, window, chunk, w;
+  int32_t slot_tok0;  // first token of the span of windows the partial buffer holds
   size_t trash_slot;  // first of two spare slot regions at the end of part_o / part_ml
   float sm_scale;
 };
@@ -394,7 +395,7 @@ __device__ __forceinline__ void kp_load_pass(KpPass<T, D>& ps, const KpArgs& a, 
   ps.ok = rho < (m.e_end - m.e_begin) * G;
   const int i = ent >> 4, j = ent & 15;
   ps.head = rho & (G - 1);
-  ps.slot = ((i - a.w * a.window) * a.h_kv + m.r) * a.top_k + j;
+  ps.slot = ((i - a.slot_tok0) * a.h_kv + m.r) * a.top_k + j;
   ps.pos = ps.ok ? a.q_start + i : -1;
   const T* qrow = q + ((size_t)i * a.h_q + m.r * G + ps.head) * D + half * 8;
 #pragma unroll
@@ -1276,6 +1277,7 @@ void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv,
   p.n_blocks = (int32_t)((((int64_t)q_start + n_q - 1) / kBlock + 1 + 7) & ~int64_t(7));
   p.window = window;
   p.n_windows = (int32_t)((n_q + window - 1) / window);
+  p.merge_windows = 1;
   p.chunk = chunk;
   p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
   const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
@@ -1295,11 +1297,15 @@ void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv,
 }
 
 // Window sizing of the sparse prefill (measured optima, see prefill_plan):
-// partial bytes a window may use at least and at most, and the average tokens
-// per (group, block) cell the window is grown to.
+// partial bytes a window may use at least and at most, the average tokens
+// per (group, block) cell the window is grown to; the partial bytes up to
+// which a window is merged on its own (the last-level cache holds them), and
+// the tokens one merge launch spans past that.
 constexpr size_t kPartialBudgetBytes = size_t(128) << 20;
 constexpr size_t kPartialCapBytes = size_t(4096) << 20;
 constexpr int64_t kCellTokens = 40;
+constexpr size_t kMergeAloneBytes = size_t(256) << 20;
+constexpr int64_t kMergeSpanTokens = 12288;
 
 PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, int32_t h_q,
                          int32_t h_kv, int32_t d_h, int32_t top_k) {
@@ -1324,8 +1330,19 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   w = std::min<int64_t>(w, std::max<int32_t>(n_q, 1));
   p.window = (int32_t)w;
   schedule_layout(p, n_q, q_start, h_kv, top_k, (int32_t)w, 512 / G);  // items of 512 (token, head) rows
+  // A window whose partials fit the last-level cache is merged on its own,
+  // while they are still cached.  Past that they reach HBM anyway; each merge
+  // launch has a fixed cost (its start, where every workgroup stages its
+  // diagonal block at once, and its tail), so the partials of several
+  // consecutive windows are kept side by side and merged by one launch.
+  int64_t mw = 1;
+  if ((size_t)w * per_token > kMergeAloneBytes) {
+    mw = std::max<int64_t>(1, std::min<int64_t>(kMergeSpanTokens / w, (int64_t)(cap / per_token) / w));
+    mw = std::min<int64_t>(mw, p.n_windows);
+  }
+  p.merge_windows = (int32_t)mw;
   size_t off = p.total;
-  const size_t prow = ((size_t)p.window * h_kv * top_k + 2) * G;  // + two trash slots
+  const size_t prow = ((size_t)p.window * mw * h_kv * top_k + 2) * G;  // + two trash slots
   p.off_part_o = off; off = align_up(off + prow * d_h * esz);
   p.off_part_lse = off; off = align_up(off + prow * 8);
   p.total = off;
@@ -1430,7 +1447,8 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   kp.items = s.items;
   kp.part_o = ws + pl.off_part_o;
   kp.part_ml = reinterpret_cast<float2*>(ws + pl.off_part_lse);
-  kp.trash_slot = (size_t)pl.window * a.h_kv * a.top_k;
+  const int span = pl.window * pl.merge_windows;  // tokens whose partials the buffer holds
+  kp.trash_slot = (size_t)span * a.h_kv * a.top_k;
   kp.n_kv = a.n_kv;
   kp.q_start = a.q_start;
   kp.h_q = a.h_q;
@@ -1463,7 +1481,7 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
   km.group = a.group;
   km.g_shift = kp.g_shift;
   km.top_k = a.top_k;
-  km.window = pl.window;
+  km.window = span;
   km.tile_tokens = kKmRows / a.group;
   km.sm_scale = a.sm_scale;
 
@@ -1472,14 +1490,17 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     const int tok = std::min<int>(pl.window, a.n_q - w * pl.window);
     const int64_t bound = (int64_t)tok * a.h_kv * a.top_k / pl.chunk + (int64_t)a.h_kv * pl.n_blocks + 1;
     kp.w = w;
+    kp.slot_tok0 = (w / pl.merge_windows) * span;
     int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kKpWgPerCu);
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
     const int pk = profile_begin(PK_KP, st);
     hipLaunchKernelGGL((kp_kernel<T, D, TC>), dim3(grid), dim3(kKpThreads), 0, st, kp);
     profile_end(pk, st);
-    km.w = w;
-    // aligned runs of tile_tokens positions that meet the window's positions
-    const int p0 = a.q_start + w * pl.window, p1 = p0 + tok;
+    // merge once the span's last window (or the call's) is done
+    if ((w + 1) % pl.merge_windows != 0 && w + 1 < pl.n_windows) continue;
+    km.w = w / pl.merge_windows;
+    // aligned runs of tile_tokens positions that meet the span's positions
+    const int p0 = a.q_start + km.w * span, p1 = a.q_start + std::min<int>(a.n_q, (km.w + 1) * span);
     km.tile0 = p0 / km.tile_tokens;
     km.n_runs = (p1 - 1) / km.tile_tokens - km.tile0 + 1;
     const int pm = profile_begin(PK_KM, st);

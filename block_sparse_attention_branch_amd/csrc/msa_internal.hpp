@@ -120,6 +120,7 @@ struct AttnArgs {
 struct PrefillPlan {
   int32_t window;           // query tokens per window
   int32_t n_windows;
+  int32_t merge_windows;    // consecutive windows whose partials one merge launch combines
   int32_t n_blocks;         // KV blocks addressable by the call
   int32_t chunk;            // max tokens per KV-outer work item
   int64_t n_cells;          // n_windows * h_kv * n_blocks

@@ -118,6 +118,24 @@ def test_workspace_size_queries():
         msa.workspace_size(9, s)
 
 
+def test_prefill_workspace_holds_the_merge_span():
+    """Partial buffers of the sparse prefill (model shape, bf16: 270336 bytes
+    per query token): a window whose partials fit the 256 MiB merge-alone
+    bound gets one buffer; past it the buffers of up to 12288 tokens of
+    windows are kept for one merge launch."""
+    s = _shape()
+    per_token = 4 * 16 * 16 * (128 * 2 + 8)
+    # 32K: window 704 tokens (40 per (group, block) cell), 190 MB: alone
+    p32 = msa.workspace_size(msa.OP_PREFILL, s, n_q=32768, n_kv=32768)
+    assert 704 * per_token <= p32 < 2 * 704 * per_token
+    # 16384 queries at 64K: window 1408 tokens (380 MB), 8 windows per merge
+    p64 = msa.workspace_size(msa.OP_PREFILL, s, n_q=16384, q_start=49152, n_kv=65536)
+    assert 8 * 1408 * per_token <= p64 < 9 * 1408 * per_token
+    # 128K: window 2752 tokens, 4 windows per merge
+    p128 = msa.workspace_size(msa.OP_PREFILL, s, n_q=131072, n_kv=131072)
+    assert 4 * 2752 * per_token <= p128 < 5 * 2752 * per_token
+
+
 def test_profile_api_host_side():
     msa.profile_enable(True)
     msa.profile_enable(False)

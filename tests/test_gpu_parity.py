@@ -781,6 +781,35 @@ def test_full_size_prefill_32k_sampled_rows():
     compare_out(o[torch.from_numpy(rows).to(DEV)], o_ref, torch.bfloat16)
 
 
+def test_prefill_merge_span_of_several_windows_sampled():
+    """16384 queries at 64K context: windows of 1408 tokens whose partials
+    (380 MB each) are merged 8 windows per launch, so the second merge covers
+    the last 4 windows, the last one ragged (896 tokens).  Rows on both sides
+    of every window edge and of the span edge are checked against the oracle."""
+    msa = _msa()
+    shape = MODEL_SHAPE
+    n_kv, n_q, win = 65536, 16384, 1408
+    inp = gen_prefill(n_kv, shape, n_q=n_q, dtype=torch.bfloat16, seed=6, device=DEV)
+    q0 = inp["q_start"]
+    _say("64K context, 16384 queries: merge spans of 8 windows")
+    bidx = msa.index_topk(inp["q_idx"], inp["k_idx"], top_k=16, q_start=q0)
+    o, lse = msa.sparse_prefill(inp["q"], inp["k"], inp["v"], bidx, q_start=q0, with_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    edges = [e + d for e in range(win, n_q, win) for d in (-1, 0)]
+    rows = np.unique(np.concatenate([edges, rng.choice(n_q, 16, replace=False), [0, n_q - 1]]))
+    g_ids = bidx.cpu().numpy()[rows]
+    o_ids, _, pooled = orc.index_topk(np64(inp["q_idx"]), np64(inp["k_idx"]), q0, 16, rows=rows)
+    compare_index_rows(g_ids, o_ids, pooled, (q0 + rows) // 128)
+    k64, v64 = np64(inp["k"]), np64(inp["v"])
+    rows_t = torch.from_numpy(rows).to(DEV)
+    q_rows = np64(inp["q"][rows_t])
+    ref = [orc.sparse_attention(q_rows[t:t + 1], k64, v64, g_ids[t:t + 1], q0 + int(i))
+           for t, i in enumerate(rows)]
+    compare_out(o[rows_t], np.stack([r[0][0] for r in ref]), torch.bfloat16)
+    compare_lse(lse[rows_t], np.stack([r[1][0] for r in ref]), torch.bfloat16)
+
+
 def test_full_size_decode_64x128k_sampled_sequences():
     """Decode step at the benchmark shape (64 x 131072 paged, random page
     table), in the benchmark's launch configuration; 3 sequences checked."""
