@@ -81,12 +81,21 @@ KiPlan ki_prefill_plan(int32_t n_q, int32_t h_kv, int32_t q_start, int32_t need_
 }
 
 // ----------------------------------------------------------- prefill kernel
+// bf16 index keys go from global memory straight into LDS (no register
+// staging), which leaves the registers for a fourth wave per SIMD.
+template <typename T, typename TC>
+constexpr bool kKiDirect = std::is_same<T, bf16_t>::value && std::is_same<TC, bf16_t>::value;
+
 // POOL: 0 block max-pool (the method), 1 block mean-pool.
 template <typename T, int DIDX, typename TC, int POOL>
-__global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs a) {
+__global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_prefill_kernel(KiPrefillArgs a) {
   constexpr int KS = DIDX / 16;                       // 16-wide contraction steps
   constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
-  constexpr int LDS_STRIDE = ROW_BYTES + 16;          // padded row, bytes
+  constexpr bool kDirect = kKiDirect<T, TC>;
+  // staged rows carry a 16-byte pad; direct copies fill whole rows, so there
+  // chunk c of row r sits at chunk c ^ swz(r) instead: either way the 8 rows
+  // one ds_read_b128 phase reads start on distinct banks
+  constexpr int LDS_STRIDE = kDirect ? ROW_BYTES : ROW_BYTES + 16;
   constexpr int CHUNKS_PER_ROW = ROW_BYTES / 16;
   constexpr int LOADS = 128 * CHUNKS_PER_ROW / kKiThreads;
   static_assert(LOADS >= 1 && (128 * CHUNKS_PER_ROW) % kKiThreads == 0, "staging split");
@@ -116,6 +125,7 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
+  auto swz = [](uint32_t r) -> uint32_t { return ROW_BYTES == 64 ? (r >> 1) & 3u : r & 7u; };
   const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
   const TC* __restrict__ k_idx = static_cast<const TC*>(a.k_idx);
 
@@ -158,7 +168,8 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
     n_pend = 0;
   };
 
-  // K_idx blocks are staged global -> registers -> LDS two blocks ahead.
+  // 8-bit and fp32 index keys are staged global -> registers -> LDS two
+  // blocks ahead (bf16 keys are copied directly, below).
   // Thread i of the workgroup copies 16-byte pieces at fixed offsets of a
   // block; only the partial last block of a contiguous cache clamps its rows
   // (those keys lie after every query, so the causal mask drops them).
@@ -180,7 +191,6 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
   constexpr int ROWS_PER_PASS = kKiThreads / CHUNKS_PER_ROW;
   const uint32_t srow = tid / CHUNKS_PER_ROW;
   const uint32_t col_off = (tid % CHUNKS_PER_ROW) * G_CHUNK;
-  Chunk pre0[LOADS], pre1[LOADS];
   // MXFP8: this thread's chunks all sit in scale column (tid % CHUNKS_PER_ROW) / 4
   const uint32_t scol = (tid % CHUNKS_PER_ROW) * 8 / kMxBlock;
   auto load_chunk = [&](Chunk& dst, const char* base, const uint8_t* sbase, uint32_t row) {
@@ -221,19 +231,9 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
     }
   };
 
-  if (b_begin < b_end) {
-    load_block(pre0, b_begin);
-    store_block(pre0, 0);
-  }
-  if (b_begin + 1 < b_end) load_block(pre0, b_begin + 1);
-  __syncthreads();
-  // one block: `cur` holds block b + 1, `nxt` receives block b + 2
-  auto block_step = [&](int b, Chunk (&cur)[LOADS], Chunk (&nxt)[LOADS]) {
-    const int buf = (b - b_begin) & 1;
-    // unconditional (past the end it reloads the last block, an L2 hit), so
-    // that the wait before storing `cur` below covers `cur` only and the
-    // loads of block b + 2 stay in flight through this block's math
-    load_block(nxt, min(b + 2, b_end - 1));
+  // Scores block b, staged in LDS buffer `buf`, against this wave's rows,
+  // pools the scores and offers the pooled score to the lane's list.
+  auto score_block = [&](int b, int buf) {
     const char* K = lds[buf];
     const bool masked = b >= min_diag;
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
@@ -245,8 +245,9 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag<T> af = *reinterpret_cast<const Frag<T>*>(
-            K + (kt * 32 + l32) * LDS_STRIDE + (ks * 16 + half * 8) * (int)sizeof(T));
+        const int row = kt * 32 + l32;
+        const int col = kDirect ? (int)(((uint32_t)(2 * ks + half) ^ swz(row)) * 16) : (ks * 16 + half * 8) * (int)sizeof(T);
+        const Frag<T> af = *reinterpret_cast<const Frag<T>*>(K + row * LDS_STRIDE + col);
         mma32(acc0, af, qf[0][ks]);
         mma32(acc1, af, qf[1][ks]);
       }
@@ -295,13 +296,65 @@ __global__ __launch_bounds__(kKiThreads, 3) void ki_prefill_kernel(KiPrefillArgs
       if (__any(n_pend == kPending)) absorb();
       if (my_valid && b == my_diag) diag_score = pooled;
     }
-    if (b + 1 < b_end) store_block(cur, buf ^ 1);
-    __syncthreads();
   };
-  // unrolled by two so the register stages swap roles without copies
-  for (int b = b_begin; b < b_end; b += 2) {
-    block_step(b, pre0, pre1);
-    if (b + 1 < b_end) block_step(b + 1, pre1, pre0);
+
+  if constexpr (kDirect) {
+    // Block b + 1 is copied into the other buffer while block b is scored
+    // (global_load_lds: lane i of a copy fills 16 bytes at the copy's LDS
+    // base + 16 i; the lane fetches the chunk that the swizzle puts there).
+    // Each wave waits for its own copies, the barrier for everyone's.
+    // the copy's LDS base goes to M0, so it is computed from uniform values;
+    // the global address is a uniform base plus a 32-bit lane offset
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto copy_block = [&](int b, int buf) {
+      const int64_t base_tok = a.page_table ? (int64_t)scalar_load(a.page_table, b) * kBlock : (int64_t)b * kBlock;
+      const char* base = reinterpret_cast<const char*>(k_idx + base_tok * DIDX);
+      const bool full = a.page_table || (int64_t)b * kBlock + kBlock <= a.n_kv;
+      const uint32_t last = full ? 127u : (uint32_t)(a.n_kv - 1 - b * kBlock);
+      char* dst = &lds[buf][wave_u * LOADS * 1024];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t pos = (uint32_t)((wave_u * LOADS + i) * 1024) + (uint32_t)lane * 16;  // byte in the buffer
+        const uint32_t r = pos / ROW_BYTES, c = ((pos % ROW_BYTES) / 16) ^ swz(r);
+        const uint32_t off = (full ? r : min(r, last)) * ROW_BYTES + c * 16;
+        __builtin_amdgcn_global_load_lds(base + off, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0,
+                                         0);
+      }
+    };
+    if (b_begin < b_end) copy_block(b_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int b = b_begin; b < b_end; ++b) {
+      const int buf = (b - b_begin) & 1;
+      if (b + 1 < b_end) copy_block(b + 1, buf ^ 1);
+      score_block(b, buf);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    Chunk pre0[LOADS], pre1[LOADS];
+    if (b_begin < b_end) {
+      load_block(pre0, b_begin);
+      store_block(pre0, 0);
+    }
+    if (b_begin + 1 < b_end) load_block(pre0, b_begin + 1);
+    __syncthreads();
+    // one block: `cur` holds block b + 1, `nxt` receives block b + 2
+    auto block_step = [&](int b, Chunk (&cur)[LOADS], Chunk (&nxt)[LOADS]) {
+      const int buf = (b - b_begin) & 1;
+      // unconditional (past the end it reloads the last block, an L2 hit), so
+      // that the wait before storing `cur` below covers `cur` only and the
+      // loads of block b + 2 stay in flight through this block's math
+      load_block(nxt, min(b + 2, b_end - 1));
+      score_block(b, buf);
+      if (b + 1 < b_end) store_block(cur, buf ^ 1);
+      __syncthreads();
+    };
+    // unrolled by two so the register stages swap roles without copies
+    for (int b = b_begin; b < b_end; b += 2) {
+      block_step(b, pre0, pre1);
+      if (b + 1 < b_end) block_step(b + 1, pre1, pre0);
+    }
   }
   absorb();
 
