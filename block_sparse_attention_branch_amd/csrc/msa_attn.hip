@@ -453,7 +453,9 @@ __device__ __forceinline__ void kp_math(const KpArgs& a, int b, const KpPass<T, 
   block_tile_math<T, D>(a.sm_scale, b, ps.ok, lds, t, mx, l);
 }
 
-template <typename T, int D>
+// NT: the partial outputs are stored non-temporally (a template parameter, as
+// the compiler merges the two kinds of store when both sit under one branch).
+template <typename T, int D, bool NT>
 __device__ __forceinline__ void kp_store(const KpArgs& a, const KpPass<T, D>& ps, const TileRegs<T, D, 1>& t,
                                          float mx, float l) {
   const int half = (threadIdx.x & 63) >> 5;
@@ -463,9 +465,8 @@ __device__ __forceinline__ void kp_store(const KpArgs& a, const KpPass<T, D>& ps
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      store8<T>(region + (size_t)part_chunk(dt, p, half, ps.head, G) * 8, t.o[0][dt], 8 * p);
-    }
+    for (int p = 0; p < 2; ++p)
+      store8<T, NT>(region + (size_t)part_chunk(dt, p, half, ps.head, G) * 8, t.o[0][dt], 8 * p);
   const size_t mrow = (half == 0 ? slot : a.trash_slot + 1) * G + ps.head;
   a.part_ml[mrow] = float2{mx * a.sm_scale, l};
 }
@@ -486,7 +487,7 @@ __device__ __forceinline__ KpItem kp_item_s(const KpArgs& a, int it) {
 // nsub, ...  Each item is two passes of 256 rows.  The next item's K/V and
 // token entries are prefetched into registers at the start of an item, the
 // next pass's queries while the current pass runs P.V.
-template <typename T, int D, typename TC = T>
+template <typename T, int D, typename TC = T, bool STREAM = false>
 __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
   using L = KvLds<T, D>;
   constexpr int NT = kKpThreads;
@@ -542,14 +543,14 @@ __global__ __launch_bounds__(kKpThreads) void kp_kernel(KpArgs a) {
       kp_load_pass<T, D>(ps, a, cur, rho0 + kKpRowsPerPass, kp_entry<T, D>(cur, rho0 + kKpRowsPerPass, a.g_shift, ent_lds));
     else if (has_next)
       kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
-    kp_store<T, D>(a, cp, t, mx, l);
+    kp_store<T, D, STREAM>(a, cp, t, mx, l);
     // pass 1
     if (two) {
       cp = ps;
       const bool act1 = __any(cp.ok);
       if (act1) kp_math<T, D>(a, cur.b, cp, L0, t, mx, l);
       if (has_next) kp_load_pass<T, D>(ps, a, nxt, rho0, nxt_ent);
-      kp_store<T, D>(a, cp, t, mx, l);
+      kp_store<T, D, STREAM>(a, cp, t, mx, l);
     }
     if (!has_next) break;
     if (NB == 1) __syncthreads();
@@ -1278,6 +1279,7 @@ void schedule_layout(PrefillPlan& p, int32_t n_q, int32_t q_start, int32_t h_kv,
   p.window = window;
   p.n_windows = (int32_t)((n_q + window - 1) / window);
   p.merge_windows = 1;
+  p.stream_partials = 0;
   p.chunk = chunk;
   p.n_cells = (int64_t)p.n_windows * h_kv * p.n_blocks;
   const int64_t n_entries = (int64_t)n_q * h_kv * top_k;
@@ -1335,10 +1337,13 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   // launch has a fixed cost (its start, where every workgroup stages its
   // diagonal block at once, and its tail), so the partials of several
   // consecutive windows are kept side by side and merged by one launch.
+  // Such partials are also stored non-temporally (streaming stores keep
+  // them from displacing the gathered queries and staged blocks in L2).
   int64_t mw = 1;
   if ((size_t)w * per_token > kMergeAloneBytes) {
     mw = std::max<int64_t>(1, std::min<int64_t>(kMergeSpanTokens / w, (int64_t)(cap / per_token) / w));
     mw = std::min<int64_t>(mw, p.n_windows);
+    p.stream_partials = 1;
   }
   p.merge_windows = (int32_t)mw;
   size_t off = p.total;
@@ -1494,7 +1499,10 @@ static hipError_t sparse_prefill_typed(const AttnArgs& a, const PrefillPlan& pl,
     int64_t g = std::min<int64_t>(bound + 8, (int64_t)n_cu * kKpWgPerCu);
     const unsigned grid = (unsigned)std::max<int64_t>(8, (g + 7) & ~int64_t(7));
     const int pk = profile_begin(PK_KP, st);
-    hipLaunchKernelGGL((kp_kernel<T, D, TC>), dim3(grid), dim3(kKpThreads), 0, st, kp);
+    if (pl.stream_partials)
+      hipLaunchKernelGGL((kp_kernel<T, D, TC, true>), dim3(grid), dim3(kKpThreads), 0, st, kp);
+    else
+      hipLaunchKernelGGL((kp_kernel<T, D, TC, false>), dim3(grid), dim3(kKpThreads), 0, st, kp);
     profile_end(pk, st);
     // merge once the span's last window (or the call's) is done
     if ((w + 1) % pl.merge_windows != 0 && w + 1 < pl.n_windows) continue;

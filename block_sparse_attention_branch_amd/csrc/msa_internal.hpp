@@ -121,6 +121,7 @@ struct PrefillPlan {
   int32_t window;           // query tokens per window
   int32_t n_windows;
   int32_t merge_windows;    // consecutive windows whose partials one merge launch combines
+  int32_t stream_partials;  // partials are written with streaming stores (they outgrow the caches)
   int32_t n_blocks;         // KV blocks addressable by the call
   int32_t chunk;            // max tokens per KV-outer work item
   int64_t n_cells;          // n_windows * h_kv * n_blocks

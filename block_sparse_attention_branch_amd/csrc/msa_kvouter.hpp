@@ -227,15 +227,28 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
 }
 
 // Store 8 consecutive values (one 16-byte store for bf16, two for fp32).
-template <typename T>
+// NT: a non-temporal (streaming) store, for data that is not read again
+// before it would have left the caches anyway.
+template <typename T, bool NT = false>
 __device__ __forceinline__ void store8(T* dst, const f32x16& o, int base) {
   if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<bf16x8*>(dst) =
-        bf16x8{from_f32<T>(o[base]), from_f32<T>(o[base + 1]), from_f32<T>(o[base + 2]), from_f32<T>(o[base + 3]),
-               from_f32<T>(o[base + 4]), from_f32<T>(o[base + 5]), from_f32<T>(o[base + 6]), from_f32<T>(o[base + 7])};
+    const bf16x8 v{from_f32<T>(o[base]), from_f32<T>(o[base + 1]), from_f32<T>(o[base + 2]), from_f32<T>(o[base + 3]),
+                   from_f32<T>(o[base + 4]), from_f32<T>(o[base + 5]), from_f32<T>(o[base + 6]),
+                   from_f32<T>(o[base + 7])};
+    if constexpr (NT)
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+    else
+      *reinterpret_cast<bf16x8*>(dst) = v;
   } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{o[base], o[base + 1], o[base + 2], o[base + 3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[base + 4], o[base + 5], o[base + 6], o[base + 7]};
+    const f32x4 lo{o[base], o[base + 1], o[base + 2], o[base + 3]};
+    const f32x4 hi{o[base + 4], o[base + 5], o[base + 6], o[base + 7]};
+    if constexpr (NT) {
+      __builtin_nontemporal_store(lo, reinterpret_cast<f32x4*>(dst));
+      __builtin_nontemporal_store(hi, reinterpret_cast<f32x4*>(dst + 4));
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = lo;
+      *reinterpret_cast<f32x4*>(dst + 4) = hi;
+    }
   }
 }
 
