@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
   constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
   constexpr bool kDirect = kKiDirect<T, TC>;
   // staged rows carry a 16-byte pad; direct copies fill whole rows, so there
-  // chunk c of row r sits at chunk c ^ swz(r) instead: either way the 8 rows
+  // chunk c of row r sits at chunk c ^ swz(r) instead: either way the rows
   // one ds_read_b128 phase reads start on distinct banks
   constexpr int LDS_STRIDE = kDirect ? ROW_BYTES : ROW_BYTES + 16;
   constexpr int CHUNKS_PER_ROW = ROW_BYTES / 16;
@@ -125,7 +125,12 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
-  auto swz = [](uint32_t r) -> uint32_t { return ROW_BYTES == 64 ? (r >> 1) & 3u : r & 7u; };
+  // chunk swizzle: the 16 rows that one ds_read_b128 phase reads (16 lanes,
+  // 64 four-byte banks) start on 16 distinct bank quads, and so do any 8
+  // consecutive rows against 32 banks
+  auto swz = [](uint32_t r) -> uint32_t {
+    return ROW_BYTES == 64 ? ((r >> 1) & 3u) ^ ((r >> 3) & 1u) : ROW_BYTES == 128 ? (r & 7u) ^ ((r >> 3) & 1u) : r & 15u;
+  };
   const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
   const TC* __restrict__ k_idx = static_cast<const TC*>(a.k_idx);
 
