@@ -612,7 +612,7 @@ __global__ __launch_bounds__(kKmThreads, 2) void km_kernel(KmArgs a) {
   // phase B's use of the same LDS
   T* od_s = reinterpret_cast<T*>(lds);                                              // [rows / G][G * D]
   float2* mld_s = reinterpret_cast<float2*>(lds + (size_t)kKmRows * D * sizeof(T));  // [rows]
-  float2* ml_s = mld_s + kKmRows;                                                   // [rows][16 slots]
+  float2* ml_s = mld_s + kKmRows;                                                   // [16 slots][rows]
   uint32_t* parts_s = reinterpret_cast<uint32_t*>(ml_s + kKmRows * kMaxTopK);      // [rows / G]
   static_assert((size_t)kKmRows * D * sizeof(T) + kKmRows * 8 * (1 + kMaxTopK) + kKmRows * 4 <= (size_t)L::BYTES,
                 "phase B fits the K/V area");
@@ -659,12 +659,14 @@ __global__ __launch_bounds__(kKmThreads, 2) void km_kernel(KmArgs a) {
       parts &= ~(1u << j);
     }
   // (max, sum) of every (row, slot), entries tid + 256 e, read now and put in
-  // LDS after the tile (the slot index is clamped; unused slots are masked)
+  // LDS after the tile (the slot index is clamped; unused slots are masked).
+  // Slot-major, so that the merge's lanes (consecutive rows, one slot) read
+  // consecutive LDS words.
   constexpr int kMlPerThread = kKmRows * kMaxTopK / kKmThreads;
   float2 mlr[kMlPerThread];
 #pragma unroll
   for (int e = 0; e < kMlPerThread; ++e) {
-    const int x = tid + kKmThreads * e, row = x / kMaxTopK, j = x % kMaxTopK;
+    const int x = tid + kKmThreads * e, row = x % kKmRows, j = x / kKmRows;
     bool okr;
     const int ir = tok(row >> a.g_shift, okr);
     const size_t slot = ((size_t)(ir - a.w * a.window) * a.h_kv + r) * a.top_k + min(j, a.top_k - 1);
@@ -725,7 +727,7 @@ __global__ __launch_bounds__(kKmThreads, 2) void km_kernel(KmArgs a) {
     float mx = md.x;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      ml[j] = ((pm >> j) & 1u) ? ml_s[row * kMaxTopK + j] : float2{-__builtin_inff(), 0.0f};
+      ml[j] = ((pm >> j) & 1u) ? ml_s[j * kKmRows + row] : float2{-__builtin_inff(), 0.0f};
       mx = fmaxf(mx, ml[j].x);
     }
     const float mref = mx == -__builtin_inff() ? 0.0f : mx;
