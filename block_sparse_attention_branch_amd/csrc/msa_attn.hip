@@ -1339,15 +1339,19 @@ PrefillPlan prefill_plan(int dtype, int32_t n_q, int32_t q_start, int32_t n_kv, 
   // launch has a fixed cost (its start, where every workgroup stages its
   // diagonal block at once, and its tail), so the partials of several
   // consecutive windows are kept side by side and merged by one launch.
-  // Such partials are also stored non-temporally (streaming stores keep
-  // them from displacing the gathered queries and staged blocks in L2).
+  // Partials that wait for a merge of several windows are stored
+  // non-temporally: streaming stores keep them from displacing the gathered
+  // queries and staged blocks in L2 (measured at 128K: KV-outer pass -6%,
+  // merge -5%).  A single long window (a chunk at long context, about 15
+  // tokens per cell, K/V most of the traffic) keeps plain stores, where
+  // streaming ones slowed the KV-outer pass by 10%.
   int64_t mw = 1;
   if ((size_t)w * per_token > kMergeAloneBytes) {
     mw = std::max<int64_t>(1, std::min<int64_t>(kMergeSpanTokens / w, (int64_t)(cap / per_token) / w));
     mw = std::min<int64_t>(mw, p.n_windows);
-    p.stream_partials = 1;
   }
   p.merge_windows = (int32_t)mw;
+  p.stream_partials = mw > 1 ? 1 : 0;
   size_t off = p.total;
   const size_t prow = ((size_t)p.window * mw * h_kv * top_k + 2) * G;  // + two trash slots
   p.off_part_o = off; off = align_up(off + prow * d_h * esz);
