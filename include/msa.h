@@ -296,8 +296,10 @@ int32_t msa_abi_version(void);
  * msa_profile_read(kernel, &total_ms, &launches): waits for the recorded
  *   launches of `kernel`, returns their summed GPU time and count, and
  *   forgets them.  Kernel names: "ki_prefill_kernel" (msa_index_topk,
- *   prefill), "kp_kernel" and "km_kernel" (msa_sparse_prefill, KV-outer
- *   pass and merge, one launch each per window of queries),
+ *   prefill), "kp_kernel" and "km_kernel" (msa_sparse_prefill: the
+ *   KV-outer pass, one launch per window of queries, and the merge, one
+ *   launch per window or, once a window's partials exceed 256 MB, per span
+ *   of consecutive windows),
  *   "ki_decode_scan_kernel" (msa_index_topk, decode), "kd_kernel"
  *   (msa_sparse_decode), "kbq_kernel" (dq pass of msa_sparse_prefill_backward,
  *   one launch per window) and "kbkv_kernel" (its dk/dv pass).  Unknown
