@@ -473,8 +473,9 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   const int p = L - 1;
   const int nb = (L + kBlock - 1) / kBlock;
   const int hi = (a.need_diag || !a.force_local) ? nb : nb - 1;
-  const int pg_begin = blockIdx.x * a.pages_per_wg;
-  const int pg_end = min(pg_begin + a.pages_per_wg, hi);
+  static_assert(kKiDecodePagesPerWg % 4 == 0 && kKiDecodePagesPerWg <= 256, "4 waves, one page id per lane");
+  const int pg_begin = blockIdx.x * kKiDecodePagesPerWg;
+  const int pg_end = min(pg_begin + kKiDecodePagesPerWg, hi);
   if (pg_begin >= pg_end) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, l16 = lane & 15;
@@ -490,7 +491,8 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   // workgroup covers at most 256 pages), read with one vector load, so no
   // page's loads wait on a page-table read of their own.
   const int my_pg = pg_begin + wave + 4 * lane;
-  const int pid = my_pg < pg_end ? pt[my_pg] : 0;
+  int pid = my_pg < pg_end ? pt[my_pg] : 0;
+  settle(pid);  // waited for here, so no later wait on it also covers page loads in flight
   // For rows of up to 128 bytes the next page's index keys are loaded while
   // the current page is scored (wider rows would not fit two pages).
   constexpr bool kPipe = sizeof(TC) * DIDX <= 128;
@@ -501,12 +503,9 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     ki_load_page<TC, DIDX>(f, sc, k_idx + tok * DIDX,
                            kIsMx<TC> ? a.k_idx_scale + tok * (DIDX / kMxBlock) : nullptr);
   };
-  int pg = pg_begin + wave;
-  int j = 0;
-  if (kPipe && pg < pg_end) load(cur, csc, __builtin_amdgcn_readlane(pid, 0));
-  for (; pg < pg_end; pg += 4, ++j) {
-    if (!kPipe) load(cur, csc, __builtin_amdgcn_readlane(pid, j));
-    if (kPipe && pg + 4 < pg_end) load(nxt, nsc, __builtin_amdgcn_readlane(pid, j + 1));
+  // Scores the page held in f (scale bytes sc): returns the pooled score of
+  // group l16 (valid in the lanes with q4 == 0 and l16 < h_kv).
+  auto score = [&](const Raw<TC>(&f)[8][KS], const uint32_t(&sc)[8], int pg) -> float {
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
     // keys on the MFMA rows, groups on the columns: acc[v] of lane (q4, l16)
     // is key kt*16 + 4*q4 + v against group l16, so the pool over the page's
@@ -517,7 +516,7 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16(acc, widen<T, TC>(cur[kt][ks], csc[kt]), qa[ks]);
+      for (int ks = 0; ks < KS; ++ks) mma16(acc, widen<T, TC>(f[kt][ks], sc[kt]), qa[ks]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const bool vis = !masked || (pg * kBlock + kt * 16 + 4 * q4 + v <= p);
@@ -537,17 +536,48 @@ __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
     }
     // mean-pool: the page's visible keys (all 128 but on the last page)
     const float inv_cnt = POOL == 0 ? 1.0f : 1.0f / (float)(masked ? p - pg * kBlock + 1 : kBlock);
-    if (q4 == 0 && l16 < a.h_kv)
-      a.scores[((size_t)s * a.h_kv + l16) * a.max_pages + pg] =
-          POOL == 0 ? m * a.idx_scale : m * a.idx_scale * inv_cnt;
-    if (kPipe) {
+    return POOL == 0 ? m * a.idx_scale : m * a.idx_scale * inv_cnt;
+  };
+  // The wave scores pages pg0, pg0 + 4, ... (at most kPw of them).  The loop
+  // is unrolled, so the two register sets take turns without copies, and the
+  // next page's loads are unconditional (past the wave's last page they load
+  // that page again, an L2 hit), so the wait before a page's math covers
+  // that page's loads only.  The scores are stored after the loop: a store
+  // inside it made the next write to its data register wait for every load
+  // in flight (the counter orders loads and stores alike).
+  constexpr int kPw = kKiDecodePagesPerWg / 4;
+  const int pg0 = pg_begin + __builtin_amdgcn_readfirstlane(wave);
+  const int n_mine = (pg_end - pg0 + 3) / 4;  // uniform; 0 or less: no page
+  float res[kPw];
+  if constexpr (kPipe) {
+    if (n_mine > 0) load(cur, csc, __builtin_amdgcn_readlane(pid, 0));
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cur[kt][ks] = nxt[kt][ks];
-        csc[kt] = nsc[kt];
+    for (int i = 0; i < kPw; ++i) {
+      if (i >= n_mine) break;
+      const int nx = min(i + 1, n_mine - 1);
+      if (i & 1) {
+        load(cur, csc, __builtin_amdgcn_readlane(pid, nx));
+        MSA_SCHED_FENCE();  // keep the next page's loads ahead of this page's math
+        res[i] = score(nxt, nsc, pg0 + 4 * i);
+      } else {
+        load(nxt, nsc, __builtin_amdgcn_readlane(pid, nx));
+        MSA_SCHED_FENCE();
+        res[i] = score(cur, csc, pg0 + 4 * i);
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPw; ++i) {
+      if (i >= n_mine) break;
+      load(cur, csc, __builtin_amdgcn_readlane(pid, i));
+      res[i] = score(cur, csc, pg0 + 4 * i);
+    }
+  }
+  if (q4 == 0 && l16 < a.h_kv) {
+    float* dst = a.scores + ((size_t)s * a.h_kv + l16) * a.max_pages;
+#pragma unroll
+    for (int i = 0; i < kPw; ++i)
+      if (i < n_mine) dst[pg0 + 4 * i] = res[i];
   }
 }
 
@@ -720,7 +750,7 @@ static hipError_t ki_prefill_typed(const KiPrefillArgs& a, hipStream_t st) {
 
 template <typename T, int DIDX, typename TC = T>
 static hipError_t ki_decode_typed(const KiDecodeArgs& a, hipStream_t st) {
-  dim3 grid((a.max_pages + a.pages_per_wg - 1) / a.pages_per_wg, a.batch);
+  dim3 grid((a.max_pages + kKiDecodePagesPerWg - 1) / kKiDecodePagesPerWg, a.batch);
   const int ps = profile_begin(PK_KI_DECODE_SCAN, st);
   if (a.pool == 1)
     hipLaunchKernelGGL((ki_decode_scan_kernel<T, DIDX, TC, 1>), grid, dim3(256), 0, st, a);
