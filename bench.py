@@ -1,24 +1,32 @@
 """Benchmark of the MSA hot path on one MI355X.
 
-One step = one pass of every hot-path row over one batch of synthetic input:
-  prefill  (1 sequence, N = 32768, 64 query / 4 KV heads, d_h 128, d_idx 64,
-            B_k 128, k 16, bf16 N(0,1)/sqrt(d)):  msa_index_topk + msa_sparse_prefill
-  decode   (64 sequences x 131072-token paged cache, same heads, bf16 N(0,1),
-            4 rotating query sets):                msa_index_topk + msa_sparse_decode
-``value`` is prefill tokens/s of the step's prefill part; the decode part is
-reported as ``decode_us_per_step``.  Each ABI call is timed with HIP events on
-the stream it is launched on; ``roofline`` covers the dominant call
-(msa_sparse_prefill, bound by MFMA) and ``rooflines`` every call.  The dense
-GQA kernel is timed at the prefill shape for comparison, outside the step.
-The float64 oracle is timed on a bounded sample on the host (cpu_baseline).
+One step = one pass of every hot-path row at 128K and 1M context, on seeded
+synthetic inputs resident in HBM (64 query / 4 KV heads, d_h 128, d_idx 64,
+B_k 128, k 16, bf16):
+  prefill128k    131072-token causal prefill with planted retrieval blocks
+                 (contiguous cache): msa_index_topk + msa_sparse_prefill
+  prefill1m      the last 8192 queries of a 1,048,576-token paged cache:
+                 msa_index_topk + msa_sparse_prefill
+  decode64x128k  one decode step of 64 sequences x 131072 tokens (paged,
+                 4 rotating query sets): msa_index_topk + msa_sparse_decode
+After the timed steps, 256 decode steps of the 1M sequence (batch 1) give
+the decode latency p50 / p99, eager and from a HIP graph.
+``value`` is prefill tokens/s over the step's four prefill calls; the decode
+legs are reported in microseconds per step.  Each ABI call is timed with HIP
+events on the stream it is launched on; ``roofline`` covers the dominant
+kernel (kp_kernel, the KV-outer pass) and ``roofline.call`` the whole
+msa_sparse_prefill call; ``rooflines`` lists every call.  The dense GQA
+kernel is timed at the 128K shape for comparison, outside the step.  The
+float64 oracle is timed on a bounded sample on the host (cpu_baseline).
 
-Other workloads print their own JSON line: prefill128k (planted), long1m,
-decode_fp8 (e4m3 caches), backward32k (the training path's gradient call at
-the 32K prefill shape), project (index projections + RoPE), copy (bandwidth
-calibration) and peak (achievable MFMA rate and copy bandwidth).
+Other workloads print their own JSON line: step32k (the 32K prefill with the
+64 x 128K decode), prefill128k (planted, with the retrieval check), long1m,
+decode_fp8 (e4m3 and MXFP8 caches), backward32k (the training path's gradient
+call at the 32K prefill shape), project (index projections + RoPE), copy
+(bandwidth calibration) and peak (achievable MFMA rate and copy bandwidth).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                       [--workload step|prefill128k|long1m|decode_fp8|backward32k|project|copy|peak]
+                       [--workload step|step32k|prefill128k|long1m|decode_fp8|backward32k|project|copy|peak]
 """
 from __future__ import annotations
 
