@@ -200,6 +200,27 @@ __device__ __forceinline__ void list_insert(uint64_t (&keys)[L], uint64_t v) {
   }
 }
 
+// Insert (v, b) into a list of scores sorted descending with their blocks
+// (capacity L), where b comes after every listed block: an equal score stays
+// ahead of v.  The caller checks v > sc[L-1]; the last entry falls off.  The
+// new score of slot s is max(sc[s], min(sc[s-1], v)), the median of the
+// three since sc[s] <= sc[s-1]; its block is the old one while sc[s] >= v,
+// b where v lands, and the block of slot s-1 below that.  Every slot is
+// computed from the old list, so there is no serial chain.
+template <int L>
+__device__ __forceinline__ void list_insert_later(float (&sc)[L], int (&id)[L], float v, int b) {
+  // bottom up, so that each slot is overwritten after the slot below has
+  // read it: the update stays in place
+#pragma unroll
+  for (int s = L - 1; s >= 0; --s) {
+    const float up = s > 0 ? sc[s - 1] : __builtin_inff();
+    const bool up_ge = s > 0 ? sc[s - 1] >= v : true;
+    const int up_id = s > 0 ? id[s - 1] : b;
+    id[s] = sc[s] >= v ? id[s] : (up_ge ? b : up_id);
+    sc[s] = __builtin_amdgcn_fmed3f(sc[s], up, v);
+  }
+}
+
 // Write one row's final index list: the `n_take` best keys of `keys`
 // (descending, 0 = empty), plus `forced` (>= 0) if given, as ascending block
 // ids padded with -1 to top_k; the pooled score of each id goes to `score_out`

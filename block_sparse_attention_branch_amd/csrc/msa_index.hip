@@ -137,6 +137,11 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
   const int my_row = row0 + wave * 64 + lane;  // row whose list this lane owns
   const bool my_valid = my_row < a.n_rows;
   const int my_diag = (a.q_start + (my_valid ? my_row : row_last) / a.h_kv) >> 7;
+  // last block this lane's list may take (the forced diagonal is added at
+  // the end); -1 for a lane without a row
+  const int my_last = !my_valid ? -1 : (a.force_local ? my_diag - 1 : my_diag);
+  // the block whose pooled score is the diagonal's (none for a lane without a row)
+  const int my_diag_b = my_valid ? my_diag : -1;
 
   // S^T columns of this lane: rows wave*64 + rt*32 + l32
   int col_pos[2];
@@ -155,21 +160,33 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) settle(qf[rt][ks]);
 
-  uint64_t keys[kMaxTopK];
+  // The lane's list: pooled scores descending (-inf = empty) with their
+  // blocks.  Blocks arrive in increasing order, so a later block must beat a
+  // score strictly to pass it, which keeps the lower block first on ties
+  // without a tie-break field; 32-bit compares and selects suffice.
+  float lsc[kMaxTopK];
+  int lid[kMaxTopK];
 #pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) keys[s] = 0ull;
+  for (int s = 0; s < kMaxTopK; ++s) {
+    lsc[s] = -__builtin_inff();
+    lid[s] = 0;
+  }
   float diag_score = -__builtin_inff();
   constexpr int kPending = 3;
-  uint64_t pend[kPending];
+  float psc[kPending];
+  int pbl[kPending];
 #pragma unroll
-  for (int p = 0; p < kPending; ++p) pend[p] = 0ull;
+  for (int p = 0; p < kPending; ++p) {
+    psc[p] = -__builtin_inff();
+    pbl[p] = 0;
+  }
   int n_pend = 0;
-  // Inserts the pending candidates that still beat the list's last entry
-  // (inserting one raises that bound for the next).
+  // Inserts the pending candidates (in block order) that still beat the
+  // list's last entry (inserting one raises that bound for the next).
   auto absorb = [&]() {
 #pragma unroll
     for (int p = 0; p < kPending; ++p)
-      if (p < n_pend && pend[p] > keys[kMaxTopK - 1]) list_insert(keys, pend[p]);
+      if (p < n_pend && psc[p] > lsc[kMaxTopK - 1]) list_insert_later(lsc, lid, psc[p], pbl[p]);
     n_pend = 0;
   };
 
@@ -292,14 +309,15 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
     // whole wave when any lane needs one, and with one insertion per block
     // that would be almost every block.
     {
-      const bool cand = my_valid && (a.force_local ? (b < my_diag) : (b <= my_diag));
-      const uint64_t k = make_key(pooled, b);
-      const bool want = cand && k > keys[kMaxTopK - 1];
+      const bool want = b <= my_last && pooled > lsc[kMaxTopK - 1];
 #pragma unroll
-      for (int p = 0; p < kPending; ++p) pend[p] = (want && n_pend == p) ? k : pend[p];
+      for (int p = 0; p < kPending; ++p) {
+        psc[p] = (want && n_pend == p) ? pooled : psc[p];
+        pbl[p] = (want && n_pend == p) ? b : pbl[p];
+      }
       n_pend += want ? 1 : 0;
       if (__any(n_pend == kPending)) absorb();
-      if (my_valid && b == my_diag) diag_score = pooled;
+      if (b == my_diag_b) diag_score = pooled;
     }
   };
 
@@ -364,6 +382,10 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
   absorb();
 
   if (!my_valid) return;
+  // the list as 64-bit keys (score, then lower block first; 0 = empty)
+  uint64_t keys[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) keys[s] = lsc[s] > -__builtin_inff() ? make_key(lsc[s], lid[s]) : 0ull;
   if (a.n_chunks == 1) {
     const int n_take = a.top_k - (a.force_local ? 1 : 0);
     write_row_list(keys, n_take, a.force_local ? my_diag : -1, diag_score, a.top_k,
