@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmsa.so")
 SOURCES = ["msa_api.hip", "msa_index.hip", "msa_project.hip", "msa_attn.hip", "msa_train.hip", "msa_profile.hip"]
-ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"  # MI355X (CDNA4) only
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
