@@ -1014,15 +1014,20 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, q4 = lane >> 4, l16 = lane & 15;
   const int G = a.group;
-  const int L = scalar_load(a.seq_lens, s);
-  const int p = L - 1, diag = p >> 7;
   const int32_t* br = a.block_idx + ((size_t)s * a.h_kv + r) * a.top_k;
-  // lane j: block and physical page of slot j.  The list and the page ids are
-  // two vector loads issued before the slots are vetted (a clamped index keeps
-  // the page-table read in the row), so the start-up waits on two loads, not
-  // on one load per slot.
-  const int bv = lane < a.top_k ? br[lane] : -1;
-  const int pall = lane < a.top_k ? a.page_table[(size_t)s * a.max_pages + min(max(bv, 0), a.max_pages - 1)] : 0;
+  const T* __restrict__ qp = static_cast<const T*>(a.q) + ((size_t)s * a.h_q + r * G) * D;
+  // The block list, the queries and the sequence length are loaded at once
+  // (every load unconditional, with clamped indices, so none waits behind a
+  // branch), then the page ids of the listed blocks: lane j holds block and
+  // physical page of slot j.  The start-up waits on two round trips.
+  const int bv_raw = br[min(lane, a.top_k - 1)];
+  Frag<T> qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qf[ks] = load_frag<T>(qp + (size_t)min(l16, G - 1) * D + kd_dim<TC, D>(q4, ks));
+  const int L = scalar_load(a.seq_lens, s);
+  const int bv = lane < a.top_k ? bv_raw : -1;
+  const int pall = a.page_table[(size_t)s * a.max_pages + min(max(bv, 0), a.max_pages - 1)];
+  const int p = L - 1, diag = p >> 7;
   uint32_t used = 0;
   {
     int prev = -1;
@@ -1039,11 +1044,9 @@ __global__ __launch_bounds__(NW * 64) void kd_kernel(KdArgs a) {
   const int bl = mine ? bv : 0;
   const int pages = mine ? pall : 0;
   const float c2 = a.sm_scale * kLog2e;
-  const T* __restrict__ qp = static_cast<const T*>(a.q) + ((size_t)s * a.h_q + r * G) * D;
-  Frag<T> qf[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = (l16 < G) ? load_frag<T>(qp + (size_t)l16 * D + kd_dim<TC, D>(q4, ks)) : zero_frag<T>();
+    if (l16 >= G) qf[ks] = zero_frag<T>();
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};

@@ -491,29 +491,34 @@ template <typename T, int DIDX, typename TC, int POOL>
 __global__ __launch_bounds__(256) void ki_decode_scan_kernel(KiDecodeArgs a) {
   constexpr int KS = DIDX / 32;
   const int s = blockIdx.y;
-  const int L = scalar_load(a.seq_lens, s);
-  const int p = L - 1;
-  const int nb = (L + kBlock - 1) / kBlock;
-  const int hi = (a.need_diag || !a.force_local) ? nb : nb - 1;
   static_assert(kKiDecodePagesPerWg % 4 == 0 && kKiDecodePagesPerWg <= 256, "4 waves, one page id per lane");
   const int pg_begin = blockIdx.x * kKiDecodePagesPerWg;
-  const int pg_end = min(pg_begin + kKiDecodePagesPerWg, hi);
-  if (pg_begin >= pg_end) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q4 = lane >> 4, l16 = lane & 15;
   const T* __restrict__ q_idx = static_cast<const T*>(a.q_idx);
   const TC* __restrict__ k_idx = static_cast<const TC*>(a.k_idx);
+  // The query and the page ids are loaded together with the sequence length
+  // (neither depends on it), so a workgroup waits for one round trip before
+  // its first page load instead of two.  Lane j holds the physical page of
+  // this wave's j-th page (at most 64: a workgroup covers at most 256 pages),
+  // read with one vector load clamped into the row; entries past the
+  // sequence's last page are never used.
+  const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
+  int pid = pt[min(pg_begin + wave + 4 * lane, a.max_pages - 1)];
   Frag<T> qa[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qa[ks] = (l16 < a.h_kv) ? load_frag<T>(q_idx + ((size_t)s * a.h_kv + l16) * DIDX + ki_dim<TC, DIDX>(q4, ks))
-                            : zero_frag<T>();
-  const int32_t* pt = a.page_table + (size_t)s * a.max_pages;
-  // Lane j holds the physical page of this wave's j-th page (at most 64: a
-  // workgroup covers at most 256 pages), read with one vector load, so no
-  // page's loads wait on a page-table read of their own.
-  const int my_pg = pg_begin + wave + 4 * lane;
-  int pid = my_pg < pg_end ? pt[my_pg] : 0;
+    qa[ks] = load_frag<T>(q_idx + ((size_t)s * a.h_kv + min(l16, a.h_kv - 1)) * DIDX + ki_dim<TC, DIDX>(q4, ks));
+  const int L = scalar_load(a.seq_lens, s);
+  const int p = L - 1;
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int hi = (a.need_diag || !a.force_local) ? nb : nb - 1;
+  // a workgroup past the sequence's last page scores nothing below (no early
+  // exit: a branch on the length would hold the loads above back behind it)
+  const int pg_end = min(pg_begin + kKiDecodePagesPerWg, hi);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    if (l16 >= a.h_kv) qa[ks] = zero_frag<T>();
   settle(pid);  // waited for here, so no later wait on it also covers page loads in flight
   // For rows of up to 128 bytes the next page's index keys are loaded while
   // the current page is scored (wider rows would not fit two pages).
@@ -669,18 +674,19 @@ __global__ __launch_bounds__(NT) void ki_decode_select_kernel(KiDecodeArgs a) {
   __shared__ uint64_t thr[kLevels];
   __shared__ int count;
   const int s = blockIdx.x / a.h_kv, r = blockIdx.x % a.h_kv;
+  const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The scores are loaded together with the sequence length (clamped into
+  // the row, not to its candidates): candidates past the row's end get key 0
+  // whatever was read.  All loads are issued before any is used: settle()
+  // keeps the compiler from moving each load under its own branch, one round
+  // trip at a time.
+  float v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = sc[min(tid + NT * u, a.max_pages - 1)];
   const int L = scalar_load(a.seq_lens, s);
   const int diag = (L - 1) / kBlock;
   const int ncand = min(a.force_local ? diag : diag + 1, a.max_pages);
-  const float* sc = a.scores + ((size_t)s * a.h_kv + r) * a.max_pages;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Candidates past the row's end read a clamped (in-bounds) entry and get
-  // key 0.  All loads are issued before any is used: settle() keeps the
-  // compiler from moving each load under its own branch, one round trip at a
-  // time.
-  float v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) v[u] = sc[max(min(tid + NT * u, ncand - 1), 0)];
 #pragma unroll
   for (int u = 0; u < U; ++u) settle(v[u]);
   uint64_t k[U];
