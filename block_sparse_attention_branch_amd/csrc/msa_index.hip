@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
       for (int i = 0; i < LOADS; ++i) {
         const uint32_t pos = (uint32_t)((wave_u * LOADS + i) * 1024) + (uint32_t)lane * 16;  // byte in the buffer
         const uint32_t r = pos / ROW_BYTES, c = ((pos % ROW_BYTES) / 16) ^ swz(r);
-        const uint32_t off = (full ? r : min(r, last)) * ROW_BYTES + c * 16;
+        const uint32_t off = min(r, last) * ROW_BYTES + c * 16;  // r <= 127: a full block needs no clamp
         __builtin_amdgcn_global_load_lds(base + off, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0,
                                          0);
       }
