@@ -292,16 +292,17 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
         }
       }
     }
-    // lanes l and l+32 hold the two key halves of rows l and 32+l: swap so
-    // that lane L ends with the whole-block max of wave row L
-    const float send = half ? m0 : m1;
-    const float recv = __shfl_xor(send, 32, 64);
+    // lanes l and l+32 hold the two key halves of rows l (m0) and 32+l (m1):
+    // swapping the upper half of m0 with the lower half of m1 leaves lane L
+    // with both halves of wave row L, one in each result
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+    const float h0 = __uint_as_float(sw[0]), h1 = __uint_as_float(sw[1]);
     float pooled;
     if constexpr (POOL == 0) {
-      pooled = fmaxf(half ? m1 : m0, recv) * a.idx_scale;
+      pooled = fmaxf(h0, h1) * a.idx_scale;
     } else {  // mean over the keys of block b visible from this lane's row
       const int cnt = min(kBlock, a.q_start + (my_valid ? my_row : row_last) / a.h_kv - b * kBlock + 1);
-      pooled = cnt > 0 ? ((half ? m1 : m0) + recv) * a.idx_scale / (float)cnt : -__builtin_inff();
+      pooled = cnt > 0 ? (h0 + h1) * a.idx_scale / (float)cnt : -__builtin_inff();
     }
     // A candidate that beats the list's last entry is set aside in this
     // lane's pending slots; the list absorbs them when some lane of the wave
