@@ -260,10 +260,9 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
     const bool masked = b >= min_diag;
     constexpr float kDrop = POOL == 0 ? -__builtin_inff() : 0.0f;  // a masked key's contribution
     float m0 = kDrop, m1 = kDrop;
-    // not unrolled: an unrolled nest keeps every tile's addresses and mask
-    // constants live and halves the occupancy
-#pragma unroll 1
-    for (int kt = 0; kt < 4; ++kt) {
+    // One 32-key tile: its MFMAs, the causal mask (diagonal blocks only) and
+    // the pool into (m0, m1).
+    auto tile = [&](int kt, bool mask) __attribute__((always_inline)) {
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -273,7 +272,7 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
         mma32(acc0, af, qf[0][ks]);
         mma32(acc1, af, qf[1][ks]);
       }
-      if (masked) {
+      if (mask) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = b * kBlock + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -291,6 +290,15 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
           m1 += acc1[v];
         }
       }
+    };
+    // The diagonal blocks (masked) run a loop; the others unrolled, so their
+    // LDS addresses are immediate offsets of the first tile's.
+    if (masked) {
+#pragma unroll 1
+      for (int kt = 0; kt < 4; ++kt) tile(kt, true);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) tile(kt, false);
     }
     // lanes l and l+32 hold the two key halves of rows l (m0) and 32+l (m1):
     // swapping the upper half of m0 with the lower half of m1 leaves lane L
