@@ -209,18 +209,14 @@ __device__ __forceinline__ void list_insert(uint64_t (&keys)[L], uint64_t v) {
 // computed from the old list, so there is no serial chain.
 template <int L>
 __device__ __forceinline__ void list_insert_later(float (&sc)[L], int (&id)[L], float v, int b) {
-  // one compare per slot, shared by the slot and the one below it
-  bool ge[L];
-#pragma unroll
-  for (int s = 0; s < L; ++s) ge[s] = sc[s] >= v;
   // bottom up, so that each slot is overwritten after the slot below has
   // read it: the update stays in place
 #pragma unroll
   for (int s = L - 1; s >= 0; --s) {
     const float up = s > 0 ? sc[s - 1] : __builtin_inff();
-    const bool up_ge = s > 0 ? ge[s - 1] : true;
+    const bool up_ge = s > 0 ? sc[s - 1] >= v : true;
     const int up_id = s > 0 ? id[s - 1] : b;
-    id[s] = ge[s] ? id[s] : (up_ge ? b : up_id);
+    id[s] = sc[s] >= v ? id[s] : (up_ge ? b : up_id);
     sc[s] = __builtin_amdgcn_fmed3f(sc[s], up, v);
   }
 }
