@@ -291,6 +291,88 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
     print(json.dumps(t))
 
 
+def _short(name, width=66):
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def summarize_stats(stats_csv):
+    """Print the kernel-statistics table of a rocprofv3 --stats run (its
+    kernel_stats.csv), and the launch-weighted mean of the KV-outer kernel's
+    instances (the per-launch figure of the step's roofline)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    print(f"{'kernel':66s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for r in rows:
+        if float(r["Percentage"]) < 0.005:
+            continue
+        print(f"{_short(r['Name']):66s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+              f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
+    kp = [(int(r["Calls"]), float(r["AverageNs"]) / 1e3) for r in rows if "kp_kernel" in r["Name"]]
+    if kp:
+        n = sum(c for c, _ in kp)
+        terms = " + ".join(f"{c} x {a:.2f}" for c, a in kp)
+        print(f"\nkp_kernel, launch-weighted mean over its instances: ({terms}) / {n} = "
+              f"{sum(c * a for c, a in kp) / n:.1f} us")
+
+
+def summarize_counters(sq_csv, tcc_csv):
+    """Print per-kernel averages of the SQ and TCC counter runs (rocprofv3
+    --pmc counter_collection.csv files): matrix-core busy share, VALU
+    instructions per MFMA instruction and L2 hit rate."""
+    import csv
+    import collections
+    import re
+
+    def load(path):
+        d = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            did = int(r["Dispatch_Id"])
+            d[did][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[did] = r["Kernel_Name"]
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for did, c in d.items():
+            m = re.search(r"(k[a-z_]+_kernel)", names[did])
+            for cn, v in c.items():
+                agg[m.group(1) if m else names[did]][cn].append(v)
+        return agg
+
+    sq, tcc = load(sq_csv), load(tcc_csv)
+    mean = lambda xs: sum(xs) / len(xs) if xs else 0.0  # noqa: E731
+    print(f"{'kernel':26s} {'launches':>8s} {'mfma_busy':>9s} {'valu/mfma':>9s} {'valu_insts':>11s} {'mfma_insts':>11s} "
+          f"{'lds_insts':>10s} {'waves':>7s} {'gui_cycles':>11s} {'l2_hit':>7s}")
+    order = ["ki_prefill_kernel", "ki_merge_kernel", "ks_count_lds_kernel", "ks_scatter_lds_kernel", "ks_items_kernel",
+             "kp_kernel", "km_kernel", "ki_decode_scan_kernel", "ki_decode_select_kernel", "kd_kernel",
+             "kd_merge_kernel"]
+    for k in order:
+        a = sq.get(k)
+        if not a:
+            continue
+        gui = mean(a["GRBM_GUI_ACTIVE"])
+        busy = mean(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui / 8 * 1024) if gui else 0.0  # 8 XCDs, 1024 SIMDs
+        valu, mfma = mean(a["SQ_INSTS_VALU"]), mean(a["SQ_INSTS_MFMA"])
+        ratio = f"{valu / mfma:9.2f}" if mfma else f"{'-':>9s}"
+        h, m = mean(tcc[k]["TCC_HIT_sum"]), mean(tcc[k]["TCC_MISS_sum"])
+        print(f"{k:26s} {len(a['GRBM_GUI_ACTIVE']):8d} {busy:9.3f} {ratio} {valu:11.4g} {mfma:11.4g} "
+              f"{mean(a['SQ_INSTS_LDS']):10.4g} {mean(a['SQ_WAVES']):7.0f} {gui:11.4g} {h / (h + m) if h + m else 0:7.3f}")
+
+
+def traffic_table():
+    """Print the per-call and per-kernel tables of profiles/traffic.json."""
+    with open(TRAFFIC_JSON) as fh:
+        t = json.load(fh)
+    print(f"{'leg':16s} {'call':16s} {'fetch_GB':>10s} {'write_GB':>10s} {'total_GB':>10s}")
+    for leg, calls in t["workloads"].items():
+        for c, r in calls.items():
+            print(f"{leg:16s} {c:16s} {r['fetch_bytes'] / 1e9:10.3f} {r['write_bytes'] / 1e9:10.3f} {r['bytes'] / 1e9:10.3f}")
+    for w, ks in t.get("kernels", {}).items():
+        print(f"\n{'kernel (' + w + ')':26s} {'fetch_MB':>10s} {'write_MB':>10s} {'total_MB':>10s}")
+        for k, r in ks.items():
+            print(f"{k:26s} {r['fetch_bytes_per_launch'] / 1e6:10.1f} {r['write_bytes_per_launch'] / 1e6:10.1f} "
+                  f"{r['bytes_per_launch'] / 1e6:10.1f}")
+
+
 def bench_copy(args):
     """A plain device-to-device copy of COPY_BYTES (counter calibration)."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -479,9 +561,23 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                              "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json for --workload from rocprofv3 counter CSVs (no GPU)")
+    ap.add_argument("--traffic-table", action="store_true", help="print the tables of profiles/traffic.json (no GPU)")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print the kernel table of a rocprofv3 --stats run (no GPU)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("SQ_CSV", "TCC_CSV"),
+                    help="print per-kernel averages of the SQ and TCC counter runs (no GPU)")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(args.workload, *args.summarize_traffic)
+        return
+    if args.traffic_table:
+        traffic_table()
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library has no "
