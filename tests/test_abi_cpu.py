@@ -405,3 +405,51 @@ def test_header_is_plain_c_and_links(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.strip() == "ok 6"
+
+
+def test_bench_summarizes_stats_and_counters_without_gpu(tmp_path, capsys):
+    # The profile tables are host logic over rocprofv3 CSVs: the kernel table
+    # with the KV-outer kernel's launch-weighted mean over its instances, and
+    # per-kernel counter averages (matrix-core share of GRBM cycles over 8 XCDs
+    # and 1024 SIMDs, VALU per MFMA instruction, L2 hit rate, several rows of one
+    # dispatch adding up).  Checked on made-up CSVs with hand-computed values.
+    import csv
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod2", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    stats = tmp_path / "stats.csv"
+    with open(stats, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                                           "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow({"Name": "msa::kp_kernel<true>", "Calls": 3, "TotalDurationNs": 900000, "AverageNs": 300000,
+                    "Percentage": 60.0, "MinNs": 1, "MaxNs": 2, "StdDev": 0})
+        w.writerow({"Name": "msa::kp_kernel<false>", "Calls": 1, "TotalDurationNs": 1100000, "AverageNs": 1100000,
+                    "Percentage": 40.0, "MinNs": 1, "MaxNs": 2, "StdDev": 0})
+    bench.summarize_stats(str(stats))
+    out = capsys.readouterr().out
+    assert "(3 x 300.00 + 1 x 1100.00) / 4 = 500.0 us" in out  # (900 + 1100) / 4
+
+    def write(path, rows):
+        with open(path, "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for did, name, c, v in rows:
+                w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+
+    k = "_ZN3msa17ki_prefill_kernelIDF16bLi64EEEv"
+    # two dispatches: GRBM 8192 cycles (1024 per XCD), MFMA busy 1024 * 1024 * 0.5 cycles, 6 VALU per MFMA
+    sq = []
+    for did in (1, 2):
+        sq += [(did, k, "GRBM_GUI_ACTIVE", 8192), (did, k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1024 * 0.5),
+               (did, k, "SQ_INSTS_VALU", 600), (did, k, "SQ_INSTS_MFMA", 100), (did, k, "SQ_INSTS_LDS", 7),
+               (did, k, "SQ_WAVES", 64), (did, k, "SQ_BUSY_CYCLES", 1)]
+    # TCC rows per dispatch split in two (they add up): 3 hits, 1 miss
+    tcc = [(1, k, "TCC_HIT_sum", 1), (1, k, "TCC_HIT_sum", 2), (1, k, "TCC_MISS_sum", 1),
+           (2, k, "TCC_HIT_sum", 3), (2, k, "TCC_MISS_sum", 1)]
+    write(tmp_path / "sq.csv", sq)
+    write(tmp_path / "tcc.csv", tcc)
+    bench.summarize_counters(str(tmp_path / "sq.csv"), str(tmp_path / "tcc.csv"))
+    row = [l for l in capsys.readouterr().out.splitlines() if l.startswith("ki_prefill_kernel")][0].split()
+    assert row[1] == "2" and row[2] == "0.500" and row[3] == "6.00" and row[-1] == "0.750"
