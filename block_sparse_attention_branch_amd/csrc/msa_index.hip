@@ -183,9 +183,10 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
   int n_pend = 0;
   // Inserts the pending candidates (in block order) that still beat the
   // list's last entry (inserting one raises that bound for the next).
+  // (slot 0 holds the newest pending candidate, slot n_pend - 1 the oldest)
   auto absorb = [&]() {
 #pragma unroll
-    for (int p = 0; p < kPending; ++p)
+    for (int p = kPending - 1; p >= 0; --p)
       if (p < n_pend && psc[p] > lsc[kMaxTopK - 1]) list_insert_later(lsc, lid, psc[p], pbl[p]);
     n_pend = 0;
   };
@@ -319,11 +320,14 @@ __global__ __launch_bounds__(kKiThreads, (kKiDirect<T, TC> ? 4 : 3)) void ki_pre
     // that would be almost every block.
     {
       const bool want = b <= my_last && pooled > lsc[kMaxTopK - 1];
+      // a shift: the new candidate enters slot 0, the others move up one
 #pragma unroll
-      for (int p = 0; p < kPending; ++p) {
-        psc[p] = (want && n_pend == p) ? pooled : psc[p];
-        pbl[p] = (want && n_pend == p) ? b : pbl[p];
+      for (int p = kPending - 1; p > 0; --p) {
+        psc[p] = want ? psc[p - 1] : psc[p];
+        pbl[p] = want ? pbl[p - 1] : pbl[p];
       }
+      psc[0] = want ? pooled : psc[0];
+      pbl[0] = want ? b : pbl[0];
       n_pend += want ? 1 : 0;
       if (__any(n_pend == kPending)) absorb();
       if (b == my_diag_b) diag_score = pooled;
